@@ -1,0 +1,84 @@
+"""The seeded input generator follows the stated recipes: its codes equal
+those of the oracle's independently written recipe implementation."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+
+def _edge_rows(K, rng):
+    """Rows exercising recipe corners: all-zero blocks, exact emax*2^j blocks,
+    tiny and huge magnitudes, ties, negative zeros."""
+    rows = [rng.standard_normal(K).astype(np.float32) * np.float32(s) for s in (1.0, 1e-3, 1e3, 1e-30)]
+    z = np.zeros(K, np.float32); z[1::2] = -0.0
+    rows.append(z)
+    p = rng.standard_normal(K).astype(np.float32); p[::16] = 448.0 * 4; p[5::16] = 6.0 / 8
+    rows.append(p)
+    t = np.tile(np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32), K // 8)
+    rows.append(t)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
+def test_mx_recipe_matches_oracle(elem):
+    rng = np.random.default_rng(0)
+    x = np.concatenate([synth.normal(5, 40, 256), _edge_rows(256, rng)])
+    c1, s1 = synth.quant_mx(x, elem)
+    c2, s2 = oracle.quant_mx(x, elem)
+    assert np.array_equal(s1, s2)
+    assert np.array_equal(c1, c2)
+
+
+def test_nvfp4_recipe_matches_oracle():
+    rng = np.random.default_rng(1)
+    for x in (synth.normal(6, 33, 320), np.concatenate([synth.normal(7, 8, 256), _edge_rows(256, rng)]),
+              np.zeros((3, 64), np.float32)):
+        c1, s1, t1 = synth.quant_nvfp4(x)
+        c2, s2, t2 = oracle.quant_nvfp4(x)
+        assert t1 == t2
+        assert np.array_equal(s1, s2)
+        assert np.array_equal(c1, c2)
+
+
+def test_bf16_recipe_matches_oracle():
+    x = synth.normal(8, 50, 300)
+    assert np.array_equal(synth.bf16_from_f32(x), oracle.quant_bf16(x))
+
+
+def test_mx_scale_is_floor_log2_of_amax_over_emax():
+    x = synth.normal(9, 16, 512)
+    for elem, emax in (("e4m3", 448.0), ("e2m1", 6.0)):
+        _, s = synth.quant_mx(x, elem)
+        amax = np.abs(x.astype(np.float64)).reshape(16, 16, 32).max(axis=2)
+        sc = oracle.decode("e8m0", s)
+        assert np.all(sc * emax <= amax) and np.all(amax < 2 * sc * emax)
+
+
+def test_fp4_packing_low_nibble_first():
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0], x[0, 1] = 1.0, 6.0        # amax 6 -> scale 1 for E2M1
+    c, s = synth.quant_mx(x, "e2m1")
+    assert s[0, 0] == 127
+    assert c[0, 0] == (0x2 | (0x7 << 4))
+
+
+def test_generator_is_deterministic_and_seeded():
+    a = synth.normal(101, 64, 128)
+    b = synth.normal(101, 64, 128)
+    c = synth.normal(102, 64, 128)
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+    w1 = synth.workload("mxfp4", 64, 32, 128, 1, 2)
+    w2 = synth.workload("mxfp4", 64, 32, 128, 1, 2)
+    for k in ("A", "B", "sA", "sB"):
+        assert np.array_equal(w1[k], w2[k])
+
+
+def test_sample_entries_structured_then_uniform():
+    em, en = synth.sample_entries(3, 8192, 8192, 4096)
+    assert em.size == en.size == 4096
+    assert (em[:16] == np.repeat([0, 255, 256, 8191], 4)).all()
+    assert (en[:16] == np.tile([0, 255, 256, 8191], 4)).all()
+    assert em.max() < 8192 and en.max() < 8192
+    em2, en2 = synth.sample_entries(3, 8192, 8192, 4096)
+    assert np.array_equal(em, em2) and np.array_equal(en, en2)
