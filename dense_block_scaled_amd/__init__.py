@@ -1,0 +1,150 @@
+"""MI355X (gfx950) block-scaled GEMM: thin Python binding of libdbs.so.
+
+    D = bf16(alpha * (sA . A) @ (sB . B)^T),  fp32 accumulation
+
+The functions take torch tensors that already live on the GPU and only
+marshal pointers, sizes and the current stream into the C ABI of
+``include/dbs.h``; every step of the computation runs in the HIP kernels.
+There is no CPU fallback: if ``libdbs.so`` is missing, or a call reports an
+error, these functions raise.
+
+Operand encodings (all K-major, contiguous):
+  gemm_bf16(A, B)                     A: (M, K) bfloat16/uint16, B: (N, K)
+  gemm_mx(elem, A, sA, B, sB)         elem 'e4m3': A (M, K) uint8;
+                                      elem 'e2m1': A (M, K/2) uint8, 2 per byte
+                                      sA: (M, K/32) uint8 E8M0 codes
+  gemm_nvfp4(A, sA, tA, B, sB, tB)    A: (M, K/2) uint8 packed E2M1,
+                                      sA: (M, K/16) uint8 E4M3 codes, tA float
+Each returns D: (M, N) torch.bfloat16 (or writes into ``out``).
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+__all__ = ["gemm_bf16", "gemm_mx", "gemm_nvfp4", "lib", "LIB_PATH", "DbsError",
+           "DBS_OK", "DBS_EINVAL", "DBS_EUNSUPPORTED", "DBS_EHIP", "K_MAJOR", "MN_MAJOR",
+           "E4M3", "E2M1", "status_str"]
+
+LIB_PATH = Path(__file__).resolve().parent / "libdbs.so"
+
+DBS_OK, DBS_EINVAL, DBS_EUNSUPPORTED, DBS_EHIP = 0, 1, 2, 3
+K_MAJOR, MN_MAJOR = 0, 1
+E4M3, E2M1 = 0, 4
+_ELEM = {"e4m3": E4M3, "e2m1": E2M1}
+
+
+class DbsError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m dense_block_scaled_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(str(LIB_PATH))
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.gemm_bf16.argtypes = [P, P, P, I64, I64, I64, I, I, P]
+        L.gemm_bf16.restype = I
+        L.gemm_mx.argtypes = [I, P, P, P, P, P, I64, I64, I64, I, I, P]
+        L.gemm_mx.restype = I
+        L.gemm_nvfp4.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P]
+        L.gemm_nvfp4.restype = I
+        L.dbs_status_str.argtypes = [I]
+        L.dbs_status_str.restype = ctypes.c_char_p
+        L.dbs_last_error.argtypes = []
+        L.dbs_last_error.restype = ctypes.c_char_p
+        L.dbs_version.restype = I
+        _lib = L
+    return _lib
+
+
+def status_str(st: int) -> str:
+    return lib().dbs_status_str(st).decode()
+
+
+def _check(st: int) -> None:
+    if st != DBS_OK:
+        raise DbsError(st, f"{status_str(st)}: {lib().dbs_last_error().decode()}")
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _out(out, M, N, like):
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=like.device)
+    _dev(out, "out", (torch.bfloat16, torch.int16, torch.uint16), (M, N))
+    return out
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def gemm_bf16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """D = A @ B^T for bf16 A (M, K), B (N, K); fp32 accumulate, bf16 out."""
+    M, K = A.shape
+    N = B.shape[0]
+    dt = (torch.bfloat16, torch.int16, torch.uint16)
+    pa = _dev(A, "A", dt, (M, K))
+    pb = _dev(B, "B", dt, (N, K))
+    out = _out(out, M, N, A)
+    _check(lib().gemm_bf16(pa, pb, ctypes.c_void_p(out.data_ptr()), M, N, K, K_MAJOR, K_MAJOR, _stream(A)))
+    return out
+
+
+def gemm_mx(elem: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor,
+            K: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """MXFP8 (elem='e4m3') or MXFP4 (elem='e2m1') GEMM with E8M0 scales per 32."""
+    code = _ELEM[elem]
+    M, N = A.shape[0], B.shape[0]
+    if K is None:
+        K = A.shape[1] * (2 if elem == "e2m1" else 1)
+    kb = K // 2 if elem == "e2m1" else K
+    u8 = (torch.uint8,)
+    pa = _dev(A, "A", u8, (M, kb))
+    pb = _dev(B, "B", u8, (N, kb))
+    psa = _dev(sA, "sA", u8, (M, K // 32))
+    psb = _dev(sB, "sB", u8, (N, K // 32))
+    out = _out(out, M, N, A)
+    _check(lib().gemm_mx(code, pa, psa, pb, psb, ctypes.c_void_p(out.data_ptr()), M, N, K,
+                         K_MAJOR, K_MAJOR, _stream(A)))
+    return out
+
+
+def gemm_nvfp4(A: torch.Tensor, sA: torch.Tensor, tA: float, B: torch.Tensor, sB: torch.Tensor, tB: float,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """NVFP4 GEMM: packed E2M1 with E4M3 scales per 16 and fp32 tensor scales."""
+    M, N = A.shape[0], B.shape[0]
+    K = A.shape[1] * 2
+    u8 = (torch.uint8,)
+    pa = _dev(A, "A", u8, (M, K // 2))
+    pb = _dev(B, "B", u8, (N, K // 2))
+    psa = _dev(sA, "sA", u8, (M, K // 16))
+    psb = _dev(sB, "sB", u8, (N, K // 16))
+    out = _out(out, M, N, A)
+    _check(lib().gemm_nvfp4(pa, psa, float(tA), pb, psb, float(tB), ctypes.c_void_p(out.data_ptr()),
+                            M, N, K, K_MAJOR, K_MAJOR, _stream(A)))
+    return out

@@ -1,0 +1,155 @@
+// dbs.cpp -- the C ABI declared in include/dbs.h: argument validation, tile
+// configuration and launch of the gfx950 kernels in gemm.hip.
+#include "dbs.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dbs_status fail(dbs_status st, const char *msg)
+{
+    std::snprintf(g_err, sizeof(g_err), "%s", msg);
+    return st;
+}
+
+dbs_status fail_hip(hipError_t e, const char *what)
+{
+    std::snprintf(g_err, sizeof(g_err), "%s: %s", what, hipGetErrorString(e));
+    return DBS_EHIP;
+}
+
+// CU count per device, looked up once (the library's only state).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+dbs_status device_cus(int *cus)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(DBS_EHIP, "device index out of range");
+    int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c <= 0) {
+        e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute");
+        if (c <= 0) return fail(DBS_EHIP, "device reports no compute units");
+        g_cus[dev].store(c, std::memory_order_relaxed);
+    }
+    *cus = c;
+    return DBS_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+dbs_status check_common(const void *A, const void *B, const void *D, int64_t M, int64_t N, int64_t K,
+                        dbs_layout la, dbs_layout lb, int64_t kmax)
+{
+    if (!A || !B || !D) return fail(DBS_EINVAL, "null pointer argument");
+    if (M <= 0 || N <= 0 || K <= 0) return fail(DBS_EINVAL, "M, N and K must be positive");
+    if (M > (int64_t(1) << 30) || N > (int64_t(1) << 30)) return fail(DBS_EINVAL, "M or N above 2^30");
+    if (K > kmax) return fail(DBS_EINVAL, "K above the supported maximum");
+    if ((la != DBS_K_MAJOR && la != DBS_MN_MAJOR) || (lb != DBS_K_MAJOR && lb != DBS_MN_MAJOR))
+        return fail(DBS_EINVAL, "unknown layout value");
+    if (!aligned(A, 16) || !aligned(B, 16)) return fail(DBS_EINVAL, "A and B must be 16-byte aligned");
+    if (!aligned(D, 2)) return fail(DBS_EINVAL, "D must be 2-byte aligned");
+    if (la != DBS_K_MAJOR || lb != DBS_K_MAJOR)
+        return fail(DBS_EUNSUPPORTED, "only K-major A and B are implemented");
+    return DBS_OK;
+}
+
+dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB, void *D, int64_t M,
+               int64_t N, int64_t K, float alpha, int elem_bits, int block, hipStream_t stream)
+{
+    int cus = 0;
+    dbs_status st = device_cus(&cus);
+    if (st != DBS_OK) return st;
+
+    dbs::Params p{};
+    p.A = static_cast<const uint8_t *>(A);
+    p.B = static_cast<const uint8_t *>(B);
+    p.sA = sA;
+    p.sB = sB;
+    p.D = static_cast<uint16_t *>(D);
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.lda = (int)(K * elem_bits / 8);
+    p.sld = block ? (int)(K / block) : 0;
+    const int sk = dbs::stage_k(fmt);
+    p.nk = (int)((K + sk - 1) / sk);
+    p.tiles_m = (int)((M + dbs::kTileM - 1) / dbs::kTileM);
+    p.tiles_n = (int)((N + dbs::kTileN - 1) / dbs::kTileN);
+    p.group_m = 4;
+    p.vec_store = (N % 4 == 0 && aligned(D, 8)) ? 1 : 0;
+    p.alpha = alpha;
+
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    if (tiles > INT32_MAX) return fail(DBS_EINVAL, "too many output tiles");
+    const int grid = (int)std::min<int64_t>(tiles, cus);
+    hipError_t e = dbs::launch_gemm(fmt, p, grid, stream);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    g_err[0] = '\0';
+    return DBS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dbs_status gemm_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, dbs_layout la,
+                     dbs_layout lb, hipStream_t stream)
+{
+    dbs_status st = check_common(A, B, D, M, N, K, la, lb, int64_t(1) << 21);
+    if (st != DBS_OK) return st;
+    if (K % 8) return fail(DBS_EINVAL, "bf16: K must be a multiple of 8");
+    return run(dbs::kBF16, A, nullptr, B, nullptr, D, M, N, K, 1.0f, 16, 0, stream);
+}
+
+dbs_status gemm_mx(dbs_mx_elem elem, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB, void *D,
+                   int64_t M, int64_t N, int64_t K, dbs_layout la, dbs_layout lb, hipStream_t stream)
+{
+    if (elem != DBS_E4M3 && elem != DBS_E2M1) return fail(DBS_EINVAL, "mx: unknown element format");
+    if (!sA || !sB) return fail(DBS_EINVAL, "null pointer argument");
+    dbs_status st = check_common(A, B, D, M, N, K, la, lb, int64_t(1) << 22);
+    if (st != DBS_OK) return st;
+    if (K % 32) return fail(DBS_EINVAL, "mx: K must be a multiple of 32");
+    if (elem == DBS_E4M3) return run(dbs::kMXFP8, A, sA, B, sB, D, M, N, K, 1.0f, 8, 32, stream);
+    return run(dbs::kMXFP4, A, sA, B, sB, D, M, N, K, 1.0f, 4, 32, stream);
+}
+
+dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA, const void *B, const uint8_t *sB, float tB,
+                      void *D, int64_t M, int64_t N, int64_t K, dbs_layout la, dbs_layout lb, hipStream_t stream)
+{
+    if (!sA || !sB) return fail(DBS_EINVAL, "null pointer argument");
+    dbs_status st = check_common(A, B, D, M, N, K, la, lb, int64_t(1) << 22);
+    if (st != DBS_OK) return st;
+    if (K % 16) return fail(DBS_EINVAL, "nvfp4: K must be a multiple of 16");
+    if (K % 32) return fail(DBS_EUNSUPPORTED, "nvfp4: K must be a multiple of 32 in this implementation");
+    return run(dbs::kNVFP4, A, sA, B, sB, D, M, N, K, tA * tB, 4, 16, stream);
+}
+
+const char *dbs_status_str(dbs_status st)
+{
+    switch (st) {
+    case DBS_OK: return "DBS_OK: success";
+    case DBS_EINVAL: return "DBS_EINVAL: invalid argument";
+    case DBS_EUNSUPPORTED: return "DBS_EUNSUPPORTED: valid request not implemented";
+    case DBS_EHIP: return "DBS_EHIP: HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *dbs_last_error(void) { return g_err; }
+
+int dbs_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// launch.h -- internal interface between the C ABI (dbs.cpp) and the gfx950
+// kernels (gemm.hip).  Not installed; callers use include/dbs.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace dbs {
+
+enum Format : int { kBF16 = 0, kMXFP8 = 1, kMXFP4 = 2, kNVFP4 = 3 };
+
+// Everything a kernel needs, passed by value.  Sizes were validated on the
+// host: every per-tile byte offset fits in 31 bits.
+struct Params {
+    const uint8_t *A;     // M x lda bytes
+    const uint8_t *B;     // N x lda bytes
+    const uint8_t *sA;    // M x sld scale bytes (null for bf16)
+    const uint8_t *sB;    // N x sld scale bytes
+    uint16_t *D;          // M x N bf16
+    int M, N, K;
+    int lda;              // bytes per operand row (K * element bits / 8)
+    int sld;              // scale bytes per row (K / block size), 0 for bf16
+    int nk;               // number of K stages
+    int tiles_m, tiles_n;
+    int group_m;          // tile rows per raster group
+    int vec_store;        // 1 if D rows allow 8-byte stores (N % 4 == 0)
+    float alpha;          // applied to the fp32 accumulator before rounding
+};
+
+// Elements of K consumed per pipeline stage for each format.
+constexpr int stage_k(int fmt) {
+    return fmt == kBF16 ? 64 : fmt == kMXFP8 ? 128 : fmt == kMXFP4 ? 256 : 64;
+}
+
+constexpr int kTileM = 256;
+constexpr int kTileN = 256;
+
+hipError_t launch_gemm(int fmt, const Params &p, int grid, hipStream_t stream);
+
+}  // namespace dbs

@@ -1,0 +1,96 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point that
+include/dbs.h declares, and rejects bad arguments with a status code before
+any device work.  No compute call is made."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+import torch
+
+import dense_block_scaled_amd as dbs
+
+ROOT = Path(__file__).resolve().parent.parent
+
+
+def _declared():
+    text = (ROOT / "include" / "dbs.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("gemm_bf16", "gemm_mx", "gemm_nvfp4", "dbs_status_str", "dbs_last_error", "dbs_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = dbs.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert L.dbs_version() == 100
+
+
+def test_status_strings():
+    for st in (0, 1, 2, 3):
+        assert dbs.status_str(st).startswith("DBS_")
+
+
+FAKE = ctypes.c_void_p(1 << 20)      # 16-byte aligned, never dereferenced
+NUL = ctypes.c_void_p(0)
+
+
+@pytest.mark.parametrize("args,want", [
+    ((NUL, FAKE, FAKE, 16, 16, 16, 0, 0), 1),          # null A
+    ((FAKE, FAKE, FAKE, 0, 16, 16, 0, 0), 1),          # M = 0
+    ((FAKE, FAKE, FAKE, 16, -1, 16, 0, 0), 1),         # N < 0
+    ((FAKE, FAKE, FAKE, 16, 16, 12, 0, 0), 1),         # K % 8
+    ((FAKE, FAKE, FAKE, 16, 16, 1 << 22, 0, 0), 1),    # K too large
+    ((ctypes.c_void_p((1 << 20) + 4), FAKE, FAKE, 16, 16, 16, 0, 0), 1),  # misaligned A
+    ((FAKE, FAKE, FAKE, 16, 16, 16, 1, 0), 2),         # MN-major A: unsupported
+    ((FAKE, FAKE, FAKE, 16, 16, 16, 0, 7), 1),         # unknown layout
+])
+def test_bf16_validation(args, want):
+    L = dbs.lib()
+    assert L.gemm_bf16(*args, NUL) == want
+    assert L.dbs_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("elem,K,want", [(0, 48, 1), (4, 16, 1), (9, 64, 1), (0, 64, 2)])
+def test_mx_validation(elem, K, want):
+    L = dbs.lib()
+    lb = 1 if want == 2 else 0
+    assert L.gemm_mx(elem, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, K, 0, lb, NUL) == want
+
+
+def test_mx_null_scales():
+    L = dbs.lib()
+    assert L.gemm_mx(0, FAKE, NUL, FAKE, FAKE, FAKE, 8, 8, 64, 0, 0, NUL) == 1
+
+
+@pytest.mark.parametrize("K,want", [(24, 1), (48, 2)])
+def test_nvfp4_validation(K, want):
+    L = dbs.lib()
+    assert L.gemm_nvfp4(FAKE, FAKE, 1.0, FAKE, FAKE, 1.0, FAKE, 8, 8, K, 0, 0, NUL) == want
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would reach a real device")
+def test_no_device_reports_ehip_without_aborting():
+    L = dbs.lib()
+    st = L.gemm_bf16(FAKE, FAKE, FAKE, 16, 16, 16, 0, 0, NUL)
+    assert st == 3
+    assert L.dbs_last_error().decode()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(dbs, "_lib", None)
+    monkeypatch.setattr(dbs, "LIB_PATH", tmp_path / "libdbs.so")
+    with pytest.raises(ImportError):
+        dbs.lib()
+
+
+def test_binding_rejects_cpu_tensors():
+    A = torch.zeros((8, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dbs.gemm_bf16(A, A)

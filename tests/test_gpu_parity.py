@@ -1,0 +1,191 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: bit-exact where the exact result is representable (identity,
+permutation, power-of-two scale shifts, integer bf16); elsewhere
+r = |D - D_ref| / (||dA_m|| ||dB_n|| |alpha|) <= 1e-2 and within the derived
+bound 2^-8 + K 2^-23 of a correct fp32-accumulating path (tests/_gpu.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests import _gpu, _pins
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["bf16", "mxfp8", "mxfp4", "nvfp4"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+
+
+def _w(fmt, M, N, K, seed=1):
+    return synth.workload(fmt, M, N, K, 100 * seed + 1, 100 * seed + 2)
+
+
+# ---- the small seeded config and ragged shapes, full comparison ----------------
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_cube_256(fmt):
+    _gpu.say(f"[parity] {fmt} 256^3 seed 0")
+    w = _w(fmt, 256, 256, 256, seed=0)
+    D = _gpu.run(fmt, w)
+    torch.cuda.synchronize()
+    _gpu.check_full(fmt, w, D)
+
+
+RAGGED = [
+    (300, 520, 352),      # partial tiles in M and N, partial last K stage
+    (257, 129, 96),       # one row / one column past a tile edge
+    (1, 1, 32),           # single output
+    (33, 7, 64),          # N not a multiple of 4 (element-wise stores)
+    (512, 260, 4096),     # long K: many ring rotations
+    (5000, 4100, 96),     # 340 tiles > one persistent round
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+def test_ragged(fmt, shape):
+    M, N, K = shape
+    _gpu.say(f"[parity] {fmt} ragged {shape}")
+    w = _w(fmt, M, N, K, seed=3)
+    D = _gpu.run(fmt, w)
+    torch.cuda.synchronize()
+    _gpu.check_full(fmt, w, D)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_random_codes_and_scales(fmt):
+    """Codes over the whole finite range with random non-unit scales at small K,
+    where one mis-applied block scale would give r >> 1e-2."""
+    _gpu.say(f"[parity] {fmt} random codes K=64")
+    rng = np.random.default_rng(21)
+    kw = {"scale_lo": 112, "scale_hi": 142}
+    if fmt == "nvfp4":
+        kw = {"scale_lo": 0x08, "scale_hi": 0x7E}
+    if fmt == "bf16":
+        kw = {"bf16_exp": (110, 144)}
+    w = _pins.make_w(fmt, 300, 280, 64, rng, **kw)
+    D = _gpu.run(fmt, w)
+    torch.cuda.synchronize()
+    _gpu.check_full(fmt, w, D)
+
+
+# ---- bit-exact cases ------------------------------------------------------------
+
+def _identity_w(fmt, M, K, rng, permute):
+    N = K
+    pi = rng.permutation(K) if permute else np.arange(K)
+    kw = {"scale_lo": 110, "scale_hi": 140} if fmt != "nvfp4" else {"scale_lo": 0x10, "scale_hi": 0x70}
+    a = _pins.random_codes(fmt, M, K, rng, **kw)
+    w = {"fmt": fmt, "M": M, "N": N, "K": K, "A": a["X"]}
+    if fmt == "bf16":
+        B = np.zeros((N, K), np.uint16)
+        B[np.arange(N), pi] = 0x3F80
+    elif fmt == "mxfp8":
+        B = np.zeros((N, K), np.uint8)
+        B[np.arange(N), pi] = 0x38
+    else:
+        codes = np.zeros((N, K), np.uint8)
+        codes[np.arange(N), pi] = 0x2
+        B = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    w["B"] = B
+    if fmt in ("mxfp8", "mxfp4"):
+        w["sA"] = a["s"]
+        w["sB"] = rng.integers(118, 137, (N, K // 32)).astype(np.uint8)
+    elif fmt == "nvfp4":
+        w["sA"] = a["s"]
+        w["sB"] = rng.integers(0x28, 0x50, (N, K // 16)).astype(np.uint8)   # non-power-of-two E4M3
+        w["tA"], w["tB"] = 1.0, 1.0
+    return w
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("permute", [False, True], ids=["identity", "permutation"])
+def test_exact_identity_permutation(fmt, permute):
+    _gpu.say(f"[exact] {fmt} permute={permute}")
+    rng = np.random.default_rng(31)
+    w = _identity_w(fmt, 300, 512, rng, permute)
+    D = _gpu.run(fmt, w)
+    torch.cuda.synchronize()
+    _gpu.check_exact(fmt, w, D)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "nvfp4"])
+def test_exact_pow2_scale_shift(fmt):
+    """Moving every A scale by a power of two (E8M0 code +3; E4M3 exponent
+    field -3) scales every output by exactly that power."""
+    _gpu.say(f"[exact] {fmt} pow2 shift")
+    w = _w(fmt, 260, 300, 512, seed=4)
+    D0 = _gpu.d_bits(_gpu.run(fmt, w))
+    w2 = dict(w)
+    if fmt == "nvfp4":
+        assert w["sA"].min() >= 0x20          # stays a normal E4M3 value
+        w2["sA"] = (w["sA"].astype(np.int64) - 24).astype(np.uint8)
+        factor = np.float32(0.125)
+    else:
+        w2["sA"] = (w["sA"].astype(np.int64) + 3).astype(np.uint8)
+        factor = np.float32(8.0)
+    D1 = _gpu.d_bits(_gpu.run(fmt, w2))
+    torch.cuda.synchronize()
+    f0 = (D0.astype(np.uint32) << 16).view(np.float32)
+    f1 = (D1.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(f1, f0 * factor)
+
+
+def test_exact_bf16_integers():
+    """bf16 integer inputs in [-8, 8] at K = 1024: every partial sum is an
+    integer below 2^24, so the fp32 result is exact and so is bf16(D)."""
+    _gpu.say("[exact] bf16 integers")
+    rng = np.random.default_rng(41)
+    M, N, K = 300, 270, 1024
+    ia = rng.integers(-8, 9, (M, K)).astype(np.float32)
+    ib = rng.integers(-8, 9, (N, K)).astype(np.float32)
+    w = {"fmt": "bf16", "M": M, "N": N, "K": K,
+         "A": (ia.view(np.uint32) >> 16).astype(np.uint16), "B": (ib.view(np.uint32) >> 16).astype(np.uint16)}
+    D = _gpu.run("bf16", w)
+    torch.cuda.synchronize()
+    _gpu.check_exact("bf16", w, D)
+
+
+def test_exact_nvfp4_tensor_scales():
+    """NVFP4 with power-of-two tensor scales tA = 2, tB = 0.25 on an identity B."""
+    _gpu.say("[exact] nvfp4 tensor scales")
+    rng = np.random.default_rng(51)
+    w = _identity_w("nvfp4", 64, 256, rng, True)
+    w["tA"], w["tB"] = 2.0, 0.25
+    D = _gpu.run("nvfp4", w)
+    torch.cuda.synchronize()
+    _gpu.check_exact("nvfp4", w, D)
+
+
+# ---- determinism (a race canary) ---------------------------------------------------
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_repeat_bit_identical(fmt):
+    _gpu.say(f"[determinism] {fmt}")
+    w = _w(fmt, 1024, 768, 1024, seed=5)
+    dev = _gpu.to_dev(w)
+    first = _gpu.d_bits(_gpu.run(fmt, w, dev))
+    for _ in range(20):
+        again = _gpu.d_bits(_gpu.run(fmt, w, dev))
+        assert np.array_equal(first, again)
+
+
+def test_out_argument_and_stream():
+    """Writing into a caller-provided output on a non-default stream."""
+    _gpu.say("[abi] out= on a side stream")
+    w = _w("bf16", 256, 256, 256, seed=6)
+    dev = _gpu.to_dev(w)
+    out = torch.full((256, 256), 7.0, dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _gpu.run("bf16", w, dev, out=out)
+    s.synchronize()
+    _gpu.check_full("bf16", w, out)
