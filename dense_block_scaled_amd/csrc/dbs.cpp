@@ -55,7 +55,7 @@ dbs_status check_common(const void *A, const void *B, const void *D, int64_t M, 
 {
     if (!A || !B || !D) return fail(DBS_EINVAL, "null pointer argument");
     if (M <= 0 || N <= 0 || K <= 0) return fail(DBS_EINVAL, "M, N and K must be positive");
-    if (M > (int64_t(1) << 30) || N > (int64_t(1) << 30)) return fail(DBS_EINVAL, "M or N above 2^30");
+    if (M > (int64_t(1) << 25) || N > (int64_t(1) << 25)) return fail(DBS_EINVAL, "M or N above 2^25");
     if (K > kmax) return fail(DBS_EINVAL, "K above the supported maximum");
     if ((la != DBS_K_MAJOR && la != DBS_MN_MAJOR) || (lb != DBS_K_MAJOR && lb != DBS_MN_MAJOR))
         return fail(DBS_EINVAL, "unknown layout value");
@@ -90,6 +90,7 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     p.tiles_n = (int)((N + dbs::kTileN - 1) / dbs::kTileN);
     p.group_m = 4;
     p.vec_store = (N % 4 == 0 && aligned(D, 8)) ? 1 : 0;
+    p.scales_aligned = (block == 0 || (p.sld % 4 == 0 && aligned(sA, 4) && aligned(sB, 4))) ? 1 : 0;
     p.alpha = alpha;
 
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;

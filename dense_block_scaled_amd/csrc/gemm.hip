@@ -15,28 +15,35 @@
 //   share A and B panels in that XCD's L2 (the locality concern of the
 //   "ThunderKittens 2.0" notes, section 6, and the raster-order tuning of the
 //   Vera Rubin post, final optimisations).
-// * Staging.  Each stage moves a 256-row x 128-byte slab of A and of B from
-//   HBM through registers into a two-slot LDS ring (2 x 64 KiB of the 160 KiB
-//   LDS; cf. the stage-count discussion of "Async Tensor Core: Hopper wgmma ->
-//   Blackwell tcgen05", sections 3.1 and 4.3).  Buffer loads return zero for
-//   out-of-range rows and K columns, which handles ragged M, N and K.  16-byte
-//   chunks are XOR-swizzled per row so fragment reads are bank-conflict-free.
-//   One barrier per stage; no fences (cf. "ThunderKittens 2.0", section 1).
+// * Staging.  Each stage moves a 256-row x 128-byte slab of A and of B into
+//   one slot of a two-slot LDS ring (2 x 64 KiB of the 160 KiB LDS; cf. the
+//   stage-count discussion of "Async Tensor Core: Hopper wgmma -> Blackwell
+//   tcgen05", sections 3.1 and 4.3).  BF16/E4M3/E2M1 slabs go straight from
+//   HBM to LDS (buffer_load_dwordx4 ... lds), so staging costs no VGPRs and no
+//   LDS-write instructions; the load for stage s+1 is issued at the start of
+//   stage s.  Each lane fetches the global chunk that belongs at its fixed LDS
+//   position under an XOR swizzle of the 16-byte chunks, which keeps fragment
+//   reads bank-conflict-free.  Buffer loads return zero for rows past M and
+//   for K columns past K (ragged shapes).  One barrier per stage and no
+//   fences (cf. "ThunderKittens 2.0", section 1).
 // * Scales.  MX scale bytes ride the same stage as their operand slab: they
 //   are loaded one stage ahead straight into VGPRs and fed to the scaled MFMA
 //   as its per-lane E8M0 operand (the gfx950 counterpart of issuing the scale
-//   copy in the same thread as the MMA, "ThunderKittens 2.0", section 2.1).
-// * Math.  Each of the 4 waves owns a 128 x 128 sub-tile as 4 x 4 MFMA
-//   32x32 blocks (256 fp32 accumulators per lane) and reuses every A and B
-//   fragment four times from VGPRs (cf. dual accumulation, "ThunderKittens
-//   2.0", section 2.2).  BF16: v_mfma_f32_32x32x16_bf16.  MXFP8/MXFP4:
+//   copy from the same thread as the MMA, "ThunderKittens 2.0", section 2.1).
+// * Math.  Each of the 4 waves owns a 128 x 128 sub-tile as 4 x 4 MFMA 32x32
+//   blocks (256 fp32 accumulators per lane) and reuses every A and B fragment
+//   four times from VGPRs (cf. dual accumulation, "ThunderKittens 2.0",
+//   section 2.2).  Fragments are double-buffered in VGPRs: the reads for
+//   k-step kk+1 are in flight while the MFMAs of kk issue, and the MFMAs of a
+//   stage's last k-step are issued after the barrier, behind the next stage's
+//   first reads.  BF16: v_mfma_f32_32x32x16_bf16.  MXFP8/MXFP4:
 //   v_mfma_scale_f32_32x32x64_f8f6f4.  NVFP4: gfx950's scaled MFMA takes only
-//   E8M0 per 32, so the loader decodes E2M1 x E4M3 exactly into fp16 (a product
-//   of 2- and 4-bit significands with magnitude in [2^-10, 2688]) while filling
-//   LDS, the math is v_mfma_f32_32x32x16_f16, and tA*tB is applied in the
-//   epilogue.
-// * Epilogue.  alpha * acc -> bf16 (round to nearest even) -> global, fused in
-//   the same kernel.
+//   E8M0 per 32, so its loader stages through VGPRs and decodes E2M1 x E4M3
+//   exactly into fp16 (a product of 2- and 4-bit significands with magnitude
+//   in [2^-10, 2688]) on the way into LDS; the math is
+//   v_mfma_f32_32x32x16_f16 and tA*tB is applied in the epilogue.
+// * Epilogue.  alpha * acc -> bf16 (round to nearest even) -> global with
+//   buffer stores (out-of-range rows and columns dropped), in the same kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -51,13 +58,15 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kThreads = 256;                  // 4 waves of 64
 constexpr int kRowBytes = 128;                 // bytes of one tile row per stage
 constexpr int kTileBytes = kTileM * kRowBytes; // 32 KiB per operand per stage
-constexpr int kStageBytes = 2 * kTileBytes;    // A + B
-constexpr int kStages = 2;
 constexpr uint32_t kOOB = 0x80000000u;         // beyond every num_records we set
+
+#define DBS_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // Buffer resource over [base, base + bytes): loads at offsets >= bytes return
 // zero, stores there are dropped.  Word 3 = 0x00020000 is the gfx9-family
@@ -67,14 +76,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// LDS byte offset of 16-byte chunk `chunk` (0..7) of tile row `row`.  The XOR
-// pattern gives 8 (and 16) consecutive rows reading the same logical chunk
-// distinct bank groups.
-__device__ __forceinline__ int lds_off(int row, int chunk)
-{
-    const int swz = (row ^ (row >> 3)) & 7;
-    return row * kRowBytes + ((chunk ^ swz) << 4);
-}
+// XOR swizzle of the 8 16-byte chunks of a tile row: 8 (and 16) consecutive
+// rows reading the same logical chunk hit distinct bank groups.
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kRowBytes + ((chunk ^ swz(row)) << 4); }
 
 // Output tile of linear id `tile`: groups of `group_m` tile rows, column-major
 // inside a group.
@@ -89,61 +95,256 @@ __device__ __forceinline__ void tile_coords(int tile, const Params &p, int &tm, 
     tn = idx / rows;
 }
 
-// ---------------------------------------------------------------- loaders
+// LDS map: A slot 0 | A slot 1 | B slot 0 | B slot 1, 32 KiB each, then for
+// the MX formats the scale slots SA 0 | SA 1 | SB 0 | SB 1 of 256 rows x BPS
+// bytes.  Slot 1 is reached through the 16-bit immediate offset of ds_read.
+constexpr int kLdsA = 0;
+constexpr int kLdsB = 2 * kTileBytes;
+constexpr int kSlotStride = kTileBytes;
+constexpr int kLdsS = 4 * kTileBytes;
 
-// 128-byte-row formats (bf16, E4M3, E2M1): thread t copies chunk t%8 of rows
-// t/8 + 32 i, i < 8, for A and for B.
-struct SlabRegs {
-    i32x4 a[8], b[8];
+// MX scale bytes per row per stage (2 blocks of 32 per 64-K k-step).
+template <int FMT>
+constexpr int scale_bps() { return FMT == kMXFP8 ? 4 : FMT == kMXFP4 ? 8 : 0; }
+template <int FMT>
+constexpr int lds_bytes() { return 4 * kTileBytes + 4 * kTileM * scale_bps<FMT>(); }
+
+// Per-lane constants of one workgroup.  w, wm, wn are wave-uniform.
+struct Ctx {
+    int t, lane, h, lr;
+    int w, wm, wn;
+    uint32_t fa[4], fb[4];   // LDS address of fragment reads at k-step 0, slot 0
+    uint32_t sa[4], sb[4];   // LDS address of the lane's MX scale byte, k-step 0, slot 0
+    uint32_t voff[8];        // direct-to-LDS source offsets at stage 0
 };
 
-__device__ __forceinline__ void load_slab(SlabRegs &r, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                          int lda, int s, int t)
+// ------------------------------------------------------------ format traits
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<kBF16> {
+    static constexpr int KK = 4;           // MFMA k-steps per stage (16 K each)
+    using Frag = bf16x8;
+};
+template <>
+struct Fmt<kNVFP4> {
+    static constexpr int KK = 4;           // fp16 in LDS, same geometry as bf16
+    using Frag = f16x8;
+};
+template <>
+struct Fmt<kMXFP8> {
+    static constexpr int KK = 2;           // 64 K per k-step, 32 bytes per lane
+    using Frag = i32x8;
+};
+template <>
+struct Fmt<kMXFP4> {
+    static constexpr int KK = 4;           // 64 K per k-step, 16 bytes per lane
+    using Frag = i32x4;
+};
+
+template <int FMT>
+struct Frags {
+    typename Fmt<FMT>::Frag a[4], b[4];
+    uint32_t sa[4], sb[4];   // MX: E8M0 byte of each row block for this k-step
+};
+
+template <typename V>
+__device__ __forceinline__ V lds_read(const uint8_t *lds, uint32_t addr)
 {
-    const int kb = s * kRowBytes + (t & 7) * 16;
-    const bool ok = kb < lda;
+    return *reinterpret_cast<const V *>(lds + addr);
+}
+
+// Fragment reads for k-step kk from ring slot `slot`.  16-bit formats: lane l
+// holds the 8 elements of chunk 2 kk + l/32 of its row.  E2M1: 32 elements,
+// chunk 2 kk + l/32.  E4M3: in the 32x32x64 scaled MFMA with 8-bit elements,
+// lane half h holds K positions [16h, 16h+16) in bytes 0..15 and
+// [32+16h, 48+16h) in bytes 16..31, and its scale applies to K block h, i.e.
+// bytes 16h..16h+15 of both halves (established with a one-instruction
+// probe); so lane half h reads chunks 4 kk + h and 4 kk + 2 + h.  With the
+// XOR swizzle, chunk 2 kk + h of a row sits at fa ^ (kk << 5) and chunk
+// 4 kk + h at fa ^ (kk << 6).  MX scales: lane l of a 32x32x64 scaled MFMA
+// supplies the E8M0 scale of K block l/32 of row l%32 in bits [7:0]; for
+// k-step kk that is byte 2 kk + l/32 of the row's stage scales.
+template <int FMT>
+__device__ __forceinline__ void read_one(typename Fmt<FMT>::Frag &v, uint32_t &sc, const uint8_t *lds, uint32_t fbase,
+                                         uint32_t sbase, int slot, int kk)
+{
+    const uint32_t so = (uint32_t)(slot * kSlotStride);
+    if constexpr (FMT == kMXFP8) {
+        const uint32_t x = (fbase ^ (uint32_t)(kk << 6)) + so;
+        const i32x4 v0 = lds_read<i32x4>(lds, x), v1 = lds_read<i32x4>(lds, x ^ 32u);
+        v = i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    } else {
+        v = lds_read<typename Fmt<FMT>::Frag>(lds, (fbase ^ (uint32_t)(kk << 5)) + so);
+    }
+    if constexpr (FMT == kMXFP8 || FMT == kMXFP4)
+        sc = lds[sbase + (uint32_t)(slot * kTileM * scale_bps<FMT>() + 2 * kk)];
+}
+
+template <int FMT>
+__device__ __forceinline__ void read_a(Frags<FMT> &f, int i, const uint8_t *lds, int slot, int kk, const Ctx &c)
+{
+    read_one<FMT>(f.a[i], f.sa[i], lds, c.fa[i], c.sa[i], slot, kk);
+}
+
+template <int FMT>
+__device__ __forceinline__ void read_b(Frags<FMT> &f, int j, const uint8_t *lds, int slot, int kk, const Ctx &c)
+{
+    read_one<FMT>(f.b[j], f.sb[j], lds, c.fb[j], c.sb[j], slot, kk);
+}
+
+template <int FMT>
+__device__ __forceinline__ void read_frags(Frags<FMT> &f, const uint8_t *lds, int slot, int kk, const Ctx &c)
+{
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = (t >> 3) + 32 * i;
-        const uint32_t off = ok ? (uint32_t)(row * lda + kb) : kOOB;
-        r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-        r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+        read_a(f, i, lds, slot, kk, c);
+        read_b(f, i, lds, slot, kk, c);
     }
 }
 
-__device__ __forceinline__ void store_slab(const SlabRegs &r, uint8_t *stage, int t)
+// ------------------------------------------------------------------ scales
+
+// MX scales of stage s for the workgroup's 256 A rows and 256 B rows go to
+// the scale slot SLOT as 256 rows x BPS bytes per operand.
+//
+// Rows whose stage scales are whole dwords (row stride K/32 a multiple of 4):
+// direct-to-LDS dword loads.  A dword wave-load writes 64 lanes x 4 bytes, so
+// for E4M3 (BPS = 4) lane i of wave w carries row 64w + i, and for E2M1
+// (BPS = 8) wave-load j carries rows 64w + 32j + i/2, dword i%2.  A dword
+// past the row's last block (partial last stage) reads zero.
+template <int FMT>
+__device__ __forceinline__ void dma_scales(uint8_t *lds, int slot, __amdgpu_buffer_rsrc_t rsa,
+                                           __amdgpu_buffer_rsrc_t rsb, const Ctx &c, int s, int sld)
 {
+    constexpr int BPS = scale_bps<FMT>();
+    constexpr int NW = BPS / 4;                      // wave-loads per wave per operand
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = (t >> 3) + 32 * i;
-        const int o = lds_off(row, t & 7);
-        *reinterpret_cast<i32x4 *>(stage + o) = r.a[i];
-        *reinterpret_cast<i32x4 *>(stage + kTileBytes + o) = r.b[i];
+    for (int j = 0; j < NW; ++j) {
+        const int row = c.w * 64 + (NW == 1 ? c.lane : j * 32 + (c.lane >> 1));
+        const int word = NW == 1 ? 0 : (c.lane & 1);
+        const int o = s * BPS + 4 * word;
+        const uint32_t off = o < sld ? (uint32_t)(row * sld + o) : kOOB;
+        const int dst = slot * kTileM * BPS + (c.w * NW + j) * 256;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void *)(lds + kLdsS + dst), 4, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(lds + kLdsS + 2 * kTileM * BPS + dst), 4, off,
+                                                 0, 0, 0);
     }
 }
 
-// NVFP4: a stage covers 64 K elements = 32 packed bytes per row.  Thread t
-// copies half t%2 (32 elements) of rows t/2 and t/2 + 128 of A and of B, with
-// the two E4M3 scales of those 32 elements, and expands them to 64 bytes of
-// fp16 (4 LDS chunks).
+// Any other row stride: thread t fetches the BPS bytes of A row t and B row
+// t one by one (bytes past the row's last block read zero) and writes them
+// to LDS before the stage's barrier.
+template <int FMT>
+struct ScaleBytes {
+    uint32_t a[scale_bps<FMT>() > 0 ? scale_bps<FMT>() : 1], b[scale_bps<FMT>() > 0 ? scale_bps<FMT>() : 1];
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_scale_bytes(ScaleBytes<FMT> &r, __amdgpu_buffer_rsrc_t rsa,
+                                                 __amdgpu_buffer_rsrc_t rsb, int t, int s, int sld)
+{
+    constexpr int BPS = scale_bps<FMT>();
+#pragma unroll
+    for (int b = 0; b < BPS; ++b) {
+        const int o = s * BPS + b;
+        const uint32_t off = o < sld ? (uint32_t)(t * sld + o) : kOOB;
+        r.a[b] = __builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0);
+        r.b[b] = __builtin_amdgcn_raw_buffer_load_b8(rsb, off, 0, 0);
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void store_scale_bytes(const ScaleBytes<FMT> &r, uint8_t *lds, int slot, int t)
+{
+    constexpr int BPS = scale_bps<FMT>();
+    uint8_t *sa = lds + kLdsS + slot * kTileM * BPS + t * BPS;
+#pragma unroll
+    for (int b = 0; b < BPS; ++b) {
+        sa[b] = (uint8_t)r.a[b];
+        sa[2 * kTileM * BPS + b] = (uint8_t)r.b[b];
+    }
+}
+
+// ------------------------------------------------------------------- math
+
+// One 32x32 block: acc[i][j] += A block i x B block j for one k-step.  The
+// MFMA's first operand is the B fragment, so each lane ends up holding 4
+// consecutive output columns.
+template <int FMT>
+__device__ __forceinline__ void mma1(f32x16 &acc, const Frags<FMT> &f, int i, int j)
+{
+    if constexpr (FMT == kBF16) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc, 0, 0, 0);
+    } else if constexpr (FMT == kNVFP4) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc, 0, 0, 0);
+    } else if constexpr (FMT == kMXFP8) {
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc, 0, 0, 0, (int)f.sb[j], 0,
+                                                              (int)f.sa[i]);
+    } else {
+        const i32x8 bb = {f.b[j][0], f.b[j][1], f.b[j][2], f.b[j][3], 0, 0, 0, 0};
+        const i32x8 aa = {f.a[i][0], f.a[i][1], f.a[i][2], f.a[i][3], 0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bb, aa, acc, 4, 4, 0, (int)f.sb[j], 0, (int)f.sa[i]);
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void mma(f32x16 (&acc)[4][4], const Frags<FMT> &f)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mma1(acc[i][j], f, i, j);
+}
+
+// ------------------------------------------------------ direct-to-LDS loads
+
+// One wave-load pair (A and B) of stage s into ring slot SLOT.  Wave w issues
+// the 8 wave-loads q of rows 64w .. 64w+63 of each operand; a wave-load
+// writes 64 lanes x 16 bytes to consecutive LDS bytes, i.e. 8 rows x 8
+// chunks, so lane i lands on row 64w + 8q + i/8, physical chunk i%8, and
+// fetches the logical chunk the swizzle places there (c.voff[q] at stage 0).
+// On the last, partial stage, chunks past the row end read zeros.
+__device__ __forceinline__ void dma_pair(uint8_t *lds, int slot, __amdgpu_buffer_rsrc_t ra,
+                                         __amdgpu_buffer_rsrc_t rb, const Ctx &c, int q, int s, bool tail, int lda)
+{
+    const uint32_t k0 = (uint32_t)(s * kRowBytes);
+    uint32_t off = c.voff[q] + k0;
+    if (tail) {
+        const int row = c.w * 64 + q * 8 + (c.lane >> 3);
+        const int lc = (c.lane & 7) ^ swz(row);
+        if ((int)k0 + lc * 16 >= lda) off = kOOB;
+    }
+    const int dst = slot * kSlotStride + (c.w * 8 + q) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(lds + kLdsA + dst), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(lds + kLdsB + dst), 16, off, 0, 0, 0);
+}
+
+// ---------------------------------------------------------- NVFP4 staging
+
+// A stage covers 64 K elements = 32 packed bytes per row.  Thread t loads
+// half t%2 (32 elements) of rows t/2 and t/2 + 128 of A and of B, with the
+// two E4M3 scales of those 32 elements, and expands them to 64 bytes of fp16
+// (4 LDS chunks).
 struct Fp4Regs {
     i32x4 a[2], b[2];
     uint32_t sa[2], sb[2];
 };
 
 __device__ __forceinline__ void load_fp4(Fp4Regs &r, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                         __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb,
-                                         int lda, int sld, int s, int t)
+                                         __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb, int lda, int sld,
+                                         int s, int t)
 {
     const int half = t & 1;
     const int kb = s * 32 + half * 16;         // packed byte within the row
     const int sb = s * 4 + half * 2;           // first of the two scale bytes
-    const bool ok = kb < lda;
+    const uint32_t pad = kb < lda ? 0u : kOOB; // K%32 == 0: a chunk is all in or all out
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int row = (t >> 1) + 128 * i;
-        const uint32_t off = ok ? (uint32_t)(row * lda + kb) : kOOB;
-        const uint32_t soff = ok ? (uint32_t)(row * sld + sb) : kOOB;
+        const uint32_t off = (uint32_t)(row * lda + kb) | pad;
+        const uint32_t soff = (uint32_t)(row * sld + sb) | pad;
         r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
         r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
         r.sa[i] = __builtin_amdgcn_raw_buffer_load_b16(rsa, soff, 0, 0);
@@ -159,19 +360,20 @@ __device__ __forceinline__ f16x2 e4m3_pair(uint32_t byte)
 }
 
 // 8 E2M1 codes (one dword) times one scale -> 8 fp16 (one 16-byte chunk).
-// The conversion runs with unit scale, so it is exact; the product by the
-// E4M3 scale is exact in fp16 as well.
+// The conversion instruction uses only the exponent of its scale operand, so
+// it runs with unit scale (exact) and the E4M3 scale is applied by an fp16
+// multiply, also exact.  Low nibble first.
 __device__ __forceinline__ i32x4 expand8(uint32_t codes, f16x2 s)
 {
     const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s;
     const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s;
     const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s;
     const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s;
-    return i32x4{__builtin_bit_cast(int, p0), __builtin_bit_cast(int, p1),
-                 __builtin_bit_cast(int, p2), __builtin_bit_cast(int, p3)};
+    return i32x4{__builtin_bit_cast(int, p0), __builtin_bit_cast(int, p1), __builtin_bit_cast(int, p2),
+                 __builtin_bit_cast(int, p3)};
 }
 
-__device__ __forceinline__ void store_fp4(const Fp4Regs &r, uint8_t *stage, int t)
+__device__ __forceinline__ void store_fp4(const Fp4Regs &r, uint8_t *lds, int slot, int t)
 {
     const int half = t & 1;
 #pragma unroll
@@ -181,257 +383,277 @@ __device__ __forceinline__ void store_fp4(const Fp4Regs &r, uint8_t *stage, int 
         const f16x2 blo = e4m3_pair(r.sb[i] & 0xFF), bhi = e4m3_pair((r.sb[i] >> 8) & 0xFF);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const int o = lds_off(row, half * 4 + d);
-            *reinterpret_cast<i32x4 *>(stage + o) = expand8((uint32_t)r.a[i][d], d < 2 ? alo : ahi);
-            *reinterpret_cast<i32x4 *>(stage + kTileBytes + o) = expand8((uint32_t)r.b[i][d], d < 2 ? blo : bhi);
+            const int o = slot * kSlotStride + lds_off(row, half * 4 + d);
+            *reinterpret_cast<i32x4 *>(lds + kLdsA + o) = expand8((uint32_t)r.a[i][d], d < 2 ? alo : ahi);
+            *reinterpret_cast<i32x4 *>(lds + kLdsB + o) = expand8((uint32_t)r.b[i][d], d < 2 ? blo : bhi);
         }
     }
 }
 
-// MX scales for one stage, per lane: the E8M0 byte of each of the wave's 4 A
-// (and B) row blocks for each MFMA k-step.  Lane l of a 32x32x64 scaled MFMA
-// supplies the scale of K block l/32 of row l%32 (for E2M1 those are exactly
-// the 32 elements the lane holds; for E4M3 see math_fp8).
-template <int KSTEPS>
-struct MxScales {
-    int a[4][KSTEPS], b[4][KSTEPS];
-};
-
-template <int KSTEPS>
-__device__ __forceinline__ void load_mx_scales(MxScales<KSTEPS> &sc, __amdgpu_buffer_rsrc_t rsa,
-                                               __amdgpu_buffer_rsrc_t rsb, int sld, int s, int wm, int wn,
-                                               int lr, int h)
-{
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-        const int blk = s * (2 * KSTEPS) + kk * 2 + h;
-        const bool ok = blk < sld;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ra = wm * 128 + i * 32 + lr, rb = wn * 128 + i * 32 + lr;
-            sc.a[i][kk] = __builtin_amdgcn_raw_buffer_load_b8(rsa, ok ? (uint32_t)(ra * sld + blk) : kOOB, 0, 0);
-            sc.b[i][kk] = __builtin_amdgcn_raw_buffer_load_b8(rsb, ok ? (uint32_t)(rb * sld + blk) : kOOB, 0, 0);
-        }
-    }
-}
-
-// ----------------------------------------------------------------- math
-
-// 16-bit formats: 4 k-steps of 16 per stage; lane l reads the 8 elements of
-// chunk (2 kk + l/32) of its row.  The MFMA's first operand is the B
-// fragment, so each lane ends up holding 4 consecutive output columns.
-template <typename V, bool F16>
-__device__ __forceinline__ void math_16bit(f32x16 (&acc)[4][4], const uint8_t *stage, int wm, int wn, int lr, int h)
-{
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        V a[4], b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            a[i] = *reinterpret_cast<const V *>(stage + lds_off(wm * 128 + i * 32 + lr, kk * 2 + h));
-            b[i] = *reinterpret_cast<const V *>(stage + kTileBytes + lds_off(wn * 128 + i * 32 + lr, kk * 2 + h));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (F16)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j], a[i], acc[i][j], 0, 0, 0);
-                else
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-            }
-    }
-}
-
-// E4M3: 2 k-steps of 64 per stage.  In the 32x32x64 scaled MFMA with 8-bit
-// elements, lane half h holds K positions [16h, 16h+16) in bytes 0..15 and
-// [32+16h, 32+16h+16) in bytes 16..31, and its scale applies to K block h,
-// i.e. bytes 16h..16h+15 of both halves (established with a one-instruction
-// probe).  So lane half h reads chunks 4 kk + h and 4 kk + 2 + h and supplies
-// the scale of block 2 kk + h.
-__device__ __forceinline__ void math_fp8(f32x16 (&acc)[4][4], const uint8_t *stage, const MxScales<2> &sc,
-                                         int wm, int wn, int lr, int h)
-{
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        i32x8 a[4], b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ra = wm * 128 + i * 32 + lr, rb = wn * 128 + i * 32 + lr;
-            const i32x4 a0 = *reinterpret_cast<const i32x4 *>(stage + lds_off(ra, kk * 4 + h));
-            const i32x4 a1 = *reinterpret_cast<const i32x4 *>(stage + lds_off(ra, kk * 4 + 2 + h));
-            const i32x4 b0 = *reinterpret_cast<const i32x4 *>(stage + kTileBytes + lds_off(rb, kk * 4 + h));
-            const i32x4 b1 = *reinterpret_cast<const i32x4 *>(stage + kTileBytes + lds_off(rb, kk * 4 + 2 + h));
-            a[i] = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            b[i] = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    b[j], a[i], acc[i][j], 0, 0, 0, sc.b[j][kk], 0, sc.a[i][kk]);
-    }
-}
-
-// E2M1: 4 k-steps of 64 per stage, 16 bytes (32 elements) per lane in the
-// low half of the 8-dword operand.
-__device__ __forceinline__ void math_fp4(f32x16 (&acc)[4][4], const uint8_t *stage, const MxScales<4> &sc,
-                                         int wm, int wn, int lr, int h)
-{
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        i32x8 a[4], b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const i32x4 a0 = *reinterpret_cast<const i32x4 *>(stage + lds_off(wm * 128 + i * 32 + lr, kk * 2 + h));
-            const i32x4 b0 =
-                *reinterpret_cast<const i32x4 *>(stage + kTileBytes + lds_off(wn * 128 + i * 32 + lr, kk * 2 + h));
-            a[i] = i32x8{a0[0], a0[1], a0[2], a0[3], 0, 0, 0, 0};
-            b[i] = i32x8{b0[0], b0[1], b0[2], b0[3], 0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    b[j], a[i], acc[i][j], 4, 4, 0, sc.b[j][kk], 0, sc.a[i][kk]);
-    }
-}
-
-// ------------------------------------------------------------- epilogue
+// --------------------------------------------------------------- epilogue
 
 // acc[i][j] holds, for output row m = wm*128 + 32 i + lane%32, the columns
-// n = wn*128 + 32 j + 8 g + 4 (lane/32) + q in register 4 g + q.
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const Params &p, int m0, int n0, int wm,
-                                           int wn, int lr, int h)
+// n = wn*128 + 32 j + 8 g + 4 (lane/32) + q in register 4 g + q.  Each
+// 32-row block is stored through its own buffer resource, so rows past M
+// and columns past N are dropped by the hardware range check.
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const Params &p, int m0, int n0,
+                                           const Ctx &c)
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * 128 + i * 32 + lr;
-        if (m >= p.M) continue;
-        uint16_t *drow = p.D + (int64_t)m * p.N;
+        const int r0 = m0 + c.wm * 128 + i * 32;
+        const int rows = max(0, min(32, p.M - r0));
+        const __amdgpu_buffer_rsrc_t rd =
+            make_rsrc(p.D + (int64_t)r0 * p.N, (uint32_t)rows * (uint32_t)p.N * 2u);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * 128 + j * 32 + g * 8 + h * 4;
-                uint16_t v[4];
+                const int n = n0 + c.wn * 128 + j * 32 + g * 8 + c.h * 4;
+                uint32_t v[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     v[q] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][4 * g + q] * p.alpha));
+                const uint32_t base = (uint32_t)(c.lr * p.N + n) * 2u;
                 if (p.vec_store) {
-                    if (n < p.N) {
-                        const uint2 pk = {(uint32_t)v[0] | ((uint32_t)v[1] << 16),
-                                          (uint32_t)v[2] | ((uint32_t)v[3] << 16)};
-                        *reinterpret_cast<uint2 *>(drow + n) = pk;
-                    }
+                    // N % 4 == 0 and n % 4 == 0: the 4 columns are all in or all out
+                    const uint32_t off = n < p.N ? base : kOOB;
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)}, rd, off,
+                                                          0, 0);
                 } else {
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        if (n + q < p.N) drow[n + q] = v[q];
+                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v[q], rd, n + q < p.N ? base + 2 * q : kOOB,
+                                                              0, 0);
                 }
             }
         }
     }
 }
 
-// ---------------------------------------------------------------- kernel
+// ------------------------------------------------------------------ kernel
 
+// Tile-invariant state threaded through the stage function.
 template <int FMT>
+struct Pipe {
+    __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+    Frags<FMT> F0, F1;                       // k-step fragments, double-buffered
+    Fp4Regs fp4;
+    ScaleBytes<FMT> sbytes;
+    bool tail;                               // the last stage is partial in K
+};
+
+// Stage s of A and B (and the MX scales) into ring slot SLOT.  Issued as
+// eight pieces so the caller can interleave them with MFMAs.
+template <int FMT, bool ALIGNED>
+__device__ __forceinline__ void load_piece(Pipe<FMT> &P, uint8_t *lds, int slot, const Params &p, const Ctx &c, int q,
+                                           int s, bool tail)
+{
+    if constexpr (FMT == kNVFP4) {
+        if (q == 0) load_fp4(P.fp4, P.ra, P.rb, P.rsa, P.rsb, p.lda, p.sld, s, c.t);
+    } else {
+        dma_pair(lds, slot, P.ra, P.rb, c, q, s, tail, p.lda);
+        if constexpr (FMT == kMXFP8 || FMT == kMXFP4) {
+            if (q == 7) {
+                if constexpr (ALIGNED)
+                    dma_scales<FMT>(lds, slot, P.rsa, P.rsb, c, s, p.sld);
+                else
+                    load_scale_bytes(P.sbytes, P.rsa, P.rsb, c.t, s, p.sld);
+            }
+        }
+    }
+}
+
+// Register-staged parts of stage s (NVFP4 data, unaligned MX scales) go to
+// LDS before the stage's barrier.
+template <int FMT, bool ALIGNED>
+__device__ __forceinline__ void commit_stage(Pipe<FMT> &P, uint8_t *lds, int slot, const Ctx &c)
+{
+    if constexpr (FMT == kNVFP4) store_fp4(P.fp4, lds, slot, c.t);
+    if constexpr ((FMT == kMXFP8 || FMT == kMXFP4) && !ALIGNED) store_scale_bytes<FMT>(P.sbytes, lds, slot, c.t);
+}
+
+// Fragments are 8 VGPRs for E4M3 (two sets do not fit beside the 256
+// accumulators), 4 for the other formats.
+template <int FMT>
+constexpr bool rolling() { return FMT == kMXFP8; }
+
+// One phase: the 16 MFMAs of fragment set `cur` while set `nxt` is read
+// (k-step rkk of slot rslot, if rd) and, if ld, stage ls of the operands is
+// loaded into slot lslot in eight pieces between MFMA pairs.  Without
+// rolling, `nxt` is read before the MFMAs.  With rolling, the MFMAs go in
+// 2x2 groups and each next fragment is read as soon as the register it
+// replaces is dead: A0/A1 after the second group, B0/B1 after the third,
+// the rest after the fourth; every fragment is read at least four MFMAs
+// before its first use in the next phase.
+template <int FMT, bool ALIGNED>
+__device__ __forceinline__ void phase(f32x16 (&acc)[4][4], Pipe<FMT> &P, const Frags<FMT> &cur, Frags<FMT> &nxt,
+                                      uint8_t *lds, const Params &p, const Ctx &c, bool rd, int rslot, int rkk,
+                                      bool ld, int lslot, int ls, bool tail)
+{
+    if constexpr (!rolling<FMT>()) {
+        if (rd) read_frags(nxt, lds, rslot, rkk, c);
+        DBS_FENCE();
+    }
+    constexpr int gi[4] = {0, 0, 2, 2}, gj[4] = {0, 2, 0, 2};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = gi[g] + (u >> 1), j = gj[g] + (u & 1);
+            mma1(acc[i][j], cur, i, j);
+            if (u & 1) {
+                DBS_FENCE();
+                if (ld) load_piece<FMT, ALIGNED>(P, lds, lslot, p, c, 2 * g + (u >> 1), ls, tail);
+                DBS_FENCE();
+            }
+        }
+        if constexpr (rolling<FMT>()) {
+            if (rd) {
+                if (g == 1) { read_a(nxt, 0, lds, rslot, rkk, c); read_a(nxt, 1, lds, rslot, rkk, c); }
+                if (g == 2) { read_b(nxt, 0, lds, rslot, rkk, c); read_b(nxt, 1, lds, rslot, rkk, c); }
+                if (g == 3) {
+                    read_a(nxt, 2, lds, rslot, rkk, c); read_a(nxt, 3, lds, rslot, rkk, c);
+                    read_b(nxt, 2, lds, rslot, rkk, c); read_b(nxt, 3, lds, rslot, rkk, c);
+                }
+            }
+            DBS_FENCE();
+        }
+    }
+}
+
+// Stage s, read from ring slot `slot` (= s & 1), while stage s+1 is loaded
+// into the other slot.  On entry F1 holds the last k-step of stage s-1
+// (zeros for s = 0): its MFMAs form the first phase, interleaved with the
+// loads of stage s+1 and with the reads of k-step 0 of stage s.  Called with
+// a constant slot the slot offsets fold into immediates.
+template <int FMT, bool ALIGNED>
+__device__ __forceinline__ void stage(Pipe<FMT> &P, f32x16 (&acc)[4][4], uint8_t *lds, int slot, const Params &p,
+                                      const Ctx &c, int s)
+{
+    constexpr int KK = Fmt<FMT>::KK;
+    const int nxt = slot ^ 1;
+    const bool more = s + 1 < p.nk;
+    const bool tail = P.tail && s + 2 == p.nk;
+    phase<FMT, ALIGNED>(acc, P, P.F1, P.F0, lds, p, c, true, slot, 0, more, nxt, s + 1, tail);
+#pragma unroll
+    for (int kk = 0; kk < KK - 1; ++kk) {
+        if (kk & 1)
+            phase<FMT, ALIGNED>(acc, P, P.F1, P.F0, lds, p, c, true, slot, kk + 1, false, 0, 0, false);
+        else
+            phase<FMT, ALIGNED>(acc, P, P.F0, P.F1, lds, p, c, true, slot, kk + 1, false, 0, 0, false);
+    }
+    if (more) commit_stage<FMT, ALIGNED>(P, lds, nxt, c);
+    __syncthreads();
+}
+
+template <int FMT, bool ALIGNED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<FMT>()];
+    constexpr int BPS = scale_bps<FMT>();
 
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int h = lane >> 5, lr = lane & 31;
-    const int wm = w >> 1, wn = w & 1;
+    Ctx c;
+    c.t = threadIdx.x;
+    c.lane = c.t & 63;
+    c.h = c.lane >> 5;
+    c.lr = c.lane & 31;
+    c.w = __builtin_amdgcn_readfirstlane(c.t >> 6);
+    c.wm = c.w >> 1;
+    c.wn = c.w & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ra = c.wm * 128 + i * 32 + c.lr, rb = c.wn * 128 + i * 32 + c.lr;
+        c.fa[i] = (uint32_t)(kLdsA + ra * kRowBytes + ((c.h ^ swz(ra)) << 4));
+        c.fb[i] = (uint32_t)(kLdsB + rb * kRowBytes + ((c.h ^ swz(rb)) << 4));
+        c.sa[i] = (uint32_t)(kLdsS + ra * BPS + c.h);
+        c.sb[i] = (uint32_t)(kLdsS + 2 * kTileM * BPS + rb * BPS + c.h);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int row = c.w * 64 + q * 8 + (c.lane >> 3);
+        c.voff[q] = (uint32_t)(row * p.lda + (((c.lane & 7) ^ swz(row)) << 4));
+    }
+
     const int ntiles = p.tiles_m * p.tiles_n;
     const int nwg = gridDim.x, wg = blockIdx.x;
     // hardware places workgroup wg on XCD wg % 8: give each XCD a contiguous
     // range of logical ids
     const int lid = (nwg & 7) == 0 ? (wg & 7) * (nwg >> 3) + (wg >> 3) : wg;
 
+    Pipe<FMT> P;
+    P.tail = (p.lda % kRowBytes) != 0;
+
     for (int tile = lid; tile < ntiles; tile += nwg) {
         int tm, tn;
         tile_coords(tile, p, tm, tn);
         const int m0 = tm * kTileM, n0 = tn * kTileN;
         const int rows_a = min(p.M - m0, kTileM), rows_b = min(p.N - n0, kTileN);
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)n0 * p.lda, (uint32_t)(rows_b * p.lda));
+        P.ra = make_rsrc(p.A + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
+        P.rb = make_rsrc(p.B + (int64_t)n0 * p.lda, (uint32_t)(rows_b * p.lda));
+        P.rsa = P.ra;
+        P.rsb = P.rb;
+        if constexpr (FMT != kBF16) {
+            P.rsa = make_rsrc(p.sA + (int64_t)m0 * p.sld, (uint32_t)(rows_a * p.sld));
+            P.rsb = make_rsrc(p.sB + (int64_t)n0 * p.sld, (uint32_t)(rows_b * p.sld));
+        }
 
         f32x16 acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+        // the "previous stage" of stage 0 contributes nothing
+        P.F1 = Frags<FMT>{};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) P.F1.sa[i] = P.F1.sb[i] = 127u;
 
-        if constexpr (FMT == kBF16 || FMT == kMXFP8 || FMT == kMXFP4) {
-            constexpr int KS = FMT == kMXFP8 ? 2 : 4;
-            __amdgpu_buffer_rsrc_t rsa = ra, rsb = rb;
-            if constexpr (FMT != kBF16) {
-                rsa = make_rsrc(p.sA + (int64_t)m0 * p.sld, (uint32_t)(rows_a * p.sld));
-                rsb = make_rsrc(p.sB + (int64_t)n0 * p.sld, (uint32_t)(rows_b * p.sld));
+        // prologue: stage 0 into slot 0
+#pragma unroll
+        for (int q = 0; q < 8; ++q) load_piece<FMT, ALIGNED>(P, lds, 0, p, c, q, 0, P.tail && p.nk == 1);
+        commit_stage<FMT, ALIGNED>(P, lds, 0, c);
+        __syncthreads();
+
+        if constexpr (FMT == kBF16 || FMT == kNVFP4) {
+            // unrolled by two: slot offsets become immediates
+            int s = 0;
+            for (; s + 1 < p.nk; s += 2) {
+                stage<FMT, ALIGNED>(P, acc, lds, 0, p, c, s);
+                stage<FMT, ALIGNED>(P, acc, lds, 1, p, c, s + 1);
             }
-            SlabRegs regs;
-            MxScales<KS> sc_cur, sc_next;
-            load_slab(regs, ra, rb, p.lda, 0, t);
-            if constexpr (FMT != kBF16) load_mx_scales<KS>(sc_cur, rsa, rsb, p.sld, 0, wm, wn, lr, h);
-            store_slab(regs, lds, t);
-            __syncthreads();
-            for (int s = 0; s < p.nk; ++s) {
-                const uint8_t *stage = lds + (s & 1) * kStageBytes;
-                const bool more = s + 1 < p.nk;
-                if (more) {
-                    load_slab(regs, ra, rb, p.lda, s + 1, t);
-                    if constexpr (FMT != kBF16) load_mx_scales<KS>(sc_next, rsa, rsb, p.sld, s + 1, wm, wn, lr, h);
-                }
-                if constexpr (FMT == kBF16)
-                    math_16bit<bf16x8, false>(acc, stage, wm, wn, lr, h);
-                else if constexpr (FMT == kMXFP8)
-                    math_fp8(acc, stage, sc_cur, wm, wn, lr, h);
-                else
-                    math_fp4(acc, stage, sc_cur, wm, wn, lr, h);
-                if (more) {
-                    store_slab(regs, lds + ((s + 1) & 1) * kStageBytes, t);
-                    if constexpr (FMT != kBF16) sc_cur = sc_next;
-                }
-                __syncthreads();
-            }
-        } else {  // NVFP4
-            const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.sA + (int64_t)m0 * p.sld, (uint32_t)(rows_a * p.sld));
-            const __amdgpu_buffer_rsrc_t rsb = make_rsrc(p.sB + (int64_t)n0 * p.sld, (uint32_t)(rows_b * p.sld));
-            Fp4Regs regs;
-            load_fp4(regs, ra, rb, rsa, rsb, p.lda, p.sld, 0, t);
-            store_fp4(regs, lds, t);
-            __syncthreads();
-            for (int s = 0; s < p.nk; ++s) {
-                const uint8_t *stage = lds + (s & 1) * kStageBytes;
-                const bool more = s + 1 < p.nk;
-                if (more) load_fp4(regs, ra, rb, rsa, rsb, p.lda, p.sld, s + 1, t);
-                math_16bit<f16x8, true>(acc, stage, wm, wn, lr, h);
-                if (more) store_fp4(regs, lds + ((s + 1) & 1) * kStageBytes, t);
-                __syncthreads();
-            }
+            if (s < p.nk) stage<FMT, ALIGNED>(P, acc, lds, 0, p, c, s);
+        } else {
+            // the scaled-MFMA body does not fit the register file twice
+            for (int s = 0; s < p.nk; ++s) stage<FMT, ALIGNED>(P, acc, lds, s & 1, p, c, s);
         }
+        phase<FMT, ALIGNED>(acc, P, P.F1, P.F0, lds, p, c, false, 0, 0, false, 0, 0, false);
 
-        store_tile(acc, p, m0, n0, wm, wn, lr, h);
+        store_tile(acc, p, m0, n0, c);
     }
+}
+
+template <int FMT>
+hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
+{
+    const dim3 g(grid), b(kThreads);
+    if (FMT == kBF16 || FMT == kNVFP4 || p.scales_aligned)
+        hipLaunchKernelGGL((gemm_kernel<FMT, true>), g, b, 0, stream, p);
+    else
+        hipLaunchKernelGGL((gemm_kernel<FMT, false>), g, b, 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int fmt, const Params &p, int grid, hipStream_t stream)
 {
-    const dim3 g(grid), b(kThreads);
     switch (fmt) {
-    case kBF16: hipLaunchKernelGGL(gemm_kernel<kBF16>, g, b, 0, stream, p); break;
-    case kMXFP8: hipLaunchKernelGGL(gemm_kernel<kMXFP8>, g, b, 0, stream, p); break;
-    case kMXFP4: hipLaunchKernelGGL(gemm_kernel<kMXFP4>, g, b, 0, stream, p); break;
-    case kNVFP4: hipLaunchKernelGGL(gemm_kernel<kNVFP4>, g, b, 0, stream, p); break;
+    case kBF16: return launch_fmt<kBF16>(p, grid, stream);
+    case kMXFP8: return launch_fmt<kMXFP8>(p, grid, stream);
+    case kMXFP4: return launch_fmt<kMXFP4>(p, grid, stream);
+    case kNVFP4: return launch_fmt<kNVFP4>(p, grid, stream);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace dbs

@@ -24,6 +24,7 @@ struct Params {
     int tiles_m, tiles_n;
     int group_m;          // tile rows per raster group
     int vec_store;        // 1 if D rows allow 8-byte stores (N % 4 == 0)
+    int scales_aligned;   // 1 if every scale row starts on a 4-byte boundary
     float alpha;          // applied to the fp32 accumulator before rounding
 };
 

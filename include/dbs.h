@@ -75,7 +75,7 @@ typedef enum {
 
 /*
  * BF16 GEMM.  A, B: bf16 (uint16 bit patterns).  K must be a multiple of 8
- * and at most 2^21.  M, N at most 2^30.
+ * and at most 2^21.  M and N at most 2^25 (for every entry point).
  */
 dbs_status gemm_bf16(const void *A, const void *B, void *D,
                      int64_t M, int64_t N, int64_t K,
