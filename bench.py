@@ -204,6 +204,8 @@ def main():
     ap.add_argument("--fmt", default="bf16", choices=["bf16", "mxfp8", "mxfp4", "nvfp4"])
     ap.add_argument("--only", action="store_true", help="time only --fmt (no per_format table)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run 5 device copies of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -220,6 +222,14 @@ def main():
     dbs.lib()
 
     fmt = args.fmt
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * 2 ** 20 // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w, D, avg, groups, tflops, gbs = measure(fmt, args.steps, args.warmup)
     M, N, K = w["M"], w["N"], w["K"]
     workload = f"{fmt}_gemm_{M}x{N}x{K}"

@@ -95,19 +95,30 @@ __device__ __forceinline__ void tile_coords(int tile, const Params &p, int &tm, 
     tn = idx / rows;
 }
 
-// LDS map: A slot 0 | A slot 1 | B slot 0 | B slot 1, 32 KiB each, then for
-// the MX formats the scale slots SA 0 | SA 1 | SB 0 | SB 1 of 256 rows x BPS
-// bytes.  Slot 1 is reached through the 16-bit immediate offset of ds_read.
+// LDS map: A slot 0 | A slot 1 | B slot 0 | B slot 1, 32 KiB each; 1 KiB
+// that L2-prefetch loads land in (never read); then for the MX formats the
+// scale slots SA 0 | SA 1 | SB 0 | SB 1 of 256 rows x BPS bytes.  (Planes of
+// 4-byte columns avoid the 2-way bank conflicts of the 8-byte E2M1 rows but
+// measured slower.)  Slot 1 of the operands is reached through the 16-bit
+// immediate offset of ds_read.
 constexpr int kLdsA = 0;
 constexpr int kLdsB = 2 * kTileBytes;
 constexpr int kSlotStride = kTileBytes;
-constexpr int kLdsS = 4 * kTileBytes;
+constexpr int kLdsJunk = 4 * kTileBytes;
+constexpr int kLdsS = kLdsJunk + 1024;
 
 // MX scale bytes per row per stage (2 blocks of 32 per 64-K k-step).
 template <int FMT>
 constexpr int scale_bps() { return FMT == kMXFP8 ? 4 : FMT == kMXFP4 ? 8 : 0; }
 template <int FMT>
-constexpr int lds_bytes() { return 4 * kTileBytes + 4 * kTileM * scale_bps<FMT>(); }
+constexpr int lds_bytes() { return kLdsS + 4 * kTileM * scale_bps<FMT>(); }
+
+// Stages ahead that an L2 prefetch touches: the direct-to-LDS load of stage
+// s+1 then mostly hits L2 instead of waiting on the Infinity Cache or HBM.
+#ifndef DBS_L2_PREFETCH
+#define DBS_L2_PREFETCH 0
+#endif
+constexpr int kPrefetch = DBS_L2_PREFETCH;   // 0: off
 
 // Per-lane constants of one workgroup.  w, wm, wn are wave-uniform.
 struct Ctx {
@@ -116,6 +127,16 @@ struct Ctx {
     uint32_t fa[4], fb[4];   // LDS address of fragment reads at k-step 0, slot 0
     uint32_t sa[4], sb[4];   // LDS address of the lane's MX scale byte, k-step 0, slot 0
     uint32_t voff[8];        // direct-to-LDS source offsets at stage 0
+    int kc[8];               // the K byte (within a stage) those loads fetch
+};
+
+// What a stage's loads fetch: stage `s` of the tile whose operand and scale
+// rows start at the four buffer resources.  inval = kOOB turns every load of
+// the target into a zero read (used when a workgroup has nothing left).
+struct Target {
+    __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+    int s;
+    uint32_t inval;
 };
 
 // ------------------------------------------------------------ format traits
@@ -206,8 +227,8 @@ __device__ __forceinline__ void read_frags(Frags<FMT> &f, const uint8_t *lds, in
 
 // ------------------------------------------------------------------ scales
 
-// MX scales of stage s for the workgroup's 256 A rows and 256 B rows go to
-// the scale slot SLOT as 256 rows x BPS bytes per operand.
+// MX scales of the target stage for the workgroup's 256 A rows and 256 B
+// rows go to scale slot `slot` as 256 rows x BPS bytes per operand.
 //
 // Rows whose stage scales are whole dwords (row stride K/32 a multiple of 4):
 // direct-to-LDS dword loads.  A dword wave-load writes 64 lanes x 4 bytes, so
@@ -215,8 +236,7 @@ __device__ __forceinline__ void read_frags(Frags<FMT> &f, const uint8_t *lds, in
 // (BPS = 8) wave-load j carries rows 64w + 32j + i/2, dword i%2.  A dword
 // past the row's last block (partial last stage) reads zero.
 template <int FMT>
-__device__ __forceinline__ void dma_scales(uint8_t *lds, int slot, __amdgpu_buffer_rsrc_t rsa,
-                                           __amdgpu_buffer_rsrc_t rsb, const Ctx &c, int s, int sld)
+__device__ __forceinline__ void dma_scales(uint8_t *lds, int slot, const Target &tg, const Ctx &c, int sld)
 {
     constexpr int BPS = scale_bps<FMT>();
     constexpr int NW = BPS / 4;                      // wave-loads per wave per operand
@@ -224,12 +244,12 @@ __device__ __forceinline__ void dma_scales(uint8_t *lds, int slot, __amdgpu_buff
     for (int j = 0; j < NW; ++j) {
         const int row = c.w * 64 + (NW == 1 ? c.lane : j * 32 + (c.lane >> 1));
         const int word = NW == 1 ? 0 : (c.lane & 1);
-        const int o = s * BPS + 4 * word;
-        const uint32_t off = o < sld ? (uint32_t)(row * sld + o) : kOOB;
+        const int o = tg.s * BPS + 4 * word;
+        const uint32_t off = ((uint32_t)(row * sld + o) | (o < sld ? 0u : kOOB)) | tg.inval;
         const int dst = slot * kTileM * BPS + (c.w * NW + j) * 256;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void *)(lds + kLdsS + dst), 4, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void *)(lds + kLdsS + 2 * kTileM * BPS + dst), 4, off,
-                                                 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(tg.rsa, (lds_void *)(lds + kLdsS + dst), 4, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(tg.rsb, (lds_void *)(lds + kLdsS + 2 * kTileM * BPS + dst), 4,
+                                                 off, 0, 0, 0);
     }
 }
 
@@ -242,16 +262,15 @@ struct ScaleBytes {
 };
 
 template <int FMT>
-__device__ __forceinline__ void load_scale_bytes(ScaleBytes<FMT> &r, __amdgpu_buffer_rsrc_t rsa,
-                                                 __amdgpu_buffer_rsrc_t rsb, int t, int s, int sld)
+__device__ __forceinline__ void load_scale_bytes(ScaleBytes<FMT> &r, const Target &tg, int t, int sld)
 {
     constexpr int BPS = scale_bps<FMT>();
 #pragma unroll
     for (int b = 0; b < BPS; ++b) {
-        const int o = s * BPS + b;
-        const uint32_t off = o < sld ? (uint32_t)(t * sld + o) : kOOB;
-        r.a[b] = __builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0);
-        r.b[b] = __builtin_amdgcn_raw_buffer_load_b8(rsb, off, 0, 0);
+        const int o = tg.s * BPS + b;
+        const uint32_t off = ((uint32_t)(t * sld + o) | (o < sld ? 0u : kOOB)) | tg.inval;
+        r.a[b] = __builtin_amdgcn_raw_buffer_load_b8(tg.rsa, off, 0, 0);
+        r.b[b] = __builtin_amdgcn_raw_buffer_load_b8(tg.rsb, off, 0, 0);
     }
 }
 
@@ -300,25 +319,20 @@ __device__ __forceinline__ void mma(f32x16 (&acc)[4][4], const Frags<FMT> &f)
 
 // ------------------------------------------------------ direct-to-LDS loads
 
-// One wave-load pair (A and B) of stage s into ring slot SLOT.  Wave w issues
-// the 8 wave-loads q of rows 64w .. 64w+63 of each operand; a wave-load
-// writes 64 lanes x 16 bytes to consecutive LDS bytes, i.e. 8 rows x 8
-// chunks, so lane i lands on row 64w + 8q + i/8, physical chunk i%8, and
-// fetches the logical chunk the swizzle places there (c.voff[q] at stage 0).
-// On the last, partial stage, chunks past the row end read zeros.
-__device__ __forceinline__ void dma_pair(uint8_t *lds, int slot, __amdgpu_buffer_rsrc_t ra,
-                                         __amdgpu_buffer_rsrc_t rb, const Ctx &c, int q, int s, bool tail, int lda)
+// One wave-load pair (A and B) of the target stage into ring slot `slot`.
+// Wave w issues the 8 wave-loads q of rows 64w .. 64w+63 of each operand; a
+// wave-load writes 64 lanes x 16 bytes to consecutive LDS bytes, i.e. 8 rows
+// x 8 chunks, so lane i lands on row 64w + 8q + i/8, physical chunk i%8, and
+// fetches the logical chunk the swizzle places there (c.voff[q] at stage 0,
+// K byte c.kc[q] within the stage).  Chunks past the row end (a partial
+// last stage) read zeros.
+__device__ __forceinline__ void dma_pair(uint8_t *lds, int slot, const Target &tg, const Ctx &c, int q, int lda)
 {
-    const uint32_t k0 = (uint32_t)(s * kRowBytes);
-    uint32_t off = c.voff[q] + k0;
-    if (tail) {
-        const int row = c.w * 64 + q * 8 + (c.lane >> 3);
-        const int lc = (c.lane & 7) ^ swz(row);
-        if ((int)k0 + lc * 16 >= lda) off = kOOB;
-    }
+    const int k0 = tg.s * kRowBytes;
+    const uint32_t off = ((c.voff[q] + (uint32_t)k0) | (k0 + c.kc[q] < lda ? 0u : kOOB)) | tg.inval;
     const int dst = slot * kSlotStride + (c.w * 8 + q) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(lds + kLdsA + dst), 16, off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(lds + kLdsB + dst), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tg.ra, (lds_void *)(lds + kLdsA + dst), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tg.rb, (lds_void *)(lds + kLdsB + dst), 16, off, 0, 0, 0);
 }
 
 // ---------------------------------------------------------- NVFP4 staging
@@ -332,23 +346,22 @@ struct Fp4Regs {
     uint32_t sa[2], sb[2];
 };
 
-__device__ __forceinline__ void load_fp4(Fp4Regs &r, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                         __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb, int lda, int sld,
-                                         int s, int t)
+__device__ __forceinline__ void load_fp4(Fp4Regs &r, const Target &tg, int lda, int sld, int t)
 {
     const int half = t & 1;
-    const int kb = s * 32 + half * 16;         // packed byte within the row
-    const int sb = s * 4 + half * 2;           // first of the two scale bytes
-    const uint32_t pad = kb < lda ? 0u : kOOB; // K%32 == 0: a chunk is all in or all out
+    const int kb = tg.s * 32 + half * 16;      // packed byte within the row
+    const int sb = tg.s * 4 + half * 2;        // first of the two scale bytes
+    // K%32 == 0: a chunk is all in or all out
+    const uint32_t pad = (kb < lda ? 0u : kOOB) | tg.inval;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int row = (t >> 1) + 128 * i;
         const uint32_t off = (uint32_t)(row * lda + kb) | pad;
         const uint32_t soff = (uint32_t)(row * sld + sb) | pad;
-        r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-        r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-        r.sa[i] = __builtin_amdgcn_raw_buffer_load_b16(rsa, soff, 0, 0);
-        r.sb[i] = __builtin_amdgcn_raw_buffer_load_b16(rsb, soff, 0, 0);
+        r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(tg.ra, off, 0, 0);
+        r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(tg.rb, off, 0, 0);
+        r.sa[i] = __builtin_amdgcn_raw_buffer_load_b16(tg.rsa, soff, 0, 0);
+        r.sb[i] = __builtin_amdgcn_raw_buffer_load_b16(tg.rsb, soff, 0, 0);
     }
 }
 
@@ -396,35 +409,38 @@ __device__ __forceinline__ void store_fp4(const Fp4Regs &r, uint8_t *lds, int sl
 // n = wn*128 + 32 j + 8 g + 4 (lane/32) + q in register 4 g + q.  Each
 // 32-row block is stored through its own buffer resource, so rows past M
 // and columns past N are dropped by the hardware range check.
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y)
+{
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+}
+
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const Params &p, int m0, int n0,
                                            const Ctx &c)
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r0 = m0 + c.wm * 128 + i * 32;
-        const int rows = max(0, min(32, p.M - r0));
-        const __amdgpu_buffer_rsrc_t rd =
-            make_rsrc(p.D + (int64_t)r0 * p.N, (uint32_t)rows * (uint32_t)p.N * 2u);
+        const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)max(0, min(32, p.M - r0)) * (uint32_t)p.N * 2u);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.D + (int64_t)r0 * p.N, bytes);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + c.wn * 128 + j * 32 + g * 8 + c.h * 4;
-                uint32_t v[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    v[q] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][4 * g + q] * p.alpha));
+                const f32x16 &a = acc[i][j];
+                const uint32_t lo = pack_bf16(a[4 * g] * p.alpha, a[4 * g + 1] * p.alpha);
+                const uint32_t hi = pack_bf16(a[4 * g + 2] * p.alpha, a[4 * g + 3] * p.alpha);
                 const uint32_t base = (uint32_t)(c.lr * p.N + n) * 2u;
                 if (p.vec_store) {
                     // N % 4 == 0 and n % 4 == 0: the 4 columns are all in or all out
-                    const uint32_t off = n < p.N ? base : kOOB;
-                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)}, rd, off,
-                                                          0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, rd, n < p.N ? base : kOOB, 0, 0);
                 } else {
+                    const uint16_t v[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v[q], rd, n + q < p.N ? base + 2 * q : kOOB,
-                                                              0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16(v[q], rd, n + q < p.N ? base + 2 * q : kOOB, 0, 0);
                 }
             }
         }
@@ -433,38 +449,60 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const Para
 
 // ------------------------------------------------------------------ kernel
 
-// Tile-invariant state threaded through the stage function.
+// L2 prefetch of stage pf.s of the current tile: one dword per thread of A
+// row t and of B row t, i.e. the first bytes of each row's stage slab (one
+// 128-byte line when the row stride is a multiple of 128).  The dwords land
+// in the junk LDS area and are never waited for or read.
+__device__ __forceinline__ void l2_prefetch(uint8_t *lds, const Target &pf, const Ctx &c, int lda)
+{
+    const int k0 = pf.s * kRowBytes;
+    const uint32_t off = ((uint32_t)(c.t * lda + k0) | (k0 < lda ? 0u : kOOB)) | pf.inval;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(pf.ra, (lds_void *)(lds + kLdsJunk + c.w * 256), 4, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(pf.rb, (lds_void *)(lds + kLdsJunk + c.w * 256), 4, off, 0, 0, 0);
+}
+
+// End of a stage: this wave's LDS reads and writes are done and all of its
+// loads except the two newest (the L2 prefetch) have landed; then all waves
+// meet.  After it the slot just read may be refilled and the slot just
+// loaded may be read.
+__device__ __forceinline__ void stage_barrier()
+{
+    if constexpr (kPrefetch > 0)
+        asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// State threaded through the stage function.
 template <int FMT>
 struct Pipe {
-    __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
     Frags<FMT> F0, F1;                       // k-step fragments, double-buffered
     Fp4Regs fp4;
     ScaleBytes<FMT> sbytes;
-    bool tail;                               // the last stage is partial in K
 };
 
-// Stage s of A and B (and the MX scales) into ring slot SLOT.  Issued as
-// eight pieces so the caller can interleave them with MFMAs.
+// Load piece q (of 8) of the target stage into ring slot `slot`, so the
+// caller can interleave the pieces with MFMAs.
 template <int FMT, bool ALIGNED>
-__device__ __forceinline__ void load_piece(Pipe<FMT> &P, uint8_t *lds, int slot, const Params &p, const Ctx &c, int q,
-                                           int s, bool tail)
+__device__ __forceinline__ void load_piece(Pipe<FMT> &P, uint8_t *lds, int slot, const Target &tg, const Params &p,
+                                           const Ctx &c, int q)
 {
     if constexpr (FMT == kNVFP4) {
-        if (q == 0) load_fp4(P.fp4, P.ra, P.rb, P.rsa, P.rsb, p.lda, p.sld, s, c.t);
+        if (q == 0) load_fp4(P.fp4, tg, p.lda, p.sld, c.t);
     } else {
-        dma_pair(lds, slot, P.ra, P.rb, c, q, s, tail, p.lda);
+        dma_pair(lds, slot, tg, c, q, p.lda);
         if constexpr (FMT == kMXFP8 || FMT == kMXFP4) {
             if (q == 7) {
                 if constexpr (ALIGNED)
-                    dma_scales<FMT>(lds, slot, P.rsa, P.rsb, c, s, p.sld);
+                    dma_scales<FMT>(lds, slot, tg, c, p.sld);
                 else
-                    load_scale_bytes(P.sbytes, P.rsa, P.rsb, c.t, s, p.sld);
+                    load_scale_bytes(P.sbytes, tg, c.t, p.sld);
             }
         }
     }
 }
 
-// Register-staged parts of stage s (NVFP4 data, unaligned MX scales) go to
+// Register-staged parts of a stage (NVFP4 data, unaligned MX scales) go to
 // LDS before the stage's barrier.
 template <int FMT, bool ALIGNED>
 __device__ __forceinline__ void commit_stage(Pipe<FMT> &P, uint8_t *lds, int slot, const Ctx &c)
@@ -479,8 +517,9 @@ template <int FMT>
 constexpr bool rolling() { return FMT == kMXFP8; }
 
 // One phase: the 16 MFMAs of fragment set `cur` while set `nxt` is read
-// (k-step rkk of slot rslot, if rd) and, if ld, stage ls of the operands is
-// loaded into slot lslot in eight pieces between MFMA pairs.  Without
+// (k-step rkk of slot rslot, if rd) and, if tg is given, the target stage is
+// loaded into slot lslot in eight pieces between MFMA pairs, followed by the
+// L2 prefetch pf.  Without
 // rolling, `nxt` is read before the MFMAs.  With rolling, the MFMAs go in
 // 2x2 groups and each next fragment is read as soon as the register it
 // replaces is dead: A0/A1 after the second group, B0/B1 after the third,
@@ -489,7 +528,7 @@ constexpr bool rolling() { return FMT == kMXFP8; }
 template <int FMT, bool ALIGNED>
 __device__ __forceinline__ void phase(f32x16 (&acc)[4][4], Pipe<FMT> &P, const Frags<FMT> &cur, Frags<FMT> &nxt,
                                       uint8_t *lds, const Params &p, const Ctx &c, bool rd, int rslot, int rkk,
-                                      bool ld, int lslot, int ls, bool tail)
+                                      const Target *tg, int lslot, const Target *pf = nullptr)
 {
     if constexpr (!rolling<FMT>()) {
         if (rd) read_frags(nxt, lds, rslot, rkk, c);
@@ -502,11 +541,16 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[4][4], Pipe<FMT> &P, const F
         for (int u = 0; u < 4; ++u) {
             const int i = gi[g] + (u >> 1), j = gj[g] + (u & 1);
             mma1(acc[i][j], cur, i, j);
-            if (u & 1) {
+            if ((u & 1) && tg) {
                 DBS_FENCE();
-                if (ld) load_piece<FMT, ALIGNED>(P, lds, lslot, p, c, 2 * g + (u >> 1), ls, tail);
+                load_piece<FMT, ALIGNED>(P, lds, lslot, *tg, p, c, 2 * g + (u >> 1));
                 DBS_FENCE();
             }
+        }
+        if (kPrefetch > 0 && g == 3 && pf) {
+            DBS_FENCE();
+            l2_prefetch(lds, *pf, c, p.lda);
+            DBS_FENCE();
         }
         if constexpr (rolling<FMT>()) {
             if (rd) {
@@ -522,29 +566,48 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[4][4], Pipe<FMT> &P, const F
     }
 }
 
-// Stage s, read from ring slot `slot` (= s & 1), while stage s+1 is loaded
-// into the other slot.  On entry F1 holds the last k-step of stage s-1
-// (zeros for s = 0): its MFMAs form the first phase, interleaved with the
-// loads of stage s+1 and with the reads of k-step 0 of stage s.  Called with
-// a constant slot the slot offsets fold into immediates.
+// One stage read from ring slot `slot` while the target stage is loaded into
+// the other slot.  On entry F1 holds the last k-step of the previous stage
+// (zeros at a tile's first stage): its MFMAs form the first phase,
+// interleaved with the loads and with the reads of k-step 0 of this stage.
 template <int FMT, bool ALIGNED>
 __device__ __forceinline__ void stage(Pipe<FMT> &P, f32x16 (&acc)[4][4], uint8_t *lds, int slot, const Params &p,
-                                      const Ctx &c, int s)
+                                      const Ctx &c, const Target &tg, const Target &pf)
 {
     constexpr int KK = Fmt<FMT>::KK;
     const int nxt = slot ^ 1;
-    const bool more = s + 1 < p.nk;
-    const bool tail = P.tail && s + 2 == p.nk;
-    phase<FMT, ALIGNED>(acc, P, P.F1, P.F0, lds, p, c, true, slot, 0, more, nxt, s + 1, tail);
+    phase<FMT, ALIGNED>(acc, P, P.F1, P.F0, lds, p, c, true, slot, 0, &tg, nxt, &pf);
 #pragma unroll
     for (int kk = 0; kk < KK - 1; ++kk) {
         if (kk & 1)
-            phase<FMT, ALIGNED>(acc, P, P.F1, P.F0, lds, p, c, true, slot, kk + 1, false, 0, 0, false);
+            phase<FMT, ALIGNED>(acc, P, P.F1, P.F0, lds, p, c, true, slot, kk + 1, nullptr, 0);
         else
-            phase<FMT, ALIGNED>(acc, P, P.F0, P.F1, lds, p, c, true, slot, kk + 1, false, 0, 0, false);
+            phase<FMT, ALIGNED>(acc, P, P.F0, P.F1, lds, p, c, true, slot, kk + 1, nullptr, 0);
     }
-    if (more) commit_stage<FMT, ALIGNED>(P, lds, nxt, c);
-    __syncthreads();
+    commit_stage<FMT, ALIGNED>(P, lds, nxt, c);
+    stage_barrier();
+}
+
+// Buffer resources of output tile `tile`: A/B rows and their scale rows.
+template <int FMT>
+__device__ __forceinline__ Target tile_target(const Params &p, int tile, int s)
+{
+    int tm, tn;
+    tile_coords(tile, p, tm, tn);
+    const int m0 = tm * kTileM, n0 = tn * kTileN;
+    const int rows_a = min(p.M - m0, kTileM), rows_b = min(p.N - n0, kTileN);
+    Target t;
+    t.ra = make_rsrc(p.A + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
+    t.rb = make_rsrc(p.B + (int64_t)n0 * p.lda, (uint32_t)(rows_b * p.lda));
+    t.rsa = t.ra;
+    t.rsb = t.rb;
+    if constexpr (FMT != kBF16) {
+        t.rsa = make_rsrc(p.sA + (int64_t)m0 * p.sld, (uint32_t)(rows_a * p.sld));
+        t.rsb = make_rsrc(p.sB + (int64_t)n0 * p.sld, (uint32_t)(rows_b * p.sld));
+    }
+    t.s = s;
+    t.inval = 0;
+    return t;
 }
 
 template <int FMT, bool ALIGNED>
@@ -572,63 +635,59 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p)
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const int row = c.w * 64 + q * 8 + (c.lane >> 3);
-        c.voff[q] = (uint32_t)(row * p.lda + (((c.lane & 7) ^ swz(row)) << 4));
+        c.kc[q] = ((c.lane & 7) ^ swz(row)) << 4;
+        c.voff[q] = (uint32_t)(row * p.lda + c.kc[q]);
     }
 
     const int ntiles = p.tiles_m * p.tiles_n;
     const int nwg = gridDim.x, wg = blockIdx.x;
     // hardware places workgroup wg on XCD wg % 8: give each XCD a contiguous
     // range of logical ids
-    const int lid = (nwg & 7) == 0 ? (wg & 7) * (nwg >> 3) + (wg >> 3) : wg;
+    int tile = (nwg & 7) == 0 ? (wg & 7) * (nwg >> 3) + (wg >> 3) : wg;
+    if (tile >= ntiles) return;
 
+    // One stream of stages over all of the workgroup's tiles: the last stage
+    // of a tile loads stage 0 of the next one, so no tile starts cold.
     Pipe<FMT> P;
-    P.tail = (p.lda % kRowBytes) != 0;
+    Target cur = tile_target<FMT>(p, tile, 0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) load_piece<FMT, ALIGNED>(P, lds, 0, cur, p, c, q);
+    commit_stage<FMT, ALIGNED>(P, lds, 0, c);
+    __syncthreads();
 
-    for (int tile = lid; tile < ntiles; tile += nwg) {
-        int tm, tn;
-        tile_coords(tile, p, tm, tn);
-        const int m0 = tm * kTileM, n0 = tn * kTileN;
-        const int rows_a = min(p.M - m0, kTileM), rows_b = min(p.N - n0, kTileN);
-        P.ra = make_rsrc(p.A + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
-        P.rb = make_rsrc(p.B + (int64_t)n0 * p.lda, (uint32_t)(rows_b * p.lda));
-        P.rsa = P.ra;
-        P.rsb = P.rb;
-        if constexpr (FMT != kBF16) {
-            P.rsa = make_rsrc(p.sA + (int64_t)m0 * p.sld, (uint32_t)(rows_a * p.sld));
-            P.rsb = make_rsrc(p.sB + (int64_t)n0 * p.sld, (uint32_t)(rows_b * p.sld));
-        }
+    int g = 0;   // stages done by this workgroup: ring slot = g & 1
+    for (;;) {
+        const int next = tile + nwg;
+        Target nt = tile_target<FMT>(p, next < ntiles ? next : tile, 0);
+        if (next >= ntiles) nt.inval = kOOB;
 
         f32x16 acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-        // the "previous stage" of stage 0 contributes nothing
+        // the "previous stage" of a tile's first stage contributes nothing
         P.F1 = Frags<FMT>{};
 #pragma unroll
         for (int i = 0; i < 4; ++i) P.F1.sa[i] = P.F1.sb[i] = 127u;
 
-        // prologue: stage 0 into slot 0
-#pragma unroll
-        for (int q = 0; q < 8; ++q) load_piece<FMT, ALIGNED>(P, lds, 0, p, c, q, 0, P.tail && p.nk == 1);
-        commit_stage<FMT, ALIGNED>(P, lds, 0, c);
-        __syncthreads();
-
-        if constexpr (FMT == kBF16 || FMT == kNVFP4) {
-            // unrolled by two: slot offsets become immediates
-            int s = 0;
-            for (; s + 1 < p.nk; s += 2) {
-                stage<FMT, ALIGNED>(P, acc, lds, 0, p, c, s);
-                stage<FMT, ALIGNED>(P, acc, lds, 1, p, c, s + 1);
-            }
-            if (s < p.nk) stage<FMT, ALIGNED>(P, acc, lds, 0, p, c, s);
-        } else {
-            // the scaled-MFMA body does not fit the register file twice
-            for (int s = 0; s < p.nk; ++s) stage<FMT, ALIGNED>(P, acc, lds, s & 1, p, c, s);
+        for (int s = 0; s < p.nk; ++s, ++g) {
+            Target tg = cur;
+            tg.s = s + 1;
+            if (s + 1 == p.nk) tg = nt;
+            Target pf = cur;
+            pf.s = s + kPrefetch;
+            if (pf.s >= p.nk) pf.inval = kOOB;
+            stage<FMT, ALIGNED>(P, acc, lds, g & 1, p, c, tg, pf);
         }
-        phase<FMT, ALIGNED>(acc, P, P.F1, P.F0, lds, p, c, false, 0, 0, false, 0, 0, false);
+        phase<FMT, ALIGNED>(acc, P, P.F1, P.F0, lds, p, c, false, 0, 0, nullptr, 0);
 
-        store_tile(acc, p, m0, n0, c);
+        int tm, tn;
+        tile_coords(tile, p, tm, tn);
+        store_tile(acc, p, tm * kTileM, tn * kTileN, c);
+        if (next >= ntiles) break;
+        tile = next;
+        cur = nt;
     }
 }
 
