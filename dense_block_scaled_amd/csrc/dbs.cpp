@@ -86,17 +86,23 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     p.sld = block ? (int)(K / block) : 0;
     const int sk = dbs::stage_k(fmt);
     p.nk = (int)((K + sk - 1) / sk);
-    p.tiles_m = (int)((M + dbs::kTileM - 1) / dbs::kTileM);
-    p.tiles_n = (int)((N + dbs::kTileN - 1) / dbs::kTileN);
+    // square tiles unless they would fill at most half of the CUs
+    const int64_t sq_tiles = ((M + dbs::kSquareTM - 1) / dbs::kSquareTM) * ((N + dbs::kSquareTN - 1) / dbs::kSquareTN);
+    const int shape = 2 * sq_tiles <= cus ? dbs::kShapeSkinny : dbs::kShapeSquare;
+    const int tm = shape == dbs::kShapeSkinny ? dbs::kSkinnyTM : dbs::kSquareTM;
+    const int tn = shape == dbs::kShapeSkinny ? dbs::kSkinnyTN : dbs::kSquareTN;
+    p.tiles_m = (int)((M + tm - 1) / tm);
+    p.tiles_n = (int)((N + tn - 1) / tn);
     p.group_m = 4;
     p.vec_store = (N % 4 == 0 && aligned(D, 8)) ? 1 : 0;
+    p.vec16 = (N % 8 == 0 && aligned(D, 16)) ? 1 : 0;
     p.scales_aligned = (block == 0 || (p.sld % 4 == 0 && aligned(sA, 4) && aligned(sB, 4))) ? 1 : 0;
     p.alpha = alpha;
 
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
     if (tiles > INT32_MAX) return fail(DBS_EINVAL, "too many output tiles");
     const int grid = (int)std::min<int64_t>(tiles, cus);
-    hipError_t e = dbs::launch_gemm(fmt, p, grid, stream);
+    hipError_t e = dbs::launch_gemm(fmt, shape, p, grid, stream);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
     g_err[0] = '\0';
     return DBS_OK;

@@ -2,50 +2,61 @@
 //
 //     D[m, n] = bf16( alpha * sum_k dA[m, k] * dB[n, k] ),   fp32 accumulation
 //
-// One persistent kernel template serves the four formats.  Design (and where
-// it departs from the Blackwell kernels the pages describe):
+// One persistent kernel template serves the four formats and two tile
+// shapes.  Design (and where it departs from the Blackwell kernels the pages
+// describe):
 //
 // * Scheduling.  A persistent grid of at most one workgroup per CU walks the
-//   256 x 256 output tiles (cf. the persistent tile loop in "ThunderKittens Now
-//   on NVIDIA Vera Rubin NVL72", Blackwell GEMM recap, and the static
-//   persistent scheduler in "Dissecting ThunderKittens").  Workgroups are
-//   dispatched round-robin over the 8 XCDs, so workgroup ids are remapped to
-//   give every XCD a contiguous run of tile ids, and tile ids are rastered in
-//   groups of `group_m` tile rows: the tiles one XCD runs at the same time
-//   share A and B panels in that XCD's L2 (the locality concern of the
-//   "ThunderKittens 2.0" notes, section 6, and the raster-order tuning of the
-//   Vera Rubin post, final optimisations).
-// * Staging.  Each stage moves a 256-row x 128-byte slab of A and of B into
-//   one slot of a two-slot LDS ring (2 x 64 KiB of the 160 KiB LDS; cf. the
-//   stage-count discussion of "Async Tensor Core: Hopper wgmma -> Blackwell
-//   tcgen05", sections 3.1 and 4.3).  BF16/E4M3/E2M1 slabs go straight from
-//   HBM to LDS (buffer_load_dwordx4 ... lds), so staging costs no VGPRs and no
-//   LDS-write instructions; the load for stage s+1 is issued at the start of
-//   stage s.  Each lane fetches the global chunk that belongs at its fixed LDS
-//   position under an XOR swizzle of the 16-byte chunks, which keeps fragment
-//   reads bank-conflict-free.  Buffer loads return zero for rows past M and
-//   for K columns past K (ragged shapes).  One barrier per stage and no
-//   fences (cf. "ThunderKittens 2.0", section 1).
-// * Scales.  MX scale bytes ride the same stage as their operand slab: they
-//   are loaded one stage ahead straight into VGPRs and fed to the scaled MFMA
-//   as its per-lane E8M0 operand (the gfx950 counterpart of issuing the scale
-//   copy from the same thread as the MMA, "ThunderKittens 2.0", section 2.1).
-// * Math.  Each of the 4 waves owns a 128 x 128 sub-tile as 4 x 4 MFMA 32x32
-//   blocks (256 fp32 accumulators per lane) and reuses every A and B fragment
-//   four times from VGPRs (cf. dual accumulation, "ThunderKittens 2.0",
-//   section 2.2).  Fragments are double-buffered in VGPRs: the reads for
-//   k-step kk+1 are in flight while the MFMAs of kk issue, and the MFMAs of a
-//   stage's last k-step are issued after the barrier, behind the next stage's
-//   first reads.  BF16: v_mfma_f32_32x32x16_bf16.  MXFP8/MXFP4:
-//   v_mfma_scale_f32_32x32x64_f8f6f4.  NVFP4: gfx950's scaled MFMA takes only
-//   E8M0 per 32, so its loader stages through VGPRs and decodes E2M1 x E4M3
-//   exactly into fp16 (a product of 2- and 4-bit significands with magnitude
-//   in [2^-10, 2688]) on the way into LDS; the math is
-//   v_mfma_f32_32x32x16_f16 and tA*tB is applied in the epilogue.
+//   output tiles (cf. the persistent tile loop in "ThunderKittens Now on
+//   NVIDIA Vera Rubin NVL72", Blackwell GEMM recap, and the static persistent
+//   scheduler in "Dissecting ThunderKittens").  Workgroups are dispatched
+//   round-robin over the 8 XCDs, so workgroup ids are remapped to give every
+//   XCD a contiguous run of tile ids, and tile ids are rastered in groups of
+//   `group_m` tile rows: the tiles one XCD runs at the same time share A and
+//   B panels in that XCD's L2 (the locality concern of the "ThunderKittens
+//   2.0" notes, section 6, and the raster-order tuning of the Vera Rubin
+//   post, final optimisations).
+// * Tile shapes (chosen by the host).  Square: 256 x 256 output tiles, 8
+//   waves (two per SIMD), each owning 128 x 64 as 4 x 2 MFMA blocks of 32 x
+//   32.  Skinny (when 256 x 256 tiles cannot fill the CUs, e.g. M = 256):
+//   256 x 64 tiles, 4 waves of 64 x 64.  Two waves per SIMD matter on
+//   gfx950: a wave that issues a global or LDS load stalls its own MFMA
+//   stream for tens of cycles, and the second wave's MFMAs fill that gap
+//   (the role split the pages obtain from dedicated producer warps).
+// * Staging.  Each stage moves a tile-rows x 128-byte slab of A and of B into
+//   one slot of a two-slot LDS ring (cf. the stage-count discussion of
+//   "Async Tensor Core: Hopper wgmma -> Blackwell tcgen05", sections 3.1 and
+//   4.3).  BF16/E4M3/E2M1 slabs go straight from HBM to LDS (buffer_load
+//   ... lds), so staging costs no VGPRs and no LDS-write instructions; the
+//   loads for stage s+1 are issued during stage s, spread between MFMAs.
+//   Each lane fetches the global chunk that belongs at its fixed LDS
+//   position under an XOR swizzle of the 16-byte chunks, which keeps
+//   fragment reads bank-conflict-free.  Buffer loads return zero for rows
+//   past M or N and for K columns past K (ragged shapes).  One barrier per
+//   stage and no fences (cf. "ThunderKittens 2.0", section 1).
+// * Scales.  MX scale bytes ride the same stage as their operand slab
+//   (direct-to-LDS dword loads), and each lane feeds its E8M0 byte to the
+//   scaled MFMA as the per-lane scale operand (the gfx950 counterpart of
+//   issuing the scale copy from the same thread as the MMA, "ThunderKittens
+//   2.0", section 2.1).
+// * Math.  Each wave reuses every A fragment for all of its B blocks and
+//   every B fragment for all of its A blocks from VGPRs (cf. dual
+//   accumulation, "ThunderKittens 2.0", section 2.2).  Fragments are
+//   double-buffered in VGPRs: the reads for k-step kk+1 are in flight while
+//   the MFMAs of kk issue, and the MFMAs of a stage's last k-step are issued
+//   after the barrier, behind the next stage's first reads.  BF16:
+//   v_mfma_f32_32x32x16_bf16.  MXFP8/MXFP4: v_mfma_scale_f32_32x32x64_f8f6f4.
+//   NVFP4: gfx950's scaled MFMA takes only E8M0 per 32, so its loader stages
+//   through VGPRs and decodes E2M1 x E4M3 exactly into fp16 (a product of 2-
+//   and 4-bit significands with magnitude in [2^-10, 2688]) on the way into
+//   LDS; the math is v_mfma_f32_32x32x16_f16 and tA*tB is applied in the
+//   epilogue.
 // * Epilogue.  alpha * acc -> bf16 (round to nearest even) -> global with
 //   buffer stores (out-of-range rows and columns dropped), in the same kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "launch.h"
 
@@ -61,9 +72,7 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kThreads = 256;                  // 4 waves of 64
 constexpr int kRowBytes = 128;                 // bytes of one tile row per stage
-constexpr int kTileBytes = kTileM * kRowBytes; // 32 KiB per operand per stage
 constexpr uint32_t kOOB = 0x80000000u;         // beyond every num_records we set
 
 #define DBS_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -95,49 +104,35 @@ __device__ __forceinline__ void tile_coords(int tile, const Params &p, int &tm, 
     tn = idx / rows;
 }
 
-// LDS map: A slot 0 | A slot 1 | B slot 0 | B slot 1, 32 KiB each; 1 KiB
-// that L2-prefetch loads land in (never read); then for the MX formats the
-// scale slots SA 0 | SA 1 | SB 0 | SB 1 of 256 rows x BPS bytes.  (Planes of
-// 4-byte columns avoid the 2-way bank conflicts of the 8-byte E2M1 rows but
-// measured slower.)  Slot 1 of the operands is reached through the 16-bit
-// immediate offset of ds_read.
-constexpr int kLdsA = 0;
-constexpr int kLdsB = 2 * kTileBytes;
-constexpr int kSlotStride = kTileBytes;
-constexpr int kLdsJunk = 4 * kTileBytes;
-constexpr int kLdsS = kLdsJunk + 1024;
+// ------------------------------------------------------------- tile shapes
 
-// MX scale bytes per row per stage (2 blocks of 32 per 64-K k-step).
-template <int FMT>
-constexpr int scale_bps() { return FMT == kMXFP8 ? 4 : FMT == kMXFP4 ? 8 : 0; }
-template <int FMT>
-constexpr int lds_bytes() { return kLdsS + 4 * kTileM * scale_bps<FMT>(); }
-
-// Stages ahead that an L2 prefetch touches: the direct-to-LDS load of stage
-// s+1 then mostly hits L2 instead of waiting on the Infinity Cache or HBM.
-#ifndef DBS_L2_PREFETCH
-#define DBS_L2_PREFETCH 0
-#endif
-constexpr int kPrefetch = DBS_L2_PREFETCH;   // 0: off
-
-// Per-lane constants of one workgroup.  w, wm, wn are wave-uniform.
-struct Ctx {
-    int t, lane, h, lr;
-    int w, wm, wn;
-    uint32_t fa[4], fb[4];   // LDS address of fragment reads at k-step 0, slot 0
-    uint32_t sa[4], sb[4];   // LDS address of the lane's MX scale byte, k-step 0, slot 0
-    uint32_t voff[8];        // direct-to-LDS source offsets at stage 0
-    int kc[8];               // the K byte (within a stage) those loads fetch
+// TM x TN output tile (TM rows of A, TN rows of B per stage) computed by a
+// WM x WN grid of waves, each owning MB x NB MFMA blocks of 32 x 32.  A stage
+// moves TM/8 + TN/8 wave-loads of 1 KiB (8 rows x 128 bytes); wave w issues
+// QA of A and QB of B.  LDS: A slot 0 | A slot 1 | B slot 0 | B slot 1 |
+// scale slots (MX formats) SA 0 | SA 1 | SB 0 | SB 1 of rows x BPS bytes.
+template <int TM_, int TN_, int WM_, int WN_>
+struct Shape {
+    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+    static constexpr int NW = WM * WN;
+    static constexpr int kThreads = 64 * NW;
+    static constexpr int MB = TM / WM / 32, NB = TN / WN / 32;
+    static constexpr int QA = TM / 8 / NW, QB = TN / 8 / NW;
+    static constexpr int kSlotA = TM * kRowBytes, kSlotB = TN * kRowBytes;
+    static constexpr int kLdsA = 0, kLdsB = 2 * kSlotA, kLdsS = 2 * (kSlotA + kSlotB);
+    static_assert(MB * 32 * WM == TM && NB * 32 * WN == TN, "waves must tile the output tile");
+    static_assert(QA * 8 * NW == TM && QB * 8 * NW == TN && QB > 0, "wave-loads must split evenly");
+    static_assert(TM % 64 == 0 && TN % 64 == 0, "row groups must be whole waves");
+    // slot offsets are single bits above every in-slot address (see read_frag)
+    static_assert((kSlotA & (kSlotA - 1)) == 0 && (kSlotB & (kSlotB - 1)) == 0 && kLdsB % (2 * kSlotB) == 0,
+                  "slot offsets must be OR-able");
 };
-
-// What a stage's loads fetch: stage `s` of the tile whose operand and scale
-// rows start at the four buffer resources.  inval = kOOB turns every load of
-// the target into a zero read (used when a workgroup has nothing left).
-struct Target {
-    __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
-    int s;
-    uint32_t inval;
-};
+using Square = Shape<kSquareTM, kSquareTN, 2, 4>;
+using Skinny = Shape<kSkinnyTM, kSkinnyTN, 4, 1>;
+// Square tiles for MX scales whose rows are not whole dwords (K % 128 != 0):
+// the register-staged scale bytes do not fit beside two waves per SIMD, so
+// this variant runs one wave per SIMD, each owning 128 x 128.
+using SquareW4 = Shape<kSquareTM, kSquareTN, 2, 2>;
 
 // ------------------------------------------------------------ format traits
 
@@ -146,28 +141,59 @@ struct Fmt;
 template <>
 struct Fmt<kBF16> {
     static constexpr int KK = 4;           // MFMA k-steps per stage (16 K each)
+    static constexpr int BPS = 0;          // MX scale bytes per row per stage
     using Frag = bf16x8;
 };
 template <>
 struct Fmt<kNVFP4> {
     static constexpr int KK = 4;           // fp16 in LDS, same geometry as bf16
+    static constexpr int BPS = 0;
     using Frag = f16x8;
 };
 template <>
 struct Fmt<kMXFP8> {
     static constexpr int KK = 2;           // 64 K per k-step, 32 bytes per lane
+    static constexpr int BPS = 4;          // 2 blocks of 32 per k-step
     using Frag = i32x8;
 };
 template <>
 struct Fmt<kMXFP4> {
     static constexpr int KK = 4;           // 64 K per k-step, 16 bytes per lane
+    static constexpr int BPS = 8;
     using Frag = i32x4;
 };
 
-template <int FMT>
+template <int FMT, class S>
+constexpr int lds_bytes() { return S::kLdsS + 2 * (S::TM + S::TN) * Fmt<FMT>::BPS; }
+
+// E4M3 fragments are 8 VGPRs: with 8 waves (256 VGPRs per wave) two full
+// sets do not fit beside the accumulators, so A fragments are single-buffered
+// and each is re-read as soon as its last MFMA of the k-step has issued.
+template <int FMT, class S>
+constexpr bool rolling() { return FMT == kMXFP8 && S::MB * S::NB >= 8; }
+
+// Per-lane constants of one workgroup.  w, wm, wn are wave-uniform.
+template <class S>
+struct Ctx {
+    int t, lane, h, lr;
+    int w, wm, wn;
+    uint32_t fa[S::MB], fb[S::NB];   // LDS address of fragment reads at k-step 0, slot 0
+    uint32_t sa, sb;                 // LDS address of the lane's MX scale byte, block 0, k-step 0, slot 0
+    uint32_t r8lda;                  // (lane/8) * row stride: the lane's row within a wave-load
+    uint32_t x4;                     // ((lane%8) ^ (lane/8)) << 4: swizzle term of the lane's chunk
+};
+
+// Whose stages a load fetches: the tile whose operand and scale rows start
+// at the four buffer resources.  A workgroup with nothing left loads from
+// empty resources, so every load reads zero.
+struct Target {
+    __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+};
+
+template <int FMT, class S>
 struct Frags {
-    typename Fmt<FMT>::Frag a[4], b[4];
-    uint32_t sa[4], sb[4];   // MX: E8M0 byte of each row block for this k-step
+    typename Fmt<FMT>::Frag a[S::MB], b[S::NB];
+    uint32_t sa[S::MB], sb[S::NB];   // MX: E8M0 byte of each row block for this k-step
 };
 
 template <typename V>
@@ -176,192 +202,232 @@ __device__ __forceinline__ V lds_read(const uint8_t *lds, uint32_t addr)
     return *reinterpret_cast<const V *>(lds + addr);
 }
 
-// Fragment reads for k-step kk from ring slot `slot`.  16-bit formats: lane l
-// holds the 8 elements of chunk 2 kk + l/32 of its row.  E2M1: 32 elements,
-// chunk 2 kk + l/32.  E4M3: in the 32x32x64 scaled MFMA with 8-bit elements,
-// lane half h holds K positions [16h, 16h+16) in bytes 0..15 and
-// [32+16h, 48+16h) in bytes 16..31, and its scale applies to K block h, i.e.
-// bytes 16h..16h+15 of both halves (established with a one-instruction
-// probe); so lane half h reads chunks 4 kk + h and 4 kk + 2 + h.  With the
-// XOR swizzle, chunk 2 kk + h of a row sits at fa ^ (kk << 5) and chunk
-// 4 kk + h at fa ^ (kk << 6).  MX scales: lane l of a 32x32x64 scaled MFMA
-// supplies the E8M0 scale of K block l/32 of row l%32 in bits [7:0]; for
-// k-step kk that is byte 2 kk + l/32 of the row's stage scales.
+// Fragment read for k-step kk at LDS address fbase of slot 0; `sel` is the
+// slot's byte offset (a power of two above every bit of fbase, so adding it
+// equals OR-ing it in).  16-bit formats: lane l holds the 8 elements of chunk
+// 2 kk + l/32 of its row.  E2M1: 32 elements, chunk 2 kk + l/32.  E4M3: in
+// the 32x32x64 scaled MFMA with 8-bit elements, lane half h holds K
+// positions [16h, 16h+16) in bytes 0..15 and [32+16h, 48+16h) in bytes
+// 16..31, and its scale applies to K block h, i.e. bytes 16h..16h+15 of both
+// halves (established with a one-instruction probe); so lane half h reads
+// chunks 4 kk + h and 4 kk + 2 + h.  With the XOR swizzle, chunk 2 kk + h of
+// a row sits at fbase ^ (kk << 5) and chunk 4 kk + h at fbase ^ (kk << 6).
+// The whole address is one XOR of fbase with a wave-uniform value, computed
+// at the read so that no per-k-step address stays live in a VGPR.
 template <int FMT>
-__device__ __forceinline__ void read_one(typename Fmt<FMT>::Frag &v, uint32_t &sc, const uint8_t *lds, uint32_t fbase,
-                                         uint32_t sbase, int slot, int kk)
+__device__ __forceinline__ typename Fmt<FMT>::Frag read_frag(const uint8_t *lds, uint32_t fbase, uint32_t sel, int kk)
 {
-    const uint32_t so = (uint32_t)(slot * kSlotStride);
     if constexpr (FMT == kMXFP8) {
-        const uint32_t x = (fbase ^ (uint32_t)(kk << 6)) + so;
+        const uint32_t x = fbase ^ (sel | (uint32_t)(kk << 6));
         const i32x4 v0 = lds_read<i32x4>(lds, x), v1 = lds_read<i32x4>(lds, x ^ 32u);
-        v = i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        return i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     } else {
-        v = lds_read<typename Fmt<FMT>::Frag>(lds, (fbase ^ (uint32_t)(kk << 5)) + so);
+        return lds_read<typename Fmt<FMT>::Frag>(lds, fbase ^ (sel | (uint32_t)(kk << 5)));
     }
-    if constexpr (FMT == kMXFP8 || FMT == kMXFP4)
-        sc = lds[sbase + (uint32_t)(slot * kTileM * scale_bps<FMT>() + 2 * kk)];
 }
 
+// MX scales: lane l of a 32x32x64 scaled MFMA supplies the E8M0 scale of K
+// block l/32 of row l%32 in bits [7:0]; for k-step kk that is byte
+// 2 kk + l/32 of the row's stage scales (the lane's base address holds l/32).
 template <int FMT>
-__device__ __forceinline__ void read_a(Frags<FMT> &f, int i, const uint8_t *lds, int slot, int kk, const Ctx &c)
+__device__ __forceinline__ uint32_t read_scale(const uint8_t *lds, uint32_t sbase, int kk)
 {
-    read_one<FMT>(f.a[i], f.sa[i], lds, c.fa[i], c.sa[i], slot, kk);
+    return lds[sbase + (uint32_t)(2 * kk)];
 }
 
-template <int FMT>
-__device__ __forceinline__ void read_b(Frags<FMT> &f, int j, const uint8_t *lds, int slot, int kk, const Ctx &c)
+template <int FMT, class S>
+__device__ __forceinline__ void read_a(Frags<FMT, S> &f, int i, const uint8_t *lds, int slot, int kk,
+                                       const Ctx<S> &c)
 {
-    read_one<FMT>(f.b[j], f.sb[j], lds, c.fb[j], c.sb[j], slot, kk);
+    constexpr int BPS = Fmt<FMT>::BPS;
+    f.a[i] = read_frag<FMT>(lds, c.fa[i], (uint32_t)(slot * S::kSlotA), kk);
+    if constexpr (BPS > 0) f.sa[i] = read_scale<FMT>(lds, c.sa + (uint32_t)(slot * S::TM * BPS + i * 32 * BPS), kk);
 }
 
-template <int FMT>
-__device__ __forceinline__ void read_frags(Frags<FMT> &f, const uint8_t *lds, int slot, int kk, const Ctx &c)
+template <int FMT, class S>
+__device__ __forceinline__ void read_b(Frags<FMT, S> &f, int j, const uint8_t *lds, int slot, int kk,
+                                       const Ctx<S> &c)
 {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        read_a(f, i, lds, slot, kk, c);
-        read_b(f, i, lds, slot, kk, c);
-    }
+    constexpr int BPS = Fmt<FMT>::BPS;
+    f.b[j] = read_frag<FMT>(lds, c.fb[j], (uint32_t)(slot * S::kSlotB), kk);
+    if constexpr (BPS > 0) f.sb[j] = read_scale<FMT>(lds, c.sb + (uint32_t)(slot * S::TN * BPS + j * 32 * BPS), kk);
 }
 
 // ------------------------------------------------------------------ scales
 
-// MX scales of the target stage for the workgroup's 256 A rows and 256 B
-// rows go to scale slot `slot` as 256 rows x BPS bytes per operand.
+// MX scales of the target stage go to scale slot `slot`: TM (A) and TN (B)
+// rows of BPS bytes, i.e. TM*BPS/4 + TN*BPS/4 dwords, stored densely.
 //
 // Rows whose stage scales are whole dwords (row stride K/32 a multiple of 4):
-// direct-to-LDS dword loads.  A dword wave-load writes 64 lanes x 4 bytes, so
-// for E4M3 (BPS = 4) lane i of wave w carries row 64w + i, and for E2M1
-// (BPS = 8) wave-load j carries rows 64w + 32j + i/2, dword i%2.  A dword
-// past the row's last block (partial last stage) reads zero.
-template <int FMT>
-__device__ __forceinline__ void dma_scales(uint8_t *lds, int slot, const Target &tg, const Ctx &c, int sld)
+// direct-to-LDS dword wave-loads.  Wave-load n of an operand writes its
+// dwords 64n .. 64n+63 (LDS bytes 256n ..); dword d is word d % (BPS/4) of
+// row d / (BPS/4).  Wave w issues wave-loads w, w + NW, ... of the
+// concatenated list (A then B).  A dword past the row's last block (partial
+// last stage) reads zero.
+template <int FMT, class S>
+__device__ __forceinline__ void dma_scales(uint8_t *lds, int slot, const Target &tg, int ks, const Ctx<S> &c, int sld)
 {
-    constexpr int BPS = scale_bps<FMT>();
-    constexpr int NW = BPS / 4;                      // wave-loads per wave per operand
+    constexpr int BPS = Fmt<FMT>::BPS, WPR = BPS / 4;
+    constexpr int NSA = S::TM * BPS / 256, NSB = S::TN * BPS / 256, NS = NSA + NSB;
 #pragma unroll
-    for (int j = 0; j < NW; ++j) {
-        const int row = c.w * 64 + (NW == 1 ? c.lane : j * 32 + (c.lane >> 1));
-        const int word = NW == 1 ? 0 : (c.lane & 1);
-        const int o = tg.s * BPS + 4 * word;
-        const uint32_t off = ((uint32_t)(row * sld + o) | (o < sld ? 0u : kOOB)) | tg.inval;
-        const int dst = slot * kTileM * BPS + (c.w * NW + j) * 256;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(tg.rsa, (lds_void *)(lds + kLdsS + dst), 4, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(tg.rsb, (lds_void *)(lds + kLdsS + 2 * kTileM * BPS + dst), 4,
-                                                 off, 0, 0, 0);
+    for (int k = 0; k < (NS + S::NW - 1) / S::NW; ++k) {
+        const int n = c.w + k * S::NW;      // wave-uniform
+        if (n < NS) {
+            const bool is_a = n < NSA;
+            const int nn = is_a ? n : n - NSA;
+            const int d = nn * 64 + c.lane;
+            const int row = d / WPR, word = d % WPR;
+            const int o = ks * BPS + 4 * word;
+            const uint32_t off = (uint32_t)(row * sld + o) | (o < sld ? 0u : kOOB);
+            const int dst = S::kLdsS + (is_a ? slot * S::TM * BPS : 2 * S::TM * BPS + slot * S::TN * BPS) + nn * 256;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? tg.rsa : tg.rsb, (lds_void *)(lds + dst), 4, off, 0, 0,
+                                                     0);
+        }
     }
 }
 
-// Any other row stride: thread t fetches the BPS bytes of A row t and B row
-// t one by one (bytes past the row's last block read zero) and writes them
-// to LDS before the stage's barrier.
-template <int FMT>
+// Any other row stride: thread t fetches the BPS bytes of rows t, t + threads,
+// ... of the concatenated row list (A rows then B rows) one by one (bytes
+// past the row's last block read zero) and writes them to LDS before the
+// stage's barrier.
+template <class S>
+constexpr int scale_units() { return (S::TM + S::TN + S::kThreads - 1) / S::kThreads; }
+
+template <int FMT, class S>
 struct ScaleBytes {
-    uint32_t a[scale_bps<FMT>() > 0 ? scale_bps<FMT>() : 1], b[scale_bps<FMT>() > 0 ? scale_bps<FMT>() : 1];
+    static constexpr int BPS = Fmt<FMT>::BPS > 0 ? Fmt<FMT>::BPS : 1;
+    uint32_t v[scale_units<S>()][BPS];
 };
 
-template <int FMT>
-__device__ __forceinline__ void load_scale_bytes(ScaleBytes<FMT> &r, const Target &tg, int t, int sld)
+template <int FMT, class S>
+__device__ __forceinline__ void load_scale_bytes(ScaleBytes<FMT, S> &r, const Target &tg, int ks, const Ctx<S> &c,
+                                                 int sld)
 {
-    constexpr int BPS = scale_bps<FMT>();
+    constexpr int BPS = Fmt<FMT>::BPS;
 #pragma unroll
-    for (int b = 0; b < BPS; ++b) {
-        const int o = tg.s * BPS + b;
-        const uint32_t off = ((uint32_t)(t * sld + o) | (o < sld ? 0u : kOOB)) | tg.inval;
-        r.a[b] = __builtin_amdgcn_raw_buffer_load_b8(tg.rsa, off, 0, 0);
-        r.b[b] = __builtin_amdgcn_raw_buffer_load_b8(tg.rsb, off, 0, 0);
+    for (int k = 0; k < scale_units<S>(); ++k) {
+        const int u0 = c.w * 64 + k * S::kThreads;   // wave-uniform: TM, TN are multiples of 64
+        if (u0 < S::TM + S::TN) {
+            const bool is_a = u0 < S::TM;
+            const int row = u0 + c.lane - (is_a ? 0 : S::TM);
+#pragma unroll
+            for (int b = 0; b < BPS; ++b) {
+                const int o = ks * BPS + b;
+                const uint32_t off = (uint32_t)(row * sld + o) | (o < sld ? 0u : kOOB);
+                r.v[k][b] = __builtin_amdgcn_raw_buffer_load_b8(is_a ? tg.rsa : tg.rsb, off, 0, 0);
+            }
+        }
     }
 }
 
-template <int FMT>
-__device__ __forceinline__ void store_scale_bytes(const ScaleBytes<FMT> &r, uint8_t *lds, int slot, int t)
+template <int FMT, class S>
+__device__ __forceinline__ void store_scale_bytes(const ScaleBytes<FMT, S> &r, uint8_t *lds, int slot, const Ctx<S> &c)
 {
-    constexpr int BPS = scale_bps<FMT>();
-    uint8_t *sa = lds + kLdsS + slot * kTileM * BPS + t * BPS;
+    constexpr int BPS = Fmt<FMT>::BPS;
 #pragma unroll
-    for (int b = 0; b < BPS; ++b) {
-        sa[b] = (uint8_t)r.a[b];
-        sa[2 * kTileM * BPS + b] = (uint8_t)r.b[b];
+    for (int k = 0; k < scale_units<S>(); ++k) {
+        const int u0 = c.w * 64 + k * S::kThreads;   // wave-uniform: TM, TN are multiples of 64
+        if (u0 < S::TM + S::TN) {
+            const bool is_a = u0 < S::TM;
+            const int row = u0 + c.lane - (is_a ? 0 : S::TM);
+            uint8_t *dst = lds + S::kLdsS + (is_a ? slot * S::TM * BPS : 2 * S::TM * BPS + slot * S::TN * BPS) +
+                           row * BPS;
+#pragma unroll
+            for (int b = 0; b < BPS; ++b) dst[b] = (uint8_t)r.v[k][b];
+        }
     }
 }
 
 // ------------------------------------------------------------------- math
 
-// One 32x32 block: acc[i][j] += A block i x B block j for one k-step.  The
-// MFMA's first operand is the B fragment, so each lane ends up holding 4
-// consecutive output columns.
+// One 32x32 block for one k-step.  The MFMA's first operand is the B
+// fragment, so each lane ends up holding 4 consecutive output columns.
 template <int FMT>
-__device__ __forceinline__ void mma1(f32x16 &acc, const Frags<FMT> &f, int i, int j)
+__device__ __forceinline__ void mma1(f32x16 &acc, const typename Fmt<FMT>::Frag &a, uint32_t sa,
+                                     const typename Fmt<FMT>::Frag &b, uint32_t sb)
 {
     if constexpr (FMT == kBF16) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc, 0, 0, 0);
     } else if constexpr (FMT == kNVFP4) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, acc, 0, 0, 0);
     } else if constexpr (FMT == kMXFP8) {
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc, 0, 0, 0, (int)f.sb[j], 0,
-                                                              (int)f.sa[i]);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc, 0, 0, 0, (int)sb, 0, (int)sa);
     } else {
-        const i32x8 bb = {f.b[j][0], f.b[j][1], f.b[j][2], f.b[j][3], 0, 0, 0, 0};
-        const i32x8 aa = {f.a[i][0], f.a[i][1], f.a[i][2], f.a[i][3], 0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bb, aa, acc, 4, 4, 0, (int)f.sb[j], 0, (int)f.sa[i]);
+        const i32x8 bb = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+        const i32x8 aa = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bb, aa, acc, 4, 4, 0, (int)sb, 0, (int)sa);
     }
-}
-
-template <int FMT>
-__device__ __forceinline__ void mma(f32x16 (&acc)[4][4], const Frags<FMT> &f)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mma1(acc[i][j], f, i, j);
 }
 
 // ------------------------------------------------------ direct-to-LDS loads
 
-// One wave-load pair (A and B) of the target stage into ring slot `slot`.
-// Wave w issues the 8 wave-loads q of rows 64w .. 64w+63 of each operand; a
-// wave-load writes 64 lanes x 16 bytes to consecutive LDS bytes, i.e. 8 rows
-// x 8 chunks, so lane i lands on row 64w + 8q + i/8, physical chunk i%8, and
-// fetches the logical chunk the swizzle places there (c.voff[q] at stage 0,
-// K byte c.kc[q] within the stage).  Chunks past the row end (a partial
-// last stage) read zeros.
-__device__ __forceinline__ void dma_pair(uint8_t *lds, int slot, const Target &tg, const Ctx &c, int q, int lda)
+// Wave-load L of an operand of the target stage into ring slot `slot`.  It
+// writes 64 lanes x 16 bytes to consecutive LDS bytes, i.e. rows 8L .. 8L+7
+// x 8 chunks, so lane i lands on row 8L + i/8, physical chunk i%8, and
+// fetches the logical chunk the swizzle places there:
+// (i%8) ^ swz(8L + i/8) = (i%8) ^ (i/8) ^ (L%8).  Chunks past the row end (a
+// partial last stage) read zeros.
+template <class S>
+__device__ __forceinline__ void dma_op(uint8_t *lds, int dst, __amdgpu_buffer_rsrc_t rsrc, const Target &tg, int ks,
+                                       const Ctx<S> &c, int L, int lda)
 {
-    const int k0 = tg.s * kRowBytes;
-    const uint32_t off = ((c.voff[q] + (uint32_t)k0) | (k0 + c.kc[q] < lda ? 0u : kOOB)) | tg.inval;
-    const int dst = slot * kSlotStride + (c.w * 8 + q) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(tg.ra, (lds_void *)(lds + kLdsA + dst), 16, off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(tg.rb, (lds_void *)(lds + kLdsB + dst), 16, off, 0, 0, 0);
+    const int k0 = ks * kRowBytes;
+    const uint32_t kc = c.x4 ^ (uint32_t)((L & 7) << 4);
+    const uint32_t off = (c.r8lda + kc + (uint32_t)(L * 8 * lda + k0)) | (kc < (uint32_t)(lda - k0) ? 0u : kOOB);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + dst + L * 1024), 16, off, 0, 0, 0);
+}
+
+// Wave w issues wave-loads w*Q + q, q < Q, of each operand.
+template <class S>
+__device__ __forceinline__ void dma_a(uint8_t *lds, int slot, const Target &tg, int ks, const Ctx<S> &c, int q,
+                                      int lda)
+{
+    dma_op(lds, S::kLdsA + slot * S::kSlotA, tg.ra, tg, ks, c, c.w * S::QA + q, lda);
+}
+
+template <class S>
+__device__ __forceinline__ void dma_b(uint8_t *lds, int slot, const Target &tg, int ks, const Ctx<S> &c, int q,
+                                      int lda)
+{
+    dma_op(lds, S::kLdsB + slot * S::kSlotB, tg.rb, tg, ks, c, c.w * S::QB + q, lda);
 }
 
 // ---------------------------------------------------------- NVFP4 staging
 
-// A stage covers 64 K elements = 32 packed bytes per row.  Thread t loads
-// half t%2 (32 elements) of rows t/2 and t/2 + 128 of A and of B, with the
-// two E4M3 scales of those 32 elements, and expands them to 64 bytes of fp16
-// (4 LDS chunks).
+// A stage covers 64 K elements = 32 packed bytes per row, i.e. two halves of
+// 16 bytes (32 elements) with two E4M3 scales each.  The concatenated list
+// of half-rows (A then B) is split over the threads: thread t takes units
+// t, t + threads, ...; each unit expands to 64 bytes of fp16 (4 LDS chunks).
+template <class S>
+constexpr int fp4_units() { return (2 * (S::TM + S::TN) + S::kThreads - 1) / S::kThreads; }
+
+template <class S>
 struct Fp4Regs {
-    i32x4 a[2], b[2];
-    uint32_t sa[2], sb[2];
+    i32x4 v[fp4_units<S>()];
+    uint32_t s[fp4_units<S>()];
 };
 
-__device__ __forceinline__ void load_fp4(Fp4Regs &r, const Target &tg, int lda, int sld, int t)
+template <class S>
+__device__ __forceinline__ void load_fp4(Fp4Regs<S> &r, const Target &tg, int ks, const Ctx<S> &c, int lda, int sld)
 {
-    const int half = t & 1;
-    const int kb = tg.s * 32 + half * 16;      // packed byte within the row
-    const int sb = tg.s * 4 + half * 2;        // first of the two scale bytes
-    // K%32 == 0: a chunk is all in or all out
-    const uint32_t pad = (kb < lda ? 0u : kOOB) | tg.inval;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = (t >> 1) + 128 * i;
-        const uint32_t off = (uint32_t)(row * lda + kb) | pad;
-        const uint32_t soff = (uint32_t)(row * sld + sb) | pad;
-        r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(tg.ra, off, 0, 0);
-        r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(tg.rb, off, 0, 0);
-        r.sa[i] = __builtin_amdgcn_raw_buffer_load_b16(tg.rsa, soff, 0, 0);
-        r.sb[i] = __builtin_amdgcn_raw_buffer_load_b16(tg.rsb, soff, 0, 0);
+    for (int k = 0; k < fp4_units<S>(); ++k) {
+        const int u0 = c.w * 64 + k * S::kThreads;   // wave-uniform
+        if (u0 < 2 * (S::TM + S::TN)) {
+            const bool is_a = u0 < 2 * S::TM;
+            const int hr = u0 + c.lane - (is_a ? 0 : 2 * S::TM);
+            const int row = hr >> 1, half = hr & 1;
+            // packed bytes ks*32 + half*16 .. +15 and scale bytes ks*4 + half*2
+            // .. +1 of the row.  K % 32 == 0, so each half is all in or all
+            // out (the two halves of a last stage can differ).  The
+            // out-of-range flag rides in the vector offset; the scalar offset
+            // carries only the in-range stage offset.
+            const uint32_t pad = ks * 32 + half * 16 < lda ? 0u : kOOB;
+            r.v[k] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? tg.ra : tg.rb,
+                                                           (uint32_t)(row * lda + half * 16) | pad, (uint32_t)(ks * 32), 0);
+            r.s[k] = __builtin_amdgcn_raw_buffer_load_b16(is_a ? tg.rsa : tg.rsb, (uint32_t)(row * sld + half * 2) | pad,
+                                                          (uint32_t)(ks * 4), 0);
+        }
     }
 }
 
@@ -386,27 +452,30 @@ __device__ __forceinline__ i32x4 expand8(uint32_t codes, f16x2 s)
                  __builtin_bit_cast(int, p3)};
 }
 
-__device__ __forceinline__ void store_fp4(const Fp4Regs &r, uint8_t *lds, int slot, int t)
+template <class S>
+__device__ __forceinline__ void store_fp4(const Fp4Regs<S> &r, uint8_t *lds, int slot, const Ctx<S> &c)
 {
-    const int half = t & 1;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = (t >> 1) + 128 * i;
-        const f16x2 alo = e4m3_pair(r.sa[i] & 0xFF), ahi = e4m3_pair((r.sa[i] >> 8) & 0xFF);
-        const f16x2 blo = e4m3_pair(r.sb[i] & 0xFF), bhi = e4m3_pair((r.sb[i] >> 8) & 0xFF);
+    for (int k = 0; k < fp4_units<S>(); ++k) {
+        const int u0 = c.w * 64 + k * S::kThreads;   // wave-uniform
+        if (u0 < 2 * (S::TM + S::TN)) {
+            const bool is_a = u0 < 2 * S::TM;
+            const int hr = u0 + c.lane - (is_a ? 0 : 2 * S::TM);
+            const int row = hr >> 1, half = hr & 1;
+            uint8_t *base = lds + (is_a ? S::kLdsA + slot * S::kSlotA : S::kLdsB + slot * S::kSlotB);
+            const f16x2 lo = e4m3_pair(r.s[k] & 0xFF), hi = e4m3_pair((r.s[k] >> 8) & 0xFF);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const int o = slot * kSlotStride + lds_off(row, half * 4 + d);
-            *reinterpret_cast<i32x4 *>(lds + kLdsA + o) = expand8((uint32_t)r.a[i][d], d < 2 ? alo : ahi);
-            *reinterpret_cast<i32x4 *>(lds + kLdsB + o) = expand8((uint32_t)r.b[i][d], d < 2 ? blo : bhi);
+            for (int d = 0; d < 4; ++d)
+                *reinterpret_cast<i32x4 *>(base + lds_off(row, half * 4 + d)) =
+                    expand8((uint32_t)r.v[k][d], d < 2 ? lo : hi);
         }
     }
 }
 
 // --------------------------------------------------------------- epilogue
 
-// acc[i][j] holds, for output row m = wm*128 + 32 i + lane%32, the columns
-// n = wn*128 + 32 j + 8 g + 4 (lane/32) + q in register 4 g + q.  Each
+// acc[i][j] holds, for output row m = wm*TM/WM + 32 i + lane%32, the columns
+// n = wn*TN/WN + 32 j + 8 g + 4 (lane/32) + q in register 4 g + q.  Each
 // 32-row block is stored through its own buffer resource, so rows past M
 // and columns past N are dropped by the hardware range check.
 __device__ __forceinline__ uint32_t pack_bf16(float x, float y)
@@ -416,19 +485,20 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
 }
 
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const Params &p, int m0, int n0,
-                                           const Ctx &c)
+template <class S>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[S::MB][S::NB], const Params &p, int m0, int n0,
+                                           const Ctx<S> &c)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r0 = m0 + c.wm * 128 + i * 32;
+    for (int i = 0; i < S::MB; ++i) {
+        const int r0 = m0 + c.wm * (S::TM / S::WM) + i * 32;
         const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)max(0, min(32, p.M - r0)) * (uint32_t)p.N * 2u);
         const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.D + (int64_t)r0 * p.N, bytes);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < S::NB; ++j) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = n0 + c.wn * 128 + j * 32 + g * 8 + c.h * 4;
+                const int n = n0 + c.wn * (S::TN / S::WN) + j * 32 + g * 8 + c.h * 4;
                 const f32x16 &a = acc[i][j];
                 const uint32_t lo = pack_bf16(a[4 * g] * p.alpha, a[4 * g + 1] * p.alpha);
                 const uint32_t hi = pack_bf16(a[4 * g + 2] * p.alpha, a[4 * g + 3] * p.alpha);
@@ -447,56 +517,119 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const Para
     }
 }
 
-// ------------------------------------------------------------------ kernel
-
-// L2 prefetch of stage pf.s of the current tile: one dword per thread of A
-// row t and of B row t, i.e. the first bytes of each row's stage slab (one
-// 128-byte line when the row stride is a multiple of 128).  The dwords land
-// in the junk LDS area and are never waited for or read.
-__device__ __forceinline__ void l2_prefetch(uint8_t *lds, const Target &pf, const Ctx &c, int lda)
+// Epilogue through LDS (when N % 8 == 0 and D is 16-byte aligned): each wave
+// writes one 32-row block-row of its bf16 results into its own 32 x (NB*64)
+// byte buffer in the just-consumed A slot `xslot` (16-byte chunks XOR-swizzled
+// by row), reads it back row-major (CPR lanes per row) and stores whole
+// 16-byte chunks, so one store instruction covers 64/CPR full rows of the
+// wave's columns instead of 32 rows x 16 bytes.  The same wave's LDS writes
+// and reads execute in order; the caller meets a barrier before the slot is
+// refilled.
+template <class S>
+__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[S::MB][S::NB], uint8_t *lds, int xslot,
+                                               const Params &p, int m0, int n0, const Ctx<S> &c)
 {
-    const int k0 = pf.s * kRowBytes;
-    const uint32_t off = ((uint32_t)(c.t * lda + k0) | (k0 < lda ? 0u : kOOB)) | pf.inval;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(pf.ra, (lds_void *)(lds + kLdsJunk + c.w * 256), 4, off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(pf.rb, (lds_void *)(lds + kLdsJunk + c.w * 256), 4, off, 0, 0, 0);
+    constexpr int RB = S::NB * 64;          // bytes per staged row
+    constexpr int CPR = RB / 16;            // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CPR;           // rows per read instruction
+    static_assert(S::NW * 32 * RB <= S::kSlotA, "epilogue buffers must fit in one A slot");
+    uint8_t *buf = lds + S::kLdsA + xslot * S::kSlotA + c.w * 32 * RB;
+    const int nc = n0 + c.wn * (S::TN / S::WN);
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i) {
+#pragma unroll
+        for (int j = 0; j < S::NB; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x16 &a = acc[i][j];
+                const uint32_t lo = pack_bf16(a[4 * g] * p.alpha, a[4 * g + 1] * p.alpha);
+                const uint32_t hi = pack_bf16(a[4 * g + 2] * p.alpha, a[4 * g + 3] * p.alpha);
+                const int ch = (4 * j + g) ^ (c.lr & (CPR - 1));
+                *reinterpret_cast<u32x2 *>(buf + c.lr * RB + 16 * ch + 8 * c.h) = u32x2{lo, hi};
+            }
+        }
+        const int r0 = m0 + c.wm * (S::TM / S::WM) + i * 32;
+        const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)max(0, min(32, p.M - r0)) * (uint32_t)p.N * 2u);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.D + (int64_t)r0 * p.N, bytes);
+#pragma unroll
+        for (int q = 0; q < 32 / RPI; ++q) {
+            const int r = q * RPI + c.lane / CPR, ch = c.lane % CPR;
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(buf + r * RB + 16 * (ch ^ (r & (CPR - 1))));
+            const int n = nc + ch * 8;
+            // N % 8 == 0 and n % 8 == 0: the 8 columns are all in or all out
+            __builtin_amdgcn_raw_buffer_store_b128(v, rd, n < p.N ? (uint32_t)(r * p.N + n) * 2u : kOOB, 0, 0);
+        }
+    }
 }
 
-// End of a stage: this wave's LDS reads and writes are done and all of its
-// loads except the two newest (the L2 prefetch) have landed; then all waves
-// meet.  After it the slot just read may be refilled and the slot just
-// loaded may be read.
+// ------------------------------------------------------------------ kernel
+
+// End of a stage: this wave's LDS reads and writes are done and its loads
+// have landed; then all waves meet.  After it the slot just read may be
+// refilled and the slot just loaded may be read.
 __device__ __forceinline__ void stage_barrier()
 {
-    if constexpr (kPrefetch > 0)
-        asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    DBS_FENCE();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    DBS_FENCE();
+}
+
+// Wait states between a tile's last MFMAs and any read of their results.
+// Without them the generated code can copy a scaled MFMA's result
+// (v_mfma_scale_f32_32x32x64_f8f6f4) out of its AGPRs in the very next
+// instruction and get a stale value (observed on MI355X: exactly the first
+// register copied of each last-issued block was wrong).  The empty asm
+// statements pin every accumulator block in the register class the MFMAs
+// write (AGPRs with one wave per SIMD, VGPRs with two), so the MFMAs write in
+// place and every copy or read comes after the 16 x 8 = 128 wait cycles,
+// which cover the longest MFMA here.  Once per tile; the cost is negligible.
+template <class S>
+__device__ __forceinline__ void mfma_drain(f32x16 (&acc)[S::MB][S::NB])
+{
+    DBS_FENCE();
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+                 "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::);
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < S::NB; ++j) {
+            if constexpr (S::NW == 8)
+                asm volatile("" : "+v"(acc[i][j]));
+            else
+                asm volatile("" : "+a"(acc[i][j]));
+        }
+    DBS_FENCE();
 }
 
 // State threaded through the stage function.
-template <int FMT>
+template <int FMT, class S>
 struct Pipe {
-    Frags<FMT> F0, F1;                       // k-step fragments, double-buffered
-    Fp4Regs fp4;
-    ScaleBytes<FMT> sbytes;
+    Frags<FMT, S> F0, F1;                    // k-step fragments, double-buffered
+    Fp4Regs<S> fp4;
+    ScaleBytes<FMT, S> sbytes;
 };
 
-// Load piece q (of 8) of the target stage into ring slot `slot`, so the
-// caller can interleave the pieces with MFMAs.
-template <int FMT, bool ALIGNED>
-__device__ __forceinline__ void load_piece(Pipe<FMT> &P, uint8_t *lds, int slot, const Target &tg, const Params &p,
-                                           const Ctx &c, int q)
+// Load pieces of a stage.  Direct-to-LDS formats: piece q issues wave-load q
+// of A (q < QA) and of B (q < QB); the MX scale loads go with the last piece.
+// NVFP4: one piece with all of the thread's register-staged loads.
+template <int FMT, class S>
+constexpr int npieces() { return FMT == kNVFP4 ? 1 : (S::QA > S::QB ? S::QA : S::QB); }
+
+template <int FMT, class S, bool ALIGNED>
+__device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int slot, const Target &tg, int ks,
+                                           const Params &p, const Ctx<S> &c, int q)
 {
     if constexpr (FMT == kNVFP4) {
-        if (q == 0) load_fp4(P.fp4, tg, p.lda, p.sld, c.t);
+        load_fp4(P.fp4, tg, ks, c, p.lda, p.sld);
     } else {
-        dma_pair(lds, slot, tg, c, q, p.lda);
+        if (q < S::QA) dma_a(lds, slot, tg, ks, c, q, p.lda);
+        if (q < S::QB) dma_b(lds, slot, tg, ks, c, q, p.lda);
         if constexpr (FMT == kMXFP8 || FMT == kMXFP4) {
-            if (q == 7) {
+            if (q == npieces<FMT, S>() - 1) {
                 if constexpr (ALIGNED)
-                    dma_scales<FMT>(lds, slot, tg, c, p.sld);
+                    dma_scales<FMT>(lds, slot, tg, ks, c, p.sld);
                 else
-                    load_scale_bytes(P.sbytes, tg, c.t, p.sld);
+                    load_scale_bytes(P.sbytes, tg, ks, c, p.sld);
             }
         }
     }
@@ -504,98 +637,112 @@ __device__ __forceinline__ void load_piece(Pipe<FMT> &P, uint8_t *lds, int slot,
 
 // Register-staged parts of a stage (NVFP4 data, unaligned MX scales) go to
 // LDS before the stage's barrier.
-template <int FMT, bool ALIGNED>
-__device__ __forceinline__ void commit_stage(Pipe<FMT> &P, uint8_t *lds, int slot, const Ctx &c)
+template <int FMT, class S, bool ALIGNED>
+__device__ __forceinline__ void commit_stage(Pipe<FMT, S> &P, uint8_t *lds, int slot, const Ctx<S> &c)
 {
-    if constexpr (FMT == kNVFP4) store_fp4(P.fp4, lds, slot, c.t);
-    if constexpr ((FMT == kMXFP8 || FMT == kMXFP4) && !ALIGNED) store_scale_bytes<FMT>(P.sbytes, lds, slot, c.t);
+    if constexpr (FMT == kNVFP4) store_fp4(P.fp4, lds, slot, c);
+    if constexpr ((FMT == kMXFP8 || FMT == kMXFP4) && !ALIGNED) store_scale_bytes(P.sbytes, lds, slot, c);
 }
 
-// Fragments are 8 VGPRs for E4M3 (two sets do not fit beside the 256
-// accumulators), 4 for the other formats.
-template <int FMT>
-constexpr bool rolling() { return FMT == kMXFP8; }
-
-// One phase: the 16 MFMAs of fragment set `cur` while set `nxt` is read
-// (k-step rkk of slot rslot, if rd) and, if tg is given, the target stage is
-// loaded into slot lslot in eight pieces between MFMA pairs, followed by the
-// L2 prefetch pf.  Without
-// rolling, `nxt` is read before the MFMAs.  With rolling, the MFMAs go in
-// 2x2 groups and each next fragment is read as soon as the register it
-// replaces is dead: A0/A1 after the second group, B0/B1 after the third,
-// the rest after the fourth; every fragment is read at least four MFMAs
-// before its first use in the next phase.
-template <int FMT, bool ALIGNED>
-__device__ __forceinline__ void phase(f32x16 (&acc)[4][4], Pipe<FMT> &P, const Frags<FMT> &cur, Frags<FMT> &nxt,
-                                      uint8_t *lds, const Params &p, const Ctx &c, bool rd, int rslot, int rkk,
-                                      const Target *tg, int lslot, const Target *pf = nullptr)
+// Phase PH of a stage (PH = 0 .. KK-1): the MB x NB MFMAs of one k-step —
+// the previous stage's last k-step (set F1) for PH = 0, k-step PH-1 of this
+// stage (set (PH-1) & 1) otherwise — while k-step PH of slot `rslot` is read
+// into the other set (if RD).  With LOADS, the stage's load pieces are issued
+// between MFMAs: piece q after MFMA number q of the stage.  Rolling formats
+// keep A in F0 only: each A fragment is re-read right after its last MFMA.
+template <int FMT, class S, bool ALIGNED, int PH, bool RD, bool LOADS>
+__device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> &P, uint8_t *lds, const Params &p,
+                                      const Ctx<S> &c, int rslot, const Target &tg, int ks, int lslot)
 {
-    if constexpr (!rolling<FMT>()) {
-        if (rd) read_frags(nxt, lds, rslot, rkk, c);
-        DBS_FENCE();
+    constexpr int MB = S::MB, NB = S::NB;
+    constexpr bool CUR1 = PH == 0 || ((PH - 1) & 1);
+    Frags<FMT, S> &cur = CUR1 ? P.F1 : P.F0;
+    Frags<FMT, S> &nxt = CUR1 ? P.F0 : P.F1;
+    constexpr bool ROLL = rolling<FMT, S>();
+    Frags<FMT, S> &fa = ROLL ? P.F0 : cur;      // where this phase's A fragments are
+    constexpr int T = Fmt<FMT>::KK * MB * NB, NP = npieces<FMT, S>();
+    // pieces go out right after the first MFMAs of the stage, so that they
+    // have the longest time to land before the stage's barrier
+    constexpr int SP = 1;
+    static_assert(NP <= T, "every piece needs an MFMA slot");
+
+    if constexpr (RD) {
+        if constexpr (ROLL) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) read_b(nxt, j, lds, rslot, PH, c);
+        } else {
+#pragma unroll
+            for (int i = 0; i < MB; ++i) read_a(nxt, i, lds, rslot, PH, c);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) read_b(nxt, j, lds, rslot, PH, c);
+        }
     }
-    constexpr int gi[4] = {0, 0, 2, 2}, gj[4] = {0, 2, 0, 2};
+    DBS_FENCE();
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int i = 0; i < MB; ++i) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = gi[g] + (u >> 1), j = gj[g] + (u & 1);
-            mma1(acc[i][j], cur, i, j);
-            if ((u & 1) && tg) {
-                DBS_FENCE();
-                load_piece<FMT, ALIGNED>(P, lds, lslot, *tg, p, c, 2 * g + (u >> 1));
-                DBS_FENCE();
-            }
-        }
-        if (kPrefetch > 0 && g == 3 && pf) {
-            DBS_FENCE();
-            l2_prefetch(lds, *pf, c, p.lda);
-            DBS_FENCE();
-        }
-        if constexpr (rolling<FMT>()) {
-            if (rd) {
-                if (g == 1) { read_a(nxt, 0, lds, rslot, rkk, c); read_a(nxt, 1, lds, rslot, rkk, c); }
-                if (g == 2) { read_b(nxt, 0, lds, rslot, rkk, c); read_b(nxt, 1, lds, rslot, rkk, c); }
-                if (g == 3) {
-                    read_a(nxt, 2, lds, rslot, rkk, c); read_a(nxt, 3, lds, rslot, rkk, c);
-                    read_b(nxt, 2, lds, rslot, rkk, c); read_b(nxt, 3, lds, rslot, rkk, c);
+        for (int j = 0; j < NB; ++j) {
+            mma1<FMT>(acc[i][j], fa.a[i], fa.sa[i], cur.b[j], cur.sb[j]);
+            if constexpr (LOADS) {
+                constexpr int base = PH * MB * NB;
+                const int pos = base + i * NB + j;   // compile-time after unrolling
+                if ((pos + 1) % SP == 0 && (pos + 1) / SP - 1 < NP) {
+                    DBS_FENCE();
+                    load_piece<FMT, S, ALIGNED>(P, lds, lslot, tg, ks, p, c, (pos + 1) / SP - 1);
+                    DBS_FENCE();
                 }
             }
+        }
+        if constexpr (ROLL && RD) {
+            DBS_FENCE();
+            read_a(P.F0, i, lds, rslot, PH, c);
             DBS_FENCE();
         }
     }
 }
 
-// One stage read from ring slot `slot` while the target stage is loaded into
-// the other slot.  On entry F1 holds the last k-step of the previous stage
-// (zeros at a tile's first stage): its MFMAs form the first phase,
+// One stage read from ring slot `slot` while stage ks of target tg is loaded
+// into the other slot.  On entry F1 holds the last k-step of the previous
+// stage (zeros at a tile's first stage): its MFMAs form the first phase,
 // interleaved with the loads and with the reads of k-step 0 of this stage.
-template <int FMT, bool ALIGNED>
-__device__ __forceinline__ void stage(Pipe<FMT> &P, f32x16 (&acc)[4][4], uint8_t *lds, int slot, const Params &p,
-                                      const Ctx &c, const Target &tg, const Target &pf)
+// The per-lane constants are re-declared opaque at every stage: addresses
+// derived from them are then recomputed where they are used instead of being
+// hoisted out of the stage loop into registers the accumulators need.
+template <class S>
+__device__ __forceinline__ void opaque(Ctx<S> &c)
+{
+    asm volatile("" : "+v"(c.t), "+v"(c.lane), "+v"(c.r8lda), "+v"(c.x4), "+v"(c.sa), "+v"(c.sb));
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i) asm volatile("" : "+v"(c.fa[i]));
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j) asm volatile("" : "+v"(c.fb[j]));
+}
+
+template <int FMT, class S, bool ALIGNED>
+__device__ __forceinline__ void stage(Pipe<FMT, S> &P, f32x16 (&acc)[S::MB][S::NB], uint8_t *lds, int slot,
+                                      const Params &p, Ctx<S> &c, const Target &tg, int ks)
 {
     constexpr int KK = Fmt<FMT>::KK;
     const int nxt = slot ^ 1;
-    phase<FMT, ALIGNED>(acc, P, P.F1, P.F0, lds, p, c, true, slot, 0, &tg, nxt, &pf);
-#pragma unroll
-    for (int kk = 0; kk < KK - 1; ++kk) {
-        if (kk & 1)
-            phase<FMT, ALIGNED>(acc, P, P.F1, P.F0, lds, p, c, true, slot, kk + 1, nullptr, 0);
-        else
-            phase<FMT, ALIGNED>(acc, P, P.F0, P.F1, lds, p, c, true, slot, kk + 1, nullptr, 0);
+    opaque(c);
+    phase<FMT, S, ALIGNED, 0, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt);
+    phase<FMT, S, ALIGNED, 1, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt);
+    if constexpr (KK > 2) {
+        phase<FMT, S, ALIGNED, 2, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt);
+        phase<FMT, S, ALIGNED, 3, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt);
     }
-    commit_stage<FMT, ALIGNED>(P, lds, nxt, c);
+    commit_stage<FMT, S, ALIGNED>(P, lds, nxt, c);
     stage_barrier();
 }
 
 // Buffer resources of output tile `tile`: A/B rows and their scale rows.
-template <int FMT>
-__device__ __forceinline__ Target tile_target(const Params &p, int tile, int s)
+template <int FMT, class S>
+__device__ __forceinline__ Target tile_target(const Params &p, int tile)
 {
     int tm, tn;
     tile_coords(tile, p, tm, tn);
-    const int m0 = tm * kTileM, n0 = tn * kTileN;
-    const int rows_a = min(p.M - m0, kTileM), rows_b = min(p.N - n0, kTileN);
+    const int m0 = tm * S::TM, n0 = tn * S::TN;
+    const int rows_a = min(p.M - m0, S::TM), rows_b = min(p.N - n0, S::TN);
     Target t;
     t.ra = make_rsrc(p.A + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
     t.rb = make_rsrc(p.B + (int64_t)n0 * p.lda, (uint32_t)(rows_b * p.lda));
@@ -605,39 +752,46 @@ __device__ __forceinline__ Target tile_target(const Params &p, int tile, int s)
         t.rsa = make_rsrc(p.sA + (int64_t)m0 * p.sld, (uint32_t)(rows_a * p.sld));
         t.rsb = make_rsrc(p.sB + (int64_t)n0 * p.sld, (uint32_t)(rows_b * p.sld));
     }
-    t.s = s;
-    t.inval = 0;
     return t;
 }
 
-template <int FMT, bool ALIGNED>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p)
+__device__ __forceinline__ Target null_target()
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<FMT>()];
-    constexpr int BPS = scale_bps<FMT>();
+    Target t;
+    t.ra = t.rb = t.rsa = t.rsb = make_rsrc(nullptr, 0);
+    return t;
+}
 
-    Ctx c;
+template <int FMT, class S, bool ALIGNED>
+__global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<FMT, S>()];
+    constexpr int BPS = Fmt<FMT>::BPS;
+    constexpr int MB = S::MB, NB = S::NB;
+
+    Ctx<S> c;
     c.t = threadIdx.x;
     c.lane = c.t & 63;
     c.h = c.lane >> 5;
     c.lr = c.lane & 31;
     c.w = __builtin_amdgcn_readfirstlane(c.t >> 6);
-    c.wm = c.w >> 1;
-    c.wn = c.w & 1;
+    c.wm = c.w / S::WN;
+    c.wn = c.w % S::WN;
+    const int ra0 = c.wm * (S::TM / S::WM) + c.lr, rb0 = c.wn * (S::TN / S::WN) + c.lr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ra = c.wm * 128 + i * 32 + c.lr, rb = c.wn * 128 + i * 32 + c.lr;
-        c.fa[i] = (uint32_t)(kLdsA + ra * kRowBytes + ((c.h ^ swz(ra)) << 4));
-        c.fb[i] = (uint32_t)(kLdsB + rb * kRowBytes + ((c.h ^ swz(rb)) << 4));
-        c.sa[i] = (uint32_t)(kLdsS + ra * BPS + c.h);
-        c.sb[i] = (uint32_t)(kLdsS + 2 * kTileM * BPS + rb * BPS + c.h);
+    for (int i = 0; i < MB; ++i) {
+        const int ra = ra0 + i * 32;
+        c.fa[i] = (uint32_t)(S::kLdsA + ra * kRowBytes + ((c.h ^ swz(ra)) << 4));
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int row = c.w * 64 + q * 8 + (c.lane >> 3);
-        c.kc[q] = ((c.lane & 7) ^ swz(row)) << 4;
-        c.voff[q] = (uint32_t)(row * p.lda + c.kc[q]);
+    for (int j = 0; j < NB; ++j) {
+        const int rb = rb0 + j * 32;
+        c.fb[j] = (uint32_t)(S::kLdsB + rb * kRowBytes + ((c.h ^ swz(rb)) << 4));
     }
+    c.sa = (uint32_t)(S::kLdsS + ra0 * BPS + c.h);
+    c.sb = (uint32_t)(S::kLdsS + 2 * S::TM * BPS + rb0 * BPS + c.h);
+    c.r8lda = (uint32_t)((c.lane >> 3) * p.lda);
+    c.x4 = (uint32_t)(((c.lane & 7) ^ (c.lane >> 3)) << 4);
 
     const int ntiles = p.tiles_m * p.tiles_n;
     const int nwg = gridDim.x, wg = blockIdx.x;
@@ -648,71 +802,103 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p)
 
     // One stream of stages over all of the workgroup's tiles: the last stage
     // of a tile loads stage 0 of the next one, so no tile starts cold.
-    Pipe<FMT> P;
-    Target cur = tile_target<FMT>(p, tile, 0);
+    Pipe<FMT, S> P;
+    // the tile whose stages the loads fetch: the current tile, and from its
+    // last stage on (which loads stage 0 of the next tile) the next one
+    Target ld = tile_target<FMT, S>(p, tile);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) load_piece<FMT, ALIGNED>(P, lds, 0, cur, p, c, q);
-    commit_stage<FMT, ALIGNED>(P, lds, 0, c);
+    for (int q = 0; q < npieces<FMT, S>(); ++q) load_piece<FMT, S, ALIGNED>(P, lds, 0, ld, 0, p, c, q);
+    commit_stage<FMT, S, ALIGNED>(P, lds, 0, c);
     __syncthreads();
 
     int g = 0;   // stages done by this workgroup: ring slot = g & 1
     for (;;) {
-        const int next = tile + nwg;
-        Target nt = tile_target<FMT>(p, next < ntiles ? next : tile, 0);
-        if (next >= ntiles) nt.inval = kOOB;
-
-        f32x16 acc[4][4];
+        f32x16 acc[MB][NB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+            for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
         // the "previous stage" of a tile's first stage contributes nothing
-        P.F1 = Frags<FMT>{};
+        P.F1 = Frags<FMT, S>{};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) P.F1.sa[i] = P.F1.sb[i] = 127u;
-
-        for (int s = 0; s < p.nk; ++s, ++g) {
-            Target tg = cur;
-            tg.s = s + 1;
-            if (s + 1 == p.nk) tg = nt;
-            Target pf = cur;
-            pf.s = s + kPrefetch;
-            if (pf.s >= p.nk) pf.inval = kOOB;
-            stage<FMT, ALIGNED>(P, acc, lds, g & 1, p, c, tg, pf);
+        for (int j = 0; j < NB; ++j) P.F1.sb[j] = 127u;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) P.F1.sa[i] = 127u;
+        if constexpr (rolling<FMT, S>()) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                P.F0.a[i] = typename Fmt<FMT>::Frag{};
+                P.F0.sa[i] = 127u;
+            }
         }
-        phase<FMT, ALIGNED>(acc, P, P.F1, P.F0, lds, p, c, false, 0, 0, nullptr, 0);
+
+        const int next = tile + nwg;
+        for (int s = 0; s < p.nk; ++s, ++g) {
+            int ks = s + 1;
+            if (ks == p.nk) {
+                ld = next < ntiles ? tile_target<FMT, S>(p, next) : null_target();
+                ks = 0;
+            }
+            stage<FMT, S, ALIGNED>(P, acc, lds, g & 1, p, c, ld, ks);
+        }
+        phase<FMT, S, ALIGNED, 0, false, false>(acc, P, lds, p, c, 0, ld, 0, 0);
+        mfma_drain<S>(acc);
 
         int tm, tn;
         tile_coords(tile, p, tm, tn);
-        store_tile(acc, p, tm * kTileM, tn * kTileN, c);
+        // (the one-wave-per-SIMD variant has no registers to spare for the
+        // staged epilogue)
+        if (S::NW == 8 || S::NB <= 2) {
+            if (p.vec16) {
+                // the slot the last stage read is free until the next
+                // tile's first stage refills it
+                store_tile_lds<S>(acc, lds, (g & 1) ^ 1, p, tm * S::TM, tn * S::TN, c);
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            } else {
+                store_tile<S>(acc, p, tm * S::TM, tn * S::TN, c);
+            }
+        } else {
+            store_tile<S>(acc, p, tm * S::TM, tn * S::TN, c);
+        }
         if (next >= ntiles) break;
         tile = next;
-        cur = nt;
     }
 }
 
-template <int FMT>
+template <int FMT, class S>
 hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
 {
-    const dim3 g(grid), b(kThreads);
-    if (FMT == kBF16 || FMT == kNVFP4 || p.scales_aligned)
-        hipLaunchKernelGGL((gemm_kernel<FMT, true>), g, b, 0, stream, p);
-    else
-        hipLaunchKernelGGL((gemm_kernel<FMT, false>), g, b, 0, stream, p);
+    const dim3 g(grid);
+    if constexpr (FMT == kMXFP8 || FMT == kMXFP4) {
+        if (!p.scales_aligned) {
+            using U = typename std::conditional<std::is_same<S, Square>::value, SquareW4, S>::type;
+            hipLaunchKernelGGL((gemm_kernel<FMT, U, false>), g, dim3(U::kThreads), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((gemm_kernel<FMT, S, true>), g, dim3(S::kThreads), 0, stream, p);
     return hipGetLastError();
+}
+
+template <class S>
+hipError_t launch_shape(int fmt, const Params &p, int grid, hipStream_t stream)
+{
+    switch (fmt) {
+    case kBF16: return launch_fmt<kBF16, S>(p, grid, stream);
+    case kMXFP8: return launch_fmt<kMXFP8, S>(p, grid, stream);
+    case kMXFP4: return launch_fmt<kMXFP4, S>(p, grid, stream);
+    case kNVFP4: return launch_fmt<kNVFP4, S>(p, grid, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int fmt, const Params &p, int grid, hipStream_t stream)
+hipError_t launch_gemm(int fmt, int shape, const Params &p, int grid, hipStream_t stream)
 {
-    switch (fmt) {
-    case kBF16: return launch_fmt<kBF16>(p, grid, stream);
-    case kMXFP8: return launch_fmt<kMXFP8>(p, grid, stream);
-    case kMXFP4: return launch_fmt<kMXFP4>(p, grid, stream);
-    case kNVFP4: return launch_fmt<kNVFP4>(p, grid, stream);
-    default: return hipErrorInvalidValue;
-    }
+    if (shape == kShapeSquare) return launch_shape<Square>(fmt, p, grid, stream);
+    if (shape == kShapeSkinny) return launch_shape<Skinny>(fmt, p, grid, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace dbs

@@ -24,6 +24,7 @@ struct Params {
     int tiles_m, tiles_n;
     int group_m;          // tile rows per raster group
     int vec_store;        // 1 if D rows allow 8-byte stores (N % 4 == 0)
+    int vec16;            // 1 if D rows allow 16-byte stores (N % 8 == 0, D 16-byte aligned)
     int scales_aligned;   // 1 if every scale row starts on a 4-byte boundary
     float alpha;          // applied to the fp32 accumulator before rounding
 };
@@ -33,9 +34,12 @@ constexpr int stage_k(int fmt) {
     return fmt == kBF16 ? 64 : fmt == kMXFP8 ? 128 : fmt == kMXFP4 ? 256 : 64;
 }
 
-constexpr int kTileM = 256;
-constexpr int kTileN = 256;
+// Output tile shapes (rows of A x rows of B per tile).  Square tiles are the
+// default; skinny tiles serve problems whose square tiles would leave CUs idle.
+enum Shape : int { kShapeSquare = 0, kShapeSkinny = 1 };
+constexpr int kSquareTM = 256, kSquareTN = 256;
+constexpr int kSkinnyTM = 256, kSkinnyTN = 64;
 
-hipError_t launch_gemm(int fmt, const Params &p, int grid, hipStream_t stream);
+hipError_t launch_gemm(int fmt, int shape, const Params &p, int grid, hipStream_t stream);
 
 }  // namespace dbs

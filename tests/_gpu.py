@@ -97,3 +97,16 @@ def check_exact(fmt: str, w: dict, D: torch.Tensor) -> None:
     same = (got == want) | (((got & 0x7FFF) == 0) & ((want & 0x7FFF) == 0))
     bad = np.argwhere(~same)
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:5].tolist()}: got {got[tuple(bad[0])]:#06x} want {want[tuple(bad[0])]:#06x}"
+
+
+def check_exact_sampled(fmt: str, w: dict, D: torch.Tensor, em, en) -> None:
+    """check_exact on the given output entries only (for shapes whose full
+    oracle product would take minutes)."""
+    d_ref, _, _ = oracle.gemm_entries(fmt, w, em, en)
+    want = oracle.encode("bf16", d_ref)
+    idx = torch.from_numpy(np.asarray(em) * w["N"] + np.asarray(en)).to(D.device)
+    got = D.view(torch.int16).reshape(-1)[idx].cpu().numpy().view(np.uint16)
+    same = (got == want) | (((got & 0x7FFF) == 0) & ((want & 0x7FFF) == 0))
+    bad = np.flatnonzero(~same)
+    assert bad.size == 0, (f"{len(bad)} mismatches, first at ({em[bad[0]]}, {en[bad[0]]}): "
+                           f"got {got[bad[0]]:#06x} want {want[bad[0]]:#06x}")

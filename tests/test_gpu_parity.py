@@ -38,18 +38,39 @@ def test_cube_256(fmt):
     _gpu.check_full(fmt, w, D)
 
 
+# The library picks 256 x 256 output tiles unless they would occupy at most
+# half of the CUs, and 256 x 64 tiles otherwise.  RAGGED exercises the
+# 256 x 64 path, SQUARE_RAGGED the 256 x 256 one (test_shape_lists_cover_both
+# checks the split against the device's CU count).  MX rows of K/32 scale
+# bytes that are not whole dwords (K % 128 != 0) take the register-staged
+# scale path.
 RAGGED = [
     (300, 520, 352),      # partial tiles in M and N, partial last K stage
     (257, 129, 96),       # one row / one column past a tile edge
     (1, 1, 32),           # single output
     (33, 7, 64),          # N not a multiple of 4 (element-wise stores)
     (512, 260, 4096),     # long K: many ring rotations
+]
+SQUARE_RAGGED = [
+    (3000, 2900, 352),    # partial tiles, partial last stage; MX scale rows of 11 bytes
+    (2900, 3000, 384),    # MX scale rows of whole dwords
+    (2100, 4200, 640),    # partial last MXFP4 stage (640 = 2.5 x 256)
     (5000, 4100, 96),     # 340 tiles > one persistent round
 ]
 
 
+def _square_tiles(M, N):
+    return -(-M // 256) * -(-N // 256)
+
+
+def test_shape_lists_cover_both():
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert all(2 * _square_tiles(M, N) <= cus for M, N, _ in RAGGED)
+    assert all(2 * _square_tiles(M, N) > cus for M, N, _ in SQUARE_RAGGED)
+
+
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", RAGGED + SQUARE_RAGGED, ids=lambda s: "x".join(map(str, s)))
 def test_ragged(fmt, shape):
     M, N, K = shape
     _gpu.say(f"[parity] {fmt} ragged {shape}")
@@ -116,12 +137,26 @@ def test_exact_identity_permutation(fmt, permute):
     _gpu.check_exact(fmt, w, D)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_exact_permutation_square_tiles(fmt):
+    """The permutation test at a shape that takes 256 x 256 tiles (and more
+    than one persistent round), checked bit for bit on sampled entries."""
+    _gpu.say(f"[exact] {fmt} permutation 3000x2944x2944")
+    rng = np.random.default_rng(33)
+    w = _identity_w(fmt, 3000, 2944, rng, True)
+    D = _gpu.run(fmt, w)
+    torch.cuda.synchronize()
+    em, en = synth.sample_entries(34, w["M"], w["N"], 4096)
+    _gpu.check_exact_sampled(fmt, w, D, em, en)
+
+
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "nvfp4"])
-def test_exact_pow2_scale_shift(fmt):
+@pytest.mark.parametrize("shape", [(260, 300, 512), (3000, 2900, 512)], ids=lambda s: "x".join(map(str, s)))
+def test_exact_pow2_scale_shift(fmt, shape):
     """Moving every A scale by a power of two (E8M0 code +3; E4M3 exponent
     field -3) scales every output by exactly that power."""
-    _gpu.say(f"[exact] {fmt} pow2 shift")
-    w = _w(fmt, 260, 300, 512, seed=4)
+    _gpu.say(f"[exact] {fmt} pow2 shift {shape}")
+    w = _w(fmt, *shape, seed=4)
     D0 = _gpu.d_bits(_gpu.run(fmt, w))
     w2 = dict(w)
     if fmt == "nvfp4":
@@ -138,12 +173,13 @@ def test_exact_pow2_scale_shift(fmt):
     assert np.array_equal(f1, f0 * factor)
 
 
-def test_exact_bf16_integers():
-    """bf16 integer inputs in [-8, 8] at K = 1024: every partial sum is an
+@pytest.mark.parametrize("shape", [(300, 270, 1024), (3000, 2900, 256)], ids=lambda s: "x".join(map(str, s)))
+def test_exact_bf16_integers(shape):
+    """bf16 integer inputs in [-8, 8] at K <= 1024: every partial sum is an
     integer below 2^24, so the fp32 result is exact and so is bf16(D)."""
-    _gpu.say("[exact] bf16 integers")
+    _gpu.say(f"[exact] bf16 integers {shape}")
     rng = np.random.default_rng(41)
-    M, N, K = 300, 270, 1024
+    M, N, K = shape
     ia = rng.integers(-8, 9, (M, K)).astype(np.float32)
     ib = rng.integers(-8, 9, (N, K)).astype(np.float32)
     w = {"fmt": "bf16", "M": M, "N": N, "K": K,
