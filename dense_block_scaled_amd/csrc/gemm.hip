@@ -172,13 +172,22 @@ constexpr int lds_bytes() { return S::kLdsS + 2 * (S::TM + S::TN) * Fmt<FMT>::BP
 template <int FMT, class S>
 constexpr bool rolling() { return FMT == kMXFP8 && S::MB * S::NB >= 8; }
 
+// NVFP4 with one wave per column of the wave grid (the skinny tiles): every
+// A row is used by a single wave, so each wave decodes its own A rows
+// straight into MFMA fragments and only B goes through LDS.  Within a stage
+// (64 K elements) lane half h then takes elements [32h, 32h+32): k-step kk
+// uses elements 32h + 8kk .. +7 of A and of B (the same permutation of K on
+// both operands leaves the dot products unchanged).
+template <int FMT, class S>
+constexpr bool adirect() { return FMT == kNVFP4 && S::WN == 1; }
+
 // Per-lane constants of one workgroup.  w, wm, wn are wave-uniform.
 template <class S>
 struct Ctx {
     int t, lane, h, lr;
     int w, wm, wn;
     uint32_t fa[S::MB], fb[S::NB];   // LDS address of fragment reads at k-step 0, slot 0
-    uint32_t sa, sb;                 // LDS address of the lane's MX scale byte, block 0, k-step 0, slot 0
+    uint32_t sa, sb;                 // LDS address of the lane's MX scale row, block 0, slot 0
     uint32_t r8lda;                  // (lane/8) * row stride: the lane's row within a wave-load
     uint32_t x4;                     // ((lane%8) ^ (lane/8)) << 4: swizzle term of the lane's chunk
 };
@@ -193,8 +202,19 @@ struct Target {
 template <int FMT, class S>
 struct Frags {
     typename Fmt<FMT>::Frag a[S::MB], b[S::NB];
-    uint32_t sa[S::MB], sb[S::NB];   // MX: E8M0 byte of each row block for this k-step
 };
+
+// MX scales of one stage for the lane's row of each row block, one dword per
+// block: the byte the scaled MFMA takes for k-step kk sits at byte
+// scale_sel<FMT>(kk), which the instruction's op_sel picks (established with
+// a one-instruction probe: op_sel k selects byte k of the scale register).
+template <class S>
+struct Scales {
+    uint32_t a[S::MB][2], b[S::NB][2];   // [0]: the op_sel-ready dword; [1]: raw high dword (E2M1)
+};
+
+template <int FMT>
+constexpr int scale_sel(int kk) { return FMT == kMXFP8 ? 2 * kk : kk; }
 
 template <typename V>
 __device__ __forceinline__ V lds_read(const uint8_t *lds, uint32_t addr)
@@ -214,7 +234,7 @@ __device__ __forceinline__ V lds_read(const uint8_t *lds, uint32_t addr)
 // a row sits at fbase ^ (kk << 5) and chunk 4 kk + h at fbase ^ (kk << 6).
 // The whole address is one XOR of fbase with a wave-uniform value, computed
 // at the read so that no per-k-step address stays live in a VGPR.
-template <int FMT>
+template <int FMT, int KSH = 5>
 __device__ __forceinline__ typename Fmt<FMT>::Frag read_frag(const uint8_t *lds, uint32_t fbase, uint32_t sel, int kk)
 {
     if constexpr (FMT == kMXFP8) {
@@ -222,35 +242,75 @@ __device__ __forceinline__ typename Fmt<FMT>::Frag read_frag(const uint8_t *lds,
         const i32x4 v0 = lds_read<i32x4>(lds, x), v1 = lds_read<i32x4>(lds, x ^ 32u);
         return i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     } else {
-        return lds_read<typename Fmt<FMT>::Frag>(lds, fbase ^ (sel | (uint32_t)(kk << 5)));
+        return lds_read<typename Fmt<FMT>::Frag>(lds, fbase ^ (sel | (uint32_t)(kk << KSH)));
     }
 }
 
 // MX scales: lane l of a 32x32x64 scaled MFMA supplies the E8M0 scale of K
-// block l/32 of row l%32 in bits [7:0]; for k-step kk that is byte
-// 2 kk + l/32 of the row's stage scales (the lane's base address holds l/32).
+// block l/32 of row l%32; for k-step kk that is byte 2 kk + l/32 of the row's
+// stage scales.  One read per row block and stage: E4M3 rows hold 4 bytes
+// (kk = 0, 1), shifted right by 8 (l/32) so k-step kk's byte is byte 2 kk;
+// E2M1 rows hold 8 bytes (kk = 0..3), of which bytes l/32, 2 + l/32,
+// 4 + l/32, 6 + l/32 are packed into bytes 0..3.
+// The stage's scale rows are read raw at the start of the stage and made
+// op_sel-ready where first needed (adjust_scales), so the adjustment does not
+// wait on reads that were just issued.
 template <int FMT>
-__device__ __forceinline__ uint32_t read_scale(const uint8_t *lds, uint32_t sbase, int kk)
+__device__ __forceinline__ void read_scale_row(uint32_t (&r)[2], const uint8_t *lds, uint32_t addr)
 {
-    return lds[sbase + (uint32_t)(2 * kk)];
+    if constexpr (FMT == kMXFP8) {
+        r[0] = lds_read<uint32_t>(lds, addr);
+    } else {
+        const u32x2 v = lds_read<u32x2>(lds, addr);
+        r[0] = v[0];
+        r[1] = v[1];
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void adjust_scale_row(uint32_t (&r)[2], int h)
+{
+    if constexpr (FMT == kMXFP8)
+        r[0] >>= 8 * h;
+    else
+        r[0] = __builtin_amdgcn_perm(r[1], r[0], 0x06040200u + 0x01010101u * (uint32_t)h);
+}
+
+template <int FMT, class S>
+__device__ __forceinline__ void read_scales(Scales<S> &sc, const uint8_t *lds, int slot, const Ctx<S> &c)
+{
+    constexpr int BPS = Fmt<FMT>::BPS;
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i)
+        read_scale_row<FMT>(sc.a[i], lds, c.sa + (uint32_t)(slot * S::TM * BPS + i * 32 * BPS));
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j)
+        read_scale_row<FMT>(sc.b[j], lds, c.sb + (uint32_t)(slot * S::TN * BPS + j * 32 * BPS));
+}
+
+template <int FMT, class S>
+__device__ __forceinline__ void adjust_scales(Scales<S> &sc, const Ctx<S> &c)
+{
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i) adjust_scale_row<FMT>(sc.a[i], c.h);
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j) adjust_scale_row<FMT>(sc.b[j], c.h);
 }
 
 template <int FMT, class S>
 __device__ __forceinline__ void read_a(Frags<FMT, S> &f, int i, const uint8_t *lds, int slot, int kk,
                                        const Ctx<S> &c)
 {
-    constexpr int BPS = Fmt<FMT>::BPS;
     f.a[i] = read_frag<FMT>(lds, c.fa[i], (uint32_t)(slot * S::kSlotA), kk);
-    if constexpr (BPS > 0) f.sa[i] = read_scale<FMT>(lds, c.sa + (uint32_t)(slot * S::TM * BPS + i * 32 * BPS), kk);
 }
 
 template <int FMT, class S>
 __device__ __forceinline__ void read_b(Frags<FMT, S> &f, int j, const uint8_t *lds, int slot, int kk,
                                        const Ctx<S> &c)
 {
-    constexpr int BPS = Fmt<FMT>::BPS;
-    f.b[j] = read_frag<FMT>(lds, c.fb[j], (uint32_t)(slot * S::kSlotB), kk);
-    if constexpr (BPS > 0) f.sb[j] = read_scale<FMT>(lds, c.sb + (uint32_t)(slot * S::TN * BPS + j * 32 * BPS), kk);
+    // with A decoded in registers, B's k-step kk is chunk 4h + kk of the row
+    constexpr int KSH = adirect<FMT, S>() ? 4 : 5;
+    f.b[j] = read_frag<FMT, KSH>(lds, c.fb[j], (uint32_t)(slot * S::kSlotB), kk);
 }
 
 // ------------------------------------------------------------------ scales
@@ -342,7 +402,9 @@ __device__ __forceinline__ void store_scale_bytes(const ScaleBytes<FMT, S> &r, u
 
 // One 32x32 block for one k-step.  The MFMA's first operand is the B
 // fragment, so each lane ends up holding 4 consecutive output columns.
-template <int FMT>
+// MX: the scale operands are the blocks' stage scale dwords, of which op_sel
+// SEL picks the byte of this k-step.
+template <int FMT, int SEL>
 __device__ __forceinline__ void mma1(f32x16 &acc, const typename Fmt<FMT>::Frag &a, uint32_t sa,
                                      const typename Fmt<FMT>::Frag &b, uint32_t sb)
 {
@@ -351,11 +413,11 @@ __device__ __forceinline__ void mma1(f32x16 &acc, const typename Fmt<FMT>::Frag 
     } else if constexpr (FMT == kNVFP4) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, acc, 0, 0, 0);
     } else if constexpr (FMT == kMXFP8) {
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc, 0, 0, 0, (int)sb, 0, (int)sa);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc, 0, 0, SEL, (int)sb, SEL, (int)sa);
     } else {
         const i32x8 bb = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
         const i32x8 aa = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bb, aa, acc, 4, 4, 0, (int)sb, 0, (int)sa);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bb, aa, acc, 4, 4, SEL, (int)sb, SEL, (int)sa);
     }
 }
 
@@ -398,24 +460,30 @@ __device__ __forceinline__ void dma_b(uint8_t *lds, int slot, const Target &tg, 
 // 16 bytes (32 elements) with two E4M3 scales each.  The concatenated list
 // of half-rows (A then B) is split over the threads: thread t takes units
 // t, t + threads, ...; each unit expands to 64 bytes of fp16 (4 LDS chunks).
-template <class S>
-constexpr int fp4_units() { return (2 * (S::TM + S::TN) + S::kThreads - 1) / S::kThreads; }
+// With A decoded in registers (adirect) the list holds the B half-rows only.
+template <class S, bool AD>
+constexpr int fp4_rows() { return AD ? S::TN : S::TM + S::TN; }
 
-template <class S>
+template <class S, bool AD>
+constexpr int fp4_units() { return (2 * fp4_rows<S, AD>() + S::kThreads - 1) / S::kThreads; }
+
+template <class S, bool AD>
 struct Fp4Regs {
-    i32x4 v[fp4_units<S>()];
-    uint32_t s[fp4_units<S>()];
+    i32x4 v[fp4_units<S, AD>()];
+    uint32_t s[fp4_units<S, AD>()];
 };
 
-template <class S>
-__device__ __forceinline__ void load_fp4(Fp4Regs<S> &r, const Target &tg, int ks, const Ctx<S> &c, int lda, int sld)
+template <class S, bool AD>
+__device__ __forceinline__ void load_fp4(Fp4Regs<S, AD> &r, const Target &tg, int ks, const Ctx<S> &c, int lda,
+                                         int sld)
 {
+    constexpr int TA = AD ? 0 : S::TM;   // A rows in the list
 #pragma unroll
-    for (int k = 0; k < fp4_units<S>(); ++k) {
+    for (int k = 0; k < fp4_units<S, AD>(); ++k) {
         const int u0 = c.w * 64 + k * S::kThreads;   // wave-uniform
-        if (u0 < 2 * (S::TM + S::TN)) {
-            const bool is_a = u0 < 2 * S::TM;
-            const int hr = u0 + c.lane - (is_a ? 0 : 2 * S::TM);
+        if (u0 < 2 * fp4_rows<S, AD>()) {
+            const bool is_a = u0 < 2 * TA;
+            const int hr = u0 + c.lane - (is_a ? 0 : 2 * TA);
             const int row = hr >> 1, half = hr & 1;
             // packed bytes ks*32 + half*16 .. +15 and scale bytes ks*4 + half*2
             // .. +1 of the row.  K % 32 == 0, so each half is all in or all
@@ -452,15 +520,16 @@ __device__ __forceinline__ i32x4 expand8(uint32_t codes, f16x2 s)
                  __builtin_bit_cast(int, p3)};
 }
 
-template <class S>
-__device__ __forceinline__ void store_fp4(const Fp4Regs<S> &r, uint8_t *lds, int slot, const Ctx<S> &c)
+template <class S, bool AD>
+__device__ __forceinline__ void store_fp4(const Fp4Regs<S, AD> &r, uint8_t *lds, int slot, const Ctx<S> &c)
 {
+    constexpr int TA = AD ? 0 : S::TM;
 #pragma unroll
-    for (int k = 0; k < fp4_units<S>(); ++k) {
+    for (int k = 0; k < fp4_units<S, AD>(); ++k) {
         const int u0 = c.w * 64 + k * S::kThreads;   // wave-uniform
-        if (u0 < 2 * (S::TM + S::TN)) {
-            const bool is_a = u0 < 2 * S::TM;
-            const int hr = u0 + c.lane - (is_a ? 0 : 2 * S::TM);
+        if (u0 < 2 * fp4_rows<S, AD>()) {
+            const bool is_a = u0 < 2 * TA;
+            const int hr = u0 + c.lane - (is_a ? 0 : 2 * TA);
             const int row = hr >> 1, half = hr & 1;
             uint8_t *base = lds + (is_a ? S::kLdsA + slot * S::kSlotA : S::kLdsB + slot * S::kSlotB);
             const f16x2 lo = e4m3_pair(r.s[k] & 0xFF), hi = e4m3_pair((r.s[k] >> 8) & 0xFF);
@@ -469,6 +538,41 @@ __device__ __forceinline__ void store_fp4(const Fp4Regs<S> &r, uint8_t *lds, int
                 *reinterpret_cast<i32x4 *>(base + lds_off(row, half * 4 + d)) =
                     expand8((uint32_t)r.v[k][d], d < 2 ? lo : hi);
         }
+    }
+}
+
+// A rows decoded in registers: the lane loads the 16 packed bytes (32
+// elements) of half h of its row in each of the wave's row blocks, with their
+// two E4M3 scales, and decodes dword kk into the fragment of k-step kk.
+template <class S>
+struct Fp4A {
+    i32x4 v[S::MB];
+    uint32_t s[S::MB];
+};
+
+template <class S>
+__device__ __forceinline__ void load_fp4_a(Fp4A<S> &r, const Target &tg, int ks, const Ctx<S> &c, int lda, int sld)
+{
+    const uint32_t pad = ks * 32 + c.h * 16 < lda ? 0u : kOOB;
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i) {
+        const int row = c.wm * (S::TM / S::WM) + i * 32 + c.lr;
+        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(tg.ra, (uint32_t)(row * lda + c.h * 16) | pad, (uint32_t)(ks * 32),
+                                                       0);
+        r.s[i] = __builtin_amdgcn_raw_buffer_load_b16(tg.rsa, (uint32_t)(row * sld + c.h * 2) | pad, (uint32_t)(ks * 4),
+                                                      0);
+    }
+}
+
+template <class S>
+__device__ __forceinline__ void decode_fp4_a(f16x8 (&a)[S::MB][4], const Fp4A<S> &r)
+{
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i) {
+        const f16x2 lo = e4m3_pair(r.s[i] & 0xFF), hi = e4m3_pair((r.s[i] >> 8) & 0xFF);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            a[i][kk] = __builtin_bit_cast(f16x8, expand8((uint32_t)r.v[i][kk], kk < 2 ? lo : hi));
     }
 }
 
@@ -605,7 +709,11 @@ __device__ __forceinline__ void mfma_drain(f32x16 (&acc)[S::MB][S::NB])
 template <int FMT, class S>
 struct Pipe {
     Frags<FMT, S> F0, F1;                    // k-step fragments, double-buffered
-    Fp4Regs<S> fp4;
+    Scales<S> sprev, scur;                   // MX scales of the previous and of this stage
+    Fp4Regs<S, adirect<FMT, S>()> fp4;
+    Fp4A<S> fp4a;                            // adirect: the wave's packed A rows of the next stage
+    f16x8 acur[S::MB][4];                    // adirect: this stage's A fragments per k-step
+    f16x8 aprev[S::MB];                      // adirect: the previous stage's last k-step
     ScaleBytes<FMT, S> sbytes;
 };
 
@@ -621,6 +729,7 @@ __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int sl
 {
     if constexpr (FMT == kNVFP4) {
         load_fp4(P.fp4, tg, ks, c, p.lda, p.sld);
+        if constexpr (adirect<FMT, S>()) load_fp4_a(P.fp4a, tg, ks, c, p.lda, p.sld);
     } else {
         if (q < S::QA) dma_a(lds, slot, tg, ks, c, q, p.lda);
         if (q < S::QB) dma_b(lds, slot, tg, ks, c, q, p.lda);
@@ -641,6 +750,13 @@ template <int FMT, class S, bool ALIGNED>
 __device__ __forceinline__ void commit_stage(Pipe<FMT, S> &P, uint8_t *lds, int slot, const Ctx<S> &c)
 {
     if constexpr (FMT == kNVFP4) store_fp4(P.fp4, lds, slot, c);
+    if constexpr (adirect<FMT, S>()) {
+        // the stage ending now keeps its last k-step for the next stage's
+        // first phase; the loaded stage becomes the current one
+#pragma unroll
+        for (int i = 0; i < S::MB; ++i) P.aprev[i] = P.acur[i][3];
+        decode_fp4_a<S>(P.acur, P.fp4a);
+    }
     if constexpr ((FMT == kMXFP8 || FMT == kMXFP4) && !ALIGNED) store_scale_bytes(P.sbytes, lds, slot, c);
 }
 
@@ -666,23 +782,34 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
     constexpr int SP = 1;
     static_assert(NP <= T, "every piece needs an MFMA slot");
 
+    // the k-step these MFMAs consume and its stage's scales
+    constexpr int KC = PH == 0 ? Fmt<FMT>::KK - 1 : PH - 1;
+    const Scales<S> &sc = PH == 0 ? P.sprev : P.scur;
+
     if constexpr (RD) {
         if constexpr (ROLL) {
 #pragma unroll
             for (int j = 0; j < NB; ++j) read_b(nxt, j, lds, rslot, PH, c);
         } else {
+            if constexpr (!adirect<FMT, S>()) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i) read_a(nxt, i, lds, rslot, PH, c);
+                for (int i = 0; i < MB; ++i) read_a(nxt, i, lds, rslot, PH, c);
+            }
 #pragma unroll
             for (int j = 0; j < NB; ++j) read_b(nxt, j, lds, rslot, PH, c);
         }
+        if constexpr (Fmt<FMT>::BPS > 0 && PH == 0) read_scales<FMT>(P.scur, lds, rslot, c);
     }
+    if constexpr (Fmt<FMT>::BPS > 0 && PH == 1) adjust_scales<FMT>(P.scur, c);
     DBS_FENCE();
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            mma1<FMT>(acc[i][j], fa.a[i], fa.sa[i], cur.b[j], cur.sb[j]);
+            if constexpr (adirect<FMT, S>())
+                mma1<FMT, 0>(acc[i][j], PH == 0 ? P.aprev[i] : P.acur[i][KC], 0u, cur.b[j], 0u);
+            else
+                mma1<FMT, scale_sel<FMT>(KC)>(acc[i][j], fa.a[i], sc.a[i][0], cur.b[j], sc.b[j][0]);
             if constexpr (LOADS) {
                 constexpr int base = PH * MB * NB;
                 const int pos = base + i * NB + j;   // compile-time after unrolling
@@ -732,6 +859,12 @@ __device__ __forceinline__ void stage(Pipe<FMT, S> &P, f32x16 (&acc)[S::MB][S::N
         phase<FMT, S, ALIGNED, 3, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt);
     }
     commit_stage<FMT, S, ALIGNED>(P, lds, nxt, c);
+    if constexpr (Fmt<FMT>::BPS > 0) {
+#pragma unroll
+        for (int i = 0; i < S::MB; ++i) P.sprev.a[i][0] = P.scur.a[i][0];
+#pragma unroll
+        for (int j = 0; j < S::NB; ++j) P.sprev.b[j][0] = P.scur.b[j][0];
+    }
     stage_barrier();
 }
 
@@ -786,10 +919,10 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         const int rb = rb0 + j * 32;
-        c.fb[j] = (uint32_t)(S::kLdsB + rb * kRowBytes + ((c.h ^ swz(rb)) << 4));
+        c.fb[j] = (uint32_t)(S::kLdsB + rb * kRowBytes + (((adirect<FMT, S>() ? 4 * c.h : c.h) ^ swz(rb)) << 4));
     }
-    c.sa = (uint32_t)(S::kLdsS + ra0 * BPS + c.h);
-    c.sb = (uint32_t)(S::kLdsS + 2 * S::TM * BPS + rb0 * BPS + c.h);
+    c.sa = (uint32_t)(S::kLdsS + ra0 * BPS);
+    c.sb = (uint32_t)(S::kLdsS + 2 * S::TM * BPS + rb0 * BPS);
     c.r8lda = (uint32_t)((c.lane >> 3) * p.lda);
     c.x4 = (uint32_t)(((c.lane & 7) ^ (c.lane >> 3)) << 4);
 
@@ -803,6 +936,12 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
     // One stream of stages over all of the workgroup's tiles: the last stage
     // of a tile loads stage 0 of the next one, so no tile starts cold.
     Pipe<FMT, S> P;
+    if constexpr (adirect<FMT, S>()) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) P.acur[i][kk] = f16x8{};
+    }
     // the tile whose stages the loads fetch: the current tile, and from its
     // last stage on (which loads stage 0 of the next tile) the next one
     Target ld = tile_target<FMT, S>(p, tile);
@@ -820,16 +959,20 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
             for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
         // the "previous stage" of a tile's first stage contributes nothing
         P.F1 = Frags<FMT, S>{};
+        if constexpr (adirect<FMT, S>()) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) P.F1.sb[j] = 127u;
-#pragma unroll
-        for (int i = 0; i < MB; ++i) P.F1.sa[i] = 127u;
+            for (int i = 0; i < MB; ++i) P.aprev[i] = f16x8{};
+        }
         if constexpr (rolling<FMT, S>()) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                P.F0.a[i] = typename Fmt<FMT>::Frag{};
-                P.F0.sa[i] = 127u;
-            }
+            for (int i = 0; i < MB; ++i) P.F0.a[i] = typename Fmt<FMT>::Frag{};
+        }
+        if constexpr (Fmt<FMT>::BPS > 0) {
+            // unit E8M0 scales (finite) for those zero fragments
+#pragma unroll
+            for (int i = 0; i < MB; ++i) P.sprev.a[i][0] = 0x7F7F7F7Fu;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) P.sprev.b[j][0] = 0x7F7F7F7Fu;
         }
 
         const int next = tile + nwg;
