@@ -84,8 +84,6 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     p.K = (int)K;
     p.lda = (int)(K * elem_bits / 8);
     p.sld = block ? (int)(K / block) : 0;
-    const int sk = dbs::stage_k(fmt);
-    p.nk = (int)((K + sk - 1) / sk);
     // square tiles unless they would fill at most half of the CUs
     const int64_t sq_tiles = ((M + dbs::kSquareTM - 1) / dbs::kSquareTM) * ((N + dbs::kSquareTN - 1) / dbs::kSquareTN);
     const int shape = 2 * sq_tiles <= cus ? dbs::kShapeSkinny : dbs::kShapeSquare;

@@ -72,7 +72,6 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kRowBytes = 128;                 // bytes of one tile row per stage
 constexpr uint32_t kOOB = 0x80000000u;         // beyond every num_records we set
 
 #define DBS_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -84,6 +83,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
+
+constexpr int kRowBytes = 128;                 // bytes of one tile row per stage
 
 // XOR swizzle of the 8 16-byte chunks of a tile row: 8 (and 16) consecutive
 // rows reading the same logical chunk hit distinct bank groups.
@@ -107,28 +108,39 @@ __device__ __forceinline__ void tile_coords(int tile, const Params &p, int &tm, 
 // ------------------------------------------------------------- tile shapes
 
 // TM x TN output tile (TM rows of A, TN rows of B per stage) computed by a
-// WM x WN grid of waves, each owning MB x NB MFMA blocks of 32 x 32.  A stage
-// moves TM/8 + TN/8 wave-loads of 1 KiB (8 rows x 128 bytes); wave w issues
-// QA of A and QB of B.  LDS: A slot 0 | A slot 1 | B slot 0 | B slot 1 |
-// scale slots (MX formats) SA 0 | SA 1 | SB 0 | SB 1 of rows x BPS bytes.
-template <int TM_, int TN_, int WM_, int WN_>
+// WM x WN grid of waves, each owning MB x NB MFMA blocks of 32 x 32, over an
+// NS-slot LDS ring.  A stage moves (TM + TN) / 8 wave-loads of 1 KiB (8 rows
+// x 128 bytes); wave w issues QA of A and QB of B.  LDS: A slots 0..NS-1 | B
+// slots 0..NS-1 | scale slots (MX formats) SA 0..NS-1 | SB 0..NS-1 of rows x
+// BPS bytes.
+constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
+
+template <int TM_, int TN_, int WM_, int WN_, int NS_ = 2>
 struct Shape {
-    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_;
+    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_, NS = NS_;
     static constexpr int NW = WM * WN;
     static constexpr int kThreads = 64 * NW;
     static constexpr int MB = TM / WM / 32, NB = TN / WN / 32;
-    static constexpr int QA = TM / 8 / NW, QB = TN / 8 / NW;
+    static constexpr int RPL = 1024 / kRowBytes;   // rows per 1 KiB wave-load
+    static constexpr int QA = TM / RPL / NW, QB = TN / RPL / NW;
     static constexpr int kSlotA = TM * kRowBytes, kSlotB = TN * kRowBytes;
-    static constexpr int kLdsA = 0, kLdsB = 2 * kSlotA, kLdsS = 2 * (kSlotA + kSlotB);
+    static constexpr int kLdsA = 0, kLdsB = NS * kSlotA, kLdsS = NS * (kSlotA + kSlotB);
     static_assert(MB * 32 * WM == TM && NB * 32 * WN == TN, "waves must tile the output tile");
-    static_assert(QA * 8 * NW == TM && QB * 8 * NW == TN && QB > 0, "wave-loads must split evenly");
+    static_assert(QA * RPL * NW == TM && QB * RPL * NW == TN && QB > 0, "wave-loads must split evenly");
     static_assert(TM % 64 == 0 && TN % 64 == 0, "row groups must be whole waves");
-    // slot offsets are single bits above every in-slot address (see read_frag)
-    static_assert((kSlotA & (kSlotA - 1)) == 0 && (kSlotB & (kSlotB - 1)) == 0 && kLdsB % (2 * kSlotB) == 0,
+    static_assert(NS >= 2, "the ring needs two slots");
+    // slot offsets only touch bits above every in-slot address (see read_frag)
+    static_assert((kSlotA & (kSlotA - 1)) == 0 && (kSlotB & (kSlotB - 1)) == 0 &&
+                      kLdsB % (pow2_at_least(NS) * kSlotB) == 0,
                   "slot offsets must be OR-able");
 };
 using Square = Shape<kSquareTM, kSquareTN, 2, 4>;
+// Skinny tiles hold 40 KiB per slot: formats whose stages arrive entirely by
+// direct-to-LDS loads use a three-slot ring (loads get two stages to land)
+// and 8 waves of 32 x 64 (two per SIMD); register-staged ones (NVFP4,
+// unaligned MX scales) keep two slots and 4 waves of 64 x 64.
 using Skinny = Shape<kSkinnyTM, kSkinnyTN, 4, 1>;
+using SkinnyDeep = Shape<kSkinnyTM, kSkinnyTN, 8, 1, 3>;
 // Square tiles for MX scales whose rows are not whole dwords (K % 128 != 0):
 // the register-staged scale bytes do not fit beside two waves per SIMD, so
 // this variant runs one wave per SIMD, each owning 128 x 128.
@@ -140,31 +152,35 @@ template <int FMT>
 struct Fmt;
 template <>
 struct Fmt<kBF16> {
-    static constexpr int KK = 4;           // MFMA k-steps per stage (16 K each)
+    static constexpr int KSB = 32;         // row bytes per MFMA k-step (16 K)
     static constexpr int BPS = 0;          // MX scale bytes per row per stage
     using Frag = bf16x8;
 };
 template <>
 struct Fmt<kNVFP4> {
-    static constexpr int KK = 4;           // fp16 in LDS, same geometry as bf16
+    static constexpr int KSB = 32;         // fp16 in LDS, same geometry as bf16
     static constexpr int BPS = 0;
     using Frag = f16x8;
 };
 template <>
 struct Fmt<kMXFP8> {
-    static constexpr int KK = 2;           // 64 K per k-step, 32 bytes per lane
+    static constexpr int KSB = 64;         // 64 K per k-step, 32 bytes per lane
     static constexpr int BPS = 4;          // 2 blocks of 32 per k-step
     using Frag = i32x8;
 };
 template <>
 struct Fmt<kMXFP4> {
-    static constexpr int KK = 4;           // 64 K per k-step, 16 bytes per lane
+    static constexpr int KSB = 32;         // 64 K per k-step, 16 bytes per lane
     static constexpr int BPS = 8;
     using Frag = i32x4;
 };
 
+// MFMA k-steps per stage
 template <int FMT, class S>
-constexpr int lds_bytes() { return S::kLdsS + 2 * (S::TM + S::TN) * Fmt<FMT>::BPS; }
+constexpr int kk_of() { return kRowBytes / Fmt<FMT>::KSB; }
+
+template <int FMT, class S>
+constexpr int lds_bytes() { return S::kLdsS + S::NS * (S::TM + S::TN) * Fmt<FMT>::BPS; }
 
 // E4M3 fragments are 8 VGPRs: with 8 waves (256 VGPRs per wave) two full
 // sets do not fit beside the accumulators, so A fragments are single-buffered
@@ -186,10 +202,10 @@ template <class S>
 struct Ctx {
     int t, lane, h, lr;
     int w, wm, wn;
-    uint32_t fa[S::MB], fb[S::NB];   // LDS address of fragment reads at k-step 0, slot 0
+    uint32_t fa, fb;                 // LDS address of the lane's fragment read, block 0, k-step 0, slot 0
     uint32_t sa, sb;                 // LDS address of the lane's MX scale row, block 0, slot 0
-    uint32_t r8lda;                  // (lane/8) * row stride: the lane's row within a wave-load
-    uint32_t x4;                     // ((lane%8) ^ (lane/8)) << 4: swizzle term of the lane's chunk
+    uint32_t r8lda;                  // the lane's row within a wave-load times the row stride
+    uint32_t x4;                     // the lane's chunk within a wave-load, swizzle applied, << 4
 };
 
 // Whose stages a load fetches: the tile whose operand and scale rows start
@@ -233,16 +249,21 @@ __device__ __forceinline__ V lds_read(const uint8_t *lds, uint32_t addr)
 // chunks 4 kk + h and 4 kk + 2 + h.  With the XOR swizzle, chunk 2 kk + h of
 // a row sits at fbase ^ (kk << 5) and chunk 4 kk + h at fbase ^ (kk << 6).
 // The whole address is one XOR of fbase with a wave-uniform value, computed
-// at the read so that no per-k-step address stays live in a VGPR.
+// at the read so that no per-k-step address stays live in a VGPR.  Row block
+// i (rows r + 32 i) differs from block 0 only by 32 i rows (an immediate
+// offset of 4096 i bytes) and by bit 2 of the swizzle when i is odd
+// (((r + 32 i) >> 3) & 7 = ((r >> 3) + 4 i) & 7), i.e. by address bit 6.
 template <int FMT, int KSH = 5>
-__device__ __forceinline__ typename Fmt<FMT>::Frag read_frag(const uint8_t *lds, uint32_t fbase, uint32_t sel, int kk)
+__device__ __forceinline__ typename Fmt<FMT>::Frag read_frag(const uint8_t *lds, uint32_t fbase, uint32_t sel, int kk,
+                                                             int blk)
 {
+    const uint32_t flip = (uint32_t)(64 * (blk & 1)), off = (uint32_t)(32 * kRowBytes * blk);
     if constexpr (FMT == kMXFP8) {
-        const uint32_t x = fbase ^ (sel | (uint32_t)(kk << 6));
-        const i32x4 v0 = lds_read<i32x4>(lds, x), v1 = lds_read<i32x4>(lds, x ^ 32u);
+        const uint32_t x = fbase ^ (sel | ((uint32_t)(kk << 6) ^ flip));
+        const i32x4 v0 = lds_read<i32x4>(lds, x + off), v1 = lds_read<i32x4>(lds, (x ^ 32u) + off);
         return i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     } else {
-        return lds_read<typename Fmt<FMT>::Frag>(lds, fbase ^ (sel | (uint32_t)(kk << KSH)));
+        return lds_read<typename Fmt<FMT>::Frag>(lds, (fbase ^ (sel | ((uint32_t)(kk << KSH) ^ flip))) + off);
     }
 }
 
@@ -301,7 +322,7 @@ template <int FMT, class S>
 __device__ __forceinline__ void read_a(Frags<FMT, S> &f, int i, const uint8_t *lds, int slot, int kk,
                                        const Ctx<S> &c)
 {
-    f.a[i] = read_frag<FMT>(lds, c.fa[i], (uint32_t)(slot * S::kSlotA), kk);
+    f.a[i] = read_frag<FMT>(lds, c.fa, (uint32_t)(slot * S::kSlotA), kk, i);
 }
 
 template <int FMT, class S>
@@ -310,7 +331,7 @@ __device__ __forceinline__ void read_b(Frags<FMT, S> &f, int j, const uint8_t *l
 {
     // with A decoded in registers, B's k-step kk is chunk 4h + kk of the row
     constexpr int KSH = adirect<FMT, S>() ? 4 : 5;
-    f.b[j] = read_frag<FMT, KSH>(lds, c.fb[j], (uint32_t)(slot * S::kSlotB), kk);
+    f.b[j] = read_frag<FMT, KSH>(lds, c.fb, (uint32_t)(slot * S::kSlotB), kk, j);
 }
 
 // ------------------------------------------------------------------ scales
@@ -339,7 +360,7 @@ __device__ __forceinline__ void dma_scales(uint8_t *lds, int slot, const Target 
             const int row = d / WPR, word = d % WPR;
             const int o = ks * BPS + 4 * word;
             const uint32_t off = (uint32_t)(row * sld + o) | (o < sld ? 0u : kOOB);
-            const int dst = S::kLdsS + (is_a ? slot * S::TM * BPS : 2 * S::TM * BPS + slot * S::TN * BPS) + nn * 256;
+            const int dst = S::kLdsS + (is_a ? slot * S::TM * BPS : S::NS * S::TM * BPS + slot * S::TN * BPS) + nn * 256;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? tg.rsa : tg.rsb, (lds_void *)(lds + dst), 4, off, 0, 0,
                                                      0);
         }
@@ -390,7 +411,7 @@ __device__ __forceinline__ void store_scale_bytes(const ScaleBytes<FMT, S> &r, u
         if (u0 < S::TM + S::TN) {
             const bool is_a = u0 < S::TM;
             const int row = u0 + c.lane - (is_a ? 0 : S::TM);
-            uint8_t *dst = lds + S::kLdsS + (is_a ? slot * S::TM * BPS : 2 * S::TM * BPS + slot * S::TN * BPS) +
+            uint8_t *dst = lds + S::kLdsS + (is_a ? slot * S::TM * BPS : S::NS * S::TM * BPS + slot * S::TN * BPS) +
                            row * BPS;
 #pragma unroll
             for (int b = 0; b < BPS; ++b) dst[b] = (uint8_t)r.v[k][b];
@@ -623,12 +644,13 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[S::MB][S::NB], co
 
 // Epilogue through LDS (when N % 8 == 0 and D is 16-byte aligned): each wave
 // writes one 32-row block-row of its bf16 results into its own 32 x (NB*64)
-// byte buffer in the just-consumed A slot `xslot` (16-byte chunks XOR-swizzled
-// by row), reads it back row-major (CPR lanes per row) and stores whole
-// 16-byte chunks, so one store instruction covers 64/CPR full rows of the
-// wave's columns instead of 32 rows x 16 bytes.  The same wave's LDS writes
-// and reads execute in order; the caller meets a barrier before the slot is
-// refilled.
+// byte buffer in the just-consumed ring slot `xslot` (its A part, or A and B
+// parts for half of the waves each when the A part is too small; 16-byte
+// chunks XOR-swizzled by row), reads it back row-major (CPR lanes per row)
+// and stores whole 16-byte chunks, so one store instruction covers 64/CPR
+// full rows of the wave's columns instead of 32 rows x 16 bytes.  The same
+// wave's LDS writes and reads execute in order; the caller meets a barrier
+// before the slot is refilled.
 template <class S>
 __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[S::MB][S::NB], uint8_t *lds, int xslot,
                                                const Params &p, int m0, int n0, const Ctx<S> &c)
@@ -636,8 +658,13 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[S::MB][S::NB]
     constexpr int RB = S::NB * 64;          // bytes per staged row
     constexpr int CPR = RB / 16;            // 16-byte chunks per staged row
     constexpr int RPI = 64 / CPR;           // rows per read instruction
-    static_assert(S::NW * 32 * RB <= S::kSlotA, "epilogue buffers must fit in one A slot");
-    uint8_t *buf = lds + S::kLdsA + xslot * S::kSlotA + c.w * 32 * RB;
+    constexpr int WB = 32 * RB;             // bytes per wave buffer
+    constexpr bool SPLIT = S::NW * WB > S::kSlotA;
+    static_assert(!SPLIT || (S::NW / 2 * WB <= S::kSlotA && S::NW / 2 * WB <= S::kSlotB),
+                  "epilogue buffers must fit in one ring slot");
+    uint8_t *buf = !SPLIT           ? lds + S::kLdsA + xslot * S::kSlotA + c.w * WB
+                   : c.w < S::NW / 2 ? lds + S::kLdsA + xslot * S::kSlotA + c.w * WB
+                                     : lds + S::kLdsB + xslot * S::kSlotB + (c.w - S::NW / 2) * WB;
     const int nc = n0 + c.wn * (S::TN / S::WN);
 #pragma unroll
     for (int i = 0; i < S::MB; ++i) {
@@ -668,14 +695,28 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[S::MB][S::NB]
 
 // ------------------------------------------------------------------ kernel
 
-// End of a stage: this wave's LDS reads and writes are done and its loads
-// have landed; then all waves meet.  After it the slot just read may be
-// refilled and the slot just loaded may be read.
+// End of a stage: this wave's LDS reads and writes are done and all but its
+// newest `newer` memory operations have completed; then all waves meet.
+// Memory operations complete in order, so with the loads of the last NS-2
+// stages left in flight the next stage's slot (loaded NS-2 stages before
+// them) has landed for every wave: after the barrier it may be read, and the
+// slot just read may be refilled.
+template <int NEWER>
 __device__ __forceinline__ void stage_barrier()
 {
     DBS_FENCE();
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(NEWER) : "memory");
     DBS_FENCE();
+}
+
+// Loads a wave issues per stage, at least (operand wave-loads, plus its share
+// of the MX scale wave-loads); only the direct-to-LDS formats use rings
+// deeper than two slots.
+template <int FMT, class S>
+constexpr int stage_loads_min()
+{
+    constexpr int NSC = Fmt<FMT>::BPS > 0 ? (S::TM + S::TN) * Fmt<FMT>::BPS / 256 : 0;
+    return S::QA + S::QB + NSC / S::NW;
 }
 
 // Wait states between a tile's last MFMAs and any read of their results.
@@ -776,14 +817,14 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
     Frags<FMT, S> &nxt = CUR1 ? P.F0 : P.F1;
     constexpr bool ROLL = rolling<FMT, S>();
     Frags<FMT, S> &fa = ROLL ? P.F0 : cur;      // where this phase's A fragments are
-    constexpr int T = Fmt<FMT>::KK * MB * NB, NP = npieces<FMT, S>();
+    constexpr int T = kk_of<FMT, S>() * MB * NB, NP = npieces<FMT, S>();
     // pieces go out right after the first MFMAs of the stage, so that they
     // have the longest time to land before the stage's barrier
     constexpr int SP = 1;
     static_assert(NP <= T, "every piece needs an MFMA slot");
 
     // the k-step these MFMAs consume and its stage's scales
-    constexpr int KC = PH == 0 ? Fmt<FMT>::KK - 1 : PH - 1;
+    constexpr int KC = PH == 0 ? kk_of<FMT, S>() - 1 : PH - 1;
     const Scales<S> &sc = PH == 0 ? P.sprev : P.scur;
 
     if constexpr (RD) {
@@ -829,7 +870,7 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
 }
 
 // One stage read from ring slot `slot` while stage ks of target tg is loaded
-// into the other slot.  On entry F1 holds the last k-step of the previous
+// into slot `nxt` (the slot read by the previous stage).  On entry F1 holds the last k-step of the previous
 // stage (zeros at a tile's first stage): its MFMAs form the first phase,
 // interleaved with the loads and with the reads of k-step 0 of this stage.
 // The per-lane constants are re-declared opaque at every stage: addresses
@@ -839,18 +880,16 @@ template <class S>
 __device__ __forceinline__ void opaque(Ctx<S> &c)
 {
     asm volatile("" : "+v"(c.t), "+v"(c.lane), "+v"(c.r8lda), "+v"(c.x4), "+v"(c.sa), "+v"(c.sb));
-#pragma unroll
-    for (int i = 0; i < S::MB; ++i) asm volatile("" : "+v"(c.fa[i]));
-#pragma unroll
-    for (int j = 0; j < S::NB; ++j) asm volatile("" : "+v"(c.fb[j]));
+    asm volatile("" : "+v"(c.fa), "+v"(c.fb));
 }
 
 template <int FMT, class S, bool ALIGNED>
 __device__ __forceinline__ void stage(Pipe<FMT, S> &P, f32x16 (&acc)[S::MB][S::NB], uint8_t *lds, int slot,
-                                      const Params &p, Ctx<S> &c, const Target &tg, int ks)
+                                      int nxt, const Params &p, Ctx<S> &c, const Target &tg, int ks)
 {
-    constexpr int KK = Fmt<FMT>::KK;
-    const int nxt = slot ^ 1;
+    constexpr int KK = kk_of<FMT, S>();
+    static_assert(S::NS == 2 || (FMT != kNVFP4 && ALIGNED), "deeper rings need direct-to-LDS stages");
+    static_assert(KK == 2 || KK == 4, "stages hold 2 or 4 k-steps");
     opaque(c);
     phase<FMT, S, ALIGNED, 0, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt);
     phase<FMT, S, ALIGNED, 1, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt);
@@ -865,7 +904,7 @@ __device__ __forceinline__ void stage(Pipe<FMT, S> &P, f32x16 (&acc)[S::MB][S::N
 #pragma unroll
         for (int j = 0; j < S::NB; ++j) P.sprev.b[j][0] = P.scur.b[j][0];
     }
-    stage_barrier();
+    stage_barrier<(S::NS - 2) * stage_loads_min<FMT, S>()>();
 }
 
 // Buffer resources of output tile `tile`: A/B rows and their scale rows.
@@ -911,18 +950,11 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
     c.wm = c.w / S::WN;
     c.wn = c.w % S::WN;
     const int ra0 = c.wm * (S::TM / S::WM) + c.lr, rb0 = c.wn * (S::TN / S::WN) + c.lr;
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-        const int ra = ra0 + i * 32;
-        c.fa[i] = (uint32_t)(S::kLdsA + ra * kRowBytes + ((c.h ^ swz(ra)) << 4));
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        const int rb = rb0 + j * 32;
-        c.fb[j] = (uint32_t)(S::kLdsB + rb * kRowBytes + (((adirect<FMT, S>() ? 4 * c.h : c.h) ^ swz(rb)) << 4));
-    }
+    // (block offsets stay below the slot bits: row + 32 i < rows per slot)
+    c.fa = (uint32_t)(S::kLdsA + ra0 * kRowBytes + ((c.h ^ swz(ra0)) << 4));
+    c.fb = (uint32_t)(S::kLdsB + rb0 * kRowBytes + (((adirect<FMT, S>() ? 4 * c.h : c.h) ^ swz(rb0)) << 4));
     c.sa = (uint32_t)(S::kLdsS + ra0 * BPS);
-    c.sb = (uint32_t)(S::kLdsS + 2 * S::TM * BPS + rb0 * BPS);
+    c.sb = (uint32_t)(S::kLdsS + S::NS * S::TM * BPS + rb0 * BPS);
     c.r8lda = (uint32_t)((c.lane >> 3) * p.lda);
     c.x4 = (uint32_t)(((c.lane & 7) ^ (c.lane >> 3)) << 4);
 
@@ -942,15 +974,21 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) P.acur[i][kk] = f16x8{};
     }
-    // the tile whose stages the loads fetch: the current tile, and from its
-    // last stage on (which loads stage 0 of the next tile) the next one
+    // The load stream runs NS-1 stages ahead of the stage being computed,
+    // across the workgroup's tiles (a tile has at least NS-1 stages: the host
+    // picks a shallower ring otherwise); ld holds the resources of the tile
+    // it loads from (empty past the last tile).
     Target ld = tile_target<FMT, S>(p, tile);
 #pragma unroll
-    for (int q = 0; q < npieces<FMT, S>(); ++q) load_piece<FMT, S, ALIGNED>(P, lds, 0, ld, 0, p, c, q);
-    commit_stage<FMT, S, ALIGNED>(P, lds, 0, c);
+    for (int f = 0; f < S::NS - 1; ++f) {
+#pragma unroll
+        for (int q = 0; q < npieces<FMT, S>(); ++q) load_piece<FMT, S, ALIGNED>(P, lds, f, ld, f, p, c, q);
+        commit_stage<FMT, S, ALIGNED>(P, lds, f, c);
+    }
     __syncthreads();
 
-    int g = 0;   // stages done by this workgroup: ring slot = g & 1
+    int rs = 0;   // ring slot the next stage reads
+    int xs = 0;   // ring slot the last stage read
     for (;;) {
         f32x16 acc[MB][NB];
 #pragma unroll
@@ -976,13 +1014,18 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
         }
 
         const int next = tile + nwg;
-        for (int s = 0; s < p.nk; ++s, ++g) {
-            int ks = s + 1;
-            if (ks == p.nk) {
-                ld = next < ntiles ? tile_target<FMT, S>(p, next) : null_target();
-                ks = 0;
+        for (int s = 0; s < p.nk; ++s) {
+            // stage s loads stage s+NS-1 of the stream into the slot the
+            // previous stage read
+            int ks = s + S::NS - 1;
+            if (ks >= p.nk) {
+                ks -= p.nk;
+                if (ks == 0) ld = next < ntiles ? tile_target<FMT, S>(p, next) : null_target();
             }
-            stage<FMT, S, ALIGNED>(P, acc, lds, g & 1, p, c, ld, ks);
+            const int ls = rs == 0 ? S::NS - 1 : rs - 1;
+            stage<FMT, S, ALIGNED>(P, acc, lds, rs, ls, p, c, ld, ks);
+            xs = rs;
+            rs = rs + 1 == S::NS ? 0 : rs + 1;
         }
         phase<FMT, S, ALIGNED, 0, false, false>(acc, P, lds, p, c, 0, ld, 0, 0);
         mfma_drain<S>(acc);
@@ -995,7 +1038,7 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
             if (p.vec16) {
                 // the slot the last stage read is free until the next
                 // tile's first stage refills it
-                store_tile_lds<S>(acc, lds, (g & 1) ^ 1, p, tm * S::TM, tn * S::TN, c);
+                store_tile_lds<S>(acc, lds, xs, p, tm * S::TM, tn * S::TN, c);
                 asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             } else {
                 store_tile<S>(acc, p, tm * S::TM, tn * S::TN, c);
@@ -1008,19 +1051,40 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
     }
 }
 
+// K elements per stage of kernel (FMT, S)
+template <int FMT, class S>
+constexpr int stage_elems()
+{
+    return FMT == kBF16 || FMT == kNVFP4 ? kRowBytes / 2 : FMT == kMXFP8 ? kRowBytes : 2 * kRowBytes;
+}
+
+template <int FMT, bool ALIGNED, class S>
+hipError_t launch_one(const Params &p0, int grid, hipStream_t stream)
+{
+    Params p = p0;
+    p.nk = (p.K + stage_elems<FMT, S>() - 1) / stage_elems<FMT, S>();
+    hipLaunchKernelGGL((gemm_kernel<FMT, S, ALIGNED>), dim3(grid), dim3(S::kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int FMT, class S>
+constexpr int stages_of(int K) { return (K + stage_elems<FMT, S>() - 1) / stage_elems<FMT, S>(); }
+
 template <int FMT, class S>
 hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
 {
-    const dim3 g(grid);
     if constexpr (FMT == kMXFP8 || FMT == kMXFP4) {
         if (!p.scales_aligned) {
             using U = typename std::conditional<std::is_same<S, Square>::value, SquareW4, S>::type;
-            hipLaunchKernelGGL((gemm_kernel<FMT, U, false>), g, dim3(U::kThreads), 0, stream, p);
-            return hipGetLastError();
+            return launch_one<FMT, false, U>(p, grid, stream);
         }
     }
-    hipLaunchKernelGGL((gemm_kernel<FMT, S, true>), g, dim3(S::kThreads), 0, stream, p);
-    return hipGetLastError();
+    // stages that arrive entirely by direct-to-LDS loads get a deeper ring
+    // when every tile has enough stages to fill it
+    if constexpr (std::is_same<S, Skinny>::value && FMT != kNVFP4) {
+        if (stages_of<FMT, SkinnyDeep>(p.K) >= SkinnyDeep::NS - 1) return launch_one<FMT, true, SkinnyDeep>(p, grid, stream);
+    }
+    return launch_one<FMT, true, S>(p, grid, stream);
 }
 
 template <class S>

@@ -20,7 +20,7 @@ struct Params {
     int M, N, K;
     int lda;              // bytes per operand row (K * element bits / 8)
     int sld;              // scale bytes per row (K / block size), 0 for bf16
-    int nk;               // number of K stages
+    int nk;               // number of K stages (set by the launcher for the kernel it picks)
     int tiles_m, tiles_n;
     int group_m;          // tile rows per raster group
     int vec_store;        // 1 if D rows allow 8-byte stores (N % 4 == 0)
@@ -28,11 +28,6 @@ struct Params {
     int scales_aligned;   // 1 if every scale row starts on a 4-byte boundary
     float alpha;          // applied to the fp32 accumulator before rounding
 };
-
-// Elements of K consumed per pipeline stage for each format.
-constexpr int stage_k(int fmt) {
-    return fmt == kBF16 ? 64 : fmt == kMXFP8 ? 128 : fmt == kMXFP4 ? 256 : 64;
-}
 
 // Output tile shapes (rows of A x rows of B per tile).  Square tiles are the
 // default; skinny tiles serve problems whose square tiles would leave CUs idle.

@@ -50,12 +50,15 @@ RAGGED = [
     (1, 1, 32),           # single output
     (33, 7, 64),          # N not a multiple of 4 (element-wise stores)
     (512, 260, 4096),     # long K: many ring rotations
+    (256, 20000, 512),    # 313 tiles: several per workgroup through the stage stream; MXFP4 has
+                          # 2 stages per tile (the 3-slot ring's loads run a whole tile ahead)
 ]
 SQUARE_RAGGED = [
     (3000, 2900, 352),    # partial tiles, partial last stage; MX scale rows of 11 bytes
     (2900, 3000, 384),    # MX scale rows of whole dwords
     (2100, 4200, 640),    # partial last MXFP4 stage (640 = 2.5 x 256)
     (5000, 4100, 96),     # 340 tiles > one persistent round
+    (2600, 3000, 64),     # a single stage (BF16, NVFP4); MX scale rows of 2 bytes
 ]
 
 
