@@ -52,6 +52,8 @@ RAGGED = [
     (512, 260, 4096),     # long K: many ring rotations
     (256, 20000, 512),    # 313 tiles: several per workgroup through the stage stream; MXFP4 has
                           # 2 stages per tile (the 3-slot ring's loads run a whole tile ahead)
+    (300, 9000, 768),     # 282 tiles, ragged M and N; NVFP4 takes the raw-ring kernel (K % 256 == 0)
+                          # with three raw stages per tile, streamed across a workgroup's tiles
 ]
 SQUARE_RAGGED = [
     (3000, 2900, 352),    # partial tiles, partial last stage; MX scale rows of 11 bytes
@@ -154,7 +156,8 @@ def test_exact_permutation_square_tiles(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "nvfp4"])
-@pytest.mark.parametrize("shape", [(260, 300, 512), (3000, 2900, 512)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", [(260, 300, 512), (3000, 2900, 512), (256, 20000, 768)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_exact_pow2_scale_shift(fmt, shape):
     """Moving every A scale by a power of two (E8M0 code +3; E4M3 exponent
     field -3) scales every output by exactly that power."""
