@@ -179,8 +179,34 @@ struct Fmt<kMXFP4> {
 template <int FMT, class S>
 constexpr int kk_of() { return kRowBytes / Fmt<FMT>::KSB; }
 
-template <int FMT, class S>
-constexpr int lds_bytes() { return S::kLdsS + S::NS * (S::TM + S::TN) * Fmt<FMT>::BPS; }
+// How MX scales reach LDS (the kernels' SM parameter):
+//  kScalesRegs:  any row stride; thread-owned byte loads through registers
+//                into NS per-stage slots of (TM + TN) rows x BPS bytes;
+//  kScalesStage: rows of whole dwords; per-stage direct-to-LDS dword loads
+//                into the same per-stage slots;
+//  kScalesChunk: rows of whole dwords, two-slot rings with a whole number of
+//                chunks per tile; the scales of kScaleChunk / BPS consecutive
+//                stages (16 bytes per row: E4M3 4 stages, E2M1 2) form a
+//                chunk, kept in two alternating buffers of (TM + TN) rows x
+//                16 bytes.  During each stage of a chunk the next chunk's
+//                rows are loaded a portion at a time, four lanes per row, so
+//                a row costs one memory request per chunk instead of one per
+//                stage (a per-stage fetch of 4 or 8 bytes from each of the
+//                tile's 512 scale rows costs as many L2 requests as the
+//                stage's operand slabs).
+constexpr int kScalesRegs = 0, kScalesStage = 1, kScalesChunk = 2;
+constexpr int kScaleChunk = 16;
+
+template <int FMT>
+constexpr int scale_spc() { return Fmt<FMT>::BPS > 0 ? kScaleChunk / Fmt<FMT>::BPS : 1; }
+
+template <int FMT, class S, int SM>
+constexpr int lds_bytes()
+{
+    return Fmt<FMT>::BPS == 0     ? S::kLdsS
+           : SM == kScalesChunk ? S::kLdsS + 2 * (S::TM + S::TN) * kScaleChunk
+                                : S::kLdsS + S::NS * (S::TM + S::TN) * Fmt<FMT>::BPS;
+}
 
 // E4M3 fragments are 8 VGPRs: with 8 waves (256 VGPRs per wave) two full
 // sets do not fit beside the accumulators, so A fragments are single-buffered
@@ -309,6 +335,20 @@ __device__ __forceinline__ void read_scales(Scales<S> &sc, const uint8_t *lds, i
         read_scale_row<FMT>(sc.b[j], lds, c.sb + (uint32_t)(slot * S::TN * BPS + j * 32 * BPS));
 }
 
+// Chunked layout: stage j (0 .. scale_spc - 1) of the chunk in buffer `par`.
+template <int FMT, class S>
+__device__ __forceinline__ void read_scales_chunk(Scales<S> &sc, const uint8_t *lds, int par, int j, const Ctx<S> &c)
+{
+    constexpr int BPS = Fmt<FMT>::BPS;
+    const uint32_t o = (uint32_t)(par * (S::TM + S::TN) * kScaleChunk + j * BPS);
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i)
+        read_scale_row<FMT>(sc.a[i], lds, c.sa + o + (uint32_t)(i * 32 * kScaleChunk));
+#pragma unroll
+    for (int jj = 0; jj < S::NB; ++jj)
+        read_scale_row<FMT>(sc.b[jj], lds, c.sb + o + (uint32_t)(jj * 32 * kScaleChunk));
+}
+
 template <int FMT, class S>
 __device__ __forceinline__ void adjust_scales(Scales<S> &sc, const Ctx<S> &c)
 {
@@ -365,6 +405,29 @@ __device__ __forceinline__ void dma_scales(uint8_t *lds, int slot, const Target 
         const uint32_t off = (uint32_t)(row * sld + o) | (o < sld ? 0u : kOOB);
         const int dst = S::kLdsS + (is_a ? slot * S::TM * BPS : S::NS * S::TM * BPS + slot * S::TN * BPS) + nn * 256;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? tg.rsa : tg.rsb, (lds_void *)(lds + dst), 4, off, 0, 0, 0);
+    }
+}
+
+// Chunked scales: portion u (0 .. scale_spc - 1) of chunk `chunk` (bytes
+// 16 chunk .. 16 chunk + 15 of every row) into chunk buffer `par`: rows
+// u R .. (u + 1) R - 1 of the concatenated row list (A rows, then B rows;
+// R = (TM + TN) / scale_spc), 16 rows per dword wave-load, lane i taking
+// dword i % 4 of row i / 4.  Dwords past a row's end read zero.
+template <int FMT, class S>
+__device__ __forceinline__ void dma_scale_portion(uint8_t *lds, int par, const Target &stg, int chunk, int u,
+                                                  const Ctx<S> &c, int sld)
+{
+    constexpr int R = (S::TM + S::TN) / scale_spc<FMT>(), NLP = R / 16;
+    static_assert(NLP % S::NW == 0 && S::TM % 16 == 0, "portions split evenly over the waves");
+    const int o = chunk * kScaleChunk + 4 * (c.lane & 3);
+#pragma unroll
+    for (int k = 0; k < NLP / S::NW; ++k) {
+        const int row0 = u * R + (c.w + k * S::NW) * 16;      // wave-uniform
+        const bool is_a = row0 < S::TM;
+        const int r = (is_a ? row0 : row0 - S::TM) + (c.lane >> 2);
+        const uint32_t off = (uint32_t)(r * sld + o) | (o < sld ? 0u : kOOB);
+        const int dst = S::kLdsS + par * (S::TM + S::TN) * kScaleChunk + row0 * kScaleChunk;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? stg.rsa : stg.rsb, (lds_void *)(lds + dst), 4, off, 0, 0, 0);
     }
 }
 
@@ -771,9 +834,17 @@ struct Pipe {
 template <int FMT, class S>
 constexpr int npieces() { return FMT == kNVFP4 ? 1 : (S::QA > S::QB ? S::QA : S::QB); }
 
-template <int FMT, class S, bool ALIGNED>
+// Where a stage stands in the chunked-scale sequence: it reads stage j of
+// the chunk in buffer pc and loads portion j of chunk `lchunk` of the tile
+// whose scale rows start at stg (the next chunk) into buffer pc ^ 1.
+struct ChunkPos {
+    int pc, j, lchunk;
+};
+
+template <int FMT, class S, int SM>
 __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int slot, const Target &tg, int ks,
-                                           const Params &p, const Ctx<S> &c, int q)
+                                           const Params &p, const Ctx<S> &c, int q, const Target &stg,
+                                           const ChunkPos &cp)
 {
     if constexpr (FMT == kNVFP4) {
         load_fp4(P.fp4, tg, ks, c, p.lda, p.sld);
@@ -783,8 +854,10 @@ __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int sl
         if (q < S::QB) dma_b(lds, slot, tg, ks, c, q, p.lda);
         if constexpr (FMT == kMXFP8 || FMT == kMXFP4) {
             if (q == npieces<FMT, S>() - 1) {
-                if constexpr (ALIGNED)
+                if constexpr (SM == kScalesStage)
                     dma_scales<FMT>(lds, slot, tg, ks, c, p.sld);
+                else if constexpr (SM == kScalesChunk)
+                    dma_scale_portion<FMT>(lds, cp.pc ^ 1, stg, cp.lchunk, cp.j, c, p.sld);
                 else
                     load_scale_bytes(P.sbytes, tg, ks, c, p.sld);
             }
@@ -794,7 +867,7 @@ __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int sl
 
 // Register-staged parts of a stage (NVFP4 data, unaligned MX scales) go to
 // LDS before the stage's barrier.
-template <int FMT, class S, bool ALIGNED>
+template <int FMT, class S, int SM>
 __device__ __forceinline__ void commit_stage(Pipe<FMT, S> &P, uint8_t *lds, int slot, const Ctx<S> &c)
 {
     if constexpr (FMT == kNVFP4) store_fp4(P.fp4, lds, slot, c);
@@ -805,7 +878,7 @@ __device__ __forceinline__ void commit_stage(Pipe<FMT, S> &P, uint8_t *lds, int 
         for (int i = 0; i < S::MB; ++i) P.aprev[i] = P.acur[i][3];
         decode_fp4_a<S>(P.acur, P.fp4a);
     }
-    if constexpr ((FMT == kMXFP8 || FMT == kMXFP4) && !ALIGNED) store_scale_bytes(P.sbytes, lds, slot, c);
+    if constexpr ((FMT == kMXFP8 || FMT == kMXFP4) && SM == kScalesRegs) store_scale_bytes(P.sbytes, lds, slot, c);
 }
 
 // Phase PH of a stage (PH = 0 .. KK-1): the MB x NB MFMAs of one k-step —
@@ -814,9 +887,10 @@ __device__ __forceinline__ void commit_stage(Pipe<FMT, S> &P, uint8_t *lds, int 
 // into the other set (if RD).  With LOADS, the stage's load pieces are issued
 // between MFMAs: piece q after MFMA number q of the stage.  Rolling formats
 // keep A in F0 only: each A fragment is re-read right after its last MFMA.
-template <int FMT, class S, bool ALIGNED, int PH, bool RD, bool LOADS>
+template <int FMT, class S, int SM, int PH, bool RD, bool LOADS>
 __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> &P, uint8_t *lds, const Params &p,
-                                      const Ctx<S> &c, int rslot, const Target &tg, int ks, int lslot)
+                                      const Ctx<S> &c, int rslot, const Target &tg, int ks, int lslot,
+                                      const Target &stg, const ChunkPos &cp)
 {
     constexpr int MB = S::MB, NB = S::NB;
     constexpr bool CUR1 = PH == 0 || ((PH - 1) & 1);
@@ -846,7 +920,12 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
 #pragma unroll
             for (int j = 0; j < NB; ++j) read_b(nxt, j, lds, rslot, PH, c);
         }
-        if constexpr (Fmt<FMT>::BPS > 0 && PH == 0) read_scales<FMT>(P.scur, lds, rslot, c);
+        if constexpr (Fmt<FMT>::BPS > 0 && PH == 0) {
+            if constexpr (SM == kScalesChunk)
+                read_scales_chunk<FMT, S>(P.scur, lds, cp.pc, cp.j, c);
+            else
+                read_scales<FMT>(P.scur, lds, rslot, c);
+        }
     }
     if constexpr (Fmt<FMT>::BPS > 0 && PH == 1) adjust_scales<FMT>(P.scur, c);
     DBS_FENCE();
@@ -863,7 +942,7 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
                 const int pos = base + i * NB + j;   // compile-time after unrolling
                 if ((pos + 1) % SP == 0 && (pos + 1) / SP - 1 < NP) {
                     DBS_FENCE();
-                    load_piece<FMT, S, ALIGNED>(P, lds, lslot, tg, ks, p, c, (pos + 1) / SP - 1);
+                    load_piece<FMT, S, SM>(P, lds, lslot, tg, ks, p, c, (pos + 1) / SP - 1, stg, cp);
                     DBS_FENCE();
                 }
             }
@@ -890,21 +969,23 @@ __device__ __forceinline__ void opaque(Ctx<S> &c)
     asm volatile("" : "+v"(c.fa), "+v"(c.fb));
 }
 
-template <int FMT, class S, bool ALIGNED>
+template <int FMT, class S, int SM>
 __device__ __forceinline__ void stage(Pipe<FMT, S> &P, f32x16 (&acc)[S::MB][S::NB], uint8_t *lds, int slot,
-                                      int nxt, const Params &p, Ctx<S> &c, const Target &tg, int ks)
+                                      int nxt, const Params &p, Ctx<S> &c, const Target &tg, int ks, const Target &stg,
+                                      const ChunkPos &cp)
 {
     constexpr int KK = kk_of<FMT, S>();
-    static_assert(S::NS == 2 || (FMT != kNVFP4 && ALIGNED), "deeper rings need direct-to-LDS stages");
+    static_assert(S::NS == 2 || (FMT != kNVFP4 && SM != kScalesRegs), "deeper rings need direct-to-LDS stages");
+    static_assert(SM != kScalesChunk || S::NS == 2, "chunked scales run on two-slot rings");
     static_assert(KK == 2 || KK == 4, "stages hold 2 or 4 k-steps");
     opaque(c);
-    phase<FMT, S, ALIGNED, 0, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt);
-    phase<FMT, S, ALIGNED, 1, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt);
+    phase<FMT, S, SM, 0, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt, stg, cp);
+    phase<FMT, S, SM, 1, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt, stg, cp);
     if constexpr (KK > 2) {
-        phase<FMT, S, ALIGNED, 2, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt);
-        phase<FMT, S, ALIGNED, 3, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt);
+        phase<FMT, S, SM, 2, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt, stg, cp);
+        phase<FMT, S, SM, 3, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt, stg, cp);
     }
-    commit_stage<FMT, S, ALIGNED>(P, lds, nxt, c);
+    commit_stage<FMT, S, SM>(P, lds, nxt, c);
     if constexpr (Fmt<FMT>::BPS > 0) {
 #pragma unroll
         for (int i = 0; i < S::MB; ++i) P.sprev.a[i][0] = P.scur.a[i][0];
@@ -941,10 +1022,10 @@ __device__ __forceinline__ Target null_target()
     return t;
 }
 
-template <int FMT, class S, bool ALIGNED>
+template <int FMT, class S, int SM>
 __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<FMT, S>()];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<FMT, S, SM>()];
     constexpr int BPS = Fmt<FMT>::BPS;
     constexpr int MB = S::MB, NB = S::NB;
 
@@ -960,8 +1041,13 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
     // (block offsets stay below the slot bits: row + 32 i < rows per slot)
     c.fa = (uint32_t)(S::kLdsA + ra0 * kRowBytes + ((c.h ^ swz(ra0)) << 4));
     c.fb = (uint32_t)(S::kLdsB + rb0 * kRowBytes + (((adirect<FMT, S>() ? 4 * c.h : c.h) ^ swz(rb0)) << 4));
-    c.sa = (uint32_t)(S::kLdsS + ra0 * BPS);
-    c.sb = (uint32_t)(S::kLdsS + S::NS * S::TM * BPS + rb0 * BPS);
+    if constexpr (SM == kScalesChunk) {
+        c.sa = (uint32_t)(S::kLdsS + ra0 * kScaleChunk);
+        c.sb = (uint32_t)(S::kLdsS + (S::TM + rb0) * kScaleChunk);
+    } else {
+        c.sa = (uint32_t)(S::kLdsS + ra0 * BPS);
+        c.sb = (uint32_t)(S::kLdsS + S::NS * S::TM * BPS + rb0 * BPS);
+    }
     c.r8lda = (uint32_t)((c.lane >> 3) * p.lda);
     c.x4 = (uint32_t)(((c.lane & 7) ^ (c.lane >> 3)) << 4);
 
@@ -986,13 +1072,24 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
     // picks a shallower ring otherwise); ld holds the resources of the tile
     // it loads from (empty past the last tile).
     Target ld = tile_target<FMT, S>(p, tile);
+    // chunked scales: stg holds the scale rows the portion loads read from,
+    // which move to the next tile a chunk ahead of the operand loads; the
+    // first tile's chunk 0 goes to buffer 0 now
+    constexpr int SPC = scale_spc<FMT>();
+    Target stg = ld;
+    ChunkPos cp{0, 0, 0};
 #pragma unroll
     for (int f = 0; f < S::NS - 1; ++f) {
 #pragma unroll
-        for (int q = 0; q < npieces<FMT, S>(); ++q) load_piece<FMT, S, ALIGNED>(P, lds, f, ld, f, p, c, q);
-        commit_stage<FMT, S, ALIGNED>(P, lds, f, c);
+        for (int q = 0; q < npieces<FMT, S>(); ++q) load_piece<FMT, S, SM>(P, lds, f, ld, f, p, c, q, stg, cp);
+        commit_stage<FMT, S, SM>(P, lds, f, c);
+    }
+    if constexpr (SM == kScalesChunk) {
+#pragma unroll
+        for (int u = 0; u < SPC; ++u) dma_scale_portion<FMT>(lds, 0, ld, 0, u, c, p.sld);
     }
     __syncthreads();
+    int pc = 0;   // chunk buffer of the stage being computed
 
     int rs = 0;   // ring slot the next stage reads
     int xs = 0;   // ring slot the last stage read
@@ -1030,11 +1127,24 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
                 if (ks == 0) ld = next < ntiles ? tile_target<FMT, S>(p, next) : null_target();
             }
             const int ls = rs == 0 ? S::NS - 1 : rs - 1;
-            stage<FMT, S, ALIGNED>(P, acc, lds, rs, ls, p, c, ld, ks);
+            if constexpr (SM == kScalesChunk) {
+                // a tile holds a whole number of chunks; stage s loads
+                // portion s % SPC of the next chunk, which past the tile's
+                // last chunk is the next tile's first
+                cp.pc = pc;
+                cp.j = s % SPC;
+                cp.lchunk = s / SPC + 1;
+                if (cp.lchunk * SPC == p.nk) {
+                    cp.lchunk = 0;
+                    if (cp.j == 0) stg = next < ntiles ? tile_target<FMT, S>(p, next) : null_target();
+                }
+            }
+            stage<FMT, S, SM>(P, acc, lds, rs, ls, p, c, ld, ks, stg, cp);
+            if constexpr (SM == kScalesChunk) pc ^= cp.j == SPC - 1 ? 1 : 0;
             xs = rs;
             rs = rs + 1 == S::NS ? 0 : rs + 1;
         }
-        phase<FMT, S, ALIGNED, 0, false, false>(acc, P, lds, p, c, 0, ld, 0, 0);
+        phase<FMT, S, SM, 0, false, false>(acc, P, lds, p, c, 0, ld, 0, 0, stg, cp);
         mfma_drain<S>(acc);
 
         int tm, tn;
@@ -1326,12 +1436,12 @@ constexpr int stage_elems()
     return FMT == kBF16 || FMT == kNVFP4 ? kRowBytes / 2 : FMT == kMXFP8 ? kRowBytes : 2 * kRowBytes;
 }
 
-template <int FMT, bool ALIGNED, class S>
+template <int FMT, int SM, class S>
 hipError_t launch_one(const Params &p0, int grid, hipStream_t stream)
 {
     Params p = p0;
     p.nk = (p.K + stage_elems<FMT, S>() - 1) / stage_elems<FMT, S>();
-    hipLaunchKernelGGL((gemm_kernel<FMT, S, ALIGNED>), dim3(grid), dim3(S::kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<FMT, S, SM>), dim3(grid), dim3(S::kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1344,7 +1454,7 @@ hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
     if constexpr (FMT == kMXFP8 || FMT == kMXFP4) {
         if (!p.scales_aligned) {
             using U = typename std::conditional<std::is_same<S, Square>::value, SquareW4, S>::type;
-            return launch_one<FMT, false, U>(p, grid, stream);
+            return launch_one<FMT, kScalesRegs, U>(p, grid, stream);
         }
     }
     // NVFP4 on skinny tiles: the raw-ring kernel when raw stages of 256 K
@@ -1362,9 +1472,16 @@ hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
     // stages that arrive entirely by direct-to-LDS loads get a deeper ring
     // when every tile has enough stages to fill it
     if constexpr (std::is_same<S, Skinny>::value && FMT != kNVFP4) {
-        if (stages_of<FMT, SkinnyDeep>(p.K) >= SkinnyDeep::NS - 1) return launch_one<FMT, true, SkinnyDeep>(p, grid, stream);
+        if (stages_of<FMT, SkinnyDeep>(p.K) >= SkinnyDeep::NS - 1)
+            return launch_one<FMT, kScalesStage, SkinnyDeep>(p, grid, stream);
     }
-    return launch_one<FMT, true, S>(p, grid, stream);
+    // MX scales in chunks when a tile's stages split into whole chunks (and
+    // a chunk's portions into whole wave-loads per wave)
+    if constexpr ((FMT == kMXFP8 || FMT == kMXFP4) && S::NS == 2 &&
+                  ((S::TM + S::TN) / scale_spc<FMT>() / 16) % S::NW == 0) {
+        if (stages_of<FMT, S>(p.K) % scale_spc<FMT>() == 0) return launch_one<FMT, kScalesChunk, S>(p, grid, stream);
+    }
+    return launch_one<FMT, kScalesStage, S>(p, grid, stream);
 }
 
 template <class S>

@@ -143,12 +143,16 @@ def test_exact_identity_permutation(fmt, permute):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_exact_permutation_square_tiles(fmt):
-    """The permutation test at a shape that takes 256 x 256 tiles (and more
-    than one persistent round), checked bit for bit on sampled entries."""
-    _gpu.say(f"[exact] {fmt} permutation 3000x2944x2944")
+@pytest.mark.parametrize("mk", [(3000, 2944), (4100, 4608)], ids=lambda s: "x".join(map(str, s)))
+def test_exact_permutation_square_tiles(fmt, mk):
+    """The permutation test at shapes that take 256 x 256 tiles, checked bit
+    for bit on sampled entries.  4100 x 4608 x 4608: 306 tiles (some
+    workgroups take two), and K = 4608 gives MXFP8 36 and MXFP4 18 stages per
+    tile, whole chunks of stage scales (4 and 2 stages)."""
+    M, K = mk
+    _gpu.say(f"[exact] {fmt} permutation {M}x{K}x{K}")
     rng = np.random.default_rng(33)
-    w = _identity_w(fmt, 3000, 2944, rng, True)
+    w = _identity_w(fmt, M, K, rng, True)
     D = _gpu.run(fmt, w)
     torch.cuda.synchronize()
     em, en = synth.sample_entries(34, w["M"], w["N"], 4096)
