@@ -138,6 +138,7 @@ unsigned orc_encode_bf16(double x)
     if (ex < -126) ex = -126;           /* subnormal binade */
     double q = ldexp(1.0, ex - 7);      /* 7 stored mantissa bits */
     double r = rint(a / q) * q;         /* default rounding mode: nearest even */
+    if (r == 0.0) return sign;          /* below half the smallest subnormal */
     if (r >= ldexp(1.0, 128)) return sign | 0x7F80u;
     frexp(r, &e);
     ex = e - 1;

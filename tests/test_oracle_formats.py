@@ -61,6 +61,11 @@ def test_saturation_and_signed_zero():
 def test_bf16_encoder_matches_numpy_rounding():
     rng = np.random.default_rng(0)
     x = rng.standard_normal(20000).astype(np.float32) * np.float32(3.0)
+    # and the bottom of the range: fp32 subnormals (some round to the
+    # smallest bf16 subnormal, some to +-0), signed zeros, the smallest normals
+    tiny = np.array([1e-40, -3e-41, 1.4e-45, -1.4e-45, 2.0 ** -134, 2.0 ** -134 * 1.5, 2.0 ** -133,
+                     -2.0 ** -133 * 0.75, 1.1754944e-38, 1e-38, 0.0, -0.0], np.float32)
+    x = np.concatenate([x, tiny, -tiny, rng.standard_normal(4000).astype(np.float32) * np.float32(1e-39)])
     # numpy reference: fp32 -> bf16 RNE via integer rounding of the bit pattern
     b = x.view(np.uint32).astype(np.uint64)
     ref = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
