@@ -24,7 +24,7 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["gemm_bf16", "gemm_mx", "gemm_nvfp4", "lib", "LIB_PATH", "DbsError",
+__all__ = ["gemm_bf16", "gemm_mx", "gemm_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError",
            "DBS_OK", "DBS_EINVAL", "DBS_EUNSUPPORTED", "DBS_EHIP", "K_MAJOR", "MN_MAJOR",
            "E4M3", "E2M1", "status_str"]
 
@@ -60,6 +60,12 @@ def lib() -> ctypes.CDLL:
         L.gemm_mx.restype = I
         L.gemm_nvfp4.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P]
         L.gemm_nvfp4.restype = I
+        L.quant_mx.argtypes = [I, P, I64, I64, P, P, P]
+        L.quant_mx.restype = I
+        L.quant_nvfp4.argtypes = [P, I64, I64, P, P, P, P]
+        L.quant_nvfp4.restype = I
+        L.quant_bf16.argtypes = [P, I64, P, P]
+        L.quant_bf16.restype = I
         L.dbs_status_str.argtypes = [I]
         L.dbs_status_str.restype = ctypes.c_char_p
         L.dbs_last_error.argtypes = []
@@ -147,4 +153,40 @@ def gemm_nvfp4(A: torch.Tensor, sA: torch.Tensor, tA: float, B: torch.Tensor, sB
     out = _out(out, M, N, A)
     _check(lib().gemm_nvfp4(pa, psa, float(tA), pb, psb, float(tB), ctypes.c_void_p(out.data_ptr()),
                             M, N, K, K_MAJOR, K_MAJOR, _stream(A)))
+    return out
+
+
+# ---- quantisers (fp32 -> GEMM input formats, on the GPU) ----------------------
+
+def quant_mx(elem: str, x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """fp32 x (rows, K) -> (codes, E8M0 scales per 32): codes (rows, K) uint8
+    for elem='e4m3', (rows, K/2) packed for elem='e2m1'; scales (rows, K/32)."""
+    code = _ELEM[elem]
+    rows, K = x.shape
+    px = _dev(x, "x", (torch.float32,), (rows, K))
+    codes = torch.empty((rows, K // 2 if elem == "e2m1" else K), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().quant_mx(code, px, rows, K, ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                          _stream(x)))
+    return codes, scales
+
+
+def quant_nvfp4(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """fp32 x (rows, K) -> (packed E2M1 codes (rows, K/2), E4M3 scales per 16
+    (rows, K/16), tensor scale t as a one-element fp32 GPU tensor)."""
+    rows, K = x.shape
+    px = _dev(x, "x", (torch.float32,), (rows, K))
+    codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, K // 16), dtype=torch.uint8, device=x.device)
+    t = torch.empty((1,), dtype=torch.float32, device=x.device)
+    _check(lib().quant_nvfp4(px, rows, K, ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                             ctypes.c_void_p(t.data_ptr()), _stream(x)))
+    return codes, scales, t
+
+
+def quant_bf16(x: torch.Tensor) -> torch.Tensor:
+    """fp32 x -> bf16 (round to nearest even), same shape."""
+    px = _dev(x, "x", (torch.float32,), tuple(x.shape))
+    out = torch.empty(tuple(x.shape), dtype=torch.bfloat16, device=x.device)
+    _check(lib().quant_bf16(px, x.numel(), ctypes.c_void_p(out.data_ptr()), _stream(x)))
     return out

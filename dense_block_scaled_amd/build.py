@@ -2,7 +2,7 @@
 
     python -m dense_block_scaled_amd.build
 
-hipcc compiles the kernels (csrc/gemm.hip) and the ABI layer (csrc/dbs.cpp)
+hipcc compiles the kernels (csrc/gemm.hip, csrc/quant.hip) and the ABI layer (csrc/dbs.cpp)
 in-tree; no GPU is needed to build.  Packed-fp32 VALU instructions are turned
 off for the device code.
 """
@@ -30,7 +30,7 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> Path:
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-function", f"-I{ROOT / 'include'}", f"-I{CSRC}",
            *DEVICE_FLAGS, *(extra or []),
-           str(CSRC / "gemm.hip"), str(CSRC / "dbs.cpp"), "-o", tmp]
+           str(CSRC / "gemm.hip"), str(CSRC / "quant.hip"), str(CSRC / "dbs.cpp"), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     try:

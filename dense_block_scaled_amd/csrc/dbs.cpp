@@ -142,6 +142,61 @@ dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA, const void *B,
     return run(dbs::kNVFP4, A, sA, B, sB, D, M, N, K, tA * tB, 4, 16, stream);
 }
 
+// ---- quantisers ----------------------------------------------------------------
+
+static dbs_status check_quant(const float *x, const void *codes, int64_t rows, int64_t K, int64_t block)
+{
+    if (!x || !codes) return fail(DBS_EINVAL, "null pointer argument");
+    if (rows <= 0 || K <= 0) return fail(DBS_EINVAL, "rows and K must be positive");
+    if (K % block) return fail(DBS_EINVAL, "K must be a multiple of the block size");
+    if (rows > (int64_t(1) << 31) || K > (int64_t(1) << 31) || rows * K > (int64_t(1) << 40))
+        return fail(DBS_EINVAL, "array too large");
+    if (!aligned(x, 16) || !aligned(codes, 16)) return fail(DBS_EINVAL, "x and codes must be 16-byte aligned");
+    return DBS_OK;
+}
+
+dbs_status quant_mx(dbs_mx_elem elem, const float *x, int64_t rows, int64_t K, void *codes, uint8_t *scales,
+                    hipStream_t stream)
+{
+    if (elem != DBS_E4M3 && elem != DBS_E2M1) return fail(DBS_EINVAL, "mx: unknown element format");
+    dbs_status st = check_quant(x, codes, rows, K, 32);
+    if (st != DBS_OK) return st;
+    if (!scales) return fail(DBS_EINVAL, "null pointer argument");
+    int cus = 0;
+    if ((st = device_cus(&cus)) != DBS_OK) return st;
+    hipError_t e = dbs::launch_quant_mx(elem == DBS_E4M3, x, rows * K, static_cast<uint8_t *>(codes), scales, cus, stream);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    g_err[0] = '\0';
+    return DBS_OK;
+}
+
+dbs_status quant_nvfp4(const float *x, int64_t rows, int64_t K, void *codes, uint8_t *scales, float *t,
+                       hipStream_t stream)
+{
+    dbs_status st = check_quant(x, codes, rows, K, 16);
+    if (st != DBS_OK) return st;
+    if (!scales || !t) return fail(DBS_EINVAL, "null pointer argument");
+    if (!aligned(t, 4)) return fail(DBS_EINVAL, "t must be 4-byte aligned");
+    int cus = 0;
+    if ((st = device_cus(&cus)) != DBS_OK) return st;
+    hipError_t e = dbs::launch_quant_nvfp4(x, rows * K, static_cast<uint8_t *>(codes), scales, t, cus, stream);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    g_err[0] = '\0';
+    return DBS_OK;
+}
+
+dbs_status quant_bf16(const float *x, int64_t n, void *out, hipStream_t stream)
+{
+    dbs_status st = check_quant(x, out, 1, n, 8);
+    if (st != DBS_OK) return st;
+    int cus = 0;
+    if ((st = device_cus(&cus)) != DBS_OK) return st;
+    hipError_t e = dbs::launch_quant_bf16(x, n, static_cast<uint16_t *>(out), cus, stream);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    g_err[0] = '\0';
+    return DBS_OK;
+}
+
 const char *dbs_status_str(dbs_status st)
 {
     switch (st) {

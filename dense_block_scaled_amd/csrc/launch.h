@@ -1,5 +1,5 @@
 // launch.h -- internal interface between the C ABI (dbs.cpp) and the gfx950
-// kernels (gemm.hip).  Not installed; callers use include/dbs.h.
+// kernels (gemm.hip, quant.hip).  Not installed; callers use include/dbs.h.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -36,5 +36,15 @@ constexpr int kSquareTM = 256, kSquareTN = 256;
 constexpr int kSkinnyTM = 256, kSkinnyTN = 64;
 
 hipError_t launch_gemm(int fmt, int shape, const Params &p, int grid, hipStream_t stream);
+
+// Quantisers (quant.hip): n elements of a row-major array whose rows are whole
+// blocks (n a multiple of 32 for MX, 16 for NVFP4, 8 for bf16); x, codes and
+// out 16-byte aligned.  NVFP4 uses *t as the tensor-amax accumulator and
+// leaves the tensor scale there.
+hipError_t launch_quant_mx(bool e4m3, const float *x, int64_t n, uint8_t *codes, uint8_t *scales, int cus,
+                           hipStream_t stream);
+hipError_t launch_quant_nvfp4(const float *x, int64_t n, uint8_t *codes, uint8_t *scales, float *t, int cus,
+                              hipStream_t stream);
+hipError_t launch_quant_bf16(const float *x, int64_t n, uint16_t *out, int cus, hipStream_t stream);
 
 }  // namespace dbs

@@ -1,0 +1,260 @@
+// quant.hip -- gfx950 kernels that quantise fp32 operands into the GEMM's
+// input formats (the step upstream of the block-scaled GEMM):
+//
+//   MXFP8 / MXFP4: per block of 32 consecutive K elements, the E8M0 scale
+//     2^e with e = floor(log2(amax / emax)) (emax = 448 for E4M3, 6 for E2M1;
+//     e clamped to [-127, 127]; an all-zero block gets scale 1), then each
+//     element x -> nearest E4M3 / E2M1 value of x * 2^-e.  This is the scale
+//     rule stated with the workloads of the "ThunderKittens 2.0" MXFP8 GEMM
+//     (section 2.1: an E8M0 scale per 32 elements) and the OCP MX v1.0
+//     definition of the scale as a power of two.
+//   NVFP4: one fp32 tensor scale t = amax / (6 * 448) (t = 1 when the tensor
+//     is zero), per block of 16 the E4M3 scale s = nearest(amax_block / (6 t)),
+//     then each element x -> nearest E2M1 value of x / (s * t); every step in
+//     fp32 with correctly rounded operations.
+//   BF16: fp32 -> bf16, round to nearest even.
+//
+// "Nearest" is round-to-nearest with ties to the even code (the code with its
+// lowest bit clear), saturating at the largest finite value (448, 6) and
+// keeping the sign of zero.  Inputs must be finite.
+//
+// All kernels are bandwidth-bound streams over the flat element array
+// (K is a multiple of the block size, so blocks never straddle rows): four
+// lanes per MX block or two per NVFP4 block, eight consecutive elements per
+// lane read as two 16-byte loads, block maxima combined across the lanes
+// with cross-lane moves, codes written as one 8-byte (E4M3) or 4-byte (E2M1)
+// store per lane.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace dbs {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// |x| rounded to the nearest E4M3 code (0..0x7E), ties to even, saturating.
+// The grid step in x's binade is 2^(E-3) for x >= 2^-6 (E = its exponent),
+// 2^-9 below (subnormals); rint() of x / step in fp32 is exact and rounds
+// ties to even, and the code of a grid value v is v / 2^-9 below 2^-6 and
+// ((E + 7) << 3) + mantissa above.
+__device__ __forceinline__ uint32_t enc_e4m3_abs(float a)
+{
+    if (a >= 448.0f) return 0x7Eu;
+    int E;
+    (void)__builtin_frexpf(a, &E);          // a in [2^(E-1), 2^E)
+    const int e = a < 0x1p-6f ? -6 : E - 1;
+    const float v = __builtin_rintf(__builtin_ldexpf(a, 3 - e)) ;   // grid units of 2^(e-3)
+    // v in [0, 16]; v == 16 moves to the next binade (mantissa 0)
+    if (e == -6 && v < 8.0f) return (uint32_t)v;                   // subnormal (or zero)
+    const int ee = v >= 16.0f ? e + 1 : e;
+    const uint32_t m = v >= 16.0f ? 0u : (uint32_t)v - 8u;
+    const uint32_t code = ((uint32_t)(ee + 7) << 3) | m;
+    return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// |x| rounded to the nearest E2M1 code (0..7), ties to even, saturating.
+// Values 0, 0.5, 1, 1.5, 2, 3, 4, 6: step 0.5 below 2, 1 in [2, 4), 2 above.
+__device__ __forceinline__ uint32_t enc_e2m1_abs(float a)
+{
+    if (a >= 6.0f) return 7u;
+    if (a < 2.0f) return (uint32_t)__builtin_rintf(a * 2.0f);           // 0..4 -> codes 0..4 (4 = 2.0)
+    if (a < 4.0f) return 2u + (uint32_t)__builtin_rintf(a);             // 2..4 -> codes 4..6
+    return 4u + (uint32_t)__builtin_rintf(a * 0.5f);                    // 2..3 -> codes 6..7
+}
+
+__device__ __forceinline__ uint32_t sign_of(float x) { return __builtin_bit_cast(uint32_t, x) >> 31; }
+
+__device__ __forceinline__ uint32_t enc_e4m3(float x) { return (sign_of(x) << 7) | enc_e4m3_abs(__builtin_fabsf(x)); }
+__device__ __forceinline__ uint32_t enc_e2m1(float x) { return (sign_of(x) << 3) | enc_e2m1_abs(__builtin_fabsf(x)); }
+
+// E4M3 code (finite, non-negative) -> its fp32 value.
+__device__ __forceinline__ float dec_e4m3_pos(uint32_t c)
+{
+    const uint32_t e = (c >> 3) & 0xF, m = c & 7;
+    return e == 0 ? __builtin_ldexpf((float)m, -9) : __builtin_ldexpf((float)(8 + m), (int)e - 10);
+}
+
+// Maximum over the `lanes` consecutive lanes that share a block (lanes = 2
+// or 4, groups aligned to it).
+template <int LANES>
+__device__ __forceinline__ float group_max(float v)
+{
+    v = __builtin_fmaxf(v, __shfl_xor(v, 1));
+    if constexpr (LANES == 4) v = __builtin_fmaxf(v, __shfl_xor(v, 2));
+    return v;
+}
+
+// e = floor(log2(amax / emax)) for amax > 0, exactly: amax = f 2^E with f in
+// [1, 2) (frexp gives f/2 in [0.5, 1)); emax = 1.75 * 2^8 (E4M3) or
+// 1.5 * 2^2 (E2M1).
+template <bool E4M3>
+__device__ __forceinline__ int mx_exponent(float amax)
+{
+    int E;
+    const float f = 2.0f * __builtin_frexpf(amax, &E);
+    --E;
+    return E4M3 ? E - 8 - (f < 1.75f ? 1 : 0) : E - 2 - (f < 1.5f ? 1 : 0);
+}
+
+// Elements 8 l .. 8 l + 7 of the flat array for lane index l (grid-stride).
+template <bool E4M3>
+__global__ __launch_bounds__(256) void quant_mx_kernel(const float *__restrict__ x, uint8_t *__restrict__ codes,
+                                                       uint8_t *__restrict__ scales, int64_t nlanes)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t l = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; l - (threadIdx.x & 3) < nlanes; l += stride) {
+        // groups of four lanes stay together: nlanes is a multiple of 4 and
+        // the loop bound is taken at the group's first lane
+        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(x + 8 * l);
+        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(x + 8 * l + 4);
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(v0[i]), __builtin_fabsf(v1[i])));
+        a = group_max<4>(a);
+        int e = a > 0.0f ? mx_exponent<E4M3>(a) : 0;
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+        if ((threadIdx.x & 3) == 0) scales[l >> 2] = (uint8_t)(e + 127);
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            y[i] = __builtin_ldexpf(v0[i], -e);
+            y[4 + i] = __builtin_ldexpf(v1[i], -e);
+        }
+        if constexpr (E4M3) {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo |= enc_e4m3(y[i]) << (8 * i);
+                hi |= enc_e4m3(y[4 + i]) << (8 * i);
+            }
+            *reinterpret_cast<uint2 *>(codes + 8 * l) = uint2{lo, hi};
+        } else {
+            uint32_t w = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w |= enc_e2m1(y[i]) << (4 * i);
+            *reinterpret_cast<uint32_t *>(codes + 4 * l) = w;
+        }
+    }
+}
+
+// Tensor amax of n elements (n a multiple of 8) into *amax_bits as the bit
+// pattern of a non-negative float (ordered like an unsigned integer); the
+// caller zeroes it first.
+__global__ __launch_bounds__(256) void amax_kernel(const float *__restrict__ x, int64_t n8, uint32_t *amax_bits)
+{
+    float a = 0.0f;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t l = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; l < n8; l += stride) {
+        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(x + 8 * l);
+        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(x + 8 * l + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(v0[i]), __builtin_fabsf(v1[i])));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, o));
+    if ((threadIdx.x & 63) == 0) atomicMax(amax_bits, __builtin_bit_cast(uint32_t, a));
+}
+
+__global__ void zero_kernel(uint32_t *p) { *p = 0u; }
+
+// t = amax / 2688 (1 for a zero tensor), in fp32, correctly rounded.
+__device__ __forceinline__ float tensor_scale(uint32_t amax_bits)
+{
+    const float amax = __builtin_bit_cast(float, amax_bits);
+    return amax > 0.0f ? __fdiv_rn(amax, 2688.0f) : 1.0f;
+}
+
+// NVFP4 blocks of 16: two lanes per block, eight elements each.
+__global__ __launch_bounds__(256) void quant_nvfp4_kernel(const float *__restrict__ x, uint8_t *__restrict__ codes,
+                                                          uint8_t *__restrict__ scales, int64_t nlanes,
+                                                          const uint32_t *amax_bits)
+{
+    const float t = tensor_scale(*amax_bits);
+    const float six_t = __fmul_rn(6.0f, t);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t l = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; l - (threadIdx.x & 1) < nlanes; l += stride) {
+        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(x + 8 * l);
+        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(x + 8 * l + 4);
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(v0[i]), __builtin_fabsf(v1[i])));
+        a = group_max<2>(a);
+        const uint32_t sc = enc_e4m3(__fdiv_rn(a, six_t));
+        if ((threadIdx.x & 1) == 0) scales[l >> 1] = (uint8_t)sc;
+        const float denom = __fmul_rn(dec_e4m3_pos(sc & 0x7F), t);
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float xi = i < 4 ? v0[i] : v1[i - 4];
+            const float q = denom > 0.0f ? __fdiv_rn(xi, denom) : xi * 0.0f;
+            w |= enc_e2m1(q) << (4 * i);
+        }
+        *reinterpret_cast<uint32_t *>(codes + 4 * l) = w;
+    }
+}
+
+// *t: the tensor amax's bit pattern -> the tensor scale.
+__global__ void finish_scale_kernel(uint32_t *t) { *t = __builtin_bit_cast(uint32_t, tensor_scale(*t)); }
+
+__global__ __launch_bounds__(256) void quant_bf16_kernel(const float *__restrict__ x, uint16_t *__restrict__ out,
+                                                         int64_t n8)
+{
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t l = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; l < n8; l += stride) {
+        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(x + 8 * l);
+        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(x + 8 * l + 4);
+        uint32_t w[4];
+        w[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v0[0], v0[1]}, bf16x2));
+        w[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v0[2], v0[3]}, bf16x2));
+        w[2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v1[0], v1[1]}, bf16x2));
+        w[3] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v1[2], v1[3]}, bf16x2));
+        *reinterpret_cast<uint4 *>(out + 8 * l) = uint4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+int grid_for(int64_t lanes, int cus)
+{
+    const int64_t blocks = (lanes + 255) / 256;
+    const int64_t cap = (int64_t)cus * 8;
+    return (int)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
+}
+
+}  // namespace
+
+hipError_t launch_quant_mx(bool e4m3, const float *x, int64_t n, uint8_t *codes, uint8_t *scales, int cus,
+                           hipStream_t stream)
+{
+    const int64_t lanes = n / 8;
+    const int grid = grid_for(lanes, cus);
+    if (e4m3)
+        hipLaunchKernelGGL(quant_mx_kernel<true>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes);
+    else
+        hipLaunchKernelGGL(quant_mx_kernel<false>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_nvfp4(const float *x, int64_t n, uint8_t *codes, uint8_t *scales, float *t, int cus,
+                              hipStream_t stream)
+{
+    const int64_t lanes = n / 8;
+    const int grid = grid_for(lanes, cus);
+    uint32_t *tb = reinterpret_cast<uint32_t *>(t);
+    hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(1), 0, stream, tb);
+    hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(256), 0, stream, x, lanes, tb);
+    hipLaunchKernelGGL(quant_nvfp4_kernel, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes, tb);
+    hipLaunchKernelGGL(finish_scale_kernel, dim3(1), dim3(1), 0, stream, tb);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_bf16(const float *x, int64_t n, uint16_t *out, int cus, hipStream_t stream)
+{
+    const int64_t lanes = n / 8;
+    hipLaunchKernelGGL(quant_bf16_kernel, dim3(grid_for(lanes, cus)), dim3(256), 0, stream, x, out, lanes);
+    return hipGetLastError();
+}
+
+}  // namespace dbs

@@ -103,6 +103,39 @@ dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA,
                       int64_t M, int64_t N, int64_t K,
                       dbs_layout la, dbs_layout lb, hipStream_t stream);
 
+/*
+ * Quantisers: fp32 -> the GEMM's input formats, on the GPU.  x holds `rows`
+ * rows of K fp32 values (row-major, finite); x and codes must be 16-byte
+ * aligned.  Every call enqueues its kernels on `stream` and returns.
+ *
+ * quant_mx: K a multiple of 32.  Per block of 32 consecutive elements of a
+ *   row, E8M0 scale 2^e with e = floor(log2(amax / emax)) (emax = 448 for
+ *   DBS_E4M3, 6 for DBS_E2M1; e clamped to [-127, 127]; scale 1 for an
+ *   all-zero block), then each element the nearest E4M3 / E2M1 code of
+ *   x / 2^e.  codes: rows x K bytes (E4M3) or rows x K/2 packed bytes (E2M1,
+ *   element 2j in the low nibble); scales: rows x K/32 bytes.  The scale rule
+ *   follows the MX scale definition (OCP MX v1.0) with the workloads'
+ *   floor(log2(amax / emax)) exponent.
+ * quant_nvfp4: K a multiple of 16.  t (device, one float, out) = amax /
+ *   (6 * 448) over the whole array (1 if it is all zero); per block of 16 the
+ *   E4M3 scale s = nearest(amax_block / (6 t)); each element the nearest E2M1
+ *   code of x / (s t); every step in correctly rounded fp32.  codes: rows x
+ *   K/2 packed bytes; scales: rows x K/16 bytes.  t doubles as the amax
+ *   accumulator while the call's kernels run (four launches on `stream`).
+ *   The per-tensor plus per-16 E4M3 layout is the NVFP4 format of the
+ *   "ThunderKittens 2.0" post (section 2.1).
+ * quant_bf16: n a multiple of 8; out: n bf16 values (uint16), nearest even.
+ *
+ * "Nearest" rounds to the closest representable value, ties to the code with
+ * an even mantissa, saturating at the largest finite value and keeping the
+ * sign of zero.  Errors as for the GEMMs (DBS_EINVAL before any device work).
+ */
+dbs_status quant_mx(dbs_mx_elem elem, const float *x, int64_t rows, int64_t K, void *codes, uint8_t *scales,
+                    hipStream_t stream);
+dbs_status quant_nvfp4(const float *x, int64_t rows, int64_t K, void *codes, uint8_t *scales, float *t,
+                       hipStream_t stream);
+dbs_status quant_bf16(const float *x, int64_t n, void *out, hipStream_t stream);
+
 /* Static text for a status code. */
 const char *dbs_status_str(dbs_status st);
 

@@ -94,3 +94,44 @@ def test_binding_rejects_cpu_tensors():
     A = torch.zeros((8, 16), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         dbs.gemm_bf16(A, A)
+
+
+# ---- quantisers ----------------------------------------------------------------
+
+@pytest.mark.parametrize("elem,x,codes,scales,K,want", [
+    (0, FAKE, FAKE, FAKE, 48, 1),                               # K % 32
+    (9, FAKE, FAKE, FAKE, 64, 1),                               # unknown element format
+    (0, NUL, FAKE, FAKE, 64, 1),                                # null x
+    (4, FAKE, FAKE, NUL, 64, 1),                                # null scales
+    (0, ctypes.c_void_p((1 << 20) + 4), FAKE, FAKE, 64, 1),     # misaligned x
+    (4, FAKE, ctypes.c_void_p((1 << 20) + 8), FAKE, 64, 1),     # misaligned codes
+])
+def test_quant_mx_validation(elem, x, codes, scales, K, want):
+    L = dbs.lib()
+    assert L.quant_mx(elem, x, 4, K, codes, scales, NUL) == want
+    assert L.dbs_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("K,t,rows,want", [(24, FAKE, 4, 1), (32, NUL, 4, 1), (32, FAKE, 0, 1)])
+def test_quant_nvfp4_validation(K, t, rows, want):
+    L = dbs.lib()
+    assert L.quant_nvfp4(FAKE, rows, K, FAKE, FAKE, t, NUL) == want
+
+
+@pytest.mark.parametrize("n,want", [(12, 1), (0, 1)])
+def test_quant_bf16_validation(n, want):
+    L = dbs.lib()
+    assert L.quant_bf16(FAKE, n, FAKE, NUL) == want
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would reach a real device")
+def test_quant_no_device_reports_ehip():
+    L = dbs.lib()
+    assert L.quant_mx(0, FAKE, 4, 64, FAKE, FAKE, NUL) == 3
+
+
+def test_quant_binding_rejects_cpu_tensors():
+    with pytest.raises(ValueError):
+        dbs.quant_mx("e4m3", torch.zeros((4, 64), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        dbs.quant_nvfp4(torch.zeros((4, 64), dtype=torch.float32))
