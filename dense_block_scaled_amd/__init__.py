@@ -24,7 +24,7 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["gemm_bf16", "gemm_mx", "gemm_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError",
+__all__ = ["gemm_bf16", "gemm_mx", "gemm_nvfp4", "gemm_grouped_bf16", "gemm_grouped_mx", "gemm_grouped_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError",
            "DBS_OK", "DBS_EINVAL", "DBS_EUNSUPPORTED", "DBS_EHIP", "K_MAJOR", "MN_MAJOR",
            "E4M3", "E2M1", "status_str"]
 
@@ -60,6 +60,12 @@ def lib() -> ctypes.CDLL:
         L.gemm_mx.restype = I
         L.gemm_nvfp4.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P]
         L.gemm_nvfp4.restype = I
+        L.gemm_grouped_bf16.argtypes = [P, P, P, P, I64, I64, I64, P]
+        L.gemm_grouped_bf16.restype = I
+        L.gemm_grouped_mx.argtypes = [I, P, P, P, P, P, P, I64, I64, I64, P]
+        L.gemm_grouped_mx.restype = I
+        L.gemm_grouped_nvfp4.argtypes = [P, P, ctypes.c_float, P, P, P, P, P, I64, I64, I64, P]
+        L.gemm_grouped_nvfp4.restype = I
         L.quant_mx.argtypes = [I, P, I64, I64, P, P, P]
         L.quant_mx.restype = I
         L.quant_nvfp4.argtypes = [P, I64, I64, P, P, P, P]
@@ -189,4 +195,63 @@ def quant_bf16(x: torch.Tensor) -> torch.Tensor:
     px = _dev(x, "x", (torch.float32,), tuple(x.shape))
     out = torch.empty(tuple(x.shape), dtype=torch.bfloat16, device=x.device)
     _check(lib().quant_bf16(px, x.numel(), ctypes.c_void_p(out.data_ptr()), _stream(x)))
+    return out
+
+
+# ---- grouped GEMMs (mixture-of-experts layout) ----------------------------------
+
+def _offsets(offsets) -> tuple[ctypes.Array, int]:
+    off = [int(v) for v in offsets]
+    return (ctypes.c_int64 * len(off))(*off), len(off) - 1
+
+
+def gemm_grouped_bf16(A: torch.Tensor, B: torch.Tensor, offsets, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Group g: D[off[g]:off[g+1]] = A[off[g]:off[g+1]] @ B[g]^T; A (M, K) and
+    B (G, N, K) bf16, offsets a host sequence of G + 1 row offsets."""
+    off, G = _offsets(offsets)
+    M, K = A.shape
+    N = B.shape[1]
+    dt = (torch.bfloat16, torch.int16, torch.uint16)
+    pa = _dev(A, "A", dt, (M, K))
+    pb = _dev(B, "B", dt, (G, N, K))
+    out = _out(out, M, N, A)
+    _check(lib().gemm_grouped_bf16(pa, pb, ctypes.c_void_p(out.data_ptr()), off, G, N, K, _stream(A)))
+    return out
+
+
+def gemm_grouped_mx(elem: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor, offsets,
+                    K: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Grouped MXFP8 / MXFP4 GEMM: A (M, K bytes) with sA (M, K/32); B (G, N, K
+    bytes) with sB (G, N, K/32); offsets as for gemm_grouped_bf16."""
+    code = _ELEM[elem]
+    off, G = _offsets(offsets)
+    M, N = A.shape[0], B.shape[1]
+    if K is None:
+        K = A.shape[1] * (2 if elem == "e2m1" else 1)
+    kb = K // 2 if elem == "e2m1" else K
+    u8 = (torch.uint8,)
+    pa = _dev(A, "A", u8, (M, kb))
+    pb = _dev(B, "B", u8, (G, N, kb))
+    psa = _dev(sA, "sA", u8, (M, K // 32))
+    psb = _dev(sB, "sB", u8, (G, N, K // 32))
+    out = _out(out, M, N, A)
+    _check(lib().gemm_grouped_mx(code, pa, psa, pb, psb, ctypes.c_void_p(out.data_ptr()), off, G, N, K, _stream(A)))
+    return out
+
+
+def gemm_grouped_nvfp4(A: torch.Tensor, sA: torch.Tensor, tA: float, B: torch.Tensor, sB: torch.Tensor, tB,
+                       offsets, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Grouped NVFP4 GEMM: one tensor scale tA for A, one tB[g] per group of B."""
+    off, G = _offsets(offsets)
+    M, N = A.shape[0], B.shape[1]
+    K = A.shape[1] * 2
+    u8 = (torch.uint8,)
+    pa = _dev(A, "A", u8, (M, K // 2))
+    pb = _dev(B, "B", u8, (G, N, K // 2))
+    psa = _dev(sA, "sA", u8, (M, K // 16))
+    psb = _dev(sB, "sB", u8, (G, N, K // 16))
+    tb = (ctypes.c_float * G)(*[float(v) for v in tB])
+    out = _out(out, M, N, A)
+    _check(lib().gemm_grouped_nvfp4(pa, psa, float(tA), pb, psb, tb, ctypes.c_void_p(out.data_ptr()), off, G, N, K,
+                                    _stream(A)))
     return out

@@ -66,8 +66,17 @@ dbs_status check_common(const void *A, const void *B, const void *D, int64_t M, 
     return DBS_OK;
 }
 
+// Groups of a grouped GEMM (host arrays): G + 1 row offsets and one output
+// scale per group.
+struct Groups {
+    const int64_t *off;
+    int64_t G;
+    const float *alpha;
+};
+
 dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB, void *D, int64_t M,
-               int64_t N, int64_t K, float alpha, int elem_bits, int block, hipStream_t stream)
+               int64_t N, int64_t K, float alpha, int elem_bits, int block, hipStream_t stream,
+               const Groups *groups = nullptr)
 {
     int cus = 0;
     dbs_status st = device_cus(&cus);
@@ -85,12 +94,36 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     p.lda = (int)(K * elem_bits / 8);
     p.sld = block ? (int)(K / block) : 0;
     // square tiles unless they would fill at most half of the CUs
-    const int64_t sq_tiles = ((M + dbs::kSquareTM - 1) / dbs::kSquareTM) * ((N + dbs::kSquareTN - 1) / dbs::kSquareTN);
+    auto tiles_of = [&](int64_t rows, int64_t tm_, int64_t tn_) { return ((rows + tm_ - 1) / tm_) * ((N + tn_ - 1) / tn_); };
+    int64_t sq_tiles = 0;
+    if (groups) {
+        for (int64_t g = 0; g < groups->G; ++g)
+            sq_tiles += tiles_of(groups->off[g + 1] - groups->off[g], dbs::kSquareTM, dbs::kSquareTN);
+    } else {
+        sq_tiles = tiles_of(M, dbs::kSquareTM, dbs::kSquareTN);
+    }
     const int shape = 2 * sq_tiles <= cus ? dbs::kShapeSkinny : dbs::kShapeSquare;
     const int tm = shape == dbs::kShapeSkinny ? dbs::kSkinnyTM : dbs::kSquareTM;
     const int tn = shape == dbs::kShapeSkinny ? dbs::kSkinnyTN : dbs::kSquareTN;
     p.tiles_m = (int)((M + tm - 1) / tm);
     p.tiles_n = (int)((N + tn - 1) / tn);
+    if (groups) {
+        // every group's tiles in sequence: tiles_m holds the total
+        int64_t acc = 0;
+        p.ngroups = (int)groups->G;
+        for (int64_t g = 0; g < groups->G; ++g) {
+            p.goff[g] = (int)groups->off[g];
+            p.gtiles[g] = (int)acc;
+            p.galpha[g] = groups->alpha ? groups->alpha[g] : alpha;
+            acc += tiles_of(groups->off[g + 1] - groups->off[g], tm, tn);
+        }
+        p.goff[groups->G] = (int)groups->off[groups->G];
+        p.gtiles[groups->G] = (int)std::min<int64_t>(acc, INT32_MAX);
+        if (acc == 0) return DBS_OK;       // all groups empty: nothing to compute
+        if (acc > INT32_MAX) return fail(DBS_EINVAL, "too many output tiles");
+        p.tiles_m = (int)acc;
+        p.tiles_n = 1;
+    }
     p.group_m = 4;
     p.vec_store = (N % 4 == 0 && aligned(D, 8)) ? 1 : 0;
     p.vec16 = (N % 8 == 0 && aligned(D, 16)) ? 1 : 0;
@@ -195,6 +228,64 @@ dbs_status quant_bf16(const float *x, int64_t n, void *out, hipStream_t stream)
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
     g_err[0] = '\0';
     return DBS_OK;
+}
+
+// ---- grouped GEMM ---------------------------------------------------------------
+
+static dbs_status check_groups(const int64_t *offsets, int64_t G, int64_t *M)
+{
+    if (!offsets) return fail(DBS_EINVAL, "null offsets");
+    if (G < 1 || G > dbs::kMaxGroups) return fail(DBS_EINVAL, "group count outside 1 .. 64");
+    if (offsets[0] != 0) return fail(DBS_EINVAL, "offsets[0] must be 0");
+    for (int64_t g = 0; g < G; ++g)
+        if (offsets[g + 1] < offsets[g]) return fail(DBS_EINVAL, "offsets must be non-decreasing");
+    *M = offsets[G];
+    if (*M <= 0) return fail(DBS_EINVAL, "the groups hold no rows");
+    return DBS_OK;
+}
+
+dbs_status gemm_grouped_bf16(const void *A, const void *B, void *D, const int64_t *offsets, int64_t G, int64_t N,
+                             int64_t K, hipStream_t stream)
+{
+    int64_t M = 0;
+    dbs_status st = check_groups(offsets, G, &M);
+    if (st != DBS_OK) return st;
+    if ((st = check_common(A, B, D, M, N, K, DBS_K_MAJOR, DBS_K_MAJOR, int64_t(1) << 21)) != DBS_OK) return st;
+    if (K % 8) return fail(DBS_EINVAL, "bf16: K must be a multiple of 8");
+    const Groups gr{offsets, G, nullptr};
+    return run(dbs::kBF16, A, nullptr, B, nullptr, D, M, N, K, 1.0f, 16, 0, stream, &gr);
+}
+
+dbs_status gemm_grouped_mx(dbs_mx_elem elem, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB,
+                           void *D, const int64_t *offsets, int64_t G, int64_t N, int64_t K, hipStream_t stream)
+{
+    if (elem != DBS_E4M3 && elem != DBS_E2M1) return fail(DBS_EINVAL, "mx: unknown element format");
+    if (!sA || !sB) return fail(DBS_EINVAL, "null pointer argument");
+    int64_t M = 0;
+    dbs_status st = check_groups(offsets, G, &M);
+    if (st != DBS_OK) return st;
+    if ((st = check_common(A, B, D, M, N, K, DBS_K_MAJOR, DBS_K_MAJOR, int64_t(1) << 22)) != DBS_OK) return st;
+    if (K % 32) return fail(DBS_EINVAL, "mx: K must be a multiple of 32");
+    const Groups gr{offsets, G, nullptr};
+    if (elem == DBS_E4M3) return run(dbs::kMXFP8, A, sA, B, sB, D, M, N, K, 1.0f, 8, 32, stream, &gr);
+    return run(dbs::kMXFP4, A, sA, B, sB, D, M, N, K, 1.0f, 4, 32, stream, &gr);
+}
+
+dbs_status gemm_grouped_nvfp4(const void *A, const uint8_t *sA, float tA, const void *B, const uint8_t *sB,
+                              const float *tB, void *D, const int64_t *offsets, int64_t G, int64_t N, int64_t K,
+                              hipStream_t stream)
+{
+    if (!sA || !sB || !tB) return fail(DBS_EINVAL, "null pointer argument");
+    int64_t M = 0;
+    dbs_status st = check_groups(offsets, G, &M);
+    if (st != DBS_OK) return st;
+    if ((st = check_common(A, B, D, M, N, K, DBS_K_MAJOR, DBS_K_MAJOR, int64_t(1) << 22)) != DBS_OK) return st;
+    if (K % 16) return fail(DBS_EINVAL, "nvfp4: K must be a multiple of 16");
+    if (K % 32) return fail(DBS_EUNSUPPORTED, "nvfp4: K must be a multiple of 32 in this implementation");
+    float alpha[dbs::kMaxGroups];
+    for (int64_t g = 0; g < G; ++g) alpha[g] = tA * tB[g];
+    const Groups gr{offsets, G, alpha};
+    return run(dbs::kNVFP4, A, sA, B, sB, D, M, N, K, 1.0f, 4, 16, stream, &gr);
 }
 
 const char *dbs_status_str(dbs_status st)

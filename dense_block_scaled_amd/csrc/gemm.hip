@@ -105,6 +105,49 @@ __device__ __forceinline__ void tile_coords(int tile, const Params &p, int &tm, 
     tn = idx / rows;
 }
 
+// Where output tile `tile` of a TM x TN tiling lies: rows m0 .. mend-1 of A
+// and D (mend: the end of its group, or M), columns n0 .. of D, its group's
+// B and sB blocks at byte offsets boff and sboff, and its output scale.
+struct TileRef {
+    int m0, mend, n0;
+    int64_t boff, sboff;
+    float alpha;
+};
+
+template <int TM, int TN>
+__device__ __forceinline__ TileRef tile_ref(int tile, const Params &p)
+{
+    TileRef r;
+    if (p.ngroups == 0) {
+        int tm, tn;
+        tile_coords(tile, p, tm, tn);
+        r.m0 = tm * TM;
+        r.mend = p.M;
+        r.n0 = tn * TN;
+        r.boff = r.sboff = 0;
+        r.alpha = p.alpha;
+        return r;
+    }
+    // the group holding the tile: the last g with gtiles[g] <= tile (binary
+    // search over the uniform table; empty groups have equal neighbours)
+    int lo = 0, hi = p.ngroups;          // gtiles[lo] <= tile < gtiles[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.gtiles[mid] <= tile) lo = mid; else hi = mid;
+    }
+    const int g = lo;
+    const int rows = p.goff[g + 1] - p.goff[g];
+    const int tmg = (rows + TM - 1) / TM;
+    const int local = tile - p.gtiles[g];
+    r.m0 = p.goff[g] + (local % tmg) * TM;
+    r.mend = p.goff[g + 1];
+    r.n0 = (local / tmg) * TN;
+    r.boff = (int64_t)g * p.N * p.lda;
+    r.sboff = (int64_t)g * p.N * p.sld;
+    r.alpha = p.galpha[g];
+    return r;
+}
+
 // ------------------------------------------------------------- tile shapes
 
 // TM x TN output tile (TM rows of A, TN rows of B per stage) computed by a
@@ -681,13 +724,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y)
 }
 
 template <class S>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[S::MB][S::NB], const Params &p, int m0, int n0,
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[S::MB][S::NB], const Params &p, const TileRef &tr,
                                            const Ctx<S> &c)
 {
+    const int m0 = tr.m0, n0 = tr.n0;
+    const float alpha = tr.alpha;
 #pragma unroll
     for (int i = 0; i < S::MB; ++i) {
         const int r0 = m0 + c.wm * (S::TM / S::WM) + i * 32;
-        const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)max(0, min(32, p.M - r0)) * (uint32_t)p.N * 2u);
+        const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)max(0, min(32, tr.mend - r0)) * (uint32_t)p.N * 2u);
         const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.D + (int64_t)r0 * p.N, bytes);
 #pragma unroll
         for (int j = 0; j < S::NB; ++j) {
@@ -695,8 +740,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[S::MB][S::NB], co
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + c.wn * (S::TN / S::WN) + j * 32 + g * 8 + c.h * 4;
                 const f32x16 &a = acc[i][j];
-                const uint32_t lo = pack_bf16(a[4 * g] * p.alpha, a[4 * g + 1] * p.alpha);
-                const uint32_t hi = pack_bf16(a[4 * g + 2] * p.alpha, a[4 * g + 3] * p.alpha);
+                const uint32_t lo = pack_bf16(a[4 * g] * alpha, a[4 * g + 1] * alpha);
+                const uint32_t hi = pack_bf16(a[4 * g + 2] * alpha, a[4 * g + 3] * alpha);
                 const uint32_t base = (uint32_t)(c.lr * p.N + n) * 2u;
                 if (p.vec_store) {
                     // N % 4 == 0 and n % 4 == 0: the 4 columns are all in or all out
@@ -723,8 +768,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[S::MB][S::NB], co
 // before the slot is refilled.
 template <class S>
 __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[S::MB][S::NB], uint8_t *lds, int xslot,
-                                               const Params &p, int m0, int n0, const Ctx<S> &c)
+                                               const Params &p, const TileRef &tr, const Ctx<S> &c)
 {
+    const int m0 = tr.m0, n0 = tr.n0;
+    const float alpha = tr.alpha;
     constexpr int RB = S::NB * 64;          // bytes per staged row
     constexpr int CPR = RB / 16;            // 16-byte chunks per staged row
     constexpr int RPI = 64 / CPR;           // rows per read instruction
@@ -743,14 +790,14 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[S::MB][S::NB]
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const f32x16 &a = acc[i][j];
-                const uint32_t lo = pack_bf16(a[4 * g] * p.alpha, a[4 * g + 1] * p.alpha);
-                const uint32_t hi = pack_bf16(a[4 * g + 2] * p.alpha, a[4 * g + 3] * p.alpha);
+                const uint32_t lo = pack_bf16(a[4 * g] * alpha, a[4 * g + 1] * alpha);
+                const uint32_t hi = pack_bf16(a[4 * g + 2] * alpha, a[4 * g + 3] * alpha);
                 const int ch = (4 * j + g) ^ (c.lr & (CPR - 1));
                 *reinterpret_cast<u32x2 *>(buf + c.lr * RB + 16 * ch + 8 * c.h) = u32x2{lo, hi};
             }
         }
         const int r0 = m0 + c.wm * (S::TM / S::WM) + i * 32;
-        const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)max(0, min(32, p.M - r0)) * (uint32_t)p.N * 2u);
+        const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)max(0, min(32, tr.mend - r0)) * (uint32_t)p.N * 2u);
         const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.D + (int64_t)r0 * p.N, bytes);
 #pragma unroll
         for (int q = 0; q < 32 / RPI; ++q) {
@@ -999,18 +1046,16 @@ __device__ __forceinline__ void stage(Pipe<FMT, S> &P, f32x16 (&acc)[S::MB][S::N
 template <int FMT, class S>
 __device__ __forceinline__ Target tile_target(const Params &p, int tile)
 {
-    int tm, tn;
-    tile_coords(tile, p, tm, tn);
-    const int m0 = tm * S::TM, n0 = tn * S::TN;
-    const int rows_a = min(p.M - m0, S::TM), rows_b = min(p.N - n0, S::TN);
+    const TileRef r = tile_ref<S::TM, S::TN>(tile, p);
+    const int rows_a = min(r.mend - r.m0, S::TM), rows_b = min(p.N - r.n0, S::TN);
     Target t;
-    t.ra = make_rsrc(p.A + (int64_t)m0 * p.lda, (uint32_t)(rows_a * p.lda));
-    t.rb = make_rsrc(p.B + (int64_t)n0 * p.lda, (uint32_t)(rows_b * p.lda));
+    t.ra = make_rsrc(p.A + (int64_t)r.m0 * p.lda, (uint32_t)(rows_a * p.lda));
+    t.rb = make_rsrc(p.B + r.boff + (int64_t)r.n0 * p.lda, (uint32_t)(rows_b * p.lda));
     t.rsa = t.ra;
     t.rsb = t.rb;
     if constexpr (FMT != kBF16) {
-        t.rsa = make_rsrc(p.sA + (int64_t)m0 * p.sld, (uint32_t)(rows_a * p.sld));
-        t.rsb = make_rsrc(p.sB + (int64_t)n0 * p.sld, (uint32_t)(rows_b * p.sld));
+        t.rsa = make_rsrc(p.sA + (int64_t)r.m0 * p.sld, (uint32_t)(rows_a * p.sld));
+        t.rsb = make_rsrc(p.sB + r.sboff + (int64_t)r.n0 * p.sld, (uint32_t)(rows_b * p.sld));
     }
     return t;
 }
@@ -1147,21 +1192,20 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
         phase<FMT, S, SM, 0, false, false>(acc, P, lds, p, c, 0, ld, 0, 0, stg, cp);
         mfma_drain<S>(acc);
 
-        int tm, tn;
-        tile_coords(tile, p, tm, tn);
+        const TileRef tr = tile_ref<S::TM, S::TN>(tile, p);
         // (the one-wave-per-SIMD variant has no registers to spare for the
         // staged epilogue)
         if (S::NW == 8 || S::NB <= 2) {
             if (p.vec16) {
                 // the slot the last stage read is free until the next
                 // tile's first stage refills it
-                store_tile_lds<S>(acc, lds, xs, p, tm * S::TM, tn * S::TN, c);
+                store_tile_lds<S>(acc, lds, xs, p, tr, c);
                 asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             } else {
-                store_tile<S>(acc, p, tm * S::TM, tn * S::TN, c);
+                store_tile<S>(acc, p, tr, c);
             }
         } else {
-            store_tile<S>(acc, p, tm * S::TM, tn * S::TN, c);
+            store_tile<S>(acc, p, tr, c);
         }
         if (next >= ntiles) break;
         tile = next;
@@ -1419,9 +1463,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_raw_kernel(Params p)
             rs = ns;
         }
         mfma_drain<S>(acc);
-        int tm, tn;
-        tile_coords(tile, p, tm, tn);
-        store_tile<S>(acc, p, tm * S::TM, tn * S::TN, c);
+        store_tile<S>(acc, p, tile_ref<S::TM, S::TN>(tile, p), c);
         // the raw-stage waits count loads; keep the stores out of them
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (next >= ntiles) break;

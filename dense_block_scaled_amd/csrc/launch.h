@@ -9,6 +9,8 @@ namespace dbs {
 
 enum Format : int { kBF16 = 0, kMXFP8 = 1, kMXFP4 = 2, kNVFP4 = 3 };
 
+constexpr int kMaxGroups = 64;
+
 // Everything a kernel needs, passed by value.  Sizes were validated on the
 // host: every per-tile byte offset fits in 31 bits.
 struct Params {
@@ -27,6 +29,14 @@ struct Params {
     int vec16;            // 1 if D rows allow 16-byte stores (N % 8 == 0, D 16-byte aligned)
     int scales_aligned;   // 1 if every scale row starts on a 4-byte boundary
     float alpha;          // applied to the fp32 accumulator before rounding
+    // Grouped GEMM (ngroups > 0): group g owns rows goff[g] .. goff[g+1]-1 of A
+    // and D, the g-th N x K block of B (and of sB) and output tiles
+    // gtiles[g] .. gtiles[g+1]-1 (tiles_m = gtiles[ngroups], tiles_n = 1);
+    // its results are scaled by galpha[g] instead of alpha.
+    int ngroups;
+    int goff[kMaxGroups + 1];
+    int gtiles[kMaxGroups + 1];
+    float galpha[kMaxGroups];
 };
 
 // Output tile shapes (rows of A x rows of B per tile).  Square tiles are the

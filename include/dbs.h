@@ -104,6 +104,26 @@ dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA,
                       dbs_layout la, dbs_layout lb, hipStream_t stream);
 
 /*
+ * Grouped GEMMs (mixture-of-experts layout): G groups (1 <= G <= 64) share N
+ * and K.  Group g owns rows offsets[g] .. offsets[g+1]-1 of A and of D (and
+ * of sA), and the g-th block of N rows of B (B holds G x N rows of K
+ * elements, sB G x N scale rows):  D_g = bf16(alpha_g (sA_g (.) A_g) .
+ * (sB_g (.) B_g)^T).  offsets (G + 1 values, offsets[0] = 0, non-decreasing,
+ * empty groups allowed) and tB (G values) are HOST arrays; everything else
+ * is as for the single GEMMs (K-major operands only).  alpha_g = 1, or
+ * tA * tB[g] for NVFP4.  One kernel launch covers every group's tiles.  The
+ * grouped GEMM is the mixture-of-experts workload the "ThunderKittens 2.0"
+ * post points to (section on what comes next).
+ */
+dbs_status gemm_grouped_bf16(const void *A, const void *B, void *D, const int64_t *offsets, int64_t G, int64_t N,
+                             int64_t K, hipStream_t stream);
+dbs_status gemm_grouped_mx(dbs_mx_elem elem, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB,
+                           void *D, const int64_t *offsets, int64_t G, int64_t N, int64_t K, hipStream_t stream);
+dbs_status gemm_grouped_nvfp4(const void *A, const uint8_t *sA, float tA, const void *B, const uint8_t *sB,
+                              const float *tB, void *D, const int64_t *offsets, int64_t G, int64_t N, int64_t K,
+                              hipStream_t stream);
+
+/*
  * Quantisers: fp32 -> the GEMM's input formats, on the GPU.  x holds `rows`
  * rows of K fp32 values (row-major, finite); x and codes must be 16-byte
  * aligned.  Every call enqueues its kernels on `stream` and returns.

@@ -135,3 +135,34 @@ def test_quant_binding_rejects_cpu_tensors():
         dbs.quant_mx("e4m3", torch.zeros((4, 64), dtype=torch.float32))
     with pytest.raises(ValueError):
         dbs.quant_nvfp4(torch.zeros((4, 64), dtype=torch.float32))
+
+
+# ---- grouped GEMMs -------------------------------------------------------------------
+
+def _off(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+@pytest.mark.parametrize("off,G,want", [
+    (_off(0, 8, 16), 2, None),          # valid (reaches the device check)
+    (_off(1, 8, 16), 2, 1),             # offsets[0] != 0
+    (_off(0, 9, 4), 2, 1),              # decreasing
+    (_off(0, 0, 0), 2, 1),              # no rows at all
+    (_off(0, 8), 0, 1),                 # G < 1
+    (_off(*range(0, 66)), 65, 1),       # G > 64
+])
+def test_grouped_validation(off, G, want):
+    L = dbs.lib()
+    st = L.gemm_grouped_bf16(FAKE, FAKE, FAKE, off, G, 16, 16, NUL)
+    if want is None:
+        assert st in (0, 3)             # 3: no device here
+    else:
+        assert st == want
+
+
+def test_grouped_null_arguments():
+    L = dbs.lib()
+    assert L.gemm_grouped_bf16(FAKE, FAKE, FAKE, NUL, 2, 16, 16, NUL) == 1
+    assert L.gemm_grouped_mx(0, FAKE, NUL, FAKE, FAKE, FAKE, _off(0, 8, 16), 2, 16, 64, NUL) == 1
+    assert L.gemm_grouped_nvfp4(FAKE, FAKE, 1.0, FAKE, FAKE, NUL, FAKE, _off(0, 8, 16), 2, 16, 64, NUL) == 1
+    assert L.gemm_grouped_mx(0, FAKE, FAKE, FAKE, FAKE, FAKE, _off(0, 8, 16), 2, 16, 48, NUL) == 1   # K % 32
