@@ -8,13 +8,16 @@ marshal pointers, sizes and the current stream into the C ABI of
 There is no CPU fallback: if ``libdbs.so`` is missing, or a call reports an
 error, these functions raise.
 
-Operand encodings (all K-major, contiguous):
+Operand encodings (contiguous; K-major unless la / lb say MN_MAJOR):
   gemm_bf16(A, B)                     A: (M, K) bfloat16/uint16, B: (N, K)
   gemm_mx(elem, A, sA, B, sB)         elem 'e4m3': A (M, K) uint8;
                                       elem 'e2m1': A (M, K/2) uint8, 2 per byte
                                       sA: (M, K/32) uint8 E8M0 codes
   gemm_nvfp4(A, sA, tA, B, sB, tB)    A: (M, K/2) uint8 packed E2M1,
                                       sA: (M, K/16) uint8 E4M3 codes, tA float
+MN-major operands (gemm_bf16, gemm_mx) are stored transposed: A (K, M), B
+(K, N), E2M1 packing two consecutive M (N) per byte, (K, M/2); scales keep
+their (M, K/32) layout.
 Each returns D: (M, N) torch.bfloat16 (or writes into ``out``).
 """
 from __future__ import annotations
@@ -115,34 +118,56 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def gemm_bf16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """D = A @ B^T for bf16 A (M, K), B (N, K); fp32 accumulate, bf16 out."""
-    M, K = A.shape
-    N = B.shape[0]
+def _layout(l: int, name: str) -> int:
+    if l not in (K_MAJOR, MN_MAJOR):
+        raise ValueError(f"{name}: layout must be K_MAJOR or MN_MAJOR")
+    return l
+
+
+def _rows(t: torch.Tensor, l: int, per_byte: int = 1) -> int:
+    """M (or N) of an operand: its row count, or (MN-major) its columns."""
+    return t.shape[0] if l == K_MAJOR else t.shape[1] * per_byte
+
+
+def _shape(rows: int, kcols: int, l: int, per_byte: int = 1) -> tuple:
+    """Expected tensor shape of an operand with `rows` rows (M or N) and K
+    of kcols elements (per_byte elements per stored byte)."""
+    return (rows, kcols // per_byte) if l == K_MAJOR else (kcols, rows // per_byte)
+
+
+def gemm_bf16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
+              la: int = K_MAJOR, lb: int = K_MAJOR) -> torch.Tensor:
+    """D = A @ B^T for bf16 A (M, K), B (N, K) (MN-major: (K, M), (K, N));
+    fp32 accumulate, bf16 out."""
+    la, lb = _layout(la, "la"), _layout(lb, "lb")
+    M, N = _rows(A, la), _rows(B, lb)
+    K = A.shape[1] if la == K_MAJOR else A.shape[0]
     dt = (torch.bfloat16, torch.int16, torch.uint16)
-    pa = _dev(A, "A", dt, (M, K))
-    pb = _dev(B, "B", dt, (N, K))
+    pa = _dev(A, "A", dt, _shape(M, K, la))
+    pb = _dev(B, "B", dt, _shape(N, K, lb))
     out = _out(out, M, N, A)
-    _check(lib().gemm_bf16(pa, pb, ctypes.c_void_p(out.data_ptr()), M, N, K, K_MAJOR, K_MAJOR, _stream(A)))
+    _check(lib().gemm_bf16(pa, pb, ctypes.c_void_p(out.data_ptr()), M, N, K, la, lb, _stream(A)))
     return out
 
 
 def gemm_mx(elem: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor,
-            K: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+            K: int | None = None, out: torch.Tensor | None = None,
+            la: int = K_MAJOR, lb: int = K_MAJOR) -> torch.Tensor:
     """MXFP8 (elem='e4m3') or MXFP4 (elem='e2m1') GEMM with E8M0 scales per 32."""
     code = _ELEM[elem]
-    M, N = A.shape[0], B.shape[0]
+    la, lb = _layout(la, "la"), _layout(lb, "lb")
+    pb_ = 2 if elem == "e2m1" else 1     # elements per byte
+    M, N = _rows(A, la, pb_), _rows(B, lb, pb_)
     if K is None:
-        K = A.shape[1] * (2 if elem == "e2m1" else 1)
-    kb = K // 2 if elem == "e2m1" else K
+        K = A.shape[1] * pb_ if la == K_MAJOR else A.shape[0]
     u8 = (torch.uint8,)
-    pa = _dev(A, "A", u8, (M, kb))
-    pb = _dev(B, "B", u8, (N, kb))
+    pa = _dev(A, "A", u8, _shape(M, K, la, pb_))
+    pb = _dev(B, "B", u8, _shape(N, K, lb, pb_))
     psa = _dev(sA, "sA", u8, (M, K // 32))
     psb = _dev(sB, "sB", u8, (N, K // 32))
     out = _out(out, M, N, A)
     _check(lib().gemm_mx(code, pa, psa, pb, psb, ctypes.c_void_p(out.data_ptr()), M, N, K,
-                         K_MAJOR, K_MAJOR, _stream(A)))
+                         la, lb, _stream(A)))
     return out
 
 

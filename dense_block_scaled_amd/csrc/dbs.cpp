@@ -61,9 +61,26 @@ dbs_status check_common(const void *A, const void *B, const void *D, int64_t M, 
         return fail(DBS_EINVAL, "unknown layout value");
     if (!aligned(A, 16) || !aligned(B, 16)) return fail(DBS_EINVAL, "A and B must be 16-byte aligned");
     if (!aligned(D, 2)) return fail(DBS_EINVAL, "D must be 2-byte aligned");
-    if (la != DBS_K_MAJOR || lb != DBS_K_MAJOR)
-        return fail(DBS_EUNSUPPORTED, "only K-major A and B are implemented");
     return DBS_OK;
+}
+
+// MN-major operands (stored K x M for A, K x N for B): each K-row of `rows`
+// elements must be whole 16-byte chunks, and the operand must stay below
+// 2^31 bytes with a stage of slack (the kernels address it with 32-bit
+// offsets from a tile's first column).
+dbs_status check_mn(dbs_layout la, dbs_layout lb, int64_t M, int64_t N, int64_t K, int elem_bits)
+{
+    auto one = [&](dbs_layout l, int64_t rows, const char *what) -> dbs_status {
+        if (l != DBS_MN_MAJOR) return DBS_OK;
+        if ((rows * elem_bits) % 128)
+            return fail(DBS_EUNSUPPORTED, what);
+        if ((K + 256) * (rows * elem_bits / 8) >= (int64_t(1) << 31))
+            return fail(DBS_EUNSUPPORTED, "MN-major operand of 2 GiB or more");
+        return DBS_OK;
+    };
+    dbs_status st = one(la, M, "MN-major A needs M * element bits to be a multiple of 128 (16-byte rows)");
+    if (st != DBS_OK) return st;
+    return one(lb, N, "MN-major B needs N * element bits to be a multiple of 128 (16-byte rows)");
 }
 
 // Groups of a grouped GEMM (host arrays): G + 1 row offsets and one output
@@ -76,7 +93,7 @@ struct Groups {
 
 dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB, void *D, int64_t M,
                int64_t N, int64_t K, float alpha, int elem_bits, int block, hipStream_t stream,
-               const Groups *groups = nullptr)
+               const Groups *groups = nullptr, dbs_layout la = DBS_K_MAJOR, dbs_layout lb = DBS_K_MAJOR)
 {
     int cus = 0;
     dbs_status st = device_cus(&cus);
@@ -93,6 +110,9 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     p.K = (int)K;
     p.lda = (int)(K * elem_bits / 8);
     p.sld = block ? (int)(K / block) : 0;
+    p.lay = (la == DBS_MN_MAJOR ? 1 : 0) | (lb == DBS_MN_MAJOR ? 2 : 0);
+    p.ldam = (int)(M * elem_bits / 8);
+    p.ldbm = (int)(N * elem_bits / 8);
     // square tiles unless they would fill at most half of the CUs
     auto tiles_of = [&](int64_t rows, int64_t tm_, int64_t tn_) { return ((rows + tm_ - 1) / tm_) * ((N + tn_ - 1) / tn_); };
     int64_t sq_tiles = 0;
@@ -149,7 +169,8 @@ dbs_status gemm_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N
     dbs_status st = check_common(A, B, D, M, N, K, la, lb, int64_t(1) << 21);
     if (st != DBS_OK) return st;
     if (K % 8) return fail(DBS_EINVAL, "bf16: K must be a multiple of 8");
-    return run(dbs::kBF16, A, nullptr, B, nullptr, D, M, N, K, 1.0f, 16, 0, stream);
+    if ((st = check_mn(la, lb, M, N, K, 16)) != DBS_OK) return st;
+    return run(dbs::kBF16, A, nullptr, B, nullptr, D, M, N, K, 1.0f, 16, 0, stream, nullptr, la, lb);
 }
 
 dbs_status gemm_mx(dbs_mx_elem elem, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB, void *D,
@@ -160,8 +181,10 @@ dbs_status gemm_mx(dbs_mx_elem elem, const void *A, const uint8_t *sA, const voi
     dbs_status st = check_common(A, B, D, M, N, K, la, lb, int64_t(1) << 22);
     if (st != DBS_OK) return st;
     if (K % 32) return fail(DBS_EINVAL, "mx: K must be a multiple of 32");
-    if (elem == DBS_E4M3) return run(dbs::kMXFP8, A, sA, B, sB, D, M, N, K, 1.0f, 8, 32, stream);
-    return run(dbs::kMXFP4, A, sA, B, sB, D, M, N, K, 1.0f, 4, 32, stream);
+    const int bits = elem == DBS_E4M3 ? 8 : 4;
+    if ((st = check_mn(la, lb, M, N, K, bits)) != DBS_OK) return st;
+    return run(elem == DBS_E4M3 ? dbs::kMXFP8 : dbs::kMXFP4, A, sA, B, sB, D, M, N, K, 1.0f, bits, 32, stream, nullptr,
+               la, lb);
 }
 
 dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA, const void *B, const uint8_t *sB, float tB,
@@ -172,6 +195,8 @@ dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA, const void *B,
     if (st != DBS_OK) return st;
     if (K % 16) return fail(DBS_EINVAL, "nvfp4: K must be a multiple of 16");
     if (K % 32) return fail(DBS_EUNSUPPORTED, "nvfp4: K must be a multiple of 32 in this implementation");
+    if (la != DBS_K_MAJOR || lb != DBS_K_MAJOR)
+        return fail(DBS_EUNSUPPORTED, "nvfp4: only K-major A and B are implemented");
     return run(dbs::kNVFP4, A, sA, B, sB, D, M, N, K, tA * tB, 4, 16, stream);
 }
 

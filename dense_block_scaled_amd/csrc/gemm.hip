@@ -70,6 +70,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr uint32_t kOOB = 0x80000000u;         // beyond every num_records we set
@@ -155,12 +157,15 @@ __device__ __forceinline__ TileRef tile_ref(int tile, const Params &p)
 // NS-slot LDS ring.  A stage moves (TM + TN) / 8 wave-loads of 1 KiB (8 rows
 // x 128 bytes); wave w issues QA of A and QB of B.  LDS: A slots 0..NS-1 | B
 // slots 0..NS-1 | scale slots (MX formats) SA 0..NS-1 | SB 0..NS-1 of rows x
-// BPS bytes.
+// BPS bytes.  LAY: bit 0 set if A is stored MN-major (K x M), bit 1 if B is
+// (K x N); a slot of an MN-major operand holds the same bytes as a K-major
+// one, arranged as the stage's K-rows (see Mn below).
 constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
 
-template <int TM_, int TN_, int WM_, int WN_, int NS_ = 2>
+template <int TM_, int TN_, int WM_, int WN_, int NS_ = 2, int LAY_ = 0>
 struct Shape {
-    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_, NS = NS_;
+    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_, NS = NS_, LAY = LAY_;
+    static constexpr bool AMN = (LAY & 1) != 0, BMN = (LAY & 2) != 0;
     static constexpr int NW = WM * WN;
     static constexpr int kThreads = 64 * NW;
     static constexpr int MB = TM / WM / 32, NB = TN / WN / 32;
@@ -188,6 +193,10 @@ using SkinnyDeep = Shape<kSkinnyTM, kSkinnyTN, 8, 1, 3>;
 // the register-staged scale bytes do not fit beside two waves per SIMD, so
 // this variant runs one wave per SIMD, each owning 128 x 128.
 using SquareW4 = Shape<kSquareTM, kSquareTN, 2, 2>;
+
+// Shape S with operand layouts LAY.
+template <class S, int LAY>
+using WithLayout = Shape<S::TM, S::TN, S::WM, S::WN, S::NS, LAY>;
 
 // ------------------------------------------------------------ format traits
 
@@ -221,6 +230,49 @@ struct Fmt<kMXFP4> {
 // MFMA k-steps per stage
 template <int FMT, class S>
 constexpr int kk_of() { return kRowBytes / Fmt<FMT>::KSB; }
+
+// MN-major operands (A stored K x M, B stored K x N; FP4 packs two elements
+// of consecutive rows of the tile, i.e. consecutive M or N, per byte, low
+// nibble first).  A slot of such an operand holds the stage's KS = 8 *
+// kRowBytes / EB K-rows, each the T elements of the tile's rows of that
+// operand (RB = T * EB / 8 bytes), as RB / 16 chunks of 16 bytes under an
+// XOR swizzle f(row).  The MFMA fragments come out of it through gfx950's
+// transposed LDS reads (ds_read_b64_tr_b16 / _b8 / _b4).  Within each group
+// of 16 lanes such a read takes a block of 4 (b16), 8 (b8) or 16 (b4) K-rows
+// x 16 columns, every lane giving the address of 8 bytes of one K-row (rows
+// in lane order, 4, 2 or 1 lanes per row), and returns to lane j the column
+// j of the block, i.e. 4, 8 or 16 consecutive K values of one output row or
+// column, packed like a K-major fragment (established with a one-wave
+// probe).  A 32-column fragment of one k-step takes 2 (BF16, E2M1) or 4
+// (E4M3) such reads, lane group g covering columns 16 (g % 2) .. +15 and
+// lane half g / 2 its half of the k-step.
+//
+// The reads of one instruction cover W = 2 * EB / 8 chunks of each of
+// 16 / W K-rows per half-wave (32 columns): the swizzle moves consecutive
+// K-rows to different banks.  Rows of RB < 256 bytes share a 256-byte bank
+// line (P = 16 / CPR of them), so f only has to separate rows P apart.
+template <int FMT, int T>
+struct Mn {
+    static constexpr int EB = FMT == kBF16 ? 16 : FMT == kMXFP8 ? 8 : 4;   // element bits
+    static constexpr int RB = T * EB / 8;                                  // bytes per K-row
+    static constexpr int KS = 8 * kRowBytes / EB;                          // K-rows per stage
+    static constexpr int CPR = RB / 16;
+    static constexpr int CPRM = CPR < 16 ? CPR : 16;
+    static constexpr int P = 16 / CPRM;
+    static constexpr int W = 2 * EB / 8;
+    static constexpr int NF = CPRM / W;                  // distinct swizzle values
+    static constexpr int PERIOD = P * NF;                // f(r + PERIOD) = f(r)
+    static constexpr int RPL = 1024 / RB;                // K-rows per 1 KiB wave-load
+    static constexpr int KSTEP = FMT == kBF16 ? 16 : 64; // K-rows per MFMA k-step
+    static constexpr int QSTEP = FMT == kBF16 ? 4 : FMT == kMXFP8 ? 8 : 16;   // K-rows between sub-reads
+    __device__ static constexpr int f(int r) { return W * ((r / P) % NF); }
+    static_assert(FMT != kNVFP4, "NVFP4 operands are K-major only");
+    static_assert(NF >= 1 && RB <= 1024 && KS * RB == T * kRowBytes, "slot geometry");
+    // the K-rows one lane reads lie whole periods apart: one swizzle value per lane
+    static_assert(KSTEP % PERIOD == 0 && QSTEP % PERIOD == 0, "one swizzle value per lane");
+    // the K-rows of wave-load L depend on L at most through its parity
+    static_assert(RPL % PERIOD == 0 || 2 * RPL == PERIOD, "wave-load swizzle");
+};
 
 // How MX scales reach LDS (the kernels' SM parameter):
 //  kScalesRegs:  any row stride; thread-owned byte loads through registers
@@ -275,6 +327,7 @@ struct Ctx {
     uint32_t sa, sb;                 // LDS address of the lane's MX scale row, block 0, slot 0
     uint32_t r8lda;                  // the lane's row within a wave-load times the row stride
     uint32_t x4;                     // the lane's chunk within a wave-load, swizzle applied, << 4
+    uint32_t ma[2], mb[2];           // MN-major A / B: the lane's global offset in a wave-load of parity 0 / 1
 };
 
 // Whose stages a load fetches: the tile whose operand and scale rows start
@@ -334,6 +387,76 @@ __device__ __forceinline__ typename Fmt<FMT>::Frag read_frag(const uint8_t *lds,
     } else {
         return lds_read<typename Fmt<FMT>::Frag>(lds, (fbase ^ (sel | ((uint32_t)(kk << KSH) ^ flip))) + off);
     }
+}
+
+// MN-major fragment of block `blk` (32 columns), k-step kk: the transposed
+// reads of the lane's K-rows (see Mn).  fbase is the lane's address for block
+// 0, k-step 0, slot 0 with the swizzle applied (mn_base); block and slot
+// offsets occupy bits no other term uses, so they enter by XOR, and the
+// k-step and sub-read rows are whole swizzle periods further down, so they
+// enter as immediate offsets.
+template <int FMT, int T>
+__device__ __forceinline__ typename Fmt<FMT>::Frag read_frag_mn(const uint8_t *lds, uint32_t fbase, uint32_t sel,
+                                                                int kk, int blk)
+{
+    using G = Mn<FMT, T>;
+    typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const uint32_t x = fbase ^ (sel | (uint32_t)(blk * 4 * G::EB));
+    auto rd = [&](int dr) -> i32x2 {
+        const uint8_t *ptr = lds + x + dr * G::RB;
+        if constexpr (FMT == kBF16)
+            return __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)ptr));
+        else if constexpr (FMT == kMXFP8)
+            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)ptr);
+        else
+            return __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2 *)ptr);
+    };
+    const int r = kk * G::KSTEP;
+    if constexpr (FMT == kMXFP8) {
+        // bytes 0..15: K 16h .. 16h+15; bytes 16..31: K 32+16h .. (see read_frag)
+        const i32x2 v0 = rd(r), v1 = rd(r + 8), v2 = rd(r + 32), v3 = rd(r + 40);
+        return i32x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+    } else {
+        const i32x2 v0 = rd(r), v1 = rd(r + G::QSTEP);
+        return __builtin_bit_cast(typename Fmt<FMT>::Frag, i32x4{v0[0], v0[1], v1[0], v1[1]});
+    }
+}
+
+// The lane's fragment-read address (block 0, k-step 0, slot 0) in an
+// MN-major operand region whose wave owns columns wc ..: lane 16 g + j
+// addresses K-row r0 of its read block (lane half g / 2 taking the second
+// half of each k-step) at the 8 bytes of columns 16 (g % 2) + .. that its
+// position in the group stands for.
+template <int FMT, int T>
+__device__ __forceinline__ uint32_t mn_base(int lane, int wc, int region)
+{
+    using G = Mn<FMT, T>;
+    const int g = lane >> 4, j = lane & 15;
+    int r0, cb;
+    if constexpr (FMT == kBF16) {
+        r0 = 8 * (g >> 1) + (j >> 2);                        // 4 lanes per K-row, 4 columns each
+        cb = 2 * (wc + 16 * (g & 1) + 4 * (j & 3));
+    } else if constexpr (FMT == kMXFP8) {
+        r0 = 16 * (g >> 1) + (j >> 1);                       // 2 lanes per K-row, 8 columns each
+        cb = wc + 16 * (g & 1) + 8 * (j & 1);
+    } else {
+        r0 = 32 * (g >> 1) + j;                              // 1 lane per K-row, 16 columns
+        cb = wc / 2 + 8 * (g & 1);
+    }
+    return (uint32_t)(region + r0 * G::RB + (cb ^ (G::f(r0) << 4)));
+}
+
+// The lane's global offset within an MN-major wave-load of parity `par`
+// (relative to the operand's first column of the tile; row stride ldx
+// bytes): it lands on slot byte 1024 L + 16 lane, i.e. K-row L RPL + r and
+// physical chunk pc, and fetches the logical chunk the swizzle puts there.
+template <int FMT, int T>
+__device__ __forceinline__ uint32_t mn_dma_lane(int lane, int par, int ldx)
+{
+    using G = Mn<FMT, T>;
+    const int r = (16 * lane) / G::RB, pc = ((16 * lane) % G::RB) >> 4;
+    return (uint32_t)(r * ldx + ((pc ^ G::f(r + par * G::RPL)) << 4));
 }
 
 // MX scales: lane l of a 32x32x64 scaled MFMA supplies the E8M0 scale of K
@@ -405,7 +528,10 @@ template <int FMT, class S>
 __device__ __forceinline__ void read_a(Frags<FMT, S> &f, int i, const uint8_t *lds, int slot, int kk,
                                        const Ctx<S> &c)
 {
-    f.a[i] = read_frag<FMT>(lds, c.fa, (uint32_t)(slot * S::kSlotA), kk, i);
+    if constexpr (S::AMN)
+        f.a[i] = read_frag_mn<FMT, S::TM>(lds, c.fa, (uint32_t)(slot * S::kSlotA), kk, i);
+    else
+        f.a[i] = read_frag<FMT>(lds, c.fa, (uint32_t)(slot * S::kSlotA), kk, i);
 }
 
 template <int FMT, class S>
@@ -414,7 +540,10 @@ __device__ __forceinline__ void read_b(Frags<FMT, S> &f, int j, const uint8_t *l
 {
     // with A decoded in registers, B's k-step kk is chunk 4h + kk of the row
     constexpr int KSH = adirect<FMT, S>() ? 4 : 5;
-    f.b[j] = read_frag<FMT, KSH>(lds, c.fb, (uint32_t)(slot * S::kSlotB), kk, j);
+    if constexpr (S::BMN)
+        f.b[j] = read_frag_mn<FMT, S::TN>(lds, c.fb, (uint32_t)(slot * S::kSlotB), kk, j);
+    else
+        f.b[j] = read_frag<FMT, KSH>(lds, c.fb, (uint32_t)(slot * S::kSlotB), kk, j);
 }
 
 // ------------------------------------------------------------------ scales
@@ -565,6 +694,24 @@ __device__ __forceinline__ void dma_op(uint8_t *lds, int dst, __amdgpu_buffer_rs
     const uint32_t kc = c.x4 ^ (uint32_t)((L & 7) << 4);
     const uint32_t off = (c.r8lda + kc + (uint32_t)(L * 8 * lda + k0)) | (kc < (uint32_t)(lda - k0) ? 0u : kOOB);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + dst + L * 1024), 16, off, 0, 0, 0);
+}
+
+// Wave-load L of an MN-major operand (T columns per tile) of stage ks into
+// slot bytes dst + 1024 L ..: K-rows ks KS + L RPL + .. of the operand,
+// whose rows are ldx bytes apart; `lo` holds the lane's offsets for even
+// and odd L (see mn_dma_lane).  K-rows past K lie past the end of the
+// resource (it ends with the operand) and read zero; columns past M or N
+// read the start of the next K-row, which only reaches outputs that are
+// never stored.
+template <int FMT, int T>
+__device__ __forceinline__ void dma_mn(uint8_t *lds, int dst, __amdgpu_buffer_rsrc_t rsrc, int ks,
+                                       const uint32_t (&lo)[2], int L, int q, int ldx)
+{
+    using G = Mn<FMT, T>;
+    // with 2 RPL = PERIOD the parity of L = w Q + q is that of q (Q even)
+    const int par = G::RPL % G::PERIOD == 0 ? 0 : (q & 1);
+    const uint32_t row = (uint32_t)(ks * G::KS + L * G::RPL) * (uint32_t)ldx;   // wave-uniform
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + dst + L * 1024), 16, lo[par] + row, 0, 0, 0);
 }
 
 // Wave w issues wave-loads w*Q + q, q < Q, of each operand.
@@ -897,8 +1044,22 @@ __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int sl
         load_fp4(P.fp4, tg, ks, c, p.lda, p.sld);
         if constexpr (adirect<FMT, S>()) load_fp4_a(P.fp4a, tg, ks, c, p.lda, p.sld);
     } else {
-        if (q < S::QA) dma_a(lds, slot, tg, ks, c, q, p.lda);
-        if (q < S::QB) dma_b(lds, slot, tg, ks, c, q, p.lda);
+        if (q < S::QA) {
+            if constexpr (S::AMN) {
+                static_assert(Mn<FMT, S::TM>::RPL % Mn<FMT, S::TM>::PERIOD == 0 || S::QA % 2 == 0, "parity");
+                dma_mn<FMT, S::TM>(lds, S::kLdsA + slot * S::kSlotA, tg.ra, ks, c.ma, c.w * S::QA + q, q, p.ldam);
+            } else {
+                dma_a(lds, slot, tg, ks, c, q, p.lda);
+            }
+        }
+        if (q < S::QB) {
+            if constexpr (S::BMN) {
+                static_assert(Mn<FMT, S::TN>::RPL % Mn<FMT, S::TN>::PERIOD == 0 || S::QB % 2 == 0, "parity");
+                dma_mn<FMT, S::TN>(lds, S::kLdsB + slot * S::kSlotB, tg.rb, ks, c.mb, c.w * S::QB + q, q, p.ldbm);
+            } else {
+                dma_b(lds, slot, tg, ks, c, q, p.lda);
+            }
+        }
         if constexpr (FMT == kMXFP8 || FMT == kMXFP4) {
             if (q == npieces<FMT, S>() - 1) {
                 if constexpr (SM == kScalesStage)
@@ -1012,8 +1173,11 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
 template <class S>
 __device__ __forceinline__ void opaque(Ctx<S> &c)
 {
-    asm volatile("" : "+v"(c.t), "+v"(c.lane), "+v"(c.r8lda), "+v"(c.x4), "+v"(c.sa), "+v"(c.sb));
+    asm volatile("" : "+v"(c.t), "+v"(c.lane), "+v"(c.sa), "+v"(c.sb));
+    if constexpr (!S::AMN || !S::BMN) asm volatile("" : "+v"(c.r8lda), "+v"(c.x4));
     asm volatile("" : "+v"(c.fa), "+v"(c.fb));
+    if constexpr (S::AMN) asm volatile("" : "+v"(c.ma[0]), "+v"(c.ma[1]));
+    if constexpr (S::BMN) asm volatile("" : "+v"(c.mb[0]), "+v"(c.mb[1]));
 }
 
 template <int FMT, class S, int SM>
@@ -1049,8 +1213,21 @@ __device__ __forceinline__ Target tile_target(const Params &p, int tile)
     const TileRef r = tile_ref<S::TM, S::TN>(tile, p);
     const int rows_a = min(r.mend - r.m0, S::TM), rows_b = min(p.N - r.n0, S::TN);
     Target t;
-    t.ra = make_rsrc(p.A + (int64_t)r.m0 * p.lda, (uint32_t)(rows_a * p.lda));
-    t.rb = make_rsrc(p.B + r.boff + (int64_t)r.n0 * p.lda, (uint32_t)(rows_b * p.lda));
+    if constexpr (S::AMN) {
+        // from the tile's first column to the end of the K x M operand
+        constexpr int EB = Mn<FMT, S::TM>::EB;
+        const int64_t c0 = (int64_t)r.m0 * EB / 8;
+        t.ra = make_rsrc(p.A + c0, (uint32_t)((int64_t)p.K * p.ldam - c0));
+    } else {
+        t.ra = make_rsrc(p.A + (int64_t)r.m0 * p.lda, (uint32_t)(rows_a * p.lda));
+    }
+    if constexpr (S::BMN) {
+        constexpr int EB = Mn<FMT, S::TN>::EB;
+        const int64_t c0 = (int64_t)r.n0 * EB / 8;
+        t.rb = make_rsrc(p.B + c0, (uint32_t)((int64_t)p.K * p.ldbm - c0));
+    } else {
+        t.rb = make_rsrc(p.B + r.boff + (int64_t)r.n0 * p.lda, (uint32_t)(rows_b * p.lda));
+    }
     t.rsa = t.ra;
     t.rsb = t.rb;
     if constexpr (FMT != kBF16) {
@@ -1095,6 +1272,16 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
     }
     c.r8lda = (uint32_t)((c.lane >> 3) * p.lda);
     c.x4 = (uint32_t)(((c.lane & 7) ^ (c.lane >> 3)) << 4);
+    if constexpr (S::AMN) {
+        c.fa = mn_base<FMT, S::TM>(c.lane, c.wm * (S::TM / S::WM), S::kLdsA);
+        c.ma[0] = mn_dma_lane<FMT, S::TM>(c.lane, 0, p.ldam);
+        c.ma[1] = mn_dma_lane<FMT, S::TM>(c.lane, 1, p.ldam);
+    }
+    if constexpr (S::BMN) {
+        c.fb = mn_base<FMT, S::TN>(c.lane, c.wn * (S::TN / S::WN), S::kLdsB);
+        c.mb[0] = mn_dma_lane<FMT, S::TN>(c.lane, 0, p.ldbm);
+        c.mb[1] = mn_dma_lane<FMT, S::TN>(c.lane, 1, p.ldbm);
+    }
 
     const int ntiles = p.tiles_m * p.tiles_n;
     const int nwg = gridDim.x, wg = blockIdx.x;
@@ -1478,12 +1665,23 @@ constexpr int stage_elems()
     return FMT == kBF16 || FMT == kNVFP4 ? kRowBytes / 2 : FMT == kMXFP8 ? kRowBytes : 2 * kRowBytes;
 }
 
-template <int FMT, int SM, class S>
+template <int FMT, int SM, class S0>
 hipError_t launch_one(const Params &p0, int grid, hipStream_t stream)
 {
     Params p = p0;
-    p.nk = (p.K + stage_elems<FMT, S>() - 1) / stage_elems<FMT, S>();
-    hipLaunchKernelGGL((gemm_kernel<FMT, S, SM>), dim3(grid), dim3(S::kThreads), 0, stream, p);
+    p.nk = (p.K + stage_elems<FMT, S0>() - 1) / stage_elems<FMT, S0>();
+    if constexpr (FMT == kNVFP4) {
+        if (p.lay != 0) return hipErrorInvalidValue;   // the host rejects MN-major NVFP4
+        hipLaunchKernelGGL((gemm_kernel<FMT, S0, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p);
+    } else {
+        switch (p.lay) {
+        case 0: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 0>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+        case 1: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 1>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 2>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+        case 3: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 3>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+        }
+    }
     return hipGetLastError();
 }
 

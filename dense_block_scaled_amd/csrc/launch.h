@@ -14,8 +14,8 @@ constexpr int kMaxGroups = 64;
 // Everything a kernel needs, passed by value.  Sizes were validated on the
 // host: every per-tile byte offset fits in 31 bits.
 struct Params {
-    const uint8_t *A;     // M x lda bytes
-    const uint8_t *B;     // N x lda bytes
+    const uint8_t *A;     // M x lda bytes (K x ldam if MN-major)
+    const uint8_t *B;     // N x lda bytes (K x ldbm if MN-major)
     const uint8_t *sA;    // M x sld scale bytes (null for bf16)
     const uint8_t *sB;    // N x sld scale bytes
     uint16_t *D;          // M x N bf16
@@ -28,6 +28,8 @@ struct Params {
     int vec_store;        // 1 if D rows allow 8-byte stores (N % 4 == 0)
     int vec16;            // 1 if D rows allow 16-byte stores (N % 8 == 0, D 16-byte aligned)
     int scales_aligned;   // 1 if every scale row starts on a 4-byte boundary
+    int lay;              // bit 0: A stored MN-major (K x M), bit 1: B stored MN-major (K x N)
+    int ldam, ldbm;       // MN-major A / B: bytes per K-row (M or N elements)
     float alpha;          // applied to the fp32 accumulator before rounding
     // Grouped GEMM (ngroups > 0): group g owns rows goff[g] .. goff[g+1]-1 of A
     // and D, the g-th N x K block of B (and of sB) and output tiles

@@ -16,9 +16,12 @@
  *   gemm_nvfp4  E2M1 elements, one E4M3 scale per 16 K elements, alpha = tA * tB
  *
  * Memory (all pointers are DEVICE pointers; dense, no leading dimensions):
- *   A   : M rows of K elements.  bf16: 2 bytes/element; E4M3: 1 byte; E2M1:
- *         two elements per byte, element 2j in bits [3:0], 2j+1 in bits [7:4].
- *   B   : N rows, same encoding as A.
+ *   A   : M rows of K elements (K-major, the default).  bf16: 2 bytes/element;
+ *         E4M3: 1 byte; E2M1: two elements per byte, element 2j in bits [3:0],
+ *         2j+1 in bits [7:4].  MN-major (la = DBS_MN_MAJOR): K rows of M
+ *         elements, i.e. A^T stored K-major, E2M1 pairs then packing
+ *         consecutive M of one K-row (element (k, 2i) in bits [3:0]).
+ *   B   : N rows, same encoding as A (MN-major: K rows of N elements).
  *   sA  : M rows of K/bs scale codes (1 byte each), row-major; bs = 32 (MX),
  *         16 (NVFP4).  sB likewise with N rows.
  *   D   : M x N bf16, row-major, fully overwritten.  Must not alias inputs.
@@ -34,9 +37,9 @@
  * Errors: DBS_EINVAL is returned before any device work for a null pointer,
  * M, N or K <= 0, a K the format cannot take (see each entry point), a base
  * pointer of A or B not 16-byte aligned, or sizes beyond the documented
- * limits.  DBS_EUNSUPPORTED marks valid requests not implemented here (the
- * MN-major layouts).  DBS_EHIP means the HIP runtime reported an error (no
- * device, launch failure); dbs_last_error() then holds its text.
+ * limits.  DBS_EUNSUPPORTED marks valid requests not implemented here (see
+ * dbs_layout and gemm_nvfp4).  DBS_EHIP means the HIP runtime reported an
+ * error (no device, launch failure); dbs_last_error() then holds its text.
  */
 #ifndef DBS_H
 #define DBS_H
@@ -61,7 +64,14 @@ typedef enum {
 } dbs_status;
 
 /* Per-operand layout.  K_MAJOR: A is M x K, B is N x K with K contiguous.
- * MN_MAJOR (A stored K x M, B stored K x N) is reserved: DBS_EUNSUPPORTED. */
+ * MN_MAJOR: A stored K x M, B stored K x N (M or N contiguous); the kernels
+ * stage such tiles as K-rows and read MFMA fragments out of them with the
+ * gfx950 transposed LDS reads, the role the "Dissecting ThunderKittens"
+ * write-up gives to layout-aware tile loads (register tiles).  Taken by
+ * gemm_bf16 and gemm_mx, for A and B independently, when each MN-major
+ * operand's K-rows are whole 16-byte chunks (M or N times the element bits a
+ * multiple of 128) and it stays below 2 GiB; DBS_EUNSUPPORTED otherwise, and
+ * for gemm_nvfp4 and the grouped GEMMs (K-major only). */
 typedef enum {
     DBS_K_MAJOR = 0,
     DBS_MN_MAJOR = 1

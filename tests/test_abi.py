@@ -48,7 +48,9 @@ NUL = ctypes.c_void_p(0)
     ((FAKE, FAKE, FAKE, 16, 16, 12, 0, 0), 1),         # K % 8
     ((FAKE, FAKE, FAKE, 16, 16, 1 << 22, 0, 0), 1),    # K too large
     ((ctypes.c_void_p((1 << 20) + 4), FAKE, FAKE, 16, 16, 16, 0, 0), 1),  # misaligned A
-    ((FAKE, FAKE, FAKE, 16, 16, 16, 1, 0), 2),         # MN-major A: unsupported
+    ((FAKE, FAKE, FAKE, 12, 16, 16, 1, 0), 2),         # MN-major A, K-rows of 24 bytes
+    ((FAKE, FAKE, FAKE, 16, 20, 16, 0, 1), 2),         # MN-major B, K-rows of 40 bytes
+    ((FAKE, FAKE, FAKE, 1 << 16, 16, 1 << 14, 1, 0), 2),  # MN-major A of 2 GiB
     ((FAKE, FAKE, FAKE, 16, 16, 16, 0, 7), 1),         # unknown layout
 ])
 def test_bf16_validation(args, want):
@@ -69,10 +71,36 @@ def test_mx_null_scales():
     assert L.gemm_mx(0, FAKE, NUL, FAKE, FAKE, FAKE, 8, 8, 64, 0, 0, NUL) == 1
 
 
-@pytest.mark.parametrize("K,want", [(24, 1), (48, 2)])
-def test_nvfp4_validation(K, want):
+@pytest.mark.parametrize("K,lay,want", [(24, (0, 0), 1), (48, (0, 0), 2), (64, (1, 0), 2), (64, (0, 1), 2)])
+def test_nvfp4_validation(K, lay, want):
     L = dbs.lib()
-    assert L.gemm_nvfp4(FAKE, FAKE, 1.0, FAKE, FAKE, 1.0, FAKE, 8, 8, K, 0, 0, NUL) == want
+    assert L.gemm_nvfp4(FAKE, FAKE, 1.0, FAKE, FAKE, 1.0, FAKE, 64, 64, K, *lay, NUL) == want
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would reach a real device")
+@pytest.mark.parametrize("fmt,M,N,lay", [("bf16", 8, 24, (1, 1)), ("e4m3", 16, 48, (1, 0)), ("e2m1", 64, 32, (0, 1))])
+def test_mn_major_passes_validation(fmt, M, N, lay):
+    """MN-major operands with whole 16-byte K-rows get past validation (to
+    the device lookup, which fails here without a GPU)."""
+    L = dbs.lib()
+    if fmt == "bf16":
+        st = L.gemm_bf16(FAKE, FAKE, FAKE, M, N, 64, *lay, NUL)
+    else:
+        st = L.gemm_mx(0 if fmt == "e4m3" else 4, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, 64, *lay, NUL)
+    assert st == 3, dbs.status_str(st)
+
+
+def test_binding_layout_shapes():
+    """The binding reads M, N and K from MN-major shapes and checks them."""
+    A = torch.zeros((32, 8), dtype=torch.bfloat16)          # MN-major: K = 32, M = 8
+    B = torch.zeros((24, 32), dtype=torch.bfloat16)         # K-major: N = 24
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dbs.gemm_bf16(A, B, la=dbs.MN_MAJOR)
+    with pytest.raises(ValueError, match="layout"):
+        dbs.gemm_bf16(A, B, la=5)
+    assert dbs._shape(8, 32, dbs.MN_MAJOR) == (32, 8)
+    assert dbs._shape(64, 32, dbs.MN_MAJOR, 2) == (32, 32)
+    assert dbs._rows(torch.zeros((32, 16), dtype=torch.uint8), dbs.MN_MAJOR, 2) == 32
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would reach a real device")
