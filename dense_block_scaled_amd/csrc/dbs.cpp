@@ -194,7 +194,6 @@ dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA, const void *B,
     dbs_status st = check_common(A, B, D, M, N, K, la, lb, int64_t(1) << 22);
     if (st != DBS_OK) return st;
     if (K % 16) return fail(DBS_EINVAL, "nvfp4: K must be a multiple of 16");
-    if (K % 32) return fail(DBS_EUNSUPPORTED, "nvfp4: K must be a multiple of 32 in this implementation");
     if (la != DBS_K_MAJOR || lb != DBS_K_MAJOR)
         return fail(DBS_EUNSUPPORTED, "nvfp4: only K-major A and B are implemented");
     return run(dbs::kNVFP4, A, sA, B, sB, D, M, N, K, tA * tB, 4, 16, stream);
@@ -306,7 +305,6 @@ dbs_status gemm_grouped_nvfp4(const void *A, const uint8_t *sA, float tA, const 
     if (st != DBS_OK) return st;
     if ((st = check_common(A, B, D, M, N, K, DBS_K_MAJOR, DBS_K_MAJOR, int64_t(1) << 22)) != DBS_OK) return st;
     if (K % 16) return fail(DBS_EINVAL, "nvfp4: K must be a multiple of 16");
-    if (K % 32) return fail(DBS_EUNSUPPORTED, "nvfp4: K must be a multiple of 32 in this implementation");
     float alpha[dbs::kMaxGroups];
     for (int64_t g = 0; g < G; ++g) alpha[g] = tA * tB[g];
     const Groups gr{offsets, G, alpha};

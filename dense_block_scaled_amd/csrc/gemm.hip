@@ -291,6 +291,14 @@ struct Mn {
 //                stage's operand slabs).
 constexpr int kScalesRegs = 0, kScalesStage = 1, kScalesChunk = 2;
 constexpr int kScaleChunk = 16;
+// NVFP4 has no MX scales; its SM parameter says whether K ends on a whole
+// 32-element half-row (kNvWhole) or halfway through one (kNvHalf: K % 32 ==
+// 16, which the format allows).  Then packed rows (K/2 bytes) start on
+// 8-byte boundaries only and scale rows (K/16 bytes) on byte boundaries, so
+// the loader fetches each half-row as two 8-byte pieces and its two scales
+// as single bytes, and the past-K piece of a row's last half reads zero
+// codes and a zero scale.
+constexpr int kNvWhole = 1, kNvHalf = 3;
 
 template <int FMT>
 constexpr int scale_spc() { return Fmt<FMT>::BPS > 0 ? kScaleChunk / Fmt<FMT>::BPS : 1; }
@@ -748,7 +756,37 @@ struct Fp4Regs {
     uint32_t s[fp4_units<S, AD>()];
 };
 
-template <class S, bool AD>
+// Packed bytes ks*32 + hoff .. +15 of a row (hoff = 16 * half) and its two
+// scale bytes ks*4 + hoff/8 .. +1.  kNvWhole: each half is all in or all out
+// (the two halves of a last stage can differ).  kNvHalf: the two 8-byte
+// pieces of the half (and their scales) are in or out separately.  The
+// out-of-range flag rides in the vector offset; the scalar offset carries
+// only the in-range stage offset.
+template <int SM>
+__device__ __forceinline__ void load_fp4_half(i32x4 &v, uint32_t &sc, __amdgpu_buffer_rsrc_t rs,
+                                              __amdgpu_buffer_rsrc_t rss, int row, int hoff, int ks, int lda, int sld)
+{
+    const int hb = ks * 32 + hoff;                     // the half's first byte in the row
+    const uint32_t pad = hb < lda ? 0u : kOOB;
+    if constexpr (SM == kNvHalf) {
+        const uint32_t pad1 = hb + 8 < lda ? 0u : kOOB;
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                       rs, (uint32_t)(row * lda + hoff) | pad, (uint32_t)(ks * 32), 0));
+        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                       rs, (uint32_t)(row * lda + hoff + 8) | pad1, (uint32_t)(ks * 32), 0));
+        v = i32x4{(int)lo[0], (int)lo[1], (int)hi[0], (int)hi[1]};
+        const uint32_t s0 = __builtin_amdgcn_raw_buffer_load_b8(rss, (uint32_t)(row * sld + hoff / 8) | pad,
+                                                                 (uint32_t)(ks * 4), 0);
+        const uint32_t s1 = __builtin_amdgcn_raw_buffer_load_b8(rss, (uint32_t)(row * sld + hoff / 8 + 1) | pad1,
+                                                                 (uint32_t)(ks * 4), 0);
+        sc = s0 | (s1 << 8);
+    } else {
+        v = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(row * lda + hoff) | pad, (uint32_t)(ks * 32), 0);
+        sc = __builtin_amdgcn_raw_buffer_load_b16(rss, (uint32_t)(row * sld + hoff / 8) | pad, (uint32_t)(ks * 4), 0);
+    }
+}
+
+template <int SM, class S, bool AD>
 __device__ __forceinline__ void load_fp4(Fp4Regs<S, AD> &r, const Target &tg, int ks, const Ctx<S> &c, int lda,
                                          int sld)
 {
@@ -760,16 +798,8 @@ __device__ __forceinline__ void load_fp4(Fp4Regs<S, AD> &r, const Target &tg, in
             const bool is_a = u0 < 2 * TA;
             const int hr = u0 + c.lane - (is_a ? 0 : 2 * TA);
             const int row = hr >> 1, half = hr & 1;
-            // packed bytes ks*32 + half*16 .. +15 and scale bytes ks*4 + half*2
-            // .. +1 of the row.  K % 32 == 0, so each half is all in or all
-            // out (the two halves of a last stage can differ).  The
-            // out-of-range flag rides in the vector offset; the scalar offset
-            // carries only the in-range stage offset.
-            const uint32_t pad = ks * 32 + half * 16 < lda ? 0u : kOOB;
-            r.v[k] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? tg.ra : tg.rb,
-                                                           (uint32_t)(row * lda + half * 16) | pad, (uint32_t)(ks * 32), 0);
-            r.s[k] = __builtin_amdgcn_raw_buffer_load_b16(is_a ? tg.rsa : tg.rsb, (uint32_t)(row * sld + half * 2) | pad,
-                                                          (uint32_t)(ks * 4), 0);
+            load_fp4_half<SM>(r.v[k], r.s[k], is_a ? tg.ra : tg.rb, is_a ? tg.rsa : tg.rsb, row, half * 16, ks, lda,
+                              sld);
         }
     }
 }
@@ -831,17 +861,13 @@ struct Fp4A {
     uint32_t s[S::MB];
 };
 
-template <class S>
+template <int SM, class S>
 __device__ __forceinline__ void load_fp4_a(Fp4A<S> &r, const Target &tg, int ks, const Ctx<S> &c, int lda, int sld)
 {
-    const uint32_t pad = ks * 32 + c.h * 16 < lda ? 0u : kOOB;
 #pragma unroll
     for (int i = 0; i < S::MB; ++i) {
         const int row = c.wm * (S::TM / S::WM) + i * 32 + c.lr;
-        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(tg.ra, (uint32_t)(row * lda + c.h * 16) | pad, (uint32_t)(ks * 32),
-                                                       0);
-        r.s[i] = __builtin_amdgcn_raw_buffer_load_b16(tg.rsa, (uint32_t)(row * sld + c.h * 2) | pad, (uint32_t)(ks * 4),
-                                                      0);
+        load_fp4_half<SM>(r.v[i], r.s[i], tg.ra, tg.rsa, row, c.h * 16, ks, lda, sld);
     }
 }
 
@@ -1041,8 +1067,8 @@ __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int sl
                                            const ChunkPos &cp)
 {
     if constexpr (FMT == kNVFP4) {
-        load_fp4(P.fp4, tg, ks, c, p.lda, p.sld);
-        if constexpr (adirect<FMT, S>()) load_fp4_a(P.fp4a, tg, ks, c, p.lda, p.sld);
+        load_fp4<SM>(P.fp4, tg, ks, c, p.lda, p.sld);
+        if constexpr (adirect<FMT, S>()) load_fp4_a<SM>(P.fp4a, tg, ks, c, p.lda, p.sld);
     } else {
         if (q < S::QA) {
             if constexpr (S::AMN) {
@@ -1708,6 +1734,10 @@ hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
             hipLaunchKernelGGL(gemm_nvfp4_raw_kernel, dim3(grid), dim3(nv::S::kThreads), 0, stream, q);
             return hipGetLastError();
         }
+    }
+    if constexpr (FMT == kNVFP4) {
+        if (p.K % 32) return launch_one<FMT, kNvHalf, S>(p, grid, stream);
+        return launch_one<FMT, kNvWhole, S>(p, grid, stream);
     }
     // stages that arrive entirely by direct-to-LDS loads get a deeper ring
     // when every tile has enough stages to fill it

@@ -104,9 +104,9 @@ dbs_status gemm_mx(dbs_mx_elem elem,
 
 /*
  * NVFP4 GEMM: packed E2M1 elements, E4M3 block scales sA (M x K/16) and sB
- * (N x K/16), per-tensor fp32 scales tA, tB; D = bf16(tA*tB * sum).  The
- * format fixes K to a multiple of 16; this implementation needs a multiple
- * of 32 (DBS_EUNSUPPORTED otherwise), at most 2^22.
+ * (N x K/16), per-tensor fp32 scales tA, tB; D = bf16(tA*tB * sum).  K must
+ * be a multiple of 16 (the format's block), at most 2^22.  K-major A and B
+ * only (DBS_EUNSUPPORTED for MN-major).
  */
 dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA,
                       const void *B, const uint8_t *sB, float tB, void *D,

@@ -71,22 +71,27 @@ def test_mx_null_scales():
     assert L.gemm_mx(0, FAKE, NUL, FAKE, FAKE, FAKE, 8, 8, 64, 0, 0, NUL) == 1
 
 
-@pytest.mark.parametrize("K,lay,want", [(24, (0, 0), 1), (48, (0, 0), 2), (64, (1, 0), 2), (64, (0, 1), 2)])
+@pytest.mark.parametrize("K,lay,want", [(24, (0, 0), 1), (40, (0, 0), 1), (64, (1, 0), 2), (64, (0, 1), 2)])
 def test_nvfp4_validation(K, lay, want):
     L = dbs.lib()
     assert L.gemm_nvfp4(FAKE, FAKE, 1.0, FAKE, FAKE, 1.0, FAKE, 64, 64, K, *lay, NUL) == want
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would reach a real device")
-@pytest.mark.parametrize("fmt,M,N,lay", [("bf16", 8, 24, (1, 1)), ("e4m3", 16, 48, (1, 0)), ("e2m1", 64, 32, (0, 1))])
-def test_mn_major_passes_validation(fmt, M, N, lay):
-    """MN-major operands with whole 16-byte K-rows get past validation (to
-    the device lookup, which fails here without a GPU)."""
+@pytest.mark.parametrize("fmt,M,N,K,lay", [("bf16", 8, 24, 64, (1, 1)), ("e4m3", 16, 48, 64, (1, 0)),
+                                            ("e2m1", 64, 32, 64, (0, 1)), ("nvfp4", 8, 8, 48, (0, 0)),
+                                            ("nvfp4", 8, 8, 16, (0, 0))])
+def test_valid_requests_pass_validation(fmt, M, N, K, lay):
+    """MN-major operands with whole 16-byte K-rows, and NVFP4 with K an odd
+    multiple of 16, get past validation (to the device lookup, which fails
+    here without a GPU)."""
     L = dbs.lib()
     if fmt == "bf16":
-        st = L.gemm_bf16(FAKE, FAKE, FAKE, M, N, 64, *lay, NUL)
+        st = L.gemm_bf16(FAKE, FAKE, FAKE, M, N, K, *lay, NUL)
+    elif fmt == "nvfp4":
+        st = L.gemm_nvfp4(FAKE, FAKE, 1.0, FAKE, FAKE, 1.0, FAKE, M, N, K, *lay, NUL)
     else:
-        st = L.gemm_mx(0 if fmt == "e4m3" else 4, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, 64, *lay, NUL)
+        st = L.gemm_mx(0 if fmt == "e4m3" else 4, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, *lay, NUL)
     assert st == 3, dbs.status_str(st)
 
 

@@ -89,3 +89,16 @@ def test_grouped_square_tiles(fmt):
             continue
         em, en = synth.sample_entries(9 + g, b - a, N, 1024)
         _gpu.check_sampled(fmt, _group_w(fmt, w, g), D[a:b].contiguous(), em, en, label=f"group {g}")
+
+
+def test_grouped_nvfp4_k_odd_multiple_of_16():
+    """NVFP4 groups with K = 80 (an odd multiple of 16)."""
+    sizes, N, K = [5, 300, 0, 64], 96, 80
+    _gpu.say(f"[grouped] nvfp4 sizes={sizes} N={N} K={K}")
+    w = _grouped_w("nvfp4", sizes, N, K, seed=10)
+    D = _run_grouped("nvfp4", w)
+    torch.cuda.synchronize()
+    for g in range(w["G"]):
+        a, b = int(w["off"][g]), int(w["off"][g + 1])
+        if a < b:
+            _gpu.check_full("nvfp4", _group_w("nvfp4", w, g), D[a:b])

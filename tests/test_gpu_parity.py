@@ -199,6 +199,36 @@ def test_exact_bf16_integers(shape):
     _gpu.check_exact("bf16", w, D)
 
 
+@pytest.mark.parametrize("shape", [(300, 520, 80), (257, 129, 16), (33, 7, 48), (256, 20000, 336),
+                                   (3000, 2900, 208)], ids=lambda s: "x".join(map(str, s)))
+def test_nvfp4_k_odd_multiple_of_16(shape):
+    """K an odd multiple of 16, which the NVFP4 format allows: packed rows
+    start on 8-byte and scale rows on byte boundaries, and each row ends with
+    one 16-element block of a 32-element half-row (256 x 64 and 256 x 256
+    tiles)."""
+    M, N, K = shape
+    _gpu.say(f"[parity] nvfp4 K % 32 == 16 {shape}")
+    w = _w("nvfp4", M, N, K, seed=9)
+    D = _gpu.run("nvfp4", w)
+    torch.cuda.synchronize()
+    _gpu.check_full("nvfp4", w, D)
+
+
+@pytest.mark.parametrize("mk", [(300, 208), (3000, 2960)], ids=lambda s: "x".join(map(str, s)))
+def test_exact_nvfp4_k_odd_multiple_of_16(mk):
+    """The permutation test with K an odd multiple of 16, bit for bit."""
+    M, K = mk
+    _gpu.say(f"[exact] nvfp4 permutation {M}x{K}x{K}")
+    w = _identity_w("nvfp4", M, K, np.random.default_rng(37), True)
+    D = _gpu.run("nvfp4", w)
+    torch.cuda.synchronize()
+    if M * K <= 1 << 20:
+        _gpu.check_exact("nvfp4", w, D)
+    else:
+        em, en = synth.sample_entries(38, M, K, 4096)
+        _gpu.check_exact_sampled("nvfp4", w, D, em, en)
+
+
 def test_exact_nvfp4_tensor_scales():
     """NVFP4 with power-of-two tensor scales tA = 2, tB = 0.25 on an identity B."""
     _gpu.say("[exact] nvfp4 tensor scales")
