@@ -7,7 +7,9 @@ package never imports the product.
 
 The arithmetic lives in ``oracle.c`` (built into ``liboracle.so`` by
 ``oracle/build.py``); this module only marshals numpy arrays.  Kinds:
-0 = BF16, 1 = MXFP8, 2 = MXFP4, 3 = NVFP4.
+0 = BF16, 1 = MXFP8, 2 = MXFP4, 3 = NVFP4, 4 = MX with E5M2 elements.  For
+fmt 'mxfp8' a workload may name each operand's 8-bit element format in
+w['elemA'] / w['elemB'] ('e4m3', the default, or 'e5m2').
 """
 from __future__ import annotations
 
@@ -39,20 +41,22 @@ def _load():
     lib.orc_decode_e4m3.restype = ctypes.c_double
     lib.orc_decode_e8m0.restype = ctypes.c_double
     lib.orc_decode_bf16.restype = ctypes.c_double
-    for f in (lib.orc_decode_e2m1, lib.orc_decode_e4m3, lib.orc_decode_e8m0, lib.orc_decode_bf16):
+    lib.orc_decode_e5m2.restype = ctypes.c_double
+    for f in (lib.orc_decode_e2m1, lib.orc_decode_e4m3, lib.orc_decode_e8m0, lib.orc_decode_bf16,
+              lib.orc_decode_e5m2):
         f.argtypes = [ctypes.c_uint]
-    for f in (lib.orc_encode_e2m1, lib.orc_encode_e4m3, lib.orc_encode_bf16):
+    for f in (lib.orc_encode_e2m1, lib.orc_encode_e4m3, lib.orc_encode_bf16, lib.orc_encode_e5m2):
         f.argtypes = [ctypes.c_double]
         f.restype = ctypes.c_uint
     lib.orc_decode_array.argtypes = [ctypes.c_int, P, I64, P]
     lib.orc_encode_array.argtypes = [ctypes.c_int, P, I64, P]
     lib.orc_set_mutation.argtypes = [ctypes.c_int]
-    lib.orc_gemm_entries.argtypes = [ctypes.c_int, P, P, ctypes.c_double, P, P, ctypes.c_double,
-                                     I64, I64, I64, P, P, I64, P, P, P, ctypes.c_int]
-    lib.orc_gemm_entries.restype = ctypes.c_int
-    lib.orc_gemm_full.argtypes = [ctypes.c_int, P, P, ctypes.c_double, P, P, ctypes.c_double,
-                                  I64, I64, I64, P, P, P, ctypes.c_int]
-    lib.orc_gemm_full.restype = ctypes.c_int
+    lib.orc_gemm_entries2.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_double, P, P, ctypes.c_double,
+                                      I64, I64, I64, P, P, I64, P, P, P, ctypes.c_int]
+    lib.orc_gemm_entries2.restype = ctypes.c_int
+    lib.orc_gemm_full2.argtypes = [ctypes.c_int, ctypes.c_int, P, P, ctypes.c_double, P, P, ctypes.c_double,
+                                   I64, I64, I64, P, P, P, ctypes.c_int]
+    lib.orc_gemm_full2.restype = ctypes.c_int
     lib.orc_quant_mx.argtypes = [ctypes.c_int, P, I64, I64, P, P]
     lib.orc_quant_mx.restype = ctypes.c_int
     lib.orc_quant_nvfp4.argtypes = [P, I64, I64, P, P, P]
@@ -85,9 +89,9 @@ def set_mutation(m: int) -> None:
 # ---- formats -------------------------------------------------------------
 
 def decode(fmt: str, codes) -> np.ndarray:
-    """Decode codes to float64: fmt in {'e2m1', 'e4m3', 'e8m0', 'bf16'}."""
+    """Decode codes to float64: fmt in {'e2m1', 'e4m3', 'e5m2', 'e8m0', 'bf16'}."""
     lib = _load()
-    idx = {"e2m1": 0, "e4m3": 1, "e8m0": 2, "bf16": 3}[fmt]
+    idx = {"e2m1": 0, "e4m3": 1, "e8m0": 2, "bf16": 3, "e5m2": 4}[fmt]
     c = _c(codes, np.uint16 if fmt == "bf16" else np.uint8).ravel()
     out = np.empty(c.size, dtype=np.float64)
     lib.orc_decode_array(idx, _ptr(c), c.size, _ptr(out))
@@ -95,9 +99,9 @@ def decode(fmt: str, codes) -> np.ndarray:
 
 
 def encode(fmt: str, x) -> np.ndarray:
-    """Nearest-even encode of float64 values: fmt in {'e2m1','e4m3','bf16'}."""
+    """Nearest-even encode of float64 values: fmt in {'e2m1','e4m3','e5m2','bf16'}."""
     lib = _load()
-    idx = {"e2m1": 0, "e4m3": 1, "bf16": 3}[fmt]
+    idx = {"e2m1": 0, "e4m3": 1, "bf16": 3, "e5m2": 4}[fmt]
     v = _c(x, np.float64).ravel()
     out = np.empty(v.size, dtype=np.uint16 if fmt == "bf16" else np.uint8)
     lib.orc_encode_array(idx, _ptr(v), v.size, _ptr(out))
@@ -115,14 +119,21 @@ def unpack_fp4(packed: np.ndarray) -> np.ndarray:
 
 # ---- GEMM ----------------------------------------------------------------
 
+_MX8 = {"e4m3": 1, "e5m2": 4}
+
+
 def _operands(fmt, w):
+    """(kind of A, kind of B, A, sA, tA, B, sB, tB) of workload w."""
     kind = KINDS[fmt]
     if fmt == "bf16":
         A, B = _c(w["A"], np.uint16), _c(w["B"], np.uint16)
-        return kind, A, None, 1.0, B, None, 1.0
+        return kind, kind, A, None, 1.0, B, None, 1.0
+    ka = kb = kind
+    if fmt == "mxfp8":
+        ka, kb = _MX8[w.get("elemA", "e4m3")], _MX8[w.get("elemB", "e4m3")]
     A, B = _c(w["A"], np.uint8), _c(w["B"], np.uint8)
     sA, sB = _c(w["sA"], np.uint8), _c(w["sB"], np.uint8)
-    return kind, A, sA, float(w.get("tA", 1.0)), B, sB, float(w.get("tB", 1.0))
+    return ka, kb, A, sA, float(w.get("tA", 1.0)), B, sB, float(w.get("tB", 1.0))
 
 
 def gemm_entries(fmt: str, w: dict, em, en, nthreads: int | None = None):
@@ -133,14 +144,14 @@ def gemm_entries(fmt: str, w: dict, em, en, nthreads: int | None = None):
     arrays, with ``anorm = ||dA_m|| * |tA|`` and ``bnorm = ||dB_n|| * |tB|``.
     """
     lib = _load()
-    kind, A, sA, tA, B, sB, tB = _operands(fmt, w)
+    ka, kb, A, sA, tA, B, sB, tB = _operands(fmt, w)
     em = _c(em, np.int64)
     en = _c(en, np.int64)
     n = em.size
     d = np.empty(n, np.float64)
     an = np.empty(n, np.float64)
     bn = np.empty(n, np.float64)
-    rc = lib.orc_gemm_entries(kind, _ptr(A), _ptr(sA), tA, _ptr(B), _ptr(sB), tB,
+    rc = lib.orc_gemm_entries2(ka, kb, _ptr(A), _ptr(sA), tA, _ptr(B), _ptr(sB), tB,
                               w["M"], w["N"], w["K"], _ptr(em), _ptr(en), n,
                               _ptr(d), _ptr(an), _ptr(bn), nthreads or default_threads())
     if rc != 0:
@@ -151,12 +162,12 @@ def gemm_entries(fmt: str, w: dict, em, en, nthreads: int | None = None):
 def gemm_full(fmt: str, w: dict, nthreads: int | None = None, norms: bool = True):
     """All M x N entries of D_ref (row-major) and, if ``norms``, the norms."""
     lib = _load()
-    kind, A, sA, tA, B, sB, tB = _operands(fmt, w)
+    ka, kb, A, sA, tA, B, sB, tB = _operands(fmt, w)
     M, N = w["M"], w["N"]
     d = np.empty((M, N), np.float64)
     an = np.empty((M, N), np.float64) if norms else None
     bn = np.empty((M, N), np.float64) if norms else None
-    rc = lib.orc_gemm_full(kind, _ptr(A), _ptr(sA), tA, _ptr(B), _ptr(sB), tB,
+    rc = lib.orc_gemm_full2(ka, kb, _ptr(A), _ptr(sA), tA, _ptr(B), _ptr(sB), tB,
                            M, N, w["K"], _ptr(d), _ptr(an), _ptr(bn),
                            nthreads or default_threads())
     if rc != 0:
@@ -170,9 +181,9 @@ def quant_mx(x: np.ndarray, elem: str):
     lib = _load()
     x = _c(x, np.float32)
     rows, K = x.shape
-    codes = np.zeros((rows, K if elem == "e4m3" else K // 2), np.uint8)
+    codes = np.zeros((rows, K // 2 if elem == "e2m1" else K), np.uint8)
     scales = np.zeros((rows, K // 32), np.uint8)
-    if lib.orc_quant_mx(1 if elem == "e4m3" else 0, _ptr(x), rows, K, _ptr(codes), _ptr(scales)):
+    if lib.orc_quant_mx({"e2m1": 0, "e4m3": 1, "e5m2": 2}[elem], _ptr(x), rows, K, _ptr(codes), _ptr(scales)):
         raise ValueError("bad K")
     return codes, scales
 

@@ -22,8 +22,11 @@
  *    fix the order; this reading is documented with the build).
  *  - The element/scale bit layouts are the OCP Microscaling (MX) v1.0
  *    definitions of E2M1, E4M3 (the "FN" variant: no infinities, S.1111.111 is
- *    NaN, max 448) and E8M0 (2^(e-127), 0xFF is NaN); bf16 is the upper half of
- *    an IEEE binary32.
+ *    NaN, max 448), E5M2 (IEEE-like: bias 15, S.11111.00 infinite, S.11111.xx
+ *    NaN otherwise, max 57344) and E8M0 (2^(e-127), 0xFF is NaN); bf16 is the
+ *    upper half of an IEEE binary32.  The pages name only E4M3 and E2M1; E5M2
+ *    is the other MXFP8 element the OCP format defines, and each operand of a
+ *    GEMM may carry its own MX element format.
  *  - Blocks: 32 elements per E8M0 scale (MXFP8, MXFP4); 16 elements per E4M3
  *    scale plus one fp32 scale per tensor, alpha = tA*tB (NVFP4).
  *
@@ -40,7 +43,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_BF16 = 0, ORC_MXFP8 = 1, ORC_MXFP4 = 2, ORC_NVFP4 = 3 };
+enum { ORC_BF16 = 0, ORC_MXFP8 = 1, ORC_MXFP4 = 2, ORC_NVFP4 = 3, ORC_MXE5M2 = 4 };
 
 enum {
     MUT_NONE = 0,
@@ -54,6 +57,8 @@ enum {
     MUT_DROP_LAST_K = 9,    /* last term of the sum dropped                    */
     MUT_E4M3_SIGN = 10,     /* E4M3 sign bit ignored                           */
     MUT_BF16_MANT = 11,     /* bf16 mantissa read as 6 bits                    */
+    MUT_E5M2_BIAS = 12,     /* E5M2 exponent bias 16 instead of 15             */
+    MUT_E5M2_SUBN = 13,     /* E5M2 subnormals read as normals (1.M)            */
 };
 static int g_mut = MUT_NONE;
 void orc_set_mutation(int m) { g_mut = m; }
@@ -80,6 +85,18 @@ double orc_decode_e4m3(unsigned c)
     if (e == 15 && m == 7) return NAN;
     double mag = (e == 0) ? ldexp(m / 8.0, 1 - bias) : ldexp(1.0 + m / 8.0, e - bias);
     if (g_mut == MUT_E4M3_SIGN) s = 0;
+    return s ? -mag : mag;
+}
+
+double orc_decode_e5m2(unsigned c)
+{
+    c &= 0xFFu;
+    int s = (c >> 7) & 1, e = (c >> 2) & 0x1F, m = c & 3;
+    int bias = (g_mut == MUT_E5M2_BIAS) ? 16 : 15;
+    double mag;
+    if (e == 31) mag = m ? NAN : INFINITY;
+    else if (e == 0 && g_mut != MUT_E5M2_SUBN) mag = ldexp(m / 4.0, 1 - bias);   /* 0.M * 2^(1-15) */
+    else mag = ldexp(1.0 + m / 4.0, e - bias);                                  /* 1.M * 2^(e-15) */
     return s ? -mag : mag;
 }
 
@@ -123,6 +140,7 @@ static unsigned encode_nearest(double x, double (*dec)(unsigned), unsigned maxco
 
 unsigned orc_encode_e2m1(double x) { return encode_nearest(x, orc_decode_e2m1, 0x7, 0x8); }
 unsigned orc_encode_e4m3(double x) { return encode_nearest(x, orc_decode_e4m3, 0x7E, 0x80); }
+unsigned orc_encode_e5m2(double x) { return encode_nearest(x, orc_decode_e5m2, 0x7B, 0x80); }
 
 /* fp64 -> bf16 bits, round to nearest even (used to state the bit-exact
  * expectation of results that are exactly representable). */
@@ -149,12 +167,13 @@ unsigned orc_encode_bf16(double x)
 
 void orc_decode_array(int fmt, const uint8_t *codes, int64_t n, double *out)
 {
-    /* fmt: 0 = E2M1 (one code per byte), 1 = E4M3, 2 = E8M0, 3 = bf16 (n uint16) */
+    /* fmt: 0 = E2M1 (one code per byte), 1 = E4M3, 2 = E8M0, 3 = bf16 (n uint16), 4 = E5M2 */
     for (int64_t i = 0; i < n; ++i) {
         switch (fmt) {
         case 0: out[i] = orc_decode_e2m1(codes[i]); break;
         case 1: out[i] = orc_decode_e4m3(codes[i]); break;
         case 2: out[i] = orc_decode_e8m0(codes[i]); break;
+        case 4: out[i] = orc_decode_e5m2(codes[i]); break;
         default: out[i] = orc_decode_bf16(((const uint16_t *)codes)[i]); break;
         }
     }
@@ -162,11 +181,12 @@ void orc_decode_array(int fmt, const uint8_t *codes, int64_t n, double *out)
 
 void orc_encode_array(int fmt, const double *x, int64_t n, uint8_t *out)
 {
-    /* fmt: 0 = E2M1 (one code per byte), 1 = E4M3, 3 = bf16 (n uint16) */
+    /* fmt: 0 = E2M1 (one code per byte), 1 = E4M3, 3 = bf16 (n uint16), 4 = E5M2 */
     for (int64_t i = 0; i < n; ++i) {
         switch (fmt) {
         case 0: out[i] = (uint8_t)orc_encode_e2m1(x[i]); break;
         case 1: out[i] = (uint8_t)orc_encode_e4m3(x[i]); break;
+        case 4: out[i] = (uint8_t)orc_encode_e5m2(x[i]); break;
         default: ((uint16_t *)out)[i] = (uint16_t)orc_encode_bf16(x[i]); break;
         }
     }
@@ -199,6 +219,8 @@ static double element(const operand *op, int64_t r, int64_t k)
     double v;
     if (op->kind == ORC_MXFP8) {
         v = orc_decode_e4m3(((const uint8_t *)op->X)[r * K + k]);
+    } else if (op->kind == ORC_MXE5M2) {
+        v = orc_decode_e5m2(((const uint8_t *)op->X)[r * K + k]);
     } else {
         uint8_t byte = ((const uint8_t *)op->X)[r * (K / 2) + k / 2];
         v = orc_decode_e2m1((k & 1) ? (byte >> 4) : (byte & 0xF));
@@ -279,22 +301,34 @@ static void *entries_worker(void *p)
     return NULL;
 }
 
+/* Operand kinds a GEMM may pair: equal kinds, or two MX 8-bit element
+ * formats (E4M3, E5M2) with E8M0 scales. */
+static int kinds_ok(int ka, int kb)
+{
+    if (ka < 0 || ka > 4 || kb < 0 || kb > 4) return 0;
+    if (ka == kb) return 1;
+    return (ka == ORC_MXFP8 || ka == ORC_MXE5M2) && (kb == ORC_MXFP8 || kb == ORC_MXE5M2);
+}
+
 /*
  * Computes D at the listed entries (em[i], en[i]) for i < count.
- *   kind   : 0 bf16 (A, B uint16), 1 MXFP8 (uint8 E4M3 + E8M0 scales),
- *            2 MXFP4 (packed E2M1 + E8M0), 3 NVFP4 (packed E2M1 + E4M3, tA, tB)
+ *   kind_a, kind_b : the operands' kinds: 0 bf16 (uint16), 1 MXFP8 (uint8
+ *            E4M3 + E8M0 scales), 2 MXFP4 (packed E2M1 + E8M0), 3 NVFP4
+ *            (packed E2M1 + E4M3, tA, tB), 4 MX with E5M2 elements (uint8 +
+ *            E8M0); see kinds_ok for the pairs
  *   d      : D_ref per entry (alpha applied)
  *   anorm  : ||dA_m||_2 * |tA| per entry (may be NULL)
  *   bnorm  : ||dB_n||_2 * |tB| per entry (may be NULL)
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
-int orc_gemm_entries(int kind, const void *A, const uint8_t *sA, double tA,
-                     const void *B, const uint8_t *sB, double tB,
-                     int64_t M, int64_t N, int64_t K,
-                     const int64_t *em, const int64_t *en, int64_t count,
-                     double *d, double *anorm, double *bnorm, int nthreads)
+int orc_gemm_entries2(int kind_a, int kind_b, const void *A, const uint8_t *sA, double tA,
+                      const void *B, const uint8_t *sB, double tB,
+                      int64_t M, int64_t N, int64_t K,
+                      const int64_t *em, const int64_t *en, int64_t count,
+                      double *d, double *anorm, double *bnorm, int nthreads)
 {
-    if (kind < 0 || kind > 3 || M < 0 || N < 0 || K < 0 || count < 0) return -1;
+    const int kind = kind_a;
+    if (!kinds_ok(kind_a, kind_b) || M < 0 || N < 0 || K < 0 || count < 0) return -1;
     if (kind != ORC_BF16 && K % block_size(kind)) return -1;
     for (int64_t i = 0; i < count; ++i)
         if (em[i] < 0 || em[i] >= M || en[i] < 0 || en[i] >= N) return -1;
@@ -304,7 +338,7 @@ int orc_gemm_entries(int kind, const void *A, const uint8_t *sA, double tA,
 
     double alpha = (kind == ORC_NVFP4 && g_mut != MUT_DROP_ALPHA) ? tA * tB : 1.0;
     double ta = (kind == ORC_NVFP4) ? tA : 1.0, tb = (kind == ORC_NVFP4) ? tB : 1.0;
-    operand oa = {kind, A, sA, M, K}, ob = {kind, B, sB, N, K};
+    operand oa = {kind_a, A, sA, M, K}, ob = {kind_b, B, sB, N, K};
 
     job *jobs = calloc((size_t)nthreads, sizeof(job));
     pthread_t *th = calloc((size_t)nthreads, sizeof(pthread_t));
@@ -332,6 +366,15 @@ int orc_gemm_entries(int kind, const void *A, const uint8_t *sA, double tA,
     free(jobs);
     free(th);
     return rc;
+}
+
+int orc_gemm_entries(int kind, const void *A, const uint8_t *sA, double tA,
+                     const void *B, const uint8_t *sB, double tB,
+                     int64_t M, int64_t N, int64_t K,
+                     const int64_t *em, const int64_t *en, int64_t count,
+                     double *d, double *anorm, double *bnorm, int nthreads)
+{
+    return orc_gemm_entries2(kind, kind, A, sA, tA, B, sB, tB, M, N, K, em, en, count, d, anorm, bnorm, nthreads);
 }
 
 /* ---------------------------------------------------------- full GEMM D */
@@ -368,13 +411,14 @@ static void *full_worker(void *p)
 }
 
 /* All M x N entries, row-major into d (and the per-entry norms if non-NULL).
- * B is decoded once (N*K doubles). */
-int orc_gemm_full(int kind, const void *A, const uint8_t *sA, double tA,
-                  const void *B, const uint8_t *sB, double tB,
-                  int64_t M, int64_t N, int64_t K,
-                  double *d, double *anorm, double *bnorm, int nthreads)
+ * B is decoded once (N*K doubles).  Kinds as for orc_gemm_entries2. */
+int orc_gemm_full2(int kind_a, int kind_b, const void *A, const uint8_t *sA, double tA,
+                   const void *B, const uint8_t *sB, double tB,
+                   int64_t M, int64_t N, int64_t K,
+                   double *d, double *anorm, double *bnorm, int nthreads)
 {
-    if (kind < 0 || kind > 3 || M < 0 || N < 0 || K < 0) return -1;
+    const int kind = kind_a;
+    if (!kinds_ok(kind_a, kind_b) || M < 0 || N < 0 || K < 0) return -1;
     if (kind != ORC_BF16 && K % block_size(kind)) return -1;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
@@ -382,7 +426,7 @@ int orc_gemm_full(int kind, const void *A, const uint8_t *sA, double tA,
 
     double alpha = (kind == ORC_NVFP4 && g_mut != MUT_DROP_ALPHA) ? tA * tB : 1.0;
     double ta = (kind == ORC_NVFP4) ? tA : 1.0, tb = (kind == ORC_NVFP4) ? tB : 1.0;
-    operand oa = {kind, A, sA, M, K}, ob = {kind, B, sB, N, K};
+    operand oa = {kind_a, A, sA, M, K}, ob = {kind_b, B, sB, N, K};
 
     double *bdec = malloc(sizeof(double) * (size_t)(N * K > 0 ? N * K : 1));
     double *bn = malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
@@ -415,6 +459,14 @@ int orc_gemm_full(int kind, const void *A, const uint8_t *sA, double tA,
     return rc;
 }
 
+int orc_gemm_full(int kind, const void *A, const uint8_t *sA, double tA,
+                  const void *B, const uint8_t *sB, double tB,
+                  int64_t M, int64_t N, int64_t K,
+                  double *d, double *anorm, double *bnorm, int nthreads)
+{
+    return orc_gemm_full2(kind, kind, A, sA, tA, B, sB, tB, M, N, K, d, anorm, bnorm, nthreads);
+}
+
 /* ------------------------------------------------- quantisation recipes */
 /* Written independently of the input generator so the CPU tests can confirm
  * that the generator's codes follow the stated recipes. */
@@ -430,11 +482,13 @@ static int floor_log2_ratio(double amax, double emax)
 
 /* MX recipe: per 32-block, scale 2^floor(log2(amax/emax)) clamped to
  * [-127, 127] (code 127 for an all-zero block); elements RNE + saturate.
- * elem: 0 = E2M1 (codes out: rows x K/2 packed), 1 = E4M3 (rows x K). */
+ * elem: 0 = E2M1 (codes out: rows x K/2 packed), 1 = E4M3 (rows x K),
+ * 2 = E5M2 (rows x K; emax 57344, the same recipe with E5M2's largest
+ * finite value). */
 int orc_quant_mx(int elem, const float *x, int64_t rows, int64_t K, uint8_t *codes, uint8_t *scales)
 {
-    if (K % 32) return -1;
-    double emax = elem == 1 ? 448.0 : 6.0;
+    if (K % 32 || elem < 0 || elem > 2) return -1;
+    double emax = elem == 1 ? 448.0 : elem == 2 ? 57344.0 : 6.0;
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t b = 0; b < K / 32; ++b) {
             const float *xb = x + r * K + b * 32;
@@ -449,6 +503,8 @@ int orc_quant_mx(int elem, const float *x, int64_t rows, int64_t K, uint8_t *cod
                 int64_t k = b * 32 + i;
                 if (elem == 1) {
                     codes[r * K + k] = (uint8_t)orc_encode_e4m3(v);
+                } else if (elem == 2) {
+                    codes[r * K + k] = (uint8_t)orc_encode_e5m2(v);
                 } else {
                     uint8_t c = (uint8_t)orc_encode_e2m1(v);
                     uint8_t *byte = &codes[r * (K / 2) + k / 2];

@@ -6,8 +6,9 @@ them into the operand encodings the GEMM consumes:
 
 * BF16: fp32 -> bf16 by round-to-nearest-even on the bit pattern.
 * MXFP8 / MXFP4: one power-of-two (E8M0) scale per 32 consecutive K elements,
-  ``scale = 2**floor(log2(amax / emax))`` with ``emax`` = 448 (E4M3) or 6
-  (E2M1), elements rounded to nearest-even on the element grid and saturated.
+  ``scale = 2**floor(log2(amax / emax))`` with ``emax`` = 448 (E4M3), 57344
+  (E5M2, the OCP format's other 8-bit element) or 6 (E2M1), elements rounded
+  to nearest-even on the element grid and saturated.
 * NVFP4: one fp32 tensor scale ``t = amax_tensor / (6 * 448)``, one E4M3 scale
   per 16 K elements ``s = RNE_e4m3(amax_block / (6 * t))``, elements
   ``RNE_e2m1(x / (s * t))`` — all divisions and products in fp32.
@@ -33,6 +34,7 @@ __all__ = [
 ]
 
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
 E2M1_MAX = 6.0
 
 
@@ -62,6 +64,17 @@ def _round_e4m3(v: np.ndarray) -> np.ndarray:
     return np.copysign(r, v)
 
 
+def _round_e5m2(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the E5M2 grid (2 mantissa bits, min exponent
+    -14, subnormal quantum 2**-16), ties to even, saturate at 57344."""
+    a = np.abs(v)
+    _, e = np.frexp(a)
+    ex = np.maximum(e - 1, -14)
+    q = np.ldexp(1.0, ex - 2)
+    r = np.minimum(np.rint(a / q) * q, E5M2_MAX)
+    return np.copysign(r, v)
+
+
 def _round_e2m1(v: np.ndarray) -> np.ndarray:
     """Round float64 values to the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6},
     ties to even mantissa, saturate at 6.  Sign kept."""
@@ -84,6 +97,20 @@ def _pack_e4m3(r: np.ndarray) -> np.ndarray:
     man_n = np.where(normal, np.rint((a / np.ldexp(1.0, ex_n) - 1.0) * 8.0), 0)
     code_n = ((ex_n + 7) << 3) + man_n.astype(np.int64)
     code_s = np.rint(a / 2.0 ** -9).astype(np.int64)
+    code = np.where(normal, code_n, code_s)
+    code = code | np.where(np.signbit(r), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def _pack_e5m2(r: np.ndarray) -> np.ndarray:
+    a = np.abs(r)
+    _, e = np.frexp(a)
+    ex = e - 1
+    normal = a >= 2.0 ** -14
+    ex_n = np.where(normal, ex, 0)
+    man_n = np.where(normal, np.rint((a / np.ldexp(1.0, ex_n) - 1.0) * 4.0), 0)
+    code_n = ((ex_n + 15) << 2) + man_n.astype(np.int64)
+    code_s = np.rint(a / 2.0 ** -16).astype(np.int64)
     code = np.where(normal, code_n, code_s)
     code = code | np.where(np.signbit(r), 0x80, 0)
     return code.astype(np.uint8)
@@ -119,15 +146,16 @@ def _floor_log2_ratio(amax: np.ndarray, emax: float) -> np.ndarray:
 def quant_mx(x: np.ndarray, elem: str) -> tuple[np.ndarray, np.ndarray]:
     """MX quantisation along the last axis (K), 32-element blocks.
 
-    Returns ``(codes, scales)``: for ``elem='e4m3'`` codes are (rows, K) uint8;
-    for ``elem='e2m1'`` they are (rows, K/2) uint8 with two elements per byte.
+    Returns ``(codes, scales)``: for ``elem='e4m3'`` or ``'e5m2'`` codes are
+    (rows, K) uint8; for ``elem='e2m1'`` they are (rows, K/2) uint8 with two
+    elements per byte.
     ``scales`` are (rows, K/32) E8M0 codes.  An all-zero block gets scale code
     127 (1.0) and zero elements.
     """
     rows, K = x.shape
     if K % 32:
         raise ValueError("K must be a multiple of 32 for MX formats")
-    emax = E4M3_MAX if elem == "e4m3" else E2M1_MAX
+    emax = {"e4m3": E4M3_MAX, "e5m2": E5M2_MAX, "e2m1": E2M1_MAX}[elem]
     xb = x.astype(np.float64).reshape(rows, K // 32, 32)
     amax = np.max(np.abs(xb), axis=2)
     e = np.where(amax > 0, _floor_log2_ratio(np.where(amax > 0, amax, 1.0), emax), 0)
@@ -135,6 +163,8 @@ def quant_mx(x: np.ndarray, elem: str) -> tuple[np.ndarray, np.ndarray]:
     v = xb / np.ldexp(1.0, e)[:, :, None]        # exact: power-of-two divisor
     if elem == "e4m3":
         codes = _pack_e4m3(_round_e4m3(v)).reshape(rows, K)
+    elif elem == "e5m2":
+        codes = _pack_e5m2(_round_e5m2(v)).reshape(rows, K)
     elif elem == "e2m1":
         codes = _pack_nibbles(_pack_e2m1(_round_e2m1(v)).reshape(rows, K))
     else:
@@ -168,11 +198,14 @@ def quant_nvfp4(x: np.ndarray) -> tuple[np.ndarray, np.ndarray, float]:
 
 # ---- the benchmark workloads --------------------------------------------------
 
-def workload(fmt: str, M: int, N: int, K: int, seed_a: int, seed_b: int) -> dict:
+def workload(fmt: str, M: int, N: int, K: int, seed_a: int, seed_b: int,
+             elem_a: str = "e4m3", elem_b: str = "e4m3") -> dict:
     """Encoded operands for one GEMM D = A . B^T of the given format.
 
     Returns a dict with numpy arrays ``A``, ``B`` (and ``sA``, ``sB``, ``tA``,
     ``tB`` where the format has scales).  A is M x K, B is N x K, K-major.
+    For ``fmt='mxfp8'`` each operand's 8-bit element format is ``elem_a`` /
+    ``elem_b`` ('e4m3' or 'e5m2'), recorded as ``elemA`` / ``elemB``.
     """
     xa = normal(seed_a, M, K)
     xb = normal(seed_b, N, K)
@@ -180,9 +213,11 @@ def workload(fmt: str, M: int, N: int, K: int, seed_a: int, seed_b: int) -> dict
     if fmt == "bf16":
         out["A"], out["B"] = bf16_from_f32(xa), bf16_from_f32(xb)
     elif fmt in ("mxfp8", "mxfp4"):
-        elem = "e4m3" if fmt == "mxfp8" else "e2m1"
-        out["A"], out["sA"] = quant_mx(xa, elem)
-        out["B"], out["sB"] = quant_mx(xb, elem)
+        ea, eb = (elem_a, elem_b) if fmt == "mxfp8" else ("e2m1", "e2m1")
+        out["A"], out["sA"] = quant_mx(xa, ea)
+        out["B"], out["sB"] = quant_mx(xb, eb)
+        if fmt == "mxfp8":
+            out["elemA"], out["elemB"] = ea, eb
     elif fmt == "nvfp4":
         out["A"], out["sA"], out["tA"] = quant_nvfp4(xa)
         out["B"], out["sB"], out["tB"] = quant_nvfp4(xb)

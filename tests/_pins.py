@@ -50,6 +50,11 @@ def ref_e4m3(codes):
     return c.view(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 
+def ref_e5m2(codes):
+    c = torch.from_numpy(np.ascontiguousarray(codes, np.uint8))
+    return c.view(torch.float8_e5m2).to(torch.float64).numpy()
+
+
 def ref_e8m0(codes):
     c = torch.from_numpy(np.ascontiguousarray(codes, np.uint8))
     return c.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
@@ -68,7 +73,7 @@ def ref_values(fmt, w, which):
     if fmt == "bf16":
         return ref_bf16(X)
     if fmt == "mxfp8":
-        el = ref_e4m3(X)
+        el = ref_e5m2(X) if w.get("elem" + which, "e4m3") == "e5m2" else ref_e4m3(X)
         sc = ref_e8m0(w["s" + which])
         return el * np.repeat(sc, 32, axis=1)
     codes = np.empty((X.shape[0], K), np.uint8)
@@ -101,6 +106,55 @@ def random_codes(fmt, rows, K, rng, scale_lo=0, scale_hi=254, finite=True, bf16_
     else:
         s = rng.integers(scale_lo, min(scale_hi, 0x7E) + 1, (rows, K // 16)).astype(np.uint8)
     return {"X": c, "s": s}
+
+
+def random_e5m2(rows, K, rng, exp=(0, 31)):
+    """Random finite E5M2 codes with exponent fields in [exp[0], exp[1])
+    (the all-ones field, infinities and NaNs, is never drawn)."""
+    sign = rng.integers(0, 2, (rows, K)) << 7
+    e = rng.integers(exp[0], min(exp[1], 31), (rows, K)) << 2
+    return (sign | e | rng.integers(0, 4, (rows, K))).astype(np.uint8)
+
+
+def make_w_mx8(elem_a, elem_b, M, N, K, rng, scale_lo=0, scale_hi=254, narrow=False):
+    """An MX 8-bit workload whose operands carry elements elem_a / elem_b
+    ('e4m3' or 'e5m2') with random E8M0 scales; `narrow` keeps E5M2 codes
+    within 2^-5 .. 2^6 so that products span few enough binades for exact
+    fp64 sums."""
+    w = {"fmt": "mxfp8", "M": M, "N": N, "K": K, "elemA": elem_a, "elemB": elem_b}
+    for X, rows, el in (("A", M, elem_a), ("B", N, elem_b)):
+        if el == "e5m2":
+            w[X] = random_e5m2(rows, K, rng, (10, 21) if narrow else (0, 31))
+        else:
+            w[X] = random_codes("mxfp8", rows, K, rng)["X"]
+        w["s" + X] = rng.integers(scale_lo, scale_hi + 1, (rows, K // 32)).astype(np.uint8)
+    return w
+
+
+def check_mixed_fraction(elem_a, elem_b, seed=20, M=3, N=4, K=96, exact_scales=False):
+    """Per-operand MX element formats against exact rational dot products of
+    independently decoded values (torch's float8 types).  With narrow scales
+    and E5M2 codes every product has at most 8 significant bits and lies in
+    2^-30 .. 2^21, so every fp64 partial sum is exact and equality is
+    required; otherwise the fp64 recursive-summation bound is used."""
+    rng = np.random.default_rng(seed)
+    kw = {"scale_lo": 124, "scale_hi": 130, "narrow": True} if exact_scales else {}
+    w = make_w_mx8(elem_a, elem_b, M, N, K, rng, **kw)
+    va, vb = ref_values("mxfp8", w, "A"), ref_values("mxfp8", w, "B")
+    d, _, _ = oracle.gemm_full("mxfp8", w, nthreads=2)
+    if not np.all(np.isfinite(d)):
+        return False
+    for m in range(M):
+        for n in range(N):
+            terms = [Fraction(float(va[m, k])) * Fraction(float(vb[n, k])) for k in range(K)]
+            exact = sum(terms)
+            got = Fraction(float(d[m, n]))
+            if exact_scales:
+                if got != exact:
+                    return False
+            elif abs(got - exact) > sum(abs(t) for t in terms) * Fraction(K + 2, 2 ** 52):
+                return False
+    return True
 
 
 def make_w(fmt, M, N, K, rng, **kw):
@@ -299,7 +353,7 @@ def check_decoders():
     table (16 codes) and numpy's binary32 view (bf16 samples)."""
     codes = np.arange(256, dtype=np.uint8)
     ok = True
-    for fmt, ref in (("e4m3", ref_e4m3), ("e8m0", ref_e8m0)):
+    for fmt, ref in (("e4m3", ref_e4m3), ("e5m2", ref_e5m2), ("e8m0", ref_e8m0)):
         got = oracle.decode(fmt, codes)
         exp = ref(codes)
         ok &= bool(np.array_equal(np.isnan(got), np.isnan(exp)))
@@ -331,4 +385,7 @@ def battery():
         res[f"{fmt}_pow2"] = check_pow2_scale_shift(fmt)
         res[f"{fmt}_unit_matmul"] = check_unit_scale_matmul(fmt)
         res[f"{fmt}_transpose"] = check_transpose_symmetry(fmt)
+    for ea, eb in (("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")):
+        res[f"mx8_{ea}x{eb}_fraction"] = check_mixed_fraction(ea, eb)
+        res[f"mx8_{ea}x{eb}_fraction_exact"] = check_mixed_fraction(ea, eb, seed=21, exact_scales=True)
     return res

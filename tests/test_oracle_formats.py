@@ -13,7 +13,7 @@ def test_decoders_match_independent_sources():
 
 
 @pytest.mark.parametrize("name,fmt", [("ocp_e4m3_anchors.txt", "e4m3"), ("ocp_e8m0_anchors.txt", "e8m0"),
-                                      ("ocp_e2m1.txt", "e2m1")])
+                                      ("ocp_e2m1.txt", "e2m1"), ("ocp_e5m2_anchors.txt", "e5m2")])
 def test_anchor_tables(name, fmt):
     table = _pins._table(name)
     codes = np.array(sorted(table), np.uint8)
@@ -26,7 +26,8 @@ def test_anchor_tables(name, fmt):
             assert g == e and math.copysign(1, g) == math.copysign(1, e), (hex(c), g, e)
 
 
-@pytest.mark.parametrize("fmt,ncodes,nan_codes", [("e2m1", 16, ()), ("e4m3", 256, (0x7F, 0xFF))])
+@pytest.mark.parametrize("fmt,ncodes,nan_codes", [("e2m1", 16, ()), ("e4m3", 256, (0x7F, 0xFF)),
+                                                  ("e5m2", 256, tuple(range(0x7C, 0x80)) + tuple(range(0xFC, 0x100)))])
 def test_encode_decode_round_trip(fmt, ncodes, nan_codes):
     codes = np.array([c for c in range(ncodes) if c not in nan_codes], np.uint8)
     vals = oracle.decode(fmt, codes)
@@ -76,3 +77,10 @@ def test_bf16_encoder_matches_numpy_rounding():
 def test_nan_codes_decode_to_nan():
     assert np.isnan(oracle.decode("e4m3", np.array([0x7F, 0xFF], np.uint8))).all()
     assert np.isnan(oracle.decode("e8m0", np.array([0xFF], np.uint8))).all()
+
+
+def test_e5m2_ties_to_even_and_saturation():
+    codes = np.arange(0, 0x7B, dtype=np.uint8)          # consecutive finite positives
+    mid = (oracle.decode("e5m2", codes) + oracle.decode("e5m2", codes + 1)) / 2
+    assert np.array_equal(oracle.encode("e5m2", mid), np.where(codes % 2 == 0, codes, codes + 1))
+    assert oracle.encode("e5m2", np.array([1e9, 61440.0, -1e9, -0.0])).tolist() == [0x7B, 0x7B, 0xFB, 0x80]

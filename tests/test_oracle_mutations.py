@@ -22,6 +22,8 @@ MUTATIONS = {
     9: "last K term dropped",
     10: "E4M3 sign ignored",
     11: "bf16 mantissa truncated",
+    12: "E5M2 exponent bias 16",
+    13: "E5M2 subnormals read as normals",
 }
 
 

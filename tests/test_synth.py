@@ -20,7 +20,7 @@ def _edge_rows(K, rng):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("elem", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("elem", ["e4m3", "e5m2", "e2m1"])
 def test_mx_recipe_matches_oracle(elem):
     rng = np.random.default_rng(0)
     x = np.concatenate([synth.normal(5, 40, 256), _edge_rows(256, rng)])
@@ -82,3 +82,16 @@ def test_sample_entries_structured_then_uniform():
     assert em.max() < 8192 and en.max() < 8192
     em2, en2 = synth.sample_entries(3, 8192, 8192, 4096)
     assert np.array_equal(em, em2) and np.array_equal(en, en2)
+
+
+def test_e5m2_recipe_extremes_match_oracle():
+    """E5M2 blocks spanning its subnormals, ties and saturation."""
+    x = np.zeros((3, 64), np.float32)
+    x[0, :32] = np.float32(2.0 ** -20) * np.arange(32, dtype=np.float32)     # subnormals after scaling
+    x[0, 32:] = np.float32(57344.0 * 2.0 ** 3)
+    x[1] = np.linspace(-7e4, 7e4, 64).astype(np.float32)
+    x[2, ::2] = np.float32(1.125)                                           # E5M2 midpoint of 1.0, 1.25
+    x[2, 1::2] = np.float32(-1.375)
+    c1, s1 = synth.quant_mx(x, "e5m2")
+    c2, s2 = oracle.quant_mx(x, "e5m2")
+    assert np.array_equal(s1, s2) and np.array_equal(c1, c2)
