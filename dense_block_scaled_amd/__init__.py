@@ -27,16 +27,16 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["gemm_bf16", "gemm_mx", "gemm_nvfp4", "gemm_grouped_bf16", "gemm_grouped_mx", "gemm_grouped_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError",
+__all__ = ["gemm_bf16", "gemm_mx", "gemm_mx_mixed", "gemm_nvfp4", "gemm_grouped_bf16", "gemm_grouped_mx", "gemm_grouped_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError",
            "DBS_OK", "DBS_EINVAL", "DBS_EUNSUPPORTED", "DBS_EHIP", "K_MAJOR", "MN_MAJOR",
-           "E4M3", "E2M1", "status_str"]
+           "E4M3", "E5M2", "E2M1", "status_str"]
 
 LIB_PATH = Path(__file__).resolve().parent / "libdbs.so"
 
 DBS_OK, DBS_EINVAL, DBS_EUNSUPPORTED, DBS_EHIP = 0, 1, 2, 3
 K_MAJOR, MN_MAJOR = 0, 1
-E4M3, E2M1 = 0, 4
-_ELEM = {"e4m3": E4M3, "e2m1": E2M1}
+E4M3, E5M2, E2M1 = 0, 1, 4
+_ELEM = {"e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1}
 
 
 class DbsError(RuntimeError):
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_bf16.restype = I
         L.gemm_mx.argtypes = [I, P, P, P, P, P, I64, I64, I64, I, I, P]
         L.gemm_mx.restype = I
+        L.gemm_mx_mixed.argtypes = [I, I, P, P, P, P, P, I64, I64, I64, I, I, P]
+        L.gemm_mx_mixed.restype = I
         L.gemm_nvfp4.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P]
         L.gemm_nvfp4.restype = I
         L.gemm_grouped_bf16.argtypes = [P, P, P, P, I64, I64, I64, P]
@@ -153,21 +155,31 @@ def gemm_bf16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
 def gemm_mx(elem: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor,
             K: int | None = None, out: torch.Tensor | None = None,
             la: int = K_MAJOR, lb: int = K_MAJOR) -> torch.Tensor:
-    """MXFP8 (elem='e4m3') or MXFP4 (elem='e2m1') GEMM with E8M0 scales per 32."""
-    code = _ELEM[elem]
+    """MXFP8 (elem='e4m3' or 'e5m2') or MXFP4 (elem='e2m1') GEMM with E8M0
+    scales per 32."""
+    return gemm_mx_mixed(elem, elem, A, sA, B, sB, K=K, out=out, la=la, lb=lb)
+
+
+def gemm_mx_mixed(elem_a: str, elem_b: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor,
+                  sB: torch.Tensor, K: int | None = None, out: torch.Tensor | None = None,
+                  la: int = K_MAJOR, lb: int = K_MAJOR) -> torch.Tensor:
+    """MX GEMM with A's elements in elem_a and B's in elem_b ('e4m3', 'e5m2'
+    or 'e2m1'; the library takes 8-bit pairs in any mix and E2M1 with E2M1)."""
+    code_a, code_b = _ELEM[elem_a], _ELEM[elem_b]
     la, lb = _layout(la, "la"), _layout(lb, "lb")
-    pb_ = 2 if elem == "e2m1" else 1     # elements per byte
-    M, N = _rows(A, la, pb_), _rows(B, lb, pb_)
+    pa_ = 2 if elem_a == "e2m1" else 1   # elements per byte
+    pb_ = 2 if elem_b == "e2m1" else 1
+    M, N = _rows(A, la, pa_), _rows(B, lb, pb_)
     if K is None:
-        K = A.shape[1] * pb_ if la == K_MAJOR else A.shape[0]
+        K = A.shape[1] * pa_ if la == K_MAJOR else A.shape[0]
     u8 = (torch.uint8,)
-    pa = _dev(A, "A", u8, _shape(M, K, la, pb_))
+    pa = _dev(A, "A", u8, _shape(M, K, la, pa_))
     pb = _dev(B, "B", u8, _shape(N, K, lb, pb_))
     psa = _dev(sA, "sA", u8, (M, K // 32))
     psb = _dev(sB, "sB", u8, (N, K // 32))
     out = _out(out, M, N, A)
-    _check(lib().gemm_mx(code, pa, psa, pb, psb, ctypes.c_void_p(out.data_ptr()), M, N, K,
-                         la, lb, _stream(A)))
+    _check(lib().gemm_mx_mixed(code_a, code_b, pa, psa, pb, psb, ctypes.c_void_p(out.data_ptr()), M, N, K,
+                               la, lb, _stream(A)))
     return out
 
 

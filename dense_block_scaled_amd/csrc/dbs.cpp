@@ -93,7 +93,8 @@ struct Groups {
 
 dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB, void *D, int64_t M,
                int64_t N, int64_t K, float alpha, int elem_bits, int block, hipStream_t stream,
-               const Groups *groups = nullptr, dbs_layout la = DBS_K_MAJOR, dbs_layout lb = DBS_K_MAJOR)
+               const Groups *groups = nullptr, dbs_layout la = DBS_K_MAJOR, dbs_layout lb = DBS_K_MAJOR,
+               int ec = 0)
 {
     int cus = 0;
     dbs_status st = device_cus(&cus);
@@ -113,6 +114,7 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     p.lay = (la == DBS_MN_MAJOR ? 1 : 0) | (lb == DBS_MN_MAJOR ? 2 : 0);
     p.ldam = (int)(M * elem_bits / 8);
     p.ldbm = (int)(N * elem_bits / 8);
+    p.ec = ec;
     // square tiles unless they would fill at most half of the CUs
     auto tiles_of = [&](int64_t rows, int64_t tm_, int64_t tn_) { return ((rows + tm_ - 1) / tm_) * ((N + tn_ - 1) / tn_); };
     int64_t sq_tiles = 0;
@@ -159,6 +161,11 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     return DBS_OK;
 }
 
+// The f8f6f4 MFMA format code of an 8-bit MX element (0 E4M3, 1 E5M2).
+int mx8_code(dbs_mx_elem e) { return e == DBS_E5M2 ? 1 : 0; }
+
+bool mx_elem_known(dbs_mx_elem e) { return e == DBS_E4M3 || e == DBS_E5M2 || e == DBS_E2M1; }
+
 }  // namespace
 
 extern "C" {
@@ -173,18 +180,30 @@ dbs_status gemm_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N
     return run(dbs::kBF16, A, nullptr, B, nullptr, D, M, N, K, 1.0f, 16, 0, stream, nullptr, la, lb);
 }
 
-dbs_status gemm_mx(dbs_mx_elem elem, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB, void *D,
-                   int64_t M, int64_t N, int64_t K, dbs_layout la, dbs_layout lb, hipStream_t stream)
+dbs_status gemm_mx_mixed(dbs_mx_elem elem_a, dbs_mx_elem elem_b, const void *A, const uint8_t *sA, const void *B,
+                         const uint8_t *sB, void *D, int64_t M, int64_t N, int64_t K, dbs_layout la, dbs_layout lb,
+                         hipStream_t stream)
 {
-    if (elem != DBS_E4M3 && elem != DBS_E2M1) return fail(DBS_EINVAL, "mx: unknown element format");
+    if (!mx_elem_known(elem_a) || !mx_elem_known(elem_b)) return fail(DBS_EINVAL, "mx: unknown element format");
     if (!sA || !sB) return fail(DBS_EINVAL, "null pointer argument");
     dbs_status st = check_common(A, B, D, M, N, K, la, lb, int64_t(1) << 22);
     if (st != DBS_OK) return st;
     if (K % 32) return fail(DBS_EINVAL, "mx: K must be a multiple of 32");
-    const int bits = elem == DBS_E4M3 ? 8 : 4;
+    if ((elem_a == DBS_E2M1) != (elem_b == DBS_E2M1))
+        return fail(DBS_EUNSUPPORTED, "mx: an 8-bit operand with an E2M1 operand is not implemented");
+    const int ec = elem_a == DBS_E2M1 ? 0 : mx8_code(elem_a) | (mx8_code(elem_b) << 3);
+    if (ec != 0 && (la != DBS_K_MAJOR || lb != DBS_K_MAJOR))
+        return fail(DBS_EUNSUPPORTED, "mx: E5M2 operands are K-major only");
+    const int bits = elem_a == DBS_E2M1 ? 4 : 8;
     if ((st = check_mn(la, lb, M, N, K, bits)) != DBS_OK) return st;
-    return run(elem == DBS_E4M3 ? dbs::kMXFP8 : dbs::kMXFP4, A, sA, B, sB, D, M, N, K, 1.0f, bits, 32, stream, nullptr,
-               la, lb);
+    return run(bits == 8 ? dbs::kMXFP8 : dbs::kMXFP4, A, sA, B, sB, D, M, N, K, 1.0f, bits, 32, stream, nullptr,
+               la, lb, ec);
+}
+
+dbs_status gemm_mx(dbs_mx_elem elem, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB, void *D,
+                   int64_t M, int64_t N, int64_t K, dbs_layout la, dbs_layout lb, hipStream_t stream)
+{
+    return gemm_mx_mixed(elem, elem, A, sA, B, sB, D, M, N, K, la, lb, stream);
 }
 
 dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA, const void *B, const uint8_t *sB, float tB,
@@ -283,7 +302,7 @@ dbs_status gemm_grouped_bf16(const void *A, const void *B, void *D, const int64_
 dbs_status gemm_grouped_mx(dbs_mx_elem elem, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB,
                            void *D, const int64_t *offsets, int64_t G, int64_t N, int64_t K, hipStream_t stream)
 {
-    if (elem != DBS_E4M3 && elem != DBS_E2M1) return fail(DBS_EINVAL, "mx: unknown element format");
+    if (!mx_elem_known(elem)) return fail(DBS_EINVAL, "mx: unknown element format");
     if (!sA || !sB) return fail(DBS_EINVAL, "null pointer argument");
     int64_t M = 0;
     dbs_status st = check_groups(offsets, G, &M);
@@ -291,7 +310,9 @@ dbs_status gemm_grouped_mx(dbs_mx_elem elem, const void *A, const uint8_t *sA, c
     if ((st = check_common(A, B, D, M, N, K, DBS_K_MAJOR, DBS_K_MAJOR, int64_t(1) << 22)) != DBS_OK) return st;
     if (K % 32) return fail(DBS_EINVAL, "mx: K must be a multiple of 32");
     const Groups gr{offsets, G, nullptr};
-    if (elem == DBS_E4M3) return run(dbs::kMXFP8, A, sA, B, sB, D, M, N, K, 1.0f, 8, 32, stream, &gr);
+    if (elem != DBS_E2M1)
+        return run(dbs::kMXFP8, A, sA, B, sB, D, M, N, K, 1.0f, 8, 32, stream, &gr, DBS_K_MAJOR, DBS_K_MAJOR,
+                   mx8_code(elem) * 9);
     return run(dbs::kMXFP4, A, sA, B, sB, D, M, N, K, 1.0f, 4, 32, stream, &gr);
 }
 
@@ -324,6 +345,6 @@ const char *dbs_status_str(dbs_status st)
 
 const char *dbs_last_error(void) { return g_err; }
 
-int dbs_version(void) { return 100; }
+int dbs_version(void) { return 101; }
 
 }  // extern "C"

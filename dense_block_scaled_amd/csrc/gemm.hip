@@ -159,13 +159,17 @@ __device__ __forceinline__ TileRef tile_ref(int tile, const Params &p)
 // slots 0..NS-1 | scale slots (MX formats) SA 0..NS-1 | SB 0..NS-1 of rows x
 // BPS bytes.  LAY: bit 0 set if A is stored MN-major (K x M), bit 1 if B is
 // (K x N); a slot of an MN-major operand holds the same bytes as a K-major
-// one, arranged as the stage's K-rows (see Mn below).
+// one, arranged as the stage's K-rows (see Mn below).  EC: the 8-bit MX
+// element formats as gfx950's f8f6f4 MFMA codes, A in bits 0..2 and B in
+// bits 3..5 (0 = E4M3, 1 = E5M2); both formats take the same bytes and
+// fragments, only the MFMA's format fields differ.
 constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
 
-template <int TM_, int TN_, int WM_, int WN_, int NS_ = 2, int LAY_ = 0>
+template <int TM_, int TN_, int WM_, int WN_, int NS_ = 2, int LAY_ = 0, int EC_ = 0>
 struct Shape {
-    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_, NS = NS_, LAY = LAY_;
+    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_, NS = NS_, LAY = LAY_, EC = EC_;
     static constexpr bool AMN = (LAY & 1) != 0, BMN = (LAY & 2) != 0;
+    static constexpr int CA = EC & 7, CB = (EC >> 3) & 7;
     static constexpr int NW = WM * WN;
     static constexpr int kThreads = 64 * NW;
     static constexpr int MB = TM / WM / 32, NB = TN / WN / 32;
@@ -194,9 +198,9 @@ using SkinnyDeep = Shape<kSkinnyTM, kSkinnyTN, 8, 1, 3>;
 // this variant runs one wave per SIMD, each owning 128 x 128.
 using SquareW4 = Shape<kSquareTM, kSquareTN, 2, 2>;
 
-// Shape S with operand layouts LAY.
-template <class S, int LAY>
-using WithLayout = Shape<S::TM, S::TN, S::WM, S::WN, S::NS, LAY>;
+// Shape S with operand layouts LAY and 8-bit MX element codes EC.
+template <class S, int LAY, int EC = S::EC>
+using WithLayout = Shape<S::TM, S::TN, S::WM, S::WN, S::NS, LAY, EC>;
 
 // ------------------------------------------------------------ format traits
 
@@ -669,7 +673,9 @@ __device__ __forceinline__ void store_scale_bytes(const ScaleBytes<FMT, S> &r, u
 // fragment, so each lane ends up holding 4 consecutive output columns.
 // MX: the scale operands are the blocks' stage scale dwords, of which op_sel
 // SEL picks the byte of this k-step.
-template <int FMT, int SEL>
+// For 8-bit MX elements CA and CB are the format codes of A and B (the
+// instruction's second and first operand).
+template <int FMT, int SEL, int CA = 0, int CB = 0>
 __device__ __forceinline__ void mma1(f32x16 &acc, const typename Fmt<FMT>::Frag &a, uint32_t sa,
                                      const typename Fmt<FMT>::Frag &b, uint32_t sb)
 {
@@ -678,7 +684,7 @@ __device__ __forceinline__ void mma1(f32x16 &acc, const typename Fmt<FMT>::Frag 
     } else if constexpr (FMT == kNVFP4) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, acc, 0, 0, 0);
     } else if constexpr (FMT == kMXFP8) {
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc, 0, 0, SEL, (int)sb, SEL, (int)sa);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc, CB, CA, SEL, (int)sb, SEL, (int)sa);
     } else {
         const i32x8 bb = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
         const i32x8 aa = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
@@ -1170,7 +1176,7 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
             if constexpr (adirect<FMT, S>())
                 mma1<FMT, 0>(acc[i][j], PH == 0 ? P.aprev[i] : P.acur[i][KC], 0u, cur.b[j], 0u);
             else
-                mma1<FMT, scale_sel<FMT>(KC)>(acc[i][j], fa.a[i], sc.a[i][0], cur.b[j], sc.b[j][0]);
+                mma1<FMT, scale_sel<FMT>(KC), S::CA, S::CB>(acc[i][j], fa.a[i], sc.a[i][0], cur.b[j], sc.b[j][0]);
             if constexpr (LOADS) {
                 constexpr int base = PH * MB * NB;
                 const int pos = base + i * NB + j;   // compile-time after unrolling
@@ -1700,6 +1706,19 @@ hipError_t launch_one(const Params &p0, int grid, hipStream_t stream)
         if (p.lay != 0) return hipErrorInvalidValue;   // the host rejects MN-major NVFP4
         hipLaunchKernelGGL((gemm_kernel<FMT, S0, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p);
     } else {
+        if constexpr (FMT == kMXFP8) {
+            if (p.ec != 0) {
+                // E5M2 on either side: K-major operands only (the host checks)
+                if (p.lay != 0) return hipErrorInvalidValue;
+                switch (p.ec) {
+                case 1: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 0, 1>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+                case 8: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 0, 8>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+                case 9: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 0, 9>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+                default: return hipErrorInvalidValue;
+                }
+                return hipGetLastError();
+            }
+        }
         switch (p.lay) {
         case 0: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 0>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
         case 1: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 1>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;

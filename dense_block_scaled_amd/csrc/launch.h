@@ -30,6 +30,7 @@ struct Params {
     int scales_aligned;   // 1 if every scale row starts on a 4-byte boundary
     int lay;              // bit 0: A stored MN-major (K x M), bit 1: B stored MN-major (K x N)
     int ldam, ldbm;       // MN-major A / B: bytes per K-row (M or N elements)
+    int ec;               // 8-bit MX element codes: A in bits 0..2, B in 3..5 (0 = E4M3, 1 = E5M2)
     float alpha;          // applied to the fp32 accumulator before rounding
     // Grouped GEMM (ngroups > 0): group g owns rows goff[g] .. goff[g+1]-1 of A
     // and D, the g-th N x K block of B (and of sB) and output tiles

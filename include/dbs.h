@@ -77,9 +77,12 @@ typedef enum {
     DBS_MN_MAJOR = 1
 } dbs_layout;
 
-/* MX element formats; the values equal gfx950's f8f6f4 MFMA format codes. */
+/* MX element formats; the values equal gfx950's f8f6f4 MFMA format codes.
+ * E5M2 (OCP MX v1.0: bias 15, two mantissa bits, infinities and NaNs) is the
+ * other 8-bit element of the OCP format; the pages name E4M3 and E2M1. */
 typedef enum {
     DBS_E4M3 = 0,
+    DBS_E5M2 = 1,
     DBS_E2M1 = 4
 } dbs_mx_elem;
 
@@ -92,15 +95,30 @@ dbs_status gemm_bf16(const void *A, const void *B, void *D,
                      dbs_layout la, dbs_layout lb, hipStream_t stream);
 
 /*
- * MX GEMM (MXFP8 for elem = DBS_E4M3, MXFP4 for elem = DBS_E2M1): elements of
- * A and B in `elem`, E8M0 scales sA (M x K/32), sB (N x K/32).  Both operands
- * use the same element format.  K must be a multiple of 32, at most 2^22.
+ * MX GEMM (MXFP8 for elem = DBS_E4M3 or DBS_E5M2, MXFP4 for elem = DBS_E2M1):
+ * elements of A and B in `elem`, E8M0 scales sA (M x K/32), sB (N x K/32).
+ * K must be a multiple of 32, at most 2^22.  E5M2 operands are K-major only
+ * (DBS_EUNSUPPORTED for MN-major).
  */
 dbs_status gemm_mx(dbs_mx_elem elem,
                    const void *A, const uint8_t *sA,
                    const void *B, const uint8_t *sB, void *D,
                    int64_t M, int64_t N, int64_t K,
                    dbs_layout la, dbs_layout lb, hipStream_t stream);
+
+/*
+ * MX GEMM with an element format per operand: A's elements in elem_a, B's in
+ * elem_b, otherwise as gemm_mx (gemm_mx(e, ...) is gemm_mx_mixed(e, e, ...)).
+ * Pairs taken: any of E4M3 / E5M2 with any of E4M3 / E5M2, and E2M1 with
+ * E2M1; an 8-bit operand with an E2M1 one returns DBS_EUNSUPPORTED.  gfx950's
+ * scaled MFMA takes a format code per operand, so each pair runs at the
+ * 8-bit rate with the bytes and scales of MXFP8.
+ */
+dbs_status gemm_mx_mixed(dbs_mx_elem elem_a, dbs_mx_elem elem_b,
+                         const void *A, const uint8_t *sA,
+                         const void *B, const uint8_t *sB, void *D,
+                         int64_t M, int64_t N, int64_t K,
+                         dbs_layout la, dbs_layout lb, hipStream_t stream);
 
 /*
  * NVFP4 GEMM: packed E2M1 elements, E4M3 block scales sA (M x K/16) and sB
@@ -120,7 +138,8 @@ dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA,
  * elements, sB G x N scale rows):  D_g = bf16(alpha_g (sA_g (.) A_g) .
  * (sB_g (.) B_g)^T).  offsets (G + 1 values, offsets[0] = 0, non-decreasing,
  * empty groups allowed) and tB (G values) are HOST arrays; everything else
- * is as for the single GEMMs (K-major operands only).  alpha_g = 1, or
+ * is as for the single GEMMs (K-major operands only; gemm_grouped_mx takes
+ * E4M3, E5M2 or E2M1 for both operands).  alpha_g = 1, or
  * tA * tB[g] for NVFP4.  One kernel launch covers every group's tiles.  The
  * grouped GEMM is the mixture-of-experts workload the "ThunderKittens 2.0"
  * post points to (section on what comes next).

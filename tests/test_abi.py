@@ -21,7 +21,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("gemm_bf16", "gemm_mx", "gemm_nvfp4", "dbs_status_str", "dbs_last_error", "dbs_version"):
+    for n in ("gemm_bf16", "gemm_mx", "gemm_mx_mixed", "gemm_nvfp4", "dbs_status_str", "dbs_last_error",
+              "dbs_version"):
         assert n in names
 
 
@@ -29,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = dbs.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.dbs_version() == 100
+    assert L.dbs_version() == 101
 
 
 def test_status_strings():
@@ -64,6 +65,28 @@ def test_mx_validation(elem, K, want):
     L = dbs.lib()
     lb = 1 if want == 2 else 0
     assert L.gemm_mx(elem, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, K, 0, lb, NUL) == want
+
+
+@pytest.mark.parametrize("ea,eb,lay,want", [
+    (0, 4, (0, 0), 2),          # E4M3 x E2M1: not implemented
+    (4, 1, (0, 0), 2),          # E2M1 x E5M2
+    (1, 1, (1, 0), 2),          # E5M2 MN-major
+    (0, 1, (0, 1), 2),
+    (2, 0, (0, 0), 1),          # unknown element code
+    (1, 7, (0, 0), 1),
+])
+def test_mx_mixed_validation(ea, eb, lay, want):
+    L = dbs.lib()
+    assert L.gemm_mx_mixed(ea, eb, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, *lay, NUL) == want
+    assert L.dbs_last_error().decode() != ""
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would reach a real device")
+@pytest.mark.parametrize("ea,eb", [(0, 1), (1, 0), (1, 1), (4, 4)])
+def test_mx_mixed_valid_pairs_pass_validation(ea, eb):
+    L = dbs.lib()
+    assert L.gemm_mx_mixed(ea, eb, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 0, 0, NUL) == 3
+    assert L.gemm_mx(1, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 0, 0, NUL) == 3
 
 
 def test_mx_null_scales():

@@ -1,0 +1,120 @@
+"""GPU parity of the 8-bit MX element formats per operand (E4M3 / E5M2 in any
+pairing, gemm_mx_mixed and gemm_mx('e5m2')) through the C ABI, against the
+oracle's per-operand decoding."""
+import numpy as np
+import pytest
+import torch
+
+import dense_block_scaled_amd as dbs
+import synth
+from tests import _gpu, _pins
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+
+
+def run_mixed(w: dict) -> torch.Tensor:
+    d = _gpu.to_dev(w)
+    ea, eb = w["elemA"], w["elemB"]
+    if ea == eb:
+        return dbs.gemm_mx(ea, d["A"], d["sA"], d["B"], d["sB"], K=w["K"])
+    return dbs.gemm_mx_mixed(ea, eb, d["A"], d["sA"], d["B"], d["sB"], K=w["K"])
+
+
+def _pid(p):
+    return f"{p[0]}x{p[1]}"
+
+
+# 256 x 64 tiles: register-staged scales (K = 352) and the three-slot ring
+# (K = 512); 256 x 256 tiles: register-staged (352), per-stage (384) and
+# chunked (512) scales.
+SHAPES = [(300, 520, 352), (256, 20000, 512), (3000, 2900, 352), (2900, 3000, 384), (2944, 3008, 512)]
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=_pid)
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_mixed_matches_oracle(shape, pair):
+    M, N, K = shape
+    _gpu.say(f"[mixed] {_pid(pair)} {shape}")
+    w = synth.workload("mxfp8", M, N, K, 500 + M % 53, 600 + N % 59, *pair)
+    D = run_mixed(w)
+    torch.cuda.synchronize()
+    if M * N <= 1 << 23:
+        _gpu.check_full("mxfp8", w, D)
+    else:
+        em, en = synth.sample_entries(72, M, N, 4096)
+        _gpu.check_sampled("mxfp8", w, D, em, en)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=_pid)
+def test_mixed_random_codes(pair):
+    """Codes over each format's whole finite range with random non-unit scales."""
+    _gpu.say(f"[mixed] {_pid(pair)} random codes")
+    w = _pins.make_w_mx8(*pair, 300, 280, 128, np.random.default_rng(23), scale_lo=112, scale_hi=142)
+    D = run_mixed(w)
+    torch.cuda.synchronize()
+    _gpu.check_full("mxfp8", w, D)
+
+
+@pytest.mark.parametrize("pair", PAIRS, ids=_pid)
+@pytest.mark.parametrize("mk", [(300, 512), (3000, 2944)], ids=lambda s: "x".join(map(str, s)))
+def test_mixed_exact_permutation(pair, mk):
+    """A (elem_a codes, random scales) times a permutation matrix in elem_b
+    with non-unit scales: every output is one decoded element of A times two
+    powers of two, exact in bf16, compared bit for bit."""
+    M, K = mk
+    ea, eb = pair
+    _gpu.say(f"[mixed] {_pid(pair)} exact permutation {M}x{K}x{K}")
+    rng = np.random.default_rng(39)
+    N = K
+    w = _pins.make_w_mx8(ea, eb, M, N, K, rng, scale_lo=110, scale_hi=140)
+    pi = rng.permutation(K)
+    B = np.zeros((N, K), np.uint8)
+    B[np.arange(N), pi] = 0x3C if eb == "e5m2" else 0x38          # 1.0
+    w["B"] = B
+    w["sB"] = rng.integers(118, 137, (N, K // 32)).astype(np.uint8)
+    D = run_mixed(w)
+    torch.cuda.synchronize()
+    if M * K <= 1 << 20:
+        _gpu.check_exact("mxfp8", w, D)
+    else:
+        em, en = synth.sample_entries(40, M, N, 4096)
+        _gpu.check_exact_sampled("mxfp8", w, D, em, en)
+
+
+def test_grouped_e5m2():
+    """The grouped MX GEMM with E5M2 elements on both sides."""
+    sizes, N, K = [0, 130, 257, 40], 200, 512
+    _gpu.say(f"[mixed] grouped e5m2 sizes={sizes}")
+    G, M = len(sizes), int(sum(sizes))
+    w = synth.workload("mxfp8", M, G * N, K, 61, 62, "e5m2", "e5m2")
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    d = _gpu.to_dev(w)
+    D = dbs.gemm_grouped_mx("e5m2", d["A"], d["sA"], d["B"].reshape(G, N, -1), d["sB"].reshape(G, N, -1),
+                            off.tolist(), K=K)
+    torch.cuda.synchronize()
+    for g in range(G):
+        a, b = int(off[g]), int(off[g + 1])
+        if a == b:
+            continue
+        wg = {"fmt": "mxfp8", "M": b - a, "N": N, "K": K, "elemA": "e5m2", "elemB": "e5m2",
+              "A": w["A"][a:b], "sA": w["sA"][a:b], "B": w["B"][g * N:(g + 1) * N], "sB": w["sB"][g * N:(g + 1) * N]}
+        _gpu.check_full("mxfp8", wg, D[a:b])
+
+
+def test_e4m3_pair_unchanged():
+    """gemm_mx_mixed('e4m3', 'e4m3') is the MXFP8 GEMM, bit for bit."""
+    _gpu.say("[mixed] e4m3 x e4m3 via gemm_mx_mixed")
+    w = synth.workload("mxfp8", 2944, 3008, 512, 63, 64)
+    d = _gpu.to_dev(w)
+    D0 = dbs.gemm_mx("e4m3", d["A"], d["sA"], d["B"], d["sB"], K=512)
+    D1 = dbs.gemm_mx_mixed("e4m3", "e4m3", d["A"], d["sA"], d["B"], d["sB"], K=512)
+    torch.cuda.synchronize()
+    assert np.array_equal(_gpu.d_bits(D0), _gpu.d_bits(D1))
