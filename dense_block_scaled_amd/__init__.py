@@ -203,7 +203,8 @@ def gemm_nvfp4(A: torch.Tensor, sA: torch.Tensor, tA: float, B: torch.Tensor, sB
 
 def quant_mx(elem: str, x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
     """fp32 x (rows, K) -> (codes, E8M0 scales per 32): codes (rows, K) uint8
-    for elem='e4m3', (rows, K/2) packed for elem='e2m1'; scales (rows, K/32)."""
+    for elem='e4m3' or 'e5m2', (rows, K/2) packed for elem='e2m1'; scales
+    (rows, K/32)."""
     code = _ELEM[elem]
     rows, K = x.shape
     px = _dev(x, "x", (torch.float32,), (rows, K))

@@ -234,13 +234,14 @@ static dbs_status check_quant(const float *x, const void *codes, int64_t rows, i
 dbs_status quant_mx(dbs_mx_elem elem, const float *x, int64_t rows, int64_t K, void *codes, uint8_t *scales,
                     hipStream_t stream)
 {
-    if (elem != DBS_E4M3 && elem != DBS_E2M1) return fail(DBS_EINVAL, "mx: unknown element format");
+    if (!mx_elem_known(elem)) return fail(DBS_EINVAL, "mx: unknown element format");
     dbs_status st = check_quant(x, codes, rows, K, 32);
     if (st != DBS_OK) return st;
     if (!scales) return fail(DBS_EINVAL, "null pointer argument");
     int cus = 0;
     if ((st = device_cus(&cus)) != DBS_OK) return st;
-    hipError_t e = dbs::launch_quant_mx(elem == DBS_E4M3, x, rows * K, static_cast<uint8_t *>(codes), scales, cus, stream);
+    hipError_t e = dbs::launch_quant_mx(elem == DBS_E2M1 ? 4 : 8, elem == DBS_E5M2, x, rows * K,
+                                        static_cast<uint8_t *>(codes), scales, cus, stream);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
     g_err[0] = '\0';
     return DBS_OK;

@@ -54,8 +54,8 @@ hipError_t launch_gemm(int fmt, int shape, const Params &p, int grid, hipStream_
 // blocks (n a multiple of 32 for MX, 16 for NVFP4, 8 for bf16); x, codes and
 // out 16-byte aligned.  NVFP4 uses *t as the tensor-amax accumulator and
 // leaves the tensor scale there.
-hipError_t launch_quant_mx(bool e4m3, const float *x, int64_t n, uint8_t *codes, uint8_t *scales, int cus,
-                           hipStream_t stream);
+hipError_t launch_quant_mx(int elem_bits, bool e5m2, const float *x, int64_t n, uint8_t *codes, uint8_t *scales,
+                           int cus, hipStream_t stream);
 hipError_t launch_quant_nvfp4(const float *x, int64_t n, uint8_t *codes, uint8_t *scales, float *t, int cus,
                               hipStream_t stream);
 hipError_t launch_quant_bf16(const float *x, int64_t n, uint16_t *out, int cus, hipStream_t stream);

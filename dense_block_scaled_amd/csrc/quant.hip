@@ -2,9 +2,10 @@
 // input formats (the step upstream of the block-scaled GEMM):
 //
 //   MXFP8 / MXFP4: per block of 32 consecutive K elements, the E8M0 scale
-//     2^e with e = floor(log2(amax / emax)) (emax = 448 for E4M3, 6 for E2M1;
-//     e clamped to [-127, 127]; an all-zero block gets scale 1), then each
-//     element x -> nearest E4M3 / E2M1 value of x * 2^-e.  This is the scale
+//     2^e with e = floor(log2(amax / emax)) (emax = 448 for E4M3, 57344 for
+//     E5M2, 6 for E2M1; e clamped to [-127, 127]; an all-zero block gets
+//     scale 1), then each element x -> nearest E4M3 / E5M2 / E2M1 value of
+//     x * 2^-e.  This is the scale
 //     rule stated with the workloads of the "ThunderKittens 2.0" MXFP8 GEMM
 //     (section 2.1: an E8M0 scale per 32 elements) and the OCP MX v1.0
 //     definition of the scale as a power of two.
@@ -16,7 +17,8 @@
 //
 // "Nearest" is round-to-nearest with ties to the even code (the code with its
 // lowest bit clear), saturating at the largest finite value (448, 6) and
-// keeping the sign of zero.  Inputs must be finite.
+// keeping the sign of zero.  Inputs must be finite.  (E5M2's saturating
+// rounding never produces its infinity code.)
 //
 // All kernels are bandwidth-bound streams over the flat element array
 // (K is a multiple of the block size, so blocks never straddle rows): four
@@ -54,6 +56,23 @@ __device__ __forceinline__ uint32_t enc_e4m3_abs(float a)
     return code > 0x7Eu ? 0x7Eu : code;
 }
 
+// |x| rounded to the nearest E5M2 code (0..0x7B), ties to even, saturating:
+// as for E4M3 with two mantissa bits, a minimum normal exponent of -14 and
+// subnormal steps of 2^-16 (OCP MX v1.0 E5M2, bias 15).
+__device__ __forceinline__ uint32_t enc_e5m2_abs(float a)
+{
+    if (a >= 57344.0f) return 0x7Bu;
+    int E;
+    (void)__builtin_frexpf(a, &E);
+    const int e = a < 0x1p-14f ? -14 : E - 1;
+    const float v = __builtin_rintf(__builtin_ldexpf(a, 2 - e));      // grid units of 2^(e-2)
+    if (e == -14 && v < 4.0f) return (uint32_t)v;                      // subnormal (or zero)
+    const int ee = v >= 8.0f ? e + 1 : e;
+    const uint32_t m = v >= 8.0f ? 0u : (uint32_t)v - 4u;
+    const uint32_t code = ((uint32_t)(ee + 15) << 2) | m;
+    return code > 0x7Bu ? 0x7Bu : code;
+}
+
 // |x| rounded to the nearest E2M1 code (0..7), ties to even, saturating.
 // Values 0, 0.5, 1, 1.5, 2, 3, 4, 6: step 0.5 below 2, 1 in [2, 4), 2 above.
 __device__ __forceinline__ uint32_t enc_e2m1_abs(float a)
@@ -68,6 +87,10 @@ __device__ __forceinline__ uint32_t sign_of(float x) { return __builtin_bit_cast
 
 __device__ __forceinline__ uint32_t enc_e4m3(float x) { return (sign_of(x) << 7) | enc_e4m3_abs(__builtin_fabsf(x)); }
 __device__ __forceinline__ uint32_t enc_e2m1(float x) { return (sign_of(x) << 3) | enc_e2m1_abs(__builtin_fabsf(x)); }
+__device__ __forceinline__ uint32_t enc_e5m2(float x) { return (sign_of(x) << 7) | enc_e5m2_abs(__builtin_fabsf(x)); }
+
+// Element formats of the MX quantiser.
+constexpr int kQE2M1 = 0, kQE4M3 = 1, kQE5M2 = 2;
 
 // E4M3 code (finite, non-negative) -> its fp32 value.
 __device__ __forceinline__ float dec_e4m3_pos(uint32_t c)
@@ -87,19 +110,21 @@ __device__ __forceinline__ float group_max(float v)
 }
 
 // e = floor(log2(amax / emax)) for amax > 0, exactly: amax = f 2^E with f in
-// [1, 2) (frexp gives f/2 in [0.5, 1)); emax = 1.75 * 2^8 (E4M3) or
-// 1.5 * 2^2 (E2M1).
-template <bool E4M3>
+// [1, 2) (frexp gives f/2 in [0.5, 1)); emax = 1.75 * 2^8 (E4M3), 1.75 *
+// 2^15 (E5M2) or 1.5 * 2^2 (E2M1).
+template <int ELEM>
 __device__ __forceinline__ int mx_exponent(float amax)
 {
     int E;
     const float f = 2.0f * __builtin_frexpf(amax, &E);
     --E;
-    return E4M3 ? E - 8 - (f < 1.75f ? 1 : 0) : E - 2 - (f < 1.5f ? 1 : 0);
+    if constexpr (ELEM == kQE4M3) return E - 8 - (f < 1.75f ? 1 : 0);
+    if constexpr (ELEM == kQE5M2) return E - 15 - (f < 1.75f ? 1 : 0);
+    return E - 2 - (f < 1.5f ? 1 : 0);
 }
 
 // Elements 8 l .. 8 l + 7 of the flat array for lane index l (grid-stride).
-template <bool E4M3>
+template <int ELEM>
 __global__ __launch_bounds__(256) void quant_mx_kernel(const float *__restrict__ x, uint8_t *__restrict__ codes,
                                                        uint8_t *__restrict__ scales, int64_t nlanes)
 {
@@ -113,7 +138,7 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const float *__restrict__
 #pragma unroll
         for (int i = 0; i < 4; ++i) a = __builtin_fmaxf(a, __builtin_fmaxf(__builtin_fabsf(v0[i]), __builtin_fabsf(v1[i])));
         a = group_max<4>(a);
-        int e = a > 0.0f ? mx_exponent<E4M3>(a) : 0;
+        int e = a > 0.0f ? mx_exponent<ELEM>(a) : 0;
         e = e < -127 ? -127 : (e > 127 ? 127 : e);
         if ((threadIdx.x & 3) == 0) scales[l >> 2] = (uint8_t)(e + 127);
         float y[8];
@@ -122,12 +147,12 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const float *__restrict__
             y[i] = __builtin_ldexpf(v0[i], -e);
             y[4 + i] = __builtin_ldexpf(v1[i], -e);
         }
-        if constexpr (E4M3) {
+        if constexpr (ELEM != kQE2M1) {
             uint32_t lo = 0, hi = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                lo |= enc_e4m3(y[i]) << (8 * i);
-                hi |= enc_e4m3(y[4 + i]) << (8 * i);
+                lo |= (ELEM == kQE4M3 ? enc_e4m3(y[i]) : enc_e5m2(y[i])) << (8 * i);
+                hi |= (ELEM == kQE4M3 ? enc_e4m3(y[4 + i]) : enc_e5m2(y[4 + i])) << (8 * i);
             }
             *reinterpret_cast<uint2 *>(codes + 8 * l) = uint2{lo, hi};
         } else {
@@ -225,15 +250,17 @@ int grid_for(int64_t lanes, int cus)
 
 }  // namespace
 
-hipError_t launch_quant_mx(bool e4m3, const float *x, int64_t n, uint8_t *codes, uint8_t *scales, int cus,
-                           hipStream_t stream)
+hipError_t launch_quant_mx(int elem_bits, bool e5m2, const float *x, int64_t n, uint8_t *codes, uint8_t *scales,
+                           int cus, hipStream_t stream)
 {
     const int64_t lanes = n / 8;
     const int grid = grid_for(lanes, cus);
-    if (e4m3)
-        hipLaunchKernelGGL(quant_mx_kernel<true>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes);
+    if (elem_bits == 4)
+        hipLaunchKernelGGL(quant_mx_kernel<kQE2M1>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes);
+    else if (e5m2)
+        hipLaunchKernelGGL(quant_mx_kernel<kQE5M2>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes);
     else
-        hipLaunchKernelGGL(quant_mx_kernel<false>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes);
+        hipLaunchKernelGGL(quant_mx_kernel<kQE4M3>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes);
     return hipGetLastError();
 }
 

@@ -159,9 +159,10 @@ dbs_status gemm_grouped_nvfp4(const void *A, const uint8_t *sA, float tA, const 
  *
  * quant_mx: K a multiple of 32.  Per block of 32 consecutive elements of a
  *   row, E8M0 scale 2^e with e = floor(log2(amax / emax)) (emax = 448 for
- *   DBS_E4M3, 6 for DBS_E2M1; e clamped to [-127, 127]; scale 1 for an
- *   all-zero block), then each element the nearest E4M3 / E2M1 code of
- *   x / 2^e.  codes: rows x K bytes (E4M3) or rows x K/2 packed bytes (E2M1,
+ *   DBS_E4M3, 57344 for DBS_E5M2, 6 for DBS_E2M1; e clamped to [-127, 127];
+ *   scale 1 for an all-zero block), then each element the nearest E4M3 /
+ *   E5M2 / E2M1 code of x / 2^e.  codes: rows x K bytes (E4M3, E5M2) or
+ *   rows x K/2 packed bytes (E2M1,
  *   element 2j in the low nibble); scales: rows x K/32 bytes.  The scale rule
  *   follows the MX scale definition (OCP MX v1.0) with the workloads'
  *   floor(log2(amax / emax)) exponent.

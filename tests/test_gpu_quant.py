@@ -53,7 +53,7 @@ def _inputs(K: int, emax: float):
     return np.concatenate([x, _special_rows(K, emax)])
 
 
-@pytest.mark.parametrize("elem,emax", [("e4m3", 448.0), ("e2m1", 6.0)])
+@pytest.mark.parametrize("elem,emax", [("e4m3", 448.0), ("e5m2", 57344.0), ("e2m1", 6.0)])
 @pytest.mark.parametrize("K", [32, 1024])
 def test_quant_mx_matches_oracle(elem, emax, K):
     _gpu.say(f"[quant] mx {elem} K={K}")
@@ -116,3 +116,17 @@ def test_quantise_then_gemm(fmt):
     D = _gpu.run(fmt, w)
     torch.cuda.synchronize()
     _gpu.check_full(fmt, w, D)
+
+
+def test_quantise_e5m2_then_mixed_gemm():
+    """GPU-quantised E5M2 A with E4M3 B through gemm_mx_mixed against the
+    oracle GEMM on the same codes."""
+    _gpu.say("[quant] e5m2 x e4m3 quantise then GEMM")
+    xa, xb = synth.normal(76, 260, 512), synth.normal(77, 300, 512)
+    ca, sa = dbs.quant_mx("e5m2", torch.from_numpy(xa).cuda())
+    cb, sb = dbs.quant_mx("e4m3", torch.from_numpy(xb).cuda())
+    D = dbs.gemm_mx_mixed("e5m2", "e4m3", ca, sa, cb, sb, K=512)
+    torch.cuda.synchronize()
+    w = {"fmt": "mxfp8", "M": 260, "N": 300, "K": 512, "elemA": "e5m2", "elemB": "e4m3",
+         "A": ca.cpu().numpy(), "sA": sa.cpu().numpy(), "B": cb.cpu().numpy(), "sB": sb.cpu().numpy()}
+    _gpu.check_full("mxfp8", w, D)
