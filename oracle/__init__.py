@@ -62,6 +62,8 @@ def _load():
     lib.orc_quant_nvfp4.argtypes = [P, I64, I64, P, P, P]
     lib.orc_quant_nvfp4.restype = ctypes.c_int
     lib.orc_quant_bf16.argtypes = [P, I64, P]
+    lib.orc_requant_nvfp4_mx8.argtypes = [P, P, I64, I64, P, P]
+    lib.orc_requant_nvfp4_mx8.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -206,6 +208,28 @@ def quant_bf16(x: np.ndarray) -> np.ndarray:
     out = np.empty(x.shape, np.uint16)
     lib.orc_quant_bf16(_ptr(x), x.size, _ptr(out))
     return out
+
+
+def requant_nvfp4_mx8(codes: np.ndarray, scales: np.ndarray, K: int):
+    """NVFP4 operand (rows x K/2 packed E2M1, rows x K/16 E4M3) -> the MXFP8
+    operand of the FP8-rate GEMM (rows x K E4M3, rows x K/32 E8M0)."""
+    lib = _load()
+    c = _c(codes, np.uint8)
+    s = _c(scales, np.uint8)
+    rows = c.shape[0]
+    out = np.zeros((rows, K), np.uint8)
+    osc = np.zeros((rows, K // 32), np.uint8)
+    if lib.orc_requant_nvfp4_mx8(_ptr(c), _ptr(s), rows, K, _ptr(out), _ptr(osc)):
+        raise ValueError("K must be a multiple of 32")
+    return out, osc
+
+
+def nvfp4_fp8_workload(w: dict) -> dict:
+    """The MXFP8 workload the FP8-rate NVFP4 GEMM computes for NVFP4 workload
+    w (its D is this workload's GEMM times tA * tB)."""
+    a, sa = requant_nvfp4_mx8(w["A"], w["sA"], w["K"])
+    b, sb = requant_nvfp4_mx8(w["B"], w["sB"], w["K"])
+    return {"fmt": "mxfp8", "M": w["M"], "N": w["N"], "K": w["K"], "A": a, "sA": sa, "B": b, "sB": sb}
 
 
 # ---- comparison ------------------------------------------------------------

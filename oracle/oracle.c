@@ -551,6 +551,43 @@ int orc_quant_nvfp4(const float *x, int64_t rows, int64_t K, uint8_t *codes, uin
 }
 
 /* bf16 recipe: fp32 -> bf16 RNE */
+/* NVFP4 -> MXFP8 requantisation (the opt-in FP8-rate NVFP4 GEMM): per
+ * 32-element block of a row, made of two 16-element groups with E4M3 scales
+ * s0, s1, the E8M0 exponent is E = floor(log2(max(|s0|, |s1|))) (0 when both
+ * are zero), and each element a (E2M1) of group g becomes the nearest E4M3
+ * code of a * s_g * 2^-E (ties to even).  That value is below 12 in
+ * magnitude, so E4M3 never saturates; values under E4M3's subnormal step
+ * lose precision.  The scale code is E + 127.  Codes in: rows x K/2 packed
+ * E2M1, rows x K/16 E4M3; out: rows x K E4M3, rows x K/32 E8M0.  K % 32 == 0.
+ * (The tensor scales are applied to the GEMM result, as for NVFP4.) */
+int orc_requant_nvfp4_mx8(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K, uint8_t *out,
+                          uint8_t *out_scales)
+{
+    if (K % 32) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < K / 32; ++b) {
+            double s0 = orc_decode_e4m3(scales[r * (K / 16) + 2 * b]);
+            double s1 = orc_decode_e4m3(scales[r * (K / 16) + 2 * b + 1]);
+            double m = fmax(fabs(s0), fabs(s1));
+            int E = 0;
+            if (m > 0.0) {
+                int ex;
+                frexp(m, &ex);              /* m in [2^(ex-1), 2^ex) */
+                E = ex - 1;
+            }
+            out_scales[r * (K / 32) + b] = (uint8_t)(E + 127);
+            for (int i = 0; i < 32; ++i) {
+                int64_t k = b * 32 + i;
+                uint8_t byte = codes[r * (K / 2) + k / 2];
+                double a = orc_decode_e2m1((k & 1) ? (byte >> 4) : (byte & 0xF));
+                double v = ldexp(a * (i < 16 ? s0 : s1), -E);      /* exact */
+                out[r * K + k] = (uint8_t)orc_encode_e4m3(v);
+            }
+        }
+    }
+    return 0;
+}
+
 void orc_quant_bf16(const float *x, int64_t n, uint16_t *out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = (uint16_t)orc_encode_bf16((double)x[i]);
