@@ -11,7 +11,8 @@ to exceed three times the 256 MB last-level cache; `warmup` launches cycling
 the groups; then `steps` back-to-back launches between two events on the
 launch stream, with a device synchronisation on both sides; a 0.5 s pause
 between kernels.  The same protocol then times the other formats at their
-shapes (reported under "per_format").
+shapes (reported under "per_format"), among them the opt-in lossy FP8-rate
+NVFP4 path (nvfp4_fp8: requantisation and MXFP8 GEMM in each timed launch).
 
 Printed: one JSON line with the throughput (TFLOP/s), the roofline fraction
 of the timed kernel, and the CPU oracle timed on a bounded sample of the same
@@ -34,8 +35,10 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 LLC_BYTES = 256 * 2 ** 20                      # MI355X Infinity Cache (MALL)
-PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "nvfp4": 2500.0}
-PEAK_NOTE = {"nvfp4": "exact NVFP4 runs on fp16 MFMA: priced at the bf16/fp16 dense peak"}
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "nvfp4": 2500.0, "nvfp4_fp8": 5000.0}
+PEAK_NOTE = {"nvfp4": "exact NVFP4 runs on fp16 MFMA: priced at the bf16/fp16 dense peak",
+             "nvfp4_fp8": "opt-in lossy FP8-rate NVFP4 (gemm_nvfp4_fp8): requantisation to MXFP8 plus the MXFP8 "
+                          "GEMM, both inside the timed launch; priced at the fp8 dense peak"}
 HBM_GBS = 8000.0
 ELEM_BITS = {"bf16": 16, "mxfp8": 8, "mxfp4": 4, "nvfp4": 4}
 BLOCK = {"bf16": 0, "mxfp8": 32, "mxfp4": 32, "nvfp4": 16}
@@ -46,7 +49,20 @@ CONFIGS = {
     "mxfp4": (3, 8192, 8192, 8192),
     "nvfp4": (4, 8192, 8192, 8192),
     "nvfp4_skinny": (4, 256, 16384, 8192),
+    "nvfp4_fp8": (4, 8192, 8192, 8192),
+    "nvfp4_fp8_skinny": (4, 256, 16384, 8192),
 }
+# the encoding each workload's inputs take, and the entry point it times
+INPUT_FMT = {"nvfp4_skinny": "nvfp4", "nvfp4_fp8": "nvfp4", "nvfp4_fp8_skinny": "nvfp4"}
+KERNEL_OF = {"nvfp4_skinny": "nvfp4", "nvfp4_fp8_skinny": "nvfp4_fp8"}
+
+
+def input_fmt(fmt):
+    return INPUT_FMT.get(fmt, fmt)
+
+
+def kernel_of(fmt):
+    return KERNEL_OF.get(fmt, fmt)
 KERNEL_SOURCES = ["dense_block_scaled_amd/csrc/gemm.hip", "dense_block_scaled_amd/csrc/launch.h"]
 
 
@@ -87,7 +103,7 @@ def traffic_for(workload):
 def make_inputs(fmt, cfg):
     import synth
     c, M, N, K = cfg
-    w = synth.workload(fmt.replace("_skinny", ""), M, N, K, 100 * c + 1, 100 * c + 2)
+    w = synth.workload(input_fmt(fmt), M, N, K, 100 * c + 1, 100 * c + 2)
     return w
 
 
@@ -111,6 +127,10 @@ def launcher(fmt, w, dev, out):
     if fmt == "mxfp4":
         return lambda: dbs.gemm_mx("e2m1", dev["A"], dev["sA"], dev["B"], dev["sB"], K=K, out=out)
     tA, tB = w["tA"], w["tB"]
+    if fmt == "nvfp4_fp8":
+        import torch
+        ws = torch.empty(dbs.nvfp4_fp8_workspace_bytes(w["M"], w["N"], K), dtype=torch.uint8, device="cuda")
+        return lambda: dbs.gemm_nvfp4_fp8(dev["A"], dev["sA"], tA, dev["B"], dev["sB"], tB, out=out, workspace=ws)
     return lambda: dbs.gemm_nvfp4(dev["A"], dev["sA"], tA, dev["B"], dev["sB"], tB, out=out)
 
 
@@ -118,13 +138,12 @@ def time_gemm(fmt, w, steps, warmup):
     """Protocol timing; returns (avg seconds per launch, groups, output tensor)."""
     import torch
     M, N, K = w["M"], w["N"], w["K"]
-    base = fmt.replace("_skinny", "")
-    in_bytes = algorithmic_bytes(base, M, N, K) - M * N * 2
+    in_bytes = algorithmic_bytes(input_fmt(fmt), M, N, K) - M * N * 2
     groups = 1 if in_bytes >= 3 * LLC_BYTES else (3 * LLC_BYTES) // in_bytes + 1
     dev0 = to_device(w)
     devs = [dev0] + [{k: v.clone() for k, v in dev0.items()} for _ in range(groups - 1)]
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    calls = [launcher(base, w, d, out) for d in devs]
+    calls = [launcher(kernel_of(fmt), w, d, out) for d in devs]
     torch.cuda.synchronize()
     for i in range(warmup):
         calls[i % groups]()
@@ -150,7 +169,7 @@ def cpu_baseline(fmt, w, D, target_s=12.0):
     import torch
     import oracle
     M, N, K = w["M"], w["N"], w["K"]
-    base = fmt.replace("_skinny", "")
+    base = input_fmt(fmt)
     threads = oracle.default_threads()
 
     def entries(r0, r1):
@@ -190,8 +209,7 @@ def measure(fmt, steps, warmup):
     avg, groups, D = time_gemm(fmt, w, steps, warmup)
     M, N, K = w["M"], w["N"], w["K"]
     tflops = 2.0 * M * N * K / avg / 1e12
-    base = fmt.replace("_skinny", "")
-    gbs = algorithmic_bytes(base, M, N, K) / avg / 1e9
+    gbs = algorithmic_bytes(input_fmt(fmt), M, N, K) / avg / 1e9
     log(f"[bench] {fmt}: {avg * 1e6:.1f} us/launch, {tflops:.1f} TFLOP/s, {gbs:.0f} GB/s, {groups} input groups")
     return w, D, avg, groups, tflops, gbs
 
@@ -234,7 +252,7 @@ def main():
     w, D, avg, groups, tflops, gbs = measure(fmt, args.steps, args.warmup)
     M, N, K = w["M"], w["N"], w["K"]
     workload = f"{fmt}_gemm_{M}x{N}x{K}"
-    peak = PEAK_TFLOPS[fmt.replace("_skinny", "")]
+    peak = PEAK_TFLOPS[kernel_of(fmt)]
     result = {
         "metric": "TFLOP/s per GEMM (BF16/MXFP8/MXFP4) at 8192^3 and % of dtype MFMA peak",
         "value": round(tflops, 2),
@@ -246,7 +264,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": fmt.replace("_skinny", ""),
+        "dtype": input_fmt(fmt),
         "data": "synthetic: seeded N(0,1) (PCG64), encoded per the format's recipe",
         "config": {"workload": workload, "format": fmt, "M": M, "N": N, "K": K,
                    "layout": "A MxK, B NxK (K-major), D MxN bf16", "input_groups": groups},
@@ -262,17 +280,16 @@ def main():
             f"sample max r {rmax:.2e}")
     if not args.only:
         per = []
-        for f in ["bf16", "mxfp8", "mxfp4", "nvfp4", "nvfp4_skinny"]:
+        for f in ["bf16", "mxfp8", "mxfp4", "nvfp4", "nvfp4_skinny", "nvfp4_fp8", "nvfp4_fp8_skinny"]:
             if f == fmt:
                 entry_t, entry_gbs, entry_avg = tflops, gbs, avg
                 wf = w
             else:
                 time.sleep(0.5)
                 wf, _, entry_avg, _, entry_t, entry_gbs = measure(f, args.steps, args.warmup)
-            base = f.replace("_skinny", "")
             per.append({"workload": f"{f}_gemm_{wf['M']}x{wf['N']}x{wf['K']}",
                         "us": round(entry_avg * 1e6, 2), "tflops": round(entry_t, 2),
-                        "frac_mfma_peak": round(entry_t / PEAK_TFLOPS[base], 4),
+                        "frac_mfma_peak": round(entry_t / PEAK_TFLOPS[kernel_of(f)], 4),
                         "gbs": round(entry_gbs, 1), "frac_hbm_peak": round(entry_gbs / HBM_GBS, 4)})
         result["per_format"] = per
         result["peak_notes"] = PEAK_NOTE

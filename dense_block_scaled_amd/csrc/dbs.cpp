@@ -166,6 +166,28 @@ int mx8_code(dbs_mx_elem e) { return e == DBS_E5M2 ? 1 : 0; }
 
 bool mx_elem_known(dbs_mx_elem e) { return e == DBS_E4M3 || e == DBS_E5M2 || e == DBS_E2M1; }
 
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace layout: A codes (M x K), B codes (N x K), A scales (M x K/32),
+// B scales (N x K/32), each starting on a 256-byte boundary.
+struct Fp8Ws {
+    uint8_t *a, *b, *sa, *sb;
+    int64_t bytes;
+};
+
+Fp8Ws fp8_ws(void *base, int64_t M, int64_t N, int64_t K)
+{
+    const int64_t ob = align256(M * K), osa = ob + align256(N * K), osb = osa + align256(M * K / 32);
+    Fp8Ws w;
+    w.bytes = osb + align256(N * K / 32);
+    uint8_t *p = static_cast<uint8_t *>(base);
+    w.a = p;
+    w.b = p ? p + ob : nullptr;
+    w.sa = p ? p + osa : nullptr;
+    w.sb = p ? p + osb : nullptr;
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -216,6 +238,39 @@ dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA, const void *B,
     if (la != DBS_K_MAJOR || lb != DBS_K_MAJOR)
         return fail(DBS_EUNSUPPORTED, "nvfp4: only K-major A and B are implemented");
     return run(dbs::kNVFP4, A, sA, B, sB, D, M, N, K, tA * tB, 4, 16, stream);
+}
+
+// ---- FP8-rate NVFP4 (opt-in, lossy) ---------------------------------------------
+
+size_t gemm_nvfp4_fp8_workspace(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || K % 32 || M > (int64_t(1) << 25) || N > (int64_t(1) << 25) ||
+        K > (int64_t(1) << 22))
+        return 0;
+    return (size_t)fp8_ws(nullptr, M, N, K).bytes;
+}
+
+dbs_status gemm_nvfp4_fp8(const void *A, const uint8_t *sA, float tA, const void *B, const uint8_t *sB, float tB,
+                          void *D, int64_t M, int64_t N, int64_t K, dbs_layout la, dbs_layout lb, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream)
+{
+    if (!sA || !sB || !workspace) return fail(DBS_EINVAL, "null pointer argument");
+    dbs_status st = check_common(A, B, D, M, N, K, la, lb, int64_t(1) << 22);
+    if (st != DBS_OK) return st;
+    if (K % 16) return fail(DBS_EINVAL, "nvfp4: K must be a multiple of 16");
+    if (K % 32) return fail(DBS_EUNSUPPORTED, "nvfp4 fp8-rate: K must be a multiple of 32 (whole MX blocks)");
+    if (la != DBS_K_MAJOR || lb != DBS_K_MAJOR)
+        return fail(DBS_EUNSUPPORTED, "nvfp4 fp8-rate: only K-major A and B are implemented");
+    if (!aligned(workspace, 256)) return fail(DBS_EINVAL, "workspace must be 256-byte aligned");
+    const Fp8Ws w = fp8_ws(workspace, M, N, K);
+    if ((int64_t)workspace_bytes < w.bytes) return fail(DBS_EINVAL, "workspace smaller than gemm_nvfp4_fp8_workspace()");
+    int cus = 0;
+    if ((st = device_cus(&cus)) != DBS_OK) return st;
+    hipError_t e = dbs::launch_requant_nvfp4_mx8(static_cast<const uint8_t *>(A), sA, M * K, w.a, w.sa, cus, stream);
+    if (e == hipSuccess)
+        e = dbs::launch_requant_nvfp4_mx8(static_cast<const uint8_t *>(B), sB, N * K, w.b, w.sb, cus, stream);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    return run(dbs::kMXFP8, w.a, w.sa, w.b, w.sb, D, M, N, K, tA * tB, 8, 32, stream);
 }
 
 // ---- quantisers ----------------------------------------------------------------

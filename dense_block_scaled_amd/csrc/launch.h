@@ -58,6 +58,11 @@ hipError_t launch_quant_mx(int elem_bits, bool e5m2, const float *x, int64_t n, 
                            int cus, hipStream_t stream);
 hipError_t launch_quant_nvfp4(const float *x, int64_t n, uint8_t *codes, uint8_t *scales, float *t, int cus,
                               hipStream_t stream);
+// NVFP4 operand of n elements (packed E2M1 codes, E4M3 scales per 16; n a
+// multiple of 32, codes and out 16-byte aligned) -> MXFP8 (E4M3 codes, E8M0
+// scales per 32) for the FP8-rate NVFP4 GEMM.
+hipError_t launch_requant_nvfp4_mx8(const uint8_t *codes, const uint8_t *scales, int64_t n, uint8_t *out,
+                                    uint8_t *out_scales, int cus, hipStream_t stream);
 hipError_t launch_quant_bf16(const float *x, int64_t n, uint16_t *out, int cus, hipStream_t stream);
 
 }  // namespace dbs

@@ -220,6 +220,62 @@ __global__ __launch_bounds__(256) void quant_nvfp4_kernel(const float *__restric
     }
 }
 
+// NVFP4 -> MXFP8 requantisation for the FP8-rate NVFP4 GEMM: lane l takes
+// block l of 32 elements of the flat operand (two E4M3 group scales, 16
+// packed bytes), picks E = floor(log2(max |s_g|)) (0 for two zero scales)
+// and writes the 32 nearest E4M3 codes of a * s_g * 2^-E (ties to even) and
+// the E8M0 code E + 127.  a * s_g * 2^-E has at most 6 significant bits, so
+// it is exact in fp32 and the rounding is the only inexact step.  Inputs
+// must be finite.
+__device__ __forceinline__ float dec_e4m3(uint32_t c)
+{
+    const float v = dec_e4m3_pos(c & 0x7F);
+    return (c & 0x80) ? -v : v;
+}
+
+__global__ __launch_bounds__(256) void requant_nvfp4_mx8_kernel(const uint8_t *__restrict__ codes,
+                                                                const uint8_t *__restrict__ scales,
+                                                                uint8_t *__restrict__ out,
+                                                                uint8_t *__restrict__ out_scales, int64_t nblocks)
+{
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride) {
+        const uint4 c = *reinterpret_cast<const uint4 *>(codes + 16 * b);
+        const float s0 = dec_e4m3(scales[2 * b]), s1 = dec_e4m3(scales[2 * b + 1]);
+        const float m = __builtin_fmaxf(__builtin_fabsf(s0), __builtin_fabsf(s1));
+        int E = 0;
+        if (m > 0.0f) {
+            (void)__builtin_frexpf(m, &E);     // m in [2^(E-1), 2^E)
+            --E;
+        }
+        out_scales[b] = (uint8_t)(E + 127);
+        const float f0 = __builtin_ldexpf(s0, -E), f1 = __builtin_ldexpf(s1, -E);
+        const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+        uint32_t o[8];
+        // byte j of an input dword holds two elements (low nibble first);
+        // the conversion decodes them exactly (unit scale)
+        auto pair = [](uint32_t w, float f, int j) -> uint32_t {
+            f32x2 v;
+            switch (j) {
+            case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
+            case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
+            case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
+            default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
+            }
+            return enc_e4m3(v[0] * f) | (enc_e4m3(v[1] * f) << 8);
+        };
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {             // dword d: elements 8d .. 8d+7, group d / 2
+            const float f = d < 2 ? f0 : f1;
+            o[2 * d] = pair(cw[d], f, 0) | (pair(cw[d], f, 1) << 16);
+            o[2 * d + 1] = pair(cw[d], f, 2) | (pair(cw[d], f, 3) << 16);
+        }
+        *reinterpret_cast<uint4 *>(out + 32 * b) = uint4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<uint4 *>(out + 32 * b + 16) = uint4{o[4], o[5], o[6], o[7]};
+    }
+}
+
 // *t: the tensor amax's bit pattern -> the tensor scale.
 __global__ void finish_scale_kernel(uint32_t *t) { *t = __builtin_bit_cast(uint32_t, tensor_scale(*t)); }
 
@@ -261,6 +317,16 @@ hipError_t launch_quant_mx(int elem_bits, bool e5m2, const float *x, int64_t n, 
         hipLaunchKernelGGL(quant_mx_kernel<kQE5M2>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes);
     else
         hipLaunchKernelGGL(quant_mx_kernel<kQE4M3>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes);
+    return hipGetLastError();
+}
+
+hipError_t launch_requant_nvfp4_mx8(const uint8_t *codes, const uint8_t *scales, int64_t n, uint8_t *out,
+                                    uint8_t *out_scales, int cus, hipStream_t stream)
+{
+    const int64_t nblocks = n / 32;
+    const int grid = grid_for(nblocks, cus);
+    hipLaunchKernelGGL(requant_nvfp4_mx8_kernel, dim3(grid), dim3(256), 0, stream, codes, scales, out, out_scales,
+                       nblocks);
     return hipGetLastError();
 }
 

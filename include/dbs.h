@@ -44,6 +44,7 @@
 #ifndef DBS_H
 #define DBS_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #if defined(__HIPCC__) || defined(__HIP_PLATFORM_AMD__)
@@ -130,6 +131,32 @@ dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA,
                       const void *B, const uint8_t *sB, float tB, void *D,
                       int64_t M, int64_t N, int64_t K,
                       dbs_layout la, dbs_layout lb, hipStream_t stream);
+
+/*
+ * FP8-rate NVFP4 GEMM (opt-in, LOSSY): the NVFP4 operands of gemm_nvfp4 are
+ * first requantised to MXFP8 in `workspace` -- per block of 32 K elements
+ * (two 16-element groups with E4M3 scales s0, s1) the E8M0 exponent is
+ * E = floor(log2(max |s_g|)) and each element a becomes the nearest E4M3
+ * code of a * s_g * 2^-E (ties to even) -- and the MXFP8 GEMM then runs at
+ * the 8-bit MFMA rate, with tA * tB applied to its result.  This is the
+ * FP8-rate form of the NVFP4 rescale step ("ThunderKittens 2.0", section
+ * 2.1, NVFP4 scale handling), for hardware whose scaled MFMA takes only
+ * E8M0 scales per 32.  Each requantised element is within 2^-4 of its exact
+ * value relative to that value (half a subnormal E4M3 step, 2^-10 * 2^E,
+ * absolutely, below 2^-6 * 2^E), so |D - D_exact| <= (2^-3 + 2^-8) *
+ * sum_k |dA dB| + the subnormal terms; with unit scales it is exact.  K a
+ * multiple of 32 (DBS_EUNSUPPORTED for K = 16 mod 32), K-major operands.
+ * workspace: device memory of at least gemm_nvfp4_fp8_workspace(M, N, K)
+ * bytes, 256-byte aligned, owned by the caller (overwritten, not read
+ * before being written; calls that share one workspace must not overlap).
+ * Two requantisation kernels and the GEMM are enqueued on `stream`.
+ */
+size_t gemm_nvfp4_fp8_workspace(int64_t M, int64_t N, int64_t K);    /* 0 for invalid sizes */
+dbs_status gemm_nvfp4_fp8(const void *A, const uint8_t *sA, float tA,
+                          const void *B, const uint8_t *sB, float tB, void *D,
+                          int64_t M, int64_t N, int64_t K,
+                          dbs_layout la, dbs_layout lb,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Grouped GEMMs (mixture-of-experts layout): G groups (1 <= G <= 64) share N

@@ -21,8 +21,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("gemm_bf16", "gemm_mx", "gemm_mx_mixed", "gemm_nvfp4", "dbs_status_str", "dbs_last_error",
-              "dbs_version"):
+    for n in ("gemm_bf16", "gemm_mx", "gemm_mx_mixed", "gemm_nvfp4", "gemm_nvfp4_fp8", "gemm_nvfp4_fp8_workspace",
+              "dbs_status_str", "dbs_last_error", "dbs_version"):
         assert n in names
 
 
@@ -87,6 +87,31 @@ def test_mx_mixed_valid_pairs_pass_validation(ea, eb):
     L = dbs.lib()
     assert L.gemm_mx_mixed(ea, eb, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 0, 0, NUL) == 3
     assert L.gemm_mx(1, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 0, 0, NUL) == 3
+
+
+def test_nvfp4_fp8_workspace_size():
+    L = dbs.lib()
+    L.gemm_nvfp4_fp8_workspace.restype = ctypes.c_size_t
+    L.gemm_nvfp4_fp8_workspace.argtypes = [ctypes.c_int64] * 3
+    a256 = lambda x: -(-x // 256) * 256
+    assert L.gemm_nvfp4_fp8_workspace(300, 200, 64) == a256(300 * 64) + a256(200 * 64) + a256(300 * 2) + a256(200 * 2)
+    assert L.gemm_nvfp4_fp8_workspace(300, 200, 48) == 0          # K % 32
+    assert L.gemm_nvfp4_fp8_workspace(0, 200, 64) == 0
+
+
+@pytest.mark.parametrize("K,ws,nbytes,lay,want", [
+    (48, FAKE, 1 << 30, (0, 0), 2),                       # K % 32 == 16: not implemented
+    (40, FAKE, 1 << 30, (0, 0), 1),                       # K % 16
+    (64, NUL, 1 << 30, (0, 0), 1),                        # no workspace
+    (64, ctypes.c_void_p((1 << 20) + 16), 1 << 30, (0, 0), 1),   # workspace not 256-byte aligned
+    (64, FAKE, 100, (0, 0), 1),                           # workspace too small
+    (64, FAKE, 1 << 30, (1, 0), 2),                       # MN-major
+])
+def test_nvfp4_fp8_validation(K, ws, nbytes, lay, want):
+    L = dbs.lib()
+    st = L.gemm_nvfp4_fp8(FAKE, FAKE, ctypes.c_float(1.0), FAKE, FAKE, ctypes.c_float(1.0), FAKE, 64, 64, K, *lay,
+                          ws, ctypes.c_size_t(nbytes), NUL)
+    assert st == want, dbs.status_str(st)
 
 
 def test_mx_null_scales():

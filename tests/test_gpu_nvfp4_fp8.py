@@ -1,0 +1,142 @@
+"""GPU checks of the opt-in FP8-rate NVFP4 GEMM (gemm_nvfp4_fp8) through the C
+ABI: its requantised operands bit for bit against the oracle's recipe, its
+result against the oracle GEMM of those operands (the usual parity bar), its
+distance from the exact NVFP4 result within the stated bound, and exactness
+at unit scales."""
+import numpy as np
+import pytest
+import torch
+
+import dense_block_scaled_amd as dbs
+import oracle
+import synth
+from tests import _gpu, _pins
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+
+
+def _a256(x):
+    return -(-x // 256) * 256
+
+
+def run_fast(w: dict):
+    """D and the workspace tensor after the call."""
+    d = _gpu.to_dev(w)
+    M, N, K = w["M"], w["N"], w["K"]
+    ws = torch.empty(dbs.nvfp4_fp8_workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+    D = dbs.gemm_nvfp4_fp8(d["A"], d["sA"], w["tA"], d["B"], d["sB"], w["tB"], workspace=ws)
+    return D, ws
+
+
+def _ws_parts(ws, M, N, K):
+    h = ws.cpu().numpy()
+    ob = _a256(M * K)
+    osa = ob + _a256(N * K)
+    osb = osa + _a256(M * K // 32)
+    return (h[:M * K].reshape(M, K), h[ob:ob + N * K].reshape(N, K),
+            h[osa:osa + M * K // 32].reshape(M, K // 32), h[osb:osb + N * K // 32].reshape(N, K // 32))
+
+
+def _fast_ref(w):
+    """Oracle D of the FP8-rate method and the norms of the r metric."""
+    wq = oracle.nvfp4_fp8_workload(w)
+    d, an, bn = oracle.gemm_full("mxfp8", wq)
+    alpha = float(np.float32(w["tA"]) * np.float32(w["tB"]))
+    return d * alpha, an * abs(w["tA"]), bn * abs(w["tB"])
+
+
+def _r(D, d_ref, an, bn):
+    return oracle.rel_errors(_gpu.d_to_numpy(D), d_ref, an, bn)
+
+
+# 256 x 64 tiles (the first two), 256 x 256 tiles (the rest)
+SHAPES = [(300, 520, 352), (256, 16384, 512), (3000, 2900, 352), (2944, 3008, 512)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_requant_and_gemm(shape):
+    M, N, K = shape
+    _gpu.say(f"[nvfp4-fp8] {shape}")
+    w = synth.workload("nvfp4", M, N, K, 900 + M % 31, 910 + N % 37)
+    D, ws = run_fast(w)
+    torch.cuda.synchronize()
+    a, b, sa, sb = _ws_parts(ws, M, N, K)
+    ra, rsa = oracle.requant_nvfp4_mx8(w["A"], w["sA"], K)
+    rb, rsb = oracle.requant_nvfp4_mx8(w["B"], w["sB"], K)
+    assert np.array_equal(sa, rsa) and np.array_equal(sb, rsb)
+    assert np.array_equal(a, ra) and np.array_equal(b, rb)
+    if M * N <= 1 << 23:
+        d_ref, an, bn = _fast_ref(w)
+        r = _r(D, d_ref, an, bn)
+        _gpu.say(f"  vs the FP8-rate oracle: max r={r.max():.3e}")
+        assert r.max() <= _gpu.tol_bound(K)
+        # distance from the exact NVFP4 product
+        de, ane, bne = oracle.gemm_full("nvfp4", w)
+        re = _r(D, de, ane, bne)
+        _gpu.say(f"  vs the exact NVFP4 oracle: max r={re.max():.3e} mean r={re.mean():.3e}")
+        assert re.max() <= 2.0 ** -3 + 2.0 ** -8 + _gpu.tol_bound(K)
+    else:
+        em, en = synth.sample_entries(73, M, N, 4096)
+        wq = oracle.nvfp4_fp8_workload(w)
+        d_ref, an, bn = oracle.gemm_entries("mxfp8", wq, em, en)
+        alpha = float(np.float32(w["tA"]) * np.float32(w["tB"]))
+        got = _gpu.d_to_numpy(D)[em, en]
+        r = oracle.rel_errors(got, d_ref * alpha, an * abs(w["tA"]), bn * abs(w["tB"]))
+        _gpu.say(f"  vs the FP8-rate oracle ({len(em)} sampled): max r={r.max():.3e}")
+        assert r.max() <= _gpu.tol_bound(K)
+
+
+def test_error_bound_on_random_codes():
+    """Codes and E4M3 scales over their whole ranges (the two groups of a
+    block far apart in scale): entry by entry, the distance from the exact
+    NVFP4 product stays within the stated bound.  Per element the
+    requantisation error is at most e = max(2^-4 |x|, 2^-10 2^E) (2^E: the
+    block's E8M0 scale), so a product's error is at most |a| e_b + |b| e_a +
+    e_a e_b; the GPU's fp32 sums and bf16 rounding come on top."""
+    _gpu.say("[nvfp4-fp8] error bound, random codes")
+    rng = np.random.default_rng(87)
+    M, N, K = 96, 80, 256
+    w = _pins.make_w("nvfp4", M, N, K, rng, scale_lo=0x08, scale_hi=0x7E)
+    D, _ = run_fast(w)
+    torch.cuda.synchronize()
+    de, _, _ = oracle.gemm_full("nvfp4", w, norms=False)
+    va, vb = _pins.ref_values("nvfp4", w, "A"), _pins.ref_values("nvfp4", w, "B")
+
+    def elem_bound(v, sc):
+        s = _pins.ref_e4m3(sc)
+        m = np.maximum(np.abs(s[:, 0::2]), np.abs(s[:, 1::2]))          # per 32-block
+        two_e = np.ldexp(1.0, np.frexp(m)[1] - 1)                        # 2^E
+        return np.maximum(2.0 ** -4 * np.abs(v), np.repeat(two_e, 32, axis=1) * 2.0 ** -10)
+
+    ea, eb = elem_bound(va, w["sA"]), elem_bound(vb, w["sB"])
+    alpha = abs(w["tA"] * w["tB"])
+    bound = alpha * (ea @ np.abs(vb).T + np.abs(va) @ eb.T + ea @ eb.T)
+    got = _gpu.d_to_numpy(D)
+    gpu_own = 2.0 ** -8 * np.abs(got) + alpha * K * 2.0 ** -22 * ((np.abs(va) + ea) @ (np.abs(vb) + eb).T)
+    worst = float(np.max(np.abs(got - de) / (bound + gpu_own)))
+    _gpu.say(f"  largest error / bound: {worst:.3f}")
+    assert worst <= 1.0
+
+
+def test_exact_at_unit_scales():
+    """Unit E4M3 scales: requantisation is lossless and A times a permutation
+    matrix comes out bit for bit equal to the exact NVFP4 product."""
+    _gpu.say("[nvfp4-fp8] exact at unit scales")
+    rng = np.random.default_rng(88)
+    M, K = 300, 512
+    N = K
+    a = _pins.random_codes("nvfp4", M, K, rng)
+    codes = np.zeros((N, K), np.uint8)
+    codes[np.arange(N), rng.permutation(K)] = 0x2
+    w = {"fmt": "nvfp4", "M": M, "N": N, "K": K, "A": a["X"], "sA": np.full((M, K // 16), 0x38, np.uint8),
+         "B": (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8), "sB": np.full((N, K // 16), 0x38, np.uint8),
+         "tA": 2.0, "tB": 0.25}
+    D, _ = run_fast(w)
+    torch.cuda.synchronize()
+    _gpu.check_exact("nvfp4", w, D)
