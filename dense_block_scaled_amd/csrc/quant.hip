@@ -225,8 +225,9 @@ __global__ __launch_bounds__(256) void quant_nvfp4_kernel(const float *__restric
 // packed bytes), picks E = floor(log2(max |s_g|)) (0 for two zero scales)
 // and writes the 32 nearest E4M3 codes of a * s_g * 2^-E (ties to even) and
 // the E8M0 code E + 127.  a * s_g * 2^-E has at most 6 significant bits, so
-// it is exact in fp32 and the rounding is the only inexact step.  Inputs
-// must be finite.
+// it is exact in fp32 and the rounding is the only inexact step (checked bit
+// for bit against the oracle's recipe over every pair of positive E4M3 group
+// scales and every E2M1 code).  Inputs must be finite.
 __device__ __forceinline__ float dec_e4m3(uint32_t c)
 {
     const float v = dec_e4m3_pos(c & 0x7F);
@@ -253,23 +254,28 @@ __global__ __launch_bounds__(256) void requant_nvfp4_mx8_kernel(const uint8_t *_
         const float f0 = __builtin_ldexpf(s0, -E), f1 = __builtin_ldexpf(s1, -E);
         const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
         uint32_t o[8];
-        // byte j of an input dword holds two elements (low nibble first);
-        // the conversion decodes them exactly (unit scale)
-        auto pair = [](uint32_t w, float f, int j) -> uint32_t {
-            f32x2 v;
+        // byte j of an input dword holds two elements (low nibble first),
+        // decoded exactly (unit scale); the products go to E4M3 through the
+        // hardware conversion, which rounds to nearest even (the default
+        // mode) and never sees a magnitude near E4M3's maximum here
+        auto elems = [](uint32_t w, int j) -> f32x2 {
             switch (j) {
-            case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
-            case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
-            case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
-            default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
+            case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+            case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+            case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+            default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
             }
-            return enc_e4m3(v[0] * f) | (enc_e4m3(v[1] * f) << 8);
+        };
+        auto four = [&](uint32_t w, float f, int j) -> uint32_t {   // bytes j, j+1 -> 4 codes
+            const f32x2 lo = elems(w, j), hi = elems(w, j + 1);
+            const int r = __builtin_amdgcn_cvt_pk_fp8_f32(lo[0] * f, lo[1] * f, 0, false);
+            return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(hi[0] * f, hi[1] * f, r, true);
         };
 #pragma unroll
         for (int d = 0; d < 4; ++d) {             // dword d: elements 8d .. 8d+7, group d / 2
             const float f = d < 2 ? f0 : f1;
-            o[2 * d] = pair(cw[d], f, 0) | (pair(cw[d], f, 1) << 16);
-            o[2 * d + 1] = pair(cw[d], f, 2) | (pair(cw[d], f, 3) << 16);
+            o[2 * d] = four(cw[d], f, 0);
+            o[2 * d + 1] = four(cw[d], f, 2);
         }
         *reinterpret_cast<uint4 *>(out + 32 * b) = uint4{o[0], o[1], o[2], o[3]};
         *reinterpret_cast<uint4 *>(out + 32 * b + 16) = uint4{o[4], o[5], o[6], o[7]};

@@ -140,3 +140,27 @@ def test_exact_at_unit_scales():
     D, _ = run_fast(w)
     torch.cuda.synchronize()
     _gpu.check_exact("nvfp4", w, D)
+
+
+def test_requant_every_scale_pair_and_code():
+    """One block per row for every pair of non-negative finite E4M3 group
+    scales (codes 0x00 .. 0x7E each), each group holding all 16 E2M1 codes:
+    the requantised codes and E8M0 scales bit for bit against the oracle."""
+    _gpu.say("[nvfp4-fp8] requantisation over every scale pair")
+    s = np.arange(0x7F, dtype=np.uint8)
+    s0, s1 = np.meshgrid(s, s, indexing="ij")
+    M, K, N = s0.size, 32, 32
+    codes = np.tile(np.arange(16, dtype=np.uint8), 2)                  # group 0 and group 1: codes 0..15
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    rng = np.random.default_rng(89)
+    b = _pins.random_codes("nvfp4", N, K, rng)
+    w = {"fmt": "nvfp4", "M": M, "N": N, "K": K, "A": np.tile(packed, (M, 1)),
+         "sA": np.stack([s0.ravel(), s1.ravel()], axis=1).astype(np.uint8),
+         "B": b["X"], "sB": np.full((N, K // 16), 0x38, np.uint8), "tA": 1.0, "tB": 1.0}
+    D, ws = run_fast(w)
+    torch.cuda.synchronize()
+    a, _, sa, _ = _ws_parts(ws, M, N, K)
+    ra, rsa = oracle.requant_nvfp4_mx8(w["A"], w["sA"], K)
+    assert np.array_equal(sa, rsa)
+    bad = np.argwhere(a != ra)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}: {a[tuple(bad[0])]:#x} vs {ra[tuple(bad[0])]:#x}"
