@@ -8,8 +8,9 @@ package never imports the product.
 The arithmetic lives in ``oracle.c`` (built into ``liboracle.so`` by
 ``oracle/build.py``); this module only marshals numpy arrays.  Kinds:
 0 = BF16, 1 = MXFP8, 2 = MXFP4, 3 = NVFP4, 4 = MX with E5M2 elements.  For
-fmt 'mxfp8' a workload may name each operand's 8-bit element format in
-w['elemA'] / w['elemB'] ('e4m3', the default, or 'e5m2').
+fmt 'mxfp8' a workload may name each operand's MX element format in
+w['elemA'] / w['elemB'] ('e4m3', the default, 'e5m2', or 'e2m1' packed two
+per byte).
 """
 from __future__ import annotations
 
@@ -121,7 +122,7 @@ def unpack_fp4(packed: np.ndarray) -> np.ndarray:
 
 # ---- GEMM ----------------------------------------------------------------
 
-_MX8 = {"e4m3": 1, "e5m2": 4}
+_MX8 = {"e4m3": 1, "e5m2": 4, "e2m1": 2}
 
 
 def _operands(fmt, w):

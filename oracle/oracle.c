@@ -301,13 +301,14 @@ static void *entries_worker(void *p)
     return NULL;
 }
 
-/* Operand kinds a GEMM may pair: equal kinds, or two MX 8-bit element
- * formats (E4M3, E5M2) with E8M0 scales. */
+/* Operand kinds a GEMM may pair: equal kinds, or any two MX kinds (E4M3,
+ * E5M2 or E2M1 elements, all with E8M0 scales per 32). */
+static int is_mx(int k) { return k == ORC_MXFP8 || k == ORC_MXE5M2 || k == ORC_MXFP4; }
+
 static int kinds_ok(int ka, int kb)
 {
     if (ka < 0 || ka > 4 || kb < 0 || kb > 4) return 0;
-    if (ka == kb) return 1;
-    return (ka == ORC_MXFP8 || ka == ORC_MXE5M2) && (kb == ORC_MXFP8 || kb == ORC_MXE5M2);
+    return ka == kb || (is_mx(ka) && is_mx(kb));
 }
 
 /*

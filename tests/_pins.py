@@ -72,7 +72,7 @@ def ref_values(fmt, w, which):
     K = w["K"]
     if fmt == "bf16":
         return ref_bf16(X)
-    if fmt == "mxfp8":
+    if fmt == "mxfp8" and w.get("elem" + which, "e4m3") != "e2m1":
         el = ref_e5m2(X) if w.get("elem" + which, "e4m3") == "e5m2" else ref_e4m3(X)
         sc = ref_e8m0(w["s" + which])
         return el * np.repeat(sc, 32, axis=1)
@@ -80,7 +80,7 @@ def ref_values(fmt, w, which):
     codes[:, 0::2] = X & 0xF
     codes[:, 1::2] = X >> 4
     el = ref_e2m1(codes)
-    if fmt == "mxfp4":
+    if fmt in ("mxfp4", "mxfp8"):          # E2M1 elements of an MX operand
         return el * np.repeat(ref_e8m0(w["s" + which]), 32, axis=1)
     return el * np.repeat(ref_e4m3(w["s" + which]), 16, axis=1)
 
@@ -125,6 +125,8 @@ def make_w_mx8(elem_a, elem_b, M, N, K, rng, scale_lo=0, scale_hi=254, narrow=Fa
     for X, rows, el in (("A", M, elem_a), ("B", N, elem_b)):
         if el == "e5m2":
             w[X] = random_e5m2(rows, K, rng, (10, 21) if narrow else (0, 31))
+        elif el == "e2m1":
+            w[X] = random_codes("mxfp4", rows, K, rng)["X"]
         else:
             w[X] = random_codes("mxfp8", rows, K, rng)["X"]
         w["s" + X] = rng.integers(scale_lo, scale_hi + 1, (rows, K // 32)).astype(np.uint8)
@@ -385,7 +387,7 @@ def battery():
         res[f"{fmt}_pow2"] = check_pow2_scale_shift(fmt)
         res[f"{fmt}_unit_matmul"] = check_unit_scale_matmul(fmt)
         res[f"{fmt}_transpose"] = check_transpose_symmetry(fmt)
-    for ea, eb in (("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")):
+    for ea, eb in (("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e4m3", "e2m1"), ("e2m1", "e5m2")):
         res[f"mx8_{ea}x{eb}_fraction"] = check_mixed_fraction(ea, eb)
         res[f"mx8_{ea}x{eb}_fraction_exact"] = check_mixed_fraction(ea, eb, seed=21, exact_scales=True)
     return res
