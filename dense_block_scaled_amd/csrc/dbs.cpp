@@ -94,7 +94,7 @@ struct Groups {
 dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB, void *D, int64_t M,
                int64_t N, int64_t K, float alpha, int elem_bits, int block, hipStream_t stream,
                const Groups *groups = nullptr, dbs_layout la = DBS_K_MAJOR, dbs_layout lb = DBS_K_MAJOR,
-               int ec = 0)
+               int ec = 0, int cv = 0)
 {
     int cus = 0;
     dbs_status st = device_cus(&cus);
@@ -115,6 +115,8 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     p.ldam = (int)(M * elem_bits / 8);
     p.ldbm = (int)(N * elem_bits / 8);
     p.ec = ec;
+    p.cv = cv;
+    p.ldc = (int)(K / 2);
     // square tiles unless they would fill at most half of the CUs
     auto tiles_of = [&](int64_t rows, int64_t tm_, int64_t tn_) { return ((rows + tm_ - 1) / tm_) * ((N + tn_ - 1) / tn_); };
     int64_t sq_tiles = 0;
@@ -211,15 +213,17 @@ dbs_status gemm_mx_mixed(dbs_mx_elem elem_a, dbs_mx_elem elem_b, const void *A, 
     dbs_status st = check_common(A, B, D, M, N, K, la, lb, int64_t(1) << 22);
     if (st != DBS_OK) return st;
     if (K % 32) return fail(DBS_EINVAL, "mx: K must be a multiple of 32");
-    if ((elem_a == DBS_E2M1) != (elem_b == DBS_E2M1))
-        return fail(DBS_EUNSUPPORTED, "mx: an 8-bit operand with an E2M1 operand is not implemented");
-    const int ec = elem_a == DBS_E2M1 ? 0 : mx8_code(elem_a) | (mx8_code(elem_b) << 3);
-    if (ec != 0 && (la != DBS_K_MAJOR || lb != DBS_K_MAJOR))
-        return fail(DBS_EUNSUPPORTED, "mx: E5M2 operands are K-major only");
-    const int bits = elem_a == DBS_E2M1 ? 4 : 8;
+    // an E2M1 operand beside an 8-bit one is widened to E4M3 inside the
+    // 8-bit kernel (exact: every E2M1 value is an E4M3 value)
+    const bool fp4_a = elem_a == DBS_E2M1, fp4_b = elem_b == DBS_E2M1;
+    const int cv = fp4_a != fp4_b ? (fp4_a ? 1 : 2) : 0;
+    const int ec = fp4_a && fp4_b ? 0 : (fp4_a ? 0 : mx8_code(elem_a)) | ((fp4_b ? 0 : mx8_code(elem_b)) << 3);
+    if ((ec != 0 || cv != 0) && (la != DBS_K_MAJOR || lb != DBS_K_MAJOR))
+        return fail(DBS_EUNSUPPORTED, "mx: E5M2 operands and 8-bit x E2M1 pairs are K-major only");
+    const int bits = fp4_a && fp4_b ? 4 : 8;
     if ((st = check_mn(la, lb, M, N, K, bits)) != DBS_OK) return st;
     return run(bits == 8 ? dbs::kMXFP8 : dbs::kMXFP4, A, sA, B, sB, D, M, N, K, 1.0f, bits, 32, stream, nullptr,
-               la, lb, ec);
+               la, lb, ec, cv);
 }
 
 dbs_status gemm_mx(dbs_mx_elem elem, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB, void *D,

@@ -162,13 +162,16 @@ __device__ __forceinline__ TileRef tile_ref(int tile, const Params &p)
 // one, arranged as the stage's K-rows (see Mn below).  EC: the 8-bit MX
 // element formats as gfx950's f8f6f4 MFMA codes, A in bits 0..2 and B in
 // bits 3..5 (0 = E4M3, 1 = E5M2); both formats take the same bytes and
-// fragments, only the MFMA's format fields differ.
+// fragments, only the MFMA's format fields differ.  CV (8-bit MX kernels):
+// bit 0 set if A arrives as E2M1, bit 1 if B does; such an operand is
+// widened to E4M3 on its way into LDS (see load_cv), so the MFMAs see E4M3.
 constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
 
-template <int TM_, int TN_, int WM_, int WN_, int NS_ = 2, int LAY_ = 0, int EC_ = 0>
+template <int TM_, int TN_, int WM_, int WN_, int NS_ = 2, int LAY_ = 0, int EC_ = 0, int CV_ = 0>
 struct Shape {
-    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_, NS = NS_, LAY = LAY_, EC = EC_;
+    static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_, NS = NS_, LAY = LAY_, EC = EC_, CV = CV_;
     static constexpr bool AMN = (LAY & 1) != 0, BMN = (LAY & 2) != 0;
+    static constexpr bool ACV = (CV & 1) != 0, BCV = (CV & 2) != 0;
     static constexpr int CA = EC & 7, CB = (EC >> 3) & 7;
     static constexpr int NW = WM * WN;
     static constexpr int kThreads = 64 * NW;
@@ -198,9 +201,10 @@ using SkinnyDeep = Shape<kSkinnyTM, kSkinnyTN, 8, 1, 3>;
 // this variant runs one wave per SIMD, each owning 128 x 128.
 using SquareW4 = Shape<kSquareTM, kSquareTN, 2, 2>;
 
-// Shape S with operand layouts LAY and 8-bit MX element codes EC.
-template <class S, int LAY, int EC = S::EC>
-using WithLayout = Shape<S::TM, S::TN, S::WM, S::WN, S::NS, LAY, EC>;
+// Shape S with operand layouts LAY, 8-bit MX element codes EC and widened
+// E2M1 operands CV.
+template <class S, int LAY, int EC = S::EC, int CV = S::CV>
+using WithLayout = Shape<S::TM, S::TN, S::WM, S::WN, S::NS, LAY, EC, CV>;
 
 // ------------------------------------------------------------ format traits
 
@@ -889,6 +893,91 @@ __device__ __forceinline__ void decode_fp4_a(f16x8 (&a)[S::MB][4], const Fp4A<S>
     }
 }
 
+// ------------------------------------------- E2M1 operands of 8-bit GEMMs
+
+// An E2M1 operand paired with an E4M3 / E5M2 one: a 128-element stage row is
+// 64 packed bytes, i.e. four 16-byte pieces; the concatenated piece list (the
+// widened operands' rows, A's first) is split over the threads, thread t
+// taking pieces t, t + threads, ...  Each piece (32 elements, one E8M0
+// block) is loaded into registers and written to LDS as the 32 E4M3 codes
+// of the same values -- every E2M1 value is an E4M3 value, so the widening
+// is exact and the MX scales stay as they are -- into logical chunks 2p and
+// 2p + 1 of its row of the E4M3 slot.
+template <class S>
+constexpr int cv_rows() { return (S::ACV ? S::TM : 0) + (S::BCV ? S::TN : 0); }
+
+template <class S>
+constexpr int cv_units() { return (4 * cv_rows<S>() + S::kThreads - 1) / S::kThreads; }
+
+// first unit of phase group g of a stage with KK phases
+template <class S, int KK>
+constexpr int cv_group(int g) { return g >= KK ? cv_units<S>() : g * ((cv_units<S>() + KK - 1) / KK) < cv_units<S>() ? g * ((cv_units<S>() + KK - 1) / KK) : cv_units<S>(); }
+
+template <class S>
+struct CvRegs {
+    i32x4 v[cv_units<S>() > 0 ? cv_units<S>() : 1];
+};
+
+// Units K0 .. K1-1 of the thread's pieces (a stage's pieces go in groups, one
+// per k-step phase: loaded at the start of a phase, written to LDS at the
+// start of the next, so only a group's registers are live at a time).
+template <class S, int K0, int K1>
+__device__ __forceinline__ void load_cv(CvRegs<S> &r, const Target &tg, int ks, const Ctx<S> &c, int ldc)
+{
+    constexpr int TA = S::ACV ? S::TM : 0;   // A rows in the list
+#pragma unroll
+    for (int k = K0; k < K1; ++k) {
+        const int u0 = c.w * 64 + k * S::kThreads;   // wave-uniform: 4 TM is a multiple of 64
+        if (u0 < 4 * cv_rows<S>()) {
+            const bool is_a = u0 < 4 * TA;
+            const int pu = u0 + c.lane - (is_a ? 0 : 4 * TA);
+            const int row = pu >> 2, piece = pu & 3;
+            // rows are K/2 bytes, K % 32 == 0: a piece is all in or all out
+            const uint32_t pad = ks * 64 + piece * 16 < ldc ? 0u : kOOB;
+            r.v[k] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? tg.ra : tg.rb, (uint32_t)(row * ldc + piece * 16) | pad,
+                                                           (uint32_t)(ks * 64), 0);
+        }
+    }
+}
+
+// 8 E2M1 codes (one dword, low nibble first) -> their 8 E4M3 codes: exact
+// decode, then the hardware's E4M3 encoding of an E4M3 value (no rounding).
+__device__ __forceinline__ u32x2 widen8(uint32_t w)
+{
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p0[0], p0[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(p1[0], p1[1], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p2[0], p2[1], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(p3[0], p3[1], hi, true);
+    return u32x2{(uint32_t)lo, (uint32_t)hi};
+}
+
+template <class S, int K0, int K1>
+__device__ __forceinline__ void store_cv(const CvRegs<S> &r, uint8_t *lds, int slot, const Ctx<S> &c)
+{
+    constexpr int TA = S::ACV ? S::TM : 0;
+#pragma unroll
+    for (int k = K0; k < K1; ++k) {
+        const int u0 = c.w * 64 + k * S::kThreads;   // wave-uniform
+        if (u0 < 4 * cv_rows<S>()) {
+            const bool is_a = u0 < 4 * TA;
+            const int pu = u0 + c.lane - (is_a ? 0 : 4 * TA);
+            const int row = pu >> 2, piece = pu & 3;
+            uint8_t *base = lds + (is_a ? S::kLdsA + slot * S::kSlotA : S::kLdsB + slot * S::kSlotB);
+            const u32x2 e0 = widen8((uint32_t)r.v[k][0]), e1 = widen8((uint32_t)r.v[k][1]);
+            const u32x2 e2 = widen8((uint32_t)r.v[k][2]), e3 = widen8((uint32_t)r.v[k][3]);
+            *reinterpret_cast<i32x4 *>(base + lds_off(row, 2 * piece)) =
+                i32x4{(int)e0[0], (int)e0[1], (int)e1[0], (int)e1[1]};
+            *reinterpret_cast<i32x4 *>(base + lds_off(row, 2 * piece + 1)) =
+                i32x4{(int)e2[0], (int)e2[1], (int)e3[0], (int)e3[1]};
+        }
+    }
+}
+
 // --------------------------------------------------------------- epilogue
 
 // acc[i][j] holds, for output row m = wm*TM/WM + 32 i + lane%32, the columns
@@ -1052,6 +1141,7 @@ struct Pipe {
     f16x8 acur[S::MB][4];                    // adirect: this stage's A fragments per k-step
     f16x8 aprev[S::MB];                      // adirect: the previous stage's last k-step
     ScaleBytes<FMT, S> sbytes;
+    CvRegs<S> cv;                            // widened E2M1 operands: the next stage's packed pieces
 };
 
 // Load pieces of a stage.  Direct-to-LDS formats: piece q issues wave-load q
@@ -1076,7 +1166,7 @@ __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int sl
         load_fp4<SM>(P.fp4, tg, ks, c, p.lda, p.sld);
         if constexpr (adirect<FMT, S>()) load_fp4_a<SM>(P.fp4a, tg, ks, c, p.lda, p.sld);
     } else {
-        if (q < S::QA) {
+        if (q < S::QA && !S::ACV) {
             if constexpr (S::AMN) {
                 static_assert(Mn<FMT, S::TM>::RPL % Mn<FMT, S::TM>::PERIOD == 0 || S::QA % 2 == 0, "parity");
                 dma_mn<FMT, S::TM>(lds, S::kLdsA + slot * S::kSlotA, tg.ra, ks, c.ma, c.w * S::QA + q, q, p.ldam);
@@ -1084,7 +1174,7 @@ __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int sl
                 dma_a(lds, slot, tg, ks, c, q, p.lda);
             }
         }
-        if (q < S::QB) {
+        if (q < S::QB && !S::BCV) {
             if constexpr (S::BMN) {
                 static_assert(Mn<FMT, S::TN>::RPL % Mn<FMT, S::TN>::PERIOD == 0 || S::QB % 2 == 0, "parity");
                 dma_mn<FMT, S::TN>(lds, S::kLdsB + slot * S::kSlotB, tg.rb, ks, c.mb, c.w * S::QB + q, q, p.ldbm);
@@ -1107,7 +1197,7 @@ __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int sl
 
 // Register-staged parts of a stage (NVFP4 data, unaligned MX scales) go to
 // LDS before the stage's barrier.
-template <int FMT, class S, int SM>
+template <int FMT, class S, int SM, bool ALL = false>
 __device__ __forceinline__ void commit_stage(Pipe<FMT, S> &P, uint8_t *lds, int slot, const Ctx<S> &c)
 {
     if constexpr (FMT == kNVFP4) store_fp4(P.fp4, lds, slot, c);
@@ -1119,6 +1209,11 @@ __device__ __forceinline__ void commit_stage(Pipe<FMT, S> &P, uint8_t *lds, int 
         decode_fp4_a<S>(P.acur, P.fp4a);
     }
     if constexpr ((FMT == kMXFP8 || FMT == kMXFP4) && SM == kScalesRegs) store_scale_bytes(P.sbytes, lds, slot, c);
+    if constexpr (S::ACV || S::BCV) {
+        // the last phase group (ALL: every group, loaded together in the prologue)
+        constexpr int KK = kk_of<FMT, S>();
+        store_cv<S, ALL ? 0 : cv_group<S, KK>(KK - 1), cv_units<S>()>(P.cv, lds, slot, c);
+    }
 }
 
 // Phase PH of a stage (PH = 0 .. KK-1): the MB x NB MFMAs of one k-step —
@@ -1168,6 +1263,12 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
         }
     }
     if constexpr (Fmt<FMT>::BPS > 0 && PH == 1) adjust_scales<FMT>(P.scur, c);
+    if constexpr ((S::ACV || S::BCV) && LOADS) {
+        // widened E2M1 pieces: the previous group to LDS, this phase's group from memory
+        constexpr int KK = kk_of<FMT, S>();
+        if constexpr (PH > 0) store_cv<S, cv_group<S, KK>(PH - 1), cv_group<S, KK>(PH)>(P.cv, lds, lslot, c);
+        load_cv<S, cv_group<S, KK>(PH), cv_group<S, KK>(PH + 1)>(P.cv, tg, ks, c, p.ldc);
+    }
     DBS_FENCE();
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
@@ -1218,7 +1319,9 @@ __device__ __forceinline__ void stage(Pipe<FMT, S> &P, f32x16 (&acc)[S::MB][S::N
                                       const ChunkPos &cp)
 {
     constexpr int KK = kk_of<FMT, S>();
-    static_assert(S::NS == 2 || (FMT != kNVFP4 && SM != kScalesRegs), "deeper rings need direct-to-LDS stages");
+    static_assert(S::NS == 2 || (FMT != kNVFP4 && SM != kScalesRegs && !S::ACV && !S::BCV),
+                  "deeper rings need direct-to-LDS stages");
+    static_assert(!(S::ACV || S::BCV) || (FMT == kMXFP8 && S::LAY == 0), "widened E2M1: 8-bit MX, K-major");
     static_assert(SM != kScalesChunk || S::NS == 2, "chunked scales run on two-slot rings");
     static_assert(KK == 2 || KK == 4, "stages hold 2 or 4 k-steps");
     opaque(c);
@@ -1250,6 +1353,8 @@ __device__ __forceinline__ Target tile_target(const Params &p, int tile)
         constexpr int EB = Mn<FMT, S::TM>::EB;
         const int64_t c0 = (int64_t)r.m0 * EB / 8;
         t.ra = make_rsrc(p.A + c0, (uint32_t)((int64_t)p.K * p.ldam - c0));
+    } else if constexpr (S::ACV) {
+        t.ra = make_rsrc(p.A + (int64_t)r.m0 * p.ldc, (uint32_t)(rows_a * p.ldc));
     } else {
         t.ra = make_rsrc(p.A + (int64_t)r.m0 * p.lda, (uint32_t)(rows_a * p.lda));
     }
@@ -1257,6 +1362,8 @@ __device__ __forceinline__ Target tile_target(const Params &p, int tile)
         constexpr int EB = Mn<FMT, S::TN>::EB;
         const int64_t c0 = (int64_t)r.n0 * EB / 8;
         t.rb = make_rsrc(p.B + c0, (uint32_t)((int64_t)p.K * p.ldbm - c0));
+    } else if constexpr (S::BCV) {
+        t.rb = make_rsrc(p.B + r.boff + (int64_t)r.n0 * p.ldc, (uint32_t)(rows_b * p.ldc));
     } else {
         t.rb = make_rsrc(p.B + r.boff + (int64_t)r.n0 * p.lda, (uint32_t)(rows_b * p.lda));
     }
@@ -1346,7 +1453,8 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
     for (int f = 0; f < S::NS - 1; ++f) {
 #pragma unroll
         for (int q = 0; q < npieces<FMT, S>(); ++q) load_piece<FMT, S, SM>(P, lds, f, ld, f, p, c, q, stg, cp);
-        commit_stage<FMT, S, SM>(P, lds, f, c);
+        if constexpr (S::ACV || S::BCV) load_cv<S, 0, cv_units<S>()>(P.cv, ld, f, c, p.ldc);
+        commit_stage<FMT, S, SM, true>(P, lds, f, c);
     }
     if constexpr (SM == kScalesChunk) {
 #pragma unroll
@@ -1707,6 +1815,7 @@ hipError_t launch_one(const Params &p0, int grid, hipStream_t stream)
         hipLaunchKernelGGL((gemm_kernel<FMT, S0, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p);
     } else {
         if constexpr (FMT == kMXFP8) {
+            if (p.cv != 0) return hipErrorInvalidValue;    // launch_cv's
             if (p.ec != 0) {
                 // E5M2 on either side: K-major operands only (the host checks)
                 if (p.lay != 0) return hipErrorInvalidValue;
@@ -1733,9 +1842,41 @@ hipError_t launch_one(const Params &p0, int grid, hipStream_t stream)
 template <int FMT, class S>
 constexpr int stages_of(int K) { return (K + stage_elems<FMT, S>() - 1) / stage_elems<FMT, S>(); }
 
+// 8-bit MX GEMMs with a widened E2M1 operand (K-major): its register-staged
+// pieces do not fit beside the 8-wave square kernel's fragments (the
+// compiler spills 160+ registers there), so square problems run on the
+// one-wave-per-SIMD tiles; scale rows take the register-staged path there and
+// on unaligned skinny problems.
+template <int SM, class S0>
+hipError_t launch_cv(const Params &p0, int grid, hipStream_t stream)
+{
+    static_assert(S0::NS == 2, "register-staged operands use two-slot rings");
+    Params p = p0;
+    p.nk = (p.K + stage_elems<kMXFP8, S0>() - 1) / stage_elems<kMXFP8, S0>();
+    if (p.lay != 0) return hipErrorInvalidValue;
+    switch (p.cv * 16 + p.ec) {
+    case 16 + 0: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 0, 1>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+    case 16 + 8: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 8, 1>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+    case 32 + 0: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 0, 2>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+    case 32 + 1: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 1, 2>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <int FMT, class S>
 hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
 {
+    if constexpr (FMT == kMXFP8) {
+        if (p.cv != 0) {
+            if constexpr (std::is_same<S, Square>::value) {
+                return launch_cv<kScalesRegs, SquareW4>(p, grid, stream);
+            } else {
+                if (p.scales_aligned) return launch_cv<kScalesStage, S>(p, grid, stream);
+                return launch_cv<kScalesRegs, S>(p, grid, stream);
+            }
+        }
+    }
     if constexpr (FMT == kMXFP8 || FMT == kMXFP4) {
         if (!p.scales_aligned) {
             using U = typename std::conditional<std::is_same<S, Square>::value, SquareW4, S>::type;
@@ -1761,7 +1902,7 @@ hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
     // stages that arrive entirely by direct-to-LDS loads get a deeper ring
     // when every tile has enough stages to fill it
     if constexpr (std::is_same<S, Skinny>::value && FMT != kNVFP4) {
-        if (stages_of<FMT, SkinnyDeep>(p.K) >= SkinnyDeep::NS - 1)
+        if (p.cv == 0 && stages_of<FMT, SkinnyDeep>(p.K) >= SkinnyDeep::NS - 1)
             return launch_one<FMT, kScalesStage, SkinnyDeep>(p, grid, stream);
     }
     // MX scales in chunks when a tile's stages split into whole chunks (and

@@ -31,6 +31,8 @@ struct Params {
     int lay;              // bit 0: A stored MN-major (K x M), bit 1: B stored MN-major (K x N)
     int ldam, ldbm;       // MN-major A / B: bytes per K-row (M or N elements)
     int ec;               // 8-bit MX element codes: A in bits 0..2, B in 3..5 (0 = E4M3, 1 = E5M2)
+    int cv;               // 8-bit MX GEMM with E2M1 operands: bit 0 A, bit 1 B (widened to E4M3)
+    int ldc;              // bytes per row of such an E2M1 operand (K / 2)
     float alpha;          // applied to the fp32 accumulator before rounding
     // Grouped GEMM (ngroups > 0): group g owns rows goff[g] .. goff[g+1]-1 of A
     // and D, the g-th N x K block of B (and of sB) and output tiles

@@ -110,10 +110,13 @@ dbs_status gemm_mx(dbs_mx_elem elem,
 /*
  * MX GEMM with an element format per operand: A's elements in elem_a, B's in
  * elem_b, otherwise as gemm_mx (gemm_mx(e, ...) is gemm_mx_mixed(e, e, ...)).
- * Pairs taken: any of E4M3 / E5M2 with any of E4M3 / E5M2, and E2M1 with
- * E2M1; an 8-bit operand with an E2M1 one returns DBS_EUNSUPPORTED.  gfx950's
- * scaled MFMA takes a format code per operand, so each pair runs at the
- * 8-bit rate with the bytes and scales of MXFP8.
+ * Every pairing of E4M3, E5M2 and E2M1 is taken.  gfx950's scaled MFMA
+ * takes a format code per operand, so 8-bit pairs run at the 8-bit rate on
+ * MXFP8's staging; an E2M1 operand beside an 8-bit one (FP8 x FP4) is widened
+ * to E4M3 on its way into LDS -- exactly, every E2M1 value being an E4M3
+ * value, with its E8M0 scales unchanged -- and multiplied at the 8-bit rate.
+ * Pairs other than E4M3 x E4M3 and E2M1 x E2M1 take K-major operands only
+ * (DBS_EUNSUPPORTED for MN-major).
  */
 dbs_status gemm_mx_mixed(dbs_mx_elem elem_a, dbs_mx_elem elem_b,
                          const void *A, const uint8_t *sA,

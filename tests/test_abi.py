@@ -68,8 +68,8 @@ def test_mx_validation(elem, K, want):
 
 
 @pytest.mark.parametrize("ea,eb,lay,want", [
-    (0, 4, (0, 0), 2),          # E4M3 x E2M1: not implemented
-    (4, 1, (0, 0), 2),          # E2M1 x E5M2
+    (0, 4, (1, 0), 2),          # E4M3 x E2M1 MN-major: not implemented
+    (4, 1, (0, 1), 2),          # E2M1 x E5M2 MN-major
     (1, 1, (1, 0), 2),          # E5M2 MN-major
     (0, 1, (0, 1), 2),
     (2, 0, (0, 0), 1),          # unknown element code
@@ -82,7 +82,7 @@ def test_mx_mixed_validation(ea, eb, lay, want):
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would reach a real device")
-@pytest.mark.parametrize("ea,eb", [(0, 1), (1, 0), (1, 1), (4, 4)])
+@pytest.mark.parametrize("ea,eb", [(0, 1), (1, 0), (1, 1), (4, 4), (0, 4), (4, 0), (1, 4), (4, 1)])
 def test_mx_mixed_valid_pairs_pass_validation(ea, eb):
     L = dbs.lib()
     assert L.gemm_mx_mixed(ea, eb, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, 0, 0, NUL) == 3

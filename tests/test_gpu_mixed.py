@@ -1,6 +1,6 @@
-"""GPU parity of the 8-bit MX element formats per operand (E4M3 / E5M2 in any
-pairing, gemm_mx_mixed and gemm_mx('e5m2')) through the C ABI, against the
-oracle's per-operand decoding."""
+"""GPU parity of the MX element formats per operand (E4M3 / E5M2 in any
+pairing, and either with E2M1: gemm_mx_mixed, gemm_mx('e5m2')) through the C
+ABI, against the oracle's per-operand decoding."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +11,8 @@ from tests import _gpu, _pins
 
 pytestmark = pytest.mark.gpu
 
-PAIRS = [("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")]
+PAIRS = [("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3"),
+         ("e4m3", "e2m1"), ("e2m1", "e4m3"), ("e5m2", "e2m1"), ("e2m1", "e5m2")]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -77,7 +78,9 @@ def test_mixed_exact_permutation(pair, mk):
     w = _pins.make_w_mx8(ea, eb, M, N, K, rng, scale_lo=110, scale_hi=140)
     pi = rng.permutation(K)
     B = np.zeros((N, K), np.uint8)
-    B[np.arange(N), pi] = 0x3C if eb == "e5m2" else 0x38          # 1.0
+    B[np.arange(N), pi] = {"e5m2": 0x3C, "e4m3": 0x38, "e2m1": 0x2}[eb]   # 1.0
+    if eb == "e2m1":
+        B = (B[:, 0::2] | (B[:, 1::2] << 4)).astype(np.uint8)
     w["B"] = B
     w["sB"] = rng.integers(118, 137, (N, K // 32)).astype(np.uint8)
     D = run_mixed(w)
