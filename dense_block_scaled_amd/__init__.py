@@ -189,18 +189,20 @@ def gemm_mx_mixed(elem_a: str, elem_b: str, A: torch.Tensor, sA: torch.Tensor, B
 
 
 def gemm_nvfp4(A: torch.Tensor, sA: torch.Tensor, tA: float, B: torch.Tensor, sB: torch.Tensor, tB: float,
-               out: torch.Tensor | None = None) -> torch.Tensor:
-    """NVFP4 GEMM: packed E2M1 with E4M3 scales per 16 and fp32 tensor scales."""
-    M, N = A.shape[0], B.shape[0]
-    K = A.shape[1] * 2
+               out: torch.Tensor | None = None, la: int = K_MAJOR, lb: int = K_MAJOR) -> torch.Tensor:
+    """NVFP4 GEMM: packed E2M1 with E4M3 scales per 16 and fp32 tensor scales
+    (MN-major operands: (K, M / 2), (K, N / 2) bytes; scales stay (rows, K / 16))."""
+    la, lb = _layout(la, "la"), _layout(lb, "lb")
+    M, N = _rows(A, la, 2), _rows(B, lb, 2)
+    K = A.shape[1] * 2 if la == K_MAJOR else A.shape[0]
     u8 = (torch.uint8,)
-    pa = _dev(A, "A", u8, (M, K // 2))
-    pb = _dev(B, "B", u8, (N, K // 2))
+    pa = _dev(A, "A", u8, _shape(M, K, la, 2))
+    pb = _dev(B, "B", u8, _shape(N, K, lb, 2))
     psa = _dev(sA, "sA", u8, (M, K // 16))
     psb = _dev(sB, "sB", u8, (N, K // 16))
     out = _out(out, M, N, A)
     _check(lib().gemm_nvfp4(pa, psa, float(tA), pb, psb, float(tB), ctypes.c_void_p(out.data_ptr()),
-                            M, N, K, K_MAJOR, K_MAJOR, _stream(A)))
+                            M, N, K, la, lb, _stream(A)))
     return out
 
 

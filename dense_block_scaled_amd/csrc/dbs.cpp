@@ -239,9 +239,16 @@ dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA, const void *B,
     dbs_status st = check_common(A, B, D, M, N, K, la, lb, int64_t(1) << 22);
     if (st != DBS_OK) return st;
     if (K % 16) return fail(DBS_EINVAL, "nvfp4: K must be a multiple of 16");
-    if (la != DBS_K_MAJOR || lb != DBS_K_MAJOR)
-        return fail(DBS_EUNSUPPORTED, "nvfp4: only K-major A and B are implemented");
-    return run(dbs::kNVFP4, A, sA, B, sB, D, M, N, K, tA * tB, 4, 16, stream);
+    // K % 32 == 0 or an MN-major operand: the raw kernels (codes staged as
+    // they are, decoded in registers), which stage K-major rows in 16-byte
+    // pieces (whole 32-element half-rows); the launcher sends K-major
+    // problems they do not suit back to the NVFP4 kernels
+    if (la == DBS_K_MAJOR && lb == DBS_K_MAJOR && K % 32)
+        return run(dbs::kNVFP4, A, sA, B, sB, D, M, N, K, tA * tB, 4, 16, stream);
+    if ((la == DBS_K_MAJOR || lb == DBS_K_MAJOR) && K % 32)
+        return fail(DBS_EUNSUPPORTED, "nvfp4: a K-major operand beside an MN-major one needs K % 32 == 0");
+    if ((st = check_mn(la, lb, M, N, K, 4)) != DBS_OK) return st;
+    return run(dbs::kNVFP4R, A, sA, B, sB, D, M, N, K, tA * tB, 4, 16, stream, nullptr, la, lb);
 }
 
 // ---- FP8-rate NVFP4 (opt-in, lossy) ---------------------------------------------

@@ -234,6 +234,16 @@ struct Fmt<kMXFP4> {
     static constexpr int BPS = 8;
     using Frag = i32x4;
 };
+template <>
+struct Fmt<kNVFP4R> {
+    static constexpr int KSB = 32;         // staged like E2M1 MX: 64 K per k-step
+    static constexpr int BPS = 16;         // E4M3 scale bytes per row per stage (one per 16 K)
+    using Frag = i32x4;
+};
+
+// MX scales: E8M0 per 32, fed to the scaled MFMA
+template <int FMT>
+constexpr bool mx_scales() { return FMT == kMXFP8 || FMT == kMXFP4; }
 
 // MFMA k-steps per stage
 template <int FMT, class S>
@@ -356,6 +366,9 @@ struct Target {
 template <int FMT, class S>
 struct Frags {
     typename Fmt<FMT>::Frag a[S::MB], b[S::NB];
+    // raw NVFP4: the two E4M3 scales of each fragment's 32 elements (lane half
+    // h holds K 32h .. 32h+31 of the k-step, two 16-element blocks)
+    uint32_t sa[FMT == kNVFP4R ? S::MB : 1], sb[FMT == kNVFP4R ? S::NB : 1];
 };
 
 // MX scales of one stage for the lane's row of each row block, one dword per
@@ -548,6 +561,8 @@ __device__ __forceinline__ void read_a(Frags<FMT, S> &f, int i, const uint8_t *l
         f.a[i] = read_frag_mn<FMT, S::TM>(lds, c.fa, (uint32_t)(slot * S::kSlotA), kk, i);
     else
         f.a[i] = read_frag<FMT>(lds, c.fa, (uint32_t)(slot * S::kSlotA), kk, i);
+    if constexpr (FMT == kNVFP4R)
+        f.sa[i] = lds_read<uint16_t>(lds, c.sa + (uint32_t)(slot * S::TM * 16 + i * 32 * 16 + 4 * kk + 2 * c.h));
 }
 
 template <int FMT, class S>
@@ -560,6 +575,8 @@ __device__ __forceinline__ void read_b(Frags<FMT, S> &f, int j, const uint8_t *l
         f.b[j] = read_frag_mn<FMT, S::TN>(lds, c.fb, (uint32_t)(slot * S::kSlotB), kk, j);
     else
         f.b[j] = read_frag<FMT, KSH>(lds, c.fb, (uint32_t)(slot * S::kSlotB), kk, j);
+    if constexpr (FMT == kNVFP4R)
+        f.sb[j] = lds_read<uint16_t>(lds, c.sb + (uint32_t)(slot * S::TN * 16 + j * 32 * 16 + 4 * kk + 2 * c.h));
 }
 
 // ------------------------------------------------------------------ scales
@@ -1182,7 +1199,7 @@ __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int sl
                 dma_b(lds, slot, tg, ks, c, q, p.lda);
             }
         }
-        if constexpr (FMT == kMXFP8 || FMT == kMXFP4) {
+        if constexpr (FMT == kMXFP8 || FMT == kMXFP4 || FMT == kNVFP4R) {
             if (q == npieces<FMT, S>() - 1) {
                 if constexpr (SM == kScalesStage)
                     dma_scales<FMT>(lds, slot, tg, ks, c, p.sld);
@@ -1208,11 +1225,43 @@ __device__ __forceinline__ void commit_stage(Pipe<FMT, S> &P, uint8_t *lds, int 
         for (int i = 0; i < S::MB; ++i) P.aprev[i] = P.acur[i][3];
         decode_fp4_a<S>(P.acur, P.fp4a);
     }
-    if constexpr ((FMT == kMXFP8 || FMT == kMXFP4) && SM == kScalesRegs) store_scale_bytes(P.sbytes, lds, slot, c);
+    if constexpr ((FMT == kMXFP8 || FMT == kMXFP4 || FMT == kNVFP4R) && SM == kScalesRegs)
+        store_scale_bytes(P.sbytes, lds, slot, c);
     if constexpr (S::ACV || S::BCV) {
         // the last phase group (ALL: every group, loaded together in the prologue)
         constexpr int KK = kk_of<FMT, S>();
         store_cv<S, ALL ? 0 : cv_group<S, KK>(KK - 1), cv_units<S>()>(P.cv, lds, slot, c);
+    }
+}
+
+// Raw NVFP4 k-step: fragment element groups d = 0..3 (K 32h + 8d .. +7 for
+// lane half h) are decoded exactly into fp16 with their block's E4M3 scale
+// (groups 0, 1: the first 16-element block, 2, 3: the second) and each group
+// feeds one v_mfma_f32_32x32x16_f16.  A and B fragments are decoded alike, so
+// the MFMAs see the same permutation of K on both sides.
+template <class S>
+__device__ __forceinline__ void nv_raw_mma(f32x16 (&acc)[S::MB][S::NB], const Frags<kNVFP4R, S> &fa,
+                                           const Frags<kNVFP4R, S> &fb)
+{
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        f16x8 a[S::MB], b[S::NB];
+#pragma unroll
+        for (int i = 0; i < S::MB; ++i) {
+            const f16x2 s2 = e4m3_two(fa.sa[i]);
+            const f16x2 s = d < 2 ? f16x2{s2[0], s2[0]} : f16x2{s2[1], s2[1]};
+            a[i] = __builtin_bit_cast(f16x8, expand8((uint32_t)fa.a[i][d], s));
+        }
+#pragma unroll
+        for (int j = 0; j < S::NB; ++j) {
+            const f16x2 s2 = e4m3_two(fb.sb[j]);
+            const f16x2 s = d < 2 ? f16x2{s2[0], s2[0]} : f16x2{s2[1], s2[1]};
+            b[j] = __builtin_bit_cast(f16x8, expand8((uint32_t)fb.b[j][d], s));
+        }
+#pragma unroll
+        for (int i = 0; i < S::MB; ++i)
+#pragma unroll
+            for (int j = 0; j < S::NB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j], a[i], acc[i][j], 0, 0, 0);
     }
 }
 
@@ -1255,14 +1304,14 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
 #pragma unroll
             for (int j = 0; j < NB; ++j) read_b(nxt, j, lds, rslot, PH, c);
         }
-        if constexpr (Fmt<FMT>::BPS > 0 && PH == 0) {
+        if constexpr (mx_scales<FMT>() && PH == 0) {
             if constexpr (SM == kScalesChunk)
                 read_scales_chunk<FMT, S>(P.scur, lds, cp.pc, cp.j, c);
             else
                 read_scales<FMT>(P.scur, lds, rslot, c);
         }
     }
-    if constexpr (Fmt<FMT>::BPS > 0 && PH == 1) adjust_scales<FMT>(P.scur, c);
+    if constexpr (mx_scales<FMT>() && PH == 1) adjust_scales<FMT>(P.scur, c);
     if constexpr ((S::ACV || S::BCV) && LOADS) {
         // widened E2M1 pieces: the previous group to LDS, this phase's group from memory
         constexpr int KK = kk_of<FMT, S>();
@@ -1270,6 +1319,18 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
         load_cv<S, cv_group<S, KK>(PH), cv_group<S, KK>(PH + 1)>(P.cv, tg, ks, c, p.ldc);
     }
     DBS_FENCE();
+    if constexpr (FMT == kNVFP4R) {
+        nv_raw_mma<S>(acc, fa, cur);
+        if constexpr (LOADS) {
+#pragma unroll
+            for (int q = 0; q < NP; ++q) {
+                DBS_FENCE();
+                if (PH == 0) load_piece<FMT, S, SM>(P, lds, lslot, tg, ks, p, c, q, stg, cp);
+                DBS_FENCE();
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
 #pragma unroll
@@ -1332,7 +1393,7 @@ __device__ __forceinline__ void stage(Pipe<FMT, S> &P, f32x16 (&acc)[S::MB][S::N
         phase<FMT, S, SM, 3, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt, stg, cp);
     }
     commit_stage<FMT, S, SM>(P, lds, nxt, c);
-    if constexpr (Fmt<FMT>::BPS > 0) {
+    if constexpr (mx_scales<FMT>()) {
 #pragma unroll
         for (int i = 0; i < S::MB; ++i) P.sprev.a[i][0] = P.scur.a[i][0];
 #pragma unroll
@@ -1481,7 +1542,7 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
 #pragma unroll
             for (int i = 0; i < MB; ++i) P.F0.a[i] = typename Fmt<FMT>::Frag{};
         }
-        if constexpr (Fmt<FMT>::BPS > 0) {
+        if constexpr (mx_scales<FMT>()) {
             // unit E8M0 scales (finite) for those zero fragments
 #pragma unroll
             for (int i = 0; i < MB; ++i) P.sprev.a[i][0] = 0x7F7F7F7Fu;
@@ -1828,8 +1889,14 @@ hipError_t launch_one(const Params &p0, int grid, hipStream_t stream)
                 return hipGetLastError();
             }
         }
+        // raw NVFP4 with K-major operands: the 8-wave square tiles only
+        constexpr bool K0 = FMT != kNVFP4R || (std::is_same<S0, Square>::value && SM == kScalesStage);
+        if (!K0 && p.lay == 0) return hipErrorInvalidValue;
         switch (p.lay) {
-        case 0: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 0>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+        case 0:
+            if constexpr (K0)
+                hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 0>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p);
+            break;
         case 1: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 1>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
         case 2: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 2>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
         case 3: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 3>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
@@ -1899,6 +1966,7 @@ hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
         if (p.K % 32) return launch_one<FMT, kNvHalf, S>(p, grid, stream);
         return launch_one<FMT, kNvWhole, S>(p, grid, stream);
     }
+
     // stages that arrive entirely by direct-to-LDS loads get a deeper ring
     // when every tile has enough stages to fill it
     if constexpr (std::is_same<S, Skinny>::value && FMT != kNVFP4) {
@@ -1914,6 +1982,29 @@ hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
     return launch_one<FMT, kScalesStage, S>(p, grid, stream);
 }
 
+// Raw NVFP4 (K % 32 == 0, or an MN-major operand).  Square tiles: the 8-wave
+// kernel when the scale rows take dword loads (K-major or not: it beats
+// decoding into LDS by about a fifth at 8192^3); otherwise the register-staged
+// scale bytes need the one-wave-per-SIMD tiles, and K-major operands go back
+// to the NVFP4 kernels.  Skinny tiles: K-major operands keep the NVFP4
+// kernels (the raw-ring kernel), MN-major ones take the deeper ring when
+// every tile has the stages to fill it.
+template <class S>
+hipError_t launch_nvfp4_raw(const Params &p, int grid, hipStream_t stream)
+{
+    if constexpr (std::is_same<S, Square>::value) {
+        if (p.scales_aligned) return launch_one<kNVFP4R, kScalesStage, Square>(p, grid, stream);
+        if (p.lay == 0) return launch_fmt<kNVFP4, S>(p, grid, stream);
+        return launch_one<kNVFP4R, kScalesRegs, SquareW4>(p, grid, stream);
+    } else {
+        if (p.lay == 0) return launch_fmt<kNVFP4, S>(p, grid, stream);
+        if (p.scales_aligned && stages_of<kNVFP4R, SkinnyDeep>(p.K) >= SkinnyDeep::NS - 1)
+            return launch_one<kNVFP4R, kScalesStage, SkinnyDeep>(p, grid, stream);
+        if (p.scales_aligned) return launch_one<kNVFP4R, kScalesStage, S>(p, grid, stream);
+        return launch_one<kNVFP4R, kScalesRegs, S>(p, grid, stream);
+    }
+}
+
 template <class S>
 hipError_t launch_shape(int fmt, const Params &p, int grid, hipStream_t stream)
 {
@@ -1922,6 +2013,7 @@ hipError_t launch_shape(int fmt, const Params &p, int grid, hipStream_t stream)
     case kMXFP8: return launch_fmt<kMXFP8, S>(p, grid, stream);
     case kMXFP4: return launch_fmt<kMXFP4, S>(p, grid, stream);
     case kNVFP4: return launch_fmt<kNVFP4, S>(p, grid, stream);
+    case kNVFP4R: return launch_nvfp4_raw<S>(p, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }

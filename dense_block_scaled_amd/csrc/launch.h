@@ -7,7 +7,10 @@
 
 namespace dbs {
 
-enum Format : int { kBF16 = 0, kMXFP8 = 1, kMXFP4 = 2, kNVFP4 = 3 };
+// kNVFP4R: NVFP4 staged raw (the E2M1 bytes as MXFP4 stages them, the E4M3
+// scales as MX scales) and decoded in registers -- the path for MN-major
+// NVFP4 operands; internal, chosen by the launcher.
+enum Format : int { kBF16 = 0, kMXFP8 = 1, kMXFP4 = 2, kNVFP4 = 3, kNVFP4R = 4 };
 
 constexpr int kMaxGroups = 64;
 

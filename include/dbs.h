@@ -69,10 +69,12 @@ typedef enum {
  * stage such tiles as K-rows and read MFMA fragments out of them with the
  * gfx950 transposed LDS reads, the role the "Dissecting ThunderKittens"
  * write-up gives to layout-aware tile loads (register tiles).  Taken by
- * gemm_bf16 and gemm_mx, for A and B independently, when each MN-major
- * operand's K-rows are whole 16-byte chunks (M or N times the element bits a
- * multiple of 128) and it stays below 2 GiB; DBS_EUNSUPPORTED otherwise, and
- * for gemm_nvfp4 and the grouped GEMMs (K-major only). */
+ * gemm_bf16, gemm_mx and gemm_nvfp4, for A and B independently, when each
+ * MN-major operand's K-rows are whole 16-byte chunks (M or N times the
+ * element bits a multiple of 128) and it stays below 2 GiB; DBS_EUNSUPPORTED
+ * otherwise, and for the grouped GEMMs (K-major only).  FP4 elements of an
+ * MN-major operand pack two consecutive M (or N) per byte, low nibble first.
+ * Block scales keep their K-major layout (rows x K/block) either way. */
 typedef enum {
     DBS_K_MAJOR = 0,
     DBS_MN_MAJOR = 1
@@ -127,8 +129,10 @@ dbs_status gemm_mx_mixed(dbs_mx_elem elem_a, dbs_mx_elem elem_b,
 /*
  * NVFP4 GEMM: packed E2M1 elements, E4M3 block scales sA (M x K/16) and sB
  * (N x K/16), per-tensor fp32 scales tA, tB; D = bf16(tA*tB * sum).  K must
- * be a multiple of 16 (the format's block), at most 2^22.  K-major A and B
- * only (DBS_EUNSUPPORTED for MN-major).
+ * be a multiple of 16 (the format's block), at most 2^22.  MN-major operands
+ * (see dbs_layout) run on kernels that stage the packed codes and decode them
+ * in registers; there a K-major operand beside an MN-major one needs K a
+ * multiple of 32 (DBS_EUNSUPPORTED otherwise).
  */
 dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA,
                       const void *B, const uint8_t *sB, float tB, void *D,

@@ -119,20 +119,25 @@ def test_mx_null_scales():
     assert L.gemm_mx(0, FAKE, NUL, FAKE, FAKE, FAKE, 8, 8, 64, 0, 0, NUL) == 1
 
 
-@pytest.mark.parametrize("K,lay,want", [(24, (0, 0), 1), (40, (0, 0), 1), (64, (1, 0), 2), (64, (0, 1), 2)])
-def test_nvfp4_validation(K, lay, want):
+@pytest.mark.parametrize("M,K,lay,want", [
+    (64, 24, (0, 0), 1), (64, 40, (0, 0), 1),
+    (64, 48, (1, 0), 2), (64, 48, (0, 1), 2),          # K-major beside MN-major: K % 32 == 0 only
+    (48, 64, (1, 0), 2),                               # MN-major A: M * 4 bits not whole 16-byte rows
+])
+def test_nvfp4_validation(M, K, lay, want):
     L = dbs.lib()
-    assert L.gemm_nvfp4(FAKE, FAKE, 1.0, FAKE, FAKE, 1.0, FAKE, 64, 64, K, *lay, NUL) == want
+    assert L.gemm_nvfp4(FAKE, FAKE, 1.0, FAKE, FAKE, 1.0, FAKE, M, 64, K, *lay, NUL) == want
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would reach a real device")
 @pytest.mark.parametrize("fmt,M,N,K,lay", [("bf16", 8, 24, 64, (1, 1)), ("e4m3", 16, 48, 64, (1, 0)),
                                             ("e2m1", 64, 32, 64, (0, 1)), ("nvfp4", 8, 8, 48, (0, 0)),
-                                            ("nvfp4", 8, 8, 16, (0, 0))])
+                                            ("nvfp4", 8, 8, 16, (0, 0)), ("nvfp4", 32, 64, 48, (1, 1)),
+                                            ("nvfp4", 32, 8, 64, (1, 0)), ("nvfp4", 8, 32, 64, (0, 1))])
 def test_valid_requests_pass_validation(fmt, M, N, K, lay):
     """MN-major operands with whole 16-byte K-rows, and NVFP4 with K an odd
-    multiple of 16, get past validation (to the device lookup, which fails
-    here without a GPU)."""
+    multiple of 16 (with both operands MN-major, or both K-major), get past
+    validation (to the device lookup, which fails here without a GPU)."""
     L = dbs.lib()
     if fmt == "bf16":
         st = L.gemm_bf16(FAKE, FAKE, FAKE, M, N, K, *lay, NUL)

@@ -14,7 +14,7 @@ from tests.test_gpu_parity import _identity_w
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ["bf16", "mxfp8", "mxfp4"]
+FMTS = ["bf16", "mxfp8", "mxfp4", "nvfp4"]
 LAYS = [(1, 0), (0, 1), (1, 1)]
 
 
@@ -41,6 +41,8 @@ def run_layout(fmt: str, w: dict, la: int, lb: int) -> torch.Tensor:
     d = _gpu.to_dev({"A": A, "B": B, **({"sA": w["sA"], "sB": w["sB"]} if fmt != "bf16" else {})})
     if fmt == "bf16":
         return dbs.gemm_bf16(d["A"], d["B"], la=la, lb=lb)
+    if fmt == "nvfp4":
+        return dbs.gemm_nvfp4(d["A"], d["sA"], w["tA"], d["B"], d["sB"], w["tB"], la=la, lb=lb)
     elem = "e4m3" if fmt == "mxfp8" else "e2m1"
     return dbs.gemm_mx(elem, d["A"], d["sA"], d["B"], d["sB"], K=w["K"], la=la, lb=lb)
 
@@ -83,7 +85,7 @@ def test_layout_matches_oracle(shape, fmt, lay):
 def test_layout_edges(fmt, lay):
     """The smallest MN-major rows each format takes (16 bytes: 8 bf16, 16
     E4M3, 32 E2M1), a single output tile, and K of one MX block."""
-    rows = {"bf16": 8, "mxfp8": 16, "mxfp4": 32}[fmt]
+    rows = {"bf16": 8, "mxfp8": 16, "mxfp4": 32, "nvfp4": 32}[fmt]
     for M, N, K in [(rows, rows, 32), (rows, 3 * rows, 96), (5 * rows, rows, 64)]:
         _gpu.say(f"[layout] {fmt} {_lay_id(lay)} edge {(M, N, K)}")
         w = synth.workload(fmt, M, N, K, 11, 12)
@@ -113,10 +115,52 @@ def test_layout_exact_permutation(fmt, lay, mk):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_layouts_agree_bitwise(fmt):
     """All four layout combinations give the same bits (the MFMAs see the
-    same fragments, whatever the staging)."""
+    same fragments, whatever the staging).  NVFP4 with an MN-major operand
+    runs other kernels than K-major NVFP4 (codes decoded in registers, K
+    summed in another grouping), so there the three MN-major combinations
+    agree with each other."""
     _gpu.say(f"[layout] {fmt} all layouts agree")
     w = synth.workload(fmt, 2944, 3008, 512, 91, 92)
-    outs = [_gpu.d_bits(run_layout(fmt, w, la, lb)) for la, lb in [(0, 0), *LAYS]]
+    lays = LAYS if fmt == "nvfp4" else [(0, 0), *LAYS]
+    outs = [_gpu.d_bits(run_layout(fmt, w, la, lb)) for la, lb in lays]
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("shape", [(32, 32, 16), (64, 96, 48), (288, 320, 336), (2944, 3072, 1040)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_nvfp4_mn_odd_blocks(shape):
+    """NVFP4 with both operands MN-major and K an odd multiple of 16: the
+    last stage ends halfway through a 32-element half-row, on K-rows and
+    scale bytes that read as zero past K."""
+    M, N, K = shape
+    _gpu.say(f"[layout] nvfp4 mnAB odd K {shape}")
+    w = synth.workload("nvfp4", M, N, K, 13 + K % 7, 14 + M % 5)
+    D = run_layout("nvfp4", w, 1, 1)
+    torch.cuda.synchronize()
+    if M * N <= 1 << 23:
+        _gpu.check_full("nvfp4", w, D)
+    else:
+        em, en = synth.sample_entries(73, M, N, 4096)
+        _gpu.check_sampled("nvfp4", w, D.contiguous(), em, en)
+
+
+@pytest.mark.parametrize("lay", LAYS, ids=_lay_id)
+def test_nvfp4_mn_scale_rows_unaligned(lay):
+    """Scale rows whose base is not dword aligned: the register-staged scale
+    path of the MN-major NVFP4 kernels."""
+    M, N, K = 288, 320, 512
+    _gpu.say(f"[layout] nvfp4 {_lay_id(lay)} unaligned scale rows")
+    w = synth.workload("nvfp4", M, N, K, 15, 16)
+    A = to_mn("nvfp4", w["A"]) if lay[0] else w["A"]
+    B = to_mn("nvfp4", w["B"]) if lay[1] else w["B"]
+    d = _gpu.to_dev({"A": A, "B": B})
+    sa = torch.zeros(w["sA"].size + 1, dtype=torch.uint8, device="cuda")
+    sb = torch.zeros(w["sB"].size + 1, dtype=torch.uint8, device="cuda")
+    sa[1:] = torch.from_numpy(w["sA"].reshape(-1)).cuda()
+    sb[1:] = torch.from_numpy(w["sB"].reshape(-1)).cuda()
+    D = dbs.gemm_nvfp4(d["A"], sa[1:].view(M, K // 16), w["tA"], d["B"], sb[1:].view(N, K // 16), w["tB"],
+                       la=lay[0], lb=lay[1])
+    torch.cuda.synchronize()
+    _gpu.check_full("nvfp4", w, D)

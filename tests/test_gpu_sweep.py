@@ -14,7 +14,8 @@ from tests.test_gpu_layouts import to_mn
 
 pytestmark = pytest.mark.gpu
 
-# (format, element pair for 8-bit MX, K granularity, MN-major row granularity or None)
+# (format, element pair for 8-bit MX ("mn": NVFP4 with an MN-major operand),
+#  K granularity, MN-major row granularity or None)
 KINDS = [
     ("bf16", None, 8, 8),
     ("mxfp8", ("e4m3", "e4m3"), 32, 16),
@@ -23,27 +24,34 @@ KINDS = [
     ("mxfp8", ("e5m2", "e5m2"), 32, None),
     ("mxfp4", None, 32, 32),
     ("nvfp4", None, 16, None),
+    ("nvfp4", "mn", 16, 32),
 ]
 CASES = [(i, k) for k in range(len(KINDS)) for i in range(6)]
 
 
-def _draw(seed, kgran, mngran):
+def _draw(seed, kgran, mngran, mn_only=False):
     g = np.random.Generator(np.random.PCG64(seed))
     lay = (int(g.integers(0, 2)), int(g.integers(0, 2))) if mngran else (0, 0)
+    if mn_only and lay == (0, 0):
+        lay = (1, 1)
     def dim(mn):
         if mn and mngran:
             return int(g.integers(1, 700 // mngran + 1)) * mngran
         return int(g.integers(1, 701))
     M, N = dim(lay[0]), dim(lay[1])
     K = int(g.integers(1, 1024 // kgran + 1)) * kgran
+    if mn_only and lay != (1, 1) and K % 32:
+        K += 16        # NVFP4 with one K-major operand: whole 32-element half-rows
     return M, N, K, lay
 
 
 @pytest.mark.parametrize("case,kind", CASES, ids=lambda v: str(v))
 def test_sweep(case, kind):
     fmt, pair, kgran, mngran = KINDS[kind]
-    M, N, K, lay = _draw(1000 * kind + case, kgran, mngran)
+    M, N, K, lay = _draw(1000 * kind + case, kgran, mngran, pair == "mn")
     _gpu.say(f"[sweep] {fmt} {pair or ''} M={M} N={N} K={K} layouts={lay}")
+    if pair == "mn":
+        pair = None
     if pair:
         w = synth.workload(fmt, M, N, K, 3 * case + 1, 3 * case + 2, *pair)
     else:
@@ -54,7 +62,7 @@ def test_sweep(case, kind):
     if fmt == "bf16":
         D = dbs.gemm_bf16(d["A"], d["B"], la=lay[0], lb=lay[1])
     elif fmt == "nvfp4":
-        D = dbs.gemm_nvfp4(d["A"], d["sA"], w["tA"], d["B"], d["sB"], w["tB"])
+        D = dbs.gemm_nvfp4(d["A"], d["sA"], w["tA"], d["B"], d["sB"], w["tB"], la=lay[0], lb=lay[1])
     else:
         ea, eb = pair if pair else ("e2m1", "e2m1")
         D = dbs.gemm_mx_mixed(ea, eb, d["A"], d["sA"], d["B"], d["sB"], K=K, la=lay[0], lb=lay[1])
