@@ -218,8 +218,8 @@ dbs_status gemm_mx_mixed(dbs_mx_elem elem_a, dbs_mx_elem elem_b, const void *A, 
     const bool fp4_a = elem_a == DBS_E2M1, fp4_b = elem_b == DBS_E2M1;
     const int cv = fp4_a != fp4_b ? (fp4_a ? 1 : 2) : 0;
     const int ec = fp4_a && fp4_b ? 0 : (fp4_a ? 0 : mx8_code(elem_a)) | ((fp4_b ? 0 : mx8_code(elem_b)) << 3);
-    if ((ec != 0 || cv != 0) && (la != DBS_K_MAJOR || lb != DBS_K_MAJOR))
-        return fail(DBS_EUNSUPPORTED, "mx: E5M2 operands and 8-bit x E2M1 pairs are K-major only");
+    if (cv != 0 && (la != DBS_K_MAJOR || lb != DBS_K_MAJOR))
+        return fail(DBS_EUNSUPPORTED, "mx: 8-bit x E2M1 pairs are K-major only");
     const int bits = fp4_a && fp4_b ? 4 : 8;
     if ((st = check_mn(la, lb, M, N, K, bits)) != DBS_OK) return st;
     return run(bits == 8 ? dbs::kMXFP8 : dbs::kMXFP4, A, sA, B, sB, D, M, N, K, 1.0f, bits, 32, stream, nullptr,

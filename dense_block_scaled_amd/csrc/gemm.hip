@@ -1866,6 +1866,32 @@ constexpr int stage_elems()
     return FMT == kBF16 || FMT == kNVFP4 ? kRowBytes / 2 : FMT == kMXFP8 ? kRowBytes : 2 * kRowBytes;
 }
 
+// 8-bit MX kernels with E5M2 on either side (element codes ec: 1 A, 8 B, 9
+// both), in each operand layout.
+template <int EC, int SM, class S0>
+hipError_t launch_ec_lay(const Params &p, int grid, hipStream_t stream)
+{
+    switch (p.lay) {
+    case 0: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, EC>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 1, EC>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 2, EC>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 3, EC>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int SM, class S0>
+hipError_t launch_ec(const Params &p, int grid, hipStream_t stream)
+{
+    switch (p.ec) {
+    case 1: return launch_ec_lay<1, SM, S0>(p, grid, stream);
+    case 8: return launch_ec_lay<8, SM, S0>(p, grid, stream);
+    case 9: return launch_ec_lay<9, SM, S0>(p, grid, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int FMT, int SM, class S0>
 hipError_t launch_one(const Params &p0, int grid, hipStream_t stream)
 {
@@ -1878,15 +1904,10 @@ hipError_t launch_one(const Params &p0, int grid, hipStream_t stream)
         if constexpr (FMT == kMXFP8) {
             if (p.cv != 0) return hipErrorInvalidValue;    // launch_cv's
             if (p.ec != 0) {
-                // E5M2 on either side: K-major operands only (the host checks)
-                if (p.lay != 0) return hipErrorInvalidValue;
-                switch (p.ec) {
-                case 1: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 0, 1>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
-                case 8: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 0, 8>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
-                case 9: hipLaunchKernelGGL((gemm_kernel<FMT, WithLayout<S0, 0, 9>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
-                default: return hipErrorInvalidValue;
-                }
-                return hipGetLastError();
+                // E5M2 on either side: the same staging as E4M3 in every
+                // layout, other MFMA format fields
+                if (p.ec != 1 && p.ec != 8 && p.ec != 9) return hipErrorInvalidValue;
+                return launch_ec<SM, S0>(p, grid, stream);
             }
         }
         // raw NVFP4 with K-major operands: the 8-wave square tiles only

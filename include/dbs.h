@@ -100,8 +100,7 @@ dbs_status gemm_bf16(const void *A, const void *B, void *D,
 /*
  * MX GEMM (MXFP8 for elem = DBS_E4M3 or DBS_E5M2, MXFP4 for elem = DBS_E2M1):
  * elements of A and B in `elem`, E8M0 scales sA (M x K/32), sB (N x K/32).
- * K must be a multiple of 32, at most 2^22.  E5M2 operands are K-major only
- * (DBS_EUNSUPPORTED for MN-major).
+ * K must be a multiple of 32, at most 2^22.
  */
 dbs_status gemm_mx(dbs_mx_elem elem,
                    const void *A, const uint8_t *sA,
@@ -117,8 +116,8 @@ dbs_status gemm_mx(dbs_mx_elem elem,
  * MXFP8's staging; an E2M1 operand beside an 8-bit one (FP8 x FP4) is widened
  * to E4M3 on its way into LDS -- exactly, every E2M1 value being an E4M3
  * value, with its E8M0 scales unchanged -- and multiplied at the 8-bit rate.
- * Pairs other than E4M3 x E4M3 and E2M1 x E2M1 take K-major operands only
- * (DBS_EUNSUPPORTED for MN-major).
+ * An E2M1 operand beside an 8-bit one takes K-major operands only
+ * (DBS_EUNSUPPORTED for MN-major); every other pair takes either layout.
  */
 dbs_status gemm_mx_mixed(dbs_mx_elem elem_a, dbs_mx_elem elem_b,
                          const void *A, const uint8_t *sA,

@@ -70,14 +70,23 @@ def test_mx_validation(elem, K, want):
 @pytest.mark.parametrize("ea,eb,lay,want", [
     (0, 4, (1, 0), 2),          # E4M3 x E2M1 MN-major: not implemented
     (4, 1, (0, 1), 2),          # E2M1 x E5M2 MN-major
-    (1, 1, (1, 0), 2),          # E5M2 MN-major
-    (0, 1, (0, 1), 2),
+    (1, 1, (1, 0), 2),          # E5M2 MN-major, M * 8 bits not whole 16-byte K-rows (M = 40)
     (2, 0, (0, 0), 1),          # unknown element code
     (1, 7, (0, 0), 1),
 ])
 def test_mx_mixed_validation(ea, eb, lay, want):
     L = dbs.lib()
-    assert L.gemm_mx_mixed(ea, eb, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, *lay, NUL) == want
+    M = 40 if (ea, eb) == (1, 1) else 64
+    assert L.gemm_mx_mixed(ea, eb, FAKE, FAKE, FAKE, FAKE, FAKE, M, 64, 64, *lay, NUL) == want
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would reach a real device")
+@pytest.mark.parametrize("ea,eb,lay", [(1, 1, (1, 0)), (0, 1, (0, 1)), (1, 0, (1, 1))])
+def test_e5m2_mn_major_passes_validation(ea, eb, lay):
+    """E5M2 pairs take MN-major operands (to the device lookup, which fails
+    here without a GPU)."""
+    L = dbs.lib()
+    assert L.gemm_mx_mixed(ea, eb, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, *lay, NUL) == 3
     assert L.dbs_last_error().decode() != ""
 
 

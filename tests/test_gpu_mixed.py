@@ -8,6 +8,7 @@ import torch
 import dense_block_scaled_amd as dbs
 import synth
 from tests import _gpu, _pins
+from tests.test_gpu_layouts import to_mn
 
 pytestmark = pytest.mark.gpu
 
@@ -121,3 +122,50 @@ def test_e4m3_pair_unchanged():
     D1 = dbs.gemm_mx_mixed("e4m3", "e4m3", d["A"], d["sA"], d["B"], d["sB"], K=512)
     torch.cuda.synchronize()
     assert np.array_equal(_gpu.d_bits(D0), _gpu.d_bits(D1))
+
+
+E5M2_PAIRS = [("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")]
+LAYS = [(1, 0), (0, 1), (1, 1)]
+# 256 x 64 tiles with register-staged (K = 352) and stage scales (K = 512,
+# three-slot ring); 256 x 256 tiles with register-staged (352) and chunked (512)
+LAYOUT_SHAPES = [(288, 320, 352), (256, 19968, 512), (2944, 3072, 352), (3008, 2944, 512)]
+
+
+def _lid(l):
+    return {(0, 0): "kk", (1, 0): "mnA", (0, 1): "mnB", (1, 1): "mnAB"}[l]
+
+
+def run_mixed_layout(w: dict, la: int, lb: int) -> torch.Tensor:
+    A = to_mn("mxfp8", w["A"]) if la else w["A"]
+    B = to_mn("mxfp8", w["B"]) if lb else w["B"]
+    d = _gpu.to_dev({"A": A, "B": B, "sA": w["sA"], "sB": w["sB"]})
+    return dbs.gemm_mx_mixed(w["elemA"], w["elemB"], d["A"], d["sA"], d["B"], d["sB"], K=w["K"], la=la, lb=lb)
+
+
+@pytest.mark.parametrize("lay", LAYS, ids=_lid)
+@pytest.mark.parametrize("pair", E5M2_PAIRS, ids=_pid)
+@pytest.mark.parametrize("shape", LAYOUT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_e5m2_layouts_match_oracle(shape, pair, lay):
+    """E5M2 pairs with MN-major operands (transposed 8-bit reads) against the
+    oracle on the K-major codes."""
+    M, N, K = shape
+    _gpu.say(f"[mixed] {_pid(pair)} {_lid(lay)} {shape}")
+    w = synth.workload("mxfp8", M, N, K, 510 + M % 41, 610 + N % 43, *pair)
+    D = run_mixed_layout(w, *lay)
+    torch.cuda.synchronize()
+    if M * N <= 1 << 23:
+        _gpu.check_full("mxfp8", w, D)
+    else:
+        em, en = synth.sample_entries(74, M, N, 4096)
+        _gpu.check_sampled("mxfp8", w, D.contiguous(), em, en)
+
+
+@pytest.mark.parametrize("pair", E5M2_PAIRS, ids=_pid)
+def test_e5m2_layouts_agree_bitwise(pair):
+    """All four layout combinations give the same bits."""
+    _gpu.say(f"[mixed] {_pid(pair)} all layouts agree")
+    w = synth.workload("mxfp8", 2944, 3008, 512, 93, 94, *pair)
+    outs = [_gpu.d_bits(run_mixed_layout(w, la, lb)) for la, lb in [(0, 0), *LAYS]]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
