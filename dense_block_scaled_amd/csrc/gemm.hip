@@ -173,6 +173,8 @@ struct Shape {
     static constexpr bool AMN = (LAY & 1) != 0, BMN = (LAY & 2) != 0;
     static constexpr bool ACV = (CV & 1) != 0, BCV = (CV & 2) != 0;
     static constexpr int CA = EC & 7, CB = (EC >> 3) & 7;
+    // an E2M1 operand (code 4) of an 8-bit kernel, staged as packed codes
+    static constexpr bool AF4 = CA == 4, BF4 = CB == 4;
     static constexpr int NW = WM * WN;
     static constexpr int kThreads = 64 * NW;
     static constexpr int MB = TM / WM / 32, NB = TN / WN / 32;
@@ -363,9 +365,22 @@ struct Target {
     __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
 };
 
+// The packed E2M1 operand of an 8-bit kernel (S::AF4 / S::BF4) has a ring of
+// its own: a slot holds 256 K of every row (128-byte rows, staged as MXFP4
+// stages them) and serves two 8-bit stages of 128 K.  Stage s of a tile
+// reads half s % 2 of slot rs (its MXFP4 k-steps 2 (s % 2), 2 (s % 2) + 1)
+// and loads the same half of the slot's wave-loads of 256-K stage ks (from
+// resource r) into slot ls = rs ^ 1, which the two stages before last read.
+struct F4Pos {
+    int rs, half, ls, ks;
+    __amdgpu_buffer_rsrc_t r;
+};
+
 template <int FMT, class S>
 struct Frags {
-    typename Fmt<FMT>::Frag a[S::MB], b[S::NB];
+    // a packed E2M1 operand of an 8-bit kernel holds MXFP4 fragments
+    typename std::conditional<S::AF4, i32x4, typename Fmt<FMT>::Frag>::type a[S::MB];
+    typename std::conditional<S::BF4, i32x4, typename Fmt<FMT>::Frag>::type b[S::NB];
     // raw NVFP4: the two E4M3 scales of each fragment's 32 elements (lane half
     // h holds K 32h .. 32h+31 of the k-step, two 16-element blocks)
     uint32_t sa[FMT == kNVFP4R ? S::MB : 1], sb[FMT == kNVFP4R ? S::NB : 1];
@@ -579,6 +594,23 @@ __device__ __forceinline__ void read_b(Frags<FMT, S> &f, int j, const uint8_t *l
         f.sb[j] = lds_read<uint16_t>(lds, c.sb + (uint32_t)(slot * S::TN * 16 + j * 32 * 16 + 4 * kk + 2 * c.h));
 }
 
+// Fragments of a packed E2M1 operand of an 8-bit kernel: MXFP4 k-step
+// 2 half + kk of its ring slot (lane half h: K 32h .. 32h + 31 of the 8-bit
+// k-step kk, the layout the f8f6f4 MFMA takes for E2M1).
+template <int FMT, class S>
+__device__ __forceinline__ void read_a_f4(Frags<FMT, S> &f, int i, const uint8_t *lds, const F4Pos &fp, int kk,
+                                          const Ctx<S> &c)
+{
+    f.a[i] = read_frag<kMXFP4>(lds, c.fa, (uint32_t)(fp.rs * S::kSlotA), 2 * fp.half + kk, i);
+}
+
+template <int FMT, class S>
+__device__ __forceinline__ void read_b_f4(Frags<FMT, S> &f, int j, const uint8_t *lds, const F4Pos &fp, int kk,
+                                          const Ctx<S> &c)
+{
+    f.b[j] = read_frag<kMXFP4>(lds, c.fb, (uint32_t)(fp.rs * S::kSlotB), 2 * fp.half + kk, j);
+}
+
 // ------------------------------------------------------------------ scales
 
 // MX scales of the target stage go to scale slot `slot`: TM (A) and TN (B)
@@ -696,16 +728,20 @@ __device__ __forceinline__ void store_scale_bytes(const ScaleBytes<FMT, S> &r, u
 // SEL picks the byte of this k-step.
 // For 8-bit MX elements CA and CB are the format codes of A and B (the
 // instruction's second and first operand).
-template <int FMT, int SEL, int CA = 0, int CB = 0>
-__device__ __forceinline__ void mma1(f32x16 &acc, const typename Fmt<FMT>::Frag &a, uint32_t sa,
-                                     const typename Fmt<FMT>::Frag &b, uint32_t sb)
+__device__ __forceinline__ i32x8 widen_frag(const i32x8 &v) { return v; }
+__device__ __forceinline__ i32x8 widen_frag(const i32x4 &v) { return i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0}; }
+
+template <int FMT, int SEL, int CA = 0, int CB = 0, class FA, class FB>
+__device__ __forceinline__ void mma1(f32x16 &acc, const FA &a, uint32_t sa, const FB &b, uint32_t sb)
 {
     if constexpr (FMT == kBF16) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc, 0, 0, 0);
     } else if constexpr (FMT == kNVFP4) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, acc, 0, 0, 0);
     } else if constexpr (FMT == kMXFP8) {
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc, CB, CA, SEL, (int)sb, SEL, (int)sa);
+        // (an E2M1 operand, code 4, takes the low four dwords)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen_frag(b), widen_frag(a), acc, CB, CA, SEL, (int)sb,
+                                                              SEL, (int)sa);
     } else {
         const i32x8 bb = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
         const i32x8 aa = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
@@ -722,12 +758,12 @@ __device__ __forceinline__ void mma1(f32x16 &acc, const typename Fmt<FMT>::Frag 
 // (i%8) ^ swz(8L + i/8) = (i%8) ^ (i/8) ^ (L%8).  Chunks past the row end (a
 // partial last stage) read zeros.
 template <class S>
-__device__ __forceinline__ void dma_op(uint8_t *lds, int dst, __amdgpu_buffer_rsrc_t rsrc, const Target &tg, int ks,
-                                       const Ctx<S> &c, int L, int lda)
+__device__ __forceinline__ void dma_op(uint8_t *lds, int dst, __amdgpu_buffer_rsrc_t rsrc, int ks, const Ctx<S> &c,
+                                       int L, int lda, uint32_t r8)
 {
     const int k0 = ks * kRowBytes;
     const uint32_t kc = c.x4 ^ (uint32_t)((L & 7) << 4);
-    const uint32_t off = (c.r8lda + kc + (uint32_t)(L * 8 * lda + k0)) | (kc < (uint32_t)(lda - k0) ? 0u : kOOB);
+    const uint32_t off = (r8 + kc + (uint32_t)(L * 8 * lda + k0)) | (kc < (uint32_t)(lda - k0) ? 0u : kOOB);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + dst + L * 1024), 16, off, 0, 0, 0);
 }
 
@@ -754,14 +790,30 @@ template <class S>
 __device__ __forceinline__ void dma_a(uint8_t *lds, int slot, const Target &tg, int ks, const Ctx<S> &c, int q,
                                       int lda)
 {
-    dma_op(lds, S::kLdsA + slot * S::kSlotA, tg.ra, tg, ks, c, c.w * S::QA + q, lda);
+    dma_op(lds, S::kLdsA + slot * S::kSlotA, tg.ra, ks, c, c.w * S::QA + q, lda, c.r8lda);
 }
 
 template <class S>
 __device__ __forceinline__ void dma_b(uint8_t *lds, int slot, const Target &tg, int ks, const Ctx<S> &c, int q,
                                       int lda)
 {
-    dma_op(lds, S::kLdsB + slot * S::kSlotB, tg.rb, tg, ks, c, c.w * S::QB + q, lda);
+    dma_op(lds, S::kLdsB + slot * S::kSlotB, tg.rb, ks, c, c.w * S::QB + q, lda, c.r8lda);
+}
+
+// Packed E2M1 operand of an 8-bit kernel (rows of ldc = K / 2 bytes): wave
+// w issues wave-loads w 2Q + half Q + q, q < Q, of 256-K stage fp.ks into
+// slot fp.ls of the operand's ring, Q = QA / 2 (A) or QB / 2 (B).
+template <class S, bool IS_A>
+constexpr int f4_q() { return (IS_A ? S::QA : S::QB) / 2; }
+
+template <class S, bool IS_A>
+__device__ __forceinline__ void dma_f4(uint8_t *lds, int slot, __amdgpu_buffer_rsrc_t r, int ks, int half,
+                                       const Ctx<S> &c, int q, int ldc)
+{
+    constexpr int Q = f4_q<S, IS_A>();
+    static_assert(2 * Q == (IS_A ? S::QA : S::QB), "a 256-K stage splits into two halves");
+    const int dst = IS_A ? S::kLdsA + slot * S::kSlotA : S::kLdsB + slot * S::kSlotB;
+    dma_op(lds, dst, r, ks, c, c.w * 2 * Q + half * Q + q, ldc, (uint32_t)((c.lane >> 3) * ldc));
 }
 
 // ---------------------------------------------------------- NVFP4 staging
@@ -1177,13 +1229,15 @@ struct ChunkPos {
 template <int FMT, class S, int SM>
 __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int slot, const Target &tg, int ks,
                                            const Params &p, const Ctx<S> &c, int q, const Target &stg,
-                                           const ChunkPos &cp)
+                                           const ChunkPos &cp, const F4Pos &fp)
 {
     if constexpr (FMT == kNVFP4) {
         load_fp4<SM>(P.fp4, tg, ks, c, p.lda, p.sld);
         if constexpr (adirect<FMT, S>()) load_fp4_a<SM>(P.fp4a, tg, ks, c, p.lda, p.sld);
     } else {
-        if (q < S::QA && !S::ACV) {
+        if constexpr (S::AF4) {
+            if (q < f4_q<S, true>()) dma_f4<S, true>(lds, fp.ls, fp.r, fp.ks, fp.half, c, q, p.ldc);
+        } else if (q < S::QA && !S::ACV) {
             if constexpr (S::AMN) {
                 static_assert(Mn<FMT, S::TM>::RPL % Mn<FMT, S::TM>::PERIOD == 0 || S::QA % 2 == 0, "parity");
                 dma_mn<FMT, S::TM>(lds, S::kLdsA + slot * S::kSlotA, tg.ra, ks, c.ma, c.w * S::QA + q, q, p.ldam);
@@ -1191,7 +1245,9 @@ __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int sl
                 dma_a(lds, slot, tg, ks, c, q, p.lda);
             }
         }
-        if (q < S::QB && !S::BCV) {
+        if constexpr (S::BF4) {
+            if (q < f4_q<S, false>()) dma_f4<S, false>(lds, fp.ls, fp.r, fp.ks, fp.half, c, q, p.ldc);
+        } else if (q < S::QB && !S::BCV) {
             if constexpr (S::BMN) {
                 static_assert(Mn<FMT, S::TN>::RPL % Mn<FMT, S::TN>::PERIOD == 0 || S::QB % 2 == 0, "parity");
                 dma_mn<FMT, S::TN>(lds, S::kLdsB + slot * S::kSlotB, tg.rb, ks, c.mb, c.w * S::QB + q, q, p.ldbm);
@@ -1274,8 +1330,16 @@ __device__ __forceinline__ void nv_raw_mma(f32x16 (&acc)[S::MB][S::NB], const Fr
 template <int FMT, class S, int SM, int PH, bool RD, bool LOADS>
 __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> &P, uint8_t *lds, const Params &p,
                                       const Ctx<S> &c, int rslot, const Target &tg, int ks, int lslot,
-                                      const Target &stg, const ChunkPos &cp)
+                                      const Target &stg, const ChunkPos &cp, const F4Pos &fp)
 {
+    auto rda = [&](Frags<FMT, S> &f, int i) {
+        if constexpr (S::AF4) read_a_f4(f, i, lds, fp, PH, c);
+        else read_a(f, i, lds, rslot, PH, c);
+    };
+    auto rdb = [&](Frags<FMT, S> &f, int j) {
+        if constexpr (S::BF4) read_b_f4(f, j, lds, fp, PH, c);
+        else read_b(f, j, lds, rslot, PH, c);
+    };
     constexpr int MB = S::MB, NB = S::NB;
     constexpr bool CUR1 = PH == 0 || ((PH - 1) & 1);
     Frags<FMT, S> &cur = CUR1 ? P.F1 : P.F0;
@@ -1295,14 +1359,14 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
     if constexpr (RD) {
         if constexpr (ROLL) {
 #pragma unroll
-            for (int j = 0; j < NB; ++j) read_b(nxt, j, lds, rslot, PH, c);
+            for (int j = 0; j < NB; ++j) rdb(nxt, j);
         } else {
             if constexpr (!adirect<FMT, S>()) {
 #pragma unroll
-                for (int i = 0; i < MB; ++i) read_a(nxt, i, lds, rslot, PH, c);
+                for (int i = 0; i < MB; ++i) rda(nxt, i);
             }
 #pragma unroll
-            for (int j = 0; j < NB; ++j) read_b(nxt, j, lds, rslot, PH, c);
+            for (int j = 0; j < NB; ++j) rdb(nxt, j);
         }
         if constexpr (mx_scales<FMT>() && PH == 0) {
             if constexpr (SM == kScalesChunk)
@@ -1325,7 +1389,7 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
 #pragma unroll
             for (int q = 0; q < NP; ++q) {
                 DBS_FENCE();
-                if (PH == 0) load_piece<FMT, S, SM>(P, lds, lslot, tg, ks, p, c, q, stg, cp);
+                if (PH == 0) load_piece<FMT, S, SM>(P, lds, lslot, tg, ks, p, c, q, stg, cp, fp);
                 DBS_FENCE();
             }
         }
@@ -1344,14 +1408,14 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
                 const int pos = base + i * NB + j;   // compile-time after unrolling
                 if ((pos + 1) % SP == 0 && (pos + 1) / SP - 1 < NP) {
                     DBS_FENCE();
-                    load_piece<FMT, S, SM>(P, lds, lslot, tg, ks, p, c, (pos + 1) / SP - 1, stg, cp);
+                    load_piece<FMT, S, SM>(P, lds, lslot, tg, ks, p, c, (pos + 1) / SP - 1, stg, cp, fp);
                     DBS_FENCE();
                 }
             }
         }
         if constexpr (ROLL && RD) {
             DBS_FENCE();
-            read_a(P.F0, i, lds, rslot, PH, c);
+            rda(P.F0, i);
             DBS_FENCE();
         }
     }
@@ -1377,20 +1441,23 @@ __device__ __forceinline__ void opaque(Ctx<S> &c)
 template <int FMT, class S, int SM>
 __device__ __forceinline__ void stage(Pipe<FMT, S> &P, f32x16 (&acc)[S::MB][S::NB], uint8_t *lds, int slot,
                                       int nxt, const Params &p, Ctx<S> &c, const Target &tg, int ks, const Target &stg,
-                                      const ChunkPos &cp)
+                                      const ChunkPos &cp, const F4Pos &fp)
 {
     constexpr int KK = kk_of<FMT, S>();
     static_assert(S::NS == 2 || (FMT != kNVFP4 && SM != kScalesRegs && !S::ACV && !S::BCV),
                   "deeper rings need direct-to-LDS stages");
     static_assert(!(S::ACV || S::BCV) || (FMT == kMXFP8 && S::LAY == 0), "widened E2M1: 8-bit MX, K-major");
+    static_assert(!(S::AF4 || S::BF4) || (FMT == kMXFP8 && S::LAY == 0 && S::NS == 2 && !S::ACV && !S::BCV &&
+                                          !(S::AF4 && S::BF4)),
+                  "packed E2M1 beside 8-bit elements: K-major, two-slot rings");
     static_assert(SM != kScalesChunk || S::NS == 2, "chunked scales run on two-slot rings");
     static_assert(KK == 2 || KK == 4, "stages hold 2 or 4 k-steps");
     opaque(c);
-    phase<FMT, S, SM, 0, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt, stg, cp);
-    phase<FMT, S, SM, 1, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt, stg, cp);
+    phase<FMT, S, SM, 0, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt, stg, cp, fp);
+    phase<FMT, S, SM, 1, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt, stg, cp, fp);
     if constexpr (KK > 2) {
-        phase<FMT, S, SM, 2, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt, stg, cp);
-        phase<FMT, S, SM, 3, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt, stg, cp);
+        phase<FMT, S, SM, 2, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt, stg, cp, fp);
+        phase<FMT, S, SM, 3, true, true>(acc, P, lds, p, c, slot, tg, ks, nxt, stg, cp, fp);
     }
     commit_stage<FMT, S, SM>(P, lds, nxt, c);
     if constexpr (mx_scales<FMT>()) {
@@ -1414,7 +1481,7 @@ __device__ __forceinline__ Target tile_target(const Params &p, int tile)
         constexpr int EB = Mn<FMT, S::TM>::EB;
         const int64_t c0 = (int64_t)r.m0 * EB / 8;
         t.ra = make_rsrc(p.A + c0, (uint32_t)((int64_t)p.K * p.ldam - c0));
-    } else if constexpr (S::ACV) {
+    } else if constexpr (S::ACV || S::AF4) {
         t.ra = make_rsrc(p.A + (int64_t)r.m0 * p.ldc, (uint32_t)(rows_a * p.ldc));
     } else {
         t.ra = make_rsrc(p.A + (int64_t)r.m0 * p.lda, (uint32_t)(rows_a * p.lda));
@@ -1423,7 +1490,7 @@ __device__ __forceinline__ Target tile_target(const Params &p, int tile)
         constexpr int EB = Mn<FMT, S::TN>::EB;
         const int64_t c0 = (int64_t)r.n0 * EB / 8;
         t.rb = make_rsrc(p.B + c0, (uint32_t)((int64_t)p.K * p.ldbm - c0));
-    } else if constexpr (S::BCV) {
+    } else if constexpr (S::BCV || S::BF4) {
         t.rb = make_rsrc(p.B + r.boff + (int64_t)r.n0 * p.ldc, (uint32_t)(rows_b * p.ldc));
     } else {
         t.rb = make_rsrc(p.B + r.boff + (int64_t)r.n0 * p.lda, (uint32_t)(rows_b * p.lda));
@@ -1510,12 +1577,21 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
     constexpr int SPC = scale_spc<FMT>();
     Target stg = ld;
     ChunkPos cp{0, 0, 0};
+    // a packed E2M1 operand: its first 256-K stage goes to slot 0 of its ring
+    constexpr bool F4 = S::AF4 || S::BF4;
+    __amdgpu_buffer_rsrc_t f4r = S::AF4 ? ld.ra : ld.rb;
+    int f4s = 0;   // the E2M1 ring slot the next stage reads
+    F4Pos fp{0, 0, 0, 0, f4r};
 #pragma unroll
     for (int f = 0; f < S::NS - 1; ++f) {
 #pragma unroll
-        for (int q = 0; q < npieces<FMT, S>(); ++q) load_piece<FMT, S, SM>(P, lds, f, ld, f, p, c, q, stg, cp);
+        for (int q = 0; q < npieces<FMT, S>(); ++q) load_piece<FMT, S, SM>(P, lds, f, ld, f, p, c, q, stg, cp, fp);
         if constexpr (S::ACV || S::BCV) load_cv<S, 0, cv_units<S>()>(P.cv, ld, f, c, p.ldc);
         commit_stage<FMT, S, SM, true>(P, lds, f, c);
+    }
+    if constexpr (F4) {
+#pragma unroll
+        for (int q = 0; q < f4_q<S, S::AF4>(); ++q) dma_f4<S, S::AF4>(lds, 0, f4r, 0, 1, c, q, p.ldc);
     }
     if constexpr (SM == kScalesChunk) {
 #pragma unroll
@@ -1540,7 +1616,7 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
         }
         if constexpr (rolling<FMT, S>()) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i) P.F0.a[i] = typename Fmt<FMT>::Frag{};
+            for (int i = 0; i < MB; ++i) P.F0.a[i] = {};
         }
         if constexpr (mx_scales<FMT>()) {
             // unit E8M0 scales (finite) for those zero fragments
@@ -1572,12 +1648,27 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
                     if (cp.j == 0) stg = next < ntiles ? tile_target<FMT, S>(p, next) : null_target();
                 }
             }
-            stage<FMT, S, SM>(P, acc, lds, rs, ls, p, c, ld, ks, stg, cp);
+            if constexpr (F4) {
+                // stages s, s + 1 (s even) load the two halves of the
+                // operand's next 256-K stage: this tile's s / 2 + 1, or the
+                // next tile's first
+                fp = F4Pos{f4s, s & 1, f4s ^ 1, s / 2 + 1, f4r};
+                if (s + 2 >= p.nk) {
+                    if (s + 2 == p.nk) {
+                        const Target t = next < ntiles ? tile_target<FMT, S>(p, next) : null_target();
+                        f4r = S::AF4 ? t.ra : t.rb;
+                    }
+                    fp.ks = 0;
+                    fp.r = f4r;
+                }
+            }
+            stage<FMT, S, SM>(P, acc, lds, rs, ls, p, c, ld, ks, stg, cp, fp);
+            if constexpr (F4) f4s ^= s & 1;
             if constexpr (SM == kScalesChunk) pc ^= cp.j == SPC - 1 ? 1 : 0;
             xs = rs;
             rs = rs + 1 == S::NS ? 0 : rs + 1;
         }
-        phase<FMT, S, SM, 0, false, false>(acc, P, lds, p, c, 0, ld, 0, 0, stg, cp);
+        phase<FMT, S, SM, 0, false, false>(acc, P, lds, p, c, 0, ld, 0, 0, stg, cp, fp);
         mfma_drain<S>(acc);
 
         const TileRef tr = tile_ref<S::TM, S::TN>(tile, p);
@@ -1587,7 +1678,8 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
             if (p.vec16) {
                 // the slot the last stage read is free until the next
                 // tile's first stage refills it
-                store_tile_lds<S>(acc, lds, xs, p, tr, c);
+                // (a packed E2M1 A: the slot of its ring the tile read last)
+                store_tile_lds<S>(acc, lds, S::AF4 ? (f4s ^ 1) : xs, p, tr, c);
                 asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             } else {
                 store_tile<S>(acc, p, tr, c);
@@ -1952,10 +2044,43 @@ hipError_t launch_cv(const Params &p0, int grid, hipStream_t stream)
     return hipGetLastError();
 }
 
+// 8-bit MX GEMMs with an E2M1 operand staged as packed codes (K % 256 == 0,
+// K-major): the element codes with 4 on the E2M1 side.
+template <int SM, class S0>
+hipError_t launch_f4(const Params &p0, int grid, hipStream_t stream)
+{
+    static_assert(S0::NS == 2, "the E2M1 ring pairs with a two-slot ring");
+    Params p = p0;
+    p.nk = p.K / stage_elems<kMXFP8, S0>();
+    if (p.lay != 0 || p.K % 256 != 0) return hipErrorInvalidValue;
+    const int ca = p.cv & 1 ? 4 : p.ec & 7, cb = p.cv & 2 ? 4 : (p.ec >> 3) & 7;
+    switch (ca | (cb << 3)) {
+    case 4: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 4>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+    case 12: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 12>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+    case 32: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 32>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+    case 33: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 33>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <int FMT, class S>
 hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
 {
     if constexpr (FMT == kMXFP8) {
+        if (p.cv != 0 && p.K % 256 == 0) {
+            // FP8 x FP4 on the MFMA's mixed formats: the E2M1 operand in its
+            // own ring of packed 256-K stages
+            if (!p.scales_aligned) {
+                using U = typename std::conditional<std::is_same<S, Square>::value, SquareW4, S>::type;
+                return launch_f4<kScalesRegs, U>(p, grid, stream);
+            }
+            if constexpr (std::is_same<S, Square>::value) {
+                if (stages_of<kMXFP8, S>(p.K) % scale_spc<kMXFP8>() == 0)
+                    return launch_f4<kScalesChunk, S>(p, grid, stream);
+            }
+            return launch_f4<kScalesStage, S>(p, grid, stream);
+        }
         if (p.cv != 0) {
             if constexpr (std::is_same<S, Square>::value) {
                 return launch_cv<kScalesRegs, SquareW4>(p, grid, stream);

@@ -169,3 +169,82 @@ def test_e5m2_layouts_agree_bitwise(pair):
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
+
+
+F4_PAIRS = [("e4m3", "e2m1"), ("e2m1", "e4m3"), ("e5m2", "e2m1"), ("e2m1", "e5m2")]
+# K % 256 == 0: the E2M1 operand stays packed in a ring of its own.  256 x 64
+# tiles (K = 256: one 256-K stage per tile, so every load after the first
+# crosses to the next tile; K = 1024 with several tiles per workgroup) and
+# 256 x 256 tiles (chunked scales at K = 1024, per-stage scales at K = 768).
+F4_SHAPES = [(300, 520, 256), (256, 20000, 1024), (3000, 2900, 1024), (2944, 3008, 768), (4100, 4200, 512)]
+
+
+@pytest.mark.parametrize("pair", F4_PAIRS, ids=_pid)
+@pytest.mark.parametrize("shape", F4_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fp8_fp4_packed_matches_oracle(shape, pair):
+    M, N, K = shape
+    _gpu.say(f"[mixed] packed {_pid(pair)} {shape}")
+    w = synth.workload("mxfp8", M, N, K, 520 + M % 37, 620 + N % 31, *pair)
+    D = run_mixed(w)
+    torch.cuda.synchronize()
+    if M * N <= 1 << 23:
+        _gpu.check_full("mxfp8", w, D)
+    else:
+        em, en = synth.sample_entries(75, M, N, 4096)
+        _gpu.check_sampled("mxfp8", w, D, em, en)
+
+
+@pytest.mark.parametrize("pair", F4_PAIRS, ids=_pid)
+@pytest.mark.parametrize("mn", [(288, 320), (2944, 3008)], ids=lambda s: "x".join(map(str, s)))
+def test_fp8_fp4_packed_unaligned_scales(pair, mn):
+    """Scale rows whose base is not dword aligned: register-staged scales
+    beside the packed E2M1 ring (256 x 64 tiles and the 4-wave 256 x 256)."""
+    M, N = mn
+    K = 512
+    _gpu.say(f"[mixed] packed {_pid(pair)} unaligned scales {M}x{N}x{K}")
+    w = synth.workload("mxfp8", M, N, K, 17, 18, *pair)
+    d = _gpu.to_dev({"A": w["A"], "B": w["B"]})
+    sa = torch.zeros(w["sA"].size + 1, dtype=torch.uint8, device="cuda")
+    sb = torch.zeros(w["sB"].size + 1, dtype=torch.uint8, device="cuda")
+    sa[1:] = torch.from_numpy(w["sA"].reshape(-1)).cuda()
+    sb[1:] = torch.from_numpy(w["sB"].reshape(-1)).cuda()
+    D = dbs.gemm_mx_mixed(pair[0], pair[1], d["A"], sa[1:].view(M, K // 32), d["B"], sb[1:].view(N, K // 32), K=K)
+    torch.cuda.synchronize()
+    _gpu.check_full("mxfp8", w, D)
+
+
+@pytest.mark.parametrize("pair", F4_PAIRS, ids=_pid)
+@pytest.mark.parametrize("mk", [(300, 1024), (3000, 2048)], ids=lambda s: "x".join(map(str, s)))
+def test_fp8_fp4_packed_exact_permutation(pair, mk):
+    """A times a permutation matrix with non-unit scales, bit for bit, on the
+    packed E2M1 path."""
+    M, K = mk
+    ea, eb = pair
+    _gpu.say(f"[mixed] packed {_pid(pair)} exact permutation {M}x{K}x{K}")
+    rng = np.random.default_rng(41)
+    N = K
+    w = _pins.make_w_mx8(ea, eb, M, N, K, rng, scale_lo=110, scale_hi=140)
+    pi = rng.permutation(K)
+    B = np.zeros((N, K), np.uint8)
+    B[np.arange(N), pi] = {"e5m2": 0x3C, "e4m3": 0x38, "e2m1": 0x2}[eb]
+    if eb == "e2m1":
+        B = (B[:, 0::2] | (B[:, 1::2] << 4)).astype(np.uint8)
+    w["B"] = B
+    w["sB"] = rng.integers(118, 137, (N, K // 32)).astype(np.uint8)
+    D = run_mixed(w)
+    torch.cuda.synchronize()
+    if M * K <= 1 << 20:
+        _gpu.check_exact("mxfp8", w, D)
+    else:
+        em, en = synth.sample_entries(42, M, N, 4096)
+        _gpu.check_exact_sampled("mxfp8", w, D, em, en)
+
+
+@pytest.mark.parametrize("pair", F4_PAIRS, ids=_pid)
+def test_fp8_fp4_packed_random_codes(pair):
+    """Codes over each format's whole finite range with random non-unit scales."""
+    _gpu.say(f"[mixed] packed {_pid(pair)} random codes")
+    w = _pins.make_w_mx8(*pair, 300, 280, 512, np.random.default_rng(29), scale_lo=112, scale_hi=142)
+    D = run_mixed(w)
+    torch.cuda.synchronize()
+    _gpu.check_full("mxfp8", w, D)
