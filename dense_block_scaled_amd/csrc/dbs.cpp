@@ -112,8 +112,9 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     p.lda = (int)(K * elem_bits / 8);
     p.sld = block ? (int)(K / block) : 0;
     p.lay = (la == DBS_MN_MAJOR ? 1 : 0) | (lb == DBS_MN_MAJOR ? 2 : 0);
-    p.ldam = (int)(M * elem_bits / 8);
-    p.ldbm = (int)(N * elem_bits / 8);
+    // (an E2M1 operand of an 8-bit kernel, cv: K-rows of M / 2 or N / 2 bytes)
+    p.ldam = (int)((cv & 1) ? M / 2 : M * elem_bits / 8);
+    p.ldbm = (int)((cv & 2) ? N / 2 : N * elem_bits / 8);
     p.ec = ec;
     p.cv = cv;
     p.ldc = (int)(K / 2);
@@ -218,10 +219,11 @@ dbs_status gemm_mx_mixed(dbs_mx_elem elem_a, dbs_mx_elem elem_b, const void *A, 
     const bool fp4_a = elem_a == DBS_E2M1, fp4_b = elem_b == DBS_E2M1;
     const int cv = fp4_a != fp4_b ? (fp4_a ? 1 : 2) : 0;
     const int ec = fp4_a && fp4_b ? 0 : (fp4_a ? 0 : mx8_code(elem_a)) | ((fp4_b ? 0 : mx8_code(elem_b)) << 3);
-    if (cv != 0 && (la != DBS_K_MAJOR || lb != DBS_K_MAJOR))
-        return fail(DBS_EUNSUPPORTED, "mx: 8-bit x E2M1 pairs are K-major only");
+    if (cv != 0 && (la != DBS_K_MAJOR || lb != DBS_K_MAJOR) && K % 256)
+        return fail(DBS_EUNSUPPORTED, "mx: 8-bit x E2M1 pairs with an MN-major operand need K % 256 == 0");
     const int bits = fp4_a && fp4_b ? 4 : 8;
-    if ((st = check_mn(la, lb, M, N, K, bits)) != DBS_OK) return st;
+    if ((st = check_mn(la, DBS_K_MAJOR, M, N, K, fp4_a ? 4 : 8)) != DBS_OK) return st;
+    if ((st = check_mn(DBS_K_MAJOR, lb, M, N, K, fp4_b ? 4 : 8)) != DBS_OK) return st;
     return run(bits == 8 ? dbs::kMXFP8 : dbs::kMXFP4, A, sA, B, sB, D, M, N, K, 1.0f, bits, 32, stream, nullptr,
                la, lb, ec, cv);
 }

@@ -175,6 +175,11 @@ struct Shape {
     static constexpr int CA = EC & 7, CB = (EC >> 3) & 7;
     // an E2M1 operand (code 4) of an 8-bit kernel, staged as packed codes
     static constexpr bool AF4 = CA == 4, BF4 = CB == 4;
+    // the format whose staging operand A / B follows in a kernel of format F
+    template <int F>
+    static constexpr int fa() { return AF4 ? 2 : F; }      // 2: kMXFP4
+    template <int F>
+    static constexpr int fb() { return BF4 ? 2 : F; }
     static constexpr int NW = WM * WN;
     static constexpr int kThreads = 64 * NW;
     static constexpr int MB = TM / WM / 32, NB = TN / WN / 32;
@@ -601,14 +606,20 @@ template <int FMT, class S>
 __device__ __forceinline__ void read_a_f4(Frags<FMT, S> &f, int i, const uint8_t *lds, const F4Pos &fp, int kk,
                                           const Ctx<S> &c)
 {
-    f.a[i] = read_frag<kMXFP4>(lds, c.fa, (uint32_t)(fp.rs * S::kSlotA), 2 * fp.half + kk, i);
+    if constexpr (S::AMN)
+        f.a[i] = read_frag_mn<kMXFP4, S::TM>(lds, c.fa, (uint32_t)(fp.rs * S::kSlotA), 2 * fp.half + kk, i);
+    else
+        f.a[i] = read_frag<kMXFP4>(lds, c.fa, (uint32_t)(fp.rs * S::kSlotA), 2 * fp.half + kk, i);
 }
 
 template <int FMT, class S>
 __device__ __forceinline__ void read_b_f4(Frags<FMT, S> &f, int j, const uint8_t *lds, const F4Pos &fp, int kk,
                                           const Ctx<S> &c)
 {
-    f.b[j] = read_frag<kMXFP4>(lds, c.fb, (uint32_t)(fp.rs * S::kSlotB), 2 * fp.half + kk, j);
+    if constexpr (S::BMN)
+        f.b[j] = read_frag_mn<kMXFP4, S::TN>(lds, c.fb, (uint32_t)(fp.rs * S::kSlotB), 2 * fp.half + kk, j);
+    else
+        f.b[j] = read_frag<kMXFP4>(lds, c.fb, (uint32_t)(fp.rs * S::kSlotB), 2 * fp.half + kk, j);
 }
 
 // ------------------------------------------------------------------ scales
@@ -808,12 +819,19 @@ constexpr int f4_q() { return (IS_A ? S::QA : S::QB) / 2; }
 
 template <class S, bool IS_A>
 __device__ __forceinline__ void dma_f4(uint8_t *lds, int slot, __amdgpu_buffer_rsrc_t r, int ks, int half,
-                                       const Ctx<S> &c, int q, int ldc)
+                                       const Ctx<S> &c, int q, int ldc, int ldm)
 {
     constexpr int Q = f4_q<S, IS_A>();
     static_assert(2 * Q == (IS_A ? S::QA : S::QB), "a 256-K stage splits into two halves");
     const int dst = IS_A ? S::kLdsA + slot * S::kSlotA : S::kLdsB + slot * S::kSlotB;
-    dma_op(lds, dst, r, ks, c, c.w * 2 * Q + half * Q + q, ldc, (uint32_t)((c.lane >> 3) * ldc));
+    const int L = c.w * 2 * Q + half * Q + q;
+    if constexpr (IS_A ? S::AMN : S::BMN) {
+        // MN-major (K-rows of ldm bytes): the parity of L is that of half Q + q
+        constexpr int T = IS_A ? S::TM : S::TN;
+        dma_mn<kMXFP4, T>(lds, dst, r, ks, IS_A ? c.ma : c.mb, L, half * Q + q, ldm);
+    } else {
+        dma_op(lds, dst, r, ks, c, L, ldc, (uint32_t)((c.lane >> 3) * ldc));
+    }
 }
 
 // ---------------------------------------------------------- NVFP4 staging
@@ -1236,7 +1254,7 @@ __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int sl
         if constexpr (adirect<FMT, S>()) load_fp4_a<SM>(P.fp4a, tg, ks, c, p.lda, p.sld);
     } else {
         if constexpr (S::AF4) {
-            if (q < f4_q<S, true>()) dma_f4<S, true>(lds, fp.ls, fp.r, fp.ks, fp.half, c, q, p.ldc);
+            if (q < f4_q<S, true>()) dma_f4<S, true>(lds, fp.ls, fp.r, fp.ks, fp.half, c, q, p.ldc, p.ldam);
         } else if (q < S::QA && !S::ACV) {
             if constexpr (S::AMN) {
                 static_assert(Mn<FMT, S::TM>::RPL % Mn<FMT, S::TM>::PERIOD == 0 || S::QA % 2 == 0, "parity");
@@ -1246,7 +1264,7 @@ __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int sl
             }
         }
         if constexpr (S::BF4) {
-            if (q < f4_q<S, false>()) dma_f4<S, false>(lds, fp.ls, fp.r, fp.ks, fp.half, c, q, p.ldc);
+            if (q < f4_q<S, false>()) dma_f4<S, false>(lds, fp.ls, fp.r, fp.ks, fp.half, c, q, p.ldc, p.ldbm);
         } else if (q < S::QB && !S::BCV) {
             if constexpr (S::BMN) {
                 static_assert(Mn<FMT, S::TN>::RPL % Mn<FMT, S::TN>::PERIOD == 0 || S::QB % 2 == 0, "parity");
@@ -1447,9 +1465,8 @@ __device__ __forceinline__ void stage(Pipe<FMT, S> &P, f32x16 (&acc)[S::MB][S::N
     static_assert(S::NS == 2 || (FMT != kNVFP4 && SM != kScalesRegs && !S::ACV && !S::BCV),
                   "deeper rings need direct-to-LDS stages");
     static_assert(!(S::ACV || S::BCV) || (FMT == kMXFP8 && S::LAY == 0), "widened E2M1: 8-bit MX, K-major");
-    static_assert(!(S::AF4 || S::BF4) || (FMT == kMXFP8 && S::LAY == 0 && S::NS == 2 && !S::ACV && !S::BCV &&
-                                          !(S::AF4 && S::BF4)),
-                  "packed E2M1 beside 8-bit elements: K-major, two-slot rings");
+    static_assert(!(S::AF4 || S::BF4) || (FMT == kMXFP8 && S::NS == 2 && !S::ACV && !S::BCV && !(S::AF4 && S::BF4)),
+                  "packed E2M1 beside 8-bit elements: two-slot rings");
     static_assert(SM != kScalesChunk || S::NS == 2, "chunked scales run on two-slot rings");
     static_assert(KK == 2 || KK == 4, "stages hold 2 or 4 k-steps");
     opaque(c);
@@ -1478,7 +1495,7 @@ __device__ __forceinline__ Target tile_target(const Params &p, int tile)
     Target t;
     if constexpr (S::AMN) {
         // from the tile's first column to the end of the K x M operand
-        constexpr int EB = Mn<FMT, S::TM>::EB;
+        constexpr int EB = Mn<S::template fa<FMT>(), S::TM>::EB;
         const int64_t c0 = (int64_t)r.m0 * EB / 8;
         t.ra = make_rsrc(p.A + c0, (uint32_t)((int64_t)p.K * p.ldam - c0));
     } else if constexpr (S::ACV || S::AF4) {
@@ -1487,7 +1504,7 @@ __device__ __forceinline__ Target tile_target(const Params &p, int tile)
         t.ra = make_rsrc(p.A + (int64_t)r.m0 * p.lda, (uint32_t)(rows_a * p.lda));
     }
     if constexpr (S::BMN) {
-        constexpr int EB = Mn<FMT, S::TN>::EB;
+        constexpr int EB = Mn<S::template fb<FMT>(), S::TN>::EB;
         const int64_t c0 = (int64_t)r.n0 * EB / 8;
         t.rb = make_rsrc(p.B + c0, (uint32_t)((int64_t)p.K * p.ldbm - c0));
     } else if constexpr (S::BCV || S::BF4) {
@@ -1540,14 +1557,16 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
     c.r8lda = (uint32_t)((c.lane >> 3) * p.lda);
     c.x4 = (uint32_t)(((c.lane & 7) ^ (c.lane >> 3)) << 4);
     if constexpr (S::AMN) {
-        c.fa = mn_base<FMT, S::TM>(c.lane, c.wm * (S::TM / S::WM), S::kLdsA);
-        c.ma[0] = mn_dma_lane<FMT, S::TM>(c.lane, 0, p.ldam);
-        c.ma[1] = mn_dma_lane<FMT, S::TM>(c.lane, 1, p.ldam);
+        constexpr int FA = S::template fa<FMT>();
+        c.fa = mn_base<FA, S::TM>(c.lane, c.wm * (S::TM / S::WM), S::kLdsA);
+        c.ma[0] = mn_dma_lane<FA, S::TM>(c.lane, 0, p.ldam);
+        c.ma[1] = mn_dma_lane<FA, S::TM>(c.lane, 1, p.ldam);
     }
     if constexpr (S::BMN) {
-        c.fb = mn_base<FMT, S::TN>(c.lane, c.wn * (S::TN / S::WN), S::kLdsB);
-        c.mb[0] = mn_dma_lane<FMT, S::TN>(c.lane, 0, p.ldbm);
-        c.mb[1] = mn_dma_lane<FMT, S::TN>(c.lane, 1, p.ldbm);
+        constexpr int FB = S::template fb<FMT>();
+        c.fb = mn_base<FB, S::TN>(c.lane, c.wn * (S::TN / S::WN), S::kLdsB);
+        c.mb[0] = mn_dma_lane<FB, S::TN>(c.lane, 0, p.ldbm);
+        c.mb[1] = mn_dma_lane<FB, S::TN>(c.lane, 1, p.ldbm);
     }
 
     const int ntiles = p.tiles_m * p.tiles_n;
@@ -1591,7 +1610,8 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
     }
     if constexpr (F4) {
 #pragma unroll
-        for (int q = 0; q < f4_q<S, S::AF4>(); ++q) dma_f4<S, S::AF4>(lds, 0, f4r, 0, 1, c, q, p.ldc);
+        for (int q = 0; q < f4_q<S, S::AF4>(); ++q)
+            dma_f4<S, S::AF4>(lds, 0, f4r, 0, 1, c, q, p.ldc, S::AF4 ? p.ldam : p.ldbm);
     }
     if constexpr (SM == kScalesChunk) {
 #pragma unroll
@@ -2052,16 +2072,15 @@ hipError_t launch_f4(const Params &p0, int grid, hipStream_t stream)
     static_assert(S0::NS == 2, "the E2M1 ring pairs with a two-slot ring");
     Params p = p0;
     p.nk = p.K / stage_elems<kMXFP8, S0>();
-    if (p.lay != 0 || p.K % 256 != 0) return hipErrorInvalidValue;
+    if (p.K % 256 != 0) return hipErrorInvalidValue;
     const int ca = p.cv & 1 ? 4 : p.ec & 7, cb = p.cv & 2 ? 4 : (p.ec >> 3) & 7;
     switch (ca | (cb << 3)) {
-    case 4: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 4>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
-    case 12: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 12>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
-    case 32: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 32>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
-    case 33: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 33>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
+    case 4: return launch_ec_lay<4, SM, S0>(p, grid, stream);
+    case 12: return launch_ec_lay<12, SM, S0>(p, grid, stream);
+    case 32: return launch_ec_lay<32, SM, S0>(p, grid, stream);
+    case 33: return launch_ec_lay<33, SM, S0>(p, grid, stream);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <int FMT, class S>

@@ -113,11 +113,14 @@ dbs_status gemm_mx(dbs_mx_elem elem,
  * elem_b, otherwise as gemm_mx (gemm_mx(e, ...) is gemm_mx_mixed(e, e, ...)).
  * Every pairing of E4M3, E5M2 and E2M1 is taken.  gfx950's scaled MFMA
  * takes a format code per operand, so 8-bit pairs run at the 8-bit rate on
- * MXFP8's staging; an E2M1 operand beside an 8-bit one (FP8 x FP4) is widened
- * to E4M3 on its way into LDS -- exactly, every E2M1 value being an E4M3
- * value, with its E8M0 scales unchanged -- and multiplied at the 8-bit rate.
- * An E2M1 operand beside an 8-bit one takes K-major operands only
- * (DBS_EUNSUPPORTED for MN-major); every other pair takes either layout.
+ * MXFP8's staging.  An E2M1 operand beside an 8-bit one (FP8 x FP4) goes to
+ * the MFMA as packed E2M1 (its format code) when K is a multiple of 256, and
+ * is otherwise widened to E4M3 on its way into LDS -- exactly, every E2M1
+ * value being an E4M3 value, with its E8M0 scales unchanged; both run at the
+ * 8-bit rate.
+ * Every pair takes either layout per operand, except that an FP8 x FP4 pair
+ * with an MN-major operand needs K a multiple of 256 (DBS_EUNSUPPORTED
+ * otherwise); an MN-major E2M1 operand then needs M (or N) a multiple of 32.
  */
 dbs_status gemm_mx_mixed(dbs_mx_elem elem_a, dbs_mx_elem elem_b,
                          const void *A, const uint8_t *sA,

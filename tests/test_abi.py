@@ -68,7 +68,7 @@ def test_mx_validation(elem, K, want):
 
 
 @pytest.mark.parametrize("ea,eb,lay,want", [
-    (0, 4, (1, 0), 2),          # E4M3 x E2M1 MN-major: not implemented
+    (0, 4, (1, 0), 2),          # E4M3 x E2M1 MN-major with K % 256 != 0: not implemented
     (4, 1, (0, 1), 2),          # E2M1 x E5M2 MN-major
     (1, 1, (1, 0), 2),          # E5M2 MN-major, M * 8 bits not whole 16-byte K-rows (M = 40)
     (2, 0, (0, 0), 1),          # unknown element code
@@ -81,12 +81,21 @@ def test_mx_mixed_validation(ea, eb, lay, want):
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would reach a real device")
-@pytest.mark.parametrize("ea,eb,lay", [(1, 1, (1, 0)), (0, 1, (0, 1)), (1, 0, (1, 1))])
-def test_e5m2_mn_major_passes_validation(ea, eb, lay):
-    """E5M2 pairs take MN-major operands (to the device lookup, which fails
-    here without a GPU)."""
+@pytest.mark.parametrize("ea,eb,lay,K", [(1, 1, (1, 0), 64), (0, 1, (0, 1), 64), (1, 0, (1, 1), 64),
+                                         (0, 4, (1, 1), 256), (4, 1, (1, 0), 512)])
+def test_mn_major_pairs_pass_validation(ea, eb, lay, K):
+    """E5M2 pairs, and FP8 x FP4 pairs with K % 256 == 0, take MN-major
+    operands (to the device lookup, which fails here without a GPU)."""
     L = dbs.lib()
-    assert L.gemm_mx_mixed(ea, eb, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 64, *lay, NUL) == 3
+    assert L.gemm_mx_mixed(ea, eb, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, K, *lay, NUL) == 3
+
+
+def test_fp4_mn_rows_need_32_elements():
+    """An MN-major E2M1 operand beside an 8-bit one needs M (or N) a multiple
+    of 32 (whole 16-byte K-rows); the 8-bit one a multiple of 16."""
+    L = dbs.lib()
+    assert L.gemm_mx_mixed(4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 48, 64, 256, 1, 0, NUL) == 2
+    assert L.gemm_mx_mixed(0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 48, 256, 0, 1, NUL) == 2
     assert L.dbs_last_error().decode() != ""
 
 

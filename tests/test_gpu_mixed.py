@@ -135,9 +135,13 @@ def _lid(l):
     return {(0, 0): "kk", (1, 0): "mnA", (0, 1): "mnB", (1, 1): "mnAB"}[l]
 
 
+def _mn(elem: str, X: np.ndarray) -> np.ndarray:
+    return to_mn("mxfp4" if elem == "e2m1" else "mxfp8", X)
+
+
 def run_mixed_layout(w: dict, la: int, lb: int) -> torch.Tensor:
-    A = to_mn("mxfp8", w["A"]) if la else w["A"]
-    B = to_mn("mxfp8", w["B"]) if lb else w["B"]
+    A = _mn(w["elemA"], w["A"]) if la else w["A"]
+    B = _mn(w["elemB"], w["B"]) if lb else w["B"]
     d = _gpu.to_dev({"A": A, "B": B, "sA": w["sA"], "sB": w["sB"]})
     return dbs.gemm_mx_mixed(w["elemA"], w["elemB"], d["A"], d["sA"], d["B"], d["sB"], K=w["K"], la=la, lb=lb)
 
@@ -248,3 +252,58 @@ def test_fp8_fp4_packed_random_codes(pair):
     D = run_mixed(w)
     torch.cuda.synchronize()
     _gpu.check_full("mxfp8", w, D)
+
+
+# MN-major operands on the packed path (K % 256 == 0; M, N multiples of 32
+# for whole 16-byte E2M1 K-rows): 256 x 64 tiles, 256 x 256 tiles with
+# per-stage (K = 768) and chunked (K = 1024) scales
+F4_LAYOUT_SHAPES = [(288, 320, 512), (256, 19968, 1024), (2944, 3072, 768), (3008, 2944, 1024)]
+
+
+@pytest.mark.parametrize("lay", LAYS, ids=_lid)
+@pytest.mark.parametrize("pair", F4_PAIRS, ids=_pid)
+@pytest.mark.parametrize("shape", F4_LAYOUT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fp8_fp4_layouts_match_oracle(shape, pair, lay):
+    M, N, K = shape
+    _gpu.say(f"[mixed] packed {_pid(pair)} {_lid(lay)} {shape}")
+    w = synth.workload("mxfp8", M, N, K, 530 + M % 29, 630 + N % 23, *pair)
+    D = run_mixed_layout(w, *lay)
+    torch.cuda.synchronize()
+    if M * N <= 1 << 23:
+        _gpu.check_full("mxfp8", w, D)
+    else:
+        em, en = synth.sample_entries(76, M, N, 4096)
+        _gpu.check_sampled("mxfp8", w, D.contiguous(), em, en)
+
+
+@pytest.mark.parametrize("pair", F4_PAIRS, ids=_pid)
+def test_fp8_fp4_layouts_agree_bitwise(pair):
+    """All four layout combinations of the packed path give the same bits."""
+    _gpu.say(f"[mixed] packed {_pid(pair)} all layouts agree")
+    w = synth.workload("mxfp8", 2944, 3008, 1024, 95, 96, *pair)
+    outs = [_gpu.d_bits(run_mixed_layout(w, la, lb)) for la, lb in [(0, 0), *LAYS]]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("lay", LAYS, ids=_lid)
+@pytest.mark.parametrize("pair", [("e4m3", "e2m1"), ("e2m1", "e5m2")], ids=_pid)
+def test_fp8_fp4_layouts_unaligned_scales(pair, lay):
+    """Register-staged scales (rows not dword aligned) with MN-major operands
+    on the packed path (the 4-wave 256 x 256 tiles)."""
+    M, N, K = 2944, 3008, 512
+    _gpu.say(f"[mixed] packed {_pid(pair)} {_lid(lay)} unaligned scales")
+    w = synth.workload("mxfp8", M, N, K, 19, 20, *pair)
+    A = _mn(pair[0], w["A"]) if lay[0] else w["A"]
+    B = _mn(pair[1], w["B"]) if lay[1] else w["B"]
+    d = _gpu.to_dev({"A": A, "B": B})
+    sa = torch.zeros(w["sA"].size + 1, dtype=torch.uint8, device="cuda")
+    sb = torch.zeros(w["sB"].size + 1, dtype=torch.uint8, device="cuda")
+    sa[1:] = torch.from_numpy(w["sA"].reshape(-1)).cuda()
+    sb[1:] = torch.from_numpy(w["sB"].reshape(-1)).cuda()
+    D = dbs.gemm_mx_mixed(pair[0], pair[1], d["A"], sa[1:].view(M, K // 32), d["B"], sb[1:].view(N, K // 32), K=K,
+                          la=lay[0], lb=lay[1])
+    torch.cuda.synchronize()
+    em, en = synth.sample_entries(77, M, N, 4096)
+    _gpu.check_sampled("mxfp8", w, D.contiguous(), em, en)
