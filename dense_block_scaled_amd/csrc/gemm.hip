@@ -291,7 +291,7 @@ struct Mn {
     static constexpr int KSTEP = FMT == kBF16 ? 16 : 64; // K-rows per MFMA k-step
     static constexpr int QSTEP = FMT == kBF16 ? 4 : FMT == kMXFP8 ? 8 : 16;   // K-rows between sub-reads
     __device__ static constexpr int f(int r) { return W * ((r / P) % NF); }
-    static_assert(FMT != kNVFP4, "NVFP4 operands are K-major only");
+    static_assert(FMT != kNVFP4, "MN-major NVFP4 operands are staged raw (kNVFP4R)");
     static_assert(NF >= 1 && RB <= 1024 && KS * RB == T * kRowBytes, "slot geometry");
     // the K-rows one lane reads lie whole periods apart: one swizzle value per lane
     static_assert(KSTEP % PERIOD == 0 && QSTEP % PERIOD == 0, "one swizzle value per lane");
@@ -2010,7 +2010,7 @@ hipError_t launch_one(const Params &p0, int grid, hipStream_t stream)
     Params p = p0;
     p.nk = (p.K + stage_elems<FMT, S0>() - 1) / stage_elems<FMT, S0>();
     if constexpr (FMT == kNVFP4) {
-        if (p.lay != 0) return hipErrorInvalidValue;   // the host rejects MN-major NVFP4
+        if (p.lay != 0) return hipErrorInvalidValue;   // MN-major NVFP4 runs on the raw kernels
         hipLaunchKernelGGL((gemm_kernel<FMT, S0, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p);
     } else {
         if constexpr (FMT == kMXFP8) {
