@@ -35,10 +35,13 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 LLC_BYTES = 256 * 2 ** 20                      # MI355X Infinity Cache (MALL)
-PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "nvfp4": 2500.0, "nvfp4_fp8": 5000.0}
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "nvfp4": 2500.0, "nvfp4_fp8": 5000.0,
+               "mx_e4m3_e2m1": 5000.0}
 PEAK_NOTE = {"nvfp4": "exact NVFP4 runs on fp16 MFMA: priced at the bf16/fp16 dense peak",
              "nvfp4_fp8": "opt-in lossy FP8-rate NVFP4 (gemm_nvfp4_fp8): requantisation to MXFP8 plus the MXFP8 "
-                          "GEMM, both inside the timed launch; priced at the fp8 dense peak"}
+                          "GEMM, both inside the timed launch; priced at the fp8 dense peak",
+             "mx_e4m3_e2m1": "E4M3 A x E2M1 B (gemm_mx_mixed, packed E2M1 on the MFMA's mixed formats): "
+                             "priced at the fp8 dense peak, the rate its MFMAs run at"}
 HBM_GBS = 8000.0
 ELEM_BITS = {"bf16": 16, "mxfp8": 8, "mxfp4": 4, "nvfp4": 4}
 BLOCK = {"bf16": 0, "mxfp8": 32, "mxfp4": 32, "nvfp4": 16}
@@ -51,9 +54,12 @@ CONFIGS = {
     "nvfp4_skinny": (4, 256, 16384, 8192),
     "nvfp4_fp8": (4, 8192, 8192, 8192),
     "nvfp4_fp8_skinny": (4, 256, 16384, 8192),
+    "mx_e4m3_e2m1": (2, 8192, 8192, 8192),
 }
+# MX element formats of A and B where they differ from the format's own
+MX_ELEMS = {"mx_e4m3_e2m1": ("e4m3", "e2m1")}
 # the encoding each workload's inputs take, and the entry point it times
-INPUT_FMT = {"nvfp4_skinny": "nvfp4", "nvfp4_fp8": "nvfp4", "nvfp4_fp8_skinny": "nvfp4"}
+INPUT_FMT = {"nvfp4_skinny": "nvfp4", "nvfp4_fp8": "nvfp4", "nvfp4_fp8_skinny": "nvfp4", "mx_e4m3_e2m1": "mxfp8"}
 KERNEL_OF = {"nvfp4_skinny": "nvfp4", "nvfp4_fp8_skinny": "nvfp4_fp8"}
 
 
@@ -71,9 +77,14 @@ def log(msg):
 
 
 def algorithmic_bytes(fmt, M, N, K):
-    b = (M + N) * K * ELEM_BITS[fmt] // 8 + M * N * 2
-    if BLOCK[fmt]:
-        b += (M + N) * (K // BLOCK[fmt])
+    """A + B + scales + D, each moved once, for workload (or format) fmt."""
+    base = input_fmt(fmt)
+    ea, eb = MX_ELEMS.get(fmt, (None, None))
+    bits_a = 4 if ea == "e2m1" else ELEM_BITS[base]
+    bits_b = 4 if eb == "e2m1" else ELEM_BITS[base]
+    b = (M * bits_a + N * bits_b) * K // 8 + M * N * 2
+    if BLOCK[base]:
+        b += (M + N) * (K // BLOCK[base])
     return b
 
 
@@ -103,7 +114,7 @@ def traffic_for(workload):
 def make_inputs(fmt, cfg):
     import synth
     c, M, N, K = cfg
-    w = synth.workload(input_fmt(fmt), M, N, K, 100 * c + 1, 100 * c + 2)
+    w = synth.workload(input_fmt(fmt), M, N, K, 100 * c + 1, 100 * c + 2, *MX_ELEMS.get(fmt, ()))
     return w
 
 
@@ -126,6 +137,9 @@ def launcher(fmt, w, dev, out):
         return lambda: dbs.gemm_mx("e4m3", dev["A"], dev["sA"], dev["B"], dev["sB"], K=K, out=out)
     if fmt == "mxfp4":
         return lambda: dbs.gemm_mx("e2m1", dev["A"], dev["sA"], dev["B"], dev["sB"], K=K, out=out)
+    if fmt in MX_ELEMS:
+        ea, eb = MX_ELEMS[fmt]
+        return lambda: dbs.gemm_mx_mixed(ea, eb, dev["A"], dev["sA"], dev["B"], dev["sB"], K=K, out=out)
     tA, tB = w["tA"], w["tB"]
     if fmt == "nvfp4_fp8":
         import torch
@@ -138,7 +152,7 @@ def time_gemm(fmt, w, steps, warmup):
     """Protocol timing; returns (avg seconds per launch, groups, output tensor)."""
     import torch
     M, N, K = w["M"], w["N"], w["K"]
-    in_bytes = algorithmic_bytes(input_fmt(fmt), M, N, K) - M * N * 2
+    in_bytes = algorithmic_bytes(fmt, M, N, K) - M * N * 2
     groups = 1 if in_bytes >= 3 * LLC_BYTES else (3 * LLC_BYTES) // in_bytes + 1
     dev0 = to_device(w)
     devs = [dev0] + [{k: v.clone() for k, v in dev0.items()} for _ in range(groups - 1)]
@@ -209,7 +223,7 @@ def measure(fmt, steps, warmup):
     avg, groups, D = time_gemm(fmt, w, steps, warmup)
     M, N, K = w["M"], w["N"], w["K"]
     tflops = 2.0 * M * N * K / avg / 1e12
-    gbs = algorithmic_bytes(input_fmt(fmt), M, N, K) / avg / 1e9
+    gbs = algorithmic_bytes(fmt, M, N, K) / avg / 1e9
     log(f"[bench] {fmt}: {avg * 1e6:.1f} us/launch, {tflops:.1f} TFLOP/s, {gbs:.0f} GB/s, {groups} input groups")
     return w, D, avg, groups, tflops, gbs
 
@@ -280,7 +294,7 @@ def main():
             f"sample max r {rmax:.2e}")
     if not args.only:
         per = []
-        for f in ["bf16", "mxfp8", "mxfp4", "nvfp4", "nvfp4_skinny", "nvfp4_fp8", "nvfp4_fp8_skinny"]:
+        for f in ["bf16", "mxfp8", "mxfp4", "nvfp4", "nvfp4_skinny", "nvfp4_fp8", "nvfp4_fp8_skinny", "mx_e4m3_e2m1"]:
             if f == fmt:
                 entry_t, entry_gbs, entry_avg = tflops, gbs, avg
                 wf = w
