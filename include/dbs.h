@@ -12,7 +12,7 @@
  * 1.2 and 2.1).  Formats (bit layouts per the OCP Microscaling v1.0 spec):
  *
  *   gemm_bf16   BF16 elements, no scales, alpha = 1
- *   gemm_mx     E4M3 or E2M1 elements, one E8M0 scale per 32 K elements, alpha = 1
+ *   gemm_mx     E4M3, E5M2 or E2M1 elements, one E8M0 scale per 32 K elements, alpha = 1
  *   gemm_nvfp4  E2M1 elements, one E4M3 scale per 16 K elements, alpha = tA * tB
  *
  * Memory (all pointers are DEVICE pointers; dense, no leading dimensions):
@@ -28,7 +28,8 @@
  *   tA, tB : host fp32 values (NVFP4 per-tensor scales).
  *
  * Ownership and threading: the caller owns every buffer.  A call validates its
- * arguments on the host, then enqueues exactly one kernel on `stream` and
+ * arguments on the host, then enqueues its kernels on `stream` (one for a
+ * GEMM; gemm_nvfp4_fp8 and the quantisers name theirs below) and
  * returns without synchronising; faults inside the kernel surface at the
  * caller's next synchronisation of that stream.  The library allocates no
  * device memory and keeps only a per-device cache of the CU count, so calls
