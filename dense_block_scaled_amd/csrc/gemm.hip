@@ -314,7 +314,11 @@ struct Mn {
 //                stage (a per-stage fetch of 4 or 8 bytes from each of the
 //                tile's 512 scale rows costs as many L2 requests as the
 //                stage's operand slabs).
-constexpr int kScalesRegs = 0, kScalesStage = 1, kScalesChunk = 2;
+//  kScalesRows16: raw NVFP4 only (16 scale bytes per row per stage), scale
+//                rows of whole 16-byte pieces on 16-byte boundaries: the
+//                per-stage slots filled by 16-byte direct-to-LDS loads, one
+//                row per lane (a quarter of the dword loads' instructions).
+constexpr int kScalesRegs = 0, kScalesStage = 1, kScalesChunk = 2, kScalesRows16 = 4;
 constexpr int kScaleChunk = 16;
 // NVFP4 has no MX scales; its SM parameter says whether K ends on a whole
 // 32-element half-row (kNvWhole) or halfway through one (kNvHalf: K % 32 ==
@@ -653,6 +657,27 @@ __device__ __forceinline__ void dma_scales(uint8_t *lds, int slot, const Target 
         const uint32_t off = (uint32_t)(row * sld + o) | (o < sld ? 0u : kOOB);
         const int dst = S::kLdsS + (is_a ? slot * S::TM * BPS : S::NS * S::TM * BPS + slot * S::TN * BPS) + nn * 256;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? tg.rsa : tg.rsb, (lds_void *)(lds + dst), 4, off, 0, 0, 0);
+    }
+}
+
+// kScalesRows16: lane i of wave-load n of the concatenated row list (A rows,
+// then B rows) fetches the 16 stage bytes of row 64 n + i.  Spare loads
+// repeat earlier ones, as in dma_scales.
+template <int FMT, class S>
+__device__ __forceinline__ void dma_scale_rows16(uint8_t *lds, int slot, const Target &tg, int ks, const Ctx<S> &c,
+                                                 int sld)
+{
+    static_assert(Fmt<FMT>::BPS == 16, "one 16-byte piece per row and stage");
+    constexpr int NSA = S::TM / 64, NSB = S::TN / 64, NL = NSA + NSB;
+#pragma unroll
+    for (int k = 0; k < (NL + S::NW - 1) / S::NW; ++k) {
+        const int n = (c.w + k * S::NW) % NL;      // wave-uniform
+        const bool is_a = n < NSA;
+        const int nn = is_a ? n : n - NSA;
+        const int o = ks * 16;
+        const uint32_t off = (uint32_t)((nn * 64 + c.lane) * sld + o) | (o < sld ? 0u : kOOB);
+        const int dst = S::kLdsS + (is_a ? slot * S::TM * 16 : S::NS * S::TM * 16 + slot * S::TN * 16) + nn * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? tg.rsa : tg.rsb, (lds_void *)(lds + dst), 16, off, 0, 0, 0);
     }
 }
 
@@ -1184,10 +1209,12 @@ __device__ __forceinline__ void stage_barrier()
 // Loads each wave issues per stage on the direct-to-LDS path (operand
 // wave-loads plus an equal share of the MX scale wave-loads); only that path
 // uses rings deeper than two slots.
-template <int FMT, class S>
+template <int FMT, class S, int SM>
 constexpr int stage_loads_min()
 {
-    constexpr int NSC = Fmt<FMT>::BPS > 0 ? (S::TM + S::TN) * Fmt<FMT>::BPS / 256 : 0;
+    constexpr int NSC = Fmt<FMT>::BPS == 0 ? 0
+                        : SM == kScalesRows16 ? (S::TM + S::TN) / 64
+                                              : (S::TM + S::TN) * Fmt<FMT>::BPS / 256;
     return S::QA + S::QB + (NSC + S::NW - 1) / S::NW;
 }
 
@@ -1277,6 +1304,8 @@ __device__ __forceinline__ void load_piece(Pipe<FMT, S> &P, uint8_t *lds, int sl
             if (q == npieces<FMT, S>() - 1) {
                 if constexpr (SM == kScalesStage)
                     dma_scales<FMT>(lds, slot, tg, ks, c, p.sld);
+                else if constexpr (SM == kScalesRows16)
+                    dma_scale_rows16<FMT>(lds, slot, tg, ks, c, p.sld);
                 else if constexpr (SM == kScalesChunk)
                     dma_scale_portion<FMT>(lds, cp.pc ^ 1, stg, cp.lchunk, cp.j, c, p.sld);
                 else
@@ -1483,7 +1512,7 @@ __device__ __forceinline__ void stage(Pipe<FMT, S> &P, f32x16 (&acc)[S::MB][S::N
 #pragma unroll
         for (int j = 0; j < S::NB; ++j) P.sprev.b[j][0] = P.scur.b[j][0];
     }
-    stage_barrier<(S::NS - 2) * stage_loads_min<FMT, S>()>();
+    stage_barrier<(S::NS - 2) * stage_loads_min<FMT, S, SM>()>();
 }
 
 // Buffer resources of output tile `tile`: A/B rows and their scale rows.
@@ -2023,7 +2052,7 @@ hipError_t launch_one(const Params &p0, int grid, hipStream_t stream)
             }
         }
         // raw NVFP4 with K-major operands: the 8-wave square tiles only
-        constexpr bool K0 = FMT != kNVFP4R || (std::is_same<S0, Square>::value && SM == kScalesStage);
+        constexpr bool K0 = FMT != kNVFP4R || (std::is_same<S0, Square>::value && SM != kScalesRegs);
         if (!K0 && p.lay == 0) return hipErrorInvalidValue;
         switch (p.lay) {
         case 0:
@@ -2157,14 +2186,20 @@ hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
 template <class S>
 hipError_t launch_nvfp4_raw(const Params &p, int grid, hipStream_t stream)
 {
+    // scale rows of whole 16-byte stage pieces on 16-byte boundaries
+    const bool r16 = p.scales_aligned && p.K % 256 == 0 &&
+                     ((reinterpret_cast<uintptr_t>(p.sA) | reinterpret_cast<uintptr_t>(p.sB)) & 15) == 0;
     if constexpr (std::is_same<S, Square>::value) {
+        if (r16) return launch_one<kNVFP4R, kScalesRows16, Square>(p, grid, stream);
         if (p.scales_aligned) return launch_one<kNVFP4R, kScalesStage, Square>(p, grid, stream);
         if (p.lay == 0) return launch_fmt<kNVFP4, S>(p, grid, stream);
         return launch_one<kNVFP4R, kScalesRegs, SquareW4>(p, grid, stream);
     } else {
         if (p.lay == 0) return launch_fmt<kNVFP4, S>(p, grid, stream);
-        if (p.scales_aligned && stages_of<kNVFP4R, SkinnyDeep>(p.K) >= SkinnyDeep::NS - 1)
+        if (p.scales_aligned && stages_of<kNVFP4R, SkinnyDeep>(p.K) >= SkinnyDeep::NS - 1) {
+            if (r16) return launch_one<kNVFP4R, kScalesRows16, SkinnyDeep>(p, grid, stream);
             return launch_one<kNVFP4R, kScalesStage, SkinnyDeep>(p, grid, stream);
+        }
         if (p.scales_aligned) return launch_one<kNVFP4R, kScalesStage, S>(p, grid, stream);
         return launch_one<kNVFP4R, kScalesRegs, S>(p, grid, stream);
     }
