@@ -75,6 +75,10 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr uint32_t kOOB = 0x80000000u;         // beyond every num_records we set
+// Cache policy of the output stores: non-temporal.  D is written once and
+// never read by the kernel; streaming it keeps more of A and B in the caches
+// (BF16 8192^3: 1.5% in an A/B run; the other formats unchanged).
+constexpr int kStoreNT = 2;
 
 #define DBS_FENCE() __builtin_amdgcn_sched_barrier(0)
 
@@ -1125,12 +1129,12 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[S::MB][S::NB], co
                 const uint32_t base = (uint32_t)(c.lr * p.N + n) * 2u;
                 if (p.vec_store) {
                     // N % 4 == 0 and n % 4 == 0: the 4 columns are all in or all out
-                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, rd, n < p.N ? base : kOOB, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, rd, n < p.N ? base : kOOB, 0, kStoreNT);
                 } else {
                     const uint16_t v[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        __builtin_amdgcn_raw_buffer_store_b16(v[q], rd, n + q < p.N ? base + 2 * q : kOOB, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16(v[q], rd, n + q < p.N ? base + 2 * q : kOOB, 0, kStoreNT);
                 }
             }
         }
@@ -1185,7 +1189,7 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[S::MB][S::NB]
             const i32x4 v = *reinterpret_cast<const i32x4 *>(buf + r * RB + 16 * (ch ^ (r & (CPR - 1))));
             const int n = nc + ch * 8;
             // N % 8 == 0 and n % 8 == 0: the 8 columns are all in or all out
-            __builtin_amdgcn_raw_buffer_store_b128(v, rd, n < p.N ? (uint32_t)(r * p.N + n) * 2u : kOOB, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rd, n < p.N ? (uint32_t)(r * p.N + n) * 2u : kOOB, 0, kStoreNT);
         }
     }
 }
