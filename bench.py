@@ -48,6 +48,7 @@ BLOCK = {"bf16": 0, "mxfp8": 32, "mxfp4": 32, "nvfp4": 16}
 # config index -> seeds 100c+1, 100c+2 (A, B); sampling seed 100c+3
 CONFIGS = {
     "bf16": (1, 8192, 8192, 8192),
+    "bf16_4096": (1, 4096, 4096, 4096),
     "mxfp8": (2, 8192, 8192, 8192),
     "mxfp4": (3, 8192, 8192, 8192),
     "nvfp4": (4, 8192, 8192, 8192),
@@ -59,8 +60,8 @@ CONFIGS = {
 # MX element formats of A and B where they differ from the format's own
 MX_ELEMS = {"mx_e4m3_e2m1": ("e4m3", "e2m1")}
 # the encoding each workload's inputs take, and the entry point it times
-INPUT_FMT = {"nvfp4_skinny": "nvfp4", "nvfp4_fp8": "nvfp4", "nvfp4_fp8_skinny": "nvfp4", "mx_e4m3_e2m1": "mxfp8"}
-KERNEL_OF = {"nvfp4_skinny": "nvfp4", "nvfp4_fp8_skinny": "nvfp4_fp8"}
+INPUT_FMT = {"bf16_4096": "bf16", "nvfp4_skinny": "nvfp4", "nvfp4_fp8": "nvfp4", "nvfp4_fp8_skinny": "nvfp4", "mx_e4m3_e2m1": "mxfp8"}
+KERNEL_OF = {"bf16_4096": "bf16", "nvfp4_skinny": "nvfp4", "nvfp4_fp8_skinny": "nvfp4_fp8"}
 
 
 def input_fmt(fmt):
@@ -294,7 +295,8 @@ def main():
             f"sample max r {rmax:.2e}")
     if not args.only:
         per = []
-        for f in ["bf16", "mxfp8", "mxfp4", "nvfp4", "nvfp4_skinny", "nvfp4_fp8", "nvfp4_fp8_skinny", "mx_e4m3_e2m1"]:
+        for f in ["bf16", "bf16_4096", "mxfp8", "mxfp4", "nvfp4", "nvfp4_skinny", "nvfp4_fp8", "nvfp4_fp8_skinny",
+                  "mx_e4m3_e2m1"]:
             if f == fmt:
                 entry_t, entry_gbs, entry_avg = tflops, gbs, avg
                 wf = w
