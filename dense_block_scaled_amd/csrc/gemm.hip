@@ -1408,6 +1408,15 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
     const Scales<S> &sc = PH == 0 ? P.sprev : P.scur;
 
     if constexpr (RD) {
+        // the stage's scale rows first: LDS reads complete in order, so the
+        // adjustment in the next phase then waits for them alone and not for
+        // the fragment reads issued after them
+        if constexpr (mx_scales<FMT>() && PH == 0) {
+            if constexpr (SM == kScalesChunk)
+                read_scales_chunk<FMT, S>(P.scur, lds, cp.pc, cp.j, c);
+            else
+                read_scales<FMT>(P.scur, lds, rslot, c);
+        }
         if constexpr (ROLL) {
 #pragma unroll
             for (int j = 0; j < NB; ++j) rdb(nxt, j);
@@ -1418,12 +1427,6 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
             }
 #pragma unroll
             for (int j = 0; j < NB; ++j) rdb(nxt, j);
-        }
-        if constexpr (mx_scales<FMT>() && PH == 0) {
-            if constexpr (SM == kScalesChunk)
-                read_scales_chunk<FMT, S>(P.scur, lds, cp.pc, cp.j, c);
-            else
-                read_scales<FMT>(P.scur, lds, rslot, c);
         }
     }
     if constexpr (mx_scales<FMT>() && PH == 1) adjust_scales<FMT>(P.scur, c);
