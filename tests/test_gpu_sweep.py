@@ -25,6 +25,9 @@ KINDS = [
     ("mxfp4", None, 32, 32),
     ("nvfp4", None, 16, None),
     ("nvfp4", "mn", 16, 32),
+    ("mxfp8", ("e5m2", "e4m3"), 32, 16),          # E5M2 pairs take MN-major operands
+    ("mxfp8", ("e4m3", "e2m1"), 256, 32),         # FP8 x FP4 packed path (K % 256 == 0), any layout
+    ("mxfp8", ("e2m1", "e5m2"), 256, 32),
 ]
 CASES = [(i, k) for k in range(len(KINDS)) for i in range(6)]
 
@@ -56,8 +59,9 @@ def test_sweep(case, kind):
         w = synth.workload(fmt, M, N, K, 3 * case + 1, 3 * case + 2, *pair)
     else:
         w = synth.workload(fmt, M, N, K, 3 * case + 1, 3 * case + 2)
-    A = to_mn(fmt, w["A"]) if lay[0] else w["A"]
-    B = to_mn(fmt, w["B"]) if lay[1] else w["B"]
+    ea, eb = pair if pair else (None, None)
+    A = to_mn("mxfp4" if ea == "e2m1" else fmt, w["A"]) if lay[0] else w["A"]
+    B = to_mn("mxfp4" if eb == "e2m1" else fmt, w["B"]) if lay[1] else w["B"]
     d = _gpu.to_dev({"A": A, "B": B, **({"sA": w["sA"], "sB": w["sB"]} if fmt != "bf16" else {})})
     if fmt == "bf16":
         D = dbs.gemm_bf16(d["A"], d["B"], la=lay[0], lb=lay[1])
