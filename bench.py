@@ -70,7 +70,9 @@ def input_fmt(fmt):
 
 def kernel_of(fmt):
     return KERNEL_OF.get(fmt, fmt)
-KERNEL_SOURCES = ["dense_block_scaled_amd/csrc/gemm.hip", "dense_block_scaled_amd/csrc/launch.h"]
+KERNEL_SOURCES = ["dense_block_scaled_amd/csrc/" + f for f in
+                  ("gemm_kernel.h", "launch.h", "gemm.hip", "gemm_bf16.hip", "gemm_mxfp8.hip", "gemm_mx8_e5m2.hip",
+                   "gemm_mx8_fp4.hip", "gemm_mxfp4.hip", "gemm_nvfp4.hip")]
 
 
 def log(msg):

@@ -2,15 +2,20 @@
 
     python -m dense_block_scaled_amd.build
 
-hipcc compiles the kernels (csrc/gemm.hip, csrc/quant.hip) and the ABI layer (csrc/dbs.cpp)
-in-tree; no GPU is needed to build.  Packed-fp32 VALU instructions are turned
-off for the device code.
+hipcc compiles the kernel translation units (csrc/gemm_*.hip: one per group
+of formats, all instantiating the template in csrc/gemm_kernel.h), the
+launcher (csrc/gemm.hip), the quantisers (csrc/quant.hip) and the ABI layer
+(csrc/dbs.cpp) to objects in parallel, then links them, in-tree; no GPU is
+needed to build.  Packed-fp32 VALU instructions are turned off for the
+device code.
 """
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
@@ -23,24 +28,49 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
+# largest first, so the longest compile starts first
+SOURCES = ["gemm_mx8_fp4.hip", "gemm_mxfp8.hip", "gemm_mx8_e5m2.hip", "gemm_nvfp4.hip", "gemm_mxfp4.hip",
+           "gemm_bf16.hip", "quant.hip", "gemm.hip", "dbs.cpp"]
+
+
+def _jobs() -> int:
+    n = os.cpu_count() or 1
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    return max(1, min(n, len(SOURCES), int(os.environ.get("MAX_JOBS", n))))
+
 
 def build(verbose: bool = False, extra: list[str] | None = None) -> Path:
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+             f"-I{ROOT / 'include'}", f"-I{CSRC}", *DEVICE_FLAGS, *(extra or [])]
+    objdir = Path(tempfile.mkdtemp(prefix="libdbs.obj.", dir=str(PKG)))
     fd, tmp = tempfile.mkstemp(prefix="libdbs.", suffix=".so.tmp", dir=str(PKG))
     os.close(fd)
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-function", f"-I{ROOT / 'include'}", f"-I{CSRC}",
-           *DEVICE_FLAGS, *(extra or []),
-           str(CSRC / "gemm.hip"), str(CSRC / "quant.hip"), str(CSRC / "dbs.cpp"), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    try:
+
+    def compile_one(name: str) -> Path:
+        obj = objdir / (name + ".o")
+        cmd = [HIPCC, *flags, "-c", str(CSRC / name), "-o", str(obj)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
+        return obj
+
+    try:
+        with ThreadPoolExecutor(max_workers=_jobs()) as pool:
+            objs = list(pool.map(compile_one, SOURCES))
+        link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[str(o) for o in objs], "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.run(link, check=True)
         os.replace(tmp, LIB)
     finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
+        shutil.rmtree(objdir, ignore_errors=True)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    build(verbose=True)
