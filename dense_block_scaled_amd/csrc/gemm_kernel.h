@@ -2,8 +2,8 @@
 //
 //     D[m, n] = bf16( alpha * sum_k dA[m, k] * dB[n, k] ),   fp32 accumulation
 //
-// One persistent kernel template serves the four formats and two tile
-// shapes.  Design (and where it departs from the Blackwell kernels the pages
+// One persistent kernel template serves the four formats (and the mixed MX
+// element pairs) and two tile shapes; the gemm_*.hip units instantiate it.  Design (and where it departs from the Blackwell kernels the pages
 // describe):
 //
 // * Scheduling.  A persistent grid of at most one workgroup per CU walks the
@@ -19,12 +19,13 @@
 // * Tile shapes (chosen by the host).  Square: 256 x 256 output tiles, 8
 //   waves (two per SIMD), each owning 128 x 64 as 4 x 2 MFMA blocks of 32 x
 //   32.  Skinny (when 256 x 256 tiles cannot fill the CUs, e.g. M = 256):
-//   256 x 64 tiles, 4 waves of 64 x 64.  Two waves per SIMD matter on
+//   256 x 64 tiles, 8 waves of 32 x 64 on a three-slot ring, or 4 waves of
+//   64 x 64 where stages pass through registers.  Two waves per SIMD matter on
 //   gfx950: a wave that issues a global or LDS load stalls its own MFMA
 //   stream for tens of cycles, and the second wave's MFMAs fill that gap
 //   (the role split the pages obtain from dedicated producer warps).
 // * Staging.  Each stage moves a tile-rows x 128-byte slab of A and of B into
-//   one slot of a two-slot LDS ring (cf. the stage-count discussion of
+//   one slot of a two-slot (skinny: up to three-slot) LDS ring (cf. the stage-count discussion of
 //   "Async Tensor Core: Hopper wgmma -> Blackwell tcgen05", sections 3.1 and
 //   4.3).  BF16/E4M3/E2M1 slabs go straight from HBM to LDS (buffer_load
 //   ... lds), so staging costs no VGPRs and no LDS-write instructions; the
@@ -45,14 +46,21 @@
 //   double-buffered in VGPRs: the reads for k-step kk+1 are in flight while
 //   the MFMAs of kk issue, and the MFMAs of a stage's last k-step are issued
 //   after the barrier, behind the next stage's first reads.  BF16:
-//   v_mfma_f32_32x32x16_bf16.  MXFP8/MXFP4: v_mfma_scale_f32_32x32x64_f8f6f4.
-//   NVFP4: gfx950's scaled MFMA takes only E8M0 per 32, so its loader stages
-//   through VGPRs and decodes E2M1 x E4M3 exactly into fp16 (a product of 2-
-//   and 4-bit significands with magnitude in [2^-10, 2688]) on the way into
-//   LDS; the math is v_mfma_f32_32x32x16_f16 and tA*tB is applied in the
-//   epilogue.
+//   v_mfma_f32_32x32x16_bf16.  MXFP8/MXFP4: v_mfma_scale_f32_32x32x64_f8f6f4,
+//   whose per-operand format codes also take E5M2 and, beside an 8-bit
+//   operand, packed E2M1 (FP8 x FP4: the E2M1 operand in a ring of its own,
+//   see F4Pos).  NVFP4: gfx950's scaled MFMA takes only E8M0 per 32, so
+//   E2M1 x E4M3 is decoded exactly into fp16 (a product of 2- and 4-bit
+//   significands with magnitude in [2^-10, 2688]) and multiplied on
+//   v_mfma_f32_32x32x16_f16, tA*tB applied in the epilogue.  Where the packed
+//   rows allow it (kNVFP4R) the codes and scales are staged as they are and
+//   decoded in registers after the fragment read; otherwise the loader
+//   decodes into LDS on the way in.
 // * Epilogue.  alpha * acc -> bf16 (round to nearest even) -> global with
-//   buffer stores (out-of-range rows and columns dropped), in the same kernel.
+//   non-temporal buffer stores (out-of-range rows and columns dropped), in
+//   the same kernel.
+// * Operand layouts.  A and B may each be stored MN-major; such slots are
+//   read with gfx950's transposed LDS reads (see Mn).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
