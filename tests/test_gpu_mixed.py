@@ -307,3 +307,15 @@ def test_fp8_fp4_layouts_unaligned_scales(pair, lay):
     torch.cuda.synchronize()
     em, en = synth.sample_entries(77, M, N, 4096)
     _gpu.check_sampled("mxfp8", w, D.contiguous(), em, en)
+
+
+@pytest.mark.parametrize("pair", F4_PAIRS, ids=_pid)
+def test_fp8_fp4_packed_edges(pair):
+    """Single rows and columns on the packed path (K % 256 == 0): one output
+    tile whose other rows read zero, and K of one 256-K stage."""
+    for M, N, K in [(1, 1, 256), (1, 300, 512), (300, 1, 512), (2, 3, 256)]:
+        _gpu.say(f"[mixed] packed {_pid(pair)} edge {(M, N, K)}")
+        w = synth.workload("mxfp8", M, N, K, 43, 44, *pair)
+        D = run_mixed(w)
+        torch.cuda.synchronize()
+        _gpu.check_full("mxfp8", w, D)
