@@ -7,10 +7,10 @@ package never imports the product.
 
 The arithmetic lives in ``oracle.c`` (built into ``liboracle.so`` by
 ``oracle/build.py``); this module only marshals numpy arrays.  Kinds:
-0 = BF16, 1 = MXFP8, 2 = MXFP4, 3 = NVFP4, 4 = MX with E5M2 elements.  For
-fmt 'mxfp8' a workload may name each operand's MX element format in
-w['elemA'] / w['elemB'] ('e4m3', the default, 'e5m2', or 'e2m1' packed two
-per byte).
+0 = BF16, 1 = MXFP8, 2 = MXFP4, 3 = NVFP4, 4 / 5 / 6 = MX with E5M2 / E2M3 /
+E3M2 elements.  For fmt 'mxfp8' a workload may name each operand's MX element
+format in w['elemA'] / w['elemB'] ('e4m3', the default, 'e5m2', 'e2m1' packed
+two per byte, or 'e2m3' / 'e3m2' packed four per three bytes).
 """
 from __future__ import annotations
 
@@ -43,10 +43,15 @@ def _load():
     lib.orc_decode_e8m0.restype = ctypes.c_double
     lib.orc_decode_bf16.restype = ctypes.c_double
     lib.orc_decode_e5m2.restype = ctypes.c_double
+    lib.orc_decode_e2m3.restype = ctypes.c_double
+    lib.orc_decode_e3m2.restype = ctypes.c_double
     for f in (lib.orc_decode_e2m1, lib.orc_decode_e4m3, lib.orc_decode_e8m0, lib.orc_decode_bf16,
-              lib.orc_decode_e5m2):
+              lib.orc_decode_e5m2, lib.orc_decode_e2m3, lib.orc_decode_e3m2):
         f.argtypes = [ctypes.c_uint]
-    for f in (lib.orc_encode_e2m1, lib.orc_encode_e4m3, lib.orc_encode_bf16, lib.orc_encode_e5m2):
+    lib.orc_fp6_get.argtypes = [P, I64]
+    lib.orc_fp6_get.restype = ctypes.c_uint
+    for f in (lib.orc_encode_e2m1, lib.orc_encode_e4m3, lib.orc_encode_bf16, lib.orc_encode_e5m2,
+              lib.orc_encode_e2m3, lib.orc_encode_e3m2):
         f.argtypes = [ctypes.c_double]
         f.restype = ctypes.c_uint
     lib.orc_decode_array.argtypes = [ctypes.c_int, P, I64, P]
@@ -92,9 +97,10 @@ def set_mutation(m: int) -> None:
 # ---- formats -------------------------------------------------------------
 
 def decode(fmt: str, codes) -> np.ndarray:
-    """Decode codes to float64: fmt in {'e2m1', 'e4m3', 'e5m2', 'e8m0', 'bf16'}."""
+    """Decode codes to float64: fmt in {'e2m1', 'e4m3', 'e5m2', 'e2m3', 'e3m2', 'e8m0', 'bf16'}
+    (one code per array element)."""
     lib = _load()
-    idx = {"e2m1": 0, "e4m3": 1, "e8m0": 2, "bf16": 3, "e5m2": 4}[fmt]
+    idx = {"e2m1": 0, "e4m3": 1, "e8m0": 2, "bf16": 3, "e5m2": 4, "e2m3": 5, "e3m2": 6}[fmt]
     c = _c(codes, np.uint16 if fmt == "bf16" else np.uint8).ravel()
     out = np.empty(c.size, dtype=np.float64)
     lib.orc_decode_array(idx, _ptr(c), c.size, _ptr(out))
@@ -102,13 +108,26 @@ def decode(fmt: str, codes) -> np.ndarray:
 
 
 def encode(fmt: str, x) -> np.ndarray:
-    """Nearest-even encode of float64 values: fmt in {'e2m1','e4m3','e5m2','bf16'}."""
+    """Nearest-even encode of float64 values: fmt in {'e2m1','e4m3','e5m2','e2m3','e3m2','bf16'}."""
     lib = _load()
-    idx = {"e2m1": 0, "e4m3": 1, "bf16": 3, "e5m2": 4}[fmt]
+    idx = {"e2m1": 0, "e4m3": 1, "bf16": 3, "e5m2": 4, "e2m3": 5, "e3m2": 6}[fmt]
     v = _c(x, np.float64).ravel()
     out = np.empty(v.size, dtype=np.uint16 if fmt == "bf16" else np.uint8)
     lib.orc_encode_array(idx, _ptr(v), v.size, _ptr(out))
     return out.reshape(np.shape(x))
+
+
+def unpack_fp6(packed: np.ndarray, K: int) -> np.ndarray:
+    """(rows, 3K/4) bytes -> (rows, K) FP6 codes, as the oracle reads them."""
+    lib = _load()
+    p = _c(packed, np.uint8)
+    rows = p.shape[0]
+    out = np.empty((rows, K), np.uint8)
+    for r in range(rows):
+        row = np.ascontiguousarray(p[r])
+        for j in range(K):
+            out[r, j] = lib.orc_fp6_get(_ptr(row), j)
+    return out
 
 
 def unpack_fp4(packed: np.ndarray) -> np.ndarray:
@@ -122,7 +141,7 @@ def unpack_fp4(packed: np.ndarray) -> np.ndarray:
 
 # ---- GEMM ----------------------------------------------------------------
 
-_MX8 = {"e4m3": 1, "e5m2": 4, "e2m1": 2}
+_MX8 = {"e4m3": 1, "e5m2": 4, "e2m1": 2, "e2m3": 5, "e3m2": 6}
 
 
 def _operands(fmt, w):
@@ -184,9 +203,11 @@ def quant_mx(x: np.ndarray, elem: str):
     lib = _load()
     x = _c(x, np.float32)
     rows, K = x.shape
-    codes = np.zeros((rows, K // 2 if elem == "e2m1" else K), np.uint8)
+    width = {"e2m1": K // 2, "e2m3": K // 4 * 3, "e3m2": K // 4 * 3}.get(elem, K)
+    codes = np.zeros((rows, width), np.uint8)
     scales = np.zeros((rows, K // 32), np.uint8)
-    if lib.orc_quant_mx({"e2m1": 0, "e4m3": 1, "e5m2": 2}[elem], _ptr(x), rows, K, _ptr(codes), _ptr(scales)):
+    idx = {"e2m1": 0, "e4m3": 1, "e5m2": 2, "e2m3": 3, "e3m2": 4}[elem]
+    if lib.orc_quant_mx(idx, _ptr(x), rows, K, _ptr(codes), _ptr(scales)):
         raise ValueError("bad K")
     return codes, scales
 

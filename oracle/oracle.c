@@ -23,7 +23,8 @@
  *  - The element/scale bit layouts are the OCP Microscaling (MX) v1.0
  *    definitions of E2M1, E4M3 (the "FN" variant: no infinities, S.1111.111 is
  *    NaN, max 448), E5M2 (IEEE-like: bias 15, S.11111.00 infinite, S.11111.xx
- *    NaN otherwise, max 57344) and E8M0 (2^(e-127), 0xFF is NaN); bf16 is the
+ *    NaN otherwise, max 57344), E2M3 and E3M2 (FP6: bias 1 / 3, no
+ *    infinities or NaNs, max 7.5 / 28) and E8M0 (2^(e-127), 0xFF is NaN); bf16 is the
  *    upper half of an IEEE binary32.  The pages name only E4M3 and E2M1; E5M2
  *    is the other MXFP8 element the OCP format defines, and each operand of a
  *    GEMM may carry its own MX element format.
@@ -43,7 +44,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_BF16 = 0, ORC_MXFP8 = 1, ORC_MXFP4 = 2, ORC_NVFP4 = 3, ORC_MXE5M2 = 4 };
+enum { ORC_BF16 = 0, ORC_MXFP8 = 1, ORC_MXFP4 = 2, ORC_NVFP4 = 3, ORC_MXE5M2 = 4, ORC_MXE2M3 = 5, ORC_MXE3M2 = 6 };
 
 enum {
     MUT_NONE = 0,
@@ -59,6 +60,9 @@ enum {
     MUT_BF16_MANT = 11,     /* bf16 mantissa read as 6 bits                    */
     MUT_E5M2_BIAS = 12,     /* E5M2 exponent bias 16 instead of 15             */
     MUT_E5M2_SUBN = 13,     /* E5M2 subnormals read as normals (1.M)            */
+    MUT_E2M3_BIAS = 14,     /* E2M3 exponent bias 2 instead of 1               */
+    MUT_E3M2_SUBN = 15,     /* E3M2 subnormals read as normals (1.M)            */
+    MUT_FP6_ORDER = 16,     /* FP6 codes read from the high end of each group  */
 };
 static int g_mut = MUT_NONE;
 void orc_set_mutation(int m) { g_mut = m; }
@@ -97,6 +101,25 @@ double orc_decode_e5m2(unsigned c)
     if (e == 31) mag = m ? NAN : INFINITY;
     else if (e == 0 && g_mut != MUT_E5M2_SUBN) mag = ldexp(m / 4.0, 1 - bias);   /* 0.M * 2^(1-15) */
     else mag = ldexp(1.0 + m / 4.0, e - bias);                                  /* 1.M * 2^(e-15) */
+    return s ? -mag : mag;
+}
+
+/* FP6 (OCP MX v1.0): no infinities or NaNs.  E2M3: bias 1, max 7.5; E3M2:
+ * bias 3, max 28. */
+double orc_decode_e2m3(unsigned c)
+{
+    c &= 0x3Fu;
+    int s = (c >> 5) & 1, e = (c >> 3) & 3, m = c & 7;
+    int bias = (g_mut == MUT_E2M3_BIAS) ? 2 : 1;
+    double mag = (e == 0) ? ldexp(m / 8.0, 1 - bias) : ldexp(1.0 + m / 8.0, e - bias);
+    return s ? -mag : mag;
+}
+
+double orc_decode_e3m2(unsigned c)
+{
+    c &= 0x3Fu;
+    int s = (c >> 5) & 1, e = (c >> 2) & 7, m = c & 3;
+    double mag = (e == 0 && g_mut != MUT_E3M2_SUBN) ? ldexp(m / 4.0, 1 - 3) : ldexp(1.0 + m / 4.0, e - 3);
     return s ? -mag : mag;
 }
 
@@ -141,6 +164,30 @@ static unsigned encode_nearest(double x, double (*dec)(unsigned), unsigned maxco
 unsigned orc_encode_e2m1(double x) { return encode_nearest(x, orc_decode_e2m1, 0x7, 0x8); }
 unsigned orc_encode_e4m3(double x) { return encode_nearest(x, orc_decode_e4m3, 0x7E, 0x80); }
 unsigned orc_encode_e5m2(double x) { return encode_nearest(x, orc_decode_e5m2, 0x7B, 0x80); }
+unsigned orc_encode_e2m3(double x) { return encode_nearest(x, orc_decode_e2m3, 0x1F, 0x20); }
+unsigned orc_encode_e3m2(double x) { return encode_nearest(x, orc_decode_e3m2, 0x1F, 0x20); }
+
+/* FP6 packing: four consecutive elements of a row in three bytes, element j
+ * of the row at bits 6j .. 6j+5 of the row's bytes read as one little-endian
+ * bit string (the pages define no FP6 layout; this is the plainest one). */
+unsigned orc_fp6_get(const uint8_t *row, int64_t j)
+{
+    if (g_mut == MUT_FP6_ORDER) j = (j & ~(int64_t)3) + (3 - (j & 3));
+    const uint8_t *g = row + (j / 4) * 3;
+    uint32_t bits = (uint32_t)g[0] | ((uint32_t)g[1] << 8) | ((uint32_t)g[2] << 16);
+    return (bits >> (6 * (j % 4))) & 0x3Fu;
+}
+
+static void fp6_put(uint8_t *row, int64_t j, unsigned c)
+{
+    uint8_t *g = row + (j / 4) * 3;
+    uint32_t bits = (uint32_t)g[0] | ((uint32_t)g[1] << 8) | ((uint32_t)g[2] << 16);
+    const int sh = 6 * (int)(j % 4);
+    bits = (bits & ~(0x3Fu << sh)) | ((c & 0x3Fu) << sh);
+    g[0] = (uint8_t)bits;
+    g[1] = (uint8_t)(bits >> 8);
+    g[2] = (uint8_t)(bits >> 16);
+}
 
 /* fp64 -> bf16 bits, round to nearest even (used to state the bit-exact
  * expectation of results that are exactly representable). */
@@ -167,13 +214,16 @@ unsigned orc_encode_bf16(double x)
 
 void orc_decode_array(int fmt, const uint8_t *codes, int64_t n, double *out)
 {
-    /* fmt: 0 = E2M1 (one code per byte), 1 = E4M3, 2 = E8M0, 3 = bf16 (n uint16), 4 = E5M2 */
+    /* fmt: 0 = E2M1 (one code per byte), 1 = E4M3, 2 = E8M0, 3 = bf16 (n uint16), 4 = E5M2,
+     * 5 = E2M3, 6 = E3M2 (one code per byte) */
     for (int64_t i = 0; i < n; ++i) {
         switch (fmt) {
         case 0: out[i] = orc_decode_e2m1(codes[i]); break;
         case 1: out[i] = orc_decode_e4m3(codes[i]); break;
         case 2: out[i] = orc_decode_e8m0(codes[i]); break;
         case 4: out[i] = orc_decode_e5m2(codes[i]); break;
+        case 5: out[i] = orc_decode_e2m3(codes[i]); break;
+        case 6: out[i] = orc_decode_e3m2(codes[i]); break;
         default: out[i] = orc_decode_bf16(((const uint16_t *)codes)[i]); break;
         }
     }
@@ -181,12 +231,15 @@ void orc_decode_array(int fmt, const uint8_t *codes, int64_t n, double *out)
 
 void orc_encode_array(int fmt, const double *x, int64_t n, uint8_t *out)
 {
-    /* fmt: 0 = E2M1 (one code per byte), 1 = E4M3, 3 = bf16 (n uint16), 4 = E5M2 */
+    /* fmt: 0 = E2M1 (one code per byte), 1 = E4M3, 3 = bf16 (n uint16), 4 = E5M2, 5 = E2M3,
+     * 6 = E3M2 */
     for (int64_t i = 0; i < n; ++i) {
         switch (fmt) {
         case 0: out[i] = (uint8_t)orc_encode_e2m1(x[i]); break;
         case 1: out[i] = (uint8_t)orc_encode_e4m3(x[i]); break;
         case 4: out[i] = (uint8_t)orc_encode_e5m2(x[i]); break;
+        case 5: out[i] = (uint8_t)orc_encode_e2m3(x[i]); break;
+        case 6: out[i] = (uint8_t)orc_encode_e3m2(x[i]); break;
         default: ((uint16_t *)out)[i] = (uint16_t)orc_encode_bf16(x[i]); break;
         }
     }
@@ -196,7 +249,7 @@ void orc_encode_array(int fmt, const double *x, int64_t n, uint8_t *out)
 
 typedef struct {
     int kind;
-    const void *X;          /* rows x K elements, K-major (FP4: rows x K/2 bytes) */
+    const void *X;          /* rows x K elements, K-major (FP4: rows x K/2 bytes, FP6: rows x 3K/4) */
     const uint8_t *sX;      /* rows x K/bs scale codes (MX: E8M0, NVFP4: E4M3)    */
     int64_t rows, K;
 } operand;
@@ -221,6 +274,9 @@ static double element(const operand *op, int64_t r, int64_t k)
         v = orc_decode_e4m3(((const uint8_t *)op->X)[r * K + k]);
     } else if (op->kind == ORC_MXE5M2) {
         v = orc_decode_e5m2(((const uint8_t *)op->X)[r * K + k]);
+    } else if (op->kind == ORC_MXE2M3 || op->kind == ORC_MXE3M2) {
+        unsigned c = orc_fp6_get((const uint8_t *)op->X + r * (K / 4 * 3), k);
+        v = op->kind == ORC_MXE2M3 ? orc_decode_e2m3(c) : orc_decode_e3m2(c);
     } else {
         uint8_t byte = ((const uint8_t *)op->X)[r * (K / 2) + k / 2];
         v = orc_decode_e2m1((k & 1) ? (byte >> 4) : (byte & 0xF));
@@ -302,12 +358,15 @@ static void *entries_worker(void *p)
 }
 
 /* Operand kinds a GEMM may pair: equal kinds, or any two MX kinds (E4M3,
- * E5M2 or E2M1 elements, all with E8M0 scales per 32). */
-static int is_mx(int k) { return k == ORC_MXFP8 || k == ORC_MXE5M2 || k == ORC_MXFP4; }
+ * E5M2, E2M3, E3M2 or E2M1 elements, all with E8M0 scales per 32). */
+static int is_mx(int k)
+{
+    return k == ORC_MXFP8 || k == ORC_MXE5M2 || k == ORC_MXFP4 || k == ORC_MXE2M3 || k == ORC_MXE3M2;
+}
 
 static int kinds_ok(int ka, int kb)
 {
-    if (ka < 0 || ka > 4 || kb < 0 || kb > 4) return 0;
+    if (ka < 0 || ka > 6 || kb < 0 || kb > 6) return 0;
     return ka == kb || (is_mx(ka) && is_mx(kb));
 }
 
@@ -316,7 +375,8 @@ static int kinds_ok(int ka, int kb)
  *   kind_a, kind_b : the operands' kinds: 0 bf16 (uint16), 1 MXFP8 (uint8
  *            E4M3 + E8M0 scales), 2 MXFP4 (packed E2M1 + E8M0), 3 NVFP4
  *            (packed E2M1 + E4M3, tA, tB), 4 MX with E5M2 elements (uint8 +
- *            E8M0); see kinds_ok for the pairs
+ *            E8M0), 5 / 6 MX with E2M3 / E3M2 elements (FP6 packed four to
+ *            three bytes + E8M0); see kinds_ok for the pairs
  *   d      : D_ref per entry (alpha applied)
  *   anorm  : ||dA_m||_2 * |tA| per entry (may be NULL)
  *   bnorm  : ||dB_n||_2 * |tB| per entry (may be NULL)
@@ -485,11 +545,16 @@ static int floor_log2_ratio(double amax, double emax)
  * [-127, 127] (code 127 for an all-zero block); elements RNE + saturate.
  * elem: 0 = E2M1 (codes out: rows x K/2 packed), 1 = E4M3 (rows x K),
  * 2 = E5M2 (rows x K; emax 57344, the same recipe with E5M2's largest
- * finite value). */
+ * finite value), 3 = E2M3 / 4 = E3M2 (rows x 3K/4 packed).  The FP6 scales
+ * follow the OCP MX recipe, 2^(floor(log2 amax) - emax) with emax the
+ * element's largest normal exponent (2 / 4), i.e. the ratio to 4 / 16: no
+ * configuration fixes a recipe for them, and this one clips only values in
+ * [7.5, 8) / [28, 32) of the scaled block maximum. */
 int orc_quant_mx(int elem, const float *x, int64_t rows, int64_t K, uint8_t *codes, uint8_t *scales)
 {
-    if (K % 32 || elem < 0 || elem > 2) return -1;
-    double emax = elem == 1 ? 448.0 : elem == 2 ? 57344.0 : 6.0;
+    if (K % 32 || elem < 0 || elem > 4) return -1;
+    const double emaxs[5] = {6.0, 448.0, 57344.0, 4.0, 16.0};
+    double emax = emaxs[elem];
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t b = 0; b < K / 32; ++b) {
             const float *xb = x + r * K + b * 32;
@@ -506,6 +571,8 @@ int orc_quant_mx(int elem, const float *x, int64_t rows, int64_t K, uint8_t *cod
                     codes[r * K + k] = (uint8_t)orc_encode_e4m3(v);
                 } else if (elem == 2) {
                     codes[r * K + k] = (uint8_t)orc_encode_e5m2(v);
+                } else if (elem >= 3) {
+                    fp6_put(codes + r * (K / 4 * 3), k, elem == 3 ? orc_encode_e2m3(v) : orc_encode_e3m2(v));
                 } else {
                     uint8_t c = (uint8_t)orc_encode_e2m1(v);
                     uint8_t *byte = &codes[r * (K / 2) + k / 2];

@@ -36,6 +36,8 @@ __all__ = [
 E4M3_MAX = 448.0
 E5M2_MAX = 57344.0
 E2M1_MAX = 6.0
+E2M3_MAX = 7.5
+E3M2_MAX = 28.0
 
 
 def normal(seed: int, rows: int, cols: int) -> np.ndarray:
@@ -86,7 +88,54 @@ def _round_e2m1(v: np.ndarray) -> np.ndarray:
     return np.copysign(r, v)
 
 
+def _round_grid(v: np.ndarray, mbits: int, emin: int, vmax: float) -> np.ndarray:
+    """Round float64 values to a grid with `mbits` mantissa bits and smallest
+    normal binade 2**emin (subnormals share its spacing), ties to even,
+    saturate at vmax.  Sign kept."""
+    a = np.abs(v)
+    _, e = np.frexp(a)
+    ex = np.maximum(e - 1, emin)
+    q = np.ldexp(1.0, ex - mbits)
+    r = np.minimum(np.rint(a / q) * q, vmax)
+    return np.copysign(r, v)
+
+
 # ---- bit packing of grid values ---------------------------------------------
+
+def _pack_fp6(r: np.ndarray, mbits: int, bias: int) -> np.ndarray:
+    """Grid values -> 6-bit codes (sign in bit 5) of an FP6 format with
+    `mbits` mantissa bits and exponent bias `bias`."""
+    a = np.abs(r)
+    _, e = np.frexp(a)
+    ex = e - 1
+    normal = a >= 2.0 ** (1 - bias)
+    ex_n = np.where(normal, ex, 0)
+    man_n = np.where(normal, np.rint((a / np.ldexp(1.0, ex_n) - 1.0) * 2 ** mbits), 0)
+    code_n = ((ex_n + bias) << mbits) + man_n.astype(np.int64)
+    code_s = np.rint(a / 2.0 ** (1 - bias - mbits)).astype(np.int64)
+    code = np.where(normal, code_n, code_s)
+    code = code | np.where(np.signbit(r), 0x20, 0)
+    return code.astype(np.uint8)
+
+
+def pack_fp6_rows(codes: np.ndarray) -> np.ndarray:
+    """(rows, K) 6-bit codes -> (rows, 3K/4) bytes: element j of a row at bits
+    6j .. 6j+5 of the row's bytes read as one little-endian bit string."""
+    c = codes.astype(np.uint32).reshape(codes.shape[0], -1, 4)
+    g = c[:, :, 0] | (c[:, :, 1] << 6) | (c[:, :, 2] << 12) | (c[:, :, 3] << 18)
+    out = np.stack([g & 0xFF, (g >> 8) & 0xFF, (g >> 16) & 0xFF], axis=2)
+    return out.reshape(codes.shape[0], -1).astype(np.uint8)
+
+
+def unpack_fp6_rows(packed: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of pack_fp6_rows."""
+    b = packed.astype(np.uint32).reshape(packed.shape[0], -1, 3)
+    g = b[:, :, 0] | (b[:, :, 1] << 8) | (b[:, :, 2] << 16)
+    out = np.stack([(g >> (6 * i)) & 0x3F for i in range(4)], axis=2)
+    return out.reshape(packed.shape[0], K).astype(np.uint8)
+
+
+
 
 def _pack_e4m3(r: np.ndarray) -> np.ndarray:
     a = np.abs(r)
@@ -148,14 +197,17 @@ def quant_mx(x: np.ndarray, elem: str) -> tuple[np.ndarray, np.ndarray]:
 
     Returns ``(codes, scales)``: for ``elem='e4m3'`` or ``'e5m2'`` codes are
     (rows, K) uint8; for ``elem='e2m1'`` they are (rows, K/2) uint8 with two
-    elements per byte.
+    elements per byte; for the FP6 ``'e2m3'`` / ``'e3m2'`` (rows, 3K/4) uint8,
+    four elements per three bytes (pack_fp6_rows).
     ``scales`` are (rows, K/32) E8M0 codes.  An all-zero block gets scale code
     127 (1.0) and zero elements.
     """
     rows, K = x.shape
     if K % 32:
         raise ValueError("K must be a multiple of 32 for MX formats")
-    emax = {"e4m3": E4M3_MAX, "e5m2": E5M2_MAX, "e2m1": E2M1_MAX}[elem]
+    # scale reference: the element's largest value, except for FP6, whose
+    # scales follow the OCP recipe 2^(floor(log2 amax) - emax) (emax 2 / 4)
+    emax = {"e4m3": E4M3_MAX, "e5m2": E5M2_MAX, "e2m1": E2M1_MAX, "e2m3": 4.0, "e3m2": 16.0}[elem]
     xb = x.astype(np.float64).reshape(rows, K // 32, 32)
     amax = np.max(np.abs(xb), axis=2)
     e = np.where(amax > 0, _floor_log2_ratio(np.where(amax > 0, amax, 1.0), emax), 0)
@@ -167,6 +219,10 @@ def quant_mx(x: np.ndarray, elem: str) -> tuple[np.ndarray, np.ndarray]:
         codes = _pack_e5m2(_round_e5m2(v)).reshape(rows, K)
     elif elem == "e2m1":
         codes = _pack_nibbles(_pack_e2m1(_round_e2m1(v)).reshape(rows, K))
+    elif elem == "e2m3":
+        codes = pack_fp6_rows(_pack_fp6(_round_grid(v, 3, 0, E2M3_MAX), 3, 1).reshape(rows, K))
+    elif elem == "e3m2":
+        codes = pack_fp6_rows(_pack_fp6(_round_grid(v, 2, -2, E3M2_MAX), 2, 3).reshape(rows, K))
     else:
         raise ValueError(elem)
     return codes, (e + 127).astype(np.uint8)
@@ -204,8 +260,9 @@ def workload(fmt: str, M: int, N: int, K: int, seed_a: int, seed_b: int,
 
     Returns a dict with numpy arrays ``A``, ``B`` (and ``sA``, ``sB``, ``tA``,
     ``tB`` where the format has scales).  A is M x K, B is N x K, K-major.
-    For ``fmt='mxfp8'`` each operand's 8-bit element format is ``elem_a`` /
-    ``elem_b`` ('e4m3' or 'e5m2'), recorded as ``elemA`` / ``elemB``.
+    For ``fmt='mxfp8'`` each operand's MX element format is ``elem_a`` /
+    ``elem_b`` ('e4m3', 'e5m2', 'e2m1', 'e2m3' or 'e3m2'), recorded as
+    ``elemA`` / ``elemB``.
     """
     xa = normal(seed_a, M, K)
     xb = normal(seed_b, N, K)
