@@ -36,12 +36,14 @@ sys.path.insert(0, str(ROOT))
 
 LLC_BYTES = 256 * 2 ** 20                      # MI355X Infinity Cache (MALL)
 PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "mxfp4": 10100.0, "nvfp4": 2500.0, "nvfp4_fp8": 5000.0,
-               "mx_e4m3_e2m1": 5000.0}
+               "mx_e4m3_e2m1": 5000.0, "mx_e2m3_e2m3": 5000.0}
 PEAK_NOTE = {"nvfp4": "exact NVFP4 runs on fp16 MFMA: priced at the bf16/fp16 dense peak",
              "nvfp4_fp8": "opt-in lossy FP8-rate NVFP4 (gemm_nvfp4_fp8): requantisation to MXFP8 plus the MXFP8 "
                           "GEMM, both inside the timed launch; priced at the fp8 dense peak",
              "mx_e4m3_e2m1": "E4M3 A x E2M1 B (gemm_mx_mixed, packed E2M1 on the MFMA's mixed formats): "
-                             "priced at the fp8 dense peak, the rate its MFMAs run at"}
+                             "priced at the fp8 dense peak, the rate its MFMAs run at",
+             "mx_e2m3_e2m3": "MXFP6 (E2M3 both sides, gemm_mx): widened to E4M3 on the way into LDS and "
+                             "multiplied at the fp8 rate; priced at the fp8 dense peak"}
 HBM_GBS = 8000.0
 ELEM_BITS = {"bf16": 16, "mxfp8": 8, "mxfp4": 4, "nvfp4": 4}
 BLOCK = {"bf16": 0, "mxfp8": 32, "mxfp4": 32, "nvfp4": 16}
@@ -56,11 +58,13 @@ CONFIGS = {
     "nvfp4_fp8": (4, 8192, 8192, 8192),
     "nvfp4_fp8_skinny": (4, 256, 16384, 8192),
     "mx_e4m3_e2m1": (2, 8192, 8192, 8192),
+    "mx_e2m3_e2m3": (2, 8192, 8192, 8192),
 }
 # MX element formats of A and B where they differ from the format's own
-MX_ELEMS = {"mx_e4m3_e2m1": ("e4m3", "e2m1")}
+MX_ELEMS = {"mx_e4m3_e2m1": ("e4m3", "e2m1"), "mx_e2m3_e2m3": ("e2m3", "e2m3")}
 # the encoding each workload's inputs take, and the entry point it times
-INPUT_FMT = {"bf16_4096": "bf16", "nvfp4_skinny": "nvfp4", "nvfp4_fp8": "nvfp4", "nvfp4_fp8_skinny": "nvfp4", "mx_e4m3_e2m1": "mxfp8"}
+INPUT_FMT = {"bf16_4096": "bf16", "nvfp4_skinny": "nvfp4", "nvfp4_fp8": "nvfp4", "nvfp4_fp8_skinny": "nvfp4", "mx_e4m3_e2m1": "mxfp8",
+             "mx_e2m3_e2m3": "mxfp8"}
 KERNEL_OF = {"bf16_4096": "bf16", "nvfp4_skinny": "nvfp4", "nvfp4_fp8_skinny": "nvfp4_fp8"}
 
 
@@ -83,8 +87,9 @@ def algorithmic_bytes(fmt, M, N, K):
     """A + B + scales + D, each moved once, for workload (or format) fmt."""
     base = input_fmt(fmt)
     ea, eb = MX_ELEMS.get(fmt, (None, None))
-    bits_a = 4 if ea == "e2m1" else ELEM_BITS[base]
-    bits_b = 4 if eb == "e2m1" else ELEM_BITS[base]
+    sub_bits = {"e2m1": 4, "e2m3": 6, "e3m2": 6}
+    bits_a = sub_bits.get(ea, ELEM_BITS[base])
+    bits_b = sub_bits.get(eb, ELEM_BITS[base])
     b = (M * bits_a + N * bits_b) * K // 8 + M * N * 2
     if BLOCK[base]:
         b += (M + N) * (K // BLOCK[base])
@@ -298,7 +303,7 @@ def main():
     if not args.only:
         per = []
         for f in ["bf16", "bf16_4096", "mxfp8", "mxfp4", "nvfp4", "nvfp4_skinny", "nvfp4_fp8", "nvfp4_fp8_skinny",
-                  "mx_e4m3_e2m1"]:
+                  "mx_e4m3_e2m1", "mx_e2m3_e2m3"]:
             if f == fmt:
                 entry_t, entry_gbs, entry_avg = tflops, gbs, avg
                 wf = w

@@ -29,14 +29,14 @@ import torch
 
 __all__ = ["gemm_bf16", "gemm_mx", "gemm_mx_mixed", "gemm_nvfp4", "gemm_nvfp4_fp8", "nvfp4_fp8_workspace_bytes", "gemm_grouped_bf16", "gemm_grouped_mx", "gemm_grouped_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError",
            "DBS_OK", "DBS_EINVAL", "DBS_EUNSUPPORTED", "DBS_EHIP", "K_MAJOR", "MN_MAJOR",
-           "E4M3", "E5M2", "E2M1", "status_str"]
+           "E4M3", "E5M2", "E2M3", "E3M2", "E2M1", "status_str"]
 
 LIB_PATH = Path(__file__).resolve().parent / "libdbs.so"
 
 DBS_OK, DBS_EINVAL, DBS_EUNSUPPORTED, DBS_EHIP = 0, 1, 2, 3
 K_MAJOR, MN_MAJOR = 0, 1
-E4M3, E5M2, E2M1 = 0, 1, 4
-_ELEM = {"e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1}
+E4M3, E5M2, E2M3, E3M2, E2M1 = 0, 1, 2, 3, 4
+_ELEM = {"e4m3": E4M3, "e5m2": E5M2, "e2m3": E2M3, "e3m2": E3M2, "e2m1": E2M1}
 
 
 class DbsError(RuntimeError):
@@ -160,26 +160,30 @@ def gemm_bf16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
 def gemm_mx(elem: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor,
             K: int | None = None, out: torch.Tensor | None = None,
             la: int = K_MAJOR, lb: int = K_MAJOR) -> torch.Tensor:
-    """MXFP8 (elem='e4m3' or 'e5m2') or MXFP4 (elem='e2m1') GEMM with E8M0
-    scales per 32."""
+    """MXFP8 (elem='e4m3' or 'e5m2'), MXFP6 (elem='e2m3' or 'e3m2', K-major)
+    or MXFP4 (elem='e2m1') GEMM with E8M0 scales per 32."""
     return gemm_mx_mixed(elem, elem, A, sA, B, sB, K=K, out=out, la=la, lb=lb)
 
 
 def gemm_mx_mixed(elem_a: str, elem_b: str, A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor,
                   sB: torch.Tensor, K: int | None = None, out: torch.Tensor | None = None,
                   la: int = K_MAJOR, lb: int = K_MAJOR) -> torch.Tensor:
-    """MX GEMM with A's elements in elem_a and B's in elem_b ('e4m3', 'e5m2'
-    or 'e2m1'; the library takes 8-bit pairs in any mix and E2M1 with E2M1)."""
+    """MX GEMM with A's elements in elem_a and B's in elem_b ('e4m3', 'e5m2',
+    'e2m1', or the FP6 'e2m3' / 'e3m2', four elements per three bytes; the
+    library takes every pairing except FP6 with E2M1, FP6 K-major only)."""
     code_a, code_b = _ELEM[elem_a], _ELEM[elem_b]
     la, lb = _layout(la, "la"), _layout(lb, "lb")
-    pa_ = 2 if elem_a == "e2m1" else 1   # elements per byte
+    fp6 = ("e2m3", "e3m2")
+    if (elem_a in fp6 and la != K_MAJOR) or (elem_b in fp6 and lb != K_MAJOR):
+        raise ValueError("FP6 operands are K-major only")
+    pa_ = 2 if elem_a == "e2m1" else 1   # elements per byte (FP6: 4 per 3, K-major)
     pb_ = 2 if elem_b == "e2m1" else 1
     M, N = _rows(A, la, pa_), _rows(B, lb, pb_)
     if K is None:
-        K = A.shape[1] * pa_ if la == K_MAJOR else A.shape[0]
+        K = (A.shape[1] * 4 // 3 if elem_a in fp6 else A.shape[1] * pa_) if la == K_MAJOR else A.shape[0]
     u8 = (torch.uint8,)
-    pa = _dev(A, "A", u8, _shape(M, K, la, pa_))
-    pb = _dev(B, "B", u8, _shape(N, K, lb, pb_))
+    pa = _dev(A, "A", u8, (M, K // 4 * 3) if elem_a in fp6 else _shape(M, K, la, pa_))
+    pb = _dev(B, "B", u8, (N, K // 4 * 3) if elem_b in fp6 else _shape(N, K, lb, pb_))
     psa = _dev(sA, "sA", u8, (M, K // 32))
     psb = _dev(sB, "sB", u8, (N, K // 32))
     out = _out(out, M, N, A)

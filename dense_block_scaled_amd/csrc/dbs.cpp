@@ -113,11 +113,12 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     p.sld = block ? (int)(K / block) : 0;
     p.lay = (la == DBS_MN_MAJOR ? 1 : 0) | (lb == DBS_MN_MAJOR ? 2 : 0);
     // (an E2M1 operand of an 8-bit kernel, cv: K-rows of M / 2 or N / 2 bytes)
-    p.ldam = (int)((cv & 1) ? M / 2 : M * elem_bits / 8);
-    p.ldbm = (int)((cv & 2) ? N / 2 : N * elem_bits / 8);
+    p.ldam = (int)((cv & 3) == 1 ? M / 2 : M * elem_bits / 8);
+    p.ldbm = (int)((cv >> 2) == 1 ? N / 2 : N * elem_bits / 8);
     p.ec = ec;
     p.cv = cv;
-    p.ldc = (int)(K / 2);
+    // rows of a widened operand: E2M1 K/2 bytes, FP6 3K/4
+    p.ldc = (int)(((cv & 3) >= 2 || (cv >> 2) >= 2) ? K / 4 * 3 : K / 2);
     // square tiles unless they would fill at most half of the CUs
     auto tiles_of = [&](int64_t rows, int64_t tm_, int64_t tn_) { return ((rows + tm_ - 1) / tm_) * ((N + tn_ - 1) / tn_); };
     int64_t sq_tiles = 0;
@@ -127,7 +128,10 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     } else {
         sq_tiles = tiles_of(M, dbs::kSquareTM, dbs::kSquareTN);
     }
-    const int shape = 2 * sq_tiles <= cus ? dbs::kShapeSkinny : dbs::kShapeSquare;
+    // FP6 operands (widened through registers) run on 256 x 64 tiles: on
+    // 256 x 256 tiles their staging registers spill
+    const bool fp6 = (cv & 3) >= 2 || (cv >> 2) >= 2;
+    const int shape = (2 * sq_tiles <= cus || fp6) ? dbs::kShapeSkinny : dbs::kShapeSquare;
     const int tm = shape == dbs::kShapeSkinny ? dbs::kSkinnyTM : dbs::kSquareTM;
     const int tn = shape == dbs::kShapeSkinny ? dbs::kSkinnyTN : dbs::kSquareTN;
     p.tiles_m = (int)((M + tm - 1) / tm);
@@ -167,7 +171,18 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
 // The f8f6f4 MFMA format code of an 8-bit MX element (0 E4M3, 1 E5M2).
 int mx8_code(dbs_mx_elem e) { return e == DBS_E5M2 ? 1 : 0; }
 
-bool mx_elem_known(dbs_mx_elem e) { return e == DBS_E4M3 || e == DBS_E5M2 || e == DBS_E2M1; }
+bool mx_elem_known(dbs_mx_elem e)
+{
+    return e == DBS_E4M3 || e == DBS_E5M2 || e == DBS_E2M1 || e == DBS_E2M3 || e == DBS_E3M2;
+}
+
+bool is_fp6(dbs_mx_elem e) { return e == DBS_E2M3 || e == DBS_E3M2; }
+
+// An operand that the 8-bit kernels widen on its way into LDS: its source
+// code (1 E2M1, 2 E2M3, 3 E3M2; 0 for E4M3 / E5M2) and the MFMA code of the
+// 8-bit format it is widened to (E2M1, E2M3 -> E4M3; E3M2 -> E5M2).
+int cv_source(dbs_mx_elem e) { return e == DBS_E2M1 ? 1 : e == DBS_E2M3 ? 2 : e == DBS_E3M2 ? 3 : 0; }
+int mfma8_code(dbs_mx_elem e) { return (e == DBS_E5M2 || e == DBS_E3M2) ? 1 : 0; }
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
@@ -214,11 +229,18 @@ dbs_status gemm_mx_mixed(dbs_mx_elem elem_a, dbs_mx_elem elem_b, const void *A, 
     dbs_status st = check_common(A, B, D, M, N, K, la, lb, int64_t(1) << 22);
     if (st != DBS_OK) return st;
     if (K % 32) return fail(DBS_EINVAL, "mx: K must be a multiple of 32");
-    // an E2M1 operand beside an 8-bit one is widened to E4M3 inside the
-    // 8-bit kernel (exact: every E2M1 value is an E4M3 value)
     const bool fp4_a = elem_a == DBS_E2M1, fp4_b = elem_b == DBS_E2M1;
-    const int cv = fp4_a != fp4_b ? (fp4_a ? 1 : 2) : 0;
-    const int ec = fp4_a && fp4_b ? 0 : (fp4_a ? 0 : mx8_code(elem_a)) | ((fp4_b ? 0 : mx8_code(elem_b)) << 3);
+    const bool fp6_a = is_fp6(elem_a), fp6_b = is_fp6(elem_b);
+    if ((fp4_a && fp6_b) || (fp6_a && fp4_b))
+        return fail(DBS_EUNSUPPORTED, "mx: E2M1 with an FP6 operand is not implemented");
+    if ((fp6_a || fp6_b) && (la != DBS_K_MAJOR || lb != DBS_K_MAJOR))
+        return fail(DBS_EUNSUPPORTED, "mx: FP6 operands are K-major only");
+    // E2M1 x E2M1 is the MXFP4 kernel; otherwise the 8-bit kernels, where an
+    // E2M1 or FP6 operand is widened to the 8-bit format that holds its
+    // values exactly (cv, per operand) and E2M1 beside an 8-bit operand goes
+    // packed to the MFMA when K % 256 == 0 (the kernels pick)
+    const int cv = fp4_a && fp4_b ? 0 : cv_source(elem_a) | (cv_source(elem_b) << 2);
+    const int ec = fp4_a && fp4_b ? 0 : mfma8_code(elem_a) | (mfma8_code(elem_b) << 3);
     if (cv != 0 && (la != DBS_K_MAJOR || lb != DBS_K_MAJOR) && K % 256)
         return fail(DBS_EUNSUPPORTED, "mx: 8-bit x E2M1 pairs with an MN-major operand need K % 256 == 0");
     const int bits = fp4_a && fp4_b ? 4 : 8;
@@ -303,6 +325,7 @@ dbs_status quant_mx(dbs_mx_elem elem, const float *x, int64_t rows, int64_t K, v
                     hipStream_t stream)
 {
     if (!mx_elem_known(elem)) return fail(DBS_EINVAL, "mx: unknown element format");
+    if (is_fp6(elem)) return fail(DBS_EUNSUPPORTED, "quant_mx: FP6 elements are not implemented");
     dbs_status st = check_quant(x, codes, rows, K, 32);
     if (st != DBS_OK) return st;
     if (!scales) return fail(DBS_EINVAL, "null pointer argument");
@@ -372,6 +395,7 @@ dbs_status gemm_grouped_mx(dbs_mx_elem elem, const void *A, const uint8_t *sA, c
                            void *D, const int64_t *offsets, int64_t G, int64_t N, int64_t K, hipStream_t stream)
 {
     if (!mx_elem_known(elem)) return fail(DBS_EINVAL, "mx: unknown element format");
+    if (is_fp6(elem)) return fail(DBS_EUNSUPPORTED, "grouped mx: FP6 elements are not implemented");
     if (!sA || !sB) return fail(DBS_EINVAL, "null pointer argument");
     int64_t M = 0;
     dbs_status st = check_groups(offsets, G, &M);
@@ -414,6 +438,6 @@ const char *dbs_status_str(dbs_status st)
 
 const char *dbs_last_error(void) { return g_err; }
 
-int dbs_version(void) { return 101; }
+int dbs_version(void) { return 102; }
 
 }  // extern "C"

@@ -187,17 +187,22 @@ __device__ __forceinline__ TileRef tile_ref(int tile, const Params &p)
 // (K x N); a slot of an MN-major operand holds the same bytes as a K-major
 // one, arranged as the stage's K-rows (see Mn below).  EC: the 8-bit MX
 // element formats as gfx950's f8f6f4 MFMA codes, A in bits 0..2 and B in
-// bits 3..5 (0 = E4M3, 1 = E5M2); both formats take the same bytes and
-// fragments, only the MFMA's format fields differ.  CV (8-bit MX kernels):
-// bit 0 set if A arrives as E2M1, bit 1 if B does; such an operand is
-// widened to E4M3 on its way into LDS (see load_cv), so the MFMAs see E4M3.
+// bits 3..5 (0 = E4M3, 1 = E5M2, 4 = E2M1 packed: see F4Pos); E4M3 and E5M2
+// take the same bytes and fragments, only the MFMA's format fields differ.
+// CV (8-bit MX kernels): the source element of an operand that arrives as
+// E2M1 or FP6 (E2M3, E3M2) and is widened on its way into LDS (see load_cv)
+// to the 8-bit format holding all its values exactly (E2M1, E2M3 -> E4M3;
+// E3M2 -> E5M2), which is what the MFMAs then see.
 constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
 
 template <int TM_, int TN_, int WM_, int WN_, int NS_ = 2, int LAY_ = 0, int EC_ = 0, int CV_ = 0>
 struct Shape {
     static constexpr int TM = TM_, TN = TN_, WM = WM_, WN = WN_, NS = NS_, LAY = LAY_, EC = EC_, CV = CV_;
     static constexpr bool AMN = (LAY & 1) != 0, BMN = (LAY & 2) != 0;
-    static constexpr bool ACV = (CV & 1) != 0, BCV = (CV & 2) != 0;
+    // widened operands: source element of A (bits 0..1) and B (bits 2..3):
+    // 0 none, 1 E2M1, 2 E2M3, 3 E3M2
+    static constexpr int ASRC = CV & 3, BSRC = (CV >> 2) & 3;
+    static constexpr bool ACV = ASRC != 0, BCV = BSRC != 0;
     static constexpr int CA = EC & 7, CB = (EC >> 3) & 7;
     // an E2M1 operand (code 4) of an 8-bit kernel, staged as packed codes
     static constexpr bool AF4 = CA == 4, BF4 = CB == 4;
@@ -1033,14 +1038,15 @@ __device__ __forceinline__ void decode_fp4_a(f16x8 (&a)[S::MB][4], const Fp4A<S>
 
 // ------------------------------------------- E2M1 operands of 8-bit GEMMs
 
-// An E2M1 operand paired with an E4M3 / E5M2 one: a 128-element stage row is
-// 64 packed bytes, i.e. four 16-byte pieces; the concatenated piece list (the
-// widened operands' rows, A's first) is split over the threads, thread t
-// taking pieces t, t + threads, ...  Each piece (32 elements, one E8M0
-// block) is loaded into registers and written to LDS as the 32 E4M3 codes
-// of the same values -- every E2M1 value is an E4M3 value, so the widening
-// is exact and the MX scales stay as they are -- into logical chunks 2p and
-// 2p + 1 of its row of the E4M3 slot.
+// An E2M1 or FP6 operand paired with an E4M3 / E5M2 one (or FP6 with FP6): a
+// 128-element stage row is four pieces of 32 elements (one E8M0 block each):
+// 16 packed bytes (E2M1) or 24 (FP6, four elements per three bytes).  The
+// concatenated piece list (the widened operands' rows, A's first) is split
+// over the threads, thread t taking pieces t, t + threads, ...  Each piece is
+// loaded into registers and written to LDS as the 32 codes of the same
+// values in the 8-bit format that holds them all exactly (E2M1 and E2M3 in
+// E4M3, E3M2 in E5M2), so the MX scales stay as they are -- into logical
+// chunks 2p and 2p + 1 of its row of the 8-bit slot.
 template <class S>
 constexpr int cv_rows() { return (S::ACV ? S::TM : 0) + (S::BCV ? S::TN : 0); }
 
@@ -1051,9 +1057,14 @@ constexpr int cv_units() { return (4 * cv_rows<S>() + S::kThreads - 1) / S::kThr
 template <class S, int KK>
 constexpr int cv_group(int g) { return g >= KK ? cv_units<S>() : g * ((cv_units<S>() + KK - 1) / KK) < cv_units<S>() ? g * ((cv_units<S>() + KK - 1) / KK) : cv_units<S>(); }
 
+// dwords per piece: 4 (E2M1) or 6 (FP6); both widened operands of an FP6 x
+// FP6 kernel have FP6 pieces
+template <class S>
+constexpr int cv_words() { return (S::ASRC >= 2 || S::BSRC >= 2) ? 6 : 4; }
+
 template <class S>
 struct CvRegs {
-    i32x4 v[cv_units<S>() > 0 ? cv_units<S>() : 1];
+    uint32_t v[cv_units<S>() > 0 ? cv_units<S>() : 1][cv_words<S>()];
 };
 
 // Units K0 .. K1-1 of the thread's pieces (a stage's pieces go in groups, one
@@ -1063,6 +1074,7 @@ template <class S, int K0, int K1>
 __device__ __forceinline__ void load_cv(CvRegs<S> &r, const Target &tg, int ks, const Ctx<S> &c, int ldc)
 {
     constexpr int TA = S::ACV ? S::TM : 0;   // A rows in the list
+    constexpr int W = cv_words<S>(), PB = 4 * W;  // dwords and bytes per piece
 #pragma unroll
     for (int k = K0; k < K1; ++k) {
         const int u0 = c.w * 64 + k * S::kThreads;   // wave-uniform: 4 TM is a multiple of 64
@@ -1070,10 +1082,24 @@ __device__ __forceinline__ void load_cv(CvRegs<S> &r, const Target &tg, int ks, 
             const bool is_a = u0 < 4 * TA;
             const int pu = u0 + c.lane - (is_a ? 0 : 4 * TA);
             const int row = pu >> 2, piece = pu & 3;
-            // rows are K/2 bytes, K % 32 == 0: a piece is all in or all out
-            const uint32_t pad = ks * 64 + piece * 16 < ldc ? 0u : kOOB;
-            r.v[k] = __builtin_amdgcn_raw_buffer_load_b128(is_a ? tg.ra : tg.rb, (uint32_t)(row * ldc + piece * 16) | pad,
-                                                           (uint32_t)(ks * 64), 0);
+            // rows are K PB / 32 bytes, K % 32 == 0: a piece is all in or all out
+            const uint32_t pad = ks * 4 * PB + piece * PB < ldc ? 0u : kOOB;
+            const uint32_t off = (uint32_t)(row * ldc + piece * PB) | pad;
+            const __amdgpu_buffer_rsrc_t rs = is_a ? tg.ra : tg.rb;
+            if constexpr (W == 4) {
+                const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, (uint32_t)(ks * 4 * PB), 0);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) r.v[k][q] = (uint32_t)v[q];
+            } else {
+                // three 8-byte loads (pieces start on 8-byte boundaries)
+#pragma unroll
+                for (int q = 0; q < 3; ++q) {
+                    const u32x2 v = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 8u * q, (uint32_t)(ks * 4 * PB), 0));
+                    r.v[k][2 * q] = v[0];
+                    r.v[k][2 * q + 1] = v[1];
+                }
+            }
         }
     }
 }
@@ -1094,6 +1120,35 @@ __device__ __forceinline__ u32x2 widen8(uint32_t w)
     return u32x2{(uint32_t)lo, (uint32_t)hi};
 }
 
+// 32 FP6 codes (six dwords, element j at bits 6j..) -> their 32 codes in
+// E4M3 (SRC 2: E2M3) or E5M2 (SRC 3: E3M2): the hardware's exact decode to
+// fp16, then its 8-bit encoding of values the 8-bit format holds exactly.
+template <int SRC>
+__device__ __forceinline__ void widen32_fp6(const uint32_t (&w)[6], uint32_t (&out)[8])
+{
+    typedef __attribute__((ext_vector_type(6))) unsigned int u32x6;
+    typedef __attribute__((ext_vector_type(32))) _Float16 f16x32;
+    typedef __attribute__((ext_vector_type(2))) short i16x2;
+    const u32x6 src = {w[0], w[1], w[2], w[3], w[4], w[5]};
+    f16x32 h;
+    if constexpr (SRC == 2)
+        h = __builtin_amdgcn_cvt_scalef32_pk32_f16_fp6(src, 1.0f);
+    else
+        h = __builtin_amdgcn_cvt_scalef32_pk32_f16_bf6(src, 1.0f);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+        i16x2 r = {0, 0};
+        if constexpr (SRC == 2) {
+            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, f16x2{h[4 * d], h[4 * d + 1]}, 1.0f, false);
+            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, f16x2{h[4 * d + 2], h[4 * d + 3]}, 1.0f, true);
+        } else {
+            r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f16(r, f16x2{h[4 * d], h[4 * d + 1]}, 1.0f, false);
+            r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f16(r, f16x2{h[4 * d + 2], h[4 * d + 3]}, 1.0f, true);
+        }
+        out[d] = __builtin_bit_cast(uint32_t, r);
+    }
+}
+
 template <class S, int K0, int K1>
 __device__ __forceinline__ void store_cv(const CvRegs<S> &r, uint8_t *lds, int slot, const Ctx<S> &c)
 {
@@ -1106,12 +1161,25 @@ __device__ __forceinline__ void store_cv(const CvRegs<S> &r, uint8_t *lds, int s
             const int pu = u0 + c.lane - (is_a ? 0 : 4 * TA);
             const int row = pu >> 2, piece = pu & 3;
             uint8_t *base = lds + (is_a ? S::kLdsA + slot * S::kSlotA : S::kLdsB + slot * S::kSlotB);
-            const u32x2 e0 = widen8((uint32_t)r.v[k][0]), e1 = widen8((uint32_t)r.v[k][1]);
-            const u32x2 e2 = widen8((uint32_t)r.v[k][2]), e3 = widen8((uint32_t)r.v[k][3]);
+            uint32_t e[8];
+            if constexpr (cv_words<S>() == 4) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x2 t = widen8(r.v[k][q]);
+                    e[2 * q] = t[0];
+                    e[2 * q + 1] = t[1];
+                }
+            } else if constexpr (S::ASRC == S::BSRC || !S::ACV || !S::BCV) {
+                widen32_fp6<S::ACV ? S::ASRC : S::BSRC>(r.v[k], e);
+            } else {
+                // E2M3 on one side, E3M2 on the other (wave-uniform choice)
+                if (is_a) widen32_fp6<S::ASRC>(r.v[k], e);
+                else widen32_fp6<S::BSRC>(r.v[k], e);
+            }
             *reinterpret_cast<i32x4 *>(base + lds_off(row, 2 * piece)) =
-                i32x4{(int)e0[0], (int)e0[1], (int)e1[0], (int)e1[1]};
+                i32x4{(int)e[0], (int)e[1], (int)e[2], (int)e[3]};
             *reinterpret_cast<i32x4 *>(base + lds_off(row, 2 * piece + 1)) =
-                i32x4{(int)e2[0], (int)e2[1], (int)e3[0], (int)e3[1]};
+                i32x4{(int)e[4], (int)e[5], (int)e[6], (int)e[7]};
         }
     }
 }
@@ -1869,13 +1937,30 @@ hipError_t launch_cv(const Params &p0, int grid, hipStream_t stream)
     Params p = p0;
     p.nk = (p.K + stage_elems<kMXFP8, S0>() - 1) / stage_elems<kMXFP8, S0>();
     if (p.lay != 0) return hipErrorInvalidValue;
-    switch (p.cv * 16 + p.ec) {
-    case 16 + 0: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 0, 1>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
-    case 16 + 8: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 8, 1>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
-    case 32 + 0: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 0, 2>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
-    case 32 + 1: hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, 1, 2>, SM>), dim3(grid), dim3(S0::kThreads), 0, stream, p); break;
-    default: return hipErrorInvalidValue;
+#define DBS_CV(CVV, ECV) \
+    case (CVV) * 64 + (ECV): \
+        hipLaunchKernelGGL((gemm_kernel<kMXFP8, WithLayout<S0, 0, ECV, CVV>, SM>), dim3(grid), dim3(S0::kThreads), 0, \
+                           stream, p); \
+        break;
+    if constexpr (std::is_same<S0, SquareW4>::value) {
+        // (FP6 operands run on 256 x 64 tiles: the host picks them)
+        switch (p.cv * 64 + p.ec) {
+            // E2M1 beside E4M3 / E5M2
+            DBS_CV(1, 0) DBS_CV(1, 8) DBS_CV(4, 0) DBS_CV(4, 1)
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (p.cv * 64 + p.ec) {
+            DBS_CV(1, 0) DBS_CV(1, 8) DBS_CV(4, 0) DBS_CV(4, 1)
+            // E2M3 (widened to E4M3) / E3M2 (to E5M2) beside E4M3 / E5M2
+            DBS_CV(2, 0) DBS_CV(2, 8) DBS_CV(3, 1) DBS_CV(3, 9)
+            DBS_CV(8, 0) DBS_CV(8, 1) DBS_CV(12, 8) DBS_CV(12, 9)
+            // FP6 x FP6
+            DBS_CV(10, 0) DBS_CV(14, 8) DBS_CV(11, 1) DBS_CV(15, 9)
+        default: return hipErrorInvalidValue;
+        }
     }
+#undef DBS_CV
     return hipGetLastError();
 }
 
@@ -1888,7 +1973,7 @@ hipError_t launch_f4(const Params &p0, int grid, hipStream_t stream)
     Params p = p0;
     p.nk = p.K / stage_elems<kMXFP8, S0>();
     if (p.K % 256 != 0) return hipErrorInvalidValue;
-    const int ca = p.cv & 1 ? 4 : p.ec & 7, cb = p.cv & 2 ? 4 : (p.ec >> 3) & 7;
+    const int ca = p.cv == 1 ? 4 : p.ec & 7, cb = p.cv == 4 ? 4 : (p.ec >> 3) & 7;
     switch (ca | (cb << 3)) {
     case 4: return launch_ec_lay<4, SM, S0>(p, grid, stream);
     case 12: return launch_ec_lay<12, SM, S0>(p, grid, stream);
@@ -1903,7 +1988,8 @@ hipError_t launch_f4(const Params &p0, int grid, hipStream_t stream)
 template <class S>
 hipError_t launch_fp8_fp4(const Params &p, int grid, hipStream_t stream)
 {
-    if (p.cv != 0 && p.K % 256 == 0) {
+    const bool e2m1 = p.cv == 1 || p.cv == 4;   // (an FP6 operand is always widened)
+    if (e2m1 && p.K % 256 == 0) {
         // FP8 x FP4 on the MFMA's mixed formats: the E2M1 operand in its
         // own ring of packed 256-K stages
         if (!p.scales_aligned) {

@@ -83,10 +83,16 @@ typedef enum {
 
 /* MX element formats; the values equal gfx950's f8f6f4 MFMA format codes.
  * E5M2 (OCP MX v1.0: bias 15, two mantissa bits, infinities and NaNs) is the
- * other 8-bit element of the OCP format; the pages name E4M3 and E2M1. */
+ * other 8-bit element of the OCP format; E2M3 (bias 1, max 7.5) and E3M2
+ * (bias 3, max 28) are its FP6 elements, neither with infinities or NaNs;
+ * the pages name E4M3 and E2M1.  FP6 rows pack four elements into three
+ * bytes: element j of a row at bits 6j .. 6j+5 of the row's bytes read as
+ * one little-endian bit string. */
 typedef enum {
     DBS_E4M3 = 0,
     DBS_E5M2 = 1,
+    DBS_E2M3 = 2,
+    DBS_E3M2 = 3,
     DBS_E2M1 = 4
 } dbs_mx_elem;
 
@@ -99,9 +105,10 @@ dbs_status gemm_bf16(const void *A, const void *B, void *D,
                      dbs_layout la, dbs_layout lb, hipStream_t stream);
 
 /*
- * MX GEMM (MXFP8 for elem = DBS_E4M3 or DBS_E5M2, MXFP4 for elem = DBS_E2M1):
- * elements of A and B in `elem`, E8M0 scales sA (M x K/32), sB (N x K/32).
- * K must be a multiple of 32, at most 2^22.
+ * MX GEMM (MXFP8 for elem = DBS_E4M3 or DBS_E5M2, MXFP6 for DBS_E2M3 or
+ * DBS_E3M2, MXFP4 for elem = DBS_E2M1): elements of A and B in `elem`, E8M0
+ * scales sA (M x K/32), sB (N x K/32).  K must be a multiple of 32, at most
+ * 2^22.  MXFP6 runs on the widening path of gemm_mx_mixed (K-major only).
  */
 dbs_status gemm_mx(dbs_mx_elem elem,
                    const void *A, const uint8_t *sA,
@@ -112,7 +119,11 @@ dbs_status gemm_mx(dbs_mx_elem elem,
 /*
  * MX GEMM with an element format per operand: A's elements in elem_a, B's in
  * elem_b, otherwise as gemm_mx (gemm_mx(e, ...) is gemm_mx_mixed(e, e, ...)).
- * Every pairing of E4M3, E5M2 and E2M1 is taken.  gfx950's scaled MFMA
+ * Every pairing of E4M3, E5M2 and E2M1 is taken, and FP6 (E2M3, E3M2) with
+ * E4M3, E5M2 or FP6, K-major only: an FP6 operand is widened on its way into
+ * LDS to the 8-bit format that holds its values exactly (E2M3 -> E4M3, E3M2 ->
+ * E5M2) and multiplied at the 8-bit rate.  FP6 with E2M1 returns
+ * DBS_EUNSUPPORTED.  gfx950's scaled MFMA
  * takes a format code per operand, so 8-bit pairs run at the 8-bit rate on
  * MXFP8's staging.  An E2M1 operand beside an 8-bit one (FP8 x FP4) goes to
  * the MFMA as packed E2M1 (its format code) when K is a multiple of 256, and

@@ -21,6 +21,7 @@ import numpy as np
 import torch
 
 import oracle
+import synth
 
 GOLDEN = Path(__file__).resolve().parent / "golden"
 
@@ -127,6 +128,8 @@ def make_w_mx8(elem_a, elem_b, M, N, K, rng, scale_lo=0, scale_hi=254, narrow=Fa
             w[X] = random_e5m2(rows, K, rng, (10, 21) if narrow else (0, 31))
         elif el == "e2m1":
             w[X] = random_codes("mxfp4", rows, K, rng)["X"]
+        elif el in ("e2m3", "e3m2"):
+            w[X] = synth.pack_fp6_rows(rng.integers(0, 64, (rows, K), dtype=np.uint8))
         else:
             w[X] = random_codes("mxfp8", rows, K, rng)["X"]
         w["s" + X] = rng.integers(scale_lo, scale_hi + 1, (rows, K // 32)).astype(np.uint8)

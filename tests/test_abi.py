@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = dbs.lib()
     for name in _declared():
         assert hasattr(L, name), name
-    assert L.dbs_version() == 101
+    assert L.dbs_version() == 102
 
 
 def test_status_strings():
@@ -71,7 +71,11 @@ def test_mx_validation(elem, K, want):
     (0, 4, (1, 0), 2),          # E4M3 x E2M1 MN-major with K % 256 != 0: not implemented
     (4, 1, (0, 1), 2),          # E2M1 x E5M2 MN-major
     (1, 1, (1, 0), 2),          # E5M2 MN-major, M * 8 bits not whole 16-byte K-rows (M = 40)
-    (2, 0, (0, 0), 1),          # unknown element code
+    (2, 4, (0, 0), 2),          # E2M3 x E2M1: not implemented
+    (4, 3, (0, 0), 2),
+    (2, 0, (1, 0), 2),          # FP6 MN-major: not implemented
+    (0, 3, (0, 1), 2),
+    (5, 0, (0, 0), 1),          # unknown element code
     (1, 7, (0, 0), 1),
 ])
 def test_mx_mixed_validation(ea, eb, lay, want):

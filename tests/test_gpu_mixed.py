@@ -319,3 +319,64 @@ def test_fp8_fp4_packed_edges(pair):
         D = run_mixed(w)
         torch.cuda.synchronize()
         _gpu.check_full("mxfp8", w, D)
+
+
+FP6_PAIRS = [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2"), ("e3m2", "e4m3"), ("e4m3", "e2m3"),
+             ("e5m2", "e3m2"), ("e2m3", "e5m2")]
+# FP6 runs on 256 x 64 tiles: register-staged scales (K = 352), per-stage
+# scales (K = 512), a square-ish problem with many tiles per workgroup
+FP6_SHAPES = [(300, 520, 352), (256, 4000, 512), (1000, 1100, 1024)]
+
+
+@pytest.mark.parametrize("pair", FP6_PAIRS, ids=_pid)
+@pytest.mark.parametrize("shape", FP6_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fp6_matches_oracle(shape, pair):
+    M, N, K = shape
+    _gpu.say(f"[mixed] fp6 {_pid(pair)} {shape}")
+    w = synth.workload("mxfp8", M, N, K, 540 + M % 19, 640 + N % 17, *pair)
+    D = run_mixed(w)
+    torch.cuda.synchronize()
+    _gpu.check_full("mxfp8", w, D)
+
+
+@pytest.mark.parametrize("pair", FP6_PAIRS, ids=_pid)
+def test_fp6_random_codes(pair):
+    """All 64 codes of each FP6 format with random non-unit scales."""
+    _gpu.say(f"[mixed] fp6 {_pid(pair)} random codes")
+    w = _pins.make_w_mx8(*pair, 300, 280, 256, np.random.default_rng(31), scale_lo=112, scale_hi=142)
+    D = run_mixed(w)
+    torch.cuda.synchronize()
+    _gpu.check_full("mxfp8", w, D)
+
+
+@pytest.mark.parametrize("pair", FP6_PAIRS, ids=_pid)
+def test_fp6_exact_permutation(pair):
+    """A times a permutation matrix in elem_b with non-unit scales, bit for bit:
+    every output is one decoded FP6 (or 8-bit) element of A times two powers
+    of two."""
+    ea, eb = pair
+    M, K = 300, 512
+    N = K
+    _gpu.say(f"[mixed] fp6 {_pid(pair)} exact permutation")
+    rng = np.random.default_rng(47)
+    w = _pins.make_w_mx8(ea, eb, M, N, K, rng, scale_lo=110, scale_hi=140)
+    pi = rng.permutation(K)
+    one = {"e5m2": 0x3C, "e4m3": 0x38, "e2m3": 0x08, "e3m2": 0x0C}[eb]
+    codes = np.zeros((N, K), np.uint8)
+    codes[np.arange(N), pi] = one
+    w["B"] = synth.pack_fp6_rows(codes) if eb in ("e2m3", "e3m2") else codes
+    w["sB"] = rng.integers(118, 137, (N, K // 32)).astype(np.uint8)
+    D = run_mixed(w)
+    torch.cuda.synchronize()
+    _gpu.check_exact("mxfp8", w, D)
+
+
+def test_fp6_edges():
+    """Single rows and columns, K of one block."""
+    for (M, N, K), pair in [((1, 1, 32), ("e2m3", "e2m3")), ((1, 300, 64), ("e3m2", "e4m3")),
+                            ((300, 1, 96), ("e4m3", "e3m2"))]:
+        _gpu.say(f"[mixed] fp6 {_pid(pair)} edge {(M, N, K)}")
+        w = synth.workload("mxfp8", M, N, K, 45, 46, *pair)
+        D = run_mixed(w)
+        torch.cuda.synchronize()
+        _gpu.check_full("mxfp8", w, D)

@@ -28,6 +28,8 @@ KINDS = [
     ("mxfp8", ("e5m2", "e4m3"), 32, 16),          # E5M2 pairs take MN-major operands
     ("mxfp8", ("e4m3", "e2m1"), 256, 32),         # FP8 x FP4 packed path (K % 256 == 0), any layout
     ("mxfp8", ("e2m1", "e5m2"), 256, 32),
+    ("mxfp8", ("e2m3", "e3m2"), 32, None),       # FP6 (widened, K-major)
+    ("mxfp8", ("e3m2", "e4m3"), 32, None),
 ]
 CASES = [(i, k) for k in range(len(KINDS)) for i in range(6)]
 
