@@ -12,7 +12,7 @@
  * 1.2 and 2.1).  Formats (bit layouts per the OCP Microscaling v1.0 spec):
  *
  *   gemm_bf16   BF16 elements, no scales, alpha = 1
- *   gemm_mx     E4M3, E5M2 or E2M1 elements, one E8M0 scale per 32 K elements, alpha = 1
+ *   gemm_mx     E4M3, E5M2, E2M3, E3M2 or E2M1 elements, one E8M0 scale per 32 K elements, alpha = 1
  *   gemm_nvfp4  E2M1 elements, one E4M3 scale per 16 K elements, alpha = tA * tB
  *
  * Memory (all pointers are DEVICE pointers; dense, no leading dimensions):
