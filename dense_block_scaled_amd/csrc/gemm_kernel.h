@@ -238,6 +238,9 @@ using SkinnyDeep = Shape<kSkinnyTM, kSkinnyTN, 8, 1, 3>;
 // the register-staged scale bytes do not fit beside two waves per SIMD, so
 // this variant runs one wave per SIMD, each owning 128 x 128.
 using SquareW4 = Shape<kSquareTM, kSquareTN, 2, 2>;
+// 256 x 64 tiles with 8 waves of 32 x 64 on a two-slot ring: FP6 operands,
+// widened through registers, with two waves per SIMD to hide their loads.
+using SkinnyW8 = Shape<kSkinnyTM, kSkinnyTN, 8, 1>;
 
 // Shape S with operand layouts LAY, 8-bit MX element codes EC and widened
 // E2M1 operands CV.
@@ -2006,6 +2009,11 @@ hipError_t launch_fp8_fp4(const Params &p, int grid, hipStream_t stream)
         if constexpr (std::is_same<S, Square>::value) {
             return launch_cv<kScalesRegs, SquareW4>(p, grid, stream);
         } else {
+            if (!e2m1) {
+                // FP6 (the host puts it on these tiles)
+                if (p.scales_aligned) return launch_cv<kScalesStage, SkinnyW8>(p, grid, stream);
+                return launch_cv<kScalesRegs, SkinnyW8>(p, grid, stream);
+            }
             if (p.scales_aligned) return launch_cv<kScalesStage, S>(p, grid, stream);
             return launch_cv<kScalesRegs, S>(p, grid, stream);
         }
