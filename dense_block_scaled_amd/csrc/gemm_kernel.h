@@ -76,7 +76,7 @@ namespace dbs {
 hipError_t launch_gemm_bf16(int shape, const Params &p, int grid, hipStream_t stream);
 hipError_t launch_gemm_mxfp8(int shape, const Params &p, int grid, hipStream_t stream);
 hipError_t launch_gemm_mx8_e5m2(int shape, const Params &p, int grid, hipStream_t stream);
-hipError_t launch_gemm_mx8_fp4(int shape, const Params &p, int grid, hipStream_t stream);
+hipError_t launch_gemm_mx8_fp4(int shape, const Params &p, int grid, hipStream_t stream);   // E2M1 or FP6 beside 8-bit
 hipError_t launch_gemm_mxfp4(int shape, const Params &p, int grid, hipStream_t stream);
 hipError_t launch_gemm_nvfp4(int shape, const Params &p, int grid, hipStream_t stream);
 hipError_t launch_gemm_nvfp4_raw(int shape, const Params &p, int grid, hipStream_t stream);
@@ -1928,11 +1928,13 @@ hipError_t launch_one(const Params &p0, int grid, hipStream_t stream)
 template <int FMT, class S>
 constexpr int stages_of(int K) { return (K + stage_elems<FMT, S>() - 1) / stage_elems<FMT, S>(); }
 
-// 8-bit MX GEMMs with a widened E2M1 operand (K-major): its register-staged
-// pieces do not fit beside the 8-wave square kernel's fragments (the
-// compiler spills 160+ registers there), so square problems run on the
-// one-wave-per-SIMD tiles; scale rows take the register-staged path there and
-// on unaligned skinny problems.
+// 8-bit MX GEMMs with a widened E2M1 or FP6 operand (K-major; cv names the
+// sources, see Shape).  The register-staged pieces do not fit beside the
+// 8-wave square kernel's fragments (the compiler spills 160+ registers
+// there): E2M1 runs square problems on the one-wave-per-SIMD tiles, FP6
+// (whose pieces spill even there) only on 256 x 64 tiles, which the host
+// picks for it.  Scale rows take the register-staged path on the square tiles
+// and on unaligned skinny problems.
 template <int SM, class S0>
 hipError_t launch_cv(const Params &p0, int grid, hipStream_t stream)
 {
@@ -1986,8 +1988,8 @@ hipError_t launch_f4(const Params &p0, int grid, hipStream_t stream)
     }
 }
 
-// 8-bit MX GEMMs with an E2M1 operand (cv != 0): the packed path when K %
-// 256 == 0, else the widening path.
+// 8-bit MX GEMMs with an E2M1 or FP6 operand (cv != 0): E2M1 takes the
+// packed path when K % 256 == 0, everything else the widening path.
 template <class S>
 hipError_t launch_fp8_fp4(const Params &p, int grid, hipStream_t stream)
 {
