@@ -244,12 +244,13 @@ def gemm_nvfp4_fp8(A: torch.Tensor, sA: torch.Tensor, tA: float, B: torch.Tensor
 
 def quant_mx(elem: str, x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
     """fp32 x (rows, K) -> (codes, E8M0 scales per 32): codes (rows, K) uint8
-    for elem='e4m3' or 'e5m2', (rows, K/2) packed for elem='e2m1'; scales
-    (rows, K/32)."""
+    for elem='e4m3' or 'e5m2', (rows, K/2) packed for elem='e2m1', (rows,
+    3K/4) packed for the FP6 'e2m3' / 'e3m2'; scales (rows, K/32)."""
     code = _ELEM[elem]
     rows, K = x.shape
     px = _dev(x, "x", (torch.float32,), (rows, K))
-    codes = torch.empty((rows, K // 2 if elem == "e2m1" else K), dtype=torch.uint8, device=x.device)
+    width = {"e2m1": K // 2, "e2m3": K // 4 * 3, "e3m2": K // 4 * 3}.get(elem, K)
+    codes = torch.empty((rows, width), dtype=torch.uint8, device=x.device)
     scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
     _check(lib().quant_mx(code, px, rows, K, ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
                           _stream(x)))

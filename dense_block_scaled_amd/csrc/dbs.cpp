@@ -329,14 +329,14 @@ dbs_status quant_mx(dbs_mx_elem elem, const float *x, int64_t rows, int64_t K, v
                     hipStream_t stream)
 {
     if (!mx_elem_known(elem)) return fail(DBS_EINVAL, "mx: unknown element format");
-    if (is_fp6(elem)) return fail(DBS_EUNSUPPORTED, "quant_mx: FP6 elements are not implemented");
     dbs_status st = check_quant(x, codes, rows, K, 32);
     if (st != DBS_OK) return st;
     if (!scales) return fail(DBS_EINVAL, "null pointer argument");
     int cus = 0;
     if ((st = device_cus(&cus)) != DBS_OK) return st;
-    hipError_t e = dbs::launch_quant_mx(elem == DBS_E2M1 ? 4 : 8, elem == DBS_E5M2, x, rows * K,
-                                        static_cast<uint8_t *>(codes), scales, cus, stream);
+    // the quantiser's element codes: 0 E2M1, 1 E4M3, 2 E5M2, 3 E2M3, 4 E3M2
+    const int qe = elem == DBS_E2M1 ? 0 : elem == DBS_E4M3 ? 1 : elem == DBS_E5M2 ? 2 : elem == DBS_E2M3 ? 3 : 4;
+    hipError_t e = dbs::launch_quant_mx(qe, x, rows * K, static_cast<uint8_t *>(codes), scales, cus, stream);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
     g_err[0] = '\0';
     return DBS_OK;

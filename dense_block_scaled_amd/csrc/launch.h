@@ -59,8 +59,8 @@ hipError_t launch_gemm(int fmt, int shape, const Params &p, int grid, hipStream_
 // blocks (n a multiple of 32 for MX, 16 for NVFP4, 8 for bf16); x, codes and
 // out 16-byte aligned.  NVFP4 uses *t as the tensor-amax accumulator and
 // leaves the tensor scale there.
-hipError_t launch_quant_mx(int elem_bits, bool e5m2, const float *x, int64_t n, uint8_t *codes, uint8_t *scales,
-                           int cus, hipStream_t stream);
+hipError_t launch_quant_mx(int elem, const float *x, int64_t n, uint8_t *codes, uint8_t *scales, int cus,
+                           hipStream_t stream);
 hipError_t launch_quant_nvfp4(const float *x, int64_t n, uint8_t *codes, uint8_t *scales, float *t, int cus,
                               hipStream_t stream);
 // NVFP4 operand of n elements (packed E2M1 codes, E4M3 scales per 16; n a

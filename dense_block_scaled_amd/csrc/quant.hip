@@ -83,6 +83,25 @@ __device__ __forceinline__ uint32_t enc_e2m1_abs(float a)
     return 4u + (uint32_t)__builtin_rintf(a * 0.5f);                    // 2..3 -> codes 6..7
 }
 
+// |x| rounded to the nearest FP6 code (0..0x1F), ties to even, saturating:
+// MB mantissa bits, smallest normal exponent EMIN (subnormal steps of
+// 2^(EMIN - MB)), bias 1 - EMIN, largest value VMAX (OCP MX v1.0 E2M3: MB 3,
+// EMIN 0, max 7.5; E3M2: MB 2, EMIN -2, max 28).
+template <int MB, int EMIN>
+__device__ __forceinline__ uint32_t enc_fp6_abs(float a, float vmax)
+{
+    if (a >= vmax) return 0x1Fu;
+    int E;
+    (void)__builtin_frexpf(a, &E);
+    const int e = a < __builtin_ldexpf(1.0f, EMIN) ? EMIN : E - 1;
+    const float v = __builtin_rintf(__builtin_ldexpf(a, MB - e));      // grid units of 2^(e-MB)
+    if (e == EMIN && v < (float)(1 << MB)) return (uint32_t)v;        // subnormal (or zero)
+    const int ee = v >= (float)(2 << MB) ? e + 1 : e;
+    const uint32_t m = v >= (float)(2 << MB) ? 0u : (uint32_t)v - (1u << MB);
+    const uint32_t code = ((uint32_t)(ee + 1 - EMIN) << MB) | m;
+    return code > 0x1Fu ? 0x1Fu : code;
+}
+
 __device__ __forceinline__ uint32_t sign_of(float x) { return __builtin_bit_cast(uint32_t, x) >> 31; }
 
 __device__ __forceinline__ uint32_t enc_e4m3(float x) { return (sign_of(x) << 7) | enc_e4m3_abs(__builtin_fabsf(x)); }
@@ -90,7 +109,15 @@ __device__ __forceinline__ uint32_t enc_e2m1(float x) { return (sign_of(x) << 3)
 __device__ __forceinline__ uint32_t enc_e5m2(float x) { return (sign_of(x) << 7) | enc_e5m2_abs(__builtin_fabsf(x)); }
 
 // Element formats of the MX quantiser.
-constexpr int kQE2M1 = 0, kQE4M3 = 1, kQE5M2 = 2;
+constexpr int kQE2M1 = 0, kQE4M3 = 1, kQE5M2 = 2, kQE2M3 = 3, kQE3M2 = 4;
+
+template <int ELEM>
+__device__ __forceinline__ uint32_t enc_fp6(float x)
+{
+    const float a = __builtin_fabsf(x);
+    const uint32_t c = ELEM == kQE2M3 ? enc_fp6_abs<3, 0>(a, 7.5f) : enc_fp6_abs<2, -2>(a, 28.0f);
+    return (sign_of(x) << 5) | c;
+}
 
 // E4M3 code (finite, non-negative) -> its fp32 value.
 __device__ __forceinline__ float dec_e4m3_pos(uint32_t c)
@@ -111,7 +138,8 @@ __device__ __forceinline__ float group_max(float v)
 
 // e = floor(log2(amax / emax)) for amax > 0, exactly: amax = f 2^E with f in
 // [1, 2) (frexp gives f/2 in [0.5, 1)); emax = 1.75 * 2^8 (E4M3), 1.75 *
-// 2^15 (E5M2) or 1.5 * 2^2 (E2M1).
+// 2^15 (E5M2) or 1.5 * 2^2 (E2M1).  FP6 follows the OCP recipe
+// floor(log2 amax) - emax with emax = 2 (E2M3) or 4 (E3M2).
 template <int ELEM>
 __device__ __forceinline__ int mx_exponent(float amax)
 {
@@ -120,6 +148,8 @@ __device__ __forceinline__ int mx_exponent(float amax)
     --E;
     if constexpr (ELEM == kQE4M3) return E - 8 - (f < 1.75f ? 1 : 0);
     if constexpr (ELEM == kQE5M2) return E - 15 - (f < 1.75f ? 1 : 0);
+    if constexpr (ELEM == kQE2M3) return E - 2;
+    if constexpr (ELEM == kQE3M2) return E - 4;
     return E - 2 - (f < 1.5f ? 1 : 0);
 }
 
@@ -147,7 +177,20 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const float *__restrict__
             y[i] = __builtin_ldexpf(v0[i], -e);
             y[4 + i] = __builtin_ldexpf(v1[i], -e);
         }
-        if constexpr (ELEM != kQE2M1) {
+        if constexpr (ELEM == kQE2M3 || ELEM == kQE3M2) {
+            // eight 6-bit codes = 48 bits: bytes 6 l .. 6 l + 5 of the row
+            // stream (element j at bits 6j..), written as three halfwords
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo |= enc_fp6<ELEM>(y[i]) << (6 * i);
+                hi |= enc_fp6<ELEM>(y[4 + i]) << (6 * i);
+            }
+            uint16_t *o = reinterpret_cast<uint16_t *>(codes + 6 * l);
+            o[0] = (uint16_t)lo;
+            o[1] = (uint16_t)((lo >> 16) | (hi << 8));
+            o[2] = (uint16_t)(hi >> 8);
+        } else if constexpr (ELEM != kQE2M1) {
             uint32_t lo = 0, hi = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -312,17 +355,19 @@ int grid_for(int64_t lanes, int cus)
 
 }  // namespace
 
-hipError_t launch_quant_mx(int elem_bits, bool e5m2, const float *x, int64_t n, uint8_t *codes, uint8_t *scales,
-                           int cus, hipStream_t stream)
+hipError_t launch_quant_mx(int elem, const float *x, int64_t n, uint8_t *codes, uint8_t *scales, int cus,
+                           hipStream_t stream)
 {
     const int64_t lanes = n / 8;
     const int grid = grid_for(lanes, cus);
-    if (elem_bits == 4)
-        hipLaunchKernelGGL(quant_mx_kernel<kQE2M1>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes);
-    else if (e5m2)
-        hipLaunchKernelGGL(quant_mx_kernel<kQE5M2>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes);
-    else
-        hipLaunchKernelGGL(quant_mx_kernel<kQE4M3>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes);
+    switch (elem) {
+    case kQE2M1: hipLaunchKernelGGL(quant_mx_kernel<kQE2M1>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes); break;
+    case kQE4M3: hipLaunchKernelGGL(quant_mx_kernel<kQE4M3>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes); break;
+    case kQE5M2: hipLaunchKernelGGL(quant_mx_kernel<kQE5M2>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes); break;
+    case kQE2M3: hipLaunchKernelGGL(quant_mx_kernel<kQE2M3>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes); break;
+    case kQE3M2: hipLaunchKernelGGL(quant_mx_kernel<kQE3M2>, dim3(grid), dim3(256), 0, stream, x, codes, scales, lanes); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

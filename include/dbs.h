@@ -213,7 +213,9 @@ dbs_status gemm_grouped_nvfp4(const void *A, const uint8_t *sA, float tA, const 
  *   rows x K/2 packed bytes (E2M1,
  *   element 2j in the low nibble); scales: rows x K/32 bytes.  The scale rule
  *   follows the MX scale definition (OCP MX v1.0) with the workloads'
- *   floor(log2(amax / emax)) exponent.
+ *   floor(log2(amax / emax)) exponent.  FP6 (DBS_E2M3, DBS_E3M2): e =
+ *   floor(log2(amax)) - 2 (E2M3) or - 4 (E3M2), the OCP recipe; codes rows x
+ *   3K/4 packed bytes (see dbs_mx_elem).
  * quant_nvfp4: K a multiple of 16.  t (device, one float, out) = amax /
  *   (6 * 448) over the whole array (1 if it is all zero); per block of 16 the
  *   E4M3 scale s = nearest(amax_block / (6 t)); each element the nearest E2M1

@@ -38,6 +38,12 @@ def _special_rows(K: int, emax: float) -> np.ndarray:
     r = np.resize(mids, K).astype(np.float32)
     r[0::32] = emax
     rows.append(r)
+    # FP6 grid midpoints: E2M3 (steps 0.125 / 0.25 / 0.5) and E3M2 (0.0625 ... 4)
+    mids6 = np.array([1.0625, 1.1875, 4.25, 4.75, 0.0625, 0.1875, 7.25, 7.75, 1.125, 1.375, 0.03125, 0.09375,
+                      18.0, 22.0, 26.0, 30.0, -0.1875, -26.0], np.float32)
+    r = np.resize(mids6, K).astype(np.float32)
+    r[0::32] = emax
+    rows.append(r)
     r = np.resize(mids, K).astype(np.float32) * np.float32(2.0 ** -7)
     r[0::32] = emax * 2.0 ** -7
     rows.append(r)
@@ -53,7 +59,8 @@ def _inputs(K: int, emax: float):
     return np.concatenate([x, _special_rows(K, emax)])
 
 
-@pytest.mark.parametrize("elem,emax", [("e4m3", 448.0), ("e5m2", 57344.0), ("e2m1", 6.0)])
+@pytest.mark.parametrize("elem,emax", [("e4m3", 448.0), ("e5m2", 57344.0), ("e2m1", 6.0), ("e2m3", 7.5),
+                                       ("e3m2", 28.0)])
 @pytest.mark.parametrize("K", [32, 1024])
 def test_quant_mx_matches_oracle(elem, emax, K):
     _gpu.say(f"[quant] mx {elem} K={K}")
@@ -128,5 +135,19 @@ def test_quantise_e5m2_then_mixed_gemm():
     D = dbs.gemm_mx_mixed("e5m2", "e4m3", ca, sa, cb, sb, K=512)
     torch.cuda.synchronize()
     w = {"fmt": "mxfp8", "M": 260, "N": 300, "K": 512, "elemA": "e5m2", "elemB": "e4m3",
+         "A": ca.cpu().numpy(), "sA": sa.cpu().numpy(), "B": cb.cpu().numpy(), "sB": sb.cpu().numpy()}
+    _gpu.check_full("mxfp8", w, D)
+
+
+def test_quantise_fp6_then_gemm():
+    """FP6 codes and scales from the GPU quantiser feed the FP6 GEMM; the
+    product matches the oracle on the same codes."""
+    _gpu.say("[quant] e2m3 x e3m2 quantise then GEMM")
+    xa, xb = synth.normal(81, 260, 512), synth.normal(82, 300, 512)
+    ca, sa = dbs.quant_mx("e2m3", torch.from_numpy(xa).cuda())
+    cb, sb = dbs.quant_mx("e3m2", torch.from_numpy(xb).cuda())
+    D = dbs.gemm_mx_mixed("e2m3", "e3m2", ca, sa, cb, sb, K=512)
+    torch.cuda.synchronize()
+    w = {"fmt": "mxfp8", "M": 260, "N": 300, "K": 512, "elemA": "e2m3", "elemB": "e3m2",
          "A": ca.cpu().numpy(), "sA": sa.cpu().numpy(), "B": cb.cpu().numpy(), "sB": sb.cpu().numpy()}
     _gpu.check_full("mxfp8", w, D)
