@@ -1065,6 +1065,11 @@ constexpr int cv_group(int g) { return g >= KK ? cv_units<S>() : g * ((cv_units<
 template <class S>
 constexpr int cv_words() { return (S::ASRC >= 2 || S::BSRC >= 2) ? 6 : 4; }
 
+// The 8-wave 256 x 64 tile has the registers for all of a stage's pieces at
+// once: loaded at the stage's start, written to LDS at its end.
+template <class S>
+constexpr bool cv_early() { return S::NW == 8 && S::TN == 64; }
+
 template <class S>
 struct CvRegs {
     uint32_t v[cv_units<S>() > 0 ? cv_units<S>() : 1][cv_words<S>()];
@@ -1430,7 +1435,7 @@ __device__ __forceinline__ void commit_stage(Pipe<FMT, S> &P, uint8_t *lds, int 
     if constexpr (S::ACV || S::BCV) {
         // the last phase group (ALL: every group, loaded together in the prologue)
         constexpr int KK = kk_of<FMT, S>();
-        store_cv<S, ALL ? 0 : cv_group<S, KK>(KK - 1), cv_units<S>()>(P.cv, lds, slot, c);
+        store_cv<S, (ALL || cv_early<S>()) ? 0 : cv_group<S, KK>(KK - 1), cv_units<S>()>(P.cv, lds, slot, c);
     }
 }
 
@@ -1524,10 +1529,16 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
     }
     if constexpr (mx_scales<FMT>() && PH == 1) adjust_scales<FMT>(P.scur, c);
     if constexpr ((S::ACV || S::BCV) && LOADS) {
-        // widened E2M1 pieces: the previous group to LDS, this phase's group from memory
         constexpr int KK = kk_of<FMT, S>();
-        if constexpr (PH > 0) store_cv<S, cv_group<S, KK>(PH - 1), cv_group<S, KK>(PH)>(P.cv, lds, lslot, c);
-        load_cv<S, cv_group<S, KK>(PH), cv_group<S, KK>(PH + 1)>(P.cv, tg, ks, c, p.ldc);
+        if constexpr (cv_early<S>()) {
+            // every piece of the next stage from memory now, all to LDS at
+            // the stage's end: a whole stage for the loads to land
+            if constexpr (PH == 0) load_cv<S, 0, cv_units<S>()>(P.cv, tg, ks, c, p.ldc);
+        } else {
+            // widened pieces: the previous group to LDS, this phase's group from memory
+            if constexpr (PH > 0) store_cv<S, cv_group<S, KK>(PH - 1), cv_group<S, KK>(PH)>(P.cv, lds, lslot, c);
+            load_cv<S, cv_group<S, KK>(PH), cv_group<S, KK>(PH + 1)>(P.cv, tg, ks, c, p.ldc);
+        }
     }
     DBS_FENCE();
     if constexpr (FMT == kNVFP4R) {
