@@ -1965,14 +1965,19 @@ hipError_t launch_cv(const Params &p0, int grid, hipStream_t stream)
             DBS_CV(1, 0) DBS_CV(1, 8) DBS_CV(4, 0) DBS_CV(4, 1)
         default: return hipErrorInvalidValue;
         }
-    } else {
+    } else if constexpr (std::is_same<S0, SkinnyW8>::value) {
+        // FP6 only (E2M1 widens on the 4-wave 256 x 64 tile)
         switch (p.cv * 64 + p.ec) {
-            DBS_CV(1, 0) DBS_CV(1, 8) DBS_CV(4, 0) DBS_CV(4, 1)
             // E2M3 (widened to E4M3) / E3M2 (to E5M2) beside E4M3 / E5M2
             DBS_CV(2, 0) DBS_CV(2, 8) DBS_CV(3, 1) DBS_CV(3, 9)
             DBS_CV(8, 0) DBS_CV(8, 1) DBS_CV(12, 8) DBS_CV(12, 9)
             // FP6 x FP6
             DBS_CV(10, 0) DBS_CV(14, 8) DBS_CV(11, 1) DBS_CV(15, 9)
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (p.cv * 64 + p.ec) {
+            DBS_CV(1, 0) DBS_CV(1, 8) DBS_CV(4, 0) DBS_CV(4, 1)
         default: return hipErrorInvalidValue;
         }
     }
