@@ -63,6 +63,9 @@ enum {
     MUT_E2M3_BIAS = 14,     /* E2M3 exponent bias 2 instead of 1               */
     MUT_E3M2_SUBN = 15,     /* E3M2 subnormals read as normals (1.M)            */
     MUT_FP6_ORDER = 16,     /* FP6 codes read from the high end of each group  */
+    MUT_FP6_SCALE = 17,     /* FP6 scale by floor(log2(amax / largest value))  */
+    MUT_NV_S16_TRUNC = 18,  /* NVFP4 block scale rounded toward zero           */
+    MUT_E5M2_EMAX = 19,     /* E5M2 scale recipe with E4M3's largest value     */
 };
 static int g_mut = MUT_NONE;
 void orc_set_mutation(int m) { g_mut = m; }
@@ -555,6 +558,8 @@ int orc_quant_mx(int elem, const float *x, int64_t rows, int64_t K, uint8_t *cod
     if (K % 32 || elem < 0 || elem > 4) return -1;
     const double emaxs[5] = {6.0, 448.0, 57344.0, 4.0, 16.0};
     double emax = emaxs[elem];
+    if (g_mut == MUT_FP6_SCALE && elem >= 3) emax = elem == 3 ? 7.5 : 28.0;
+    if (g_mut == MUT_E5M2_EMAX && elem == 2) emax = 448.0;
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t b = 0; b < K / 32; ++b) {
             const float *xb = x + r * K + b * 32;
@@ -603,6 +608,7 @@ int orc_quant_nvfp4(const float *x, int64_t rows, int64_t K, uint8_t *codes, uin
             float six_t = six * t;
             float v = ab / six_t;
             uint8_t sc = (uint8_t)orc_encode_e4m3((double)v);
+            if (g_mut == MUT_NV_S16_TRUNC && orc_decode_e4m3(sc) > (double)v && sc > 0) --sc;
             scales[r * (K / 16) + b] = sc;
             float denom = (float)orc_decode_e4m3(sc) * t;
             for (int i = 0; i < 16; ++i) {
