@@ -1320,33 +1320,6 @@ constexpr int stage_loads_min()
     return S::QA + S::QB + (NSC + S::NW - 1) / S::NW;
 }
 
-// Wait states between a tile's last MFMAs and any read of their results.
-// Without them the generated code can copy a scaled MFMA's result
-// (v_mfma_scale_f32_32x32x64_f8f6f4) out of its AGPRs in the very next
-// instruction and get a stale value (observed on MI355X: exactly the first
-// register copied of each last-issued block was wrong).  The empty asm
-// statements pin every accumulator block in the register class the MFMAs
-// write (AGPRs with one wave per SIMD, VGPRs with two), so the MFMAs write in
-// place and every copy or read comes after the 16 x 8 = 128 wait cycles,
-// which cover the longest MFMA here.  Once per tile; the cost is negligible.
-template <class S>
-__device__ __forceinline__ void mfma_drain(f32x16 (&acc)[S::MB][S::NB])
-{
-    DBS_FENCE();
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
-                 "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::);
-#pragma unroll
-    for (int i = 0; i < S::MB; ++i)
-#pragma unroll
-        for (int j = 0; j < S::NB; ++j) {
-            if constexpr (S::NW == 8)
-                asm volatile("" : "+v"(acc[i][j]));
-            else
-                asm volatile("" : "+a"(acc[i][j]));
-        }
-    DBS_FENCE();
-}
-
 // State threaded through the stage function.
 template <int FMT, class S>
 struct Pipe {
@@ -1829,7 +1802,6 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
             rs = rs + 1 == S::NS ? 0 : rs + 1;
         }
         phase<FMT, S, SM, 0, false, false>(acc, P, lds, p, c, 0, ld, 0, 0, stg, cp, fp);
-        mfma_drain<S>(acc);
 
         const TileRef tr = tile_ref<S::TM, S::TN>(tile, p);
         // (the one-wave-per-SIMD variant has no registers to spare for the

@@ -257,7 +257,6 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_raw_kernel(Params p)
             d = d1;      // four sub-stages advance the index by 4 = 1 (mod 3)
             rs = ns;
         }
-        mfma_drain<S>(acc);
         store_tile<S>(acc, p, tile_ref<S::TM, S::TN>(tile, p), c);
         // the raw-stage waits count loads; keep the stores out of them
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

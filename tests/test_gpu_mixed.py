@@ -323,8 +323,8 @@ def test_fp8_fp4_packed_edges(pair):
 
 FP6_PAIRS = [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2"), ("e3m2", "e4m3"), ("e4m3", "e2m3"),
              ("e5m2", "e3m2"), ("e2m3", "e5m2")]
-# FP6 runs on 256 x 64 tiles: register-staged scales (K = 352), per-stage
-# scales (K = 512), a square-ish problem with many tiles per workgroup
+# FP6: register-staged scales (K = 352), per-stage scales (K = 512), a
+# square-ish problem (72 tiles of 256 x 64, one per workgroup)
 FP6_SHAPES = [(300, 520, 352), (256, 4000, 512), (1000, 1100, 1024)]
 
 
@@ -337,6 +337,56 @@ def test_fp6_matches_oracle(shape, pair):
     D = run_mixed(w)
     torch.cuda.synchronize()
     _gpu.check_full("mxfp8", w, D)
+
+
+@pytest.mark.parametrize("pair", FP6_PAIRS, ids=_pid)
+def test_fp6_many_tiles_per_workgroup(pair):
+    """More output tiles than CUs (1024 x 4160: 4 x 65 = 260 tiles of
+    256 x 64), so workgroups run a second tile whose first stages were loaded
+    during the first one's last."""
+    M, N, K = 1024, 4160, 256
+    _gpu.say(f"[mixed] fp6 {_pid(pair)} {M}x{N}x{K} (260 tiles)")
+    w = synth.workload("mxfp8", M, N, K, 551, 651, *pair)
+    D = run_mixed(w)
+    torch.cuda.synchronize()
+    em, en = synth.sample_entries(78, M, N, 4096)
+    _gpu.check_sampled("mxfp8", w, D, em, en)
+
+
+@pytest.mark.parametrize("pair", [("e2m3", "e2m3"), ("e3m2", "e4m3")], ids=_pid)
+def test_fp6_many_tiles_exact_permutation(pair):
+    """A permutation B over 260 tiles of 256 x 64 with K = 4160 (a partial
+    last 128-K stage), bit for bit on sampled entries."""
+    ea, eb = pair
+    M, K = 1024, 4160
+    N = K
+    _gpu.say(f"[mixed] fp6 {_pid(pair)} exact permutation {M}x{N}x{K}")
+    rng = np.random.default_rng(53)
+    w = _pins.make_w_mx8(ea, eb, M, N, K, rng, scale_lo=110, scale_hi=140)
+    pi = rng.permutation(K)
+    one = {"e5m2": 0x3C, "e4m3": 0x38, "e2m3": 0x08, "e3m2": 0x0C}[eb]
+    codes = np.zeros((N, K), np.uint8)
+    codes[np.arange(N), pi] = one
+    w["B"] = synth.pack_fp6_rows(codes) if eb in ("e2m3", "e3m2") else codes
+    w["sB"] = rng.integers(118, 137, (N, K // 32)).astype(np.uint8)
+    D = run_mixed(w)
+    torch.cuda.synchronize()
+    em, en = synth.sample_entries(79, M, N, 4096)
+    _gpu.check_exact_sampled("mxfp8", w, D, em, en)
+
+
+@pytest.mark.parametrize("shape", [(1024, 4160, 384), (4352, 4096, 384)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("pair", [("e4m3", "e2m1"), ("e2m1", "e5m2")], ids=_pid)
+def test_e2m1_widening_many_tiles_per_workgroup(shape, pair):
+    """The E2M1 widening path (K % 256 == 128) with more tiles than CUs:
+    260 tiles of 256 x 64 and 272 of 256 x 256."""
+    M, N, K = shape
+    _gpu.say(f"[mixed] widen {_pid(pair)} {shape}")
+    w = synth.workload("mxfp8", M, N, K, 552, 652, *pair)
+    D = run_mixed(w)
+    torch.cuda.synchronize()
+    em, en = synth.sample_entries(80, M, N, 4096)
+    _gpu.check_sampled("mxfp8", w, D, em, en)
 
 
 @pytest.mark.parametrize("pair", FP6_PAIRS, ids=_pid)

@@ -247,10 +247,11 @@ def test_repeat_bit_identical(fmt):
     _gpu.say(f"[determinism] {fmt}")
     w = _w(fmt, 1024, 768, 1024, seed=5)
     dev = _gpu.to_dev(w)
-    first = _gpu.d_bits(_gpu.run(fmt, w, dev))
-    for _ in range(20):
-        again = _gpu.d_bits(_gpu.run(fmt, w, dev))
-        assert np.array_equal(first, again)
+    first = _gpu.run(fmt, w, dev).view(torch.int16).clone()
+    again = torch.empty_like(first).view(torch.bfloat16)
+    for i in range(100):
+        _gpu.run(fmt, w, dev, out=again)
+        assert torch.equal(first, again.view(torch.int16)), f"repeat {i} differs"
 
 
 def test_out_argument_and_stream():
