@@ -182,13 +182,25 @@ class ClockReader:
             log(f"[bench] no GPU clock readings: {e}")
 
     def read(self):
+        """Mean of the per-XCD current graphics clocks from the GPU metrics
+        table (the SMU's own readings), else its average clock; None if
+        neither is available."""
         if self.h is None:
             return None
         try:
-            c = self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.GFX)["clk"]
-            return float(c) if c not in (None, "N/A") else None
+            m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
         except Exception:
             return None
+        xcd = m.get("current_gfxclks")
+        if isinstance(xcd, (list, tuple)):
+            v = [float(x) for x in xcd if isinstance(x, (int, float)) and 0 < x < 10000]
+            if v:
+                return sum(v) / len(v)
+        for key in ("average_gfxclk_frequency", "current_gfxclk"):
+            x = m.get(key)
+            if isinstance(x, (int, float)) and 0 < x < 10000:
+                return float(x)
+        return None
 
 
 def clock_under_load(clock, call, seconds=0.3):
