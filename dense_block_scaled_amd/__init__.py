@@ -27,7 +27,7 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["gemm_bf16", "gemm_mx", "gemm_mx_mixed", "gemm_nvfp4", "gemm_nvfp4_fp8", "nvfp4_fp8_workspace_bytes", "gemm_grouped_bf16", "gemm_grouped_mx", "gemm_grouped_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError",
+__all__ = ["gemm_bf16", "gemm_mx", "gemm_mx_mixed", "gemm_nvfp4", "gemm_nvfp4_fp8", "gemm_nvfp4_fp8_noalloc", "nvfp4_fp8_workspace_bytes", "gemm_grouped_bf16", "gemm_grouped_mx", "gemm_grouped_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError",
            "DBS_OK", "DBS_EINVAL", "DBS_EUNSUPPORTED", "DBS_EHIP", "K_MAJOR", "MN_MAJOR",
            "E4M3", "E5M2", "E2M3", "E3M2", "E2M1", "status_str"]
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_nvfp4_fp8.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P,
                                      ctypes.c_size_t, P]
         L.gemm_nvfp4_fp8.restype = I
+        L.gemm_nvfp4_fp8_noalloc.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P]
+        L.gemm_nvfp4_fp8_noalloc.restype = I
         L.gemm_grouped_bf16.argtypes = [P, P, P, P, I64, I64, I64, P]
         L.gemm_grouped_bf16.restype = I
         L.gemm_grouped_mx.argtypes = [I, P, P, P, P, P, P, I64, I64, I64, P]
@@ -334,4 +336,24 @@ def gemm_grouped_nvfp4(A: torch.Tensor, sA: torch.Tensor, tA: float, B: torch.Te
     out = _out(out, M, N, A)
     _check(lib().gemm_grouped_nvfp4(pa, psa, float(tA), pb, psb, tb, ctypes.c_void_p(out.data_ptr()), off, G, N, K,
                                     _stream(A)))
+    return out
+
+
+def gemm_nvfp4_fp8_noalloc(A: torch.Tensor, sA: torch.Tensor, tA: float, B: torch.Tensor, sB: torch.Tensor,
+                           tB: float, out: torch.Tensor) -> torch.Tensor:
+    """gemm_nvfp4_fp8 without any allocation: the library's static 64 MiB
+    device workspace replaces the caller's (see include/dbs.h; problems whose
+    workspace would be larger raise DbsError with DBS_EINVAL).  ``out`` (M x N
+    bfloat16 on the GPU) is required, since allocating it would defeat the
+    purpose."""
+    M, N = A.shape[0], B.shape[0]
+    K = A.shape[1] * 2
+    u8 = (torch.uint8,)
+    pa = _dev(A, "A", u8, (M, K // 2))
+    pb = _dev(B, "B", u8, (N, K // 2))
+    psa = _dev(sA, "sA", u8, (M, K // 16))
+    psb = _dev(sB, "sB", u8, (N, K // 16))
+    po = _dev(out, "out", (torch.bfloat16,), (M, N))
+    _check(lib().gemm_nvfp4_fp8_noalloc(pa, psa, float(tA), pb, psb, float(tB), po, M, N, K, K_MAJOR, K_MAJOR,
+                                        _stream(A)))
     return out

@@ -212,6 +212,44 @@ Fp8Ws fp8_ws(void *base, int64_t M, int64_t N, int64_t K)
 
 }  // namespace
 
+namespace dbs {
+
+void set_error(const char *msg) { std::snprintf(g_err, sizeof(g_err), "%s", msg); }
+
+int nvfp4_fp8_check(const void *A, const uint8_t *sA, const void *B, const uint8_t *sB, const void *D, int64_t M,
+                    int64_t N, int64_t K, int la, int lb)
+{
+    if (!sA || !sB) return fail(DBS_EINVAL, "null pointer argument");
+    dbs_status st = check_common(A, B, D, M, N, K, static_cast<dbs_layout>(la), static_cast<dbs_layout>(lb),
+                                 int64_t(1) << 22);
+    if (st != DBS_OK) return st;
+    if (K % 16) return fail(DBS_EINVAL, "nvfp4: K must be a multiple of 16");
+    if (K % 32) return fail(DBS_EUNSUPPORTED, "nvfp4 fp8-rate: K must be a multiple of 32 (whole MX blocks)");
+    if (la != DBS_K_MAJOR || lb != DBS_K_MAJOR)
+        return fail(DBS_EUNSUPPORTED, "nvfp4 fp8-rate: only K-major A and B are implemented");
+    return DBS_OK;
+}
+
+int64_t nvfp4_fp8_workspace_bytes(int64_t M, int64_t N, int64_t K) { return fp8_ws(nullptr, M, N, K).bytes; }
+
+int nvfp4_fp8_run(const void *A, const uint8_t *sA, float tA, const void *B, const uint8_t *sB, float tB, void *D,
+                  int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!aligned(workspace, 256)) return fail(DBS_EINVAL, "workspace must be 256-byte aligned");
+    const Fp8Ws w = fp8_ws(workspace, M, N, K);
+    if ((int64_t)workspace_bytes < w.bytes) return fail(DBS_EINVAL, "workspace smaller than gemm_nvfp4_fp8_workspace()");
+    int cus = 0;
+    dbs_status st = device_cus(&cus);
+    if (st != DBS_OK) return st;
+    hipError_t e = launch_requant_nvfp4_mx8(static_cast<const uint8_t *>(A), sA, M * K, w.a, w.sa, cus, stream);
+    if (e == hipSuccess)
+        e = launch_requant_nvfp4_mx8(static_cast<const uint8_t *>(B), sB, N * K, w.b, w.sb, cus, stream);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    return run(kMXFP8, w.a, w.sa, w.b, w.sb, D, M, N, K, tA * tB, 8, 32, stream);
+}
+
+}  // namespace dbs
+
 extern "C" {
 
 dbs_status gemm_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K, dbs_layout la,
@@ -293,23 +331,11 @@ dbs_status gemm_nvfp4_fp8(const void *A, const uint8_t *sA, float tA, const void
                           void *D, int64_t M, int64_t N, int64_t K, dbs_layout la, dbs_layout lb, void *workspace,
                           size_t workspace_bytes, hipStream_t stream)
 {
-    if (!sA || !sB || !workspace) return fail(DBS_EINVAL, "null pointer argument");
-    dbs_status st = check_common(A, B, D, M, N, K, la, lb, int64_t(1) << 22);
+    if (!workspace) return fail(DBS_EINVAL, "null pointer argument");
+    dbs_status st = static_cast<dbs_status>(dbs::nvfp4_fp8_check(A, sA, B, sB, D, M, N, K, la, lb));
     if (st != DBS_OK) return st;
-    if (K % 16) return fail(DBS_EINVAL, "nvfp4: K must be a multiple of 16");
-    if (K % 32) return fail(DBS_EUNSUPPORTED, "nvfp4 fp8-rate: K must be a multiple of 32 (whole MX blocks)");
-    if (la != DBS_K_MAJOR || lb != DBS_K_MAJOR)
-        return fail(DBS_EUNSUPPORTED, "nvfp4 fp8-rate: only K-major A and B are implemented");
-    if (!aligned(workspace, 256)) return fail(DBS_EINVAL, "workspace must be 256-byte aligned");
-    const Fp8Ws w = fp8_ws(workspace, M, N, K);
-    if ((int64_t)workspace_bytes < w.bytes) return fail(DBS_EINVAL, "workspace smaller than gemm_nvfp4_fp8_workspace()");
-    int cus = 0;
-    if ((st = device_cus(&cus)) != DBS_OK) return st;
-    hipError_t e = dbs::launch_requant_nvfp4_mx8(static_cast<const uint8_t *>(A), sA, M * K, w.a, w.sa, cus, stream);
-    if (e == hipSuccess)
-        e = dbs::launch_requant_nvfp4_mx8(static_cast<const uint8_t *>(B), sB, N * K, w.b, w.sb, cus, stream);
-    if (e != hipSuccess) return fail_hip(e, "kernel launch");
-    return run(dbs::kMXFP8, w.a, w.sa, w.b, w.sb, D, M, N, K, tA * tB, 8, 32, stream);
+    return static_cast<dbs_status>(
+        dbs::nvfp4_fp8_run(A, sA, tA, B, sB, tB, D, M, N, K, workspace, workspace_bytes, stream));
 }
 
 // ---- quantisers ----------------------------------------------------------------

@@ -70,4 +70,15 @@ hipError_t launch_requant_nvfp4_mx8(const uint8_t *codes, const uint8_t *scales,
                                     uint8_t *out_scales, int cus, hipStream_t stream);
 hipError_t launch_quant_bf16(const float *x, int64_t n, uint16_t *out, int cus, hipStream_t stream);
 
+// The FP8-rate NVFP4 GEMM behind both of its entry points (dbs.cpp): host
+// validation of the arguments (a dbs_status, with the error text recorded),
+// its workspace size, and the requantisation into `workspace` plus the GEMM.
+int nvfp4_fp8_check(const void *A, const uint8_t *sA, const void *B, const uint8_t *sB, const void *D, int64_t M,
+                    int64_t N, int64_t K, int la, int lb);
+int64_t nvfp4_fp8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int nvfp4_fp8_run(const void *A, const uint8_t *sA, float tA, const void *B, const uint8_t *sB, float tB, void *D,
+                  int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes, hipStream_t stream);
+// Records the text dbs_last_error() returns on this thread.
+void set_error(const char *msg);
+
 }  // namespace dbs

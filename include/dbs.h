@@ -32,8 +32,10 @@
  * GEMM; gemm_nvfp4_fp8 and the quantisers name theirs below) and
  * returns without synchronising; faults inside the kernel surface at the
  * caller's next synchronisation of that stream.  The library allocates no
- * device memory and keeps only a per-device cache of the CU count, so calls
- * from several host threads are safe.
+ * device memory and keeps only a per-device cache of the CU count (and, for
+ * gemm_nvfp4_fp8_noalloc, its static workspace array and that array's
+ * address per device), so calls from several host threads are safe, except
+ * overlapping gemm_nvfp4_fp8_noalloc calls on one GPU (see there).
  *
  * Errors: DBS_EINVAL is returned before any device work for a null pointer,
  * M, N or K <= 0, a K the format cannot take (see each entry point), a base
@@ -178,6 +180,29 @@ dbs_status gemm_nvfp4_fp8(const void *A, const uint8_t *sA, float tA,
                           int64_t M, int64_t N, int64_t K,
                           dbs_layout la, dbs_layout lb,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gemm_nvfp4_fp8 for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, validation, arithmetic and result
+ * as gemm_nvfp4_fp8 (bit for bit), except that the requantisation workspace
+ * is the library's own static device array of DBS_NOALLOC_WORKSPACE_BYTES
+ * (64 MiB): each GPU the library runs on holds one copy from the first call
+ * on it until the process ends.  A call whose gemm_nvfp4_fp8_workspace(M, N,
+ * K) exceeds that returns DBS_EINVAL before any device work (use
+ * gemm_nvfp4_fp8 with a caller workspace instead).  The call allocates
+ * nothing: the array's device address is looked up once per device, on the
+ * first call with that device current (DBS_EHIP if that fails).  Every call
+ * on one GPU uses the same array, which keeps the last call's contents (each
+ * call overwrites what it reads); calls that overlap on one GPU -- on
+ * different streams, or from different host threads without ordering --
+ * race for it and must not be issued.
+ */
+#define DBS_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+dbs_status gemm_nvfp4_fp8_noalloc(const void *A, const uint8_t *sA, float tA,
+                                  const void *B, const uint8_t *sB, float tB, void *D,
+                                  int64_t M, int64_t N, int64_t K,
+                                  dbs_layout la, dbs_layout lb, hipStream_t stream);
 
 /*
  * Grouped GEMMs (mixture-of-experts layout): G groups (1 <= G <= 64) share N

@@ -274,3 +274,19 @@ def test_grouped_null_arguments():
     assert L.gemm_grouped_mx(0, FAKE, NUL, FAKE, FAKE, FAKE, _off(0, 8, 16), 2, 16, 64, NUL) == 1
     assert L.gemm_grouped_nvfp4(FAKE, FAKE, 1.0, FAKE, FAKE, NUL, FAKE, _off(0, 8, 16), 2, 16, 64, NUL) == 1
     assert L.gemm_grouped_mx(0, FAKE, FAKE, FAKE, FAKE, FAKE, _off(0, 8, 16), 2, 16, 48, NUL) == 1   # K % 32
+
+
+def test_nvfp4_fp8_noalloc_validation():
+    """The allocation-free FP8-rate entry point validates like gemm_nvfp4_fp8,
+    rejects problems whose workspace exceeds its static 64 MiB before any
+    device work, and reports the missing device on a valid small problem."""
+    L = dbs.lib()
+    f = ctypes.c_float(1.0)
+    call = lambda M, N, K, la=0: L.gemm_nvfp4_fp8_noalloc(FAKE, FAKE, f, FAKE, FAKE, f, FAKE, M, N, K, la, 0, NUL)
+    assert call(64, 64, 48) == 2                                 # K % 32 != 0
+    assert call(64, 64, 64, la=1) == 2                           # MN-major
+    assert call(0, 64, 64) == 1
+    assert L.gemm_nvfp4_fp8_workspace(4096, 4096, 8192) > (64 << 20)
+    assert call(4096, 4096, 8192) == 1
+    assert "workspace" in L.dbs_last_error().decode()
+    assert call(256, 256, 256) == 3                              # no GPU here
