@@ -134,7 +134,7 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     // half of them (128 tiles) the square kernels measured 20-27% faster
     // than 256 x 64 tiles, BF16 and NVFP4 10% slower.
     const bool fp6 = (cv & 3) >= 2 || (cv >> 2) >= 2;
-    const bool mx = (fmt == dbs::kMXFP8 || fmt == dbs::kMXFP4) && cv == 0;
+    const bool mx = (fmt == dbs::kMXFP8 || fmt == dbs::kMXFP4 || fmt == dbs::kMXFP6) && cv == 0;
     const int shape = ((mx ? 4 : 2) * sq_tiles <= cus || fp6) ? dbs::kShapeSkinny : dbs::kShapeSquare;
     const int tm = shape == dbs::kShapeSkinny ? dbs::kSkinnyTM : dbs::kSquareTM;
     const int tn = shape == dbs::kShapeSkinny ? dbs::kSkinnyTN : dbs::kSquareTN;
@@ -286,6 +286,18 @@ dbs_status gemm_mx_mixed(dbs_mx_elem elem_a, dbs_mx_elem elem_b, const void *A, 
     if (cv != 0 && (la != DBS_K_MAJOR || lb != DBS_K_MAJOR) && K % 256)
         return fail(DBS_EUNSUPPORTED, "mx: 8-bit x E2M1 pairs with an MN-major operand need K % 256 == 0");
     const int bits = fp4_a && fp4_b ? 4 : 8;
+    if (fp6_a && fp6_b && K % dbs::kFp6StageK == 0 && K >= 2 * dbs::kFp6StageK && aligned(sA, 4) &&
+        aligned(sB, 4)) {
+        // FP6 on both sides at the FP6 rate (256 x 256 tiles), when those
+        // tiles occupy at least a quarter of the CUs; otherwise the widening
+        // path on 256 x 64 tiles below
+        int cus = 0;
+        if ((st = device_cus(&cus)) != DBS_OK) return st;
+        const int64_t sq = ((M + dbs::kSquareTM - 1) / dbs::kSquareTM) * ((N + dbs::kSquareTN - 1) / dbs::kSquareTN);
+        if (4 * sq > cus)
+            return run(dbs::kMXFP6, A, sA, B, sB, D, M, N, K, 1.0f, 6, 32, stream, nullptr, la, lb,
+                       (int)elem_a | ((int)elem_b << 3), 0);
+    }
     if ((st = check_mn(la, DBS_K_MAJOR, M, N, K, fp4_a ? 4 : 8)) != DBS_OK) return st;
     if ((st = check_mn(DBS_K_MAJOR, lb, M, N, K, fp4_b ? 4 : 8)) != DBS_OK) return st;
     return run(bits == 8 ? dbs::kMXFP8 : dbs::kMXFP4, A, sA, B, sB, D, M, N, K, 1.0f, bits, 32, stream, nullptr,

@@ -1,6 +1,6 @@
 // gemm.hip -- the kernel launcher the C ABI calls: picks the translation unit
 // of the format (gemm_bf16.hip, gemm_mxfp8.hip, gemm_mx8_e5m2.hip,
-// gemm_mx8_fp4.hip, gemm_mxfp4.hip, gemm_nvfp4.hip); the kernels and their
+// gemm_mx8_fp4.hip, gemm_mxfp4.hip, gemm_nvfp4.hip, gemm_mxfp6.hip); the kernels and their
 // design notes are in gemm_kernel.h.
 #include "gemm_kernel.h"
 
@@ -14,6 +14,7 @@ hipError_t launch_gemm(int fmt, int shape, const Params &p, int grid, hipStream_
     case kMXFP4: return launch_gemm_mxfp4(shape, p, grid, stream);
     case kNVFP4: return launch_gemm_nvfp4(shape, p, grid, stream);
     case kNVFP4R: return launch_gemm_nvfp4_raw(shape, p, grid, stream);
+    case kMXFP6: return shape == kShapeSquare ? launch_gemm_mxfp6(p, grid, stream) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }

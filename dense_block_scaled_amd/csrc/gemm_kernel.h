@@ -82,6 +82,8 @@ hipError_t launch_gemm_nvfp4(int shape, const Params &p, int grid, hipStream_t s
 hipError_t launch_gemm_nvfp4_raw(int shape, const Params &p, int grid, hipStream_t stream);
 // NVFP4 on 256 x 64 tiles through the raw-ring kernel (gemm_nvfp4.hip).
 hipError_t launch_nvfp4_ring(const Params &p, int grid, hipStream_t stream);
+// FP6 x FP6 at the FP6 rate on 256 x 256 tiles (gemm_mxfp6.hip).
+hipError_t launch_gemm_mxfp6(const Params &p, int grid, hipStream_t stream);
 
 namespace {
 
@@ -1248,22 +1250,19 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[S::MB][S::NB], co
 // full rows of the wave's columns instead of 32 rows x 16 bytes.  The same
 // wave's LDS writes and reads execute in order; the caller meets a barrier
 // before the slot is refilled.
+// The wave's staging buffer holds 32 rows of NB * 64 bytes.
 template <class S>
-__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[S::MB][S::NB], uint8_t *lds, int xslot,
-                                               const Params &p, const TileRef &tr, const Ctx<S> &c)
+constexpr int epilogue_wave_bytes() { return 32 * S::NB * 64; }
+
+template <class S>
+__device__ __forceinline__ void store_tile_lds_at(const f32x16 (&acc)[S::MB][S::NB], uint8_t *buf, const Params &p,
+                                                  const TileRef &tr, const Ctx<S> &c)
 {
     const int m0 = tr.m0, n0 = tr.n0;
     const float alpha = tr.alpha;
     constexpr int RB = S::NB * 64;          // bytes per staged row
     constexpr int CPR = RB / 16;            // 16-byte chunks per staged row
     constexpr int RPI = 64 / CPR;           // rows per read instruction
-    constexpr int WB = 32 * RB;             // bytes per wave buffer
-    constexpr bool SPLIT = S::NW * WB > S::kSlotA;
-    static_assert(!SPLIT || (S::NW / 2 * WB <= S::kSlotA && S::NW / 2 * WB <= S::kSlotB),
-                  "epilogue buffers must fit in one ring slot");
-    uint8_t *buf = !SPLIT           ? lds + S::kLdsA + xslot * S::kSlotA + c.w * WB
-                   : c.w < S::NW / 2 ? lds + S::kLdsA + xslot * S::kSlotA + c.w * WB
-                                     : lds + S::kLdsB + xslot * S::kSlotB + (c.w - S::NW / 2) * WB;
     const int nc = n0 + c.wn * (S::TN / S::WN);
 #pragma unroll
     for (int i = 0; i < S::MB; ++i) {
@@ -1290,6 +1289,20 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[S::MB][S::NB]
             __builtin_amdgcn_raw_buffer_store_b128(v, rd, n < p.N ? (uint32_t)(r * p.N + n) * 2u : kOOB, 0, kStoreNT);
         }
     }
+}
+
+template <class S>
+__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[S::MB][S::NB], uint8_t *lds, int xslot,
+                                               const Params &p, const TileRef &tr, const Ctx<S> &c)
+{
+    constexpr int WB = epilogue_wave_bytes<S>();
+    constexpr bool SPLIT = S::NW * WB > S::kSlotA;
+    static_assert(!SPLIT || (S::NW / 2 * WB <= S::kSlotA && S::NW / 2 * WB <= S::kSlotB),
+                  "epilogue buffers must fit in one ring slot");
+    uint8_t *buf = !SPLIT           ? lds + S::kLdsA + xslot * S::kSlotA + c.w * WB
+                   : c.w < S::NW / 2 ? lds + S::kLdsA + xslot * S::kSlotA + c.w * WB
+                                     : lds + S::kLdsB + xslot * S::kSlotB + (c.w - S::NW / 2) * WB;
+    store_tile_lds_at<S>(acc, buf, p, tr, c);
 }
 
 // ------------------------------------------------------------------ kernel

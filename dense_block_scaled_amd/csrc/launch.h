@@ -9,8 +9,10 @@ namespace dbs {
 
 // kNVFP4R: NVFP4 staged raw (the E2M1 bytes as MXFP4 stages them, the E4M3
 // scales as MX scales) and decoded in registers -- the path for MN-major
-// NVFP4 operands; internal, chosen by the launcher.
-enum Format : int { kBF16 = 0, kMXFP8 = 1, kMXFP4 = 2, kNVFP4 = 3, kNVFP4R = 4 };
+// NVFP4 operands; internal, chosen by the launcher.  kMXFP6: FP6 elements on
+// both sides at the MFMA's FP6 rate (gemm_mxfp6.hip; ec holds the two FP6
+// codes).
+enum Format : int { kBF16 = 0, kMXFP8 = 1, kMXFP4 = 2, kNVFP4 = 3, kNVFP4R = 4, kMXFP6 = 5 };
 
 constexpr int kMaxGroups = 64;
 
@@ -54,6 +56,10 @@ constexpr int kSquareTM = 256, kSquareTN = 256;
 constexpr int kSkinnyTM = 256, kSkinnyTN = 64;
 
 hipError_t launch_gemm(int fmt, int shape, const Params &p, int grid, hipStream_t stream);
+// The native FP6 kernel's conditions beyond FP6 on both sides: K-major, K a
+// multiple of 128 and at least 256, scale rows on 4-byte boundaries, 256 x
+// 256 tiles.
+constexpr int kFp6StageK = 128;
 
 // Quantisers (quant.hip): n elements of a row-major array whose rows are whole
 // blocks (n a multiple of 32 for MX, 16 for NVFP4, 8 for bf16); x, codes and
