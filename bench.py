@@ -13,7 +13,7 @@ between two events on the launch stream, with a device synchronisation on
 both sides; a 0.5 s pause between workloads.  The same protocol then times
 every other workload (reported under "per_format"): BF16 4096^3, MXFP8,
 MXFP4 at 8192^3 and 16384^3, NVFP4 square and skinny (256 x 16384 x 8192),
-the opt-in lossy FP8-rate NVFP4 path, E4M3 x E2M1 and MXFP6.
+the opt-in lossy FP8- and FP4-rate NVFP4 paths, E4M3 x E2M1 and MXFP6.
 
 Each line is priced against the dense MFMA peak of the arithmetic its
 kernels run (NVFP4's exact path multiplies in fp16, and is also quoted
@@ -64,13 +64,16 @@ W = {
     "nvfp4_fp8": dict(c=4, shape=(8192, 8192, 8192), enc="nvfp4", kernel="nvfp4_fp8", mfma="fp8", alt="fp4"),
     "nvfp4_fp8_skinny": dict(c=4, shape=(256, 16384, 8192), enc="nvfp4", kernel="nvfp4_fp8", mfma="fp8",
                              alt="fp4"),
+    "nvfp4_fp6": dict(c=4, shape=(8192, 8192, 8192), enc="nvfp4", kernel="nvfp4_fp6", mfma="fp6", alt="fp4"),
+    "nvfp4_fp6_skinny": dict(c=4, shape=(256, 16384, 8192), enc="nvfp4", kernel="nvfp4_fp6", mfma="fp6",
+                             alt="fp4"),
     "mx_e4m3_e2m1": dict(c=2, shape=(8192, 8192, 8192), enc="mxfp8", kernel="mx_mixed", mfma="fp8",
                          elems=("e4m3", "e2m1")),
     "mx_e2m3_e2m3": dict(c=2, shape=(8192, 8192, 8192), enc="mxfp8", kernel="mx_mixed", mfma="fp6",
                          elems=("e2m3", "e2m3")),
 }
 ORDER = ["bf16", "bf16_4096", "mxfp8", "mxfp4", "mxfp4_16384", "nvfp4", "nvfp4_skinny", "nvfp4_fp8",
-         "nvfp4_fp8_skinny", "mx_e4m3_e2m1", "mx_e2m3_e2m3"]
+         "nvfp4_fp8_skinny", "nvfp4_fp6", "nvfp4_fp6_skinny", "mx_e4m3_e2m1", "mx_e2m3_e2m3"]
 PEAK_NOTE = {
     "nvfp4": "exact NVFP4 runs its products on fp16 MFMA (no FP8/FP4 operand holds an E2M1 x E4M3 product): "
              "frac_mfma_peak is against the fp16 dense peak; frac_fp4_peak against the FP4 dense peak",
@@ -78,6 +81,12 @@ PEAK_NOTE = {
     "nvfp4_fp8": "opt-in lossy FP8-rate NVFP4 (gemm_nvfp4_fp8): requantisation to MXFP8 plus the MXFP8 GEMM, "
                  "both inside the timed launch; priced at the fp8 dense peak; max_r is against the oracle of "
                  "the same method, max_r_vs_exact against the exact NVFP4 oracle",
+    "nvfp4_fp6": "opt-in lossy FP4-rate NVFP4 (gemm_nvfp4_fp6): requantisation to MXFP6 E2M3 plus the FP6 GEMM "
+                 "(the FP6-rate kernel on 256 x 256 tiles), both inside the timed launch; priced at the FP6 dense "
+                 "peak (= FP4); max_r is against the oracle of the same method, max_r_vs_exact against the exact "
+                 "NVFP4 oracle",
+    "nvfp4_fp6_skinny": "as nvfp4_fp6; this shape's 64 square tiles are too few for the FP6-rate kernel, so its "
+                        "GEMM runs widened to 8 bits on 256 x 64 tiles",
     "mx_e4m3_e2m1": "E4M3 A x E2M1 B (gemm_mx_mixed, packed E2M1 on the MFMA's mixed formats): priced at the "
                     "fp8 dense peak, the rate its MFMAs run at",
     "mx_e2m3_e2m3": "MXFP6 (E2M3 both sides): priced at the FP6 dense peak",
@@ -164,6 +173,10 @@ def launcher(name, w, dev, out):
         import torch
         ws = torch.empty(dbs.nvfp4_fp8_workspace_bytes(w["M"], w["N"], K), dtype=torch.uint8, device="cuda")
         return lambda: dbs.gemm_nvfp4_fp8(dev["A"], dev["sA"], tA, dev["B"], dev["sB"], tB, out=out, workspace=ws)
+    if kern == "nvfp4_fp6":
+        import torch
+        ws = torch.empty(dbs.nvfp4_fp6_workspace_bytes(w["M"], w["N"], K), dtype=torch.uint8, device="cuda")
+        return lambda: dbs.gemm_nvfp4_fp6(dev["A"], dev["sA"], tA, dev["B"], dev["sB"], tB, out=out, workspace=ws)
     return lambda: dbs.gemm_nvfp4(dev["A"], dev["sA"], tA, dev["B"], dev["sB"], tB, out=out)
 
 
@@ -282,9 +295,9 @@ def parity_sample(name, w, D):
     got = gather(D, em, en, N)
     d, an, bn = oracle.gemm_entries(spec["enc"], w, em, en)
     r_exact = float(np.max(oracle.rel_errors(got, d, an, bn)))
-    if spec["kernel"] != "nvfp4_fp8":
+    if spec["kernel"] not in ("nvfp4_fp8", "nvfp4_fp6"):
         return r_exact, None
-    wq = oracle.nvfp4_fp8_workload(w)
+    wq = oracle.nvfp4_fp8_workload(w) if spec["kernel"] == "nvfp4_fp8" else oracle.nvfp4_fp6_workload(w)
     dq, aq, bq = oracle.gemm_entries("mxfp8", wq, em, en)
     alpha = float(w["tA"]) * float(w["tB"])
     r = float(np.max(oracle.rel_errors(got, dq * alpha, aq * abs(alpha), bq)))

@@ -27,7 +27,7 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["gemm_bf16", "gemm_mx", "gemm_mx_mixed", "gemm_nvfp4", "gemm_nvfp4_fp8", "gemm_nvfp4_fp8_noalloc", "nvfp4_fp8_workspace_bytes", "gemm_grouped_bf16", "gemm_grouped_mx", "gemm_grouped_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError",
+__all__ = ["gemm_bf16", "gemm_mx", "gemm_mx_mixed", "gemm_nvfp4", "gemm_nvfp4_fp8", "gemm_nvfp4_fp8_noalloc", "nvfp4_fp8_workspace_bytes", "gemm_nvfp4_fp6", "nvfp4_fp6_workspace_bytes", "gemm_grouped_bf16", "gemm_grouped_mx", "gemm_grouped_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError",
            "DBS_OK", "DBS_EINVAL", "DBS_EUNSUPPORTED", "DBS_EHIP", "K_MAJOR", "MN_MAJOR",
            "E4M3", "E5M2", "E2M3", "E3M2", "E2M1", "status_str"]
 
@@ -70,6 +70,11 @@ def lib() -> ctypes.CDLL:
         L.gemm_nvfp4_fp8.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P,
                                      ctypes.c_size_t, P]
         L.gemm_nvfp4_fp8.restype = I
+        L.gemm_nvfp4_fp6_workspace.argtypes = [I64, I64, I64]
+        L.gemm_nvfp4_fp6_workspace.restype = ctypes.c_size_t
+        L.gemm_nvfp4_fp6.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P,
+                                     ctypes.c_size_t, P]
+        L.gemm_nvfp4_fp6.restype = I
         L.gemm_nvfp4_fp8_noalloc.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P]
         L.gemm_nvfp4_fp8_noalloc.restype = I
         L.gemm_grouped_bf16.argtypes = [P, P, P, P, I64, I64, I64, P]
@@ -356,4 +361,34 @@ def gemm_nvfp4_fp8_noalloc(A: torch.Tensor, sA: torch.Tensor, tA: float, B: torc
     po = _dev(out, "out", (torch.bfloat16,), (M, N))
     _check(lib().gemm_nvfp4_fp8_noalloc(pa, psa, float(tA), pb, psb, float(tB), po, M, N, K, K_MAJOR, K_MAJOR,
                                         _stream(A)))
+    return out
+
+
+def nvfp4_fp6_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Device workspace gemm_nvfp4_fp6 needs for an M x N x K problem (0 if
+    the sizes are invalid)."""
+    return int(lib().gemm_nvfp4_fp6_workspace(M, N, K))
+
+
+def gemm_nvfp4_fp6(A: torch.Tensor, sA: torch.Tensor, tA: float, B: torch.Tensor, sB: torch.Tensor, tB: float,
+                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """FP4-rate NVFP4 GEMM (opt-in, lossy; see include/dbs.h): the NVFP4
+    operands are requantised to MXFP6 E2M3 in ``workspace`` (a uint8 GPU
+    tensor of at least nvfp4_fp6_workspace_bytes(M, N, K) bytes, allocated
+    here if not given) and multiplied at the FP6 (= FP4) MFMA rate."""
+    M, N = A.shape[0], B.shape[0]
+    K = A.shape[1] * 2
+    u8 = (torch.uint8,)
+    pa = _dev(A, "A", u8, (M, K // 2))
+    pb = _dev(B, "B", u8, (N, K // 2))
+    psa = _dev(sA, "sA", u8, (M, K // 16))
+    psb = _dev(sB, "sB", u8, (N, K // 16))
+    out = _out(out, M, N, A)
+    need = nvfp4_fp6_workspace_bytes(M, N, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=A.device)
+    _dev(workspace, "workspace", u8, (workspace.numel(),))
+    _check(lib().gemm_nvfp4_fp6(pa, psa, float(tA), pb, psb, float(tB), ctypes.c_void_p(out.data_ptr()),
+                                M, N, K, K_MAJOR, K_MAJOR, ctypes.c_void_p(workspace.data_ptr()),
+                                workspace.numel(), _stream(A)))
     return out

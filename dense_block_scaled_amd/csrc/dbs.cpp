@@ -210,6 +210,44 @@ Fp8Ws fp8_ws(void *base, int64_t M, int64_t N, int64_t K)
     return w;
 }
 
+// Workspace layout of the FP4-rate path: A codes (M x 3K/4), B codes
+// (N x 3K/4), A scales (M x K/32), B scales (N x K/32), each on a 256-byte
+// boundary.
+Fp8Ws fp6_ws(void *base, int64_t M, int64_t N, int64_t K)
+{
+    const int64_t ob = align256(M * K / 4 * 3), osa = ob + align256(N * K / 4 * 3), osb = osa + align256(M * K / 32);
+    Fp8Ws w;
+    w.bytes = osb + align256(N * K / 32);
+    uint8_t *p = static_cast<uint8_t *>(base);
+    w.a = p;
+    w.b = p ? p + ob : nullptr;
+    w.sa = p ? p + osa : nullptr;
+    w.sb = p ? p + osb : nullptr;
+    return w;
+}
+
+// FP6 on both sides, K-major (elements ea, eb: E2M3 or E3M2): at the FP6
+// rate on 256 x 256 tiles when those occupy more than a quarter of the CUs,
+// K is whole 128-K stages and the scale rows start on 4-byte boundaries;
+// otherwise widened to 8 bits on 256 x 64 tiles.
+dbs_status fp6_gemm(dbs_mx_elem ea, dbs_mx_elem eb, const void *A, const uint8_t *sA, const void *B,
+                    const uint8_t *sB, void *D, int64_t M, int64_t N, int64_t K, float alpha, hipStream_t stream)
+{
+    if (K % dbs::kFp6StageK == 0 && aligned(sA, 4) && aligned(sB, 4)) {
+        int cus = 0;
+        dbs_status st = device_cus(&cus);
+        if (st != DBS_OK) return st;
+        const int64_t sq = ((M + dbs::kSquareTM - 1) / dbs::kSquareTM) * ((N + dbs::kSquareTN - 1) / dbs::kSquareTN);
+        if (4 * sq > cus)
+            return run(dbs::kMXFP6, A, sA, B, sB, D, M, N, K, alpha, 6, 32, stream, nullptr, DBS_K_MAJOR,
+                       DBS_K_MAJOR, (int)ea | ((int)eb << 3), 0);
+    }
+    const int cv = cv_source(ea) | (cv_source(eb) << 2);
+    const int ec = mfma8_code(ea) | (mfma8_code(eb) << 3);
+    return run(dbs::kMXFP8, A, sA, B, sB, D, M, N, K, alpha, 8, 32, stream, nullptr, DBS_K_MAJOR, DBS_K_MAJOR, ec,
+               cv);
+}
+
 }  // namespace
 
 namespace dbs {
@@ -224,9 +262,9 @@ int nvfp4_fp8_check(const void *A, const uint8_t *sA, const void *B, const uint8
                                  int64_t(1) << 22);
     if (st != DBS_OK) return st;
     if (K % 16) return fail(DBS_EINVAL, "nvfp4: K must be a multiple of 16");
-    if (K % 32) return fail(DBS_EUNSUPPORTED, "nvfp4 fp8-rate: K must be a multiple of 32 (whole MX blocks)");
+    if (K % 32) return fail(DBS_EUNSUPPORTED, "nvfp4 requantised: K must be a multiple of 32 (whole MX blocks)");
     if (la != DBS_K_MAJOR || lb != DBS_K_MAJOR)
-        return fail(DBS_EUNSUPPORTED, "nvfp4 fp8-rate: only K-major A and B are implemented");
+        return fail(DBS_EUNSUPPORTED, "nvfp4 requantised: only K-major A and B are implemented");
     return DBS_OK;
 }
 
@@ -286,18 +324,7 @@ dbs_status gemm_mx_mixed(dbs_mx_elem elem_a, dbs_mx_elem elem_b, const void *A, 
     if (cv != 0 && (la != DBS_K_MAJOR || lb != DBS_K_MAJOR) && K % 256)
         return fail(DBS_EUNSUPPORTED, "mx: 8-bit x E2M1 pairs with an MN-major operand need K % 256 == 0");
     const int bits = fp4_a && fp4_b ? 4 : 8;
-    if (fp6_a && fp6_b && K % dbs::kFp6StageK == 0 && K >= 2 * dbs::kFp6StageK && aligned(sA, 4) &&
-        aligned(sB, 4)) {
-        // FP6 on both sides at the FP6 rate (256 x 256 tiles), when those
-        // tiles occupy at least a quarter of the CUs; otherwise the widening
-        // path on 256 x 64 tiles below
-        int cus = 0;
-        if ((st = device_cus(&cus)) != DBS_OK) return st;
-        const int64_t sq = ((M + dbs::kSquareTM - 1) / dbs::kSquareTM) * ((N + dbs::kSquareTN - 1) / dbs::kSquareTN);
-        if (4 * sq > cus)
-            return run(dbs::kMXFP6, A, sA, B, sB, D, M, N, K, 1.0f, 6, 32, stream, nullptr, la, lb,
-                       (int)elem_a | ((int)elem_b << 3), 0);
-    }
+    if (fp6_a && fp6_b) return fp6_gemm(elem_a, elem_b, A, sA, B, sB, D, M, N, K, 1.0f, stream);
     if ((st = check_mn(la, DBS_K_MAJOR, M, N, K, fp4_a ? 4 : 8)) != DBS_OK) return st;
     if ((st = check_mn(DBS_K_MAJOR, lb, M, N, K, fp4_b ? 4 : 8)) != DBS_OK) return st;
     return run(bits == 8 ? dbs::kMXFP8 : dbs::kMXFP4, A, sA, B, sB, D, M, N, K, 1.0f, bits, 32, stream, nullptr,
@@ -348,6 +375,35 @@ dbs_status gemm_nvfp4_fp8(const void *A, const uint8_t *sA, float tA, const void
     if (st != DBS_OK) return st;
     return static_cast<dbs_status>(
         dbs::nvfp4_fp8_run(A, sA, tA, B, sB, tB, D, M, N, K, workspace, workspace_bytes, stream));
+}
+
+// ---- FP4-rate NVFP4 (opt-in, lossy) ---------------------------------------------
+
+size_t gemm_nvfp4_fp6_workspace(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || K % 32 || M > (int64_t(1) << 25) || N > (int64_t(1) << 25) ||
+        K > (int64_t(1) << 22))
+        return 0;
+    return (size_t)fp6_ws(nullptr, M, N, K).bytes;
+}
+
+dbs_status gemm_nvfp4_fp6(const void *A, const uint8_t *sA, float tA, const void *B, const uint8_t *sB, float tB,
+                          void *D, int64_t M, int64_t N, int64_t K, dbs_layout la, dbs_layout lb, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream)
+{
+    if (!workspace) return fail(DBS_EINVAL, "null pointer argument");
+    dbs_status st = static_cast<dbs_status>(dbs::nvfp4_fp8_check(A, sA, B, sB, D, M, N, K, la, lb));
+    if (st != DBS_OK) return st;
+    if (!aligned(workspace, 256)) return fail(DBS_EINVAL, "workspace must be 256-byte aligned");
+    const Fp8Ws w = fp6_ws(workspace, M, N, K);
+    if ((int64_t)workspace_bytes < w.bytes) return fail(DBS_EINVAL, "workspace smaller than gemm_nvfp4_fp6_workspace()");
+    int cus = 0;
+    if ((st = device_cus(&cus)) != DBS_OK) return st;
+    hipError_t e = dbs::launch_requant_nvfp4_e2m3(static_cast<const uint8_t *>(A), sA, M * K, w.a, w.sa, cus, stream);
+    if (e == hipSuccess)
+        e = dbs::launch_requant_nvfp4_e2m3(static_cast<const uint8_t *>(B), sB, N * K, w.b, w.sb, cus, stream);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    return fp6_gemm(DBS_E2M3, DBS_E2M3, w.a, w.sa, w.b, w.sb, D, M, N, K, tA * tB, stream);
 }
 
 // ---- quantisers ----------------------------------------------------------------

@@ -57,8 +57,8 @@ constexpr int kSkinnyTM = 256, kSkinnyTN = 64;
 
 hipError_t launch_gemm(int fmt, int shape, const Params &p, int grid, hipStream_t stream);
 // The native FP6 kernel's conditions beyond FP6 on both sides: K-major, K a
-// multiple of 128 and at least 256, scale rows on 4-byte boundaries, 256 x
-// 256 tiles.
+// multiple of 128 (whole stages), scale rows on 4-byte boundaries, 256 x 256
+// tiles.
 constexpr int kFp6StageK = 128;
 
 // Quantisers (quant.hip): n elements of a row-major array whose rows are whole
@@ -74,6 +74,10 @@ hipError_t launch_quant_nvfp4(const float *x, int64_t n, uint8_t *codes, uint8_t
 // scales per 32) for the FP8-rate NVFP4 GEMM.
 hipError_t launch_requant_nvfp4_mx8(const uint8_t *codes, const uint8_t *scales, int64_t n, uint8_t *out,
                                     uint8_t *out_scales, int cus, hipStream_t stream);
+// NVFP4 operand of n elements -> MXFP6 E2M3 (packed codes, E8M0 scales per
+// 32) for the FP4-rate NVFP4 GEMM; out 8-byte aligned.
+hipError_t launch_requant_nvfp4_e2m3(const uint8_t *codes, const uint8_t *scales, int64_t n, uint8_t *out,
+                                     uint8_t *out_scales, int cus, hipStream_t stream);
 hipError_t launch_quant_bf16(const float *x, int64_t n, uint16_t *out, int cus, hipStream_t stream);
 
 // The FP8-rate NVFP4 GEMM behind both of its entry points (dbs.cpp): host

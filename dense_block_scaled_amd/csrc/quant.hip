@@ -325,6 +325,65 @@ __global__ __launch_bounds__(256) void requant_nvfp4_mx8_kernel(const uint8_t *_
     }
 }
 
+// NVFP4 -> MXFP6 (E2M3) requantisation (the FP4-rate NVFP4 GEMM), one lane
+// per 32-element block: with m the larger |scale| of the block's two groups
+// and e0 = floor(log2 m), the E8M0 exponent is E = e0 if m <= 1.25 * 2^e0,
+// else e0 + 1 -- the smallest E with 6 m <= 7.5 * 2^E, so that the block's
+// largest possible value a * s_g * 2^-E (exact in fp32) never exceeds E2M3's
+// 7.5 -- and each value goes to E2M3 through the hardware conversion of 32
+// fp32 values to packed FP6 (round to nearest even at unit scale, both
+// established with a one-wave probe; element j of the block lands at bits
+// 6j .. 6j+5 of 24 bytes, the rows' own packing).  Checked
+// bit for bit against the oracle's recipe over every pair of finite E4M3
+// group scales and every E2M1 code.
+__global__ __launch_bounds__(256) void requant_nvfp4_e2m3_kernel(const uint8_t *__restrict__ codes,
+                                                                 const uint8_t *__restrict__ scales,
+                                                                 uint8_t *__restrict__ out,
+                                                                 uint8_t *__restrict__ out_scales, int64_t nblocks)
+{
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    typedef __attribute__((ext_vector_type(16))) float f32x16;
+    typedef __attribute__((ext_vector_type(6))) unsigned int u32x6;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride) {
+        const uint4 c = *reinterpret_cast<const uint4 *>(codes + 16 * b);
+        const float s0 = dec_e4m3(scales[2 * b]), s1 = dec_e4m3(scales[2 * b + 1]);
+        const float m = __builtin_fmaxf(__builtin_fabsf(s0), __builtin_fabsf(s1));
+        int E = 0;
+        if (m > 0.0f) {
+            (void)__builtin_frexpf(m, &E);     // m in [2^(E-1), 2^E)
+            --E;
+            if (m > __builtin_ldexpf(1.25f, E)) ++E;
+        }
+        out_scales[b] = (uint8_t)(E + 127);
+        const float f0 = __builtin_ldexpf(s0, -E), f1 = __builtin_ldexpf(s1, -E);
+        const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+        // the conversion packs its two 16-value inputs interleaved (output
+        // element 2i from the first's value i, 2i + 1 from the second's;
+        // established with a one-wave probe), so the even elements go in
+        // the first, the odd ones in the second
+        f32x16 ev, od;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {             // dword d: elements 8d .. 8d+7, group d / 2
+            const float f = d < 2 ? f0 : f1;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {         // byte t: elements 8d + 2t (low nibble), 8d + 2t + 1
+                const f32x2 e = t == 0   ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[d], 1.0f, 0)
+                                : t == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[d], 1.0f, 1)
+                                : t == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[d], 1.0f, 2)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[d], 1.0f, 3);
+                ev[4 * d + t] = e[0] * f;
+                od[4 * d + t] = e[1] * f;
+            }
+        }
+        const u32x6 r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
+        uint2 *dst = reinterpret_cast<uint2 *>(out + 24 * b);
+        dst[0] = uint2{r[0], r[1]};
+        dst[1] = uint2{r[2], r[3]};
+        dst[2] = uint2{r[4], r[5]};
+    }
+}
+
 // *t: the tensor amax's bit pattern -> the tensor scale.
 __global__ void finish_scale_kernel(uint32_t *t) { *t = __builtin_bit_cast(uint32_t, tensor_scale(*t)); }
 
@@ -377,6 +436,16 @@ hipError_t launch_requant_nvfp4_mx8(const uint8_t *codes, const uint8_t *scales,
     const int64_t nblocks = n / 32;
     const int grid = grid_for(nblocks, cus);
     hipLaunchKernelGGL(requant_nvfp4_mx8_kernel, dim3(grid), dim3(256), 0, stream, codes, scales, out, out_scales,
+                       nblocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_requant_nvfp4_e2m3(const uint8_t *codes, const uint8_t *scales, int64_t n, uint8_t *out,
+                                     uint8_t *out_scales, int cus, hipStream_t stream)
+{
+    const int64_t nblocks = n / 32;
+    const int grid = grid_for(nblocks, cus);
+    hipLaunchKernelGGL(requant_nvfp4_e2m3_kernel, dim3(grid), dim3(256), 0, stream, codes, scales, out, out_scales,
                        nblocks);
     return hipGetLastError();
 }

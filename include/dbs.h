@@ -29,7 +29,7 @@
  *
  * Ownership and threading: the caller owns every buffer.  A call validates its
  * arguments on the host, then enqueues its kernels on `stream` (one for a
- * GEMM; gemm_nvfp4_fp8 and the quantisers name theirs below) and
+ * GEMM; gemm_nvfp4_fp8, gemm_nvfp4_fp6 and the quantisers name theirs below) and
  * returns without synchronising; faults inside the kernel surface at the
  * caller's next synchronisation of that stream.  The library allocates no
  * device memory and keeps only a per-device cache of the CU count (and, for
@@ -176,6 +176,37 @@ dbs_status gemm_nvfp4(const void *A, const uint8_t *sA, float tA,
  */
 size_t gemm_nvfp4_fp8_workspace(int64_t M, int64_t N, int64_t K);    /* 0 for invalid sizes */
 dbs_status gemm_nvfp4_fp8(const void *A, const uint8_t *sA, float tA,
+                          const void *B, const uint8_t *sB, float tB, void *D,
+                          int64_t M, int64_t N, int64_t K,
+                          dbs_layout la, dbs_layout lb,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * FP4-rate NVFP4 GEMM (opt-in, LOSSY): the NVFP4 operands of gemm_nvfp4 are
+ * requantised to MXFP6 E2M3 in `workspace` and multiplied at the FP6 rate of
+ * gfx950's scaled MFMA, which equals its FP4 rate.  Per block of 32 K
+ * elements (two 16-element groups with E4M3 scales s0, s1; m = max(|s0|,
+ * |s1|)) the E8M0 exponent E is the smallest integer with 6 m <= 7.5 * 2^E
+ * (the block's largest possible magnitude then fits E2M3's largest value,
+ * 7.5, without saturating), and each element a becomes the nearest E2M3 code
+ * of a * s_g * 2^-E (ties to even); tA * tB scales the result.  This is the
+ * FP4-rate form of the NVFP4 rescale step ("ThunderKittens 2.0", section
+ * 2.1) for hardware whose scaled MFMA takes only E8M0 scales per 32.  E2M3
+ * keeps E4M3's three mantissa bits but only two exponent bits: each
+ * requantised element is within max(2^-4 |a s_g|, 2^-4 * 2^E) of its exact
+ * value, 2^E < 1.6 m, so |D - D_exact| <= sum_k (|a_k| e_b,k + |b_k| e_a,k +
+ * e_a,k e_b,k) * |tA tB| plus the fp32/bf16 terms of any GEMM; with unit
+ * scales it is exact.  K a multiple of 32 (DBS_EUNSUPPORTED for K = 16 mod
+ * 32), K-major operands.  workspace: device memory of at least
+ * gemm_nvfp4_fp6_workspace(M, N, K) bytes, 256-byte aligned, owned by the
+ * caller (overwritten, not read before being written; calls sharing one
+ * workspace must not overlap).  Two requantisation kernels and the GEMM are
+ * enqueued on `stream`; the GEMM runs at the FP6 rate on 256 x 256 tiles when
+ * K is a multiple of 128 and those tiles fill more than a quarter of the
+ * CUs, else widened to 8 bits on 256 x 64 tiles (gemm_mx_mixed's FP6 paths).
+ */
+size_t gemm_nvfp4_fp6_workspace(int64_t M, int64_t N, int64_t K);    /* 0 for invalid sizes */
+dbs_status gemm_nvfp4_fp6(const void *A, const uint8_t *sA, float tA,
                           const void *B, const uint8_t *sB, float tB, void *D,
                           int64_t M, int64_t N, int64_t K,
                           dbs_layout la, dbs_layout lb,

@@ -70,6 +70,8 @@ def _load():
     lib.orc_quant_bf16.argtypes = [P, I64, P]
     lib.orc_requant_nvfp4_mx8.argtypes = [P, P, I64, I64, P, P]
     lib.orc_requant_nvfp4_mx8.restype = ctypes.c_int
+    lib.orc_requant_nvfp4_e2m3.argtypes = [P, P, I64, I64, P, P]
+    lib.orc_requant_nvfp4_e2m3.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -244,6 +246,29 @@ def requant_nvfp4_mx8(codes: np.ndarray, scales: np.ndarray, K: int):
     if lib.orc_requant_nvfp4_mx8(_ptr(c), _ptr(s), rows, K, _ptr(out), _ptr(osc)):
         raise ValueError("K must be a multiple of 32")
     return out, osc
+
+
+def requant_nvfp4_e2m3(codes: np.ndarray, scales: np.ndarray, K: int):
+    """NVFP4 operand (rows x K/2 packed E2M1, rows x K/16 E4M3) -> the MXFP6
+    operand of the FP4-rate GEMM (rows x 3K/4 packed E2M3, rows x K/32 E8M0)."""
+    lib = _load()
+    c = _c(codes, np.uint8)
+    s = _c(scales, np.uint8)
+    rows = c.shape[0]
+    out = np.zeros((rows, K // 4 * 3), np.uint8)
+    osc = np.zeros((rows, K // 32), np.uint8)
+    if lib.orc_requant_nvfp4_e2m3(_ptr(c), _ptr(s), rows, K, _ptr(out), _ptr(osc)):
+        raise ValueError("K must be a multiple of 32")
+    return out, osc
+
+
+def nvfp4_fp6_workload(w: dict) -> dict:
+    """The MXFP6 (E2M3) workload the FP4-rate NVFP4 GEMM computes for NVFP4
+    workload w (its D is this workload's GEMM times tA * tB)."""
+    a, sa = requant_nvfp4_e2m3(w["A"], w["sA"], w["K"])
+    b, sb = requant_nvfp4_e2m3(w["B"], w["sB"], w["K"])
+    return {"fmt": "mxfp8", "M": w["M"], "N": w["N"], "K": w["K"], "elemA": "e2m3", "elemB": "e2m3",
+            "A": a, "sA": sa, "B": b, "sB": sb}
 
 
 def nvfp4_fp8_workload(w: dict) -> dict:

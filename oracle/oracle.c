@@ -66,6 +66,7 @@ enum {
     MUT_FP6_SCALE = 17,     /* FP6 scale by floor(log2(amax / largest value))  */
     MUT_NV_S16_TRUNC = 18,  /* NVFP4 block scale rounded toward zero           */
     MUT_E5M2_EMAX = 19,     /* E5M2 scale recipe with E4M3's largest value     */
+    MUT_E2M3_REQ_E = 20,    /* E2M3 requantisation exponent floor(log2 m)      */
 };
 static int g_mut = MUT_NONE;
 void orc_set_mutation(int m) { g_mut = m; }
@@ -656,6 +657,47 @@ int orc_requant_nvfp4_mx8(const uint8_t *codes, const uint8_t *scales, int64_t r
                 double a = orc_decode_e2m1((k & 1) ? (byte >> 4) : (byte & 0xF));
                 double v = ldexp(a * (i < 16 ? s0 : s1), -E);      /* exact */
                 out[r * K + k] = (uint8_t)orc_encode_e4m3(v);
+            }
+        }
+    }
+    return 0;
+}
+
+/* NVFP4 -> MXFP6 (E2M3) requantisation (the opt-in FP4-rate NVFP4 GEMM):
+ * per 32-element block of a row (two 16-element groups with E4M3 scales s0,
+ * s1; m = max(|s0|, |s1|)), the E8M0 exponent E is the smallest integer with
+ * 6 m <= 7.5 * 2^E, i.e. the block's largest possible magnitude fits E2M3's
+ * largest value (never saturating) as high in its range as it goes: with
+ * e0 = floor(log2 m), E = e0 if m <= 1.25 * 2^e0, else e0 + 1 (E = 0 when
+ * both scales are zero).  Each element a (E2M1) of group g becomes the
+ * nearest E2M3 code of a * s_g * 2^-E (ties to even).  Codes in: rows x K/2
+ * packed E2M1, rows x K/16 E4M3; out: rows x 3K/4 packed E2M3 (element j at
+ * bits 6j .. 6j+5 of the row), rows x K/32 E8M0.  K % 32 == 0.  (The tensor
+ * scales are applied to the GEMM result, as for NVFP4.) */
+int orc_requant_nvfp4_e2m3(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K, uint8_t *out,
+                           uint8_t *out_scales)
+{
+    if (K % 32) return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        uint8_t *orow = out + r * (K / 4 * 3);
+        for (int64_t b = 0; b < K / 32; ++b) {
+            double s0 = orc_decode_e4m3(scales[r * (K / 16) + 2 * b]);
+            double s1 = orc_decode_e4m3(scales[r * (K / 16) + 2 * b + 1]);
+            double m = fmax(fabs(s0), fabs(s1));
+            int E = 0;
+            if (m > 0.0) {
+                int ex;
+                frexp(m, &ex);              /* m in [2^(ex-1), 2^ex) */
+                E = ex - 1;
+                if (g_mut != MUT_E2M3_REQ_E && m > ldexp(1.25, E)) E += 1;
+            }
+            out_scales[r * (K / 32) + b] = (uint8_t)(E + 127);
+            for (int i = 0; i < 32; ++i) {
+                int64_t k = b * 32 + i;
+                uint8_t byte = codes[r * (K / 2) + k / 2];
+                double a = orc_decode_e2m1((k & 1) ? (byte >> 4) : (byte & 0xF));
+                double v = ldexp(a * (i < 16 ? s0 : s1), -E);      /* exact */
+                fp6_put(orow, k, orc_encode_e2m3(v));
             }
         }
     }

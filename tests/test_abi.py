@@ -290,3 +290,24 @@ def test_nvfp4_fp8_noalloc_validation():
     assert call(4096, 4096, 8192) == 1
     assert "workspace" in L.dbs_last_error().decode()
     assert call(256, 256, 256) == 3                              # no GPU here
+
+
+def test_nvfp4_fp6_workspace_and_validation():
+    """The FP4-rate NVFP4 entry point: workspace size (E2M3 codes of both
+    operands, 3K/4 bytes per row, and their E8M0 scales, each part 256-byte
+    aligned), validation before any device work."""
+    L = dbs.lib()
+    M, N, K = 300, 200, 512
+    a256 = lambda x: (x + 255) // 256 * 256
+    want = a256(M * K * 3 // 4) + a256(N * K * 3 // 4) + a256(M * K // 32) + a256(N * K // 32)
+    assert L.gemm_nvfp4_fp6_workspace(M, N, K) == want
+    assert L.gemm_nvfp4_fp6_workspace(M, N, 48) == 0
+    f = ctypes.c_float(1.0)
+    call = lambda M, N, K, ws, nb, la=0: L.gemm_nvfp4_fp6(FAKE, FAKE, f, FAKE, FAKE, f, FAKE, M, N, K, la, 0, ws, nb,
+                                                          NUL)
+    assert call(64, 64, 64, NUL, 1 << 20) == 1                   # no workspace
+    assert call(64, 64, 48, FAKE, 1 << 20) == 2                  # K % 32
+    assert call(64, 64, 64, FAKE, 1 << 20, la=1) == 2            # MN-major
+    assert call(64, 64, 64, ctypes.c_void_p((1 << 20) + 64), 1 << 20) == 1   # misaligned workspace
+    assert call(64, 64, 64, FAKE, 16) == 1                       # too small
+    assert call(64, 64, 64, FAKE, 1 << 20) == 3                  # no GPU here
