@@ -195,31 +195,32 @@ class ClockReader:
             log(f"[bench] no GPU clock readings: {e}")
 
     def read(self):
-        """Mean of the per-XCD current graphics clocks from the GPU metrics
-        table (the SMU's own readings), else its average clock; None if
-        neither is available."""
+        """(mean of the per-XCD current graphics clocks in MHz, GFX activity
+        in %) from the SMU's metrics table, or None."""
         if self.h is None:
             return None
         try:
             m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
         except Exception:
             return None
+        act = m.get("average_gfx_activity")
+        act = float(act) if isinstance(act, (int, float)) else None
         xcd = m.get("current_gfxclks")
         if isinstance(xcd, (list, tuple)):
             v = [float(x) for x in xcd if isinstance(x, (int, float)) and 0 < x < 10000]
             if v:
-                return sum(v) / len(v)
-        for key in ("average_gfxclk_frequency", "current_gfxclk"):
-            x = m.get(key)
-            if isinstance(x, (int, float)) and 0 < x < 10000:
-                return float(x)
+                return sum(v) / len(v), act
+        x = m.get("current_gfxclk")
+        if isinstance(x, (int, float)) and 0 < x < 10000:
+            return float(x), act
         return None
 
 
-def clock_under_load(clock, call, seconds=0.3):
+def clock_under_load(clock, call, seconds=1.6):
     """Median graphics clock while `call` runs back to back for ~seconds (a
-    window of its own after the timed one; the readings do not overlap the
-    timing)."""
+    window of its own after the timed one).  The metrics table refreshes
+    about once a second, so only readings taken while it reports the GPU
+    busy (activity >= 80%) count; None if there are none."""
     import torch
     if clock is None or clock.h is None:
         return None
@@ -227,16 +228,16 @@ def clock_under_load(clock, call, seconds=0.3):
 
     def poll():
         while not stop.is_set():
-            v = clock.read()
-            if v:
-                samples.append(v)
-            time.sleep(0.002)
+            r = clock.read()
+            if r and r[1] is not None and r[1] >= 80:
+                samples.append(r[0])
+            time.sleep(0.005)
 
     th = threading.Thread(target=poll)
     t_end = time.perf_counter() + seconds
     th.start()
     while time.perf_counter() < t_end:
-        for _ in range(8):
+        for _ in range(4):
             call()
         torch.cuda.synchronize()
     stop.set()
@@ -384,6 +385,7 @@ def main():
                     help="workload to time (nvfp4_skinny: the 256x16384x8192 NVFP4 GEMM)")
     ap.add_argument("--only", action="store_true", help="time only --fmt (no per_format table)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-clock", action="store_true", help="skip the GPU-clock window (for profiled runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run 5 device copies of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -400,7 +402,7 @@ def main():
     torch.cuda.set_device(0)
     import dense_block_scaled_amd as dbs
     dbs.lib()
-    clock = ClockReader()
+    clock = None if args.no_clock else ClockReader()
 
     fmt = args.fmt
     if args.calib_copy_mib:

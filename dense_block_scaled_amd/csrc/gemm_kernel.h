@@ -591,17 +591,24 @@ __device__ __forceinline__ void read_scales(Scales<S> &sc, const uint8_t *lds, i
 }
 
 // Chunked layout: stage j (0 .. scale_spc - 1) of the chunk in buffer `par`.
+// A row's 16 chunk bytes hold its dwords in the order d ^ 2 s, s = bit 4 of
+// the row's index in the concatenated list (see dma_scale_portion): the 32
+// rows one read covers are 16 bytes apart, so rows r and r + 16 share four
+// banks, and the swizzle puts their dwords in different ones.  c.sa and c.sb
+// carry 8 s in their (otherwise zero) bit 3, so the stage's byte offset
+// enters by XOR.
 template <int FMT, class S>
 __device__ __forceinline__ void read_scales_chunk(Scales<S> &sc, const uint8_t *lds, int par, int j, const Ctx<S> &c)
 {
     constexpr int BPS = Fmt<FMT>::BPS;
-    const uint32_t o = (uint32_t)(par * (S::TM + S::TN) * kScaleChunk + j * BPS);
+    const uint32_t o = (uint32_t)(par * (S::TM + S::TN) * kScaleChunk);
+    const uint32_t jb = (uint32_t)(j * BPS);
 #pragma unroll
     for (int i = 0; i < S::MB; ++i)
-        read_scale_row<FMT>(sc.a[i], lds, c.sa + o + (uint32_t)(i * 32 * kScaleChunk));
+        read_scale_row<FMT>(sc.a[i], lds, (c.sa ^ jb) + o + (uint32_t)(i * 32 * kScaleChunk));
 #pragma unroll
     for (int jj = 0; jj < S::NB; ++jj)
-        read_scale_row<FMT>(sc.b[jj], lds, c.sb + o + (uint32_t)(jj * 32 * kScaleChunk));
+        read_scale_row<FMT>(sc.b[jj], lds, (c.sb ^ jb) + o + (uint32_t)(jj * 32 * kScaleChunk));
 }
 
 template <int FMT, class S>
@@ -720,18 +727,20 @@ __device__ __forceinline__ void dma_scale_rows16(uint8_t *lds, int slot, const T
 // Chunked scales: portion u (0 .. scale_spc - 1) of chunk `chunk` (bytes
 // 16 chunk .. 16 chunk + 15 of every row) into chunk buffer `par`: rows
 // u R .. (u + 1) R - 1 of the concatenated row list (A rows, then B rows;
-// R = (TM + TN) / scale_spc), 16 rows per dword wave-load, lane i taking
-// dword i % 4 of row i / 4.  Dwords past a row's end read zero.
+// R = (TM + TN) / scale_spc), 16 rows per dword wave-load: lane i lands on
+// dword position i % 4 of row i / 4 and fetches the row's dword
+// (i % 4) ^ 2 s, s = bit 4 of the row's index (the same for the 16 rows of a
+// wave-load; see read_scales_chunk).  Dwords past a row's end read zero.
 template <int FMT, class S>
 __device__ __forceinline__ void dma_scale_portion(uint8_t *lds, int par, const Target &stg, int chunk, int u,
                                                   const Ctx<S> &c, int sld)
 {
     constexpr int R = (S::TM + S::TN) / scale_spc<FMT>(), NLP = R / 16;
-    static_assert(NLP % S::NW == 0 && S::TM % 16 == 0, "portions split evenly over the waves");
-    const int o = chunk * kScaleChunk + 4 * (c.lane & 3);
+    static_assert(NLP % S::NW == 0 && S::TM % 32 == 0, "portions split evenly over the waves; B rows keep bit 4");
 #pragma unroll
     for (int k = 0; k < NLP / S::NW; ++k) {
         const int row0 = u * R + (c.w + k * S::NW) * 16;      // wave-uniform
+        const int o = chunk * kScaleChunk + 4 * ((c.lane & 3) ^ (2 * ((row0 >> 4) & 1)));
         const bool is_a = row0 < S::TM;
         const int r = (is_a ? row0 : row0 - S::TM) + (c.lane >> 2);
         const uint32_t off = (uint32_t)(r * sld + o) | (o < sld ? 0u : kOOB);
@@ -1674,8 +1683,10 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
     c.fa = (uint32_t)(S::kLdsA + ra0 * kRowBytes + ((c.h ^ swz(ra0)) << 4));
     c.fb = (uint32_t)(S::kLdsB + rb0 * kRowBytes + (((adirect<FMT, S>() ? 4 * c.h : c.h) ^ swz(rb0)) << 4));
     if constexpr (SM == kScalesChunk) {
-        c.sa = (uint32_t)(S::kLdsS + ra0 * kScaleChunk);
-        c.sb = (uint32_t)(S::kLdsS + (S::TM + rb0) * kScaleChunk);
+        // bit 4 of the row index swizzles the row's dwords (read_scales_chunk);
+        // rows 32 i further down keep it
+        c.sa = (uint32_t)(S::kLdsS + ra0 * kScaleChunk) | (uint32_t)(8 * ((ra0 >> 4) & 1));
+        c.sb = (uint32_t)(S::kLdsS + (S::TM + rb0) * kScaleChunk) | (uint32_t)(8 * (((S::TM + rb0) >> 4) & 1));
     } else {
         c.sa = (uint32_t)(S::kLdsS + ra0 * BPS);
         c.sb = (uint32_t)(S::kLdsS + S::NS * S::TM * BPS + rb0 * BPS);
