@@ -14,6 +14,10 @@ both sides; a 0.5 s pause between workloads.  The same protocol then times
 every other workload (reported under "per_format"): BF16 4096^3, MXFP8,
 MXFP4 at 8192^3 and 16384^3, NVFP4 square and skinny (256 x 16384 x 8192),
 the opt-in lossy FP8- and FP4-rate NVFP4 paths, E4M3 x E2M1 and MXFP6.
+With --only, --fmt also names workloads outside that table (the skinny
+BF16/MXFP8/MXFP4 shapes, E2M1 x E4M3, E4M3 x E2M1 with K = 8064 on the
+widening path, E3M2 x E4M3 widened), and --layout hands A and/or B over
+MN-major.
 
 Each line is priced against the dense MFMA peak of the arithmetic its
 kernels run (NVFP4's exact path multiplies in fp16, and is also quoted
@@ -72,6 +76,21 @@ W = {
     "mx_e2m3_e2m3": dict(c=2, shape=(8192, 8192, 8192), enc="mxfp8", kernel="mx_mixed", mfma="fp6",
                          elems=("e2m3", "e2m3")),
 }
+# timed only when named with --fmt (not in the default table): the other
+# tilings and element pairings the library routes to
+W.update({
+    "bf16_skinny": dict(c=1, shape=(256, 16384, 8192), enc="bf16", kernel="bf16", mfma="bf16"),
+    "mxfp8_skinny": dict(c=2, shape=(256, 16384, 8192), enc="mxfp8", kernel="mxfp8", mfma="fp8"),
+    "mxfp4_skinny": dict(c=3, shape=(256, 16384, 8192), enc="mxfp4", kernel="mxfp4", mfma="fp4"),
+    "mx_e2m1_e4m3": dict(c=2, shape=(8192, 8192, 8192), enc="mxfp8", kernel="mx_mixed", mfma="fp8",
+                         elems=("e2m1", "e4m3")),
+    "mx_e4m3_e2m1_skinny": dict(c=2, shape=(256, 16384, 8192), enc="mxfp8", kernel="mx_mixed", mfma="fp8",
+                                elems=("e4m3", "e2m1")),
+    "mx_e4m3_e2m1_k8064": dict(c=2, shape=(8192, 8192, 8064), enc="mxfp8", kernel="mx_mixed", mfma="fp8",
+                               elems=("e4m3", "e2m1")),
+    "mx_e3m2_e4m3": dict(c=2, shape=(8192, 8192, 8192), enc="mxfp8", kernel="mx_mixed", mfma="fp8",
+                         elems=("e3m2", "e4m3")),
+})
 ORDER = ["bf16", "bf16_4096", "mxfp8", "mxfp4", "mxfp4_16384", "nvfp4", "nvfp4_skinny", "nvfp4_fp8",
          "nvfp4_fp8_skinny", "nvfp4_fp6", "nvfp4_fp6_skinny", "mx_e4m3_e2m1", "mx_e2m3_e2m3"]
 PEAK_NOTE = {
@@ -93,7 +112,7 @@ PEAK_NOTE = {
 }
 KERNEL_SOURCES = ["dense_block_scaled_amd/csrc/" + f for f in
                   ("gemm_kernel.h", "launch.h", "gemm.hip", "gemm_bf16.hip", "gemm_mxfp8.hip", "gemm_mx8_e5m2.hip",
-                   "gemm_mx8_fp4.hip", "gemm_mxfp4.hip", "gemm_nvfp4.hip")]
+                   "gemm_mx8_fp4.hip", "gemm_mxfp4.hip", "gemm_nvfp4.hip", "gemm_mxfp6.hip", "quant.hip")]
 
 
 def log(msg):
@@ -145,26 +164,41 @@ def make_inputs(name):
     return synth.workload(spec["enc"], M, N, K, 100 * c + 1, 100 * c + 2, *spec.get("elems", ()))
 
 
-def to_device(w):
+def to_mn(enc, X):
+    """K-major operand storage (rows, K) -> MN-major storage (K, rows); E2M1
+    codes are re-packed two per byte along the rows."""
+    if enc in ("bf16", "mxfp8"):
+        return np.ascontiguousarray(X.T)
+    codes = np.empty((X.shape[0], 2 * X.shape[1]), np.uint8)
+    codes[:, 0::2] = X & 0xF
+    codes[:, 1::2] = X >> 4
+    t = np.ascontiguousarray(codes.T)
+    return (t[:, 0::2] | (t[:, 1::2] << 4)).astype(np.uint8)
+
+
+def to_device(w, lay="kk"):
     import torch
     out = {}
     for k in ("A", "B", "sA", "sB"):
         if k in w:
             a = np.ascontiguousarray(w[k])
+            if (k == "A" and lay[0] == "m") or (k == "B" and lay[1] == "m"):
+                a = to_mn(w["fmt"], a)
             out[k] = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to("cuda")
     return out
 
 
-def launcher(name, w, dev, out):
+def launcher(name, w, dev, out, lay="kk"):
     import dense_block_scaled_amd as dbs
     K = w["K"]
     kern = W[name]["kernel"]
+    la, lb = int(lay[0] == "m"), int(lay[1] == "m")
     if kern == "bf16":
-        return lambda: dbs.gemm_bf16(dev["A"], dev["B"], out=out)
+        return lambda: dbs.gemm_bf16(dev["A"], dev["B"], out=out, la=la, lb=lb)
     if kern == "mxfp8":
-        return lambda: dbs.gemm_mx("e4m3", dev["A"], dev["sA"], dev["B"], dev["sB"], K=K, out=out)
+        return lambda: dbs.gemm_mx("e4m3", dev["A"], dev["sA"], dev["B"], dev["sB"], K=K, out=out, la=la, lb=lb)
     if kern == "mxfp4":
-        return lambda: dbs.gemm_mx("e2m1", dev["A"], dev["sA"], dev["B"], dev["sB"], K=K, out=out)
+        return lambda: dbs.gemm_mx("e2m1", dev["A"], dev["sA"], dev["B"], dev["sB"], K=K, out=out, la=la, lb=lb)
     if kern == "mx_mixed":
         ea, eb = W[name]["elems"]
         return lambda: dbs.gemm_mx_mixed(ea, eb, dev["A"], dev["sA"], dev["B"], dev["sB"], K=K, out=out)
@@ -177,7 +211,7 @@ def launcher(name, w, dev, out):
         import torch
         ws = torch.empty(dbs.nvfp4_fp6_workspace_bytes(w["M"], w["N"], K), dtype=torch.uint8, device="cuda")
         return lambda: dbs.gemm_nvfp4_fp6(dev["A"], dev["sA"], tA, dev["B"], dev["sB"], tB, out=out, workspace=ws)
-    return lambda: dbs.gemm_nvfp4(dev["A"], dev["sA"], tA, dev["B"], dev["sB"], tB, out=out)
+    return lambda: dbs.gemm_nvfp4(dev["A"], dev["sA"], tA, dev["B"], dev["sB"], tB, out=out, la=la, lb=lb)
 
 
 class ClockReader:
@@ -245,17 +279,17 @@ def clock_under_load(clock, call, seconds=1.6):
     return float(np.median(samples)) if samples else None
 
 
-def time_gemm(name, w, steps, warmup, clock=None):
+def time_gemm(name, w, steps, warmup, clock=None, lay="kk"):
     """Protocol timing; returns (avg seconds per launch, groups, output tensor,
     clock MHz under load)."""
     import torch
     M, N, K = w["M"], w["N"], w["K"]
     in_bytes = algorithmic_bytes(name, M, N, K) - M * N * 2
     groups = 1 if in_bytes >= 3 * LLC_BYTES else (3 * LLC_BYTES) // in_bytes + 1
-    dev0 = to_device(w)
+    dev0 = to_device(w, lay)
     devs = [dev0] + [{k: v.clone() for k, v in dev0.items()} for _ in range(groups - 1)]
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    calls = [launcher(name, w, d, out) for d in devs]
+    calls = [launcher(name, w, d, out, lay) for d in devs]
     torch.cuda.synchronize()
     for i in range(warmup):
         calls[i % groups]()
@@ -343,12 +377,12 @@ def cpu_baseline(name, w, D, target_s=12.0):
     }, float(np.max(r))
 
 
-def measure(name, steps, warmup, clock):
+def measure(name, steps, warmup, clock, lay="kk"):
     t = time.perf_counter()
     w = make_inputs(name)
     M, N, K = w["M"], w["N"], w["K"]
     log(f"[bench] {name} {M}x{N}x{K}: inputs ready in {time.perf_counter() - t:.1f} s")
-    avg, groups, D, mhz = time_gemm(name, w, steps, warmup, clock)
+    avg, groups, D, mhz = time_gemm(name, w, steps, warmup, clock, lay)
     tflops = 2.0 * M * N * K / avg / 1e12
     gbs = algorithmic_bytes(name, M, N, K) / avg / 1e9
     log(f"[bench] {name}: {avg * 1e6:.1f} us/launch, {tflops:.1f} TFLOP/s, {gbs:.0f} GB/s, {groups} input groups, "
@@ -381,11 +415,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--fmt", default="bf16", choices=ORDER,
+    ap.add_argument("--fmt", default="bf16", choices=list(W),
                     help="workload to time (nvfp4_skinny: the 256x16384x8192 NVFP4 GEMM)")
     ap.add_argument("--only", action="store_true", help="time only --fmt (no per_format table)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-clock", action="store_true", help="skip the GPU-clock window (for profiled runs)")
+    ap.add_argument("--layout", default="kk", choices=["kk", "mk", "km", "mm"],
+                    help="operand storage of A and B: k K-major (rows x K), m MN-major (K x rows); "
+                         "BF16, MXFP8, MXFP4 and NVFP4 workloads, with --only")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run 5 device copies of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -405,6 +442,10 @@ def main():
     clock = None if args.no_clock else ClockReader()
 
     fmt = args.fmt
+    lay = args.layout
+    if lay != "kk" and (not args.only or W[fmt]["kernel"] not in ("bf16", "mxfp8", "mxfp4", "nvfp4")):
+        print("--layout takes a BF16, MXFP8, MXFP4 or NVFP4 workload and --only", file=sys.stderr)
+        sys.exit(2)
     if args.calib_copy_mib:
         n = args.calib_copy_mib * 2 ** 20 // 4
         src = torch.randn(n, device="cuda")
@@ -413,11 +454,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    w, D, avg, groups, tflops, gbs, mhz = measure(fmt, args.steps, args.warmup, clock)
+    w, D, avg, groups, tflops, gbs, mhz = measure(fmt, args.steps, args.warmup, clock, lay)
     r, r_exact = parity_sample(fmt, w, D)
     head = record(fmt, w, avg, tflops, gbs, mhz, r, r_exact)
     M, N, K = w["M"], w["N"], w["K"]
-    workload = f"{fmt}_gemm_{M}x{N}x{K}"
+    workload = f"{fmt}_gemm_{M}x{N}x{K}" + ("" if lay == "kk" else "_" + lay)
+    storage = {"kk": "A MxK, B NxK (K-major)", "mk": "A KxM (MN-major), B NxK", "km": "A MxK, B KxN (MN-major)",
+               "mm": "A KxM, B KxN (both MN-major)"}[lay]
     peak = PEAK[W[fmt]["mfma"]]
     result = {
         "metric": "TFLOP/s per GEMM (BF16/MXFP8/MXFP4) at 8192^3 and % of dtype MFMA peak",
@@ -433,7 +476,7 @@ def main():
         "dtype": W[fmt]["enc"],
         "data": "synthetic: seeded N(0,1) (PCG64), encoded per the format's recipe",
         "config": {"workload": workload, "format": fmt, "M": M, "N": N, "K": K,
-                   "layout": "A MxK, B NxK (K-major), D MxN bf16", "input_groups": groups},
+                   "layout": storage + ", D MxN bf16", "input_groups": groups},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": traffic_for(workload)},
         "sclk_mhz": head["sclk_mhz"],
@@ -448,7 +491,7 @@ def main():
             f"rows max r {rmax:.2e}")
     del D
     if not args.only:
-        per = []
+        per = [] if fmt in ORDER else [head]
         for f in ORDER:
             if f == fmt:
                 per.append(head)

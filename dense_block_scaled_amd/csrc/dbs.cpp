@@ -167,6 +167,8 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     if (tiles > INT32_MAX) return fail(DBS_EINVAL, "too many output tiles");
     const int grid = (int)std::min<int64_t>(tiles, cus);
     hipError_t e = dbs::launch_gemm(fmt, shape, p, grid, stream);
+    if (e == hipErrorNotSupported)
+        return fail(DBS_EUNSUPPORTED, "no kernel for this element format pair, layout and tile shape");
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
     g_err[0] = '\0';
     return DBS_OK;

@@ -2021,6 +2021,8 @@ hipError_t launch_fp8_fp4(const Params &p, int grid, hipStream_t stream)
     }
     if (p.cv != 0) {
         if constexpr (std::is_same<S, Square>::value) {
+            // widened FP6 has 256 x 64 kernels only (the host routes it there)
+            if (!e2m1) return hipErrorNotSupported;
             return launch_cv<kScalesRegs, SquareW4>(p, grid, stream);
         } else {
             if (!e2m1) {

@@ -27,9 +27,15 @@
 //   lane fetching the piece that belongs at its fixed cell.
 // * The fragment of k-step kk for lane half h is pieces 4 kk + 2 h and
 //   4 kk + 2 h + 1 of its row: two ds_read_b96 of 16-byte-aligned cells.
-// * E8M0 scales ride the same stage: 4 bytes (blocks 0..3 of the stage) per
-//   row, one dword wave-load per wave, read once per stage per row block and
-//   fed to the MFMA with op_sel picking the k-step's byte, as for MXFP8.
+// * E8M0 scales: 4 bytes (blocks 0..3 of the stage) per row, read once per
+//   stage per row block and fed to the MFMA with op_sel picking the k-step's
+//   byte, as for MXFP8.  When a tile's stages come in whole chunks of four
+//   (K % 512 == 0) a row's scales arrive 16 bytes (four stages) at a time
+//   into two alternating chunk buffers, a quarter of the next chunk's rows
+//   per stage, so a scale row costs one memory request per four stages (a
+//   per-stage dword of each of the tile's 512 rows costs as many requests as
+//   the stage's operand rows); else one dword wave-load per wave and stage
+//   into per-stage slots.
 //
 // Problems this kernel takes (the host checks): FP6 on both operands,
 // K-major, K a multiple of 128 (whole stages; rows of whole dwords of
@@ -50,11 +56,17 @@ constexpr int kOp = S::TM * kRow;                      // one operand's part of 
 constexpr int kSlot = 2 * kOp;                         // A rows, then B rows
 constexpr int NS = 2;
 constexpr int kScaleSlot = (S::TM + S::TN) * 4;        // A rows, then B rows, 4 bytes each
+constexpr int kChunk = 16;                             // chunked scales: bytes per row per chunk
+constexpr int kSpc = kChunk / 4;                       // stages per chunk
+constexpr int kChunkBuf = (S::TM + S::TN) * kChunk;    // one chunk buffer: A rows, then B rows
 constexpr int kLdsS = NS * kSlot;
-constexpr int kLds = kLdsS + NS * kScaleSlot;
+template <bool CH>
+constexpr int lds_bytes() { return kLdsS + (CH ? 2 * kChunkBuf : NS * kScaleSlot); }
 constexpr int kLoadsOp = S::TM / 8 / S::NW;            // wave-loads per wave, operand and stage
 constexpr int kLoads = 2 * kLoadsOp + 1;               // and one scale wave-load
-static_assert(kLds <= 160 * 1024, "LDS budget");
+static_assert(lds_bytes<false>() <= 160 * 1024 && lds_bytes<true>() <= 160 * 1024, "LDS budget");
+static_assert((S::TM + S::TN) / kSpc == 16 * S::NW && S::TM % ((S::TM + S::TN) / kSpc) == 0,
+              "a chunk portion is one 16-row dword wave-load per wave, all of one operand");
 static_assert(S::TM == S::TN && S::MB == 4 && S::NB == 2, "square tiles, 128 x 64 per wave");
 static_assert(S::NW * epilogue_wave_bytes<S>() <= kSlot, "epilogue staging fits in a ring slot");
 static_assert((S::TM + S::TN) * 4 == S::NW * 256, "one scale wave-load per wave");
@@ -80,6 +92,16 @@ struct Lane {
     uint32_t fa, fb;        // LDS address of the lane's first cell: block 0, k-step 0, slot 0, swizzle applied
     uint32_t r8;            // (lane / 8) * lda: the lane's row within a wave-load
     uint32_t x;             // (lane % 8) ^ (lane / 8): the lane's cell within a wave-load, before (L % 8)
+    uint32_t sa, sb;        // chunked scales: LDS address of the lane's A / B row in chunk buffer 0, with
+                            // 8 (bit 4 of the row) in bit 3
+};
+
+// Where the chunked scales of a stage come from and go: the stage reads
+// dword j of chunk buffer pc and loads portion j of chunk lchunk, from the
+// scale rows sa / sb, into buffer pc ^ 1.
+struct Chunk6 {
+    int pc, j, lchunk;
+    __amdgpu_buffer_rsrc_t sa, sb;
 };
 
 typedef __attribute__((ext_vector_type(3))) int i32x3;
@@ -122,6 +144,20 @@ __device__ __forceinline__ void read_scales(Sc6 &sc, const uint8_t *lds, int slo
         sc.b[j] = lds_read<uint32_t>(lds, base + (uint32_t)((S::TM + c.wn * 64 + 32 * j + c.lr) * 4));
 }
 
+// Chunked layout: a row's 16 bytes hold its dwords (one per stage) in the
+// order d ^ 2 s, s = bit 4 of the row's index in the concatenated list: the
+// 32 rows one read covers are 16 bytes apart, so rows r and r + 16 would
+// share banks, and the swizzle moves r + 16's dword to other ones.
+__device__ __forceinline__ void read_scales_chunk(Sc6 &sc, const uint8_t *lds, int pc, int j, const Lane &c)
+{
+    const uint32_t o = (uint32_t)(pc * kChunkBuf), jb = (uint32_t)(4 * j);
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i) sc.a[i] = lds_read<uint32_t>(lds, (c.sa ^ jb) + o + (uint32_t)(i * 32 * kChunk));
+#pragma unroll
+    for (int jj = 0; jj < S::NB; ++jj)
+        sc.b[jj] = lds_read<uint32_t>(lds, (c.sb ^ jb) + o + (uint32_t)(jj * 32 * kChunk));
+}
+
 // Lane half h takes blocks 2 kk + h of the stage: byte 2 kk after a shift by 8 h.
 __device__ __forceinline__ void adjust(Sc6 &sc, const Lane &c)
 {
@@ -157,14 +193,37 @@ __device__ __forceinline__ void load_scales(uint8_t *lds, int slot, const Target
     __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? tg.rsa : tg.rsb, (lds_void *)(lds + dst), 4, off, 0, 0, 0);
 }
 
-// Load n (0 .. kLoads-1) of the wave's share of a stage.
+// Chunked scales: portion u (0 .. 3) of chunk `chunk` (bytes 16 chunk ..
+// 16 chunk + 15 of every scale row) into chunk buffer `pc`: rows 128 u ..
+// 128 u + 127 of the concatenated list (A rows, then B rows), wave w taking
+// rows 128 u + 16 w .. + 15: lane i lands on dword position i % 4 of row
+// i / 4 and fetches the row's dword (i % 4) ^ 2 s, s = bit 4 of the row's
+// index (that of the wave-load's first row; see read_scales_chunk).  Dwords
+// past a row's end and rows past the operand's read zero.
+__device__ __forceinline__ void load_scale_portion(uint8_t *lds, int pc, __amdgpu_buffer_rsrc_t sa,
+                                                   __amdgpu_buffer_rsrc_t sb, int chunk, int u, const Lane &c, int sld)
+{
+    const int row0 = u * ((S::TM + S::TN) / kSpc) + c.w * 16;     // wave-uniform
+    const bool is_a = row0 < S::TM;
+    const int r = (is_a ? row0 : row0 - S::TM) + (c.lane >> 2);
+    const int o = chunk * kChunk + 4 * ((c.lane & 3) ^ (2 * ((row0 >> 4) & 1)));
+    const uint32_t off = (uint32_t)(r * sld + o) | (o < sld ? 0u : kOOB);
+    const int dst = kLdsS + pc * kChunkBuf + row0 * kChunk;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? sa : sb, (lds_void *)(lds + dst), 4, off, 0, 0, 0);
+}
+
+// Load n (0 .. kLoads-1) of the wave's share of a stage: operand rows, then
+// the stage's scales (per stage) or a portion of the next chunk (CH).
+template <bool CH>
 __device__ __forceinline__ void load_piece(uint8_t *lds, int slot, const Target &tg, int ks, int n, const Lane &c,
-                                           const Params &p)
+                                           const Params &p, const Chunk6 &cp)
 {
     if (n < kLoadsOp)
         load_op<true>(lds, slot, tg.ra, ks, n, c, p.lda);
     else if (n < 2 * kLoadsOp)
         load_op<false>(lds, slot, tg.rb, ks, n - kLoadsOp, c, p.lda);
+    else if constexpr (CH)
+        load_scale_portion(lds, cp.pc ^ 1, cp.sa, cp.sb, cp.lchunk, cp.j, c, p.sld);
     else
         load_scales(lds, slot, tg, ks, c, p.sld);
 }
@@ -181,9 +240,10 @@ __device__ __forceinline__ void mma(f32x16 &acc, const Frag6 &a, uint32_t sa, co
 // meanwhile: B first (into the other buffer), then each A fragment right
 // after its last MFMA.  With LOADS, the wave's load pieces of stage ks go
 // out one after each MFMA (the ninth after the last).
-template <int CA, int CB, int SEL, int CUR, bool RD, bool LOADS>
+template <int CA, int CB, int SEL, int CUR, bool RD, bool LOADS, bool CH>
 __device__ __forceinline__ void mfmas(f32x16 (&acc)[S::MB][S::NB], Frags6 &F, const Sc6 &sc, uint8_t *lds, int rs,
-                                      int rk, int lslot, const Target &tg, int ks, const Lane &c, const Params &p)
+                                      int rk, int lslot, const Target &tg, int ks, const Lane &c, const Params &p,
+                                      const Chunk6 &cp)
 {
     if constexpr (RD) {
 #pragma unroll
@@ -198,8 +258,8 @@ __device__ __forceinline__ void mfmas(f32x16 (&acc)[S::MB][S::NB], Frags6 &F, co
                 constexpr int per = S::MB * S::NB;           // 8 MFMAs, 9 loads: two after the last
                 const int m = i * S::NB + j;
                 DBS_FENCE();
-                load_piece(lds, lslot, tg, ks, m, c, p);
-                if (m == per - 1) load_piece(lds, lslot, tg, ks, per, c, p);
+                load_piece<CH>(lds, lslot, tg, ks, m, c, p, cp);
+                if (m == per - 1) load_piece<CH>(lds, lslot, tg, ks, per, c, p, cp);
                 DBS_FENCE();
             }
         }
@@ -215,16 +275,20 @@ __device__ __forceinline__ void mfmas(f32x16 (&acc)[S::MB][S::NB], Frags6 &F, co
 // other slot.  On entry F holds the previous stage's last k-step (A, and B
 // in buffer 1; zeros and unit scales at a tile's first stage): its MFMAs go
 // first, behind the reads of this stage's scales and first k-step.
-template <int CA, int CB>
+template <int CA, int CB, bool CH>
 __device__ __forceinline__ void stage(f32x16 (&acc)[S::MB][S::NB], Frags6 &F, Sc6 &sprev, Sc6 &scur, uint8_t *lds,
-                                      int rs, const Target &tg, int ks, const Lane &c, const Params &p)
+                                      int rs, const Target &tg, int ks, const Lane &c, const Params &p,
+                                      const Chunk6 &cp)
 {
-    read_scales(scur, lds, rs, c);
+    if constexpr (CH)
+        read_scales_chunk(scur, lds, cp.pc, cp.j, c);
+    else
+        read_scales(scur, lds, rs, c);
     DBS_FENCE();
-    mfmas<CA, CB, 2, 1, true, true>(acc, F, sprev, lds, rs, 0, rs ^ 1, tg, ks, c, p);
+    mfmas<CA, CB, 2, 1, true, true, CH>(acc, F, sprev, lds, rs, 0, rs ^ 1, tg, ks, c, p, cp);
     DBS_FENCE();
     adjust(scur, c);
-    mfmas<CA, CB, 0, 0, true, false>(acc, F, scur, lds, rs, 1, rs ^ 1, tg, ks, c, p);
+    mfmas<CA, CB, 0, 0, true, false, CH>(acc, F, scur, lds, rs, 1, rs ^ 1, tg, ks, c, p, cp);
     sprev = scur;
     // this wave's loads have landed and its reads of slot rs are done; after
     // the barrier every wave's have: the next stage may read the other slot
@@ -234,11 +298,11 @@ __device__ __forceinline__ void stage(f32x16 (&acc)[S::MB][S::NB], Frags6 &F, Sc
 
 }  // namespace f6
 
-template <int CA, int CB>
+template <int CA, int CB, bool CH>
 __global__ __launch_bounds__(512, 1) void gemm_mxfp6_kernel(Params p)
 {
     using namespace f6;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<CH>()];
     Lane c;
     const int t = threadIdx.x;
     c.lane = t & 63;
@@ -255,6 +319,10 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp6_kernel(Params p)
     c.fb = (uint32_t)(kOp + (c.wn * 64 + c.lr) * kRow) | ((sw << 4) ^ (uint32_t)(32 * c.h));
     c.r8 = (uint32_t)((c.lane >> 3) * p.lda);
     c.x = (uint32_t)((c.lane & 7) ^ (c.lane >> 3));
+    // chunk rows wm*128 + lr (A), TM + wn*64 + lr (B): bit 4 of either is that of lr
+    const uint32_t s4 = (uint32_t)(8 * ((c.lr >> 4) & 1));
+    c.sa = (uint32_t)(kLdsS + (c.wm * 128 + c.lr) * kChunk) | s4;
+    c.sb = (uint32_t)(kLdsS + (S::TM + c.wn * 64 + c.lr) * kChunk) | s4;
 
     const int ntiles = p.tiles_m * p.tiles_n;
     const int nwg = gridDim.x, wg = blockIdx.x;
@@ -264,8 +332,16 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp6_kernel(Params p)
     // the first stage of the first tile; the stage stream then runs one
     // stage ahead across the workgroup's tiles
     Target ld = tile_target<kMXFP8, S>(p, tile);
+    Chunk6 cp{0, 0, 0, ld.rsa, ld.rsb};
+    if constexpr (CH) {
 #pragma unroll
-    for (int n = 0; n < kLoads; ++n) load_piece(lds, 0, ld, 0, n, c, p);
+        for (int n = 0; n < 2 * kLoadsOp; ++n) load_piece<CH>(lds, 0, ld, 0, n, c, p, cp);
+#pragma unroll
+        for (int u = 0; u < kSpc; ++u) load_scale_portion(lds, 0, cp.sa, cp.sb, 0, u, c, p.sld);
+    } else {
+#pragma unroll
+        for (int n = 0; n < kLoads; ++n) load_piece<CH>(lds, 0, ld, 0, n, c, p, cp);
+    }
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
     Frags6 F;
@@ -288,20 +364,48 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp6_kernel(Params p)
         for (int j = 0; j < S::NB; ++j) sprev.b[j] = 0x7F7F7F7Fu;
 
         const int next = tile + nwg;
-        for (int s = 0; s < p.nk; ++s) {
-            // stage s loads the next one of the stream: this tile's s + 1,
-            // or the next tile's first
-            int ks = s + 1;
-            if (ks == p.nk) {
-                ks = 0;
-                ld = next < ntiles ? tile_target<kMXFP8, S>(p, next) : null_target();
+        if constexpr (CH) {
+            // the chunk stream runs one chunk ahead: the tile's last chunk
+            // loads the next tile's first (cp.sa / cp.sb switch to its scale
+            // rows there; ld, the operand rows, at the tile's last stage)
+            const int nch = p.nk / kSpc;
+            for (int s = 0; s < p.nk; ++s) {
+                int ks = s + 1;
+                if (ks == p.nk) {
+                    ks = 0;
+                    ld = next < ntiles ? tile_target<kMXFP8, S>(p, next) : null_target();
+                }
+                cp.j = s & (kSpc - 1);
+                cp.lchunk = s / kSpc + 1;
+                if (cp.lchunk == nch) {
+                    cp.lchunk = 0;
+                    if (cp.j == 0) {
+                        const Target nt = next < ntiles ? tile_target<kMXFP8, S>(p, next) : null_target();
+                        cp.sa = nt.rsa;
+                        cp.sb = nt.rsb;
+                    }
+                }
+                stage<CA, CB, CH>(acc, F, sprev, scur, lds, rs, ld, ks, c, p, cp);
+                if (cp.j == kSpc - 1) cp.pc ^= 1;
+                xs = rs;
+                rs ^= 1;
             }
-            stage<CA, CB>(acc, F, sprev, scur, lds, rs, ld, ks, c, p);
-            xs = rs;
-            rs ^= 1;
+        } else {
+            for (int s = 0; s < p.nk; ++s) {
+                // stage s loads the next one of the stream: this tile's s + 1,
+                // or the next tile's first
+                int ks = s + 1;
+                if (ks == p.nk) {
+                    ks = 0;
+                    ld = next < ntiles ? tile_target<kMXFP8, S>(p, next) : null_target();
+                }
+                stage<CA, CB, CH>(acc, F, sprev, scur, lds, rs, ld, ks, c, p, cp);
+                xs = rs;
+                rs ^= 1;
+            }
         }
         // the last k-step
-        mfmas<CA, CB, 2, 1, false, false>(acc, F, sprev, lds, 0, 0, 0, ld, 0, c, p);
+        mfmas<CA, CB, 2, 1, false, false, CH>(acc, F, sprev, lds, 0, 0, 0, ld, 0, c, p, cp);
 
         // epilogue through the slot the last stage read (refilled only by the
         // stage after the next barrier)
@@ -332,13 +436,20 @@ hipError_t launch_gemm_mxfp6(const Params &p0, int grid, hipStream_t stream)
     p.nk = p.K / f6::kKs;
     if (p.K % f6::kKs || p.nk < 1 || !p.scales_aligned || p.lay != 0) return hipErrorInvalidValue;
     const int ca = p.ec & 7, cb = (p.ec >> 3) & 7;
+    // chunked scales when every tile's stages come in whole chunks
+    const bool ch = p.nk % f6::kSpc == 0;
+#define DBS_F6(A_, B_) \
+    case (A_) | ((B_) << 3): \
+        if (ch) \
+            hipLaunchKernelGGL((gemm_mxfp6_kernel<A_, B_, true>), dim3(grid), dim3(512), 0, stream, p); \
+        else \
+            hipLaunchKernelGGL((gemm_mxfp6_kernel<A_, B_, false>), dim3(grid), dim3(512), 0, stream, p); \
+        break;
     switch (ca | (cb << 3)) {
-    case 2 | (2 << 3): hipLaunchKernelGGL((gemm_mxfp6_kernel<2, 2>), dim3(grid), dim3(512), 0, stream, p); break;
-    case 2 | (3 << 3): hipLaunchKernelGGL((gemm_mxfp6_kernel<2, 3>), dim3(grid), dim3(512), 0, stream, p); break;
-    case 3 | (2 << 3): hipLaunchKernelGGL((gemm_mxfp6_kernel<3, 2>), dim3(grid), dim3(512), 0, stream, p); break;
-    case 3 | (3 << 3): hipLaunchKernelGGL((gemm_mxfp6_kernel<3, 3>), dim3(grid), dim3(512), 0, stream, p); break;
+        DBS_F6(2, 2) DBS_F6(2, 3) DBS_F6(3, 2) DBS_F6(3, 3)
     default: return hipErrorInvalidValue;
     }
+#undef DBS_F6
     return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 """GPU parity of the native-rate FP6 path (FP6 on both operands; 256 x 256
-tiles; K a multiple of 128): every E2M3 / E3M2 pairing against the oracle,
+tiles; K a multiple of 128; scales per stage, or in chunks of four stages
+when K % 512 == 0): every E2M3 / E3M2 pairing against the oracle,
 codes over all 64 values with random scales, exact permutation products with
 non-unit scales, ragged edges, a second persistent round, and the smallest K
 the three-slot ring takes.  Smaller FP6 problems take the widening path
@@ -42,10 +43,14 @@ def check(w, D, seed):
         _gpu.check_sampled("mxfp8", w, D, em, en)
 
 
-# 81 tiles (a third of the CUs); ragged 9 x 10 tiles with K of three stages
-# (the ring wraps inside a tile); 289 tiles (a second persistent round) with
-# K of two stages, the smallest the ring takes
-SHAPES = [(2304, 2304, 1024), (2200, 2500, 384), (4352, 4352, 256)]
+# Per-stage scales (K % 512 != 0): ragged 9 x 10 tiles with K of three
+# stages (the ring wraps inside a tile); 289 tiles (a second persistent
+# round) with K of two stages, the smallest the ring takes.  Chunked scales
+# (four stages a chunk): 81 tiles with two chunks; 289 tiles with one chunk
+# (every chunk load fetches the next tile's); 289 tiles with three chunks
+# (the chunk buffers alternate across tiles); ragged tiles with four chunks.
+SHAPES = [(2200, 2500, 384), (4352, 4352, 256), (2304, 2304, 1024), (4352, 4352, 512), (4352, 4352, 1536),
+          (2200, 2500, 2048)]
 
 
 @pytest.mark.parametrize("pair", PAIRS, ids=_pid)
@@ -69,13 +74,14 @@ def test_fp6_native_random_codes(pair):
     _gpu.check_full("mxfp8", w, D)
 
 
+@pytest.mark.parametrize("K", [2304, 2048], ids=["per-stage-scales", "chunked-scales"])
 @pytest.mark.parametrize("pair", PAIRS, ids=_pid)
-def test_fp6_native_exact_permutation(pair):
+def test_fp6_native_exact_permutation(pair, K):
     """A (random codes, random scales) times a permutation matrix in B's
     format with non-unit scales: every output is one element of A times two
     powers of two, compared bit for bit (sampled)."""
     ea, eb = pair
-    M, K = 2304, 2304
+    M = 2304
     N = K
     _gpu.say(f"[fp6] {_pid(pair)} exact permutation {M}x{N}x{K}")
     rng = np.random.default_rng(59)
@@ -91,12 +97,13 @@ def test_fp6_native_exact_permutation(pair):
     _gpu.check_exact_sampled("mxfp8", w, D, em, en)
 
 
-def test_fp6_native_unit_scale_identity():
+@pytest.mark.parametrize("K", [2304, 2048], ids=["per-stage-scales", "chunked-scales"])
+def test_fp6_native_unit_scale_identity(K):
     """B = the identity (N = K) with unit scales: D reproduces A's decoded
     values exactly, so every fragment, unit rotation and ring slot lands
     where the MFMA expects it."""
-    M, K = 2304, 2304
-    _gpu.say("[fp6] identity")
+    M = 2304
+    _gpu.say(f"[fp6] identity K={K}")
     rng = np.random.default_rng(61)
     w = _pins.make_w_mx8("e2m3", "e2m3", M, K, K, rng, scale_lo=127, scale_hi=127)
     codes = np.zeros((K, K), np.uint8)
