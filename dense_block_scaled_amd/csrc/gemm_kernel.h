@@ -590,13 +590,24 @@ __device__ __forceinline__ void read_scales(Scales<S> &sc, const uint8_t *lds, i
         read_scale_row<FMT>(sc.b[j], lds, c.sb + (uint32_t)(slot * S::TN * BPS + j * 32 * BPS));
 }
 
-// Chunked layout: stage j (0 .. scale_spc - 1) of the chunk in buffer `par`.
-// A row's 16 chunk bytes hold its dwords in the order d ^ 2 s, s = bit 4 of
-// the row's index in the concatenated list (see dma_scale_portion): the 32
-// rows one read covers are 16 bytes apart, so rows r and r + 16 share four
-// banks, and the swizzle puts their dwords in different ones.  c.sa and c.sb
-// carry 8 s in their (otherwise zero) bit 3, so the stage's byte offset
+// Chunked layout: a row's 16 chunk bytes hold dword d at position
+// d ^ chunk_swz(row), row = the row's index in the concatenated list (see
+// dma_scale_portion).  The 32 rows one scale read covers lie 16 bytes apart:
+// rows 8 apart are 128 bytes apart and rows 16 apart 256, so without the
+// swizzle they would meet in one bank whether the LDS serves a read 128 or
+// 256 bytes at a time.  Dword reads (E4M3; 32 lanes) take position
+// d ^ ((row / 8) % 4), so rows r, r + 8, r + 16, r + 24 use four different
+// dwords; 8-byte reads (E2M1; a stage's two dwords stay together) swap the
+// row's two halves by bit 3 ^ bit 4 of the row, which separates rows 8 apart
+// (16 lanes a pass) and rows 16 apart (32 lanes a pass).  c.sa and c.sb carry
+// 4 chunk_swz in their (otherwise zero) bits 2-3, so the stage's byte offset
 // enters by XOR.
+template <int FMT>
+__device__ __forceinline__ constexpr int chunk_swz(int row)
+{
+    return Fmt<FMT>::BPS == 4 ? (row >> 3) & 3 : 2 * (((row >> 3) ^ (row >> 4)) & 1);
+}
+
 template <int FMT, class S>
 __device__ __forceinline__ void read_scales_chunk(Scales<S> &sc, const uint8_t *lds, int par, int j, const Ctx<S> &c)
 {
@@ -729,8 +740,8 @@ __device__ __forceinline__ void dma_scale_rows16(uint8_t *lds, int slot, const T
 // u R .. (u + 1) R - 1 of the concatenated row list (A rows, then B rows;
 // R = (TM + TN) / scale_spc), 16 rows per dword wave-load: lane i lands on
 // dword position i % 4 of row i / 4 and fetches the row's dword
-// (i % 4) ^ 2 s, s = bit 4 of the row's index (the same for the 16 rows of a
-// wave-load; see read_scales_chunk).  Dwords past a row's end read zero.
+// (i % 4) ^ chunk_swz(row) (see read_scales_chunk).  Dwords past a row's end
+// read zero.
 template <int FMT, class S>
 __device__ __forceinline__ void dma_scale_portion(uint8_t *lds, int par, const Target &stg, int chunk, int u,
                                                   const Ctx<S> &c, int sld)
@@ -740,7 +751,7 @@ __device__ __forceinline__ void dma_scale_portion(uint8_t *lds, int par, const T
 #pragma unroll
     for (int k = 0; k < NLP / S::NW; ++k) {
         const int row0 = u * R + (c.w + k * S::NW) * 16;      // wave-uniform
-        const int o = chunk * kScaleChunk + 4 * ((c.lane & 3) ^ (2 * ((row0 >> 4) & 1)));
+        const int o = chunk * kScaleChunk + 4 * ((c.lane & 3) ^ chunk_swz<FMT>(row0 + (c.lane >> 2)));
         const bool is_a = row0 < S::TM;
         const int r = (is_a ? row0 : row0 - S::TM) + (c.lane >> 2);
         const uint32_t off = (uint32_t)(r * sld + o) | (o < sld ? 0u : kOOB);
@@ -1683,10 +1694,10 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
     c.fa = (uint32_t)(S::kLdsA + ra0 * kRowBytes + ((c.h ^ swz(ra0)) << 4));
     c.fb = (uint32_t)(S::kLdsB + rb0 * kRowBytes + (((adirect<FMT, S>() ? 4 * c.h : c.h) ^ swz(rb0)) << 4));
     if constexpr (SM == kScalesChunk) {
-        // bit 4 of the row index swizzles the row's dwords (read_scales_chunk);
-        // rows 32 i further down keep it
-        c.sa = (uint32_t)(S::kLdsS + ra0 * kScaleChunk) | (uint32_t)(8 * ((ra0 >> 4) & 1));
-        c.sb = (uint32_t)(S::kLdsS + (S::TM + rb0) * kScaleChunk) | (uint32_t)(8 * (((S::TM + rb0) >> 4) & 1));
+        // bits 3-4 of the row index swizzle the row's dwords
+        // (read_scales_chunk); rows 32 i further down keep them
+        c.sa = (uint32_t)(S::kLdsS + ra0 * kScaleChunk) | (uint32_t)(4 * chunk_swz<FMT>(ra0));
+        c.sb = (uint32_t)(S::kLdsS + (S::TM + rb0) * kScaleChunk) | (uint32_t)(4 * chunk_swz<FMT>(S::TM + rb0));
     } else {
         c.sa = (uint32_t)(S::kLdsS + ra0 * BPS);
         c.sb = (uint32_t)(S::kLdsS + S::NS * S::TM * BPS + rb0 * BPS);

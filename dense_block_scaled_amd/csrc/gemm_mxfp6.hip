@@ -93,7 +93,7 @@ struct Lane {
     uint32_t r8;            // (lane / 8) * lda: the lane's row within a wave-load
     uint32_t x;             // (lane % 8) ^ (lane / 8): the lane's cell within a wave-load, before (L % 8)
     uint32_t sa, sb;        // chunked scales: LDS address of the lane's A / B row in chunk buffer 0, with
-                            // 8 (bit 4 of the row) in bit 3
+                            // 4 ((row / 8) % 4) in bits 2-3
 };
 
 // Where the chunked scales of a stage come from and go: the stage reads
@@ -144,10 +144,11 @@ __device__ __forceinline__ void read_scales(Sc6 &sc, const uint8_t *lds, int slo
         sc.b[j] = lds_read<uint32_t>(lds, base + (uint32_t)((S::TM + c.wn * 64 + 32 * j + c.lr) * 4));
 }
 
-// Chunked layout: a row's 16 bytes hold its dwords (one per stage) in the
-// order d ^ 2 s, s = bit 4 of the row's index in the concatenated list: the
-// 32 rows one read covers are 16 bytes apart, so rows r and r + 16 would
-// share banks, and the swizzle moves r + 16's dword to other ones.
+// Chunked layout: a row's 16 bytes hold dword d (one per stage) at position
+// d ^ ((row / 8) % 4), row = the row's index in the concatenated list: the
+// 32 rows one read covers are 16 bytes apart, so rows 8 and 16 apart (128
+// and 256 bytes) would meet in one bank, and the swizzle gives rows r,
+// r + 8, r + 16, r + 24 four different dwords.
 __device__ __forceinline__ void read_scales_chunk(Sc6 &sc, const uint8_t *lds, int pc, int j, const Lane &c)
 {
     const uint32_t o = (uint32_t)(pc * kChunkBuf), jb = (uint32_t)(4 * j);
@@ -197,16 +198,16 @@ __device__ __forceinline__ void load_scales(uint8_t *lds, int slot, const Target
 // 16 chunk + 15 of every scale row) into chunk buffer `pc`: rows 128 u ..
 // 128 u + 127 of the concatenated list (A rows, then B rows), wave w taking
 // rows 128 u + 16 w .. + 15: lane i lands on dword position i % 4 of row
-// i / 4 and fetches the row's dword (i % 4) ^ 2 s, s = bit 4 of the row's
-// index (that of the wave-load's first row; see read_scales_chunk).  Dwords
-// past a row's end and rows past the operand's read zero.
+// i / 4 and fetches the row's dword (i % 4) ^ ((row / 8) % 4) (see
+// read_scales_chunk).  Dwords past a row's end and rows past the operand's
+// read zero.
 __device__ __forceinline__ void load_scale_portion(uint8_t *lds, int pc, __amdgpu_buffer_rsrc_t sa,
                                                    __amdgpu_buffer_rsrc_t sb, int chunk, int u, const Lane &c, int sld)
 {
     const int row0 = u * ((S::TM + S::TN) / kSpc) + c.w * 16;     // wave-uniform
     const bool is_a = row0 < S::TM;
     const int r = (is_a ? row0 : row0 - S::TM) + (c.lane >> 2);
-    const int o = chunk * kChunk + 4 * ((c.lane & 3) ^ (2 * ((row0 >> 4) & 1)));
+    const int o = chunk * kChunk + 4 * ((c.lane & 3) ^ (((row0 + (c.lane >> 2)) >> 3) & 3));
     const uint32_t off = (uint32_t)(r * sld + o) | (o < sld ? 0u : kOOB);
     const int dst = kLdsS + pc * kChunkBuf + row0 * kChunk;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? sa : sb, (lds_void *)(lds + dst), 4, off, 0, 0, 0);
@@ -319,8 +320,8 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp6_kernel(Params p)
     c.fb = (uint32_t)(kOp + (c.wn * 64 + c.lr) * kRow) | ((sw << 4) ^ (uint32_t)(32 * c.h));
     c.r8 = (uint32_t)((c.lane >> 3) * p.lda);
     c.x = (uint32_t)((c.lane & 7) ^ (c.lane >> 3));
-    // chunk rows wm*128 + lr (A), TM + wn*64 + lr (B): bit 4 of either is that of lr
-    const uint32_t s4 = (uint32_t)(8 * ((c.lr >> 4) & 1));
+    // chunk rows wm*128 + lr (A), TM + wn*64 + lr (B): bits 3-4 of either are those of lr
+    const uint32_t s4 = (uint32_t)(4 * ((c.lr >> 3) & 3));
     c.sa = (uint32_t)(kLdsS + (c.wm * 128 + c.lr) * kChunk) | s4;
     c.sb = (uint32_t)(kLdsS + (S::TM + c.wn * 64 + c.lr) * kChunk) | s4;
 

@@ -50,11 +50,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#if defined(__HIPCC__) || defined(__HIP_PLATFORM_AMD__)
-#include <hip/hip_runtime_api.h>
-#else
+/* the HIP runtime's stream handle (hip_runtime_api.h declares the same type;
+ * repeating an identical typedef is valid C11 and C++) */
 typedef struct ihipStream_t *hipStream_t;
-#endif
 
 #ifdef __cplusplus
 extern "C" {
