@@ -640,7 +640,7 @@ __device__ __forceinline__ void read_a(Frags<FMT, S> &f, int i, const uint8_t *l
     else
         f.a[i] = read_frag<FMT>(lds, c.fa, (uint32_t)(slot * S::kSlotA), kk, i);
     if constexpr (FMT == kNVFP4R)
-        f.sa[i] = lds_read<uint16_t>(lds, c.sa + (uint32_t)(slot * S::TM * 16 + i * 32 * 16 + 4 * kk + 2 * c.h));
+        f.sa[i] = lds_read<uint16_t>(lds, (c.sa ^ (uint32_t)(4 * kk)) + (uint32_t)(slot * S::TM * 16 + i * 32 * 16 + 2 * c.h));
 }
 
 template <int FMT, class S>
@@ -654,7 +654,7 @@ __device__ __forceinline__ void read_b(Frags<FMT, S> &f, int j, const uint8_t *l
     else
         f.b[j] = read_frag<FMT, KSH>(lds, c.fb, (uint32_t)(slot * S::kSlotB), kk, j);
     if constexpr (FMT == kNVFP4R)
-        f.sb[j] = lds_read<uint16_t>(lds, c.sb + (uint32_t)(slot * S::TN * 16 + j * 32 * 16 + 4 * kk + 2 * c.h));
+        f.sb[j] = lds_read<uint16_t>(lds, (c.sb ^ (uint32_t)(4 * kk)) + (uint32_t)(slot * S::TN * 16 + j * 32 * 16 + 2 * c.h));
 }
 
 // Fragments of a packed E2M1 operand of an 8-bit kernel: MXFP4 k-step
@@ -707,7 +707,9 @@ __device__ __forceinline__ void dma_scales(uint8_t *lds, int slot, const Target 
         const int nn = is_a ? n : n - NSA;
         const int d = nn * 64 + c.lane;
         const int row = d / WPR, word = d % WPR;
-        const int o = ks * BPS + 4 * word;
+        // raw NVFP4 (16-byte rows): position `word` of the row holds its
+        // dword word ^ ((row / 8) % 4) (see the kernel's scale addresses)
+        const int o = ks * BPS + 4 * (BPS == 16 ? word ^ ((row >> 3) & 3) : word);
         const uint32_t off = (uint32_t)(row * sld + o) | (o < sld ? 0u : kOOB);
         const int dst = S::kLdsS + (is_a ? slot * S::TM * BPS : S::NS * S::TM * BPS + slot * S::TN * BPS) + nn * 256;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? tg.rsa : tg.rsb, (lds_void *)(lds + dst), 4, off, 0, 0, 0);
@@ -1698,6 +1700,14 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
         // (read_scales_chunk); rows 32 i further down keep them
         c.sa = (uint32_t)(S::kLdsS + ra0 * kScaleChunk) | (uint32_t)(4 * chunk_swz<FMT>(ra0));
         c.sb = (uint32_t)(S::kLdsS + (S::TM + rb0) * kScaleChunk) | (uint32_t)(4 * chunk_swz<FMT>(S::TM + rb0));
+    } else if constexpr (FMT == kNVFP4R && SM == kScalesStage) {
+        // raw NVFP4 scale rows of 16 bytes read 2 bytes of one dword per
+        // lane: rows 8 and 16 apart (128 and 256 bytes) would meet in one
+        // bank, so dword d of a row sits at position d ^ ((row / 8) % 4)
+        // (dma_scales), carried here in bits 2-3 for the k-step's XOR;
+        // rows 32 i further down keep them
+        c.sa = (uint32_t)(S::kLdsS + ra0 * BPS) | (uint32_t)(4 * ((ra0 >> 3) & 3));
+        c.sb = (uint32_t)(S::kLdsS + S::NS * S::TM * BPS + rb0 * BPS) | (uint32_t)(4 * ((rb0 >> 3) & 3));
     } else {
         c.sa = (uint32_t)(S::kLdsS + ra0 * BPS);
         c.sb = (uint32_t)(S::kLdsS + S::NS * S::TM * BPS + rb0 * BPS);
@@ -2104,7 +2114,6 @@ hipError_t launch_nvfp4_raw(const Params &p, int grid, hipStream_t stream)
     const bool r16 = p.scales_aligned && p.K % 256 == 0 &&
                      ((reinterpret_cast<uintptr_t>(p.sA) | reinterpret_cast<uintptr_t>(p.sB)) & 15) == 0;
     if constexpr (std::is_same<S, Square>::value) {
-        if (r16) return launch_one<kNVFP4R, kScalesRows16, Square>(p, grid, stream);
         if (p.scales_aligned) return launch_one<kNVFP4R, kScalesStage, Square>(p, grid, stream);
         if (p.lay == 0) return launch_fmt<kNVFP4, S>(p, grid, stream);
         return launch_one<kNVFP4R, kScalesRegs, SquareW4>(p, grid, stream);
