@@ -16,7 +16,9 @@ MXFP4 at 8192^3 and 16384^3, NVFP4 square and skinny (256 x 16384 x 8192),
 the opt-in lossy FP8- and FP4-rate NVFP4 paths, E4M3 x E2M1 and MXFP6.
 With --only, --fmt also names workloads outside that table (the skinny
 BF16/MXFP8/MXFP4 shapes, E2M1 x E4M3, E4M3 x E2M1 with K = 8064 on the
-widening path, E3M2 x E4M3 widened), and --layout hands A and/or B over
+widening path, E3M2 x E4M3 widened, BF16 on the decoupled-ring kernel
+with A released early or at the stage's end), and
+--layout hands A and/or B over
 MN-major.
 
 Each line is priced against the dense MFMA peak of the arithmetic its
@@ -90,6 +92,10 @@ W.update({
                                elems=("e4m3", "e2m1")),
     "mx_e3m2_e4m3": dict(c=2, shape=(8192, 8192, 8192), enc="mxfp8", kernel="mx_mixed", mfma="fp8",
                          elems=("e3m2", "e4m3")),
+    "bf16_rings_early_a": dict(c=1, shape=(8192, 8192, 8192), enc="bf16", kernel="bf16_ea", mfma="bf16"),
+    "bf16_rings_late_a": dict(c=1, shape=(8192, 8192, 8192), enc="bf16", kernel="bf16_el", mfma="bf16"),
+    "bf16_rings_early_a_4096": dict(c=1, shape=(4096, 4096, 4096), enc="bf16", kernel="bf16_ea", mfma="bf16"),
+    "bf16_rings_late_a_4096": dict(c=1, shape=(4096, 4096, 4096), enc="bf16", kernel="bf16_el", mfma="bf16"),
 })
 ORDER = ["bf16", "bf16_4096", "mxfp8", "mxfp4", "mxfp4_16384", "nvfp4", "nvfp4_skinny", "nvfp4_fp8",
          "nvfp4_fp8_skinny", "nvfp4_fp6", "nvfp4_fp6_skinny", "mx_e4m3_e2m1", "mx_e2m3_e2m3"]
@@ -112,7 +118,8 @@ PEAK_NOTE = {
 }
 KERNEL_SOURCES = ["dense_block_scaled_amd/csrc/" + f for f in
                   ("gemm_kernel.h", "launch.h", "gemm.hip", "gemm_bf16.hip", "gemm_mxfp8.hip", "gemm_mx8_e5m2.hip",
-                   "gemm_mx8_fp4.hip", "gemm_mxfp4.hip", "gemm_nvfp4.hip", "gemm_mxfp6.hip", "quant.hip")]
+                   "gemm_mx8_fp4.hip", "gemm_mxfp4.hip", "gemm_nvfp4.hip", "gemm_mxfp6.hip", "quant.hip",
+                   "gemm_bf16_ea.hip")]
 
 
 def log(msg):
@@ -195,6 +202,9 @@ def launcher(name, w, dev, out, lay="kk"):
     la, lb = int(lay[0] == "m"), int(lay[1] == "m")
     if kern == "bf16":
         return lambda: dbs.gemm_bf16(dev["A"], dev["B"], out=out, la=la, lb=lb)
+    if kern in ("bf16_ea", "bf16_el"):
+        early = kern == "bf16_ea"
+        return lambda: dbs.gemm_bf16_decoupled(dev["A"], dev["B"], out=out, early_release_a=early)
     if kern == "mxfp8":
         return lambda: dbs.gemm_mx("e4m3", dev["A"], dev["sA"], dev["B"], dev["sB"], K=K, out=out, la=la, lb=lb)
     if kern == "mxfp4":

@@ -10,6 +10,7 @@ error, these functions raise.
 
 Operand encodings (contiguous; K-major unless la / lb say MN_MAJOR):
   gemm_bf16(A, B)                     A: (M, K) bfloat16/uint16, B: (N, K)
+  gemm_bf16_decoupled(A, B)           the same on the decoupled-ring kernel (K-major, K > 64)
   gemm_mx(elem, A, sA, B, sB)         elem 'e4m3': A (M, K) uint8;
                                       elem 'e2m1': A (M, K/2) uint8, 2 per byte
                                       sA: (M, K/32) uint8 E8M0 codes
@@ -27,7 +28,7 @@ from pathlib import Path
 
 import torch
 
-__all__ = ["gemm_bf16", "gemm_mx", "gemm_mx_mixed", "gemm_nvfp4", "gemm_nvfp4_fp8", "gemm_nvfp4_fp8_noalloc", "nvfp4_fp8_workspace_bytes", "gemm_nvfp4_fp6", "nvfp4_fp6_workspace_bytes", "gemm_grouped_bf16", "gemm_grouped_mx", "gemm_grouped_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError",
+__all__ = ["gemm_bf16", "gemm_bf16_decoupled", "gemm_mx", "gemm_mx_mixed", "gemm_nvfp4", "gemm_nvfp4_fp8", "gemm_nvfp4_fp8_noalloc", "nvfp4_fp8_workspace_bytes", "gemm_nvfp4_fp6", "nvfp4_fp6_workspace_bytes", "gemm_grouped_bf16", "gemm_grouped_mx", "gemm_grouped_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError",
            "DBS_OK", "DBS_EINVAL", "DBS_EUNSUPPORTED", "DBS_EHIP", "K_MAJOR", "MN_MAJOR",
            "E4M3", "E5M2", "E2M3", "E3M2", "E2M1", "status_str"]
 
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
         P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.gemm_bf16.argtypes = [P, P, P, I64, I64, I64, I, I, P]
         L.gemm_bf16.restype = I
+        L.gemm_bf16_decoupled.argtypes = [P, P, P, I64, I64, I64, I, P]
+        L.gemm_bf16_decoupled.restype = I
         L.gemm_mx.argtypes = [I, P, P, P, P, P, I64, I64, I64, I, I, P]
         L.gemm_mx.restype = I
         L.gemm_mx_mixed.argtypes = [I, I, P, P, P, P, P, I64, I64, I64, I, I, P]
@@ -161,6 +164,21 @@ def gemm_bf16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
     pb = _dev(B, "B", dt, _shape(N, K, lb))
     out = _out(out, M, N, A)
     _check(lib().gemm_bf16(pa, pb, ctypes.c_void_p(out.data_ptr()), M, N, K, la, lb, _stream(A)))
+    return out
+
+
+def gemm_bf16_decoupled(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
+                        early_release_a: bool = True) -> torch.Tensor:
+    """gemm_bf16 (K-major A (M, K), B (N, K)) on the kernel with decoupled A
+    and B rings, A's slot released early (or at the stage's end); K > 64."""
+    M, K = A.shape
+    N = B.shape[0]
+    dt = (torch.bfloat16, torch.int16, torch.uint16)
+    pa = _dev(A, "A", dt, (M, K))
+    pb = _dev(B, "B", dt, (N, K))
+    out = _out(out, M, N, A)
+    _check(lib().gemm_bf16_decoupled(pa, pb, ctypes.c_void_p(out.data_ptr()), M, N, K, int(bool(early_release_a)),
+                                     _stream(A)))
     return out
 
 

@@ -30,7 +30,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 # largest first, so the longest compile starts first
 SOURCES = ["gemm_mx8_fp4.hip", "gemm_mxfp8.hip", "gemm_mx8_e5m2.hip", "gemm_nvfp4.hip", "gemm_mxfp4.hip", "gemm_mxfp6.hip",
-           "gemm_bf16.hip", "quant.hip", "gemm.hip", "scratch.hip", "dbs.cpp"]
+           "gemm_bf16.hip", "gemm_bf16_ea.hip", "quant.hip", "gemm.hip", "scratch.hip", "dbs.cpp"]
 
 
 def _jobs() -> int:

@@ -135,7 +135,9 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     // than 256 x 64 tiles, BF16 and NVFP4 10% slower.
     const bool fp6 = (cv & 3) >= 2 || (cv >> 2) >= 2;
     const bool mx = (fmt == dbs::kMXFP8 || fmt == dbs::kMXFP4 || fmt == dbs::kMXFP6) && cv == 0;
-    const int shape = ((mx ? 4 : 2) * sq_tiles <= cus || fp6) ? dbs::kShapeSkinny : dbs::kShapeSquare;
+    // (the early-A BF16 kernel has square tiles only)
+    const int shape = (fmt == dbs::kBF16EA || fmt == dbs::kBF16EL) ? dbs::kShapeSquare
+                      : ((mx ? 4 : 2) * sq_tiles <= cus || fp6) ? dbs::kShapeSkinny : dbs::kShapeSquare;
     const int tm = shape == dbs::kShapeSkinny ? dbs::kSkinnyTM : dbs::kSquareTM;
     const int tn = shape == dbs::kShapeSkinny ? dbs::kSkinnyTN : dbs::kSquareTN;
     p.tiles_m = (int)((M + tm - 1) / tm);
@@ -300,6 +302,18 @@ dbs_status gemm_bf16(const void *A, const void *B, void *D, int64_t M, int64_t N
     if (K % 8) return fail(DBS_EINVAL, "bf16: K must be a multiple of 8");
     if ((st = check_mn(la, lb, M, N, K, 16)) != DBS_OK) return st;
     return run(dbs::kBF16, A, nullptr, B, nullptr, D, M, N, K, 1.0f, 16, 0, stream, nullptr, la, lb);
+}
+
+dbs_status gemm_bf16_decoupled(const void *A, const void *B, void *D, int64_t M, int64_t N, int64_t K,
+                               int early_release_a, hipStream_t stream)
+{
+    dbs_status st = check_common(A, B, D, M, N, K, DBS_K_MAJOR, DBS_K_MAJOR, int64_t(1) << 21);
+    if (st != DBS_OK) return st;
+    if (K % 8) return fail(DBS_EINVAL, "bf16: K must be a multiple of 8");
+    if (early_release_a != 0 && early_release_a != 1) return fail(DBS_EINVAL, "early_release_a must be 0 or 1");
+    if (K <= 64) return fail(DBS_EUNSUPPORTED, "bf16 decoupled rings: K must exceed 64 (two stages)");
+    return run(early_release_a ? dbs::kBF16EA : dbs::kBF16EL, A, nullptr, B, nullptr, D, M, N, K, 1.0f, 16, 0,
+               stream);
 }
 
 dbs_status gemm_mx_mixed(dbs_mx_elem elem_a, dbs_mx_elem elem_b, const void *A, const uint8_t *sA, const void *B,

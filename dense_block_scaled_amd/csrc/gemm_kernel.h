@@ -84,6 +84,9 @@ hipError_t launch_gemm_nvfp4_raw(int shape, const Params &p, int grid, hipStream
 hipError_t launch_nvfp4_ring(const Params &p, int grid, hipStream_t stream);
 // FP6 x FP6 at the FP6 rate on 256 x 256 tiles (gemm_mxfp6.hip).
 hipError_t launch_gemm_mxfp6(const Params &p, int grid, hipStream_t stream);
+// BF16 with decoupled A / B rings, A's slot released early or at the
+// stage's end (gemm_bf16_ea.hip).
+hipError_t launch_gemm_bf16_ea(const Params &p, bool early, int grid, hipStream_t stream);
 
 namespace {
 

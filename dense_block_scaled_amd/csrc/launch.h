@@ -12,7 +12,7 @@ namespace dbs {
 // NVFP4 operands; internal, chosen by the launcher.  kMXFP6: FP6 elements on
 // both sides at the MFMA's FP6 rate (gemm_mxfp6.hip; ec holds the two FP6
 // codes).
-enum Format : int { kBF16 = 0, kMXFP8 = 1, kMXFP4 = 2, kNVFP4 = 3, kNVFP4R = 4, kMXFP6 = 5 };
+enum Format : int { kBF16 = 0, kMXFP8 = 1, kMXFP4 = 2, kNVFP4 = 3, kNVFP4R = 4, kMXFP6 = 5, kBF16EA = 6, kBF16EL = 7 };
 
 constexpr int kMaxGroups = 64;
 

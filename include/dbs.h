@@ -105,10 +105,29 @@ dbs_status gemm_bf16(const void *A, const void *B, void *D,
                      dbs_layout la, dbs_layout lb, hipStream_t stream);
 
 /*
+ * The BF16 GEMM of gemm_bf16 (K-major A and B) on a kernel with decoupled A
+ * and B rings, each of two slots: 256 x 256 tiles on one wave per SIMD
+ * (128 x 128 each, accumulators in AGPRs).  early_release_a = 1 runs the
+ * schedule that the "ThunderKittens Now on NVIDIA Vera Rubin NVL72" post
+ * lists among its new features (item 5), where the loader refills A's slot
+ * as soon as every consumer has read it: every wave first copies a stage's A
+ * fragments into registers, the waves meet, and the next-but-one A stage is
+ * loaded into the slot while the stage's MFMAs run.  early_release_a = 0
+ * hands A's slot back at the stage's end, as B's (the comparison).  Same
+ * inputs, outputs, limits and errors as gemm_bf16, plus: K must exceed 64
+ * (DBS_EUNSUPPORTED otherwise); early_release_a other than 0 or 1 is
+ * DBS_EINVAL.  The result is bit for bit that of gemm_bf16 (the same fp32
+ * accumulation order).  Opt-in: gemm_bf16's own kernel (two waves per SIMD)
+ * is the faster one on the shapes measured.
+ */
+dbs_status gemm_bf16_decoupled(const void *A, const void *B, void *D,
+                               int64_t M, int64_t N, int64_t K, int early_release_a, hipStream_t stream);
+
+/*
  * MX GEMM (MXFP8 for elem = DBS_E4M3 or DBS_E5M2, MXFP6 for DBS_E2M3 or
  * DBS_E3M2, MXFP4 for elem = DBS_E2M1): elements of A and B in `elem`, E8M0
  * scales sA (M x K/32), sB (N x K/32).  K must be a multiple of 32, at most
- * 2^22.  MXFP6 runs on the widening path of gemm_mx_mixed (K-major only).
+ * 2^22.  MXFP6 is K-major only and runs as gemm_mx_mixed runs it.
  */
 dbs_status gemm_mx(dbs_mx_elem elem,
                    const void *A, const uint8_t *sA,

@@ -60,6 +60,19 @@ def test_bf16_validation(args, want):
     assert L.dbs_last_error().decode() != ""
 
 
+@pytest.mark.parametrize("args,want", [
+    ((NUL, FAKE, FAKE, 16, 16, 128, 1), 1),            # null A
+    ((FAKE, FAKE, FAKE, 16, 16, 132, 1), 1),           # K % 8
+    ((FAKE, FAKE, FAKE, 16, 16, 64, 0), 2),            # one stage: not this kernel
+    ((FAKE, FAKE, FAKE, 16, 16, 128, 2), 1),           # release flag not 0 or 1
+    ((ctypes.c_void_p((1 << 20) + 4), FAKE, FAKE, 16, 16, 128, 1), 1),  # misaligned A
+])
+def test_bf16_decoupled_validation(args, want):
+    L = dbs.lib()
+    assert L.gemm_bf16_decoupled(*args, NUL) == want
+    assert L.dbs_last_error().decode() != ""
+
+
 @pytest.mark.parametrize("elem,K,want", [(0, 48, 1), (4, 16, 1), (9, 64, 1), (0, 64, 2)])
 def test_mx_validation(elem, K, want):
     L = dbs.lib()

@@ -27,7 +27,7 @@ import pytest
 ROOT = Path(__file__).resolve().parent.parent
 CSRC = ROOT / "dense_block_scaled_amd" / "csrc"
 UNITS = ["gemm_bf16.hip", "gemm_mxfp8.hip", "gemm_mx8_e5m2.hip", "gemm_mx8_fp4.hip", "gemm_mxfp4.hip",
-         "gemm_nvfp4.hip", "gemm_mxfp6.hip"]
+         "gemm_nvfp4.hip", "gemm_mxfp6.hip", "gemm_bf16_ea.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
