@@ -24,9 +24,10 @@
 //   and meet again (B's slot is free).  A's loads get about a stage and a
 //   half to land instead of one.
 // * EARLY = false is the same kernel with A's slot handed back at the
-//   stage's end, as B's is: A(g+1) loads during stage g into the slot stage
-//   g-1 read, no barrier between the A reads and the MFMAs, and every load
-//   of the stage lands before its closing barrier.
+//   stage's end, as B's is: A(g+1) loads at the start of stage g, beside
+//   B(g+1), into the slot stage g-1 read (as early as that slot allows), no
+//   barrier between the A reads and the MFMAs, and every load of the stage
+//   lands before its closing barrier.
 //
 // Problems this kernel takes (the host checks): K-major BF16, K % 8 == 0,
 // at least two stages (K > 64).
@@ -167,6 +168,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_ea_kernel(Params p)
             DBS_FENCE();
 #pragma unroll
             for (int q = 0; q < kLoads; ++q) load<false>(lds, (g + 1) & 1, tb.rb, kb, q, c, p.lda);
+            if constexpr (!EARLY) {
+                // A(s+1) into the slot stage s-1 read, as early as that allows
+#pragma unroll
+                for (int q = 0; q < kLoads; ++q) load<true>(lds, (g + 1) & 1, ta.ra, ka, q, c, p.lda);
+            }
             mfmas(acc, F.a[KK - 1], F.b[1]);
             DBS_FENCE();
 #pragma unroll
@@ -177,9 +183,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_ea_kernel(Params p)
             DBS_FENCE();
             if constexpr (EARLY) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             DBS_FENCE();
-            // A's loads: A(s+2) into the slot just released (EARLY), else
-            // A(s+1) into the one stage s-1 read
-            const int la = EARLY ? g & 1 : (g + 1) & 1;
+            // (EARLY) A(s+2)'s loads go into the slot just released
             // k-steps 0 .. KK-2, each reading B's next k-step; A(s+2)'s
             // loads go out two per k-step
 #pragma unroll
@@ -191,17 +195,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_ea_kernel(Params p)
 #pragma unroll
                     for (int j = 0; j < S::NB; ++j) {
                         mma(acc[i][j], F.a[kk][i], F.b[kk & 1][j]);
-                        if (j == S::NB - 1 && (i & 1)) {
+                        if (EARLY && j == S::NB - 1 && (i & 1)) {
                             // wave-loads 0 .. 5 over k-steps 0 .. 2
                             DBS_FENCE();
-                            load<true>(lds, la, ta.ra, ka, 2 * kk + (i >> 1), c, p.lda);
+                            load<true>(lds, g & 1, ta.ra, ka, 2 * kk + (i >> 1), c, p.lda);
                             DBS_FENCE();
                         }
                     }
                 }
             }
+            if constexpr (EARLY) {
 #pragma unroll
-            for (int q = 2 * (KK - 1); q < kLoads; ++q) load<true>(lds, la, ta.ra, ka, q, c, p.lda);
+                for (int q = 2 * (KK - 1); q < kLoads; ++q) load<true>(lds, g & 1, ta.ra, ka, q, c, p.lda);
+            }
             // the A stream moves on, to the following tile past the last stage
             if (++ka == p.nk) {
                 ka = 0;
@@ -211,7 +217,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_ea_kernel(Params p)
             // A(s+1) and B(s+1) have landed for this wave (memory operations
             // complete in order; with EARLY A(s+2)'s kLoads stay in flight)
             // and its reads of B(s) are done; after the barrier, for every
-            // wave
+            // wave.  At a tile's last stage the compiler may read the
+            // accumulators right after the barrier (moving them between
+            // registers), and it counts the barrier's inline assembly as wait
+            // states it does not emit: five explicit ones keep every such read
+            // at least 11 (an 8-pass MFMA's) after the last MFMA.
+            DBS_FENCE();
+            asm volatile("s_nop 4");
             DBS_FENCE();
             asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(EARLY ? kLoads : 0) : "memory");
             DBS_FENCE();
