@@ -96,6 +96,9 @@ W.update({
     "bf16_rings_late_a": dict(c=1, shape=(8192, 8192, 8192), enc="bf16", kernel="bf16_el", mfma="bf16"),
     "bf16_rings_early_a_4096": dict(c=1, shape=(4096, 4096, 4096), enc="bf16", kernel="bf16_ea", mfma="bf16"),
     "bf16_rings_late_a_4096": dict(c=1, shape=(4096, 4096, 4096), enc="bf16", kernel="bf16_el", mfma="bf16"),
+    "bf16_16384": dict(c=1, shape=(16384, 16384, 16384), enc="bf16", kernel="bf16", mfma="bf16"),
+    "bf16_rings_early_a_16384": dict(c=1, shape=(16384, 16384, 16384), enc="bf16", kernel="bf16_ea", mfma="bf16"),
+    "bf16_rings_late_a_16384": dict(c=1, shape=(16384, 16384, 16384), enc="bf16", kernel="bf16_el", mfma="bf16"),
 })
 ORDER = ["bf16", "bf16_4096", "mxfp8", "mxfp4", "mxfp4_16384", "nvfp4", "nvfp4_skinny", "nvfp4_fp8",
          "nvfp4_fp8_skinny", "nvfp4_fp6", "nvfp4_fp6_skinny", "mx_e4m3_e2m1", "mx_e2m3_e2m3"]
