@@ -115,12 +115,32 @@ def test_fp6_native_unit_scale_identity(K):
     _gpu.check_exact_sampled("mxfp8", w, D, em, en)
 
 
-def test_fp6_native_layouts_of_d():
+@pytest.mark.parametrize("K", [256, 512], ids=["per-stage-scales", "chunked-scales"])
+def test_fp6_native_layouts_of_d(K):
     """Output rows whose length is not a multiple of 8 take the direct
     stores instead of the staged epilogue."""
-    M, N, K = 2304, 2300, 256
+    M, N = 2304, 2300
     _gpu.say(f"[fp6] direct-store epilogue {M}x{N}x{K}")
     w = synth.workload("mxfp8", M, N, K, 711, 811, "e3m2", "e2m3")
     D = run(w)
     torch.cuda.synchronize()
     check(w, D, 84)
+
+
+def test_fp6_native_chunks_across_rounds_exact():
+    """Chunked scales over 324 tiles (a second persistent round) with nine
+    chunks a tile (an odd count: the chunk buffers alternate across tiles): a
+    permutation product with non-unit scales, bit for bit."""
+    M, K = 4608, 4608
+    N = K
+    _gpu.say(f"[fp6] chunked exact permutation {M}x{N}x{K}")
+    rng = np.random.default_rng(63)
+    w = _pins.make_w_mx8("e2m3", "e3m2", M, N, K, rng, scale_lo=112, scale_hi=142)
+    codes = np.zeros((N, K), np.uint8)
+    codes[np.arange(N), rng.permutation(K)] = ONE["e3m2"]
+    w["B"] = synth.pack_fp6_rows(codes)
+    w["sB"] = rng.integers(118, 137, (N, K // 32)).astype(np.uint8)
+    D = run(w)
+    torch.cuda.synchronize()
+    em, en = synth.sample_entries(88, M, N, 4096)
+    _gpu.check_exact_sampled("mxfp8", w, D, em, en)
