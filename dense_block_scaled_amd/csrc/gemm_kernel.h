@@ -246,6 +246,10 @@ using SquareW4 = Shape<kSquareTM, kSquareTN, 2, 2>;
 // 256 x 64 tiles with 8 waves of 32 x 64 on a two-slot ring: FP6 operands,
 // widened through registers, with two waves per SIMD to hide their loads.
 using SkinnyW8 = Shape<kSkinnyTM, kSkinnyTN, 8, 1>;
+// 256 x 64 tiles for raw NVFP4 with K-major operands: 4 waves of 64 x 64 (one
+// per SIMD, accumulators in AGPRs) decode 4 fragments per 4 MFMAs, a third
+// less VALU work per MFMA than 8 waves of 32 x 64; a three-slot ring.
+using SkinnyW4Deep = Shape<kSkinnyTM, kSkinnyTN, 4, 1, 3>;
 
 // Shape S with operand layouts LAY, 8-bit MX element codes EC and widened
 // E2M1 operands CV.
@@ -1358,10 +1362,18 @@ constexpr int stage_loads_min()
     return S::QA + S::QB + (NSC + S::NW - 1) / S::NW;
 }
 
+// Raw NVFP4: the fp16 fragments of one element group (one MFMA k-step) of
+// the k-step whose MFMAs come next, decoded while the current ones issue.
+template <class S>
+struct NvDec {
+    f16x8 a[S::MB], b[S::NB];
+};
+
 // State threaded through the stage function.
 template <int FMT, class S>
 struct Pipe {
     Frags<FMT, S> F0, F1;                    // k-step fragments, double-buffered
+    NvDec<S> dec;                            // raw NVFP4: the next element group, decoded
     Scales<S> sprev, scur;                   // MX scales of the previous and of this stage
     Fp4Regs<S, adirect<FMT, S>()> fp4;
     Fp4A<S> fp4a;                            // adirect: the wave's packed A rows of the next stage
@@ -1456,28 +1468,52 @@ __device__ __forceinline__ void commit_stage(Pipe<FMT, S> &P, uint8_t *lds, int 
 // feeds one v_mfma_f32_32x32x16_f16.  A and B fragments are decoded alike, so
 // the MFMAs see the same permutation of K on both sides.
 template <class S>
-__device__ __forceinline__ void nv_raw_mma(f32x16 (&acc)[S::MB][S::NB], const Frags<kNVFP4R, S> &fa,
-                                           const Frags<kNVFP4R, S> &fb)
+__device__ __forceinline__ void nv_decode(NvDec<S> &o, const Frags<kNVFP4R, S> &f, int d)
+{
+#pragma unroll
+    for (int i = 0; i < S::MB; ++i) {
+        const f16x2 s2 = e4m3_two(f.sa[i]);
+        o.a[i] = __builtin_bit_cast(f16x8, expand8((uint32_t)f.a[i][d], d < 2 ? f16x2{s2[0], s2[0]}
+                                                                              : f16x2{s2[1], s2[1]}));
+    }
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j) {
+        const f16x2 s2 = e4m3_two(f.sb[j]);
+        o.b[j] = __builtin_bit_cast(f16x8, expand8((uint32_t)f.b[j][d], d < 2 ? f16x2{s2[0], s2[0]}
+                                                                              : f16x2{s2[1], s2[1]}));
+    }
+}
+
+// The MFMAs of k-step `cur`, software-pipelined over its element groups: dec
+// holds group 0, already decoded; the MFMAs of group d issue while group d + 1
+// is decoded (the VALU work then runs beside the matrix core instead of ahead
+// of it), and during the last group's MFMAs group 0 of the next k-step (`nxt`,
+// read from LDS in this phase) is decoded into dec (NEXT; the tile's last
+// phase has no next k-step).  The 8-wave square tiles (8 MFMAs a group)
+// alternate one MFMA with six VALU instructions; the other shapes keep the
+// compiler's order (measured better on the skinny tiles).
+template <class S, bool NEXT>
+__device__ __forceinline__ void nv_raw_mma(f32x16 (&acc)[S::MB][S::NB], NvDec<S> &dec,
+                                           const Frags<kNVFP4R, S> &cur, const Frags<kNVFP4R, S> &nxt)
 {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        f16x8 a[S::MB], b[S::NB];
-#pragma unroll
-        for (int i = 0; i < S::MB; ++i) {
-            const f16x2 s2 = e4m3_two(fa.sa[i]);
-            const f16x2 s = d < 2 ? f16x2{s2[0], s2[0]} : f16x2{s2[1], s2[1]};
-            a[i] = __builtin_bit_cast(f16x8, expand8((uint32_t)fa.a[i][d], s));
-        }
-#pragma unroll
-        for (int j = 0; j < S::NB; ++j) {
-            const f16x2 s2 = e4m3_two(fb.sb[j]);
-            const f16x2 s = d < 2 ? f16x2{s2[0], s2[0]} : f16x2{s2[1], s2[1]};
-            b[j] = __builtin_bit_cast(f16x8, expand8((uint32_t)fb.b[j][d], s));
-        }
+        NvDec<S> nd;
+        if (d < 3) nv_decode<S>(nd, cur, d + 1);
+        else if constexpr (NEXT) nv_decode<S>(nd, nxt, 0);
 #pragma unroll
         for (int i = 0; i < S::MB; ++i)
 #pragma unroll
-            for (int j = 0; j < S::NB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j], a[i], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < S::NB; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(dec.b[j], dec.a[i], acc[i][j], 0, 0, 0);
+        if (d < 3 || NEXT) dec = nd;
+    }
+    if constexpr (S::NW == 8 && S::MB * S::NB >= 8) {
+#pragma unroll
+        for (int q = 0; q < 4 * S::MB * S::NB; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
+        }
     }
 }
 
@@ -1553,7 +1589,7 @@ __device__ __forceinline__ void phase(f32x16 (&acc)[S::MB][S::NB], Pipe<FMT, S> 
     }
     DBS_FENCE();
     if constexpr (FMT == kNVFP4R) {
-        nv_raw_mma<S>(acc, fa, cur);
+        nv_raw_mma<S, RD>(acc, P.dec, cur, nxt);
         if constexpr (LOADS) {
 #pragma unroll
             for (int q = 0; q < NP; ++q) {
@@ -1791,6 +1827,7 @@ __global__ __launch_bounds__(S::kThreads, 1) void gemm_kernel(Params p)
             for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
         // the "previous stage" of a tile's first stage contributes nothing
         P.F1 = Frags<FMT, S>{};
+        if constexpr (FMT == kNVFP4R) P.dec = NvDec<S>{};   // its group 0, decoded
         if constexpr (adirect<FMT, S>()) {
 #pragma unroll
             for (int i = 0; i < MB; ++i) P.aprev[i] = f16x8{};
@@ -1939,8 +1976,10 @@ hipError_t launch_one(const Params &p0, int grid, hipStream_t stream)
                 if (p.ec != 0) return hipErrorInvalidValue;
             }
         }
-        // raw NVFP4 with K-major operands: the 8-wave square tiles only
-        constexpr bool K0 = FMT != kNVFP4R || (std::is_same<S0, Square>::value && SM != kScalesRegs);
+        // raw NVFP4 with K-major operands: the 8-wave square tiles and the
+        // 4-wave skinny ones with 16-byte scale pieces only
+        constexpr bool K0 = FMT != kNVFP4R || (std::is_same<S0, Square>::value && SM != kScalesRegs) ||
+                            (std::is_same<S0, SkinnyW4Deep>::value && SM == kScalesRows16);
         if (!K0 && p.lay == 0) return hipErrorInvalidValue;
         switch (p.lay) {
         case 0:
@@ -2075,9 +2114,10 @@ hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
             return launch_one<FMT, kScalesRegs, U, E5>(p, grid, stream);
         }
     }
-    // NVFP4 on skinny tiles: the raw-ring kernel when raw stages of 256 K
-    // elements tile K (at least two of them) and the scale rows start on
-    // 16-byte boundaries
+    // NVFP4 (the grouped GEMM; a single GEMM takes launch_nvfp4_raw's 4-wave
+    // kernel under the same conditions) on skinny tiles: the raw-ring kernel
+    // when raw stages of 256 K elements tile K (at least two of them) and the
+    // scale rows start on 16-byte boundaries
     if constexpr (std::is_same<S, Skinny>::value && FMT == kNVFP4) {
         const bool s16 = ((reinterpret_cast<uintptr_t>(p.sA) | reinterpret_cast<uintptr_t>(p.sB)) & 15) == 0;
         if (p.K % 256 == 0 && p.K >= 512 && s16) return launch_nvfp4_ring(p, grid, stream);
@@ -2121,6 +2161,8 @@ hipError_t launch_nvfp4_raw(const Params &p, int grid, hipStream_t stream)
         if (p.lay == 0) return launch_fmt<kNVFP4, S>(p, grid, stream);
         return launch_one<kNVFP4R, kScalesRegs, SquareW4>(p, grid, stream);
     } else {
+        if (p.lay == 0 && r16 && stages_of<kNVFP4R, SkinnyW4Deep>(p.K) >= SkinnyW4Deep::NS - 1)
+            return launch_one<kNVFP4R, kScalesRows16, SkinnyW4Deep>(p, grid, stream);
         if (p.lay == 0) return launch_fmt<kNVFP4, S>(p, grid, stream);
         if (p.scales_aligned && stages_of<kNVFP4R, SkinnyDeep>(p.K) >= SkinnyDeep::NS - 1) {
             if (r16) return launch_one<kNVFP4R, kScalesRows16, SkinnyDeep>(p, grid, stream);

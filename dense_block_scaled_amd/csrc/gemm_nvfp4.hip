@@ -9,8 +9,9 @@ namespace {
 
 // --------------------------------------------- NVFP4, skinny tiles, raw ring
 
-// NVFP4 on 256 x 64 tiles when K % 256 == 0 and the scale rows start on
-// 16-byte boundaries.  The packed E2M1 rows and their E4M3 scales arrive by
+// Grouped NVFP4 on 256 x 64 tiles when K % 256 == 0 and the scale rows start
+// on 16-byte boundaries (a single GEMM under these conditions runs on the
+// 4-wave raw kernel of gemm_kernel.h, which measured faster).  The packed E2M1 rows and their E4M3 scales arrive by
 // direct-to-LDS loads, unchanged, into a ring of kRawSlots raw slots; a raw
 // stage covers 256 K elements, i.e. one 128-byte line of every packed row and
 // 16 bytes of every scale row, so each row costs one memory request per
