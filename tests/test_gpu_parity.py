@@ -52,8 +52,8 @@ RAGGED = [
     (512, 260, 4096),     # long K: many ring rotations
     (256, 20000, 512),    # 313 tiles: several per workgroup through the stage stream; MXFP4 has
                           # 2 stages per tile (the 3-slot ring's loads run a whole tile ahead)
-    (300, 9000, 768),     # 282 tiles, ragged M and N; NVFP4 takes the raw-ring kernel (K % 256 == 0)
-                          # with three raw stages per tile, streamed across a workgroup's tiles
+    (300, 9000, 768),     # 282 tiles, ragged M and N; NVFP4 takes the 4-wave raw kernel (K % 256 == 0)
+                          # with three stages per tile, streamed across a workgroup's tiles
 ]
 SQUARE_RAGGED = [
     (3000, 2900, 352),    # partial tiles, partial last stage; MX scale rows of 11 bytes
