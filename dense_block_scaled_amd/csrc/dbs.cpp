@@ -536,7 +536,9 @@ dbs_status gemm_grouped_nvfp4(const void *A, const uint8_t *sA, float tA, const 
     float alpha[dbs::kMaxGroups];
     for (int64_t g = 0; g < G; ++g) alpha[g] = tA * tB[g];
     const Groups gr{offsets, G, alpha};
-    return run(dbs::kNVFP4, A, sA, B, sB, D, M, N, K, 1.0f, 4, 16, stream, &gr);
+    // K % 32 == 0: the raw kernels of gemm_nvfp4 (codes staged as they are,
+    // decoded in registers); else the kernels that decode into LDS
+    return run(K % 32 ? dbs::kNVFP4 : dbs::kNVFP4R, A, sA, B, sB, D, M, N, K, 1.0f, 4, 16, stream, &gr);
 }
 
 const char *dbs_status_str(dbs_status st)

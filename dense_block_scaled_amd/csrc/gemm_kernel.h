@@ -20,7 +20,7 @@
 //   waves (two per SIMD), each owning 128 x 64 as 4 x 2 MFMA blocks of 32 x
 //   32.  Skinny (when 256 x 256 tiles cannot fill the CUs, e.g. M = 256):
 //   256 x 64 tiles, 8 waves of 32 x 64 on a three-slot ring, or 4 waves of
-//   64 x 64 where stages pass through registers.  Two waves per SIMD matter on
+//   64 x 64 (raw NVFP4, and where stages pass through registers).  Two waves per SIMD matter on
 //   gfx950: a wave that issues a global or LDS load stalls its own MFMA
 //   stream for tens of cycles, and the second wave's MFMAs fill that gap
 //   (the role split the pages obtain from dedicated producer warps).
@@ -80,8 +80,6 @@ hipError_t launch_gemm_mx8_fp4(int shape, const Params &p, int grid, hipStream_t
 hipError_t launch_gemm_mxfp4(int shape, const Params &p, int grid, hipStream_t stream);
 hipError_t launch_gemm_nvfp4(int shape, const Params &p, int grid, hipStream_t stream);
 hipError_t launch_gemm_nvfp4_raw(int shape, const Params &p, int grid, hipStream_t stream);
-// NVFP4 on 256 x 64 tiles through the raw-ring kernel (gemm_nvfp4.hip).
-hipError_t launch_nvfp4_ring(const Params &p, int grid, hipStream_t stream);
 // FP6 x FP6 at the FP6 rate on 256 x 256 tiles (gemm_mxfp6.hip).
 hipError_t launch_gemm_mxfp6(const Params &p, int grid, hipStream_t stream);
 // BF16 with decoupled A / B rings, A's slot released early or at the
@@ -2113,14 +2111,6 @@ hipError_t launch_fmt(const Params &p, int grid, hipStream_t stream)
             using U = typename std::conditional<std::is_same<S, Square>::value, SquareW4, S>::type;
             return launch_one<FMT, kScalesRegs, U, E5>(p, grid, stream);
         }
-    }
-    // NVFP4 (the grouped GEMM; a single GEMM takes launch_nvfp4_raw's 4-wave
-    // kernel under the same conditions) on skinny tiles: the raw-ring kernel
-    // when raw stages of 256 K elements tile K (at least two of them) and the
-    // scale rows start on 16-byte boundaries
-    if constexpr (std::is_same<S, Skinny>::value && FMT == kNVFP4) {
-        const bool s16 = ((reinterpret_cast<uintptr_t>(p.sA) | reinterpret_cast<uintptr_t>(p.sB)) & 15) == 0;
-        if (p.K % 256 == 0 && p.K >= 512 && s16) return launch_nvfp4_ring(p, grid, stream);
     }
     if constexpr (FMT == kNVFP4) {
         if (p.K % 32) return launch_one<FMT, kNvHalf, S>(p, grid, stream);

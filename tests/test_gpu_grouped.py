@@ -60,8 +60,9 @@ FMTS = ["bf16", "mxfp8", "mxfp4", "nvfp4"]
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("sizes,N,K", [
     ([0, 1, 300, 77, 520], 260, 352),      # empty and one-row groups, ragged edges, 256 x 64 tiles
-    ([130, 0, 257], 200, 512),             # MX scale rows of whole 16-byte chunks; raw-ring NVFP4
-], ids=["mixed", "aligned"])
+    ([130, 0, 257], 200, 512),             # MX scale rows of whole 16-byte chunks; 4-wave raw NVFP4
+    ([200, 0, 700, 64], 5000, 768),        # 395 tiles of 256 x 64: a second persistent round, 3 stages a tile
+], ids=["mixed", "aligned", "rounds"])
 def test_grouped_matches_oracle(fmt, sizes, N, K):
     _gpu.say(f"[grouped] {fmt} sizes={sizes} N={N} K={K}")
     w = _grouped_w(fmt, sizes, N, K, seed=7)
