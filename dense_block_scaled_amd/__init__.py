@@ -23,12 +23,13 @@ Each returns D: (M, N) torch.bfloat16 (or writes into ``out``).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 from pathlib import Path
 
 import torch
 
-__all__ = ["gemm_bf16", "gemm_bf16_decoupled", "gemm_mx", "gemm_mx_mixed", "gemm_nvfp4", "gemm_nvfp4_fp8", "gemm_nvfp4_fp8_noalloc", "nvfp4_fp8_workspace_bytes", "gemm_nvfp4_fp6", "nvfp4_fp6_workspace_bytes", "gemm_grouped_bf16", "gemm_grouped_mx", "gemm_grouped_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError",
+__all__ = ["gemm_bf16", "gemm_bf16_decoupled", "gemm_mx", "gemm_mx_mixed", "gemm_nvfp4", "gemm_nvfp4_fp8", "gemm_nvfp4_fp8_noalloc", "nvfp4_fp8_workspace_bytes", "gemm_nvfp4_fp6", "nvfp4_fp6_workspace_bytes", "gemm_grouped_bf16", "gemm_grouped_mx", "gemm_grouped_nvfp4", "quant_mx", "quant_nvfp4", "quant_bf16", "lib", "LIB_PATH", "DbsError", "load_poison_library", "using_library",
            "DBS_OK", "DBS_EINVAL", "DBS_EUNSUPPORTED", "DBS_EHIP", "K_MAJOR", "MN_MAJOR",
            "E4M3", "E5M2", "E2M3", "E3M2", "E2M1", "status_str"]
 
@@ -49,56 +50,85 @@ class DbsError(RuntimeError):
 _lib = None
 
 
+def _load(path: Path) -> ctypes.CDLL:
+    if not path.exists():
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m dense_block_scaled_amd.build` (or __graft_entry__.build())")
+    L = ctypes.CDLL(str(path))
+    _declare(L)
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """The loaded C-ABI library; raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not LIB_PATH.exists():
-            raise ImportError(f"{LIB_PATH} is missing: build it with "
-                              "`python -m dense_block_scaled_amd.build` (or __graft_entry__.build())")
-        L = ctypes.CDLL(str(LIB_PATH))
-        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        L.gemm_bf16.argtypes = [P, P, P, I64, I64, I64, I, I, P]
-        L.gemm_bf16.restype = I
-        L.gemm_bf16_decoupled.argtypes = [P, P, P, I64, I64, I64, I, P]
-        L.gemm_bf16_decoupled.restype = I
-        L.gemm_mx.argtypes = [I, P, P, P, P, P, I64, I64, I64, I, I, P]
-        L.gemm_mx.restype = I
-        L.gemm_mx_mixed.argtypes = [I, I, P, P, P, P, P, I64, I64, I64, I, I, P]
-        L.gemm_mx_mixed.restype = I
-        L.gemm_nvfp4.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P]
-        L.gemm_nvfp4.restype = I
-        L.gemm_nvfp4_fp8_workspace.argtypes = [I64, I64, I64]
-        L.gemm_nvfp4_fp8_workspace.restype = ctypes.c_size_t
-        L.gemm_nvfp4_fp8.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P,
-                                     ctypes.c_size_t, P]
-        L.gemm_nvfp4_fp8.restype = I
-        L.gemm_nvfp4_fp6_workspace.argtypes = [I64, I64, I64]
-        L.gemm_nvfp4_fp6_workspace.restype = ctypes.c_size_t
-        L.gemm_nvfp4_fp6.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P,
-                                     ctypes.c_size_t, P]
-        L.gemm_nvfp4_fp6.restype = I
-        L.gemm_nvfp4_fp8_noalloc.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P]
-        L.gemm_nvfp4_fp8_noalloc.restype = I
-        L.gemm_grouped_bf16.argtypes = [P, P, P, P, I64, I64, I64, P]
-        L.gemm_grouped_bf16.restype = I
-        L.gemm_grouped_mx.argtypes = [I, P, P, P, P, P, P, I64, I64, I64, P]
-        L.gemm_grouped_mx.restype = I
-        L.gemm_grouped_nvfp4.argtypes = [P, P, ctypes.c_float, P, P, P, P, P, I64, I64, I64, P]
-        L.gemm_grouped_nvfp4.restype = I
-        L.quant_mx.argtypes = [I, P, I64, I64, P, P, P]
-        L.quant_mx.restype = I
-        L.quant_nvfp4.argtypes = [P, I64, I64, P, P, P, P]
-        L.quant_nvfp4.restype = I
-        L.quant_bf16.argtypes = [P, I64, P, P]
-        L.quant_bf16.restype = I
-        L.dbs_status_str.argtypes = [I]
-        L.dbs_status_str.restype = ctypes.c_char_p
-        L.dbs_last_error.argtypes = []
-        L.dbs_last_error.restype = ctypes.c_char_p
-        L.dbs_version.restype = I
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+def load_poison_library() -> ctypes.CDLL:
+    """The LDS-poison debug build of the library (libdbs_poison.so: every
+    direct-to-LDS load first fills its destination with 0xFF), for the
+    race-detection tests; raises if it has not been built."""
+    return _load(LIB_PATH.with_name("libdbs_poison.so"))
+
+
+@contextlib.contextmanager
+def using_library(L: ctypes.CDLL):
+    """Route this module's calls through library L (e.g. the poison build)
+    inside the block."""
+    global _lib
+    prev = lib()
+    _lib = L
+    try:
+        yield L
+    finally:
+        _lib = prev
+
+
+def _declare(L: ctypes.CDLL) -> None:
+    """Argument and result types of the C ABI's entry points."""
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.gemm_bf16.argtypes = [P, P, P, I64, I64, I64, I, I, P]
+    L.gemm_bf16.restype = I
+    L.gemm_bf16_decoupled.argtypes = [P, P, P, I64, I64, I64, I, P]
+    L.gemm_bf16_decoupled.restype = I
+    L.gemm_mx.argtypes = [I, P, P, P, P, P, I64, I64, I64, I, I, P]
+    L.gemm_mx.restype = I
+    L.gemm_mx_mixed.argtypes = [I, I, P, P, P, P, P, I64, I64, I64, I, I, P]
+    L.gemm_mx_mixed.restype = I
+    L.gemm_nvfp4.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P]
+    L.gemm_nvfp4.restype = I
+    L.gemm_nvfp4_fp8_workspace.argtypes = [I64, I64, I64]
+    L.gemm_nvfp4_fp8_workspace.restype = ctypes.c_size_t
+    L.gemm_nvfp4_fp8.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P,
+                                 ctypes.c_size_t, P]
+    L.gemm_nvfp4_fp8.restype = I
+    L.gemm_nvfp4_fp6_workspace.argtypes = [I64, I64, I64]
+    L.gemm_nvfp4_fp6_workspace.restype = ctypes.c_size_t
+    L.gemm_nvfp4_fp6.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P,
+                                 ctypes.c_size_t, P]
+    L.gemm_nvfp4_fp6.restype = I
+    L.gemm_nvfp4_fp8_noalloc.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, P, I64, I64, I64, I, I, P]
+    L.gemm_nvfp4_fp8_noalloc.restype = I
+    L.gemm_grouped_bf16.argtypes = [P, P, P, P, I64, I64, I64, P]
+    L.gemm_grouped_bf16.restype = I
+    L.gemm_grouped_mx.argtypes = [I, P, P, P, P, P, P, I64, I64, I64, P]
+    L.gemm_grouped_mx.restype = I
+    L.gemm_grouped_nvfp4.argtypes = [P, P, ctypes.c_float, P, P, P, P, P, I64, I64, I64, P]
+    L.gemm_grouped_nvfp4.restype = I
+    L.quant_mx.argtypes = [I, P, I64, I64, P, P, P]
+    L.quant_mx.restype = I
+    L.quant_nvfp4.argtypes = [P, I64, I64, P, P, P, P]
+    L.quant_nvfp4.restype = I
+    L.quant_bf16.argtypes = [P, I64, P, P]
+    L.quant_bf16.restype = I
+    L.dbs_status_str.argtypes = [I]
+    L.dbs_status_str.restype = ctypes.c_char_p
+    L.dbs_last_error.argtypes = []
+    L.dbs_last_error.restype = ctypes.c_char_p
+    L.dbs_version.restype = I
 
 
 def status_str(st: int) -> str:

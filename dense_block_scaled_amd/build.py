@@ -7,7 +7,10 @@ of formats, all instantiating the template in csrc/gemm_kernel.h), the
 launcher (csrc/gemm.hip), the quantisers (csrc/quant.hip) and the ABI layer
 (csrc/dbs.cpp) to objects in parallel, then links them, in-tree; no GPU is
 needed to build.  Packed-fp32 VALU instructions are turned off for the
-device code.
+device code.  build(poison=True) builds the same sources with
+DBS_LDS_POISON=1 into libdbs_poison.so, a debug library whose direct-to-LDS
+loads first fill their destination with 0xFF (see gemm_kernel.h); the
+race-detection tests compare its results with libdbs.so's bit for bit.
 """
 from __future__ import annotations
 
@@ -22,6 +25,7 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libdbs.so"
+POISON_LIB = PKG / "libdbs_poison.so"
 ARCH = os.environ.get("DBS_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -42,9 +46,11 @@ def _jobs() -> int:
     return max(1, min(n, len(SOURCES), int(os.environ.get("MAX_JOBS", n))))
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> Path:
+def build(verbose: bool = False, extra: list[str] | None = None, poison: bool = False) -> Path:
     flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
-             f"-I{ROOT / 'include'}", f"-I{CSRC}", *DEVICE_FLAGS, *(extra or [])]
+             f"-I{ROOT / 'include'}", f"-I{CSRC}", *DEVICE_FLAGS, *(["-DDBS_LDS_POISON=1"] if poison else []),
+             *(extra or [])]
+    out = POISON_LIB if poison else LIB
     objdir = Path(tempfile.mkdtemp(prefix="libdbs.obj.", dir=str(PKG)))
     fd, tmp = tempfile.mkstemp(prefix="libdbs.", suffix=".so.tmp", dir=str(PKG))
     os.close(fd)
@@ -64,13 +70,14 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> Path:
         if verbose:
             print(" ".join(link), flush=True)
         subprocess.run(link, check=True)
-        os.replace(tmp, LIB)
+        os.replace(tmp, out)
     finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
         shutil.rmtree(objdir, ignore_errors=True)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":
     build(verbose=True)
+    build(verbose=True, poison=True)

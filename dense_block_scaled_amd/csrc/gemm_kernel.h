@@ -107,12 +107,49 @@ constexpr int kStoreNT = 2;
 
 #define DBS_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+// Debug builds with DBS_LDS_POISON=1 (a separate library, libdbs_poison.so)
+// fill the LDS destination of every direct-to-LDS load with 0xFF bytes before
+// issuing it: NaN as bf16, E4M3, E5M2, E8M0 and as an NVFP4 scale, -6 and -7.5
+// as E2M1 and E2M3 codes.  A fragment or scale read that ran ahead of its
+// load's wait would then see poison instead of the data of an older stage,
+// and the debug build's results would differ from the product build's.
+#ifndef DBS_LDS_POISON
+#define DBS_LDS_POISON 0
+#endif
+
 // Buffer resource over [base, base + bytes): loads at offsets >= bytes return
 // zero, stores there are dropped.  Word 3 = 0x00020000 is the gfx9-family
 // raw-buffer configuration (32-bit data format, no swizzle, no stride).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Direct-to-LDS load of BYTES (4, 12 or 16) per lane into the wave's block
+// at `dst` (lane i's bytes at dst + 4 i for dword loads, in a 16-byte cell
+// dst + 16 i otherwise).  In the poison build the lane first fills that cell
+// with 0xFF and waits for the write, so the load's data lands after it; every
+// poisoned cell is rewritten by the same lane's load, which the stage's
+// barrier waits for.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t rsrc, uint8_t *dst, uint32_t voff)
+{
+    static_assert(BYTES == 4 || BYTES == 12 || BYTES == 16, "dword, dwordx3 or dwordx4 loads");
+#if DBS_LDS_POISON
+    const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    if constexpr (BYTES == 4)
+        *reinterpret_cast<uint32_t *>(dst + 4 * lane) = ~0u;
+    else
+        *reinterpret_cast<i32x4 *>(dst + 16 * lane) = i32x4{-1, -1, -1, -1};
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#endif
+    // (the builtin takes its size as a literal)
+    if constexpr (BYTES == 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)dst, 4, voff, 0, 0, 0);
+    else if constexpr (BYTES == 12)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)dst, 12, voff, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)dst, 16, voff, 0, 0, 0);
 }
 
 constexpr int kRowBytes = 128;                 // bytes of one tile row per stage
@@ -717,7 +754,7 @@ __device__ __forceinline__ void dma_scales(uint8_t *lds, int slot, const Target 
         const int o = ks * BPS + 4 * (BPS == 16 ? word ^ ((row >> 3) & 3) : word);
         const uint32_t off = (uint32_t)(row * sld + o) | (o < sld ? 0u : kOOB);
         const int dst = S::kLdsS + (is_a ? slot * S::TM * BPS : S::NS * S::TM * BPS + slot * S::TN * BPS) + nn * 256;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? tg.rsa : tg.rsb, (lds_void *)(lds + dst), 4, off, 0, 0, 0);
+        lds_dma<4>(is_a ? tg.rsa : tg.rsb, lds + dst, off);
     }
 }
 
@@ -738,7 +775,7 @@ __device__ __forceinline__ void dma_scale_rows16(uint8_t *lds, int slot, const T
         const int o = ks * 16;
         const uint32_t off = (uint32_t)((nn * 64 + c.lane) * sld + o) | (o < sld ? 0u : kOOB);
         const int dst = S::kLdsS + (is_a ? slot * S::TM * 16 : S::NS * S::TM * 16 + slot * S::TN * 16) + nn * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? tg.rsa : tg.rsb, (lds_void *)(lds + dst), 16, off, 0, 0, 0);
+        lds_dma<16>(is_a ? tg.rsa : tg.rsb, lds + dst, off);
     }
 }
 
@@ -763,7 +800,7 @@ __device__ __forceinline__ void dma_scale_portion(uint8_t *lds, int par, const T
         const int r = (is_a ? row0 : row0 - S::TM) + (c.lane >> 2);
         const uint32_t off = (uint32_t)(r * sld + o) | (o < sld ? 0u : kOOB);
         const int dst = S::kLdsS + par * (S::TM + S::TN) * kScaleChunk + row0 * kScaleChunk;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? stg.rsa : stg.rsb, (lds_void *)(lds + dst), 4, off, 0, 0, 0);
+        lds_dma<4>(is_a ? stg.rsa : stg.rsb, lds + dst, off);
     }
 }
 
@@ -863,7 +900,7 @@ __device__ __forceinline__ void dma_op(uint8_t *lds, int dst, __amdgpu_buffer_rs
     const int k0 = ks * kRowBytes;
     const uint32_t kc = c.x4 ^ (uint32_t)((L & 7) << 4);
     const uint32_t off = (r8 + kc + (uint32_t)(L * 8 * lda + k0)) | (kc < (uint32_t)(lda - k0) ? 0u : kOOB);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + dst + L * 1024), 16, off, 0, 0, 0);
+    lds_dma<16>(rsrc, lds + dst + L * 1024, off);
 }
 
 // Wave-load L of an MN-major operand (T columns per tile) of stage ks into
@@ -881,7 +918,7 @@ __device__ __forceinline__ void dma_mn(uint8_t *lds, int dst, __amdgpu_buffer_rs
     // with 2 RPL = PERIOD the parity of L = w Q + q is that of q (Q even)
     const int par = G::RPL % G::PERIOD == 0 ? 0 : (q & 1);
     const uint32_t row = (uint32_t)(ks * G::KS + L * G::RPL) * (uint32_t)ldx;   // wave-uniform
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(lds + dst + L * 1024), 16, lo[par] + row, 0, 0, 0);
+    lds_dma<16>(rsrc, lds + dst + L * 1024, lo[par] + row);
 }
 
 // Wave w issues wave-loads w*Q + q, q < Q, of each operand.

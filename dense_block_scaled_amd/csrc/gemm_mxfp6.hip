@@ -181,7 +181,7 @@ __device__ __forceinline__ void load_op(uint8_t *lds, int slot, __amdgpu_buffer_
     const uint32_t piece = c.x ^ (uint32_t)(L & 7);
     const uint32_t off = c.r8 + (uint32_t)(L * 8 * lda + ks * kGRow) + 12u * piece;
     const int dst = slot * kSlot + (IS_A ? 0 : kOp) + L * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(lds + dst), 12, off, 0, 0, 0);
+    lds_dma<12>(r, lds + dst, off);
 }
 
 // The stage's scales: wave w fetches the dword of rows 64 (w % 4) + lane of
@@ -191,7 +191,7 @@ __device__ __forceinline__ void load_scales(uint8_t *lds, int slot, const Target
     const bool is_a = c.w < 4;
     const uint32_t off = (uint32_t)((64 * (c.w & 3) + c.lane) * sld + 4 * ks);
     const int dst = kLdsS + slot * kScaleSlot + c.w * 256;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? tg.rsa : tg.rsb, (lds_void *)(lds + dst), 4, off, 0, 0, 0);
+    lds_dma<4>(is_a ? tg.rsa : tg.rsb, lds + dst, off);
 }
 
 // Chunked scales: portion u (0 .. 3) of chunk `chunk` (bytes 16 chunk ..
@@ -210,7 +210,7 @@ __device__ __forceinline__ void load_scale_portion(uint8_t *lds, int pc, __amdgp
     const int o = chunk * kChunk + 4 * ((c.lane & 3) ^ (((row0 + (c.lane >> 2)) >> 3) & 3));
     const uint32_t off = (uint32_t)(r * sld + o) | (o < sld ? 0u : kOOB);
     const int dst = kLdsS + pc * kChunkBuf + row0 * kChunk;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? sa : sb, (lds_void *)(lds + dst), 4, off, 0, 0, 0);
+    lds_dma<4>(is_a ? sa : sb, lds + dst, off);
 }
 
 // Load n (0 .. kLoads-1) of the wave's share of a stage: operand rows, then
