@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import dense_block_scaled_amd as dbs
 import synth
 from tests import _gpu, _pins
 
@@ -238,6 +239,27 @@ def test_exact_nvfp4_tensor_scales():
     D = _gpu.run("nvfp4", w)
     torch.cuda.synchronize()
     _gpu.check_exact("nvfp4", w, D)
+
+
+@pytest.mark.parametrize("K", [256, 512, 768])
+@pytest.mark.parametrize("shift", [0, 4, 1], ids=["scales16", "scales4", "scales1"])
+def test_nvfp4_skinny_kernel_choice(K, shift):
+    """K-major NVFP4 on 256 x 64 tiles through each kernel the launcher picks:
+    the 4-wave raw kernel (16-byte-aligned scale rows, K % 256 == 0, two or
+    more stages), and the kernels that decode into LDS (a single stage, scale
+    rows on 4-byte or 1-byte boundaries)."""
+    M, N = 300, 3000
+    _gpu.say(f"[parity] nvfp4 skinny K={K} scale offset {shift}")
+    w = _w("nvfp4", M, N, K, seed=13)
+    d = _gpu.to_dev(w)
+    sa = torch.zeros(w["sA"].size + 16, dtype=torch.uint8, device="cuda")
+    sb = torch.zeros(w["sB"].size + 16, dtype=torch.uint8, device="cuda")
+    sa[shift:shift + w["sA"].size] = torch.from_numpy(w["sA"].reshape(-1)).cuda()
+    sb[shift:shift + w["sB"].size] = torch.from_numpy(w["sB"].reshape(-1)).cuda()
+    D = dbs.gemm_nvfp4(d["A"], sa[shift:shift + w["sA"].size].view(M, K // 16), w["tA"],
+                       d["B"], sb[shift:shift + w["sB"].size].view(N, K // 16), w["tB"])
+    torch.cuda.synchronize()
+    _gpu.check_full("nvfp4", w, D)
 
 
 # ---- determinism (a race canary) ---------------------------------------------------
