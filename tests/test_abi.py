@@ -33,6 +33,20 @@ def test_library_exports_every_declared_symbol():
     assert L.dbs_version() == 102
 
 
+def test_poison_library_exports_the_same_symbols():
+    """The LDS-poison debug build (race-detection tests) is the same library,
+    and switching to it and back restores the product build."""
+    P = dbs.load_poison_library()
+    assert P._name != dbs.lib()._name
+    for name in _declared():
+        assert hasattr(P, name), name
+    assert P.dbs_version() == dbs.lib().dbs_version()
+    prod = dbs.lib()
+    with dbs.using_library(P):
+        assert dbs.lib() is P
+    assert dbs.lib() is prod
+
+
 def test_status_strings():
     for st in (0, 1, 2, 3):
         assert dbs.status_str(st).startswith("DBS_")
