@@ -103,6 +103,24 @@ def test_random_codes_and_scales(fmt):
     _gpu.check_full(fmt, w, D)
 
 
+@pytest.mark.parametrize("shape", [(300, 3000, 512), (3000, 2900, 768)], ids=lambda s: "x".join(map(str, s)))
+def test_nvfp4_random_codes_and_scales_raw(shape):
+    """NVFP4 codes over the whole E2M1 range with random E4M3 scales (most of
+    the finite range) through the raw-staged kernels' pipelined decode:
+    4-wave 256 x 64 tiles and 8-wave 256 x 256 tiles, several stages."""
+    M, N, K = shape
+    _gpu.say(f"[parity] nvfp4 random codes and scales {shape}")
+    rng = np.random.default_rng(23)
+    w = _pins.make_w("nvfp4", M, N, K, rng, scale_lo=0x08, scale_hi=0x7E)
+    D = _gpu.run("nvfp4", w)
+    torch.cuda.synchronize()
+    if M * N <= 1_000_000:
+        _gpu.check_full("nvfp4", w, D)
+    else:
+        em, en = synth.sample_entries(24, M, N, 4096)
+        _gpu.check_sampled("nvfp4", w, D, em, en)
+
+
 # ---- bit-exact cases ------------------------------------------------------------
 
 def _identity_w(fmt, M, K, rng, permute):
