@@ -94,7 +94,7 @@ struct Groups {
 dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const uint8_t *sB, void *D, int64_t M,
                int64_t N, int64_t K, float alpha, int elem_bits, int block, hipStream_t stream,
                const Groups *groups = nullptr, dbs_layout la = DBS_K_MAJOR, dbs_layout lb = DBS_K_MAJOR,
-               int ec = 0, int cv = 0)
+               int ec = 0, int cv = 0, int blk6 = 0)
 {
     int cus = 0;
     dbs_status st = device_cus(&cus);
@@ -117,6 +117,7 @@ dbs_status run(int fmt, const void *A, const uint8_t *sA, const void *B, const u
     p.ldbm = (int)((cv >> 2) == 1 ? N / 2 : N * elem_bits / 8);
     p.ec = ec;
     p.cv = cv;
+    p.blk6 = blk6;
     // rows of a widened operand: E2M1 K/2 bytes, FP6 3K/4
     p.ldc = (int)(((cv & 3) >= 2 || (cv >> 2) >= 2) ? K / 4 * 3 : K / 2);
     // square tiles unless they would fill at most half of the CUs
@@ -214,12 +215,16 @@ Fp8Ws fp8_ws(void *base, int64_t M, int64_t N, int64_t K)
     return w;
 }
 
-// Workspace layout of the FP4-rate path: A codes (M x 3K/4), B codes
-// (N x 3K/4), A scales (M x K/32), B scales (N x K/32), each on a 256-byte
-// boundary.
+int64_t round8(int64_t x) { return (x + 7) / 8 * 8; }
+
+// Workspace layout of the FP4-rate path: A codes (M x 3K/4, rows padded to a
+// multiple of 8: the FP6-rate kernel's stage-blocked layout needs whole
+// groups of 8), B codes (N x 3K/4, likewise), A scales (M x K/32), B scales
+// (N x K/32), each on a 256-byte boundary.
 Fp8Ws fp6_ws(void *base, int64_t M, int64_t N, int64_t K)
 {
-    const int64_t ob = align256(M * K / 4 * 3), osa = ob + align256(N * K / 4 * 3), osb = osa + align256(M * K / 32);
+    const int64_t ob = align256(round8(M) * K / 4 * 3), osa = ob + align256(round8(N) * K / 4 * 3),
+                  osb = osa + align256(M * K / 32);
     Fp8Ws w;
     w.bytes = osb + align256(N * K / 32);
     uint8_t *p = static_cast<uint8_t *>(base);
@@ -230,22 +235,36 @@ Fp8Ws fp6_ws(void *base, int64_t M, int64_t N, int64_t K)
     return w;
 }
 
-// FP6 on both sides, K-major (elements ea, eb: E2M3 or E3M2): at the FP6
-// rate on 256 x 256 tiles when those occupy more than a quarter of the CUs,
-// K is whole 128-K stages and the scale rows start on 4-byte boundaries;
-// otherwise widened to 8 bits on 256 x 64 tiles.
-dbs_status fp6_gemm(dbs_mx_elem ea, dbs_mx_elem eb, const void *A, const uint8_t *sA, const void *B,
-                    const uint8_t *sB, void *D, int64_t M, int64_t N, int64_t K, float alpha, hipStream_t stream)
+// Whether FP6 x FP6 (K-major) runs at the FP6 rate: on 256 x 256 tiles when
+// those occupy more than a quarter of the CUs, K is whole 128-K stages and
+// the scale rows start on 4-byte boundaries.
+dbs_status fp6_native(int64_t M, int64_t N, int64_t K, const uint8_t *sA, const uint8_t *sB, bool *native)
 {
-    if (K % dbs::kFp6StageK == 0 && aligned(sA, 4) && aligned(sB, 4)) {
-        int cus = 0;
-        dbs_status st = device_cus(&cus);
-        if (st != DBS_OK) return st;
-        const int64_t sq = ((M + dbs::kSquareTM - 1) / dbs::kSquareTM) * ((N + dbs::kSquareTN - 1) / dbs::kSquareTN);
-        if (4 * sq > cus)
-            return run(dbs::kMXFP6, A, sA, B, sB, D, M, N, K, alpha, 6, 32, stream, nullptr, DBS_K_MAJOR,
-                       DBS_K_MAJOR, (int)ea | ((int)eb << 3), 0);
-    }
+    *native = false;
+    if (K % dbs::kFp6StageK || !aligned(sA, 4) || !aligned(sB, 4)) return DBS_OK;
+    int cus = 0;
+    dbs_status st = device_cus(&cus);
+    if (st != DBS_OK) return st;
+    const int64_t sq = ((M + dbs::kSquareTM - 1) / dbs::kSquareTM) * ((N + dbs::kSquareTN - 1) / dbs::kSquareTN);
+    *native = 4 * sq > cus;
+    return DBS_OK;
+}
+
+// FP6 on both sides, K-major (elements ea, eb: E2M3 or E3M2): at the FP6
+// rate where fp6_native says so, otherwise widened to 8 bits on 256 x 64
+// tiles.  blocked: the operands are stage-blocked (only the FP6-rate kernel
+// reads that layout; the caller has checked fp6_native).
+dbs_status fp6_gemm(dbs_mx_elem ea, dbs_mx_elem eb, const void *A, const uint8_t *sA, const void *B,
+                    const uint8_t *sB, void *D, int64_t M, int64_t N, int64_t K, float alpha, hipStream_t stream,
+                    bool blocked = false)
+{
+    bool native = false;
+    dbs_status st = fp6_native(M, N, K, sA, sB, &native);
+    if (st != DBS_OK) return st;
+    if (native)
+        return run(dbs::kMXFP6, A, sA, B, sB, D, M, N, K, alpha, 6, 32, stream, nullptr, DBS_K_MAJOR, DBS_K_MAJOR,
+                   (int)ea | ((int)eb << 3), 0, blocked ? 1 : 0);
+    if (blocked) return fail(DBS_EINVAL, "stage-blocked FP6 operands need the FP6-rate kernel");
     const int cv = cv_source(ea) | (cv_source(eb) << 2);
     const int ec = mfma8_code(ea) | (mfma8_code(eb) << 3);
     return run(dbs::kMXFP8, A, sA, B, sB, D, M, N, K, alpha, 8, 32, stream, nullptr, DBS_K_MAJOR, DBS_K_MAJOR, ec,
@@ -415,11 +434,15 @@ dbs_status gemm_nvfp4_fp6(const void *A, const uint8_t *sA, float tA, const void
     if ((int64_t)workspace_bytes < w.bytes) return fail(DBS_EINVAL, "workspace smaller than gemm_nvfp4_fp6_workspace()");
     int cus = 0;
     if ((st = device_cus(&cus)) != DBS_OK) return st;
-    hipError_t e = dbs::launch_requant_nvfp4_e2m3(static_cast<const uint8_t *>(A), sA, M * K, w.a, w.sa, cus, stream);
+    // the FP6-rate kernel reads the requantised codes stage-blocked
+    bool blocked = false;
+    if ((st = fp6_native(M, N, K, w.sa, w.sb, &blocked)) != DBS_OK) return st;
+    hipError_t e = dbs::launch_requant_nvfp4_e2m3(static_cast<const uint8_t *>(A), sA, M, K, blocked, w.a, w.sa, cus,
+                                                  stream);
     if (e == hipSuccess)
-        e = dbs::launch_requant_nvfp4_e2m3(static_cast<const uint8_t *>(B), sB, N * K, w.b, w.sb, cus, stream);
+        e = dbs::launch_requant_nvfp4_e2m3(static_cast<const uint8_t *>(B), sB, N, K, blocked, w.b, w.sb, cus, stream);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
-    return fp6_gemm(DBS_E2M3, DBS_E2M3, w.a, w.sa, w.b, w.sb, D, M, N, K, tA * tB, stream);
+    return fp6_gemm(DBS_E2M3, DBS_E2M3, w.a, w.sa, w.b, w.sb, D, M, N, K, tA * tB, stream, blocked);
 }
 
 // ---- quantisers ----------------------------------------------------------------

@@ -37,6 +37,17 @@
 //   the stage's operand rows); else one dword wave-load per wave and stage
 //   into per-stage slots.
 //
+// * Stage-blocked operands (Params::blk6, the FP4-rate NVFP4 path, whose
+//   workspace this library lays out itself): the 96 bytes of a stage of eight
+//   consecutive rows 8g .. 8g+7 lie together, 768 contiguous bytes at
+//   (g nk + ks) 768 + 96 (row % 8) for nk stages a row, so a wave-load
+//   (eight rows of one stage) reads six whole 128-byte lines where eight
+//   96-byte row pieces of the row-major layout touch twelve on average
+//   (a piece straddles two lines half of the time).  Row group g starts
+//   where row 8g of the row-major layout would, so the tile's rows start
+//   at the same offset; operand rows are padded to a multiple of 8 (the
+//   padding rows only feed outputs that are never stored).
+//
 // Problems this kernel takes (the host checks): FP6 on both operands,
 // K-major, K a multiple of 128 (whole stages; rows of whole dwords of
 // scales), scale rows on 4-byte boundaries, and enough 256 x 256 tiles to
@@ -90,7 +101,8 @@ struct Sc6 {
 struct Lane {
     int lane, h, lr, w, wm, wn;
     uint32_t fa, fb;        // LDS address of the lane's first cell: block 0, k-step 0, slot 0, swizzle applied
-    uint32_t r8;            // (lane / 8) * lda: the lane's row within a wave-load
+    uint32_t r8;            // the lane's row within a wave-load: (lane / 8) * lda, or (lane / 8) * 96 stage-blocked
+    uint32_t kst;           // bytes from one stage of a row to the next: 96, or 768 stage-blocked
     uint32_t x;             // (lane % 8) ^ (lane / 8): the lane's cell within a wave-load, before (L % 8)
     uint32_t sa, sb;        // chunked scales: LDS address of the lane's A / B row in chunk buffer 0, with
                             // 4 ((row / 8) % 4) in bits 2-3
@@ -172,14 +184,15 @@ __device__ __forceinline__ void adjust(Sc6 &sc, const Lane &c)
 // slot rows 8L .. 8L+7 with L = w kLoadsOp + q; lane i lands on cell i % 8
 // of row 8L + i / 8, whose swizzle is (i / 8) ^ (L % 8), and fetches the
 // 12-byte piece (i % 8) ^ (i / 8) ^ (L % 8) of that row's stage.  Rows past
-// the operand's end lie past the buffer resource and read zero.
+// the operand's end lie past the buffer resource and read zero (stage-blocked:
+// the resource ends with the last row's group of 8, padding rows included).
 template <bool IS_A>
 __device__ __forceinline__ void load_op(uint8_t *lds, int slot, __amdgpu_buffer_rsrc_t r, int ks, int q,
                                         const Lane &c, int lda)
 {
     const int L = c.w * kLoadsOp + q;
     const uint32_t piece = c.x ^ (uint32_t)(L & 7);
-    const uint32_t off = c.r8 + (uint32_t)(L * 8 * lda + ks * kGRow) + 12u * piece;
+    const uint32_t off = c.r8 + (uint32_t)(L * 8 * lda) + (uint32_t)ks * c.kst + 12u * piece;
     const int dst = slot * kSlot + (IS_A ? 0 : kOp) + L * 1024;
     lds_dma<12>(r, lds + dst, off);
 }
@@ -215,6 +228,20 @@ __device__ __forceinline__ void load_scale_portion(uint8_t *lds, int pc, __amdgp
 
 // Load n (0 .. kLoads-1) of the wave's share of a stage: operand rows, then
 // the stage's scales (per stage) or a portion of the next chunk (CH).
+// Buffer resources of a tile: those of the 8-bit kernels, with the operand
+// resources extended to whole groups of 8 rows when stage-blocked.
+__device__ __forceinline__ Target target6(const Params &p, int tile)
+{
+    Target t = tile_target<kMXFP8, S>(p, tile);
+    if (p.blk6) {
+        const TileRef r = tile_ref<S::TM, S::TN>(tile, p);
+        const int ra = (min(r.mend - r.m0, S::TM) + 7) & ~7, rb = (min(p.N - r.n0, S::TN) + 7) & ~7;
+        t.ra = make_rsrc(p.A + (int64_t)r.m0 * p.lda, (uint32_t)(ra * p.lda));
+        t.rb = make_rsrc(p.B + r.boff + (int64_t)r.n0 * p.lda, (uint32_t)(rb * p.lda));
+    }
+    return t;
+}
+
 template <bool CH>
 __device__ __forceinline__ void load_piece(uint8_t *lds, int slot, const Target &tg, int ks, int n, const Lane &c,
                                            const Params &p, const Chunk6 &cp)
@@ -318,7 +345,8 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp6_kernel(Params p)
     const uint32_t sw = (uint32_t)(((c.lr & 7) ^ (c.lr >> 3)) & 7);
     c.fa = (uint32_t)((c.wm * 128 + c.lr) * kRow) | ((sw << 4) ^ (uint32_t)(32 * c.h));
     c.fb = (uint32_t)(kOp + (c.wn * 64 + c.lr) * kRow) | ((sw << 4) ^ (uint32_t)(32 * c.h));
-    c.r8 = (uint32_t)((c.lane >> 3) * p.lda);
+    c.r8 = (uint32_t)((c.lane >> 3) * (p.blk6 ? kGRow : p.lda));
+    c.kst = (uint32_t)(p.blk6 ? 8 * kGRow : kGRow);
     c.x = (uint32_t)((c.lane & 7) ^ (c.lane >> 3));
     // chunk rows wm*128 + lr (A), TM + wn*64 + lr (B): bits 3-4 of either are those of lr
     const uint32_t s4 = (uint32_t)(4 * ((c.lr >> 3) & 3));
@@ -332,7 +360,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp6_kernel(Params p)
 
     // the first stage of the first tile; the stage stream then runs one
     // stage ahead across the workgroup's tiles
-    Target ld = tile_target<kMXFP8, S>(p, tile);
+    Target ld = target6(p, tile);
     Chunk6 cp{0, 0, 0, ld.rsa, ld.rsb};
     if constexpr (CH) {
 #pragma unroll
@@ -374,14 +402,14 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp6_kernel(Params p)
                 int ks = s + 1;
                 if (ks == p.nk) {
                     ks = 0;
-                    ld = next < ntiles ? tile_target<kMXFP8, S>(p, next) : null_target();
+                    ld = next < ntiles ? target6(p, next) : null_target();
                 }
                 cp.j = s & (kSpc - 1);
                 cp.lchunk = s / kSpc + 1;
                 if (cp.lchunk == nch) {
                     cp.lchunk = 0;
                     if (cp.j == 0) {
-                        const Target nt = next < ntiles ? tile_target<kMXFP8, S>(p, next) : null_target();
+                        const Target nt = next < ntiles ? target6(p, next) : null_target();
                         cp.sa = nt.rsa;
                         cp.sb = nt.rsb;
                     }
@@ -398,7 +426,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp6_kernel(Params p)
                 int ks = s + 1;
                 if (ks == p.nk) {
                     ks = 0;
-                    ld = next < ntiles ? tile_target<kMXFP8, S>(p, next) : null_target();
+                    ld = next < ntiles ? target6(p, next) : null_target();
                 }
                 stage<CA, CB, CH>(acc, F, sprev, scur, lds, rs, ld, ks, c, p, cp);
                 xs = rs;

@@ -47,6 +47,9 @@ struct Params {
     int goff[kMaxGroups + 1];
     int gtiles[kMaxGroups + 1];
     float galpha[kMaxGroups];
+
+    int blk6;             // FP6 kernel: operand rows stored stage-blocked (see gemm_mxfp6.hip), rows
+                          // padded to a multiple of 8
 };
 
 // Output tile shapes (rows of A x rows of B per tile).  Square tiles are the
@@ -74,10 +77,12 @@ hipError_t launch_quant_nvfp4(const float *x, int64_t n, uint8_t *codes, uint8_t
 // scales per 32) for the FP8-rate NVFP4 GEMM.
 hipError_t launch_requant_nvfp4_mx8(const uint8_t *codes, const uint8_t *scales, int64_t n, uint8_t *out,
                                     uint8_t *out_scales, int cus, hipStream_t stream);
-// NVFP4 operand of n elements -> MXFP6 E2M3 (packed codes, E8M0 scales per
-// 32) for the FP4-rate NVFP4 GEMM; out 8-byte aligned.
-hipError_t launch_requant_nvfp4_e2m3(const uint8_t *codes, const uint8_t *scales, int64_t n, uint8_t *out,
-                                     uint8_t *out_scales, int cus, hipStream_t stream);
+// NVFP4 operand of rows x K elements (K-major) -> MXFP6 E2M3 (packed codes,
+// E8M0 scales per 32, row-major) for the FP4-rate NVFP4 GEMM; out 8-byte
+// aligned.  blocked: codes in the FP6 kernel's stage-blocked layout (K a
+// multiple of 128), rows padded to a multiple of 8 with zero codes.
+hipError_t launch_requant_nvfp4_e2m3(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
+                                     bool blocked, uint8_t *out, uint8_t *out_scales, int cus, hipStream_t stream);
 hipError_t launch_quant_bf16(const float *x, int64_t n, uint16_t *out, int cus, hipStream_t stream);
 
 // The FP8-rate NVFP4 GEMM behind both of its entry points (dbs.cpp): host

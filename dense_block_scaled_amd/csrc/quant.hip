@@ -336,18 +336,39 @@ __global__ __launch_bounds__(256) void requant_nvfp4_mx8_kernel(const uint8_t *_
 // 6j .. 6j+5 of 24 bytes, the rows' own packing).  Checked
 // bit for bit against the oracle's recipe over every pair of finite E4M3
 // group scales and every E2M1 code.
+//
+// Output order: lane b writes the 24 bytes at 24 b.  Row-major (nk = 0) that
+// is block b of the rows; stage-blocked (nk = stages of 128 elements a row,
+// the FP6 kernel's layout) b counts the four blocks of a stage of a row, the
+// eight rows of a group, the stages, then the groups, so the 768 bytes of one
+// stage of rows 8g .. 8g+7 lie together; padding rows past the last
+// (rows rounded up to 8) get zero codes.  Scales stay row-major either way.
 __global__ __launch_bounds__(256) void requant_nvfp4_e2m3_kernel(const uint8_t *__restrict__ codes,
                                                                  const uint8_t *__restrict__ scales,
                                                                  uint8_t *__restrict__ out,
-                                                                 uint8_t *__restrict__ out_scales, int64_t nblocks)
+                                                                 uint8_t *__restrict__ out_scales, int64_t rows,
+                                                                 int kbr, int nk)
 {
     typedef __attribute__((ext_vector_type(2))) float f32x2;
     typedef __attribute__((ext_vector_type(16))) float f32x16;
     typedef __attribute__((ext_vector_type(6))) unsigned int u32x6;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t nblocks = (nk ? (rows + 7) / 8 * 8 : rows) * kbr;
     for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride) {
-        const uint4 c = *reinterpret_cast<const uint4 *>(codes + 16 * b);
-        const float s0 = dec_e4m3(scales[2 * b]), s1 = dec_e4m3(scales[2 * b + 1]);
+        uint2 *dst = reinterpret_cast<uint2 *>(out + 24 * b);
+        int64_t sb = b;         // the block's index in the row-major order of the input
+        if (nk) {
+            const int64_t t = b >> 5;
+            const int64_t g = t / nk;
+            const int64_t row = 8 * g + ((b >> 2) & 7);
+            if (row >= rows) {
+                dst[0] = dst[1] = dst[2] = uint2{0u, 0u};
+                continue;
+            }
+            sb = row * kbr + 4 * (t - g * nk) + (b & 3);
+        }
+        const uint4 c = *reinterpret_cast<const uint4 *>(codes + 16 * sb);
+        const float s0 = dec_e4m3(scales[2 * sb]), s1 = dec_e4m3(scales[2 * sb + 1]);
         const float m = __builtin_fmaxf(__builtin_fabsf(s0), __builtin_fabsf(s1));
         int E = 0;
         if (m > 0.0f) {
@@ -355,7 +376,7 @@ __global__ __launch_bounds__(256) void requant_nvfp4_e2m3_kernel(const uint8_t *
             --E;
             if (m > __builtin_ldexpf(1.25f, E)) ++E;
         }
-        out_scales[b] = (uint8_t)(E + 127);
+        out_scales[sb] = (uint8_t)(E + 127);
         const float f0 = __builtin_ldexpf(s0, -E), f1 = __builtin_ldexpf(s1, -E);
         const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
         // the conversion packs its two 16-value inputs interleaved (output
@@ -377,7 +398,6 @@ __global__ __launch_bounds__(256) void requant_nvfp4_e2m3_kernel(const uint8_t *
             }
         }
         const u32x6 r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 1.0f);
-        uint2 *dst = reinterpret_cast<uint2 *>(out + 24 * b);
         dst[0] = uint2{r[0], r[1]};
         dst[1] = uint2{r[2], r[3]};
         dst[2] = uint2{r[4], r[5]};
@@ -440,13 +460,14 @@ hipError_t launch_requant_nvfp4_mx8(const uint8_t *codes, const uint8_t *scales,
     return hipGetLastError();
 }
 
-hipError_t launch_requant_nvfp4_e2m3(const uint8_t *codes, const uint8_t *scales, int64_t n, uint8_t *out,
-                                     uint8_t *out_scales, int cus, hipStream_t stream)
+hipError_t launch_requant_nvfp4_e2m3(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
+                                     bool blocked, uint8_t *out, uint8_t *out_scales, int cus, hipStream_t stream)
 {
-    const int64_t nblocks = n / 32;
+    if (K % 32 || (blocked && K % 128)) return hipErrorInvalidValue;
+    const int64_t nblocks = (blocked ? (rows + 7) / 8 * 8 : rows) * (K / 32);
     const int grid = grid_for(nblocks, cus);
     hipLaunchKernelGGL(requant_nvfp4_e2m3_kernel, dim3(grid), dim3(256), 0, stream, codes, scales, out, out_scales,
-                       nblocks);
+                       rows, (int)(K / 32), blocked ? (int)(K / 128) : 0);
     return hipGetLastError();
 }
 

@@ -217,10 +217,12 @@ dbs_status gemm_nvfp4_fp8(const void *A, const uint8_t *sA, float tA,
  * 32), K-major operands.  workspace: device memory of at least
  * gemm_nvfp4_fp6_workspace(M, N, K) bytes, 256-byte aligned, owned by the
  * caller (overwritten, not read before being written; calls sharing one
- * workspace must not overlap).  Two requantisation kernels and the GEMM are
- * enqueued on `stream`; the GEMM runs at the FP6 rate on 256 x 256 tiles when
- * K is a multiple of 128 and those tiles fill more than a quarter of the
- * CUs, else widened to 8 bits on 256 x 64 tiles (gemm_mx_mixed's FP6 paths).
+ * workspace must not overlap; its layout is internal to the library).  Two
+ * requantisation kernels and the GEMM are enqueued on `stream`; the GEMM
+ * runs at the FP6 rate on 256 x 256 tiles when K is a multiple of 128 and
+ * those tiles fill more than a quarter of the CUs (the requantised codes are
+ * then stored in that kernel's stage-blocked order), else widened to 8 bits
+ * on 256 x 64 tiles (gemm_mx_mixed's FP6 paths).
  */
 size_t gemm_nvfp4_fp6_workspace(int64_t M, int64_t N, int64_t K);    /* 0 for invalid sizes */
 dbs_status gemm_nvfp4_fp6(const void *A, const uint8_t *sA, float tA,

@@ -321,13 +321,15 @@ def test_nvfp4_fp8_noalloc_validation():
 
 def test_nvfp4_fp6_workspace_and_validation():
     """The FP4-rate NVFP4 entry point: workspace size (E2M3 codes of both
-    operands, 3K/4 bytes per row, and their E8M0 scales, each part 256-byte
-    aligned), validation before any device work."""
+    operands, 3K/4 bytes per row with the rows padded to a multiple of 8,
+    and their E8M0 scales, each part 256-byte aligned), validation before
+    any device work."""
     L = dbs.lib()
-    M, N, K = 300, 200, 512
     a256 = lambda x: (x + 255) // 256 * 256
-    want = a256(M * K * 3 // 4) + a256(N * K * 3 // 4) + a256(M * K // 32) + a256(N * K // 32)
-    assert L.gemm_nvfp4_fp6_workspace(M, N, K) == want
+    r8 = lambda x: (x + 7) // 8 * 8
+    for M, N, K in [(300, 200, 512), (301, 203, 512), (1, 9, 96)]:
+        want = a256(r8(M) * K * 3 // 4) + a256(r8(N) * K * 3 // 4) + a256(M * K // 32) + a256(N * K // 32)
+        assert L.gemm_nvfp4_fp6_workspace(M, N, K) == want, (M, N, K)
     assert L.gemm_nvfp4_fp6_workspace(M, N, 48) == 0
     f = ctypes.c_float(1.0)
     call = lambda M, N, K, ws, nb, la=0: L.gemm_nvfp4_fp6(FAKE, FAKE, f, FAKE, FAKE, f, FAKE, M, N, K, la, 0, ws, nb,

@@ -7,8 +7,8 @@ outputs must agree bit for bit (and the product build's with the oracle).
 The cases walk every ring of the kernels: 256 x 256 and 256 x 64 tiles, more
 tiles than CUs, a partial last stage, two- and three-slot rings, chunked and
 per-stage MX scales, the packed E2M1 ring beside an 8-bit operand, the FP6
-kernel's chunk buffers, the raw NVFP4 stages, MN-major staging and both
-release points of the decoupled-ring BF16 kernel."""
+kernel's chunk buffers and stage-blocked operands, the raw NVFP4 stages,
+MN-major staging and both release points of the decoupled-ring BF16 kernel."""
 import numpy as np
 import pytest
 import torch
@@ -74,6 +74,18 @@ def test_poison_mixed(poison, pair, shape):
     d = _gpu.to_dev(w)
     _same(lambda: dbs.gemm_mx_mixed(pair[0], pair[1], d["A"], d["sA"], d["B"], d["sB"], K=K), poison,
           f"{pair} {shape}")
+
+
+@pytest.mark.parametrize("shape", [(2304, 2304, 512), (2301, 2299, 640)], ids=lambda s: "x".join(map(str, s)))
+def test_poison_nvfp4_fp6(poison, shape):
+    """The FP6-rate kernel on the FP4-rate NVFP4 path's stage-blocked operands
+    (chunked scales; per-stage scales and partial row groups)."""
+    M, N, K = shape
+    _gpu.say(f"[poison] nvfp4_fp6 {shape}")
+    w = synth.workload("nvfp4", M, N, K, 79, 80)
+    d = _gpu.to_dev(w)
+    _same(lambda: dbs.gemm_nvfp4_fp6(d["A"], d["sA"], w["tA"], d["B"], d["sB"], w["tB"]), poison,
+          f"nvfp4_fp6 {shape}")
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp4", "nvfp4"])
