@@ -220,7 +220,7 @@ dbs_status gemm_nvfp4_fp8(const void *A, const uint8_t *sA, float tA,
  * workspace must not overlap; its layout is internal to the library).  Two
  * requantisation kernels and the GEMM are enqueued on `stream`; the GEMM
  * runs at the FP6 rate on 256 x 256 tiles when K is a multiple of 128 and
- * those tiles fill more than a quarter of the CUs (the requantised codes are
+ * those tiles fill at least a quarter of the CUs (the requantised codes are
  * then stored in that kernel's stage-blocked order), else widened to 8 bits
  * on 256 x 64 tiles (gemm_mx_mixed's FP6 paths).
  */

@@ -41,10 +41,10 @@ def _r8(x):
 
 def fp6_rate(M, N, K):
     """Whether the GEMM runs on the FP6-rate kernel (256 x 256 tiles filling
-    more than a quarter of the CUs, K whole 128-K stages), which reads the
+    at least a quarter of the CUs, K whole 128-K stages), which reads the
     requantised codes stage-blocked."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    return K % 128 == 0 and 4 * (-(-M // 256)) * (-(-N // 256)) > cus
+    return K % 128 == 0 and 4 * (-(-M // 256)) * (-(-N // 256)) >= cus
 
 
 def _unblock(h, rows, K):
@@ -76,10 +76,12 @@ def _r(got, d_ref, an, bn):
     return oracle.rel_errors(got, d_ref, an, bn)
 
 
-# the FP6-rate kernel (256 x 256 tiles, K % 128 == 0: the first three; the
-# third with rows that leave partial groups of 8 and an odd stage count), the
-# widening path (few tiles; K % 128 != 0)
-SHAPES = [(2304, 2304, 512), (2200, 2600, 256), (2301, 2299, 640), (300, 520, 384), (2304, 2304, 352)]
+# the FP6-rate kernel (256 x 256 tiles, K % 128 == 0: the first four; the
+# third with rows that leave partial groups of 8 and an odd stage count, the
+# fourth at exactly a quarter of the CUs' worth of tiles on a 256-CU part),
+# the widening path (few tiles; K % 128 != 0)
+SHAPES = [(2304, 2304, 512), (2200, 2600, 256), (2301, 2299, 640), (256, 16384, 512), (300, 520, 384),
+          (2304, 2304, 352)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
