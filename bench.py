@@ -150,6 +150,34 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def git_sha():
+    """HEAD's commit id, read from the repository's .git files (None where the
+    tree carries no git metadata, as in a copied snapshot)."""
+    g = ROOT / ".git"
+    try:
+        head = (g / "HEAD").read_text().strip()
+        if not head.startswith("ref: "):
+            return head or None
+        ref = head[5:]
+        if (g / ref).exists():
+            return (g / ref).read_text().strip() or None
+        for line in (g / "packed-refs").read_text().splitlines():
+            if line.endswith(" " + ref):
+                return line.split()[0]
+    except OSError:
+        return None
+    return None
+
+
+def provenance(name):
+    """Where a record's numbers come from: the seeds of the workload's inputs
+    (A and its scales, B and its scales) and of its sampled output entries,
+    the hash of the kernel sources, the commit."""
+    c = W[name]["c"]
+    return {"seeds": {"A": 100 * c + 1, "B": 100 * c + 2, "sampled_entries": 100 * c + 3},
+            "kernel_source_sha": kernel_source_hash(), "git_sha": git_sha()}
+
+
 def traffic_for(workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
@@ -412,7 +440,7 @@ def record(name, w, avg, tflops, gbs, mhz, r, r_exact):
          "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_GBS, 4),
          "sclk_mhz": round(mhz, 0) if mhz else None,
          "frac_mfma_peak_at_sclk": round(tflops / (peak * mhz / CLOCK_PEAK_MHZ), 4) if mhz else None,
-         "max_r": r}
+         "max_r": r, "seeds": provenance(name)["seeds"]}
     if "alt" in spec:
         e["frac_" + spec["alt"] + "_peak"] = round(tflops / PEAK[spec["alt"]], 4)
     if name.endswith("skinny"):
@@ -494,6 +522,7 @@ def main():
                      "frac": round(tflops / peak, 4), "traffic": traffic_for(workload)},
         "sclk_mhz": head["sclk_mhz"],
         "parity_sample_max_r": r,
+        "provenance": provenance(fmt),
     }
     if not args.no_cpu:
         cb, rmax = cpu_baseline(fmt, w, D)
