@@ -3,7 +3,7 @@
     python tests/asan_run.py
 
 Copies the repository to a temporary folder, builds there the C-ABI library
-with its host code instrumented (each translation unit through hipcc with the
+and its LDS-poison debug build with their host code instrumented (each translation unit through hipcc with the
 sanitizer flags on the host side only; the gfx950 device code is built as
 usual) and the C oracle with the sanitizer, and runs `pytest -m "not gpu"`
 against those builds with the sanitizer runtime preloaded.  Exits with
@@ -36,17 +36,20 @@ def main() -> int:
         csrc = repo / "dense_block_scaled_amd" / "csrc"
         flags = [f"--offload-arch={b.ARCH}", "-O1", "-g", "-std=c++17", "-fPIC", f"-I{repo / 'include'}",
                  f"-I{csrc}", *b.DEVICE_FLAGS, *HOST_ASAN]
-        objs = []
 
-        def one(name):
-            obj = tmp / (name + ".o")
-            subprocess.run([HIPCC, *flags, "-c", str(csrc / name), "-o", str(obj)], check=True)
+        def one(job):
+            name, poison = job
+            obj = tmp / (name + (".poison.o" if poison else ".o"))
+            subprocess.run([HIPCC, *flags, *(["-DDBS_LDS_POISON=1"] if poison else []), "-c", str(csrc / name),
+                            "-o", str(obj)], check=True)
             return obj
 
-        with ThreadPoolExecutor(max_workers=min(len(b.SOURCES), os.cpu_count() or 1)) as pool:
-            objs = list(pool.map(one, b.SOURCES))
-        subprocess.run([HIPCC, f"--offload-arch={b.ARCH}", "-shared", "-fPIC", *HOST_ASAN, *map(str, objs), "-o",
-                        str(repo / "dense_block_scaled_amd" / "libdbs.so")], check=True)
+        # the product library and the LDS-poison debug build, both with instrumented host code
+        for poison, lib in ((False, "libdbs.so"), (True, "libdbs_poison.so")):
+            with ThreadPoolExecutor(max_workers=min(len(b.SOURCES), os.cpu_count() or 1)) as pool:
+                objs = list(pool.map(one, [(n, poison) for n in b.SOURCES]))
+            subprocess.run([HIPCC, f"--offload-arch={b.ARCH}", "-shared", "-fPIC", *HOST_ASAN, *map(str, objs), "-o",
+                            str(repo / "dense_block_scaled_amd" / lib)], check=True)
         subprocess.run(["gcc", "-std=c11", "-O1", "-g", "-fPIC", "-shared", "-fsanitize=address",
                         "-fno-omit-frame-pointer", "-ffp-contract=off", "-Wall", "-pthread",
                         str(repo / "oracle" / "oracle.c"), "-o", str(repo / "oracle" / "liboracle.so"), "-lm"],
