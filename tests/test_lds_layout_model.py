@@ -15,12 +15,15 @@ Layouts:
 * raw NVFP4 per-stage scale rows (16 bytes, each lane half reading two bytes
   of the k-step's dword), dwords permuted by bits 3-4 of the row;
 * operand rows of 128 bytes, 16-byte chunks permuted by (row ^ row / 8) % 8,
-  read 16 bytes a lane.
+  read 16 bytes a lane;
+* the FP6 kernel's operand rows: 12-byte pieces landing in 16-byte cells
+  under the same permutation, read 12 bytes a lane (taken here in the
+  passes of 16-byte reads).
 """
 import pytest
 
 TM = TN = 256
-MODELS = {"128B": (32, {4: 32, 8: 16, 16: 8}), "256B": (64, {4: 32, 8: 32, 16: 16})}
+MODELS = {"128B": (32, {4: 32, 8: 16, 12: 8, 16: 8}), "256B": (64, {4: 32, 8: 32, 12: 16, 16: 16})}
 
 
 def banks_ok(addrs, nbytes, model):
@@ -158,3 +161,42 @@ def test_operand_chunk_swizzle():
             # lanes 0..31 (h = 0) and 32..63 (h = 1) go in separate passes
             for model in MODELS:
                 assert banks_ok(addrs[:32], 16, model) and banks_ok(addrs[32:], 16, model), (base, kk, model)
+
+
+# ---- the FP6 kernel's operand rows ------------------------------------------------
+
+def test_fp6_operand_pieces():
+    """gemm_mxfp6: wave-load L (0 .. 31) of an operand's 256 rows puts lane i's
+    12 bytes in cell i % 8 of row 8L + i / 8, fetching piece (i % 8) ^ (i / 8) ^
+    (L % 8) of that row's stage (so cell c of row r holds piece c ^ swz(r)).
+    Lane (h, lr) of wave (wm, wn) reads k-step kk of block blk from base
+    (row * 128) | ((swz(lr) << 4) ^ 32 h), XORed with 64 (kk ^ blk % 2), plus
+    blk * 4096, and the cell after it (address ^ 16): pieces 4 kk + 2 h and
+    4 kk + 2 h + 1 of rows wm * 128 + 32 blk + lr (A, 4 blocks) and
+    wn * 64 + 32 blk + lr (B, 2 blocks)."""
+    def swz(r):
+        return (r ^ (r >> 3)) & 7
+    lds = {}
+    for L in range(32):
+        for i in range(64):
+            r, c = 8 * L + i // 8, i % 8
+            lds[r * 128 + 16 * c] = (r, (i % 8) ^ (i // 8) ^ (L % 8))
+    assert all(piece == (a % 128) // 16 ^ swz(r) for a, (r, piece) in lds.items())
+    for nblk, nw, rows_per_wave in ((4, 2, 128), (2, 4, 64)):
+        for wv in range(nw):
+            for kk in range(2):
+                for blk in range(nblk):
+                    addrs = []
+                    for lane in range(64):
+                        h, lr = lane >> 5, lane & 31
+                        base = ((wv * rows_per_wave + lr) * 128) | ((swz(lr) << 4) ^ (32 * h))
+                        x = (base ^ (64 * (kk ^ (blk & 1)))) + blk * 32 * 128
+                        row = wv * rows_per_wave + 32 * blk + lr
+                        assert lds[x] == (row, 4 * kk + 2 * h) and lds[x ^ 16] == (row, 4 * kk + 2 * h + 1)
+                        addrs.append(x)
+                    # the two reads of the fragment (x, then x ^ 16), each in two lane halves
+                    for rd in (addrs, [x ^ 16 for x in addrs]):
+                        for model in MODELS:
+                            assert banks_ok(rd[:32], 12, model) and banks_ok(rd[32:], 12, model), \
+                                (nblk, wv, kk, blk, model)
+
